@@ -1,0 +1,111 @@
+"""Seeded synthetic inputs for the SSD scan (shared by the tests and the benchmark).
+
+This module draws random tensors and nothing else: it holds none of the scan's
+arithmetic.  The distributions are the workload recipe of the project (the pages
+publish no data set):
+
+* x, D, dy, d_final ~ N(0, 1)
+* B, C ~ N(0, 1) / sqrt(dstate), iid per element and head (no group sharing)
+* dt = softplus(z - dt_shift), z ~ N(0, 1)   (the discretised step is the input)
+* A_h = -exp(u * ln 16), u ~ U(0, 1), so A lies in [-16, -1]
+* initial_state = init_std * N(0, 1)  (init_std = 0 gives zeros)
+* d_m2 ~ N(0, 1) [b, h, r, r], d_m1 ~ N(0, 1) [b, h, r]
+
+Draw order is fixed (x, B, C, z, u, D, init, dy, d_final, d_m2, d_m1) from one
+CPU ``torch.Generator`` seeded with ``seed``.  For bf16 workloads x, B, C and dy
+are rounded to bfloat16 (round-to-nearest-even) after the fp32 draw; every other
+tensor stays fp32.
+
+Layouts follow the pages' tensor naming: x/dy ``[b, n, l, h, p]``, B/C
+``[b, n, l, h, r]``, dt ``[b, h, n, l]``, A/D ``[h]``, states ``[b, h, p, r]``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    seq: int
+    nheads: int
+    headdim: int
+    dstate: int
+    chunk_len: int
+    io: str = "f32"            # "f32" or "bf16" (x, B, C, dy, y and their gradients)
+    dt_shift: float = 2.0
+    init_std: float = 0.0
+    valid_len: Optional[Sequence[int]] = None
+    seed: int = 1000
+
+    @property
+    def nchunks(self) -> int:
+        return self.seq // self.chunk_len
+
+    def describe(self) -> dict:
+        d = dict(workload=self.name, batch=self.batch, seq_len=self.seq, nheads=self.nheads,
+                 headdim=self.headdim, dstate=self.dstate, chunk_len=self.chunk_len,
+                 io_dtype=self.io)
+        if self.valid_len is not None:
+            d["valid_len"] = list(self.valid_len)
+        return d
+
+
+# The five named workloads (shapes only; "130M"/"2.7B" borrow model shapes, no weights).
+WORKLOADS = {
+    "tiny_fp32": Workload("tiny_fp32", 1, 256, 2, 16, 16, 64, seed=1000),
+    "mamba2_130m_fp32": Workload("mamba2_130m_fp32", 4, 2048, 24, 64, 128, 256, seed=1001),
+    "mamba2_2p7b_bf16": Workload("mamba2_2p7b_bf16", 2, 4096, 80, 64, 128, 256, io="bf16",
+                                 seed=1002),
+    "long_context_64k_fp32": Workload("long_context_64k_fp32", 1, 65536, 32, 64, 128, 256,
+                                      dt_shift=4.0, init_std=0.1, seed=1003),
+    "moments_valid_len_fp32": Workload("moments_valid_len_fp32", 2, 4096, 24, 64, 64, 128,
+                                       valid_len=(4096, 3000), seed=1004),
+}
+WORKLOAD_ORDER = list(WORKLOADS)
+
+
+def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
+    """Draw every input of workload ``w`` on the CPU (see module docstring)."""
+    g = torch.Generator().manual_seed(w.seed if seed is None else seed)
+    b, n, l, h, p, r = w.batch, w.nchunks, w.chunk_len, w.nheads, w.headdim, w.dstate
+    if n * l != w.seq:
+        raise ValueError("seq must be a multiple of chunk_len")
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, dtype=torch.float32)
+
+    x = randn(b, n, l, h, p)
+    B = randn(b, n, l, h, r) / math.sqrt(r)
+    C = randn(b, n, l, h, r) / math.sqrt(r)
+    z = randn(b, h, n, l)
+    u = torch.rand(h, generator=g, dtype=torch.float32)
+    D = randn(h)
+    init = randn(b, h, p, r) * w.init_std
+    dy = randn(b, n, l, h, p)
+    d_final = randn(b, h, p, r)
+    d_m2 = randn(b, h, r, r)
+    d_m1 = randn(b, h, r)
+    dt = torch.nn.functional.softplus(z - w.dt_shift)
+    A = -torch.exp(u * math.log(16.0))
+    if w.io == "bf16":
+        x, B, C, dy = (t.to(torch.bfloat16) for t in (x, B, C, dy))
+    elif w.io != "f32":
+        raise ValueError(f"unknown io dtype {w.io!r}")
+    out = dict(x=x, dt=dt, A=A, B=B, C=C, D=D, init=init, dy=dy, d_final=d_final,
+               d_m2=d_m2, d_m1=d_m1)
+    if w.valid_len is not None:
+        out["valid_len"] = torch.tensor(list(w.valid_len), dtype=torch.int64)
+    return out
+
+
+def custom(name="custom", batch=1, seq=256, nheads=2, headdim=16, dstate=16, chunk_len=64,
+           io="f32", dt_shift=2.0, init_std=0.0, valid_len=None, seed=7) -> Workload:
+    """A workload with the standard distributions and arbitrary shapes (for tests)."""
+    return Workload(name, batch, seq, nheads, headdim, dstate, chunk_len, io=io,
+                    dt_shift=dt_shift, init_std=init_std, valid_len=valid_len, seed=seed)

@@ -1,0 +1,167 @@
+"""CPU oracle for the Mamba-2 SSD chunked scan -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (``mamba_ssd_chunked_amd``
+and its HIP library) never imports, links or calls it, and the two share no code.
+
+The computation lives in ``ssd_oracle.c`` (plain C, fp64, single-threaded): the
+token-by-token recurrence ``h_t = exp(dt_t A) h_{t-1} + dt_t x_t (outer) B_t``,
+``y_t = C_t . h_t + D x_t`` and its reverse-mode recurrence, plus the pooled
+state moments of the burn-mamba ``state_moments.rs`` page and their gradient.
+This module only builds the shared library with gcc and marshals numpy arrays.
+
+Every function takes and returns float64 numpy arrays in the pages' layouts:
+x/y ``[b, n, l, h, p]``, B/C ``[b, n, l, h, r]``, dt ``[b, h, n, l]``,
+A/D ``[h]``, states ``[b, h, p, r]``, m2 ``[b, h, r, r]``, m1 ``[b, h, r]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssd_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_build", "libssd_oracle.so")
+
+_lib = None
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_int64) for k in
+                ("batch", "nchunks", "chunk_len", "nheads", "headdim", "dstate")]
+
+
+def build(force: bool = True) -> str:
+    """Compile ``ssd_oracle.c`` with gcc (-O2, no fast-math) into ``_build/``."""
+    os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c99", "-fno-fast-math", "-ffp-contract=off",
+                        "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build(force=True)
+    _lib = _open(_LIB_PATH)
+    return _lib
+
+
+def use_library(path):
+    """Point this module at another build of ``ssd_oracle.c`` (the mutation tests
+    use it to run the pins against deliberately broken copies).  Returns the
+    previous library handle; ``use_library(None)`` restores the default build."""
+    global _lib
+    prev = _lib
+    _lib = None if path is None else _open(path)
+    return prev
+
+
+def _open(path):
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.oracle_ssd_fwd.argtypes = [ctypes.POINTER(_Dims)] + [P] * 9
+    lib.oracle_ssd_bwd.argtypes = [ctypes.POINTER(_Dims)] + [P] * 16 + [ctypes.c_int64]
+    lib.oracle_state_moments.argtypes = [ctypes.POINTER(_Dims)] + [P] * 9
+    lib.oracle_state_moments_bwd.argtypes = [ctypes.POINTER(_Dims)] + [P] * 13 + [ctypes.c_int64]
+    for f in (lib.oracle_ssd_fwd, lib.oracle_ssd_bwd, lib.oracle_state_moments,
+              lib.oracle_state_moments_bwd):
+        f.restype = ctypes.c_int
+    return lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor -> numpy (CPU copy)
+        a = a.detach().cpu().double().numpy()
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dims(x, B):
+    b, n, l, h, p = x.shape
+    r = B.shape[-1]
+    return _Dims(b, n, l, h, p, r)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise RuntimeError(f"oracle {name} failed with code {rc}")
+
+
+def ssd_fwd(x, dt, A, B, C, D, init=None):
+    """Token-by-token forward.  Returns ``(y, final_state)``."""
+    x, dt, A, B, C, D, init = map(_f64, (x, dt, A, B, C, D, init))
+    d = _dims(x, B)
+    y = np.empty_like(x)
+    final = np.empty((d.batch, d.nheads, d.headdim, d.dstate))
+    rc = _load().oracle_ssd_fwd(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                _ptr(D), _ptr(init), _ptr(y), _ptr(final))
+    _check(rc, "ssd_fwd")
+    return y, final
+
+
+def ssd_bwd(dy, d_final, x, dt, A, B, C, D, init=None, seg: int = 256):
+    """Reverse-mode recurrence.  Returns a dict with the seven gradients."""
+    dy, d_final, x, dt, A, B, C, D, init = map(_f64, (dy, d_final, x, dt, A, B, C, D, init))
+    d = _dims(x, B)
+    out = dict(d_x=np.empty_like(x), d_dt=np.empty_like(dt), d_A=np.empty_like(A),
+               d_B=np.empty_like(B), d_C=np.empty_like(C), d_D=np.empty_like(D),
+               d_init=np.empty((d.batch, d.nheads, d.headdim, d.dstate)))
+    rc = _load().oracle_ssd_bwd(ctypes.byref(d), _ptr(dy), _ptr(d_final), _ptr(x), _ptr(dt),
+                                _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init),
+                                _ptr(out["d_x"]), _ptr(out["d_dt"]), _ptr(out["d_A"]),
+                                _ptr(out["d_B"]), _ptr(out["d_C"]), _ptr(out["d_D"]),
+                                _ptr(out["d_init"]), int(seg))
+    _check(rc, "ssd_bwd")
+    return out
+
+
+def _valid(valid_len, batch):
+    if valid_len is None:
+        return None
+    v = np.ascontiguousarray(np.asarray(valid_len, dtype=np.int64).reshape(batch))
+    return v
+
+
+def state_moments(x, dt, A, B, init=None, valid_len=None):
+    """Brute-force pooled moments.  Returns ``(m2, m1, count)``."""
+    x, dt, A, B, init = map(_f64, (x, dt, A, B, init))
+    d = _dims(x, B)
+    v = _valid(valid_len, d.batch)
+    m2 = np.empty((d.batch, d.nheads, d.dstate, d.dstate))
+    m1 = np.empty((d.batch, d.nheads, d.dstate))
+    count = np.empty((d.batch,), dtype=np.int64)
+    rc = _load().oracle_state_moments(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                      _ptr(init), None if v is None else _ptr(v), _ptr(m2),
+                                      _ptr(m1), _ptr(count))
+    _check(rc, "state_moments")
+    return m2, m1, count
+
+
+def state_moments_bwd(d_m2, d_m1, x, dt, A, B, init=None, valid_len=None, seg: int = 256):
+    """Gradient of ``<d_m2, m2> + <d_m1, m1>``.  Returns a dict of five gradients."""
+    d_m2, d_m1, x, dt, A, B, init = map(_f64, (d_m2, d_m1, x, dt, A, B, init))
+    d = _dims(x, B)
+    v = _valid(valid_len, d.batch)
+    out = dict(d_x=np.empty_like(x), d_dt=np.empty_like(dt), d_A=np.empty_like(A),
+               d_B=np.empty_like(B), d_init=np.empty((d.batch, d.nheads, d.headdim, d.dstate)))
+    rc = _load().oracle_state_moments_bwd(ctypes.byref(d), _ptr(d_m2), _ptr(d_m1), _ptr(x),
+                                          _ptr(dt), _ptr(A), _ptr(B), _ptr(init),
+                                          None if v is None else _ptr(v), _ptr(out["d_x"]),
+                                          _ptr(out["d_dt"]), _ptr(out["d_A"]), _ptr(out["d_B"]),
+                                          _ptr(out["d_init"]), int(seg))
+    _check(rc, "state_moments_bwd")
+    return out

@@ -1,0 +1,74 @@
+"""The oracle's pins must catch plausible mistakes (no GPU).
+
+Each case copies ``oracle/ssd_oracle.c``, plants one mistake by a textual
+substitution (a dropped term, a wrong sign, a wrong operand or index, a missing
+transpose), builds the copy with gcc into a temporary directory and runs the pin
+tests against it.  At least one pin must fail for every planted mistake.  The
+committed oracle is never modified.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_moments as tm
+import test_oracle_ssd as ts
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")
+
+MUTANTS = {
+    "drop_skip_term": ("yt[p] = acc + D[h] * xt[p];", "yt[p] = acc;"),
+    "decay_sign": ("const double a = exp(dtv * A[h]);", "const double a = exp(-dtv * A[h]);"),
+    "y_reads_B_not_C": ("acc += H[p * R + r] * Ct[r];", "acc += H[p * R + r] * Bt[r];"),
+    "dC_uses_previous_state": ("acc += dyt[p] * Ht[p * R + r];", "acc += dyt[p] * Hp[p * R + r];"),
+    "ddt_drops_decay_term": ("d_dt[off_dt(d, b, h, t)] = gw + Ah * q;",
+                             "d_dt[off_dt(d, b, h, t)] = gw;"),
+    "adjoint_not_decayed": ("for (int64_t i = 0; i < PR; ++i) G[i] *= a;",
+                            "for (int64_t i = 0; i < PR; ++i) G[i] *= 1.0;"),
+    "dB_missing_dt": ("dBt[r] = dtv * acc;", "dBt[r] = acc;"),
+    "dA_missing_dt": ("*d_A_acc += dtv * q;", "*d_A_acc += q;"),
+    "m1_squares_rows": ("M1[r1] += row[r1];", "M1[r1] += row[r1] * row[r1];"),
+    "dm2_not_symmetrised": ("S[i * R + j] = dm2[i * R + j] + dm2[j * R + i];",
+                            "S[i * R + j] = 2.0 * dm2[i * R + j];"),
+    "dx_transposed_contraction": ("for (int64_t r = 0; r < R; ++r) acc += G[p * R + r] * Bt[r];",
+                                  "for (int64_t r = 0; r < R; ++r) acc += G[r * (P > R ? 0 : 1) + p * R] * Bt[r];"),
+    "moments_count_without_headdim": ("count[b] = v * P;", "count[b] = v;"),
+}
+
+PINS = [
+    lambda: ts.test_I1_chunked_forward_matches_recurrence(4),
+    ts.test_I2_scalar_case_is_a_first_order_iir_filter,
+    ts.test_golden_hand_worked_example,
+    lambda: ts.test_chunked_backward_matches_reverse_recurrence(4),
+    ts.test_I3_finite_differences_all_seven_gradients,
+    ts.test_I5_euler_identities,
+    tm.test_I6_explicit_sum_brute_force,
+    tm.test_I7_closed_form_matches,
+    tm.test_moments_finite_differences,
+    tm.test_golden_hand_worked_moments,
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    before, after = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(before) == 1, f"mutation anchor for {name} not unique"
+    mutant = tmp_path / "mutant.c"
+    mutant.write_text(src.replace(before, after))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-shared", "-fPIC", str(mutant), "-o", str(so), "-lm"],
+                   check=True)
+    prev = oracle.use_library(str(so))
+    caught = []
+    try:
+        for pin in PINS:
+            try:
+                pin()
+            except (AssertionError, RuntimeError):
+                caught.append(getattr(pin, "__name__", "pin"))
+    finally:
+        oracle.use_library(None)
+        oracle._lib = prev
+    assert caught, f"no pin caught the planted mistake {name}"
