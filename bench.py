@@ -1,0 +1,200 @@
+"""Benchmark: SSD forward + recompute backward on one MI355X.
+
+One step = ``ssd_fwd`` + ``ssd_bwd`` (K1-K5 forward, then the recompute
+backward) over one batch of the workload, inputs already resident in HBM.
+Prints ONE JSON line with tokens/s, the roofline of the dominant kernel
+(algorithmic work per launch / its mean duration, measured with HIP events on
+the launch stream during the timed region) and the CPU oracle timed on a
+bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload mamba2_130m_fp32]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD fwd+bwd tokens/s on 1 MI355X; % MFMA peak (GEMMs), % HBM BW (K1/K4)"
+PEAK_FP32_MFMA = 157.3e12   # FLOP/s, MI355X dense fp32 matrix
+PEAK_HBM = 8.0e12           # B/s
+
+
+def kernel_work(w, kernel: str):
+    """Algorithmic work of ONE launch of `kernel` for workload w: (amount, kind).
+
+    kind "flop": the products the kernel performs, causal triangle only
+    (pairs s <= t of a chunk); kind "byte": the HBM bytes the kernel must move."""
+    b, n, l, h, p, r = w.batch, w.nchunks, w.chunk_len, w.nheads, w.headdim, w.dstate
+    ch = b * n * h                      # chunk-heads
+    tok = ch * l                        # token-heads
+    pairs = l * (l + 1) // 2            # (t, s) pairs with s <= t per chunk
+    if kernel == "k_chunk_states":      # fwd: 1 job; bwd: 2 jobs (timed per launch: see jobs)
+        return 2 * l * p * r * ch, "flop"
+    if kernel == "k5_chunk_scan":
+        return (2 * l * p * r + 2 * pairs * r + 2 * pairs * p) * ch, "flop"
+    if kernel == "k_bwd_target":
+        return (2 * l * p * r + 2 * pairs * r + 2 * pairs * p + 2 * pairs * r) * ch, "flop"
+    if kernel == "k_bwd_source":
+        return (4 * l * p * r + 2 * pairs * r + 2 * pairs * p + 2 * pairs * p + 2 * pairs * r) * ch, "flop"
+    if kernel == "k1_cumsum":
+        return 12 * tok + 4 * h, "byte"
+    if kernel == "k4_state_pass":
+        return 8 * p * r * ch + 8 * ch + 8 * b * h * p * r, "byte"
+    if kernel == "k4_state_pass_bwd":
+        return 16 * p * r * ch + 8 * ch + 8 * b * h * p * r, "byte"
+    if kernel == "k1t_revcumsum":
+        return 24 * tok + 8 * ch, "byte"
+    return None, None
+
+
+def method_flops(w):
+    """Algorithmic fwd + bwd flops of the method per step (causal triangle only)."""
+    b, n, l, h, p, r = w.batch, w.nchunks, w.chunk_len, w.nheads, w.headdim, w.dstate
+    per_tok_fwd = (l + 1) * r + 4 * p * r + (l + 1) * p
+    per_tok_bwd = 3 * (l + 1) * r + 12 * p * r + 2 * (l + 1) * p
+    return (per_tok_fwd + per_tok_bwd) * b * n * l * h
+
+
+def cpu_baseline(w, inp, budget_s: float = 12.0, cap_s: float = 40.0):
+    """Time the oracle (single-threaded fp64 C) on (batch 0, head k) slices of the
+    workload until about `budget_s` of CPU work; scale to full tokens/s."""
+    import oracle
+    import torch
+    seq = w.seq
+    sl = 0
+    t_tot = 0.0
+    for k in range(w.nheads):
+        hs = [k]
+        x = inp["x"][:1, :, :, hs].double().numpy()
+        dy = inp["dy"][:1, :, :, hs].double().numpy()
+        B = inp["B"][:1, :, :, hs].double().numpy()
+        C = inp["C"][:1, :, :, hs].double().numpy()
+        dt = inp["dt"][:1, hs].double().numpy()
+        A = inp["A"][hs].double().numpy()
+        D = inp["D"][hs].double().numpy()
+        init = inp["init"][:1, hs].double().numpy()
+        t0 = time.perf_counter()
+        oracle.ssd_fwd(x, dt, A, B, C, D, init)
+        oracle.ssd_bwd(dy, None, x, dt, A, B, C, D, init)
+        t_tot += time.perf_counter() - t0
+        sl += 1
+        if t_tot >= budget_s or t_tot >= cap_s:
+            break
+    del torch
+    token_heads_per_s = sl * seq / t_tot
+    return {"value": token_heads_per_s / w.nheads, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"fwd+bwd of {sl} (batch 0, head) slice(s) x {seq} tokens of {w.name} "
+                      f"in {t_tot:.1f} s; tokens/s = token-heads/s / {w.nheads} heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba2_130m_fp32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the sequence/head sharding across GPUs is described, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mamba_ssd_chunked_amd import inputs, ssd
+
+    w = inputs.WORKLOADS[args.workload]
+    inp = inputs.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    d = {k: v.to(dev) for k, v in inp.items() if isinstance(v, torch.Tensor) and k != "valid_len"}
+    dims = ssd.dims_of(d["x"], d["B"])
+    init = d["init"] if w.init_std > 0 else None
+    y = torch.empty_like(d["x"])
+    final = torch.empty_like(d["d_final"])
+    gx, gB, gC = torch.empty_like(d["x"]), torch.empty_like(d["B"]), torch.empty_like(d["C"])
+    gdt, gA, gD = torch.empty_like(d["dt"]), torch.empty_like(d["A"]), torch.empty_like(d["D"])
+    ginit = torch.empty_like(d["d_final"])
+    ws_f = ssd.workspace(dims, ssd.SSD_OP_FWD, dev)
+    ws_b = ssd.workspace(dims, ssd.SSD_OP_BWD, dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        rc = ssd.ssd_fwd(dims, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], init, y, final,
+                         ws_f, stream)
+        if rc:
+            raise ssd.SsdError(rc, "ssd_fwd", ssd.ssd_last_error())
+        rc = ssd.ssd_bwd(dims, d["dy"], None, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
+                         init, gx, gdt, gA, gB, gC, gD, ginit, ws_b, stream)
+        if rc:
+            raise ssd.SsdError(rc, "ssd_bwd", ssd.ssd_last_error())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ssd.ssd_timing_enable(True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ssd.ssd_timing_enable(False)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    kt = ssd.ssd_timing_collect()
+    tokens = w.batch * w.seq
+    value = tokens / (ms / 1e3)
+
+    kernels = {}
+    for name, (tot, cnt) in kt.items():
+        avg = tot / cnt
+        work, kind = kernel_work(w, name)
+        ent = {"avg_ms": round(avg, 5), "launches_per_step": cnt / args.steps}
+        if name == "k_chunk_states":
+            # launched once in ssd_fwd (1 job) and once in ssd_bwd (2 jobs): average work
+            work = work * 1.5
+        if work is not None:
+            rate = work / (avg / 1e3)
+            if kind == "flop":
+                ent.update(tflops=round(rate / 1e12, 2), mfma_frac=round(rate / PEAK_FP32_MFMA, 4))
+            else:
+                ent.update(gbps=round(rate / 1e9, 1), hbm_frac=round(rate / PEAK_HBM, 4))
+        kernels[name] = ent
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches_per_step"])
+    work, kind = kernel_work(w, dom)
+    davg = kernels[dom]["avg_ms"]
+    if kind == "flop":
+        ach = work / (davg / 1e3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 3), "peak": 157.3,
+                "unit": "TFLOP/s", "frac": round(ach / 157.3, 4), "traffic": None}
+    else:
+        ach = work / (davg / 1e3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": 8000.0,
+                "unit": "GB/s", "frac": round(ach / 8000.0, 4), "traffic": None}
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.io == "bf16" else "f32",
+        "data": "synthetic (seeded draws of the workload recipe; no dataset)",
+        "config": w.describe(),
+        "roofline": roof,
+        "method_tflops": round(method_flops(w) / (ms / 1e3) / 1e12, 3),
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

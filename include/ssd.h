@@ -1,0 +1,168 @@
+/*
+ * mamba_ssd_chunked_amd -- C ABI of the Mamba-2 SSD chunked scan for MI355X (gfx950).
+ *
+ * The operation is the selective state-space scan of Mamba-2, computed chunk by
+ * chunk as in the burn-mamba page "mamba2/ssd/serial_recalculated/
+ * combined_backward.rs":
+ *
+ *   h_t = exp(dt_t * A_h) * h_{t-1} + dt_t * x_t (outer) B_t,
+ *   y_t = C_t . h_t + D_h * x_t,          h_{-1} = initial_state,
+ *
+ * where the chunked form runs K1 (inclusive per-chunk cumsum of dt*A),
+ * K2 (C B^T inside a chunk), K3 (chunk-end states), K4 (serial state passing
+ * across chunks) and K5 (chunk-scan output plus the D skip).  The backward is
+ * that page's recompute backward: it takes the seven leaf inputs again,
+ * recomputes K1-K4 and returns the gradients of every input (the page's
+ * CombinedGrads).  The state moments are the StateMoments of the burn-mamba
+ * page "modules/state_moments.rs"; their backward follows the per-token
+ * cotangent of the burn-mamba "mamba3/moments/backward" module page with no
+ * rotation.
+ *
+ * Tensor layouts (row-major, contiguous; b batch, n nchunks, l chunk_len,
+ * h nheads, p headdim, r dstate; the pages' naming):
+ *   x, dy, y, d_x          [b, n, l, h, p]   io dtype
+ *   B, C, d_B, d_C         [b, n, l, h, r]   io dtype (one B/C per head, no groups)
+ *   dt, d_dt               [b, h, n, l]      fp32 (the discretised step; no softplus here)
+ *   A, D, d_A, d_D         [h]               fp32 (A is used as is: dA = dt * A)
+ *   init, final, d_final,
+ *   d_init                 [b, h, p, r]      fp32
+ *   m2 / m1                [b, h, r, r] / [b, h, r]   fp32
+ *   valid_len, count       [b]               int64, HOST memory
+ * io dtype SSD_F32: everything fp32.  SSD_BF16: x, B, C, dy, y, d_x, d_B, d_C
+ * are bfloat16 (results rounded to nearest even); everything else stays fp32.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers on the current HIP device, except
+ *    valid_len and count (host).  The caller owns every buffer, including the
+ *    workspace sized by ssd_workspace_size(); the library never allocates,
+ *    frees or synchronises, and enqueues all work on `stream` (a hipStream_t;
+ *    NULL = the default stream).
+ *  - Outputs are overwritten, never accumulated.  Inputs are not modified.
+ *  - Supported shapes: chunk_len in {64, 128, 256}; headdim and dstate in
+ *    {16, 32, 64, 128}; batch >= 0, nchunks >= 0 (an empty sequence is valid:
+ *    final = init, d_init = d_final, d_A = d_D = 0).  Tensor pointers must be
+ *    16-byte aligned (8-byte for bf16 tensors).
+ *  - Results are bitwise reproducible for equal inputs (no float atomics).
+ *  - Every call validates all arguments before it enqueues anything.  Return 0
+ *    on success or one of the ssd_status codes; ssd_last_error() then gives a
+ *    message (thread-local, valid until the next call on the thread).
+ */
+#ifndef MAMBA_SSD_CHUNKED_AMD_SSD_H
+#define MAMBA_SSD_CHUNKED_AMD_SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ssd_dims {
+    int64_t batch;     /* b */
+    int64_t nchunks;   /* n: sequence length = nchunks * chunk_len */
+    int64_t chunk_len; /* l */
+    int64_t nheads;    /* h */
+    int64_t headdim;   /* p (per_head_dim) */
+    int64_t dstate;    /* r (state_rank) */
+    int32_t io_dtype;  /* SSD_F32 or SSD_BF16 */
+    int32_t reserved;  /* must be 0 */
+} ssd_dims;
+
+enum ssd_io_dtype { SSD_F32 = 0, SSD_BF16 = 1 };
+
+enum ssd_status {
+    SSD_OK = 0,
+    SSD_ERR_NULL = 1,        /* a required pointer is NULL */
+    SSD_ERR_SHAPE = 2,       /* a dimension is negative / zero where not allowed, or valid_len out of range */
+    SSD_ERR_UNSUPPORTED = 3, /* shape or alignment outside the supported set above */
+    SSD_ERR_DTYPE = 4,       /* io_dtype not SSD_F32 / SSD_BF16, or reserved != 0 */
+    SSD_ERR_WORKSPACE = 5,   /* ws_bytes smaller than ssd_workspace_size(), or ws NULL */
+    SSD_ERR_HIP = 6          /* a HIP launch failed (message names the kernel) */
+};
+
+enum ssd_op { SSD_OP_FWD = 0, SSD_OP_BWD = 1, SSD_OP_MOMENTS = 2, SSD_OP_MOMENTS_BWD = 3 };
+
+/*
+ * Workspace bytes that entry point `op` needs for `dims` (written to *bytes,
+ * host).  The value depends only on dims and op.  0 is a valid answer.
+ */
+int ssd_workspace_size(const ssd_dims* dims, int op, size_t* bytes);
+
+/*
+ * Forward (combined_backward.rs page: K1, K2, K3, K4, K5 with the SKIP term).
+ *   y           [b,n,l,h,p] out, io dtype
+ *   final_state [b,h,p,r]   out, fp32, nullable (not written when NULL)
+ *   init        [b,h,p,r]   in, nullable (NULL = zero initial state)
+ * Nothing is saved for the backward: ssd_bwd recomputes from the leaves.
+ */
+int ssd_fwd(const ssd_dims* dims, const void* x, const float* dt, const float* A,
+            const void* B, const void* C, const float* D, const float* init,
+            void* y, float* final_state, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Recompute backward (combined_backward.rs page: recompute K1-K4, SKIP
+ * backward, BLUE/ORANGE and K4 backward, K3/K2/K1 backward, combine).
+ *   dy       [b,n,l,h,p] in, io dtype: gradient of y
+ *   d_final  [b,h,p,r]   in, nullable (NULL = zero): gradient of final_state
+ *   x, dt, A, B, C, D, init: the forward's leaves (init nullable = zero)
+ *   d_x, d_B, d_C (io dtype), d_dt, d_A, d_D (fp32): out, all required
+ *   d_init   [b,h,p,r]   out, nullable (not written when NULL)
+ * d_A and d_D are summed over batch (their parameters are shared by batch).
+ */
+int ssd_bwd(const ssd_dims* dims, const void* dy, const float* d_final, const void* x,
+            const float* dt, const float* A, const void* B, const void* C, const float* D,
+            const float* init, void* d_x, float* d_dt, float* d_A, void* d_B, void* d_C,
+            float* d_D, float* d_init, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Pooled state moments (state_moments.rs page, StateMoments): over the tokens
+ * t < valid_len[b] of each (b, h), with h_t the state after token t,
+ *   m2[b,h] = sum_t h_t^T h_t   [r,r]     m1[b,h] = sum_t sum_p h_t[p,:]   [r]
+ *   count[b] = valid_len[b] * headdim  (host, int64)
+ * valid_len (host int64 [b]) is nullable (NULL = full sequence); each entry
+ * must lie in [0, nchunks * chunk_len].  valid_len masks only the moments.
+ * Optionally also runs the forward: y (with C and D) and final_state are
+ * nullable; y requires C and D.
+ */
+int ssd_state_moments(const ssd_dims* dims, const void* x, const float* dt, const float* A,
+                      const void* B, const float* init, const int64_t* valid_len,
+                      float* m2, float* m1, int64_t* count, void* y, const void* C,
+                      const float* D, float* final_state, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/*
+ * Backward of <d_m2, m2> + <d_m1, m1> (moments/backward module page with the
+ * rotation equal to the identity): per token t < valid_len[b] the state
+ * receives the cotangent h_t (d_m2 + d_m2^T) + 1_p (outer) d_m1.
+ *   d_m2 [b,h,r,r] in (need not be symmetric); d_m1 [b,h,r] in, nullable (= 0)
+ *   d_x, d_B (io dtype), d_dt, d_A (fp32): out; d_init out, nullable
+ * Tokens at or past valid_len get exactly zero gradient.
+ */
+int ssd_state_moments_bwd(const ssd_dims* dims, const float* d_m2, const float* d_m1,
+                          const void* x, const float* dt, const float* A, const void* B,
+                          const float* init, const int64_t* valid_len, void* d_x,
+                          float* d_dt, float* d_A, void* d_B, float* d_init, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Message for the last nonzero status returned on this thread ("" if none). */
+const char* ssd_last_error(void);
+
+/*
+ * Benchmark instrumentation (not part of the computation).  While enabled, every
+ * kernel an entry point enqueues is bracketed by two HIP events recorded on the
+ * caller's stream.  ssd_timing_collect() waits for the recorded events (a host
+ * synchronisation), then writes per kernel name (NUL-terminated, at most
+ * name_stride bytes each, into names[k * name_stride]) the summed elapsed
+ * milliseconds and the number of launches, for up to max_kernels names, sets
+ * *n_kernels to the number of distinct names and clears the records.  Returns 0
+ * or SSD_ERR_NULL / SSD_ERR_HIP.
+ */
+int ssd_timing_enable(int on);
+int ssd_timing_collect(int max_kernels, char* names, size_t name_stride, double* total_ms,
+                       int64_t* launches, int* n_kernels);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SSD_CHUNKED_AMD_SSD_H */

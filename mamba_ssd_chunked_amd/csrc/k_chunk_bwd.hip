@@ -1,0 +1,454 @@
+// Chunk-parallel MFMA kernels of the recompute backward.
+//
+// Page: burn-mamba "mamba2/ssd/serial_recalculated/combined_backward.rs".  The
+// page runs one reverse loop over chunks that mixes the K5 backward (BLUE and
+// ORANGE) with the K4 backward step, then batched K3/K2/K1 backwards.  Only the
+// K4 carry is serial, and the quantity it consumes from each chunk (the BLUE
+// "d_chunk_input_state = C^T d_ch") is chunk-local, so here the work is split
+// into: a chunk-parallel pass for d_chunk_input_state (k_chunk_states, job 1),
+// the serial carry (k4_state_pass_bwd), and the two chunk-parallel kernels of
+// this file, which consume the carried gradient d_intra of every chunk.
+//
+// With e_t = exp(cum[t]), decay(t,s) = exp(cum[t] - cum[s]) for s <= t,
+// CB = C B^T, W = CB * decay * dt[s], d_w = dy x^T (kept for s <= t),
+// d_CB = d_w * dt[s] * decay and d_diff = d_CB * CB (ORANGE backward), and
+// b_scaled = B * bbar with bbar = dt * exp(end - cum) (K3):
+//
+//   target side, rows t (bwd_target):
+//     d_C[t]     = e_t dy[t] S_in              (BLUE backward, d_C_blue)
+//                + sum_{s<=t} d_CB[t,s] B[s]    (K2 backward, d_c = d_cb B)
+//     g1[t]      = sum_r C[t,r] d_C_blue[t,r]   (BLUE d_da)
+//                + sum_{s<=t} d_diff[t,s]        (ORANGE d_da, target side)
+//     d_end      = exp(end) <d_intra, S_in>      (K4 backward, d_da_chunk_end)
+//   source side, rows s (bwd_source):
+//     d_x[s]     = D dy[s]                                   (SKIP backward)
+//                + sum_{t>=s} W[t,s] dy[t]                    (ORANGE, d_x = w^T d_orange)
+//                + bbar[s] d_intra B[s]^T                     (K3, d_x = d_intra b_scaled^T)
+//     d_B[s]     = sum_{t>=s} d_CB[t,s] C[t]                  (K2, d_b = d_cb^T c)
+//                + bbar[s] x[s] d_intra                       (K3, d_b = d_b_scaled bbar)
+//     d_dt[s]    = sum_{t>=s} d_w CB decay                    (ORANGE d_dt)
+//                + d_bbar[s] exp(end - cum[s])                (K3 d_dt), d_bbar = <x[s] d_intra, B[s]>
+//     g2[s]      = -sum_{t>=s} d_diff[t,s]                    (ORANGE d_da, source side)
+//     d_delta[s] = d_bbar[s] dt[s] exp(end - cum[s])          (K3: gradient of end - cum[s])
+//     dD_part    = sum dy x                                   (SKIP, d_D)
+// k1t_revcumsum then turns g1 + g2, d_delta and d_end into d_cum's suffix sum
+// (for d_dt).
+//
+// d_A is NOT formed as sum_t d_da[t] dt[t]: the suffix sums of rowsum - colsum
+// cancel the large near-diagonal ORANGE terms, which costs d_A ~1e-5 relative
+// accuracy in fp32.  Summing each term against the dt it depends on gives the
+// same value exactly (cumA = A cdt with cdt the cumsum of dt):
+//   d_A = sum_pairs d_diff[t,s] (cdt[t] - cdt[s]) + sum_t blue[t] cdt[t]
+//       + sum_s d_delta[s] (cdt[L-1] - cdt[s]) + d_end cdt[L-1]
+// per chunk, where near-diagonal pairs get small weights instead of cancelling.
+// The target side writes the first two sums (plus the d_end term), the source
+// side the third; reduce_heads adds them per head.
+//
+// Layout trick (no LDS transposes): every 16x16 product tile is computed with
+// its M index along the rows the NEXT product contracts over, so the four MFMA
+// result registers of a lane (M = 4g+v, N = i) are exactly the B operand the
+// next MFMA needs.  The target side therefore accumulates d_C^T tiles
+// (M = r, N = t) and the source side d_x^T / d_B^T tiles (M = p or r, N = s);
+// each lane finally stores four consecutive features of one token.
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+template <class IO, int P, int R>
+__global__ __launch_bounds__(NT) void k_bwd_target(
+    const typename IO::T* __restrict__ dy, const typename IO::T* __restrict__ x,
+    const float* __restrict__ dt, const typename IO::T* __restrict__ Bm,
+    const typename IO::T* __restrict__ Cm, const float* __restrict__ Av,
+    const double* __restrict__ cdt, const float* __restrict__ S, const float* __restrict__ dS,
+    typename IO::T* __restrict__ dC, float* __restrict__ g1, float* __restrict__ d_end,
+    double* __restrict__ dA_T, int N, int H, int L, int64_t CH) {
+    constexpr int RS = R + 4, PS = P + 4;
+    constexpr int ROWS = P > TB ? P : TB;
+    __shared__ float sBS[ROWS * RS];  // S_in [P, R], then B of the source block
+    __shared__ float sX[TB * PS];
+    __shared__ double sCdtT[TB], sCdtS[TB];
+    __shared__ float sDt[TB];
+    __shared__ double sRed[NT / 64];
+    const int nblk = L / TB;
+    const int tb = nblk - 1 - static_cast<int>(blockIdx.x / CH);  // heaviest first
+    const ChunkHead c = decode_ch(blockIdx.x % CH, N, H);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    const int64_t xrow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(P);
+    const int64_t xstride = static_cast<int64_t>(H) * P;
+    const int64_t brow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(R);
+    const int64_t bstride = static_cast<int64_t>(H) * R;
+    const double* cc = cdt + c.c_bhn * L;
+    const float* dtc = dt + c.c_bhn * L;
+    const double a = static_cast<double>(Av[c.h]);
+    const int tl = 16 * wave + i;  // target row of this lane inside the block
+
+    v4f creg[R / 16], dyreg[P / 16];
+    {
+        const int64_t crow = brow0 + static_cast<int64_t>(tb * TB + tl) * bstride;
+#pragma unroll
+        for (int kk = 0; kk < R / 16; ++kk) creg[kk] = io<IO>::ld4(Cm, crow + 16 * kk + 4 * g);
+        const int64_t yrow = xrow0 + static_cast<int64_t>(tb * TB + tl) * xstride;
+#pragma unroll
+        for (int kk = 0; kk < P / 16; ++kk) dyreg[kk] = io<IO>::ld4(dy, yrow + 16 * kk + 4 * g);
+    }
+    stage_mat<R>(sBS, S + c.ch * (P * R), P);
+    if (tid < TB) sCdtT[tid] = cc[tb * TB + tid];
+    __syncthreads();
+
+    double dA = 0.0;  // this thread's part of the chunk's d_A (see the file header)
+    // K4 backward: d_end = exp(A cdt[L-1]) <d_intra, S_in>, once per chunk (block 0).
+    if (tb == 0) {
+        const float* dsp = dS + c.ch * (P * R);
+        double part = 0.0;
+        for (int idx = tid; idx < P * (R / 4); idx += NT) {
+            const int row = idx / (R / 4), c4 = idx - (idx / (R / 4)) * (R / 4);
+            const v4f u = *reinterpret_cast<const v4f*>(dsp + row * R + c4 * 4);
+            const v4f w = *reinterpret_cast<const v4f*>(sBS + row * RS + c4 * 4);
+            part += static_cast<double>(u[0] * w[0] + u[1] * w[1]) +
+                    static_cast<double>(u[2] * w[2] + u[3] * w[3]);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+        if (lane == 0) sRed[wave] = part;
+        __syncthreads();
+        if (tid == 0) {
+            const double end = cc[L - 1];
+            const double de = (sRed[0] + sRed[1] + sRed[2] + sRed[3]) * exp(a * end);
+            const float def = static_cast<float>(de);
+            d_end[c.c_bhn] = def;
+            dA += static_cast<double>(def) * end;
+        }
+    }
+
+    // BLUE: d_C^T[r, t] = e_t sum_p S_in[p, r] dy[t, p]
+    v4f acc[R / 16];
+#pragma unroll
+    for (int rt = 0; rt < R / 16; ++rt) acc[rt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < P / 16; ++kk) {
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                acc[rt] = mfma16(sBS[(16 * kk + 4 * g + v) * RS + rt * 16 + i], dyreg[kk][v], acc[rt]);
+        }
+    }
+    const double ct = sCdtT[tl];
+    const float et = expf(static_cast<float>(a * ct));
+    float gsum = 0.0f;  // this lane's part of g1[t = tl]
+#pragma unroll
+    for (int rt = 0; rt < R / 16; ++rt) {
+        acc[rt] *= et;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) gsum += creg[rt][v] * acc[rt][v];
+    }
+    dA += static_cast<double>(gsum) * ct;
+
+    for (int sb = 0; sb <= tb; ++sb) {
+        __syncthreads();
+        stage_rows<IO, R>(sBS, Bm + brow0 + static_cast<int64_t>(sb * TB) * bstride, bstride);
+        stage_rows<IO, P>(sX, x + xrow0 + static_cast<int64_t>(sb * TB) * xstride, xstride);
+        if (tid < TB) {
+            sCdtS[tid] = cc[sb * TB + tid];
+            sDt[tid] = dtc[sb * TB + tid];
+        }
+        __syncthreads();
+        const int jmax = (sb == tb) ? wave : 3;
+        for (int j = 0; j <= jmax; ++j) {
+            // tiles with M = s (16j + 4g + v), N = t (tl)
+            v4f cbt = zero4(), dwt = zero4();
+#pragma unroll
+            for (int kk = 0; kk < R / 16; ++kk) {
+                const v4f u = *reinterpret_cast<const v4f*>(sBS + (16 * j + i) * RS + 16 * kk + 4 * g);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) cbt = mfma16(u[v], creg[kk][v], cbt);
+            }
+#pragma unroll
+            for (int kk = 0; kk < P / 16; ++kk) {
+                const v4f u = *reinterpret_cast<const v4f*>(sX + (16 * j + i) * PS + 16 * kk + 4 * g);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) dwt = mfma16(u[v], dyreg[kk][v], dwt);
+            }
+            float dcb[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int s_ = 16 * j + 4 * g + v;
+                const bool keep = (sb < tb) || (s_ <= tl);
+                const double gap = ct - sCdtS[s_];
+                const float dec = keep ? expf(static_cast<float>(a * gap)) : 0.0f;
+                dcb[v] = dwt[v] * sDt[s_] * dec;
+                const float ddiff = dcb[v] * cbt[v];
+                gsum += ddiff;
+                dA += static_cast<double>(ddiff) * gap;
+            }
+            // K2 backward: d_C^T[r, t] += sum_s B[s, r] d_CB[t, s]
+#pragma unroll
+            for (int rt = 0; rt < R / 16; ++rt) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[rt] = mfma16(sBS[(16 * j + 4 * g + v) * RS + rt * 16 + i], dcb[v], acc[rt]);
+            }
+        }
+    }
+    // store d_C[t = tl][r = 16 rt + 4g .. +3]
+    {
+        const int64_t row = brow0 + static_cast<int64_t>(tb * TB + tl) * bstride;
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt) io<IO>::st4(dC, row + rt * 16 + 4 * g, acc[rt]);
+    }
+    gsum = sum_over_g(gsum);
+    if (g == 0) g1[c.c_bhn * L + tb * TB + tl] = gsum;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dA += __shfl_xor(dA, off);
+    __syncthreads();
+    if (lane == 0) sRed[wave] = dA;
+    __syncthreads();
+    if (tid == 0) dA_T[c.ch * nblk + tb] = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+}
+
+template <class IO, int P, int R>
+__global__ __launch_bounds__(NT) void k_bwd_source(
+    const typename IO::T* __restrict__ dy, const typename IO::T* __restrict__ x,
+    const float* __restrict__ dt, const typename IO::T* __restrict__ Bm,
+    const typename IO::T* __restrict__ Cm, const float* __restrict__ Av,
+    const float* __restrict__ Dv, const double* __restrict__ cdt, const float* __restrict__ dS,
+    typename IO::T* __restrict__ dx, typename IO::T* __restrict__ dB, float* __restrict__ d_dt,
+    float* __restrict__ g2, float* __restrict__ d_delta, double* __restrict__ dA_S,
+    double* __restrict__ dD_part, int N, int H, int L, int64_t CH) {
+    constexpr int RS = R + 4, PS = P + 4;
+    constexpr int ROWS = P > TB ? P : TB;
+    __shared__ float sCT[ROWS * RS];  // d_intra [P, R], then C of the target block
+    __shared__ float sDY[TB * PS];
+    __shared__ double sCdtT[TB];
+    __shared__ double sRed[2 * (NT / 64)];
+    const int nblk = L / TB;
+    const int sb = static_cast<int>(blockIdx.x / CH);  // block 0 has the most targets
+    const ChunkHead c = decode_ch(blockIdx.x % CH, N, H);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    const int64_t xrow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(P);
+    const int64_t xstride = static_cast<int64_t>(H) * P;
+    const int64_t brow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(R);
+    const int64_t bstride = static_cast<int64_t>(H) * R;
+    const double* cc = cdt + c.c_bhn * L;
+    const float* dtc = dt + c.c_bhn * L;
+    const double a = static_cast<double>(Av[c.h]);
+    const int sl = 16 * wave + i;   // source row of this lane inside the block
+    const int spos = sb * TB + sl;  // ... inside the chunk
+
+    v4f xreg[P / 16], breg[R / 16];
+    const int64_t xrow = xrow0 + static_cast<int64_t>(spos) * xstride;
+    const int64_t brow = brow0 + static_cast<int64_t>(spos) * bstride;
+#pragma unroll
+    for (int kk = 0; kk < P / 16; ++kk) xreg[kk] = io<IO>::ld4(x, xrow + 16 * kk + 4 * g);
+#pragma unroll
+    for (int kk = 0; kk < R / 16; ++kk) breg[kk] = io<IO>::ld4(Bm, brow + 16 * kk + 4 * g);
+    stage_mat<R>(sCT, dS + c.ch * (P * R), P);
+    const double end = cc[L - 1];
+    const double cs = cc[spos];
+    const float dts = dtc[spos];
+    const float dec_end = expf(static_cast<float>(a * (end - cs)));
+    const float bbar = dts * dec_end;
+    __syncthreads();
+
+    // K3 backward.  d_b_scaled^T[r, s] = sum_p d_intra[p, r] x[s, p]
+    v4f accB[R / 16];
+#pragma unroll
+    for (int rt = 0; rt < R / 16; ++rt) accB[rt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < P / 16; ++kk) {
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                accB[rt] = mfma16(sCT[(16 * kk + 4 * g + v) * RS + rt * 16 + i], xreg[kk][v], accB[rt]);
+        }
+    }
+    float dbb = 0.0f;  // d_bbar[s] = sum_r d_b_scaled[s, r] B[s, r] (this lane's part)
+#pragma unroll
+    for (int rt = 0; rt < R / 16; ++rt) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dbb += accB[rt][v] * breg[rt][v];
+        accB[rt] *= bbar;
+    }
+    // d_x^T[p, s] = bbar[s] sum_r d_intra[p, r] B[s, r]
+    v4f accX[P / 16];
+#pragma unroll
+    for (int pt = 0; pt < P / 16; ++pt) accX[pt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < R / 16; ++kk) {
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt) {
+            const v4f u = *reinterpret_cast<const v4f*>(sCT + (pt * 16 + i) * RS + 16 * kk + 4 * g);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) accX[pt] = mfma16(u[v], breg[kk][v], accX[pt]);
+        }
+    }
+    // SKIP backward: d_x += D dy; d_D partial sum dy x
+    const float Dh = Dv[c.h];
+    double dD = 0.0;
+#pragma unroll
+    for (int pt = 0; pt < P / 16; ++pt) {
+        const v4f dyv = io<IO>::ld4(dy, xrow + pt * 16 + 4 * g);
+        accX[pt] = accX[pt] * bbar + Dh * dyv;
+        dD += static_cast<double>(dyv[0] * xreg[pt][0] + dyv[1] * xreg[pt][1]) +
+              static_cast<double>(dyv[2] * xreg[pt][2] + dyv[3] * xreg[pt][3]);
+    }
+
+    float ddt_or = 0.0f, dsrc = 0.0f;
+    for (int tb = sb; tb < nblk; ++tb) {
+        __syncthreads();
+        stage_rows<IO, R>(sCT, Cm + brow0 + static_cast<int64_t>(tb * TB) * bstride, bstride);
+        stage_rows<IO, P>(sDY, dy + xrow0 + static_cast<int64_t>(tb * TB) * xstride, xstride);
+        if (tid < TB) sCdtT[tid] = cc[tb * TB + tid];
+        __syncthreads();
+        const int jmin = (tb == sb) ? wave : 0;
+        for (int j = jmin; j < 4; ++j) {
+            // tiles with M = t (16j + 4g + v), N = s (sl)
+            v4f cb = zero4(), dw = zero4();
+#pragma unroll
+            for (int kk = 0; kk < R / 16; ++kk) {
+                const v4f u = *reinterpret_cast<const v4f*>(sCT + (16 * j + i) * RS + 16 * kk + 4 * g);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) cb = mfma16(u[v], breg[kk][v], cb);
+            }
+#pragma unroll
+            for (int kk = 0; kk < P / 16; ++kk) {
+                const v4f u = *reinterpret_cast<const v4f*>(sDY + (16 * j + i) * PS + 16 * kk + 4 * g);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) dw = mfma16(u[v], xreg[kk][v], dw);
+            }
+            float wv[4], dcb[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = 16 * j + 4 * g + v;
+                const bool keep = (tb > sb) || (t >= sl);
+                const float dec = keep ? expf(static_cast<float>(a * (sCdtT[t] - cs))) : 0.0f;
+                const float cbd = cb[v] * dec;
+                wv[v] = cbd * dts;
+                dcb[v] = dw[v] * dts * dec;
+                ddt_or += dw[v] * cbd;
+                dsrc += dcb[v] * cb[v];
+            }
+            // ORANGE: d_x^T[p, s] += sum_t dy[t, p] W[t, s]
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    accX[pt] = mfma16(sDY[(16 * j + 4 * g + v) * PS + pt * 16 + i], wv[v], accX[pt]);
+            }
+            // K2 backward: d_B^T[r, s] += sum_t C[t, r] d_CB[t, s]
+#pragma unroll
+            for (int rt = 0; rt < R / 16; ++rt) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    accB[rt] = mfma16(sCT[(16 * j + 4 * g + v) * RS + rt * 16 + i], dcb[v], accB[rt]);
+            }
+        }
+    }
+#pragma unroll
+    for (int pt = 0; pt < P / 16; ++pt) io<IO>::st4(dx, xrow + pt * 16 + 4 * g, accX[pt]);
+#pragma unroll
+    for (int rt = 0; rt < R / 16; ++rt) io<IO>::st4(dB, brow + rt * 16 + 4 * g, accB[rt]);
+
+    dbb = sum_over_g(dbb);
+    ddt_or = sum_over_g(ddt_or);
+    dsrc = sum_over_g(dsrc);
+    double dA = 0.0;
+    if (g == 0) {
+        const int64_t o = c.c_bhn * L + spos;
+        const float dl = dbb * dts * dec_end;
+        d_dt[o] = ddt_or + dbb * dec_end;
+        g2[o] = -dsrc;
+        d_delta[o] = dl;
+        dA = static_cast<double>(dl) * (end - cs);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        dD += __shfl_xor(dD, off);
+        dA += __shfl_xor(dA, off);
+    }
+    if (lane == 0) {
+        sRed[wave] = dD;
+        sRed[4 + wave] = dA;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        dD_part[c.ch * nblk + sb] = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+        dA_S[c.ch * nblk + sb] = sRed[4] + sRed[5] + sRed[6] + sRed[7];
+    }
+}
+
+// ------------------------------------------------------------------ dispatch
+#define SSD_FOR_EACH_PR(X) \
+    X(16, 16) X(16, 32) X(16, 64) X(16, 128) \
+    X(32, 16) X(32, 32) X(32, 64) X(32, 128) \
+    X(64, 16) X(64, 32) X(64, 64) X(64, 128) \
+    X(128, 16) X(128, 32) X(128, 64) X(128, 128)
+
+template <class IO>
+static hipError_t target_io(const Shape& s, const void* dy, const void* x, const float* dt,
+                            const void* Bm, const void* Cm, const float* A, const double* cdt,
+                            const float* S, const float* dS, void* dC, float* g1, float* d_end,
+                            double* dA_T, hipStream_t st) {
+    using T = typename IO::T;
+    const int64_t CH = static_cast<int64_t>(s.B) * s.N * s.H;
+    if (CH == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(CH * s.nblk()));
+#define X(PP, RR)                                                                                \
+    if (s.P == PP && s.R == RR) {                                                                \
+        hipLaunchKernelGGL((k_bwd_target<IO, PP, RR>), grid, dim3(NT), 0, st,                   \
+                           static_cast<const T*>(dy), static_cast<const T*>(x), dt,              \
+                           static_cast<const T*>(Bm), static_cast<const T*>(Cm), A, cdt, S, dS,  \
+                           static_cast<T*>(dC), g1, d_end, dA_T, s.N, s.H, s.L, CH);             \
+        return hipGetLastError();                                                                \
+    }
+    SSD_FOR_EACH_PR(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_target(const Shape& s, const void* dy, const void* x, const float* dt,
+                             const void* Bm, const void* Cm, const float* A, const double* cdt,
+                             const float* S, const float* dS, void* dC, float* g1, float* d_end,
+                             double* dA_T, hipStream_t st) {
+    return s.io == 1 ? target_io<BF16>(s, dy, x, dt, Bm, Cm, A, cdt, S, dS, dC, g1, d_end, dA_T, st)
+                     : target_io<F32>(s, dy, x, dt, Bm, Cm, A, cdt, S, dS, dC, g1, d_end, dA_T, st);
+}
+
+template <class IO>
+static hipError_t source_io(const Shape& s, const void* dy, const void* x, const float* dt,
+                            const void* Bm, const void* Cm, const float* A, const float* D,
+                            const double* cdt, const float* dS, void* dx, void* dB, float* d_dt,
+                            float* g2, float* d_delta, double* dA_S, double* dD_part,
+                            hipStream_t st) {
+    using T = typename IO::T;
+    const int64_t CH = static_cast<int64_t>(s.B) * s.N * s.H;
+    if (CH == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(CH * s.nblk()));
+#define X(PP, RR)                                                                                 \
+    if (s.P == PP && s.R == RR) {                                                                 \
+        hipLaunchKernelGGL((k_bwd_source<IO, PP, RR>), grid, dim3(NT), 0, st,                    \
+                           static_cast<const T*>(dy), static_cast<const T*>(x), dt,               \
+                           static_cast<const T*>(Bm), static_cast<const T*>(Cm), A, D, cdt, dS,   \
+                           static_cast<T*>(dx), static_cast<T*>(dB), d_dt, g2, d_delta, dA_S,     \
+                           dD_part, s.N, s.H, s.L, CH);                                           \
+        return hipGetLastError();                                                                 \
+    }
+    SSD_FOR_EACH_PR(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_source(const Shape& s, const void* dy, const void* x, const float* dt,
+                             const void* Bm, const void* Cm, const float* A, const float* D,
+                             const double* cdt, const float* dS, void* dx, void* dB, float* d_dt,
+                             float* g2, float* d_delta, double* dA_S, double* dD_part,
+                             hipStream_t st) {
+    return s.io == 1 ? source_io<BF16>(s, dy, x, dt, Bm, Cm, A, D, cdt, dS, dx, dB, d_dt, g2,
+                                       d_delta, dA_S, dD_part, st)
+                     : source_io<F32>(s, dy, x, dt, Bm, Cm, A, D, cdt, dS, dx, dB, d_dt, g2,
+                                      d_delta, dA_S, dD_part, st);
+}
+
+}  // namespace ssd

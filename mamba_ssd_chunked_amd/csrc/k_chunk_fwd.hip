@@ -1,0 +1,278 @@
+// Chunk-parallel MFMA kernels of the forward: K3 (chunk states) and K5 (chunk
+// scan with K2 fused in, plus the D skip).  The backward reuses the K3 kernel
+// for its BLUE state gradient (the same contraction with dy, C and exp(cum)).
+//
+// Page: burn-mamba "mamba2/ssd/serial_recalculated/combined_backward.rs".
+//  - K3 (k3_ssd_chunk_state_extended): intra[p,r] = sum_t x[t,p] * b_scaled[t,r]
+//    with b_scaled = B * dt * exp(cumA_last - cumA).
+//  cumA is formed as A * cdt with cdt the fp64 cumsum of dt (K1).
+//  - K5 is defined there by its backward: y = BLUE + ORANGE + D x with
+//    BLUE[t,p]   = exp(cumA[t]) sum_r C[t,r] state[p,r]   (the chunk-entry state)
+//    ORANGE[t,p] = sum_{s<=t} CB[t,s] exp(cumA[t] - cumA[s]) dt[s] x[s,p],
+//    CB = C B^T (K2), the mask keeping s <= t (diagonal included).
+//  - The backward's "d_chunk_input_state = C^T d_ch" with d_ch = dy * exp(cumA)
+//    (BLUE backward) is job 1 of the state kernel.
+// The [l, l] CB and decay matrices never leave the chip: K5 builds each 16x16
+// tile of CB^T with MFMA, scales it in registers and feeds it straight back to
+// the next MFMA as its A operand.
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+// ------------------------------------------------------------------ K3 / dS
+// One workgroup per (chunk-head, job).  Output [P, R] is split into 16x16 tiles
+// dealt round-robin to the 4 waves; K (tokens) runs over 64-token blocks staged
+// through LDS (U rows as is, V rows pre-scaled by the token weight).
+template <class IO, int P, int R>
+__global__ __launch_bounds__(NT) void k_chunk_states(
+    const typename IO::T* __restrict__ x, const typename IO::T* __restrict__ Bm,
+    const typename IO::T* __restrict__ dy, const typename IO::T* __restrict__ Cm,
+    const float* __restrict__ dt, const float* __restrict__ Av, const double* __restrict__ cdt,
+    float* __restrict__ S, float* __restrict__ dS, int N, int H, int L, int job0) {
+    __shared__ float sU[TB * (P + 4)];
+    __shared__ float sV[TB * (R + 4)];
+    __shared__ float sw[TB];
+    const int job = job0 + static_cast<int>(blockIdx.y);
+    const ChunkHead c = decode_ch(blockIdx.x, N, H);
+    const typename IO::T* U = job == 0 ? x : dy;
+    const typename IO::T* V = job == 0 ? Bm : Cm;
+    float* out = (job == 0 ? S : dS) + c.ch * (P * R);
+    const int64_t urow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(P);
+    const int64_t ustride = static_cast<int64_t>(H) * P;
+    const int64_t vrow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(R);
+    const int64_t vstride = static_cast<int64_t>(H) * R;
+    const double* cc = cdt + c.c_bhn * L;
+    const float* dtc = dt + c.c_bhn * L;
+    const double a = static_cast<double>(Av[c.h]);
+    const double end = cc[L - 1];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    constexpr int NTR = R / 16, NTILE = (P / 16) * NTR, TPW = (NTILE + 3) / 4;
+    v4f acc[TPW];
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) acc[q] = zero4();
+
+    for (int t0 = 0; t0 < L; t0 += TB) {
+        if (tid < TB) {
+            const int t = t0 + tid;
+            sw[tid] = job == 0 ? dtc[t] * expf(static_cast<float>(a * (end - cc[t])))
+                               : expf(static_cast<float>(a * cc[t]));
+        }
+        __syncthreads();
+        stage_rows<IO, P>(sU, U + urow0 + t0 * ustride, ustride);
+        {
+            constexpr int VV = R / 4;
+            for (int idx = tid; idx < TB * VV; idx += NT) {
+                const int row = idx / VV, c4 = idx - (idx / VV) * VV;
+                v4f v = io<IO>::ld4(V, vrow0 + (t0 + row) * vstride + c4 * 4);
+                v *= sw[row];
+                *reinterpret_cast<v4f*>(sV + row * (R + 4) + c4 * 4) = v;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < TPW; ++q) {
+            const int tile = wave + 4 * q;
+            if (tile < NTILE) {
+                const int pt = tile / NTR, rt = tile - (tile / NTR) * NTR;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int t = 16 * kk + 4 * g + v;
+                        acc[q] = mfma16(sU[t * (P + 4) + pt * 16 + i], sV[t * (R + 4) + rt * 16 + i],
+                                        acc[q]);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+        const int tile = wave + 4 * q;
+        if (tile < NTILE) {
+            const int pt = tile / NTR, rt = tile - (tile / NTR) * NTR;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) out[(pt * 16 + 4 * g + v) * R + rt * 16 + i] = acc[q][v];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------- K5
+// One workgroup per (chunk-head, 64-token target block tb); wave w owns target
+// rows t = 16w .. 16w+15 of the block and keeps its C rows in registers.
+//   BLUE:   acc[t, p] = exp(cum[t]) sum_r C[t,r] S_in[p,r]
+//   ORANGE: for every source block sb <= tb and 16-token source tile j,
+//           CB^T[s, t] = sum_r B[s,r] C[t,r]  (MFMA; lane holds t = i, s = 4g+v),
+//           W[t, s] = CB * exp(cum[t] - cum[s]) * dt[s]  (s <= t),
+//           acc[t, p] += sum_s W[t,s] x[s,p]  (the W registers are the A operand).
+//   y = acc + D x.
+template <class IO, int P, int R>
+__global__ __launch_bounds__(NT) void k5_chunk_scan(
+    const typename IO::T* __restrict__ x, const float* __restrict__ dt,
+    const typename IO::T* __restrict__ Bm, const typename IO::T* __restrict__ Cm,
+    const float* __restrict__ Av, const float* __restrict__ Dv, const double* __restrict__ cdt,
+    const float* __restrict__ S, typename IO::T* __restrict__ y, int N, int H, int L, int64_t CH) {
+    constexpr int RS = R + 4, PS = P + 4;
+    constexpr int ROWS = P > TB ? P : TB;
+    __shared__ float sBS[ROWS * RS];  // S_in [P, R] for BLUE, then B of the source block
+    __shared__ float sX[TB * PS];
+    __shared__ double sCumT[TB], sCumS[TB];
+    __shared__ float sDt[TB];
+    const int nblk = L / TB;
+    const int tb = nblk - 1 - static_cast<int>(blockIdx.x / CH);  // heaviest blocks first
+    const ChunkHead c = decode_ch(blockIdx.x % CH, N, H);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    const int64_t xrow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(P);
+    const int64_t xstride = static_cast<int64_t>(H) * P;
+    const int64_t brow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(R);
+    const int64_t bstride = static_cast<int64_t>(H) * R;
+    const double* cc = cdt + c.c_bhn * L;
+    const float* dtc = dt + c.c_bhn * L;
+    const double a = static_cast<double>(Av[c.h]);
+    const int tl = 16 * wave + i;  // this lane's target row inside the block (operand layout)
+
+    v4f creg[R / 16];
+    {
+        const int64_t row = brow0 + static_cast<int64_t>(tb * TB + tl) * bstride;
+#pragma unroll
+        for (int kk = 0; kk < R / 16; ++kk) creg[kk] = io<IO>::ld4(Cm, row + 16 * kk + 4 * g);
+    }
+    stage_mat<R>(sBS, S + c.ch * (P * R), P);
+    if (tid < TB) sCumT[tid] = cc[tb * TB + tid];
+    __syncthreads();
+
+    v4f acc[P / 16];
+#pragma unroll
+    for (int pt = 0; pt < P / 16; ++pt) acc[pt] = zero4();
+    // BLUE: A = C rows (k = r), B operand = S_in[p, r] read along r
+#pragma unroll
+    for (int kk = 0; kk < R / 16; ++kk) {
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt) {
+            const v4f bop = *reinterpret_cast<const v4f*>(sBS + (pt * 16 + i) * RS + 16 * kk + 4 * g);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[pt] = mfma16(creg[kk][v], bop[v], acc[pt]);
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const float e = expf(static_cast<float>(a * sCumT[16 * wave + 4 * g + v]));
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt) acc[pt][v] *= e;
+    }
+
+    const double ct = sCumT[tl];
+    for (int sb = 0; sb <= tb; ++sb) {
+        __syncthreads();
+        stage_rows<IO, R>(sBS, Bm + brow0 + static_cast<int64_t>(sb * TB) * bstride, bstride);
+        stage_rows<IO, P>(sX, x + xrow0 + static_cast<int64_t>(sb * TB) * xstride, xstride);
+        if (tid < TB) {
+            sCumS[tid] = cc[sb * TB + tid];
+            sDt[tid] = dtc[sb * TB + tid];
+        }
+        __syncthreads();
+        const int jmax = (sb == tb) ? wave : 3;
+        for (int j = 0; j <= jmax; ++j) {
+            v4f cbt = zero4();
+#pragma unroll
+            for (int kk = 0; kk < R / 16; ++kk) {
+                const v4f aop = *reinterpret_cast<const v4f*>(sBS + (16 * j + i) * RS + 16 * kk + 4 * g);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) cbt = mfma16(aop[v], creg[kk][v], cbt);
+            }
+            float wv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int s = 16 * j + 4 * g + v;
+                const bool keep = (sb < tb) || (s <= tl);
+                wv[v] = keep ? cbt[v] * expf(static_cast<float>(a * (ct - sCumS[s]))) * sDt[s] : 0.0f;
+            }
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[pt] = mfma16(wv[v], sX[(16 * j + 4 * g + v) * PS + pt * 16 + i], acc[pt]);
+            }
+        }
+    }
+    // sX now holds x of the target block (the last source block is tb itself).
+    const float Dh = Dv[c.h];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int t = 16 * wave + 4 * g + v;
+        const int64_t row = xrow0 + static_cast<int64_t>(tb * TB + t) * xstride;
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt) {
+            const float val = acc[pt][v] + Dh * sX[t * PS + pt * 16 + i];
+            io<IO>::st(y, row + pt * 16 + i, val);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ dispatch
+#define SSD_FOR_EACH_PR(X) \
+    X(16, 16) X(16, 32) X(16, 64) X(16, 128) \
+    X(32, 16) X(32, 32) X(32, 64) X(32, 128) \
+    X(64, 16) X(64, 32) X(64, 64) X(64, 128) \
+    X(128, 16) X(128, 32) X(128, 64) X(128, 128)
+
+template <class IO>
+static hipError_t states_io(const Shape& s, bool js, bool jd, const void* x, const void* Bm,
+                            const void* dy, const void* Cm, const float* dt, const float* A,
+                            const double* cdt, float* S, float* dS, hipStream_t st) {
+    using T = typename IO::T;
+    const int64_t CH = static_cast<int64_t>(s.B) * s.N * s.H;
+    if (CH == 0 || (!js && !jd)) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(CH), (js && jd) ? 2u : 1u);
+    const int job0 = js ? 0 : 1;
+#define X(PP, RR)                                                                                \
+    if (s.P == PP && s.R == RR) {                                                                \
+        hipLaunchKernelGGL((k_chunk_states<IO, PP, RR>), grid, dim3(NT), 0, st,                 \
+                           static_cast<const T*>(x), static_cast<const T*>(Bm),                  \
+                           static_cast<const T*>(dy), static_cast<const T*>(Cm), dt, A, cdt, S, dS, \
+                           s.N, s.H, s.L, job0);                                                 \
+        return hipGetLastError();                                                                \
+    }
+    SSD_FOR_EACH_PR(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_states(const Shape& s, bool job_state, bool job_dstate, const void* x,
+                               const void* Bm, const void* dy, const void* Cm, const float* dt,
+                               const float* A, const double* cdt, float* S, float* dS,
+                               hipStream_t st) {
+    return s.io == 1 ? states_io<BF16>(s, job_state, job_dstate, x, Bm, dy, Cm, dt, A, cdt, S, dS, st)
+                     : states_io<F32>(s, job_state, job_dstate, x, Bm, dy, Cm, dt, A, cdt, S, dS, st);
+}
+
+template <class IO>
+static hipError_t k5_io(const Shape& s, const void* x, const float* dt, const void* Bm,
+                        const void* Cm, const float* A, const float* D, const double* cdt,
+                        const float* S, void* y, hipStream_t st) {
+    using T = typename IO::T;
+    const int64_t CH = static_cast<int64_t>(s.B) * s.N * s.H;
+    if (CH == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(CH * s.nblk()));
+#define X(PP, RR)                                                                              \
+    if (s.P == PP && s.R == RR) {                                                              \
+        hipLaunchKernelGGL((k5_chunk_scan<IO, PP, RR>), grid, dim3(NT), 0, st,                \
+                           static_cast<const T*>(x), dt, static_cast<const T*>(Bm),            \
+                           static_cast<const T*>(Cm), A, D, cdt, S, static_cast<T*>(y), s.N, s.H, \
+                           s.L, CH);                                                           \
+        return hipGetLastError();                                                              \
+    }
+    SSD_FOR_EACH_PR(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_k5_scan(const Shape& s, const void* x, const float* dt, const void* Bm,
+                          const void* Cm, const float* A, const float* D, const double* cdt,
+                          const float* S, void* y, hipStream_t st) {
+    return s.io == 1 ? k5_io<BF16>(s, x, dt, Bm, Cm, A, D, cdt, S, y, st)
+                     : k5_io<F32>(s, x, dt, Bm, Cm, A, D, cdt, S, y, st);
+}
+
+}  // namespace ssd

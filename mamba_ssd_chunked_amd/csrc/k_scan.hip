@@ -1,0 +1,300 @@
+// Bandwidth-bound passes of the SSD scan: K1 (within-chunk cumsum), the K4
+// serial carry across chunks and its reverse, K1's backward (suffix sums), the
+// per-head reductions of d_A / d_D, and a small fill kernel.
+//
+// Page: burn-mamba "mamba2/ssd/serial_recalculated/combined_backward.rs".
+//  - K1 is the inclusive cumsum of dt * a_decay inside each chunk (RECOMPUTE
+//    section); its backward is the suffix sum of the gradient w.r.t. the
+//    cumsum ("SUM GRADIENT CONTRIBUTIONS + K1 BACKWARD").
+//  - K4 passes s_{i+1} = exp(end_i) s_i + intra_i across chunks; its reverse
+//    ("K4 backward step") keeps d_s_i = exp(end_i) d_s_{i+1} + d_chunk_input_i
+//    and hands d_s_{i+1} to chunk i as the gradient of its intra-chunk state.
+//
+// Precision: A is constant per head, so the cumsum of dt * A equals A times the
+// cumsum of dt.  K1 stores cdt = cumsum(dt) in fp64 and every consumer forms a
+// decay exponent as A * (cdt[t] - cdt[s]) in fp64 before one fp32 exp.  At
+// |cumsum| of several hundred an fp32 cumsum would put relative errors of
+// 1e-5..1e-4 on the decays; cdt also gives d_A its exact per-pair weights
+// (see k_chunk_bwd.hip).
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+// One wave64 per chunk; lane j owns positions [j*E, j*E + E), E = L / 64.
+__global__ __launch_bounds__(NT) void k1_cumsum(const float* __restrict__ dt,
+                                                 double* __restrict__ cdt, int64_t nchunks_total,
+                                                 int L) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    if (c >= nchunks_total) return;
+    const int E = L >> 6;
+    const float* src = dt + c * L + lane * E;
+    double v[4];
+    double run = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (e < E) {
+            run += static_cast<double>(src[e]);
+            v[e] = run;
+        }
+    double incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    double excl = __shfl_up(incl, 1);
+    if (lane == 0) excl = 0.0;
+    double* dst = cdt + c * L + lane * E;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (e < E) dst[e] = v[e] + excl;
+}
+
+hipError_t launch_k1_cumsum(const Shape& s, const float* dt, double* cdt, hipStream_t st) {
+    const int64_t nc = s.chunks();
+    if (nc == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>((nc + 3) / 4));
+    hipLaunchKernelGGL(k1_cumsum, grid, dim3(NT), 0, st, dt, cdt, nc, s.L);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------- K4
+// One thread per (b, h, 4 consecutive state elements); a serial loop over the
+// chunks.  The load of chunk i+1 is issued before the store of chunk i so the
+// memory pipe stays ahead of the FMA chain.
+__device__ __forceinline__ float chunk_decay(const double* cdt_bh, double a, int i, int L) {
+    return static_cast<float>(exp(a * cdt_bh[static_cast<int64_t>(i) * L + (L - 1)]));
+}
+
+__global__ __launch_bounds__(NT) void k4_state_pass(float* __restrict__ S,
+                                                     const double* __restrict__ cdt,
+                                                     const float* __restrict__ A,
+                                                     const float* __restrict__ init,
+                                                     float* __restrict__ final_state, int N,
+                                                     int H, int L, int PR, int64_t total4) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
+    if (idx >= total4) return;
+    const int PR4 = PR >> 2;
+    const int64_t bh = idx / PR4;
+    const int e = static_cast<int>(idx - bh * PR4) * 4;
+    const int h = static_cast<int>(bh % H);
+    const int64_t b = bh / H;
+    const double* cdt_bh = cdt + bh * N * L;
+    const double a = static_cast<double>(A[h]);
+    const int64_t stride = static_cast<int64_t>(H) * PR;
+    v4f s = init ? *reinterpret_cast<const v4f*>(init + bh * PR + e) : zero4();
+    float* p = S + (b * N * H + h) * PR + e;
+    v4f cur = N > 0 ? *reinterpret_cast<const v4f*>(p) : zero4();
+    for (int i = 0; i < N; ++i) {
+        const v4f nxt = (i + 1 < N) ? *reinterpret_cast<const v4f*>(p + stride) : zero4();
+        *reinterpret_cast<v4f*>(p) = s;
+        const float dec = chunk_decay(cdt_bh, a, i, L);
+        s = dec * s + cur;
+        cur = nxt;
+        p += stride;
+    }
+    if (final_state) *reinterpret_cast<v4f*>(final_state + bh * PR + e) = s;
+}
+
+__global__ __launch_bounds__(NT) void k4_state_pass_bwd(
+    float* __restrict__ S, float* __restrict__ dS, const double* __restrict__ cdt,
+    const float* __restrict__ A, const float* __restrict__ init, const float* __restrict__ d_final,
+    float* __restrict__ d_init, int N, int H, int L, int PR, int64_t total4) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
+    if (idx >= total4) return;
+    const int PR4 = PR >> 2;
+    const int64_t bh = idx / PR4;
+    const int e = static_cast<int>(idx - bh * PR4) * 4;
+    const int h = static_cast<int>(bh % H);
+    const int64_t b = bh / H;
+    const double* cdt_bh = cdt + bh * N * L;
+    const double a = static_cast<double>(A[h]);
+    const int64_t stride = static_cast<int64_t>(H) * PR;
+    // forward: chunk-entry states
+    {
+        v4f s = init ? *reinterpret_cast<const v4f*>(init + bh * PR + e) : zero4();
+        float* p = S + (b * N * H + h) * PR + e;
+        v4f cur = N > 0 ? *reinterpret_cast<const v4f*>(p) : zero4();
+        for (int i = 0; i < N; ++i) {
+            const v4f nxt = (i + 1 < N) ? *reinterpret_cast<const v4f*>(p + stride) : zero4();
+            *reinterpret_cast<v4f*>(p) = s;
+            s = chunk_decay(cdt_bh, a, i, L) * s + cur;
+            cur = nxt;
+            p += stride;
+        }
+    }
+    // reverse: gradient of the state leaving each chunk
+    v4f gacc = d_final ? *reinterpret_cast<const v4f*>(d_final + bh * PR + e) : zero4();
+    if (N > 0) {
+        float* p = dS + ((b * N + (N - 1)) * H + h) * PR + e;
+        v4f cur = *reinterpret_cast<const v4f*>(p);
+        for (int i = N - 1; i >= 0; --i) {
+            const v4f nxt = (i > 0) ? *reinterpret_cast<const v4f*>(p - stride) : zero4();
+            *reinterpret_cast<v4f*>(p) = gacc;
+            gacc = chunk_decay(cdt_bh, a, i, L) * gacc + cur;
+            cur = nxt;
+            p -= stride;
+        }
+    }
+    if (d_init) *reinterpret_cast<v4f*>(d_init + bh * PR + e) = gacc;
+}
+
+hipError_t launch_k4_pass(const Shape& s, float* S, const double* cdt, const float* A,
+                          const float* init, float* final_state, hipStream_t st) {
+    const int PR = s.P * s.R;
+    const int64_t total4 = static_cast<int64_t>(s.B) * s.H * (PR / 4);
+    if (total4 == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>((total4 + NT - 1) / NT));
+    hipLaunchKernelGGL(k4_state_pass, grid, dim3(NT), 0, st, S, cdt, A, init, final_state, s.N, s.H,
+                       s.L, PR, total4);
+    return hipGetLastError();
+}
+
+hipError_t launch_k4_pass_bwd(const Shape& s, float* S, float* dS, const double* cdt,
+                              const float* A, const float* init, const float* d_final,
+                              float* d_init, hipStream_t st) {
+    const int PR = s.P * s.R;
+    const int64_t total4 = static_cast<int64_t>(s.B) * s.H * (PR / 4);
+    if (total4 == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>((total4 + NT - 1) / NT));
+    hipLaunchKernelGGL(k4_state_pass_bwd, grid, dim3(NT), 0, st, S, dS, cdt, A, init, d_final,
+                       d_init, s.N, s.H, s.L, PR, total4);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------- K1^T
+// Per chunk (one wave64): with g[k] = g1[k] + g2[k] the gradient w.r.t. the
+// cumsum at k from BLUE/ORANGE, d_delta[k] the K3 gradient w.r.t. the decay
+// exponent (end - cumsum[k]) and d_end the K4 gradient w.r.t. end = cumsum[L-1],
+// the gradient w.r.t. dA_t = dt_t * A is
+//   d_da[t] = sum_{k>=t} g[k] + sum_{k<t} d_delta[k] + d_end
+// (end - cumsum[k] sums dA over positions k+1..L-1, so d_delta[k] reaches every
+// t > k), and d_dt[t] += A d_da[t].  (d_A is assembled from per-pair weights in
+// the chunk kernels instead of sum_t d_da[t] dt[t], which cancels badly.)
+__global__ __launch_bounds__(NT) void k1t_revcumsum(
+    const float* __restrict__ g1, const float* __restrict__ g2,
+    const float* __restrict__ d_delta, const float* __restrict__ d_end,
+    const float* __restrict__ A, float* __restrict__ d_dt, int64_t nchunks_total, int H, int N,
+    int L) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    if (c >= nchunks_total) return;
+    const int h = static_cast<int>((c / N) % H);
+    const double a = static_cast<double>(A[h]);
+    const int E = L >> 6;
+    const int64_t base = c * L + lane * E;
+    double gv[4], dl[4];
+    double gtot = 0.0, dtot = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (e < E) {
+            gv[e] = static_cast<double>(g1[base + e]) + static_cast<double>(g2[base + e]);
+            dl[e] = static_cast<double>(d_delta[base + e]);
+            gtot += gv[e];
+            dtot += dl[e];
+        }
+    // sum of g over the lanes after this one; sum of d_delta over the lanes before it
+    double suf = gtot, pre = dtot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double o1 = __shfl_down(suf, off);
+        const double o2 = __shfl_up(pre, off);
+        if (lane + off < 64) suf += o1;
+        if (lane >= off) pre += o2;
+    }
+    double after = __shfl_down(suf, 1);
+    if (lane == 63) after = 0.0;
+    double before = __shfl_up(pre, 1);
+    if (lane == 0) before = 0.0;
+    const double dend = static_cast<double>(d_end[c]);
+    double sfx[4];
+    double run = after;
+#pragma unroll
+    for (int e = 3; e >= 0; --e)
+        if (e < E) {
+            run += gv[e];
+            sfx[e] = run;
+        }
+    double pfx = before;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (e < E) {
+            const double dda = sfx[e] + pfx + dend;
+            pfx += dl[e];
+            d_dt[base + e] = static_cast<float>(static_cast<double>(d_dt[base + e]) + a * dda);
+        }
+}
+
+hipError_t launch_k1t(const Shape& s, const float* g1, const float* g2, const float* d_delta,
+                      const float* d_end, const float* A, float* d_dt, hipStream_t st) {
+    const int64_t nc = s.chunks();
+    if (nc == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>((nc + 3) / 4));
+    hipLaunchKernelGGL(k1t_revcumsum, grid, dim3(NT), 0, st, g1, g2, d_delta, d_end, A, d_dt, nc,
+                       s.H, s.N, s.L);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------- head reductions
+// One workgroup per head sums partials stored in [b, n, h, k] order (k < nk) in
+// a fixed order: thread j takes a fixed strided subset, then a fixed tree, so
+// the result does not depend on scheduling.  Up to two arrays are summed per
+// output (d_A gets the target- and source-side partials).
+__global__ __launch_bounds__(NT) void reduce_heads(const double* __restrict__ a0,
+                                                   const double* __restrict__ a1,
+                                                   const double* __restrict__ d0,
+                                                   float* __restrict__ d_A,
+                                                   float* __restrict__ d_D, int B, int H,
+                                                   int N, int nk) {
+    __shared__ double ra[NT], rd[NT];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    double a = 0.0, d = 0.0;
+    const int64_t total = static_cast<int64_t>(B) * N * nk;
+    for (int64_t j = tid; j < total; j += NT) {
+        const int64_t bn = j / nk, k = j - (j / nk) * nk;
+        const int64_t o = (bn * H + h) * nk + k;
+        if (a0) a += a0[o];
+        if (a1) a += a1[o];
+        if (d0) d += d0[o];
+    }
+    ra[tid] = a;
+    rd[tid] = d;
+    __syncthreads();
+    for (int w = NT / 2; w > 0; w >>= 1) {
+        if (tid < w) {
+            ra[tid] += ra[tid + w];
+            rd[tid] += rd[tid + w];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        if (d_A) d_A[h] = static_cast<float>(ra[0]);
+        if (d_D) d_D[h] = static_cast<float>(rd[0]);
+    }
+}
+
+hipError_t launch_reduce_heads(const Shape& s, const double* dA_part0, const double* dA_part1,
+                               const double* dD_part, int nk, float* d_A, float* d_D,
+                               hipStream_t st) {
+    if (s.H == 0) return hipSuccess;
+    hipLaunchKernelGGL(reduce_heads, dim3(s.H), dim3(NT), 0, st, dA_part0, dA_part1, dD_part, d_A,
+                       d_D, s.B, s.H, s.N, nk);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(NT) void copy_or_zero(float* __restrict__ dst,
+                                                  const float* __restrict__ src, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.0f;
+}
+
+hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t st) {
+    if (n <= 0 || !dst) return hipSuccess;
+    hipLaunchKernelGGL(copy_or_zero, dim3(static_cast<unsigned>((n + NT - 1) / NT)), dim3(NT), 0,
+                       st, dst, src, n);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

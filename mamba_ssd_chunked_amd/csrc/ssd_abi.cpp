@@ -1,0 +1,365 @@
+// C ABI of the SSD scan: argument validation, workspace plan and the launch
+// sequence of each entry point (declared and documented in include/ssd.h).
+//
+// Every entry point validates all of its arguments before it enqueues anything,
+// then enqueues its kernels on the caller's stream and returns without
+// synchronising.  The workspace is caller-owned; the library allocates nothing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <initializer_list>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "ssd.h"
+#include "ssd_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return SSD_OK;
+}
+
+bool pow2_in(int64_t v, int64_t lo, int64_t hi) {
+    return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+int validate_dims(const ssd_dims* d, ssd::Shape* s) {
+    if (!d) return fail(SSD_ERR_NULL, "dims is NULL");
+    if ((d->io_dtype != SSD_F32 && d->io_dtype != SSD_BF16) || d->reserved != 0)
+        return fail(SSD_ERR_DTYPE, "io_dtype must be SSD_F32 (0) or SSD_BF16 (1) and reserved 0 (got %d, %d)",
+                    d->io_dtype, d->reserved);
+    if (d->batch < 0 || d->nchunks < 0 || d->chunk_len <= 0 || d->nheads <= 0 || d->headdim <= 0 ||
+        d->dstate <= 0)
+        return fail(SSD_ERR_SHAPE,
+                    "need batch >= 0, nchunks >= 0 and chunk_len, nheads, headdim, dstate > 0 "
+                    "(got b=%lld n=%lld l=%lld h=%lld p=%lld r=%lld)",
+                    (long long)d->batch, (long long)d->nchunks, (long long)d->chunk_len,
+                    (long long)d->nheads, (long long)d->headdim, (long long)d->dstate);
+    if (!pow2_in(d->chunk_len, 64, 256))
+        return fail(SSD_ERR_UNSUPPORTED, "chunk_len must be 64, 128 or 256 (got %lld)", (long long)d->chunk_len);
+    if (!pow2_in(d->headdim, 16, 128) || !pow2_in(d->dstate, 16, 128))
+        return fail(SSD_ERR_UNSUPPORTED, "headdim and dstate must be 16, 32, 64 or 128 (got %lld, %lld)",
+                    (long long)d->headdim, (long long)d->dstate);
+    // index arithmetic and grid limits
+    const double ch_blocks = (double)d->batch * (double)d->nchunks * (double)d->nheads *
+                             (double)(d->chunk_len / 64);
+    const double elems = (double)d->batch * d->nchunks * d->chunk_len * d->nheads * 128.0;
+    if (ch_blocks > 2.0e9 || elems > 4.0e18 || d->nchunks > (1 << 30) || d->nheads > (1 << 30) ||
+        d->batch > (1 << 30))
+        return fail(SSD_ERR_UNSUPPORTED, "problem too large for one call (split the batch)");
+    s->B = (int)d->batch;
+    s->N = (int)d->nchunks;
+    s->L = (int)d->chunk_len;
+    s->H = (int)d->nheads;
+    s->P = (int)d->headdim;
+    s->R = (int)d->dstate;
+    s->io = d->io_dtype;
+    return SSD_OK;
+}
+
+int check_align(const void* p, const char* name, size_t a) {
+    if (p && (reinterpret_cast<uintptr_t>(p) % a) != 0)
+        return fail(SSD_ERR_UNSUPPORTED, "%s is not %zu-byte aligned", name, a);
+    return SSD_OK;
+}
+
+size_t round_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+// Workspace plan (256-byte aligned regions):
+//   cdt    fp64 [b,h,n,l]  cumsum of dt inside each chunk (K1)
+//   S      fp32 [b,n,h,p,r] chunk states (K3, then chunk-entry states after K4)
+//   bwd:   dS fp32 [b,n,h,p,r] (BLUE state gradient, then the carried d_intra),
+//          g1, g2, dlt fp32 [b,h,n,l], dend fp32 [b,h,n],
+//          dAT, dAS, dD fp64 [b,n,h,l/64] (per-block d_A / d_D partials)
+struct Ws {
+    size_t cdt = 0, S = 0, dS = 0, g1 = 0, g2 = 0, dlt = 0, dend = 0, dAT = 0, dAS = 0, dD = 0;
+    size_t total = 0;
+};
+
+Ws plan(const ssd::Shape& s, int op) {
+    Ws w;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += round_up(bytes);
+        return at;
+    };
+    const size_t tok = static_cast<size_t>(s.B) * s.H * s.N * s.L;  // (b, h, token)
+    const size_t chunks = static_cast<size_t>(s.B) * s.H * s.N;
+    const size_t states = chunks * s.P * s.R;
+    w.cdt = take(8 * tok);
+    w.S = take(4 * states);
+    if (op == SSD_OP_BWD || op == SSD_OP_MOMENTS_BWD) {
+        w.dS = take(4 * states);
+        w.g1 = take(4 * tok);
+        w.g2 = take(4 * tok);
+        w.dlt = take(4 * tok);
+        w.dend = take(4 * chunks);
+        w.dAT = take(8 * chunks * s.nblk());
+        w.dAS = take(8 * chunks * s.nblk());
+        w.dD = take(8 * chunks * s.nblk());
+    }
+    w.total = off;
+    return w;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// ---------------------------------------------------------------- timing
+// Optional per-kernel timing: when enabled, every launch below is bracketed by
+// a pair of HIP events recorded on the caller's stream; ssd_timing_collect()
+// waits for them and sums the elapsed times per kernel name.
+struct TimingRec {
+    const char* name;
+    hipEvent_t a, b;
+};
+std::mutex g_tm;
+bool g_timing = false;
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t pool_event() {
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t st, F&& launch) {
+    bool on;
+    {
+        std::lock_guard<std::mutex> lk(g_tm);
+        on = g_timing;
+    }
+    if (!on) return launch();
+    hipEvent_t a, b;
+    {
+        std::lock_guard<std::mutex> lk(g_tm);
+        a = pool_event();
+        b = pool_event();
+    }
+    if (!a || !b) return launch();
+    hipEventRecord(a, st);
+    const hipError_t e = launch();
+    hipEventRecord(b, st);
+    std::lock_guard<std::mutex> lk(g_tm);
+    g_recs.push_back({name, a, b});
+    return e;
+}
+
+#define SSD_HIP(call, what)                                                         \
+    do {                                                                            \
+        hipError_t e_ = timed(what, st, [&]() { return (call); });                  \
+        if (e_ != hipSuccess)                                                       \
+            return fail(SSD_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e_)); \
+    } while (0)
+
+int check_ws(const ssd::Shape& s, int op, void* ws, size_t ws_bytes) {
+    const size_t need = plan(s, op).total;
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(SSD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
+                    ws ? "" : ", NULL pointer");
+    if (need > 0 && (reinterpret_cast<uintptr_t>(ws) % 256) != 0)
+        return fail(SSD_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
+    return SSD_OK;
+}
+
+int check_io_ptrs(const ssd::Shape& s, std::initializer_list<std::pair<const void*, const char*>> io,
+                  std::initializer_list<std::pair<const void*, const char*>> f32) {
+    const size_t ia = s.io == SSD_BF16 ? 8 : 16;
+    for (auto& p : io)
+        if (int rc = check_align(p.first, p.second, ia)) return rc;
+    for (auto& p : f32)
+        if (int rc = check_align(p.first, p.second, 16)) return rc;
+    return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_last_error(void) { return g_err; }
+
+int ssd_timing_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_tm);
+    g_timing = on != 0;
+    return ok();
+}
+
+int ssd_timing_collect(int max_kernels, char* names, size_t name_stride, double* total_ms,
+                       int64_t* launches, int* n_kernels) {
+    if (!n_kernels || (max_kernels > 0 && (!names || !total_ms || !launches)) || name_stride < 2)
+        return fail(SSD_ERR_NULL, "ssd_timing_collect: output arrays are required");
+    std::vector<TimingRec> recs;
+    {
+        std::lock_guard<std::mutex> lk(g_tm);
+        recs.swap(g_recs);
+    }
+    std::vector<const char*> seen;
+    std::vector<double> ms;
+    std::vector<int64_t> cnt;
+    int rc = SSD_OK;
+    for (const TimingRec& r : recs) {
+        float el = 0.f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&el, r.a, r.b) != hipSuccess)
+            rc = fail(SSD_ERR_HIP, "ssd_timing_collect: event query failed");
+        size_t k = 0;
+        while (k < seen.size() && std::strcmp(seen[k], r.name) != 0) ++k;
+        if (k == seen.size()) {
+            seen.push_back(r.name);
+            ms.push_back(0.0);
+            cnt.push_back(0);
+        }
+        ms[k] += el;
+        cnt[k] += 1;
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_tm);
+        for (const TimingRec& r : recs) {
+            g_pool.push_back(r.a);
+            g_pool.push_back(r.b);
+        }
+    }
+    const int n = static_cast<int>(seen.size());
+    *n_kernels = n;
+    for (int k = 0; k < n && k < max_kernels; ++k) {
+        std::snprintf(names + static_cast<size_t>(k) * name_stride, name_stride, "%s", seen[k]);
+        total_ms[k] = ms[k];
+        launches[k] = cnt[k];
+    }
+    return rc == SSD_OK ? ok() : rc;
+}
+
+int ssd_workspace_size(const ssd_dims* dims, int op, size_t* bytes) {
+    ssd::Shape s;
+    if (int rc = validate_dims(dims, &s)) return rc;
+    if (!bytes) return fail(SSD_ERR_NULL, "bytes is NULL");
+    if (op < SSD_OP_FWD || op > SSD_OP_MOMENTS_BWD)
+        return fail(SSD_ERR_SHAPE, "unknown op %d", op);
+    *bytes = plan(s, op).total;
+    return ok();
+}
+
+int ssd_fwd(const ssd_dims* dims, const void* x, const float* dt, const float* A, const void* B,
+            const void* C, const float* D, const float* init, void* y, float* final_state, void* ws,
+            size_t ws_bytes, void* stream) {
+    ssd::Shape s;
+    if (int rc = validate_dims(dims, &s)) return rc;
+    const bool tok = s.B > 0 && s.N > 0;  // token tensors are non-empty
+    if (!A || !D || (tok && (!x || !dt || !B || !C || !y)))
+        return fail(SSD_ERR_NULL, "ssd_fwd: x, dt, A, B, C, D and y are required");
+    if (int rc = check_io_ptrs(s, {{x, "x"}, {B, "B"}, {C, "C"}, {y, "y"}},
+                               {{dt, "dt"}, {init, "init"}, {final_state, "final_state"}}))
+        return rc;
+    if (int rc = check_ws(s, SSD_OP_FWD, ws, ws_bytes)) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t nstate = static_cast<int64_t>(s.B) * s.H * s.P * s.R;
+    if (s.B == 0 || s.N == 0) {
+        if (final_state) SSD_HIP(ssd::launch_copy_or_zero(final_state, init, nstate, st), "copy init");
+        return ok();
+    }
+    const Ws w = plan(s, SSD_OP_FWD);
+    double* cdt = at<double>(ws, w.cdt);
+    float* S = at<float>(ws, w.S);
+    SSD_HIP(ssd::launch_k1_cumsum(s, dt, cdt, st), "k1_cumsum");
+    SSD_HIP(ssd::launch_chunk_states(s, true, false, x, B, nullptr, nullptr, dt, A, cdt, S, nullptr, st),
+            "k_chunk_states");
+    SSD_HIP(ssd::launch_k4_pass(s, S, cdt, A, init, final_state, st), "k4_state_pass");
+    SSD_HIP(ssd::launch_k5_scan(s, x, dt, B, C, A, D, cdt, S, y, st), "k5_chunk_scan");
+    return ok();
+}
+
+int ssd_bwd(const ssd_dims* dims, const void* dy, const float* d_final, const void* x,
+            const float* dt, const float* A, const void* B, const void* C, const float* D,
+            const float* init, void* d_x, float* d_dt, float* d_A, void* d_B, void* d_C,
+            float* d_D, float* d_init, void* ws, size_t ws_bytes, void* stream) {
+    ssd::Shape s;
+    if (int rc = validate_dims(dims, &s)) return rc;
+    const bool tok = s.B > 0 && s.N > 0;
+    if (!A || !D || !d_A || !d_D ||
+        (tok && (!dy || !x || !dt || !B || !C || !d_x || !d_dt || !d_B || !d_C)))
+        return fail(SSD_ERR_NULL,
+                    "ssd_bwd: dy, x, dt, A, B, C, D, d_x, d_dt, d_A, d_B, d_C and d_D are required");
+    if (int rc = check_io_ptrs(s, {{dy, "dy"}, {x, "x"}, {B, "B"}, {C, "C"}, {d_x, "d_x"}, {d_B, "d_B"}, {d_C, "d_C"}},
+                               {{dt, "dt"}, {d_dt, "d_dt"}, {init, "init"}, {d_final, "d_final"}, {d_init, "d_init"}}))
+        return rc;
+    if (int rc = check_ws(s, SSD_OP_BWD, ws, ws_bytes)) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t nstate = static_cast<int64_t>(s.B) * s.H * s.P * s.R;
+    if (s.B == 0 || s.N == 0) {
+        SSD_HIP(ssd::launch_copy_or_zero(d_A, nullptr, s.H, st), "zero d_A");
+        SSD_HIP(ssd::launch_copy_or_zero(d_D, nullptr, s.H, st), "zero d_D");
+        if (d_init) SSD_HIP(ssd::launch_copy_or_zero(d_init, d_final, nstate, st), "copy d_final");
+        return ok();
+    }
+    const Ws w = plan(s, SSD_OP_BWD);
+    double* cdt = at<double>(ws, w.cdt);
+    float* S = at<float>(ws, w.S);
+    float* dS = at<float>(ws, w.dS);
+    float* g1 = at<float>(ws, w.g1);
+    float* g2 = at<float>(ws, w.g2);
+    float* dlt = at<float>(ws, w.dlt);
+    float* dend = at<float>(ws, w.dend);
+    double* dAT = at<double>(ws, w.dAT);
+    double* dAS = at<double>(ws, w.dAS);
+    double* dDp = at<double>(ws, w.dD);
+    SSD_HIP(ssd::launch_k1_cumsum(s, dt, cdt, st), "k1_cumsum");
+    SSD_HIP(ssd::launch_chunk_states(s, true, true, x, B, dy, C, dt, A, cdt, S, dS, st), "k_chunk_states");
+    SSD_HIP(ssd::launch_k4_pass_bwd(s, S, dS, cdt, A, init, d_final, d_init, st), "k4_state_pass_bwd");
+    SSD_HIP(ssd::launch_bwd_target(s, dy, x, dt, B, C, A, cdt, S, dS, d_C, g1, dend, dAT, st),
+            "k_bwd_target");
+    SSD_HIP(ssd::launch_bwd_source(s, dy, x, dt, B, C, A, D, cdt, dS, d_x, d_B, d_dt, g2, dlt, dAS, dDp, st),
+            "k_bwd_source");
+    SSD_HIP(ssd::launch_k1t(s, g1, g2, dlt, dend, A, d_dt, st), "k1t_revcumsum");
+    SSD_HIP(ssd::launch_reduce_heads(s, dAT, dAS, dDp, s.nblk(), d_A, d_D, st), "reduce_heads");
+    return ok();
+}
+
+int ssd_state_moments(const ssd_dims* dims, const void* x, const float* dt, const float* A,
+                      const void* B, const float* init, const int64_t* valid_len, float* m2,
+                      float* m1, int64_t* count, void* y, const void* C, const float* D,
+                      float* final_state, void* ws, size_t ws_bytes, void* stream) {
+    ssd::Shape s;
+    if (int rc = validate_dims(dims, &s)) return rc;
+    (void)x; (void)dt; (void)A; (void)B; (void)init; (void)valid_len; (void)m2; (void)m1;
+    (void)count; (void)y; (void)C; (void)D; (void)final_state; (void)ws; (void)ws_bytes; (void)stream;
+    return fail(SSD_ERR_UNSUPPORTED, "ssd_state_moments: not available yet");
+}
+
+int ssd_state_moments_bwd(const ssd_dims* dims, const float* d_m2, const float* d_m1,
+                          const void* x, const float* dt, const float* A, const void* B,
+                          const float* init, const int64_t* valid_len, void* d_x, float* d_dt,
+                          float* d_A, void* d_B, float* d_init, void* ws, size_t ws_bytes,
+                          void* stream) {
+    ssd::Shape s;
+    if (int rc = validate_dims(dims, &s)) return rc;
+    (void)d_m2; (void)d_m1; (void)x; (void)dt; (void)A; (void)B; (void)init; (void)valid_len;
+    (void)d_x; (void)d_dt; (void)d_A; (void)d_B; (void)d_init; (void)ws; (void)ws_bytes; (void)stream;
+    return fail(SSD_ERR_UNSUPPORTED, "ssd_state_moments_bwd: not available yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+// Device-side building blocks shared by the SSD kernels (gfx950, wave64).
+//
+// Tiling convention used by every chunk kernel: a chunk of l tokens is split
+// into blocks of TB = 64 tokens; a workgroup has 4 wave64s and wave w owns the
+// 16 token rows [16w, 16w+16) of its block.  Matrix products use the fp32
+// MFMA v_mfma_f32_16x16x4_f32: for lane L (i = L % 16, g = L / 16) the
+// A operand is A[i][k = g], the B operand B[k = g][i], and the four result
+// registers hold D[4g + v][i], v = 0..3.  Four MFMAs that take element v of a
+// float4 read at k = 4g .. 4g+3 cover 16 consecutive k exactly once (the k
+// order inside the group is permuted identically on both operands, which a
+// sum does not see).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int TB = 64;   // tokens per block
+constexpr int NT = 256;  // threads per workgroup
+
+__device__ __forceinline__ v4f mfma16(float a, float b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4f zero4() { return v4f{0.f, 0.f, 0.f, 0.f}; }
+
+// ------------------------------------------------------------------ io types
+struct F32 {
+    using T = float;
+};
+struct BF16 {
+    using T = uint16_t;  // raw bfloat16 bits
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+    return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <class IO>
+struct io;
+
+template <>
+struct io<F32> {
+    using T = float;
+    static __device__ __forceinline__ float ld(const T* p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ v4f ld4(const T* p, size_t i) {
+        return *reinterpret_cast<const v4f*>(p + i);
+    }
+    static __device__ __forceinline__ void st4(T* p, size_t i, v4f v) {
+        *reinterpret_cast<v4f*>(p + i) = v;
+    }
+    static __device__ __forceinline__ void st(T* p, size_t i, float v) { p[i] = v; }
+};
+
+template <>
+struct io<BF16> {
+    using T = uint16_t;
+    static __device__ __forceinline__ float ld(const T* p, size_t i) { return bf16_to_f32(p[i]); }
+    static __device__ __forceinline__ v4f ld4(const T* p, size_t i) {
+        uint2 w = *reinterpret_cast<const uint2*>(p + i);
+        return v4f{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+    }
+    static __device__ __forceinline__ void st4(T* p, size_t i, v4f v) {
+        uint2 w;
+        w.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+        w.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+        *reinterpret_cast<uint2*>(p + i) = w;
+    }
+    static __device__ __forceinline__ void st(T* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// ------------------------------------------------------------------ geometry
+// Index helpers for one chunk-head (b, n, h).  Token row t of x sits at
+// xrow(t) = ((b*n_chunks + n) * l + t) * h_heads * width + h * width.
+struct ChunkHead {
+    int b, n, h;
+    int64_t bn;     // b * nchunks + n
+    int64_t c_bhn;  // (b * nheads + h) * nchunks + n   (index of the chunk in dt / cumA order)
+    int64_t ch;     // (b * nchunks + n) * nheads + h   (index in the [b, n, h, ...] state order)
+};
+
+__device__ __forceinline__ ChunkHead decode_ch(int64_t ch, int N, int H) {
+    ChunkHead c;
+    c.ch = ch;
+    c.h = static_cast<int>(ch % H);
+    c.bn = ch / H;
+    c.n = static_cast<int>(c.bn % N);
+    c.b = static_cast<int>(c.bn / N);
+    c.c_bhn = (static_cast<int64_t>(c.b) * H + c.h) * N + c.n;
+    return c;
+}
+
+// Stage TB token rows of width W (io dtype in global, row stride gstride
+// elements) into LDS as fp32 rows of stride W + 4.
+template <class IO, int W>
+__device__ __forceinline__ void stage_rows(float* lds, const typename IO::T* g, int64_t gstride) {
+    constexpr int V = W / 4;
+    for (int idx = threadIdx.x; idx < TB * V; idx += NT) {
+        const int row = idx / V, c4 = idx - (idx / V) * V;
+        v4f v = io<IO>::ld4(g, static_cast<size_t>(row) * gstride + c4 * 4);
+        *reinterpret_cast<v4f*>(lds + row * (W + 4) + c4 * 4) = v;
+    }
+}
+
+// Stage a contiguous fp32 [rows, W] matrix into LDS rows of stride W + 4.
+template <int W>
+__device__ __forceinline__ void stage_mat(float* lds, const float* g, int rows) {
+    constexpr int V = W / 4;
+    for (int idx = threadIdx.x; idx < rows * V; idx += NT) {
+        const int row = idx / V, c4 = idx - (idx / V) * V;
+        v4f v = *reinterpret_cast<const v4f*>(g + static_cast<size_t>(row) * W + c4 * 4);
+        *reinterpret_cast<v4f*>(lds + row * (W + 4) + c4 * 4) = v;
+    }
+}
+
+__device__ __forceinline__ float lds4(const float* base, int idx, int v) {
+    return base[idx + v];
+}
+
+// Sum over the four lane groups g = 0..3 that share i = lane % 16.
+__device__ __forceinline__ float sum_over_g(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+__device__ __forceinline__ double sum_over_g(double v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+}  // namespace ssd

@@ -1,0 +1,71 @@
+// Host-side launchers of the SSD kernels (all enqueue on `stream`, never sync).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct Shape {
+    int B, N, L, H, P, R;  // batch, nchunks, chunk_len, nheads, headdim, dstate
+    int io;                // 0 = fp32, 1 = bf16
+    int64_t chunks() const { return static_cast<int64_t>(B) * H * N; }  // (b, h, n) chunks
+    int64_t tokens() const { return static_cast<int64_t>(B) * N * L; }
+    int nblk() const { return L / 64; }
+};
+
+// K1: cdt[b,h,n,t] = sum_{k<=t} dt[b,h,n,k]  (fp64; the cumsum of dt*A is A[h] * cdt)
+hipError_t launch_k1_cumsum(const Shape& s, const float* dt, double* cdt, hipStream_t st);
+
+// Chunk-local token contractions (states order [b,n,h,p,r]):
+//   job 0 (K3): S[p,r]  = sum_t x[t,p] * dt[t] * exp(A (cdt[L-1] - cdt[t])) * B[t,r]
+//   job 1:      dS[p,r] = sum_t dy[t,p] * exp(A cdt[t]) * C[t,r]
+hipError_t launch_chunk_states(const Shape& s, bool job_state, bool job_dstate, const void* x,
+                               const void* Bm, const void* dy, const void* Cm, const float* dt,
+                               const float* A, const double* cdt, float* S, float* dS,
+                               hipStream_t st);
+
+// K4: in place over S: S[i] <- state entering chunk i; final <- state after the last chunk.
+hipError_t launch_k4_pass(const Shape& s, float* S, const double* cdt, const float* A,
+                          const float* init, float* final_state, hipStream_t st);
+
+// K4 recompute and its reverse in one pass: S as in launch_k4_pass; in place over dS:
+// dS[i] <- gradient reaching the state that leaves chunk i; d_init <- gradient of init.
+hipError_t launch_k4_pass_bwd(const Shape& s, float* S, float* dS, const double* cdt,
+                              const float* A, const float* init, const float* d_final,
+                              float* d_init, hipStream_t st);
+
+// K5: y = BLUE + ORANGE + D x.
+hipError_t launch_k5_scan(const Shape& s, const void* x, const float* dt, const void* Bm,
+                          const void* Cm, const float* A, const float* D, const double* cdt,
+                          const float* S, void* y, hipStream_t st);
+
+// Backward, target side (rows t): d_C, g1 (BLUE + ORANGE-target gradient w.r.t. the
+// cumsum), d_end, and d_A partials dA_T [b,n,h,block].
+hipError_t launch_bwd_target(const Shape& s, const void* dy, const void* x, const float* dt,
+                             const void* Bm, const void* Cm, const float* A, const double* cdt,
+                             const float* S, const float* dS, void* dC, float* g1, float* d_end,
+                             double* dA_T, hipStream_t st);
+
+// Backward, source side (rows s): d_x, d_B, partial d_dt, g2 (-ORANGE-source), d_delta (K3),
+// d_A partials dA_S and d_D partials dD_part, both [b,n,h,block].
+hipError_t launch_bwd_source(const Shape& s, const void* dy, const void* x, const float* dt,
+                             const void* Bm, const void* Cm, const float* A, const float* D,
+                             const double* cdt, const float* dS, void* dx, void* dB, float* d_dt,
+                             float* g2, float* d_delta, double* dA_S, double* dD_part,
+                             hipStream_t st);
+
+// K1 backward: suffix sums inside each chunk, d_dt += A d_da.
+hipError_t launch_k1t(const Shape& s, const float* g1, const float* g2, const float* d_delta,
+                      const float* d_end, const float* A, float* d_dt, hipStream_t st);
+
+// Deterministic per-head sums of partials in [b, n, h, k] order (k < nk):
+// d_A[h] = sum of dA_part0 + dA_part1, d_D[h] = sum of dD_part.  NULL parts/outputs are skipped.
+hipError_t launch_reduce_heads(const Shape& s, const double* dA_part0, const double* dA_part1,
+                               const double* dD_part, int nk, float* d_A, float* d_D,
+                               hipStream_t st);
+
+// dst[i] = src ? src[i] : 0   (i < n)
+hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t st);
+
+}  // namespace ssd

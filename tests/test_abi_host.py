@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI (no GPU needed; no kernel is ever launched here).
+
+* the HIP library loads and exports every function ``include/ssd.h`` declares;
+* ``ssd_workspace_size`` follows the documented plan;
+* every entry point rejects bad arguments with its documented status code
+  before it touches HIP (fake, aligned device addresses are never dereferenced
+  because validation fails first);
+* the Python binding refuses buffers of the wrong device, dtype or size, and
+  fails loudly when the library is missing.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from mamba_ssd_chunked_amd import build as hipbuild
+from mamba_ssd_chunked_amd import ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+FAKE = 1 << 20  # an aligned non-null address: only validation ever sees it
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssd.LIB_PATH):
+        hipbuild.build()
+    return ssd.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_entry_points():
+    assert header_functions() == sorted(ssd.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def dims(b=2, n=3, l=64, h=2, p=16, r=32, io=0):
+    return ssd.make_dims(b, n, l, h, p, r, io)
+
+
+def test_workspace_plan(lib):
+    d = dims(b=4, n=8, l=256, h=24, p=64, r=128)
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    tok, chunks = 4 * 24 * 8 * 256, 4 * 24 * 8
+    states = chunks * 64 * 128
+    assert ssd.ssd_workspace_size(d, ssd.SSD_OP_FWD) == up(8 * tok) + up(4 * states)
+    bwd = up(8 * tok) + 2 * up(4 * states) + 3 * up(4 * tok) + up(4 * chunks) \
+        + 3 * up(8 * chunks * 4)
+    assert ssd.ssd_workspace_size(d, ssd.SSD_OP_BWD) == bwd
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(l=32), 3), (dict(l=96), 3), (dict(l=512), 3), (dict(p=8), 3), (dict(p=48), 3),
+    (dict(r=256), 3), (dict(b=-1), 2), (dict(n=-1), 2), (dict(h=0), 2), (dict(p=0), 2),
+    (dict(io=2), 4),
+])
+def test_bad_dims_are_rejected(lib, bad, code):
+    d = dims(**bad)
+    out = ctypes.c_size_t(0)
+    assert lib.ssd_workspace_size(ctypes.byref(d), 0, ctypes.byref(out)) == code
+    assert ssd.ssd_last_error() != ""
+    rc = lib.ssd_fwd(ctypes.byref(d), *([FAKE] * 10), 1 << 30, FAKE)
+    assert rc == code
+
+
+def test_null_dims_and_null_pointers(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.ssd_workspace_size(None, 0, ctypes.byref(out)) == 1
+    d = dims()
+    args = [FAKE] * 10
+    for i in (0, 1, 2, 3, 4, 5, 7):  # x, dt, A, B, C, D, y (init and final are nullable)
+        a = list(args)
+        a[i] = None
+        assert lib.ssd_fwd(ctypes.byref(d), *a, 1 << 30, None) == 1, i
+    bargs = [FAKE] * 17
+    for i, name in enumerate(["dy", "d_final", "x", "dt", "A", "B", "C", "D", "init", "d_x",
+                              "d_dt", "d_A", "d_B", "d_C", "d_D", "d_init"]):
+        if name in ("d_final", "init", "d_init"):
+            continue
+        a = list(bargs)
+        a[i] = None
+        assert lib.ssd_bwd(ctypes.byref(d), *a, 1 << 30, None) == 1, name
+
+
+def test_workspace_too_small_and_misaligned(lib):
+    d = dims()
+    need = ssd.ssd_workspace_size(d, ssd.SSD_OP_FWD)
+    assert lib.ssd_fwd(ctypes.byref(d), *([FAKE] * 9), FAKE, need - 1, None) == 5
+    assert lib.ssd_fwd(ctypes.byref(d), *([FAKE] * 9), None, need, None) == 5
+    assert lib.ssd_fwd(ctypes.byref(d), *([FAKE] * 9), FAKE + 4, need, None) == 3
+    # misaligned tensor pointers
+    a = [FAKE] * 10
+    a[0] = FAKE + 4
+    assert lib.ssd_fwd(ctypes.byref(d), *a, need, None) == 3
+    bf = dims(io=1)
+    a[0] = FAKE + 8  # 8-byte alignment is enough for bf16 tensors ...
+    need_bf = ssd.ssd_workspace_size(bf, ssd.SSD_OP_FWD)
+    assert lib.ssd_fwd(ctypes.byref(bf), *a[:9], FAKE + 4, need_bf, None) == 3  # ... not for ws
+
+
+def test_moments_validation(lib):
+    d = dims()
+    assert lib.ssd_state_moments(None, *([FAKE] * 14), 1 << 30, None) == 1
+    assert lib.ssd_state_moments_bwd(ctypes.byref(dims(l=100)), *([FAKE] * 14), 1 << 30,
+                                     None) == 3
+    del d
+
+
+def test_binding_refuses_wrong_buffers(lib):
+    d = dims(b=1, n=1, l=64, h=1, p=16, r=16)
+    x = torch.zeros(1, 1, 64, 1, 16)
+    with pytest.raises(ValueError, match="device tensor"):
+        ssd.ssd_fwd(d, x, x, x, x, x, x, None, x, None, None)
+    with pytest.raises(ValueError, match="elements"):
+        ssd.ssd_fwd(d, torch.zeros(5), x, x, x, x, x, None, x, None, None)
+    with pytest.raises(TypeError, match="float32"):
+        ssd.ssd_fwd(d, x.double(), x, x, x, x, x, None, x, None, None)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(ssd, "_lib", None)
+    with pytest.raises(ImportError, match="missing"):
+        ssd.load_library("/nonexistent/libmamba_ssd_hip.so")

@@ -1,0 +1,120 @@
+"""GPU parity of ssd_fwd / ssd_bwd against the CPU oracle (needs an MI355X).
+
+Every case draws seeded inputs, runs the HIP library through the C ABI
+(``mamba_ssd_chunked_amd.ssd`` marshals torch tensors into ``include/ssd.h``)
+and compares each output tensor with the fp64 oracle by relative L2 error:
+<= 1e-5 for fp32 inputs, <= 2e-2 for bf16 inputs (the oracle is fed the same
+bf16-rounded values).  Small shapes are compared in full; the five named
+workloads run at full size in the benchmark's launch configuration and are
+compared on all batches of sampled heads (heads are independent, so the oracle
+computes exactly those outputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import (GRADS, TOL, compare, gpu_fwd_bwd, oracle_fwd_bwd, say, select_heads)
+from mamba_ssd_chunked_amd import inputs, ssd
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("y", "final") + GRADS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ssd.load_library()
+
+
+@pytest.mark.parametrize("use_init,use_d_final", [(False, False), (True, True)])
+def test_tiny_workload_full(use_init, use_d_final):
+    w = inputs.WORKLOADS["tiny_fp32"]
+    w = inputs.Workload(**{**w.__dict__, "init_std": 0.5 if use_init else 0.0})
+    say(f"case tiny_fp32 init={use_init} d_final={use_d_final}")
+    inp = inputs.make_inputs(w)
+    gpu = gpu_fwd_bwd(inp, use_init=use_init, use_d_final=use_d_final)
+    ref = oracle_fwd_bwd(inp, use_init=use_init, use_d_final=use_d_final)
+    compare(gpu, ref, TOL["f32"], KEYS, "tiny_fp32")
+
+
+SHAPES = [
+    # batch, seq, nheads, headdim, dstate, chunk_len, io
+    (2, 768, 3, 64, 128, 256, "f32"),
+    (1, 384, 2, 32, 64, 128, "f32"),
+    (2, 320, 3, 16, 32, 64, "f32"),
+    (1, 256, 2, 128, 16, 64, "f32"),
+    (1, 512, 1, 16, 128, 128, "f32"),
+    (1, 256, 2, 128, 128, 128, "f32"),
+    (1, 64, 1, 64, 64, 64, "f32"),
+    (2, 512, 2, 64, 128, 256, "bf16"),
+    (1, 384, 3, 32, 16, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b%d_s%d_h%d_p%d_r%d_l%d_%s" % s)
+def test_shapes_full(shape):
+    b, seq, h, p, r, l, io = shape
+    w = inputs.custom(batch=b, seq=seq, nheads=h, headdim=p, dstate=r, chunk_len=l, io=io,
+                      init_std=0.3, seed=100 + seq + p + r)
+    say(f"case {shape}")
+    inp = inputs.make_inputs(w)
+    gpu = gpu_fwd_bwd(inp)
+    ref = oracle_fwd_bwd(inp)
+    compare(gpu, ref, TOL[io], KEYS, str(shape))
+
+
+FULL = [("mamba2_130m_fp32", [0, 13]), ("mamba2_2p7b_bf16", [41]),
+        ("long_context_64k_fp32", [7]), ("moments_valid_len_fp32", [3])]
+
+
+@pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled_heads(name, heads):
+    w = inputs.WORKLOADS[name]
+    say(f"case {name} full size, heads {heads}")
+    inp = inputs.make_inputs(w)
+    use_init = w.init_std > 0
+    gpu = gpu_fwd_bwd(inp, use_init=use_init, use_d_final=False)
+    ref = oracle_fwd_bwd(inp, heads=heads, use_init=use_init, use_d_final=False)
+    compare(select_heads(gpu, heads), ref, TOL[w.io], KEYS, name)
+    for k in KEYS:
+        assert np.all(np.isfinite(gpu[k])), k
+
+
+def test_bitwise_deterministic():
+    w = inputs.custom(batch=2, seq=1024, nheads=4, headdim=64, dstate=128, chunk_len=256,
+                      init_std=0.2, seed=77)
+    say("case determinism")
+    inp = inputs.make_inputs(w)
+    a = gpu_fwd_bwd(inp)
+    b = gpu_fwd_bwd(inp)
+    for k in KEYS:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_null_init_and_d_final_mean_zero():
+    w = inputs.custom(batch=1, seq=256, nheads=2, headdim=32, dstate=32, chunk_len=64,
+                      init_std=0.0, seed=5)
+    inp = inputs.make_inputs(w)
+    inp["d_final"] = torch.zeros_like(inp["d_final"])
+    say("case null init/d_final")
+    a = gpu_fwd_bwd(inp, use_init=False, use_d_final=False)
+    b = gpu_fwd_bwd(inp, use_init=True, use_d_final=True)
+    for k in KEYS:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_empty_sequence_and_batch():
+    say("case empty")
+    w = inputs.custom(batch=2, seq=0, nheads=3, headdim=16, dstate=32, chunk_len=64,
+                      init_std=1.0, seed=9)
+    inp = inputs.make_inputs(w)
+    gpu = gpu_fwd_bwd(inp)
+    assert np.array_equal(gpu["final"], inp["init"].numpy())
+    assert np.array_equal(gpu["d_init"], inp["d_final"].numpy())
+    assert np.all(gpu["d_A"] == 0) and np.all(gpu["d_D"] == 0)
+    w0 = inputs.custom(batch=0, seq=128, nheads=3, headdim=16, dstate=32, chunk_len=64, seed=9)
+    inp0 = inputs.make_inputs(w0)
+    gpu0 = gpu_fwd_bwd(inp0)
+    assert gpu0["y"].size == 0 and np.all(gpu0["d_A"] == 0) and np.all(gpu0["d_D"] == 0)
