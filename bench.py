@@ -62,23 +62,23 @@ def method_flops(w):
 
 
 def cpu_baseline(w, inp, budget_s: float = 12.0, cap_s: float = 40.0):
-    """Time the oracle (single-threaded fp64 C) on (batch 0, head k) slices of the
-    workload until about `budget_s` of CPU work; scale to full tokens/s."""
+    """Time the oracle (single-threaded fp64 C) on (batch, head) slices of the
+    workload, in order, until about `budget_s` of CPU work; scale to full tokens/s."""
     import oracle
     import torch
     seq = w.seq
     sl = 0
     t_tot = 0.0
-    for k in range(w.nheads):
-        hs = [k]
-        x = inp["x"][:1, :, :, hs].double().numpy()
-        dy = inp["dy"][:1, :, :, hs].double().numpy()
-        B = inp["B"][:1, :, :, hs].double().numpy()
-        C = inp["C"][:1, :, :, hs].double().numpy()
-        dt = inp["dt"][:1, hs].double().numpy()
+    for k in range(w.batch * w.nheads):
+        bs, hs = [k // w.nheads], [k % w.nheads]
+        x = inp["x"][bs][:, :, :, hs].double().numpy()
+        dy = inp["dy"][bs][:, :, :, hs].double().numpy()
+        B = inp["B"][bs][:, :, :, hs].double().numpy()
+        C = inp["C"][bs][:, :, :, hs].double().numpy()
+        dt = inp["dt"][bs][:, hs].double().numpy()
         A = inp["A"][hs].double().numpy()
         D = inp["D"][hs].double().numpy()
-        init = inp["init"][:1, hs].double().numpy()
+        init = inp["init"][bs][:, hs].double().numpy()
         t0 = time.perf_counter()
         oracle.ssd_fwd(x, dt, A, B, C, D, init)
         oracle.ssd_bwd(dy, None, x, dt, A, B, C, D, init)
@@ -90,7 +90,7 @@ def cpu_baseline(w, inp, budget_s: float = 12.0, cap_s: float = 40.0):
     token_heads_per_s = sl * seq / t_tot
     return {"value": token_heads_per_s / w.nheads, "unit": "tokens/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"fwd+bwd of {sl} (batch 0, head) slice(s) x {seq} tokens of {w.name} "
+            "sample": f"fwd+bwd of {sl} (batch, head) slice(s) x {seq} tokens of {w.name} "
                       f"in {t_tot:.1f} s; tokens/s = token-heads/s / {w.nheads} heads"}
 
 
@@ -101,6 +101,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mamba2_130m_fp32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB 3 times (a plain copy "
+                         "kernel of known size, to calibrate HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -193,6 +196,14 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp)
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes"] = 4 * n
     print(json.dumps(out), flush=True)
 
 
