@@ -12,6 +12,8 @@
 //    CB = C B^T (K2), the mask keeping s <= t (diagonal included).
 //  - The backward's "d_chunk_input_state = C^T d_ch" with d_ch = dy * exp(cumA)
 //    (BLUE backward) is job 1 of the state kernel.
+//  - Job 2 is the same contraction for the state moments: T = X^T diag(v) B with
+//    v_t = dt_t exp(cumA_t) phi_t (see k_moments.hip).
 // The [l, l] CB and decay matrices never leave the chip: K5 builds each 16x16
 // tile of CB^T with MFMA, scales it in registers and feeds it straight back to
 // the next MFMA as its A operand.
@@ -29,15 +31,16 @@ __global__ __launch_bounds__(NT) void k_chunk_states(
     const typename IO::T* __restrict__ x, const typename IO::T* __restrict__ Bm,
     const typename IO::T* __restrict__ dy, const typename IO::T* __restrict__ Cm,
     const float* __restrict__ dt, const float* __restrict__ Av, const double* __restrict__ cdt,
-    float* __restrict__ S, float* __restrict__ dS, int N, int H, int L, int job0) {
+    float* __restrict__ S, float* __restrict__ dS, const double* __restrict__ phi,
+    float* __restrict__ T, int N, int H, int L, int job0) {
     __shared__ float sU[TB * (P + 4)];
     __shared__ float sV[TB * (R + 4)];
     __shared__ float sw[TB];
     const int job = job0 + static_cast<int>(blockIdx.y);
     const ChunkHead c = decode_ch(blockIdx.x, N, H);
-    const typename IO::T* U = job == 0 ? x : dy;
-    const typename IO::T* V = job == 0 ? Bm : Cm;
-    float* out = (job == 0 ? S : dS) + c.ch * (P * R);
+    const typename IO::T* U = job == 1 ? dy : x;
+    const typename IO::T* V = job == 1 ? Cm : Bm;
+    float* out = (job == 0 ? S : job == 1 ? dS : T) + c.ch * (P * R);
     const int64_t urow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(P);
     const int64_t ustride = static_cast<int64_t>(H) * P;
     const int64_t vrow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(R);
@@ -55,8 +58,10 @@ __global__ __launch_bounds__(NT) void k_chunk_states(
     for (int t0 = 0; t0 < L; t0 += TB) {
         if (tid < TB) {
             const int t = t0 + tid;
-            sw[tid] = job == 0 ? dtc[t] * expf(static_cast<float>(a * (end - cc[t])))
-                               : expf(static_cast<float>(a * cc[t]));
+            sw[tid] = job == 0   ? dtc[t] * expf(static_cast<float>(a * (end - cc[t])))
+                      : job == 1 ? expf(static_cast<float>(a * cc[t]))
+                                 : static_cast<float>(static_cast<double>(dtc[t]) * exp(a * cc[t]) *
+                                                      phi[c.c_bhn * L + t]);
         }
         __syncthreads();
         stage_rows<IO, P>(sU, U + urow0 + t0 * ustride, ustride);
@@ -220,18 +225,20 @@ __global__ __launch_bounds__(NT) void k5_chunk_scan(
 template <class IO>
 static hipError_t states_io(const Shape& s, bool js, bool jd, const void* x, const void* Bm,
                             const void* dy, const void* Cm, const float* dt, const float* A,
-                            const double* cdt, float* S, float* dS, hipStream_t st) {
+                            const double* cdt, float* S, float* dS, const double* phi,
+                            float* Tm, hipStream_t st) {
     using T = typename IO::T;
     const int64_t CH = static_cast<int64_t>(s.B) * s.N * s.H;
-    if (CH == 0 || (!js && !jd)) return hipSuccess;
-    const dim3 grid(static_cast<unsigned>(CH), (js && jd) ? 2u : 1u);
-    const int job0 = js ? 0 : 1;
+    const bool jm = phi && Tm;
+    if (CH == 0 || (!js && !jd && !jm)) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(CH), jm ? 1u : (js && jd) ? 2u : 1u);
+    const int job0 = jm ? 2 : js ? 0 : 1;
 #define X(PP, RR)                                                                                \
     if (s.P == PP && s.R == RR) {                                                                \
         hipLaunchKernelGGL((k_chunk_states<IO, PP, RR>), grid, dim3(NT), 0, st,                 \
                            static_cast<const T*>(x), static_cast<const T*>(Bm),                  \
                            static_cast<const T*>(dy), static_cast<const T*>(Cm), dt, A, cdt, S, dS, \
-                           s.N, s.H, s.L, job0);                                                 \
+                           phi, Tm, s.N, s.H, s.L, job0);                                        \
         return hipGetLastError();                                                                \
     }
     SSD_FOR_EACH_PR(X)
@@ -242,9 +249,10 @@ static hipError_t states_io(const Shape& s, bool js, bool jd, const void* x, con
 hipError_t launch_chunk_states(const Shape& s, bool job_state, bool job_dstate, const void* x,
                                const void* Bm, const void* dy, const void* Cm, const float* dt,
                                const float* A, const double* cdt, float* S, float* dS,
-                               hipStream_t st) {
-    return s.io == 1 ? states_io<BF16>(s, job_state, job_dstate, x, Bm, dy, Cm, dt, A, cdt, S, dS, st)
-                     : states_io<F32>(s, job_state, job_dstate, x, Bm, dy, Cm, dt, A, cdt, S, dS, st);
+                               hipStream_t st, const double* phi, float* T) {
+    return s.io == 1
+               ? states_io<BF16>(s, job_state, job_dstate, x, Bm, dy, Cm, dt, A, cdt, S, dS, phi, T, st)
+               : states_io<F32>(s, job_state, job_dstate, x, Bm, dy, Cm, dt, A, cdt, S, dS, phi, T, st);
 }
 
 template <class IO>

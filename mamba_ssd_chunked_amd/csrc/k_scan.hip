@@ -101,7 +101,7 @@ __global__ __launch_bounds__(NT) void k4_state_pass(float* __restrict__ S,
 __global__ __launch_bounds__(NT) void k4_state_pass_bwd(
     float* __restrict__ S, float* __restrict__ dS, const double* __restrict__ cdt,
     const float* __restrict__ A, const float* __restrict__ init, const float* __restrict__ d_final,
-    float* __restrict__ d_init, int N, int H, int L, int PR, int64_t total4) {
+    float* __restrict__ d_init, int N, int H, int L, int PR, int64_t total4, int forward) {
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
     if (idx >= total4) return;
     const int PR4 = PR >> 2;
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(NT) void k4_state_pass_bwd(
     const double a = static_cast<double>(A[h]);
     const int64_t stride = static_cast<int64_t>(H) * PR;
     // forward: chunk-entry states
-    {
+    if (forward) {
         v4f s = init ? *reinterpret_cast<const v4f*>(init + bh * PR + e) : zero4();
         float* p = S + (b * N * H + h) * PR + e;
         v4f cur = N > 0 ? *reinterpret_cast<const v4f*>(p) : zero4();
@@ -154,13 +154,13 @@ hipError_t launch_k4_pass(const Shape& s, float* S, const double* cdt, const flo
 
 hipError_t launch_k4_pass_bwd(const Shape& s, float* S, float* dS, const double* cdt,
                               const float* A, const float* init, const float* d_final,
-                              float* d_init, hipStream_t st) {
+                              float* d_init, hipStream_t st, bool forward) {
     const int PR = s.P * s.R;
     const int64_t total4 = static_cast<int64_t>(s.B) * s.H * (PR / 4);
     if (total4 == 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>((total4 + NT - 1) / NT));
     hipLaunchKernelGGL(k4_state_pass_bwd, grid, dim3(NT), 0, st, S, dS, cdt, A, init, d_final,
-                       d_init, s.N, s.H, s.L, PR, total4);
+                       d_init, s.N, s.H, s.L, PR, total4, forward ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -288,6 +288,27 @@ __global__ __launch_bounds__(NT) void copy_or_zero(float* __restrict__ dst,
                                                   const float* __restrict__ src, int64_t n) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
     if (i < n) dst[i] = src ? src[i] : 0.0f;
+}
+
+struct I64Pack {
+    int64_t v[64];
+};
+
+__global__ void set_i64(int64_t* __restrict__ dst, I64Pack vals, int n) {
+    const int i = threadIdx.x;
+    if (i < n) dst[i] = vals.v[i];
+}
+
+hipError_t launch_set_i64(int64_t* dst, const int64_t* vals, int64_t fill, int64_t n, hipStream_t st) {
+    for (int64_t o = 0; o < n; o += 64) {
+        I64Pack pk;
+        const int m = static_cast<int>(n - o < 64 ? n - o : 64);
+        for (int k = 0; k < 64; ++k) pk.v[k] = k < m ? (vals ? vals[o + k] : fill) : 0;
+        hipLaunchKernelGGL(set_i64, dim3(1), dim3(64), 0, st, dst + o, pk, m);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t st) {

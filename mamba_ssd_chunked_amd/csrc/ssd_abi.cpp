@@ -87,8 +87,15 @@ size_t round_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 //   bwd:   dS fp32 [b,n,h,p,r] (BLUE state gradient, then the carried d_intra),
 //          g1, g2, dlt fp32 [b,h,n,l], dend fp32 [b,h,n],
 //          dAT, dAS, dD fp64 [b,n,h,l/64] (per-block d_A / d_D partials)
+//   moments: valid int64 [b]; phi, psi, phit, psit fp64 [b,h,n,l]; T fp32 [b,n,h,p,r];
+//          fwd: U [b,n,h,l/64,r,r], W [b,n,h,r,r], m1b [b,n,h,l/64,r], m1c [b,n,h,r] fp32
+//          bwd: HS, dS fp32 [b,n,h,p,r]; BS fp32 [b,n,h,l,r]; fin fp32 [b,h,p,r];
+//               hsh, hdm fp64 [b,n,h]; dend2 fp64 [b,h,n]; ddtW, rho, eta, zeta fp32
+//               [b,h,n,l]; dA fp64 [b,n,h,l/64]
 struct Ws {
     size_t cdt = 0, S = 0, dS = 0, g1 = 0, g2 = 0, dlt = 0, dend = 0, dAT = 0, dAS = 0, dD = 0;
+    size_t valid = 0, phi = 0, psi = 0, phit = 0, psit = 0, T = 0, U = 0, W = 0, m1b = 0, m1c = 0, HS = 0, BS = 0,
+           fin = 0, hsh = 0, hdm = 0, dend2 = 0, ddtW = 0, rho = 0, eta = 0, zeta = 0, dA = 0;
     size_t total = 0;
 };
 
@@ -103,17 +110,47 @@ Ws plan(const ssd::Shape& s, int op) {
     const size_t tok = static_cast<size_t>(s.B) * s.H * s.N * s.L;  // (b, h, token)
     const size_t chunks = static_cast<size_t>(s.B) * s.H * s.N;
     const size_t states = chunks * s.P * s.R;
+    const size_t nb = static_cast<size_t>(s.nblk());
     w.cdt = take(8 * tok);
     w.S = take(4 * states);
-    if (op == SSD_OP_BWD || op == SSD_OP_MOMENTS_BWD) {
+    if (op == SSD_OP_BWD) {
         w.dS = take(4 * states);
         w.g1 = take(4 * tok);
         w.g2 = take(4 * tok);
         w.dlt = take(4 * tok);
         w.dend = take(4 * chunks);
-        w.dAT = take(8 * chunks * s.nblk());
-        w.dAS = take(8 * chunks * s.nblk());
-        w.dD = take(8 * chunks * s.nblk());
+        w.dAT = take(8 * chunks * nb);
+        w.dAS = take(8 * chunks * nb);
+        w.dD = take(8 * chunks * nb);
+    }
+    if (op == SSD_OP_MOMENTS || op == SSD_OP_MOMENTS_BWD) {
+        w.valid = take(8 * static_cast<size_t>(s.B));
+        w.phi = take(8 * tok);
+        w.psi = take(8 * tok);
+        w.phit = take(8 * tok);
+        w.psit = take(8 * tok);
+        w.T = take(4 * states);
+    }
+    if (op == SSD_OP_MOMENTS) {
+        const size_t rr = static_cast<size_t>(s.R) * s.R;
+        w.U = take(4 * chunks * nb * rr);
+        w.W = take(4 * chunks * rr);
+        w.m1b = take(4 * chunks * nb * s.R);
+        w.m1c = take(4 * chunks * s.R);
+    }
+    if (op == SSD_OP_MOMENTS_BWD) {
+        w.HS = take(4 * states);
+        w.dS = take(4 * states);
+        w.BS = take(4 * tok * s.R);
+        w.fin = take(4 * static_cast<size_t>(s.B) * s.H * s.P * s.R);
+        w.hsh = take(8 * chunks);
+        w.hdm = take(8 * chunks);
+        w.dend2 = take(8 * chunks);
+        w.ddtW = take(4 * tok);
+        w.rho = take(4 * tok);
+        w.eta = take(4 * tok);
+        w.zeta = take(4 * tok);
+        w.dA = take(8 * chunks * nb);
     }
     w.total = off;
     return w;
@@ -195,6 +232,16 @@ int check_io_ptrs(const ssd::Shape& s, std::initializer_list<std::pair<const voi
         if (int rc = check_align(p.first, p.second, ia)) return rc;
     for (auto& p : f32)
         if (int rc = check_align(p.first, p.second, 16)) return rc;
+    return SSD_OK;
+}
+
+int check_valid_len(const ssd::Shape& s, const int64_t* valid_len) {
+    if (!valid_len) return SSD_OK;
+    const int64_t seq = static_cast<int64_t>(s.N) * s.L;
+    for (int b = 0; b < s.B; ++b)
+        if (valid_len[b] < 0 || valid_len[b] > seq)
+            return fail(SSD_ERR_SHAPE, "valid_len[%d] = %lld is outside [0, %lld]", b,
+                        (long long)valid_len[b], (long long)seq);
     return SSD_OK;
 }
 
@@ -345,9 +392,54 @@ int ssd_state_moments(const ssd_dims* dims, const void* x, const float* dt, cons
                       float* final_state, void* ws, size_t ws_bytes, void* stream) {
     ssd::Shape s;
     if (int rc = validate_dims(dims, &s)) return rc;
-    (void)x; (void)dt; (void)A; (void)B; (void)init; (void)valid_len; (void)m2; (void)m1;
-    (void)count; (void)y; (void)C; (void)D; (void)final_state; (void)ws; (void)ws_bytes; (void)stream;
-    return fail(SSD_ERR_UNSUPPORTED, "ssd_state_moments: not available yet");
+    const bool tok = s.B > 0 && s.N > 0;
+    if (!A || (s.B > 0 && (!m2 || !m1 || !count)) || (tok && (!x || !dt || !B)))
+        return fail(SSD_ERR_NULL, "ssd_state_moments: x, dt, A, B, m2, m1 and count are required");
+    if (y && (!C || !D)) return fail(SSD_ERR_NULL, "ssd_state_moments: y needs C and D");
+    if (int rc = check_io_ptrs(s, {{x, "x"}, {B, "B"}, {C, "C"}, {y, "y"}},
+                               {{dt, "dt"}, {init, "init"}, {m2, "m2"}, {m1, "m1"},
+                                {final_state, "final_state"}}))
+        return rc;
+    if (int rc = check_valid_len(s, valid_len)) return rc;
+    if (int rc = check_ws(s, SSD_OP_MOMENTS, ws, ws_bytes)) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t seq = static_cast<int64_t>(s.N) * s.L;
+    for (int b = 0; b < s.B; ++b) count[b] = (valid_len ? valid_len[b] : seq) * s.P;
+    const int64_t nstate = static_cast<int64_t>(s.B) * s.H * s.P * s.R;
+    if (!tok) {
+        SSD_HIP(ssd::launch_copy_or_zero(m2, nullptr, static_cast<int64_t>(s.B) * s.H * s.R * s.R, st), "zero m2");
+        SSD_HIP(ssd::launch_copy_or_zero(m1, nullptr, static_cast<int64_t>(s.B) * s.H * s.R, st), "zero m1");
+        if (final_state) SSD_HIP(ssd::launch_copy_or_zero(final_state, init, nstate, st), "copy init");
+        return ok();
+    }
+    const Ws w = plan(s, SSD_OP_MOMENTS);
+    double* cdt = at<double>(ws, w.cdt);
+    float* S = at<float>(ws, w.S);
+    int64_t* vd = at<int64_t>(ws, w.valid);
+    double* phi = at<double>(ws, w.phi);
+    double* psi = at<double>(ws, w.psi);
+    float* T = at<float>(ws, w.T);
+    SSD_HIP(ssd::launch_set_i64(vd, valid_len, seq, s.B, st), "set_i64");
+    SSD_HIP(ssd::launch_k1_cumsum(s, dt, cdt, st), "k1_cumsum");
+    SSD_HIP(ssd::launch_chunk_states(s, true, false, x, B, nullptr, nullptr, dt, A, cdt, S, nullptr, st),
+            "k_chunk_states");
+    SSD_HIP(ssd::launch_k4_pass(s, S, cdt, A, init, final_state, st), "k4_state_pass");
+    SSD_HIP(ssd::launch_km_phi(s, cdt, A, vd, phi, psi, at<double>(ws, w.phit), at<double>(ws, w.psit), st),
+            "km_phi");
+    SSD_HIP(ssd::launch_chunk_states(s, false, false, x, B, nullptr, nullptr, dt, A, cdt, nullptr,
+                                     nullptr, st, phi, T),
+            "k_chunk_states");
+    SSD_HIP(ssd::launch_km_fwd_rows(s, x, B, dt, A, cdt, phi, psi, at<float>(ws, w.U),
+                                    at<float>(ws, w.m1b), st),
+            "km_fwd_rows");
+    SSD_HIP(ssd::launch_km_chunk(s, S, T, cdt, A, phi, psi, at<float>(ws, w.W), at<float>(ws, w.m1c),
+                                 nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, st),
+            "km_chunk");
+    SSD_HIP(ssd::launch_km_reduce(s, at<float>(ws, w.U), at<float>(ws, w.W), at<float>(ws, w.m1b),
+                                  at<float>(ws, w.m1c), m2, m1, st),
+            "km_reduce");
+    if (y) SSD_HIP(ssd::launch_k5_scan(s, x, dt, B, C, A, D, cdt, S, y, st), "k5_chunk_scan");
+    return ok();
 }
 
 int ssd_state_moments_bwd(const ssd_dims* dims, const float* d_m2, const float* d_m1,
@@ -357,9 +449,66 @@ int ssd_state_moments_bwd(const ssd_dims* dims, const float* d_m2, const float* 
                           void* stream) {
     ssd::Shape s;
     if (int rc = validate_dims(dims, &s)) return rc;
-    (void)d_m2; (void)d_m1; (void)x; (void)dt; (void)A; (void)B; (void)init; (void)valid_len;
-    (void)d_x; (void)d_dt; (void)d_A; (void)d_B; (void)d_init; (void)ws; (void)ws_bytes; (void)stream;
-    return fail(SSD_ERR_UNSUPPORTED, "ssd_state_moments_bwd: not available yet");
+    const bool tok = s.B > 0 && s.N > 0;
+    if (!A || !d_A || (s.B > 0 && !d_m2) || (tok && (!x || !dt || !B || !d_x || !d_dt || !d_B)))
+        return fail(SSD_ERR_NULL,
+                    "ssd_state_moments_bwd: d_m2, x, dt, A, B, d_x, d_dt, d_A and d_B are required");
+    if (int rc = check_io_ptrs(s, {{x, "x"}, {B, "B"}, {d_x, "d_x"}, {d_B, "d_B"}},
+                               {{dt, "dt"}, {d_dt, "d_dt"}, {init, "init"}, {d_m2, "d_m2"},
+                                {d_m1, "d_m1"}, {d_init, "d_init"}}))
+        return rc;
+    if (int rc = check_valid_len(s, valid_len)) return rc;
+    if (int rc = check_ws(s, SSD_OP_MOMENTS_BWD, ws, ws_bytes)) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t seq = static_cast<int64_t>(s.N) * s.L;
+    const int64_t nstate = static_cast<int64_t>(s.B) * s.H * s.P * s.R;
+    if (!tok) {
+        SSD_HIP(ssd::launch_copy_or_zero(d_A, nullptr, s.H, st), "zero d_A");
+        if (d_init) SSD_HIP(ssd::launch_copy_or_zero(d_init, nullptr, nstate, st), "zero d_init");
+        return ok();
+    }
+    const Ws w = plan(s, SSD_OP_MOMENTS_BWD);
+    double* cdt = at<double>(ws, w.cdt);
+    float* S = at<float>(ws, w.S);
+    int64_t* vd = at<int64_t>(ws, w.valid);
+    double* phi = at<double>(ws, w.phi);
+    double* psi = at<double>(ws, w.psi);
+    float* T = at<float>(ws, w.T);
+    float* HS = at<float>(ws, w.HS);
+    float* dS = at<float>(ws, w.dS);
+    float* BS = at<float>(ws, w.BS);
+    float* fin = at<float>(ws, w.fin);
+    double* hsh = at<double>(ws, w.hsh);
+    double* hdm = at<double>(ws, w.hdm);
+    double* dend2 = at<double>(ws, w.dend2);
+    float* ddtW = at<float>(ws, w.ddtW);
+    float* rho = at<float>(ws, w.rho);
+    float* eta = at<float>(ws, w.eta);
+    float* zeta = at<float>(ws, w.zeta);
+    double* dA = at<double>(ws, w.dA);
+    SSD_HIP(ssd::launch_set_i64(vd, valid_len, seq, s.B, st), "set_i64");
+    SSD_HIP(ssd::launch_k1_cumsum(s, dt, cdt, st), "k1_cumsum");
+    SSD_HIP(ssd::launch_chunk_states(s, true, false, x, B, nullptr, nullptr, dt, A, cdt, S, nullptr, st),
+            "k_chunk_states");
+    SSD_HIP(ssd::launch_k4_pass(s, S, cdt, A, init, fin, st), "k4_state_pass");
+    SSD_HIP(ssd::launch_km_phi(s, cdt, A, vd, phi, psi, at<double>(ws, w.phit), at<double>(ws, w.psit), st),
+            "km_phi");
+    SSD_HIP(ssd::launch_chunk_states(s, false, false, x, B, nullptr, nullptr, dt, A, cdt, nullptr,
+                                     nullptr, st, phi, T),
+            "k_chunk_states");
+    SSD_HIP(ssd::launch_km_chunk(s, S, T, cdt, A, phi, psi, nullptr, nullptr, d_m2, d_m1, B, HS, dS,
+                                 BS, hsh, hdm, st),
+            "km_chunk");
+    SSD_HIP(ssd::launch_k4_pass_bwd(s, S, dS, cdt, A, init, nullptr, d_init, st, false),
+            "k4_state_pass_bwd");
+    SSD_HIP(ssd::launch_km_bwd_rows(s, x, B, dt, A, cdt, phi, psi, at<double>(ws, w.phit),
+                                    at<double>(ws, w.psit), HS, BS, dS, S, fin, d_m1, hsh, hdm, d_x,
+                                    d_B, ddtW, rho, eta, zeta, dend2, dA, st),
+            "km_bwd_rows");
+    SSD_HIP(ssd::launch_km_scan_bwd(s, cdt, dt, A, vd, ddtW, rho, eta, zeta, hsh, hdm, dend2, d_dt, st),
+            "km_scan_bwd");
+    SSD_HIP(ssd::launch_reduce_heads(s, dA, nullptr, nullptr, s.nblk(), d_A, nullptr, st), "reduce_heads");
+    return ok();
 }
 
 }  // extern "C"

@@ -20,10 +20,55 @@ hipError_t launch_k1_cumsum(const Shape& s, const float* dt, double* cdt, hipStr
 // Chunk-local token contractions (states order [b,n,h,p,r]):
 //   job 0 (K3): S[p,r]  = sum_t x[t,p] * dt[t] * exp(A (cdt[L-1] - cdt[t])) * B[t,r]
 //   job 1:      dS[p,r] = sum_t dy[t,p] * exp(A cdt[t]) * C[t,r]
+//   job 2:      T[p,r]  = sum_t x[t,p] * dt[t] * exp(A cdt[t]) * phi[t] * B[t,r]   (moments)
 hipError_t launch_chunk_states(const Shape& s, bool job_state, bool job_dstate, const void* x,
                                const void* Bm, const void* dy, const void* Cm, const float* dt,
                                const float* A, const double* cdt, float* S, float* dS,
-                               hipStream_t st);
+                               hipStream_t st, const double* phi = nullptr, float* T = nullptr);
+
+// ---------------------------------------------------------------- moments
+// Per chunk (one wave each): phi[t] = sum_{u>=t} mask_u exp(2A(cdt_u - cdt_t)),
+// psi[t] = sum_{u>=t} mask_u exp(A(cdt_u - cdt_t)), mask_u = (chunk start + u < valid[b]).
+// phit[t] = sum_{u>=t} mask_u (cdt_u - cdt_t) exp(2A(cdt_u - cdt_t)), psit likewise with A.
+hipError_t launch_km_phi(const Shape& s, const double* cdt, const float* A, const int64_t* valid,
+                         double* phi, double* psi, double* phit, double* psit, hipStream_t st);
+
+// Forward, per (chunk-head, 64-row block): U = sum_{s in block} B_s Z_s^T with
+// Z = (K o G) B over the whole chunk; m1 block part sum_s u_s (1^T x_s) B_s.
+hipError_t launch_km_fwd_rows(const Shape& s, const void* x, const void* Bm, const float* dt,
+                              const float* A, const double* cdt, const double* phi,
+                              const double* psi, float* U, float* m1b, hipStream_t st);
+
+// Per chunk-head.  Forward (dm2 == nullptr): W = H^T (2T + c2 H), m1c = c1 colsum(H).
+// Backward: HS = H S, dS_local = (c2 H + T) S + c1 1 dm1^T, BS = B S, and the chunk
+// scalars hsh = <H, HS>, hdm = dm1 . colsum(H); S = dm2 + dm2^T.
+hipError_t launch_km_chunk(const Shape& s, const float* Sin, const float* T, const double* cdt,
+                           const float* A, const double* phi, const double* psi, float* W,
+                           float* m1c, const float* dm2, const float* dm1, const void* Bm,
+                           float* HS, float* dSl, float* BS, double* hsh, double* hdm,
+                           hipStream_t st);
+
+// m2[b,h] = sym(sum U + sum W), m1[b,h] = sum m1b + sum m1c.
+hipError_t launch_km_reduce(const Shape& s, const float* U, const float* W, const float* m1b,
+                            const float* m1c, float* m2, float* m1, hipStream_t st);
+
+// Backward, per (chunk-head, 64-row block): d_x, d_B, the per-token scalars
+// ddtW, rho, eta, zeta, the d_A partials [b,n,h,block]; block 0 also <d_intra, h_end>.
+hipError_t launch_km_bwd_rows(const Shape& s, const void* x, const void* Bm, const float* dt,
+                              const float* A, const double* cdt, const double* phi,
+                              const double* psi, const double* phit, const double* psit,
+                              const float* HS, const float* BS, const float* dI, const float* Sin,
+                              const float* final_state, const float* dm1, const double* hsh,
+                              const double* hdm, void* dx, void* dB, float* ddtW, float* rho,
+                              float* eta, float* zeta, double* dend2, double* dA_part,
+                              hipStream_t st);
+
+// Backward, per chunk (one wave): the per-token recurrences and d_dt.
+hipError_t launch_km_scan_bwd(const Shape& s, const double* cdt, const float* dt, const float* A,
+                              const int64_t* valid, const float* ddtW, const float* rho,
+                              const float* eta, const float* zeta, const double* hsh,
+                              const double* hdm, const double* dend2, float* d_dt,
+                              hipStream_t st);
 
 // K4: in place over S: S[i] <- state entering chunk i; final <- state after the last chunk.
 hipError_t launch_k4_pass(const Shape& s, float* S, const double* cdt, const float* A,
@@ -31,9 +76,10 @@ hipError_t launch_k4_pass(const Shape& s, float* S, const double* cdt, const flo
 
 // K4 recompute and its reverse in one pass: S as in launch_k4_pass; in place over dS:
 // dS[i] <- gradient reaching the state that leaves chunk i; d_init <- gradient of init.
+// With forward == false only the reverse carry runs (S untouched).
 hipError_t launch_k4_pass_bwd(const Shape& s, float* S, float* dS, const double* cdt,
                               const float* A, const float* init, const float* d_final,
-                              float* d_init, hipStream_t st);
+                              float* d_init, hipStream_t st, bool forward = true);
 
 // K5: y = BLUE + ORANGE + D x.
 hipError_t launch_k5_scan(const Shape& s, const void* x, const float* dt, const void* Bm,
@@ -67,5 +113,8 @@ hipError_t launch_reduce_heads(const Shape& s, const double* dA_part0, const dou
 
 // dst[i] = src ? src[i] : 0   (i < n)
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t st);
+
+// dst[i] = (vals ? vals[i] : fill) for i < n; the values travel as kernel arguments.
+hipError_t launch_set_i64(int64_t* dst, const int64_t* vals, int64_t fill, int64_t n, hipStream_t st);
 
 }  // namespace ssd

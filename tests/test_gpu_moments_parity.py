@@ -1,0 +1,178 @@
+"""GPU parity of ssd_state_moments / ssd_state_moments_bwd against the CPU oracle.
+
+The oracle pools h_t^T h_t and sum_p h_t[p,:] over the valid tokens of the
+token-by-token recurrence and back-propagates the per-token cotangent; the GPU
+path uses the chunk-parallel closed form.  Per-tensor relative L2 <= 1e-5 (fp32
+inputs) or <= 2e-2 (bf16 inputs); gradients at tokens past valid_len must be
+exactly zero; the optional y / final_state outputs must equal ssd_fwd's bitwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import TOL, compare, rel_l2, say, to_dev
+from mamba_ssd_chunked_amd import inputs, ssd
+
+pytestmark = pytest.mark.gpu
+
+MGRADS = ("d_x", "d_dt", "d_A", "d_B", "d_init")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ssd.load_library()
+
+
+def gpu_moments(inp, valid, use_init=True, use_dm1=True):
+    d = to_dev(inp)
+    init = d["init"] if use_init else None
+    mo = ssd.state_moments(d["x"], d["dt"], d["A"], d["B"], init, valid_len=valid, C=d["C"],
+                           D=d["D"], want_y=True, want_final=True)
+    g = ssd.state_moments_bwd(d["d_m2"], d["x"], d["dt"], d["A"], d["B"], init, valid_len=valid,
+                              d_m1=d["d_m1"] if use_dm1 else None)
+    torch.cuda.synchronize()
+    out = {k: (v.float().cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in mo.items()}
+    out.update({k: v.float().cpu().numpy() for k, v in g.items()})
+    return out
+
+
+def oracle_moments(inp, valid, heads=None, use_init=True, use_dm1=True):
+    def sel(k):
+        v = inp[k].double()
+        if heads is None:
+            return v.numpy()
+        if k in ("x", "B"):
+            return v[:, :, :, heads, :].numpy()
+        if k in ("dt", "init", "d_m2", "d_m1"):
+            return v[:, heads].numpy()
+        return v[heads].numpy()
+    x, dt, A, B, init, dm2, dm1 = (sel(k) for k in ("x", "dt", "A", "B", "init", "d_m2", "d_m1"))
+    init = init if use_init else None
+    dm1 = dm1 if use_dm1 else None
+    m2, m1, count = oracle.state_moments(x, dt, A, B, init, valid)
+    g = oracle.state_moments_bwd(dm2, dm1, x, dt, A, B, init, valid)
+    out = dict(m2=m2, m1=m1, count=count)
+    out.update(g)
+    return out
+
+
+def heads_of(gpu, heads):
+    out = {}
+    for k, v in gpu.items():
+        if k in ("m2", "m1", "d_dt", "d_init", "final_state"):
+            out[k] = v[:, heads]
+        elif k in ("d_x", "d_B", "y"):
+            out[k] = v[:, :, :, heads, :]
+        elif k == "d_A":
+            out[k] = v[heads]
+        else:
+            out[k] = v
+    return out
+
+
+SHAPES = [
+    # batch, seq, nheads, headdim, dstate, chunk_len, io, valid_len
+    (2, 256, 2, 16, 16, 64, "f32", (256, 150)),
+    (1, 384, 3, 32, 64, 128, "f32", (300,)),
+    (2, 512, 2, 64, 128, 256, "f32", (512, 77)),
+    (1, 256, 1, 128, 32, 64, "f32", (193,)),
+    (2, 256, 2, 64, 64, 128, "bf16", (256, 200)),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b%d_s%d_h%d_p%d_r%d_l%d_%s" % s[:7])
+def test_moments_shapes_full(shape):
+    b, seq, h, p, r, l, io, valid = shape
+    w = inputs.custom(batch=b, seq=seq, nheads=h, headdim=p, dstate=r, chunk_len=l, io=io,
+                      init_std=0.3, valid_len=valid, seed=300 + seq + p + r)
+    say(f"case moments {shape}")
+    inp = inputs.make_inputs(w)
+    gpu = gpu_moments(inp, valid)
+    ref = oracle_moments(inp, list(valid))
+    compare(gpu, ref, TOL[io], ("m2", "m1") + MGRADS, f"moments {shape}")
+    assert list(gpu["count"]) == list(ref["count"])
+
+
+def test_moments_workload_sampled_heads():
+    w = inputs.WORKLOADS["moments_valid_len_fp32"]
+    heads = [3]
+    say(f"case moments_valid_len_fp32 full size, heads {heads}")
+    inp = inputs.make_inputs(w)
+    valid = list(w.valid_len)
+    gpu = gpu_moments(inp, valid, use_init=False)
+    ref = oracle_moments(inp, valid, heads=heads, use_init=False)
+    compare(heads_of(gpu, heads), ref, TOL["f32"], ("m2", "m1") + MGRADS, "moments workload")
+    # PR = (tr S)^2 / tr(S^2) of the uncentred covariance, from the GPU moments (fp64 host)
+    S = gpu["m2"].astype(np.float64) / gpu["count"][:, None, None, None]
+    pr = np.einsum("bhrr->bh", S) ** 2 / np.einsum("bhrs,bhrs->bh", S, S)
+    assert np.all(pr >= 1 - 1e-6) and np.all(pr <= w.dstate + 1e-6)
+    So = ref["m2"] / ref["count"][:, None, None, None]
+    pro = np.einsum("bhrr->bh", So) ** 2 / np.einsum("bhrs,bhrs->bh", So, So)
+    assert rel_l2(pr[:, heads], pro) < 1e-5
+
+
+def test_moments_optional_outputs_match_forward_bitwise():
+    w = inputs.custom(batch=2, seq=512, nheads=3, headdim=64, dstate=64, chunk_len=128,
+                      init_std=0.2, seed=41)
+    inp = inputs.make_inputs(w)
+    say("case moments y/final vs ssd_fwd")
+    d = to_dev(inp)
+    mo = ssd.state_moments(d["x"], d["dt"], d["A"], d["B"], d["init"], valid_len=[512, 100],
+                           C=d["C"], D=d["D"], want_y=True, want_final=True)
+    y, fin = ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init"])
+    torch.cuda.synchronize()
+    assert torch.equal(mo["y"], y) and torch.equal(mo["final_state"], fin)
+
+
+def test_moments_gradients_vanish_past_valid_len_and_zero_valid():
+    w = inputs.custom(batch=3, seq=512, nheads=2, headdim=32, dstate=64, chunk_len=128,
+                      init_std=0.2, seed=43)
+    inp = inputs.make_inputs(w)
+    valid = [512, 201, 0]
+    say("case moments masking")
+    gpu = gpu_moments(inp, valid)
+    x = gpu["d_x"].reshape(3, 512, 2, 32)
+    B = gpu["d_B"].reshape(3, 512, 2, 64)
+    assert np.all(x[1, 201:] == 0) and np.all(B[1, 201:] == 0)
+    assert np.all(gpu["d_dt"].reshape(3, 2, 512)[1, :, 201:] == 0)
+    assert np.all(x[2] == 0) and np.all(B[2] == 0) and np.all(gpu["m2"][2] == 0)
+    assert np.any(x[1, :201] != 0)
+    assert list(gpu["count"]) == [512 * 32, 201 * 32, 0]
+    ref = oracle_moments(inp, valid)
+    compare(gpu, ref, TOL["f32"], ("m2", "m1") + MGRADS, "masking")
+
+
+def test_moments_merge_across_calls():
+    """StateMoments::merge: two calls chained through final_state add up to one call."""
+    w = inputs.custom(batch=2, seq=1024, nheads=2, headdim=64, dstate=64, chunk_len=128,
+                      init_std=0.2, seed=47)
+    inp = inputs.make_inputs(w)
+    say("case moments merge")
+    d = to_dev(inp)
+    whole = ssd.state_moments(d["x"], d["dt"], d["A"], d["B"], d["init"])
+    first = ssd.state_moments(d["x"][:, :5].contiguous(), d["dt"][:, :, :5].contiguous(), d["A"],
+                              d["B"][:, :5].contiguous(), d["init"], want_final=True)
+    second = ssd.state_moments(d["x"][:, 5:].contiguous(), d["dt"][:, :, 5:].contiguous(), d["A"],
+                               d["B"][:, 5:].contiguous(), first["final_state"])
+    torch.cuda.synchronize()
+    assert rel_l2((first["m2"] + second["m2"]).cpu().numpy(), whole["m2"].cpu().numpy()) < 1e-5
+    assert rel_l2((first["m1"] + second["m1"]).cpu().numpy(), whole["m1"].cpu().numpy()) < 1e-5
+    assert list((first["count"] + second["count"]).numpy()) == list(whole["count"].numpy())
+
+
+def test_moments_null_d_m1_and_determinism():
+    w = inputs.custom(batch=1, seq=256, nheads=2, headdim=32, dstate=32, chunk_len=64,
+                      init_std=0.2, seed=49)
+    inp = inputs.make_inputs(w)
+    say("case moments null d_m1 / determinism")
+    a = gpu_moments(inp, None, use_dm1=False)
+    z = dict(inp)
+    z["d_m1"] = torch.zeros_like(inp["d_m1"])
+    b = gpu_moments(z, None)
+    c = gpu_moments(z, None)
+    for k in MGRADS:
+        assert np.array_equal(b[k], c[k]), k
+        assert rel_l2(a[k], b[k]) < 1e-6, k
