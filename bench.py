@@ -53,6 +53,19 @@ def kernel_work(w, kernel: str):
     return None, None
 
 
+def moments_kernel_work(w, kernel: str):
+    """Algorithmic flops of one launch of a moments kernel (pairs over the whole chunk)."""
+    b, n, l, h, p, r = w.batch, w.nchunks, w.chunk_len, w.nheads, w.headdim, w.dstate
+    ch = b * n * h
+    if kernel == "km_fwd_rows":    # G tiles (l^2 p) + Z = Q B (l^2 r) + U = B^T Z (l r^2)
+        return (2 * l * l * p + 2 * l * l * r + 2 * l * r * r) * ch
+    if kernel == "km_bwd_rows":    # G, Qb tiles + two pair products + four per-row products
+        return (2 * l * l * p + 2 * l * l * r + 2 * l * l * p + 2 * l * l * r + 8 * l * p * r) * ch
+    if kernel == "km_chunk":       # fwd: H^T V (2 p r^2); bwd: HS, (c2H+T)S (4 p r^2) + BS (2 l r^2)
+        return None
+    return None
+
+
 def method_flops(w):
     """Algorithmic fwd + bwd flops of the method per step (causal triangle only)."""
     b, n, l, h, p, r = w.batch, w.nchunks, w.chunk_len, w.nheads, w.headdim, w.dstate
@@ -94,6 +107,86 @@ def cpu_baseline(w, inp, budget_s: float = 12.0, cap_s: float = 40.0):
                       f"in {t_tot:.1f} s; tokens/s = token-heads/s / {w.nheads} heads"}
 
 
+def bench_moments(args, inp_cache):
+    """ssd_state_moments (with y) + ssd_state_moments_bwd on the moments workload."""
+    import torch
+    from mamba_ssd_chunked_amd import inputs, ssd
+    w = inputs.WORKLOADS["moments_valid_len_fp32"]
+    inp = inputs.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    d = {k: v.to(dev) for k, v in inp.items() if isinstance(v, torch.Tensor) and k != "valid_len"}
+    valid = inp["valid_len"].clone()
+    dims = ssd.dims_of(d["x"], d["B"])
+    m2 = torch.empty_like(d["d_m2"])
+    m1 = torch.empty_like(d["d_m1"])
+    count = torch.empty(w.batch, dtype=torch.int64)
+    y = torch.empty_like(d["x"])
+    gx, gB = torch.empty_like(d["x"]), torch.empty_like(d["B"])
+    gdt, gA = torch.empty_like(d["dt"]), torch.empty_like(d["A"])
+    ginit = torch.empty_like(d["d_final"])
+    ws_f = ssd.workspace(dims, ssd.SSD_OP_MOMENTS, dev)
+    ws_b = ssd.workspace(dims, ssd.SSD_OP_MOMENTS_BWD, dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        rc = ssd.ssd_state_moments(dims, d["x"], d["dt"], d["A"], d["B"], None, valid, m2, m1, count,
+                                   y, d["C"], d["D"], None, ws_f, stream)
+        if rc:
+            raise ssd.SsdError(rc, "ssd_state_moments", ssd.ssd_last_error())
+        rc = ssd.ssd_state_moments_bwd(dims, d["d_m2"], d["d_m1"], d["x"], d["dt"], d["A"], d["B"],
+                                       None, valid, gx, gdt, gA, gB, ginit, ws_b, stream)
+        if rc:
+            raise ssd.SsdError(rc, "ssd_state_moments_bwd", ssd.ssd_last_error())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ssd.ssd_timing_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ssd.ssd_timing_enable(False)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    kt = ssd.ssd_timing_collect()
+    kernels = {}
+    for name, (tot, cnt) in kt.items():
+        avg = tot / cnt
+        ent = {"avg_ms": round(avg, 5), "launches_per_step": cnt / args.steps}
+        work = moments_kernel_work(w, name)
+        if work is None and name in ("k_chunk_states", "k5_chunk_scan", "k1_cumsum", "k4_state_pass",
+                                     "k4_state_pass_bwd"):
+            work, kind = kernel_work(w, name)
+            if kind == "byte":
+                ent.update(gbps=round(work / (avg / 1e3) / 1e9, 1))
+                work = None
+        if work is not None:
+            rate = work / (avg / 1e3)
+            ent.update(tflops=round(rate / 1e12, 2), mfma_frac=round(rate / PEAK_FP32_MFMA, 4))
+        kernels[name] = ent
+    res = {"workload": w.describe(), "ms_per_step": round(ms, 4),
+           "value": round(w.batch * w.seq / (ms / 1e3), 1), "unit": "tokens/s",
+           "step": "ssd_state_moments (with y) + ssd_state_moments_bwd", "kernels": kernels}
+    if not args.no_cpu_baseline:
+        import oracle
+        hs = [0]
+        t0 = time.perf_counter()
+        sl = {k: inp[k][:, :, :, hs].double().numpy() for k in ("x", "B")}
+        dt = inp["dt"][:, hs].double().numpy()
+        A = inp["A"][hs].double().numpy()
+        oracle.state_moments(sl["x"], dt, A, sl["B"], None, list(w.valid_len))
+        oracle.state_moments_bwd(inp["d_m2"][:, hs].double().numpy(), inp["d_m1"][:, hs].double().numpy(),
+                                 sl["x"], dt, A, sl["B"], None, list(w.valid_len))
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(w.batch * w.seq / w.nheads / el, 2), "unit": "tokens/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"moments fwd+bwd of head 0, all {w.batch} batches x {w.seq} "
+                                         f"tokens in {el:.1f} s; tokens/s = token-heads/s / {w.nheads} heads"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +194,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mamba2_130m_fp32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-moments", action="store_true",
+                    help="skip the state-moments leg (moments_valid_len_fp32 workload)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (a plain copy "
                          "kernel of known size, to calibrate HBM byte counters)")
@@ -196,6 +291,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp)
+    if not args.no_moments:
+        out["moments"] = bench_moments(args, inp_cache={})
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, device=dev)

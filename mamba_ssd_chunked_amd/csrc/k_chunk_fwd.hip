@@ -23,9 +23,12 @@
 namespace ssd {
 
 // ------------------------------------------------------------------ K3 / dS
-// One workgroup per (chunk-head, job).  Output [P, R] is split into 16x16 tiles
-// dealt round-robin to the 4 waves; K (tokens) runs over 64-token blocks staged
-// through LDS (U rows as is, V rows pre-scaled by the token weight).
+// One workgroup per (chunk-head, job).  K (tokens) runs over 64-token blocks
+// staged through LDS TRANSPOSED ([feature][token], the V rows pre-scaled by the
+// token weight), so both MFMA operands are float4 reads along the contraction.
+// Output [P, R] in 16x16 tiles: each wave owns whole 16-row p strips (its A
+// operand is read once per k group and reused over all r tiles); with fewer than
+// four p strips the r tiles of a strip are split between waves.
 template <class IO, int P, int R>
 __global__ __launch_bounds__(NT) void k_chunk_states(
     const typename IO::T* __restrict__ x, const typename IO::T* __restrict__ Bm,
@@ -33,8 +36,9 @@ __global__ __launch_bounds__(NT) void k_chunk_states(
     const float* __restrict__ dt, const float* __restrict__ Av, const double* __restrict__ cdt,
     float* __restrict__ S, float* __restrict__ dS, const double* __restrict__ phi,
     float* __restrict__ T, int N, int H, int L, int job0) {
-    __shared__ float sU[TB * (P + 4)];
-    __shared__ float sV[TB * (R + 4)];
+    constexpr int TS = TB + 4;  // token stride of the transposed tiles
+    __shared__ float sU[P * TS];
+    __shared__ float sV[R * TS];
     __shared__ float sw[TB];
     const int job = job0 + static_cast<int>(blockIdx.y);
     const ChunkHead c = decode_ch(blockIdx.x, N, H);
@@ -50,10 +54,18 @@ __global__ __launch_bounds__(NT) void k_chunk_states(
     const double a = static_cast<double>(Av[c.h]);
     const double end = cc[L - 1];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
-    constexpr int NTR = R / 16, NTILE = (P / 16) * NTR, TPW = (NTILE + 3) / 4;
-    v4f acc[TPW];
+    constexpr int NPT = P / 16, NRT = R / 16;
+    constexpr int PPW = NPT >= 4 ? NPT / 4 : 1;          // p strips per wave
+    constexpr int WPS = NPT >= 4 ? 1 : 4 / NPT;          // waves per p strip
+    constexpr int RPW = NRT >= WPS ? NRT / WPS : 1;      // r tiles per wave
+    const int pt0 = NPT >= 4 ? wave : wave / WPS;
+    const int rt0 = (NPT >= 4 ? 0 : wave % WPS) * RPW;
+    const bool active = rt0 < NRT;
+    v4f acc[PPW][RPW];
 #pragma unroll
-    for (int q = 0; q < TPW; ++q) acc[q] = zero4();
+    for (int q = 0; q < PPW; ++q)
+#pragma unroll
+        for (int k = 0; k < RPW; ++k) acc[q][k] = zero4();
 
     for (int t0 = 0; t0 < L; t0 += TB) {
         if (tid < TB) {
@@ -64,42 +76,49 @@ __global__ __launch_bounds__(NT) void k_chunk_states(
                                                       phi[c.c_bhn * L + t]);
         }
         __syncthreads();
-        stage_rows<IO, P>(sU, U + urow0 + t0 * ustride, ustride);
         {
+            constexpr int UU = P / 4;
+            for (int idx = tid; idx < TB * UU; idx += NT) {
+                const int row = idx / UU, c4 = idx - (idx / UU) * UU;
+                const v4f v = io<IO>::ld4(U, urow0 + (t0 + row) * ustride + c4 * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sU[(c4 * 4 + e) * TS + row] = v[e];
+            }
             constexpr int VV = R / 4;
             for (int idx = tid; idx < TB * VV; idx += NT) {
                 const int row = idx / VV, c4 = idx - (idx / VV) * VV;
-                v4f v = io<IO>::ld4(V, vrow0 + (t0 + row) * vstride + c4 * 4);
-                v *= sw[row];
-                *reinterpret_cast<v4f*>(sV + row * (R + 4) + c4 * 4) = v;
+                const v4f v = io<IO>::ld4(V, vrow0 + (t0 + row) * vstride + c4 * 4) * sw[row];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sV[(c4 * 4 + e) * TS + row] = v[e];
             }
         }
         __syncthreads();
+        if (active) {
 #pragma unroll
-        for (int q = 0; q < TPW; ++q) {
-            const int tile = wave + 4 * q;
-            if (tile < NTILE) {
-                const int pt = tile / NTR, rt = tile - (tile / NTR) * NTR;
+            for (int kk = 0; kk < 4; ++kk) {
+                v4f av[PPW];
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
+                for (int q = 0; q < PPW; ++q)
+                    av[q] = *reinterpret_cast<const v4f*>(sU + ((pt0 + 4 * q) * 16 + i) * TS + 16 * kk + 4 * g);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int t = 16 * kk + 4 * g + v;
-                        acc[q] = mfma16(sU[t * (P + 4) + pt * 16 + i], sV[t * (R + 4) + rt * 16 + i],
-                                        acc[q]);
-                    }
+                for (int k = 0; k < RPW; ++k) {
+                    const v4f bv = *reinterpret_cast<const v4f*>(sV + ((rt0 + k) * 16 + i) * TS + 16 * kk + 4 * g);
+#pragma unroll
+                    for (int q = 0; q < PPW; ++q)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[q][k] = mfma16(av[q][v], bv[v], acc[q][k]);
                 }
             }
         }
     }
+    if (active) {
 #pragma unroll
-    for (int q = 0; q < TPW; ++q) {
-        const int tile = wave + 4 * q;
-        if (tile < NTILE) {
-            const int pt = tile / NTR, rt = tile - (tile / NTR) * NTR;
+        for (int q = 0; q < PPW; ++q)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) out[(pt * 16 + 4 * g + v) * R + rt * 16 + i] = acc[q][v];
-        }
+            for (int k = 0; k < RPW; ++k)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    out[((pt0 + 4 * q) * 16 + 4 * g + v) * R + (rt0 + k) * 16 + i] = acc[q][k][v];
     }
 }
 

@@ -427,41 +427,50 @@ __global__ __launch_bounds__(NT) void km_chunk(
 }
 
 // ------------------------------------------------------------------- reduce
-// m2[b,h] = (Z + Z^T)/2 with Z = sum over chunks and blocks of U and W;
-// m1[b,h] = sum of the m1 parts.  Fixed summation order.
-__global__ __launch_bounds__(NT) void km_reduce(const float* __restrict__ U,
-                                                 const float* __restrict__ W,
-                                                 const float* __restrict__ m1b,
-                                                 const float* __restrict__ m1c,
-                                                 float* __restrict__ m2, float* __restrict__ m1,
-                                                 int N, int H, int R, int nblk) {
+// m2[b,h] = (Z + Z^T)/2 with Z = sum over chunks (and blocks) of U and W;
+// m1[b,h] = sum of the m1 parts.  First a coalesced sum (one thread per output
+// element, fixed order over the partials) written into m2/m1, then an in-place
+// symmetrisation (one thread per pair r1 < r2).
+__global__ __launch_bounds__(NT) void km_reduce_sum(const float* __restrict__ U,
+                                                     const float* __restrict__ W,
+                                                     const float* __restrict__ m1b,
+                                                     const float* __restrict__ m1c,
+                                                     float* __restrict__ m2, float* __restrict__ m1,
+                                                     int N, int H, int R, int nblk) {
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / H, h = bh - (bh / H) * H;
     const int RR = R * R;
-    for (int idx = threadIdx.x; idx < RR; idx += NT) {
-        const int r1 = idx / R, r2 = idx - (idx / R) * R;
-        const int tr = r2 * R + r1;
+    const int idx = blockIdx.y * NT + threadIdx.x;
+    if (idx < RR) {
         double acc = 0.0;
         for (int n = 0; n < N; ++n) {
             const int64_t ch = (b * N + n) * H + h;
-            for (int k = 0; k < nblk; ++k) {
-                const float* u = U + (ch * nblk + k) * RR;
-                acc += static_cast<double>(u[idx]) + static_cast<double>(u[tr]);
-            }
-            const float* w = W + ch * RR;
-            acc += static_cast<double>(w[idx]) + static_cast<double>(w[tr]);
+            for (int k = 0; k < nblk; ++k) acc += static_cast<double>(U[(ch * nblk + k) * RR + idx]);
+            acc += static_cast<double>(W[ch * RR + idx]);
         }
-        m2[bh * RR + idx] = static_cast<float>(0.5 * acc);
-    }
-    for (int r = threadIdx.x; r < R; r += NT) {
+        m2[bh * RR + idx] = static_cast<float>(acc);
+    } else if (idx < RR + R) {
+        const int r = idx - RR;
         double acc = 0.0;
         for (int n = 0; n < N; ++n) {
             const int64_t ch = (b * N + n) * H + h;
-            for (int k = 0; k < nblk; ++k) acc += m1b[(ch * nblk + k) * R + r];
-            acc += m1c[ch * R + r];
+            for (int k = 0; k < nblk; ++k) acc += static_cast<double>(m1b[(ch * nblk + k) * R + r]);
+            acc += static_cast<double>(m1c[ch * R + r]);
         }
         m1[bh * R + r] = static_cast<float>(acc);
     }
+}
+
+__global__ __launch_bounds__(NT) void km_symmetrise(float* __restrict__ m2, int R) {
+    const int64_t bh = blockIdx.x;
+    const int idx = blockIdx.y * NT + threadIdx.x;
+    if (idx >= R * R) return;
+    const int r1 = idx / R, r2 = idx - (idx / R) * R;
+    if (r1 >= r2) return;
+    float* m = m2 + bh * R * R;
+    const float avg = 0.5f * (m[r1 * R + r2] + m[r2 * R + r1]);
+    m[r1 * R + r2] = avg;
+    m[r2 * R + r1] = avg;
 }
 
 // ----------------------------------------------------------- backward rows
@@ -871,8 +880,14 @@ hipError_t launch_km_reduce(const Shape& s, const float* U, const float* W, cons
                             const float* m1c, float* m2, float* m1, hipStream_t st) {
     const int64_t BH = static_cast<int64_t>(s.B) * s.H;
     if (BH == 0) return hipSuccess;
-    hipLaunchKernelGGL(km_reduce, dim3(static_cast<unsigned>(BH)), dim3(NT), 0, st, U, W, m1b, m1c,
-                       m2, m1, s.N, s.H, s.R, s.nblk());
+    const int RR = s.R * s.R;
+    hipLaunchKernelGGL(km_reduce_sum, dim3(static_cast<unsigned>(BH),
+                                           static_cast<unsigned>((RR + s.R + NT - 1) / NT)),
+                       dim3(NT), 0, st, U, W, m1b, m1c, m2, m1, s.N, s.H, s.R, s.nblk());
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(km_symmetrise, dim3(static_cast<unsigned>(BH), static_cast<unsigned>((RR + NT - 1) / NT)),
+                       dim3(NT), 0, st, m2, s.R);
     return hipGetLastError();
 }
 
