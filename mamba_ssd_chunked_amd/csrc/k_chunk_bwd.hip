@@ -56,7 +56,7 @@
 namespace ssd {
 
 template <class IO, int P, int R>
-__global__ __launch_bounds__(NT) void k_bwd_target(
+__global__ __launch_bounds__(NT, 2) void k_bwd_target(
     const typename IO::T* __restrict__ dy, const typename IO::T* __restrict__ x,
     const float* __restrict__ dt, const typename IO::T* __restrict__ Bm,
     const typename IO::T* __restrict__ Cm, const float* __restrict__ Av,
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(NT) void k_bwd_target(
 #pragma unroll
         for (int kk = 0; kk < P / 16; ++kk) dyreg[kk] = io<IO>::ld4(dy, yrow + 16 * kk + 4 * g);
     }
-    stage_mat<R>(sBS, S + c.ch * (P * R), P);
+    stage_mat<R, P>(sBS, S + c.ch * (P * R));
     if (tid < TB) sCdtT[tid] = cc[tb * TB + tid];
     __syncthreads();
 
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(NT) void k_bwd_target(
 }
 
 template <class IO, int P, int R>
-__global__ __launch_bounds__(NT) void k_bwd_source(
+__global__ __launch_bounds__(NT, 2) void k_bwd_source(
     const typename IO::T* __restrict__ dy, const typename IO::T* __restrict__ x,
     const float* __restrict__ dt, const typename IO::T* __restrict__ Bm,
     const typename IO::T* __restrict__ Cm, const float* __restrict__ Av,
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(NT) void k_bwd_source(
     for (int kk = 0; kk < P / 16; ++kk) xreg[kk] = io<IO>::ld4(x, xrow + 16 * kk + 4 * g);
 #pragma unroll
     for (int kk = 0; kk < R / 16; ++kk) breg[kk] = io<IO>::ld4(Bm, brow + 16 * kk + 4 * g);
-    stage_mat<R>(sCT, dS + c.ch * (P * R), P);
+    stage_mat<R, P>(sCT, dS + c.ch * (P * R));
     const double end = cc[L - 1];
     const double cs = cc[spos];
     const float dts = dtc[spos];

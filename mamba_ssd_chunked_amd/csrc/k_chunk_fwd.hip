@@ -76,22 +76,8 @@ __global__ __launch_bounds__(NT) void k_chunk_states(
                                                       phi[c.c_bhn * L + t]);
         }
         __syncthreads();
-        {
-            constexpr int UU = P / 4;
-            for (int idx = tid; idx < TB * UU; idx += NT) {
-                const int row = idx / UU, c4 = idx - (idx / UU) * UU;
-                const v4f v = io<IO>::ld4(U, urow0 + (t0 + row) * ustride + c4 * 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sU[(c4 * 4 + e) * TS + row] = v[e];
-            }
-            constexpr int VV = R / 4;
-            for (int idx = tid; idx < TB * VV; idx += NT) {
-                const int row = idx / VV, c4 = idx - (idx / VV) * VV;
-                const v4f v = io<IO>::ld4(V, vrow0 + (t0 + row) * vstride + c4 * 4) * sw[row];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sV[(c4 * 4 + e) * TS + row] = v[e];
-            }
-        }
+        stage_rows_t<IO, P>(sU, U + urow0 + t0 * ustride, ustride, nullptr);
+        stage_rows_t<IO, R>(sV, V + vrow0 + t0 * vstride, vstride, sw);
         __syncthreads();
         if (active) {
 #pragma unroll
@@ -132,7 +118,7 @@ __global__ __launch_bounds__(NT) void k_chunk_states(
 //           acc[t, p] += sum_s W[t,s] x[s,p]  (the W registers are the A operand).
 //   y = acc + D x.
 template <class IO, int P, int R>
-__global__ __launch_bounds__(NT) void k5_chunk_scan(
+__global__ __launch_bounds__(NT, 2) void k5_chunk_scan(
     const typename IO::T* __restrict__ x, const float* __restrict__ dt,
     const typename IO::T* __restrict__ Bm, const typename IO::T* __restrict__ Cm,
     const float* __restrict__ Av, const float* __restrict__ Dv, const double* __restrict__ cdt,
@@ -162,7 +148,7 @@ __global__ __launch_bounds__(NT) void k5_chunk_scan(
 #pragma unroll
         for (int kk = 0; kk < R / 16; ++kk) creg[kk] = io<IO>::ld4(Cm, row + 16 * kk + 4 * g);
     }
-    stage_mat<R>(sBS, S + c.ch * (P * R), P);
+    stage_mat<R, P>(sBS, S + c.ch * (P * R));
     if (tid < TB) sCumT[tid] = cc[tb * TB + tid];
     __syncthreads();
 

@@ -170,7 +170,7 @@ hipError_t launch_km_phi(const Shape& s, const double* cdt, const float* A, cons
 //   U_blk   = sum_{s in block} B_s Z_s^T      (r x r, written as a partial)
 //   m1_blk  = sum_{s in block} u_s (1^T x_s) B_s
 template <class IO, int P, int R>
-__global__ __launch_bounds__(NT) void km_fwd_rows(
+__global__ __launch_bounds__(NT, 2) void km_fwd_rows(
     const typename IO::T* __restrict__ x, const typename IO::T* __restrict__ Bm,
     const float* __restrict__ dt, const float* __restrict__ Av, const double* __restrict__ cdt,
     const double* __restrict__ phi, const double* __restrict__ psi, float* __restrict__ U,
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(NT) void km_bwd_rows(
     v4f accX[P / 16], accB[R / 16];
     float eta_s = 0.f, xdb = 0.f;
     // phase 1a: HS terms
-    stage_mat<R>(sM, HS + c.ch * (P * R), P);
+    stage_mat<R, P>(sM, HS + c.ch * (P * R));
     __syncthreads();
     {
         v4f t[P / 16];
@@ -584,7 +584,7 @@ __global__ __launch_bounds__(NT) void km_bwd_rows(
     }
     __syncthreads();
     // phase 1b: d_intra (the carried gradient of the chunk's last state) terms
-    stage_mat<R>(sM, dI + c.ch * (P * R), P);
+    stage_mat<R, P>(sM, dI + c.ch * (P * R));
     __syncthreads();
     {
         v4f t[P / 16];
@@ -657,7 +657,7 @@ __global__ __launch_bounds__(NT) void km_bwd_rows(
     for (int b2 = 0; b2 < nblk; ++b2) {
         __syncthreads();
         stage_rows<IO, P>(sX, x + xrow0 + static_cast<int64_t>(b2 * TB) * xstride, xstride);
-        stage_mat<R>(sQ, BS + (c.ch * L + b2 * TB) * static_cast<int64_t>(R), TB);
+        stage_mat<R, TB>(sQ, BS + (c.ch * L + b2 * TB) * static_cast<int64_t>(R));
         if (tid < TB) {
             sC[tid] = cc[b2 * TB + tid];
             sPhi[tid] = ph[b2 * TB + tid];

@@ -102,31 +102,60 @@ __device__ __forceinline__ ChunkHead decode_ch(int64_t ch, int N, int H) {
     return c;
 }
 
-// Stage TB token rows of width W (io dtype in global, row stride gstride
-// elements) into LDS as fp32 rows of stride W + 4.
-template <class IO, int W>
+// Stage ROWS rows of width W (io dtype in global, row stride gstride elements)
+// into LDS as fp32 rows of stride W + 4.  All global loads of a thread are
+// issued before its first LDS write, so the block waits for memory once.
+template <class IO, int W, int ROWS = TB>
 __device__ __forceinline__ void stage_rows(float* lds, const typename IO::T* g, int64_t gstride) {
-    constexpr int V = W / 4;
-    for (int idx = threadIdx.x; idx < TB * V; idx += NT) {
-        const int row = idx / V, c4 = idx - (idx / V) * V;
-        v4f v = io<IO>::ld4(g, static_cast<size_t>(row) * gstride + c4 * 4);
-        *reinterpret_cast<v4f*>(lds + row * (W + 4) + c4 * 4) = v;
+    constexpr int V = W / 4, TOTAL = ROWS * V, IT = (TOTAL + NT - 1) / NT;
+    constexpr int BATCH = IT < 4 ? IT : 4;  // at most 4 float4 in flight per thread
+#pragma unroll
+    for (int b0 = 0; b0 < IT; b0 += BATCH) {
+        v4f tmp[BATCH];
+#pragma unroll
+        for (int it = 0; it < BATCH; ++it) {
+            const int idx = static_cast<int>(threadIdx.x) + (b0 + it) * NT;
+            if (b0 + it < IT && (TOTAL % NT == 0 || idx < TOTAL))
+                tmp[it] = io<IO>::ld4(g, static_cast<int64_t>(idx / V) * gstride + (idx % V) * 4);
+        }
+#pragma unroll
+        for (int it = 0; it < BATCH; ++it) {
+            const int idx = static_cast<int>(threadIdx.x) + (b0 + it) * NT;
+            if (b0 + it < IT && (TOTAL % NT == 0 || idx < TOTAL))
+                *reinterpret_cast<v4f*>(lds + (idx / V) * (W + 4) + (idx % V) * 4) = tmp[it];
+        }
     }
 }
 
-// Stage a contiguous fp32 [rows, W] matrix into LDS rows of stride W + 4.
-template <int W>
-__device__ __forceinline__ void stage_mat(float* lds, const float* g, int rows) {
-    constexpr int V = W / 4;
-    for (int idx = threadIdx.x; idx < rows * V; idx += NT) {
-        const int row = idx / V, c4 = idx - (idx / V) * V;
-        v4f v = *reinterpret_cast<const v4f*>(g + static_cast<size_t>(row) * W + c4 * 4);
-        *reinterpret_cast<v4f*>(lds + row * (W + 4) + c4 * 4) = v;
-    }
+// Stage a contiguous fp32 [ROWS, W] matrix into LDS rows of stride W + 4.
+template <int W, int ROWS>
+__device__ __forceinline__ void stage_mat(float* lds, const float* g) {
+    stage_rows<F32, W, ROWS>(lds, g, W);
 }
 
-__device__ __forceinline__ float lds4(const float* base, int idx, int v) {
-    return base[idx + v];
+// Stage TB token rows of width W transposed: lds[f * (TB + 4) + t] = scale[t] * g[t, f]
+// (scale may be null).
+template <class IO, int W>
+__device__ __forceinline__ void stage_rows_t(float* lds, const typename IO::T* g, int64_t gstride,
+                                             const float* scale) {
+    constexpr int V = W / 4, TOTAL = TB * V, IT = (TOTAL + NT - 1) / NT;
+    v4f tmp[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int idx = static_cast<int>(threadIdx.x) + it * NT;
+        if (TOTAL % NT == 0 || idx < TOTAL)
+            tmp[it] = io<IO>::ld4(g, static_cast<int64_t>(idx / V) * gstride + (idx % V) * 4);
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int idx = static_cast<int>(threadIdx.x) + it * NT;
+        if (TOTAL % NT == 0 || idx < TOTAL) {
+            const int row = idx / V, c4 = idx % V;
+            const v4f v = scale ? tmp[it] * scale[row] : tmp[it];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) lds[(c4 * 4 + e) * (TB + 4) + row] = v[e];
+        }
+    }
 }
 
 // Sum over the four lane groups g = 0..3 that share i = lane % 16.
