@@ -134,23 +134,31 @@ __device__ __forceinline__ void stage_mat(float* lds, const float* g) {
 }
 
 // Stage TB token rows of width W transposed: lds[f * (TB + 4) + t] = scale[t] * g[t, f]
-// (scale may be null).
+// (scale may be null).  Element (row t, float4 column c4) is handled by linear
+// index idx with t % 16 = idx % 16, c4 % 4 = (idx / 16) % 4, t / 16 = (idx / 64) % 4,
+// c4 / 4 = idx / 256: one 64-lane store then covers 16 rows x 4 columns, i.e.
+// 64 distinct LDS banks (the token stride TB + 4 shifts each column by 4 banks),
+// and every row is still read as a 64-byte segment.
 template <class IO, int W>
 __device__ __forceinline__ void stage_rows_t(float* lds, const typename IO::T* g, int64_t gstride,
                                              const float* scale) {
     constexpr int V = W / 4, TOTAL = TB * V, IT = (TOTAL + NT - 1) / NT;
+    constexpr int CL = V < 4 ? V : 4;  // float4 columns per 64-lane group
     v4f tmp[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int idx = static_cast<int>(threadIdx.x) + it * NT;
+        const int row = (idx & 15) + 16 * ((idx / (16 * CL)) & 3);
+        const int c4 = (idx / 16) % CL + CL * (idx / (64 * CL));
         if (TOTAL % NT == 0 || idx < TOTAL)
-            tmp[it] = io<IO>::ld4(g, static_cast<int64_t>(idx / V) * gstride + (idx % V) * 4);
+            tmp[it] = io<IO>::ld4(g, static_cast<int64_t>(row) * gstride + c4 * 4);
     }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int idx = static_cast<int>(threadIdx.x) + it * NT;
+        const int row = (idx & 15) + 16 * ((idx / (16 * CL)) & 3);
+        const int c4 = (idx / 16) % CL + CL * (idx / (64 * CL));
         if (TOTAL % NT == 0 || idx < TOTAL) {
-            const int row = idx / V, c4 = idx % V;
             const v4f v = scale ? tmp[it] * scale[row] : tmp[it];
 #pragma unroll
             for (int e = 0; e < 4; ++e) lds[(c4 * 4 + e) * (TB + 4) + row] = v[e];
