@@ -181,7 +181,8 @@ hipEvent_t pool_event() {
         return e;
     }
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    // timing-only events: no system-scope fence (cache write-back) at each record
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
 }
 
