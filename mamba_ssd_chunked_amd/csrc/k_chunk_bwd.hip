@@ -67,8 +67,9 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target(
     constexpr int ROWS = P > TB ? P : TB;
     __shared__ float sBS[ROWS * RS];  // S_in [P, R], then B of the source block
     __shared__ float sX[TB * PS];
-    __shared__ double sCdtT[TB], sCdtS[TB];
-    __shared__ float sDt[TB];
+    __shared__ __align__(16) double sCdtT[TB];
+    __shared__ __align__(16) double sCdtS[TB];
+    __shared__ __align__(16) float sDt[TB];
     __shared__ double sRed[NT / 64];
     const int nblk = L / TB;
     const int tb = nblk - 1 - static_cast<int>(blockIdx.x / CH);  // heaviest first
@@ -81,6 +82,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target(
     const double* cc = cdt + c.c_bhn * L;
     const float* dtc = dt + c.c_bhn * L;
     const double a = static_cast<double>(Av[c.h]);
+    const double la2 = a * kLog2e;
     const int tl = 16 * wave + i;  // target row of this lane inside the block
 
     v4f creg[R / 16], dyreg[P / 16];
@@ -154,8 +156,10 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target(
             sDt[tid] = dtc[sb * TB + tid];
         }
         __syncthreads();
-        const int jmax = (sb == tb) ? wave : 3;
-        for (int j = 0; j <= jmax; ++j) {
+        const int jmax = (sb == tb) ? wave : 3;  // diagonal block: s-tiles up to this wave's
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j > jmax) break;
             // tiles with M = s (16j + 4g + v), N = t (tl)
             v4f cbt = zero4(), dwt = zero4();
 #pragma unroll
@@ -170,14 +174,19 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target(
 #pragma unroll
                 for (int v = 0; v < 4; ++v) dwt = mfma16(u[v], dyreg[kk][v], dwt);
             }
+            // this lane's four source rows: cumsums and dt as 16-byte LDS reads
+            const v2d cs01 = *reinterpret_cast<const v2d*>(sCdtS + 16 * j + 4 * g);
+            const v2d cs23 = *reinterpret_cast<const v2d*>(sCdtS + 16 * j + 4 * g + 2);
+            const v4f dts = *reinterpret_cast<const v4f*>(sDt + 16 * j + 4 * g);
+            const double csv[4] = {cs01.x, cs01.y, cs23.x, cs23.y};
             float dcb[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int s_ = 16 * j + 4 * g + v;
-                const bool keep = (sb < tb) || (s_ <= tl);
-                const double gap = ct - sCdtS[s_];
-                const float dec = keep ? expf(static_cast<float>(a * gap)) : 0.0f;
-                dcb[v] = dwt[v] * sDt[s_] * dec;
+                const bool keep = (sb < tb) || (16 * j + 4 * g + v <= tl);
+                const double gap = ct - csv[v];
+                const float e = exp2_of(la2 * gap);  // masked pairs: gap < 0, discarded below
+                const float dec = keep ? e : 0.0f;
+                dcb[v] = dwt[v] * dts[v] * dec;
                 const float ddiff = dcb[v] * cbt[v];
                 gsum += ddiff;
                 dA += static_cast<double>(ddiff) * gap;
@@ -220,7 +229,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     constexpr int ROWS = P > TB ? P : TB;
     __shared__ float sCT[ROWS * RS];  // d_intra [P, R], then C of the target block
     __shared__ float sDY[TB * PS];
-    __shared__ double sCdtT[TB];
+    __shared__ __align__(16) double sCdtT[TB];
     __shared__ double sRed[2 * (NT / 64)];
     const int nblk = L / TB;
     const int sb = static_cast<int>(blockIdx.x / CH);  // block 0 has the most targets
@@ -233,6 +242,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     const double* cc = cdt + c.c_bhn * L;
     const float* dtc = dt + c.c_bhn * L;
     const double a = static_cast<double>(Av[c.h]);
+    const double la2 = a * kLog2e;
     const int sl = 16 * wave + i;   // source row of this lane inside the block
     const int spos = sb * TB + sl;  // ... inside the chunk
 
@@ -302,7 +312,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
         stage_rows<IO, P>(sDY, dy + xrow0 + static_cast<int64_t>(tb * TB) * xstride, xstride);
         if (tid < TB) sCdtT[tid] = cc[tb * TB + tid];
         __syncthreads();
-        const int jmin = (tb == sb) ? wave : 0;
+        const int jmin = (tb == sb) ? wave : 0;  // diagonal block: t-tiles from this wave's on
         for (int j = jmin; j < 4; ++j) {
             // tiles with M = t (16j + 4g + v), N = s (sl)
             v4f cb = zero4(), dw = zero4();
@@ -318,12 +328,16 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
 #pragma unroll
                 for (int v = 0; v < 4; ++v) dw = mfma16(u[v], xreg[kk][v], dw);
             }
+            // this lane's four target rows: cumsums as two 16-byte LDS reads
+            const v2d ct01 = *reinterpret_cast<const v2d*>(sCdtT + 16 * j + 4 * g);
+            const v2d ct23 = *reinterpret_cast<const v2d*>(sCdtT + 16 * j + 4 * g + 2);
+            const double ctv[4] = {ct01.x, ct01.y, ct23.x, ct23.y};
             float wv[4], dcb[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int t = 16 * j + 4 * g + v;
-                const bool keep = (tb > sb) || (t >= sl);
-                const float dec = keep ? expf(static_cast<float>(a * (sCdtT[t] - cs))) : 0.0f;
+                const bool keep = (tb > sb) || (16 * j + 4 * g + v >= sl);
+                const float e = exp2_of(la2 * (ctv[v] - cs));  // masked pairs discarded below
+                const float dec = keep ? e : 0.0f;
                 const float cbd = cb[v] * dec;
                 wv[v] = cbd * dts;
                 dcb[v] = dw[v] * dts * dec;

@@ -127,8 +127,9 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan(
     constexpr int ROWS = P > TB ? P : TB;
     __shared__ float sBS[ROWS * RS];  // S_in [P, R] for BLUE, then B of the source block
     __shared__ float sX[TB * PS];
-    __shared__ double sCumT[TB], sCumS[TB];
-    __shared__ float sDt[TB];
+    __shared__ double sCumT[TB];
+    __shared__ __align__(16) double sCumS[TB];
+    __shared__ __align__(16) float sDt[TB];
     const int nblk = L / TB;
     const int tb = nblk - 1 - static_cast<int>(blockIdx.x / CH);  // heaviest blocks first
     const ChunkHead c = decode_ch(blockIdx.x % CH, N, H);
@@ -173,6 +174,7 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan(
     }
 
     const double ct = sCumT[tl];
+    const double la2 = a * kLog2e;
     for (int sb = 0; sb <= tb; ++sb) {
         __syncthreads();
         stage_rows<IO, R>(sBS, Bm + brow0 + static_cast<int64_t>(sb * TB) * bstride, bstride);
@@ -182,8 +184,10 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan(
             sDt[tid] = dtc[sb * TB + tid];
         }
         __syncthreads();
-        const int jmax = (sb == tb) ? wave : 3;
-        for (int j = 0; j <= jmax; ++j) {
+        const int jmax = (sb == tb) ? wave : 3;  // diagonal block: s-tiles up to this wave's
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j > jmax) break;
             v4f cbt = zero4();
 #pragma unroll
             for (int kk = 0; kk < R / 16; ++kk) {
@@ -191,12 +195,17 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan(
 #pragma unroll
                 for (int v = 0; v < 4; ++v) cbt = mfma16(aop[v], creg[kk][v], cbt);
             }
+            // this lane's four source rows: cumsums and dt as 16-byte LDS reads
+            const v2d cs01 = *reinterpret_cast<const v2d*>(sCumS + 16 * j + 4 * g);
+            const v2d cs23 = *reinterpret_cast<const v2d*>(sCumS + 16 * j + 4 * g + 2);
+            const v4f dts = *reinterpret_cast<const v4f*>(sDt + 16 * j + 4 * g);
+            const double csv[4] = {cs01.x, cs01.y, cs23.x, cs23.y};
             float wv[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int s = 16 * j + 4 * g + v;
-                const bool keep = (sb < tb) || (s <= tl);
-                wv[v] = keep ? cbt[v] * expf(static_cast<float>(a * (ct - sCumS[s]))) * sDt[s] : 0.0f;
+                const bool keep = (sb < tb) || (16 * j + 4 * g + v <= tl);
+                const float e = exp2_of(la2 * (ct - csv[v]));  // masked pairs discarded below
+                wv[v] = keep ? cbt[v] * e * dts[v] : 0.0f;
             }
 #pragma unroll
             for (int pt = 0; pt < P / 16; ++pt) {

@@ -27,6 +27,17 @@ __device__ __forceinline__ v4f mfma16(float a, float b, v4f c) {
 
 __device__ __forceinline__ v4f zero4() { return v4f{0.f, 0.f, 0.f, 0.f}; }
 
+typedef double v2d __attribute__((ext_vector_type(2)));
+
+// Decay factors exp(a * gap), gap an fp64 difference of cumulative sums of dt:
+// the caller forms the base-2 exponent (a log2 e) * gap in fp64; it is rounded
+// once to fp32 and raised with the hardware base-2 exponential (v_exp_f32,
+// about 1 ulp).  Results below the fp32 range flush to 0.
+constexpr double kLog2e = 1.4426950408889634;
+__device__ __forceinline__ float exp2_of(double e2) {
+    return __builtin_amdgcn_exp2f(static_cast<float>(e2));
+}
+
 // ------------------------------------------------------------------ io types
 struct F32 {
     using T = float;
