@@ -149,11 +149,17 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target(
 
     for (int sb = 0; sb <= tb; ++sb) {
         __syncthreads();
-        stage_rows<IO, R>(sBS, Bm + brow0 + static_cast<int64_t>(sb * TB) * bstride, bstride);
-        stage_rows<IO, P>(sX, x + xrow0 + static_cast<int64_t>(sb * TB) * xstride, xstride);
+        double cnext = 0.0;
+        float dnext = 0.0f;
         if (tid < TB) {
-            sCdtS[tid] = cc[sb * TB + tid];
-            sDt[tid] = dtc[sb * TB + tid];
+            cnext = cc[sb * TB + tid];
+            dnext = dtc[sb * TB + tid];
+        }
+        stage_rows2<IO, R, P>(sBS, Bm + brow0 + static_cast<int64_t>(sb * TB) * bstride, bstride,
+                              sX, x + xrow0 + static_cast<int64_t>(sb * TB) * xstride, xstride);
+        if (tid < TB) {
+            sCdtS[tid] = cnext;
+            sDt[tid] = dnext;
         }
         __syncthreads();
         const int jmax = (sb == tb) ? wave : 3;  // diagonal block: s-tiles up to this wave's
@@ -308,9 +314,10 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     float ddt_or = 0.0f, dsrc = 0.0f;
     for (int tb = sb; tb < nblk; ++tb) {
         __syncthreads();
+        const double cnext = tid < TB ? cc[tb * TB + tid] : 0.0;
         stage_rows<IO, R>(sCT, Cm + brow0 + static_cast<int64_t>(tb * TB) * bstride, bstride);
         stage_rows<IO, P>(sDY, dy + xrow0 + static_cast<int64_t>(tb * TB) * xstride, xstride);
-        if (tid < TB) sCdtT[tid] = cc[tb * TB + tid];
+        if (tid < TB) sCdtT[tid] = cnext;
         __syncthreads();
         const int jmin = (tb == sb) ? wave : 0;  // diagonal block: t-tiles from this wave's on
         for (int j = jmin; j < 4; ++j) {

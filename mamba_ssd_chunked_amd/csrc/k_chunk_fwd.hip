@@ -177,11 +177,17 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan(
     const double la2 = a * kLog2e;
     for (int sb = 0; sb <= tb; ++sb) {
         __syncthreads();
-        stage_rows<IO, R>(sBS, Bm + brow0 + static_cast<int64_t>(sb * TB) * bstride, bstride);
-        stage_rows<IO, P>(sX, x + xrow0 + static_cast<int64_t>(sb * TB) * xstride, xstride);
+        double cnext = 0.0;
+        float dnext = 0.0f;
         if (tid < TB) {
-            sCumS[tid] = cc[sb * TB + tid];
-            sDt[tid] = dtc[sb * TB + tid];
+            cnext = cc[sb * TB + tid];
+            dnext = dtc[sb * TB + tid];
+        }
+        stage_rows2<IO, R, P>(sBS, Bm + brow0 + static_cast<int64_t>(sb * TB) * bstride, bstride,
+                              sX, x + xrow0 + static_cast<int64_t>(sb * TB) * xstride, xstride);
+        if (tid < TB) {
+            sCumS[tid] = cnext;
+            sDt[tid] = dnext;
         }
         __syncthreads();
         const int jmax = (sb == tb) ? wave : 3;  // diagonal block: s-tiles up to this wave's

@@ -193,6 +193,7 @@ __global__ __launch_bounds__(NT, 2) void km_fwd_rows(
     const double* ph = phi + c.c_bhn * L;
     const float* dtc = dt + c.c_bhn * L;
     const double a = static_cast<double>(Av[c.h]);
+    const double la2 = a * kLog2e;
     const int sl = 16 * wave + i, spos = sb * TB + sl;
 
     v4f xreg[P / 16];
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(NT, 2) void km_fwd_rows(
                 const bool pm = ppos >= spos;               // partner is the later one
                 const double gap = pm ? cp - cs : cs - cp;
                 const double phm = pm ? sPhi[sp] : phs;
-                const float kv = static_cast<float>(static_cast<double>(dts) * sDt[sp] * exp(a * gap) * phm);
+                const float kv = dts * sDt[sp] * exp2_of(la2 * gap) * static_cast<float>(phm);
                 q[v] = kv * gt[v];
             }
             // Z[s, r] += sum_{s'} Q[s, s'] B[s', r]
@@ -506,6 +507,7 @@ __global__ __launch_bounds__(NT) void km_bwd_rows(
     const double* ph = phi + c.c_bhn * L;
     const float* dtc = dt + c.c_bhn * L;
     const double a = static_cast<double>(Av[c.h]);
+    const double la2 = a * kLog2e;
     const int sl = 16 * wave + i, spos = sb * TB + sl;
     const int64_t bh = static_cast<int64_t>(c.b) * H + c.h;
 
@@ -689,17 +691,17 @@ __global__ __launch_bounds__(NT) void km_bwd_rows(
                 const double gap = pm ? cp - cs : cs - cp;
                 const double phm = pm ? sPhi[sp] : phs;
                 const double phtm = pm ? sPhit[sp] : phts;
-                const double ex = exp(a * gap);
-                const double dex = static_cast<double>(sDt[sp]) * ex;
-                const float kp = static_cast<float>(dex * phm);  // K / dt_s
+                const float dex = sDt[sp] * exp2_of(la2 * gap);
+                const float kp = dex * static_cast<float>(phm);  // K / dt_s
                 const float kv = dts * kp;
                 const float nv = gt[v] * qt[v];
                 kq[v] = kv * qt[v];
                 kg[v] = kv * gt[v];
                 kpn += kp * nv;
-                dAacc += static_cast<double>(nv) * static_cast<double>(dts) * dex * (phtm + 0.5 * gap * phm);
-                if (ppos < spos) rh += static_cast<float>(ex) * sDt[sp] * nv;
-                else if (ppos == spos) rh += 0.5f * dts * nv;
+                // pair term of d_A: weight formed in fp64, product in fp32, sum in fp64
+                const float wA = static_cast<float>(phtm + 0.5 * gap * phm);
+                dAacc += static_cast<double>(nv * dts * dex * wA);
+                rh += ppos < spos ? dex * nv : (ppos == spos ? 0.5f * dts * nv : 0.0f);
             }
 #pragma unroll
             for (int pt = 0; pt < P / 16; ++pt)

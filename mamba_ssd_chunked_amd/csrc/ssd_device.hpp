@@ -138,6 +138,39 @@ __device__ __forceinline__ void stage_rows(float* lds, const typename IO::T* g, 
     }
 }
 
+// Stage two TB-row blocks (widths W1, W2; LDS row strides W + 4) with every
+// global load of both in flight before the first LDS write: one memory latency
+// per call instead of one per batch.  For use where the caller's other
+// temporaries are dead (between the barriers around a block change).
+template <class IO, int W1, int W2>
+__device__ __forceinline__ void stage_rows2(float* l1, const typename IO::T* g1, int64_t s1,
+                                            float* l2, const typename IO::T* g2, int64_t s2) {
+    constexpr int V1 = W1 / 4, T1 = TB * V1, I1 = (T1 + NT - 1) / NT;
+    constexpr int V2 = W2 / 4, T2 = TB * V2, I2 = (T2 + NT - 1) / NT;
+    const int tid = static_cast<int>(threadIdx.x);
+    v4f a[I1], b[I2];
+#pragma unroll
+    for (int it = 0; it < I1; ++it) {
+        const int idx = tid + it * NT;
+        if (T1 % NT == 0 || idx < T1) a[it] = io<IO>::ld4(g1, static_cast<int64_t>(idx / V1) * s1 + (idx % V1) * 4);
+    }
+#pragma unroll
+    for (int it = 0; it < I2; ++it) {
+        const int idx = tid + it * NT;
+        if (T2 % NT == 0 || idx < T2) b[it] = io<IO>::ld4(g2, static_cast<int64_t>(idx / V2) * s2 + (idx % V2) * 4);
+    }
+#pragma unroll
+    for (int it = 0; it < I1; ++it) {
+        const int idx = tid + it * NT;
+        if (T1 % NT == 0 || idx < T1) *reinterpret_cast<v4f*>(l1 + (idx / V1) * (W1 + 4) + (idx % V1) * 4) = a[it];
+    }
+#pragma unroll
+    for (int it = 0; it < I2; ++it) {
+        const int idx = tid + it * NT;
+        if (T2 % NT == 0 || idx < T2) *reinterpret_cast<v4f*>(l2 + (idx / V2) * (W2 + 4) + (idx % V2) * 4) = b[it];
+    }
+}
+
 // Stage a contiguous fp32 [ROWS, W] matrix into LDS rows of stride W + 4.
 template <int W, int ROWS>
 __device__ __forceinline__ void stage_mat(float* lds, const float* g) {
