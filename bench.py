@@ -7,6 +7,11 @@ Prints ONE JSON line with tokens/s, the roofline of the dominant kernel
 the launch stream during the timed region) and the CPU oracle timed on a
 bounded sample of the same workload.
 
+The kernels run the chunked algorithm at the library's automatic kernel chunk
+length (min(chunk_len, 128); the workload's chunk_len fixes the buffer layout);
+the same step with the kernels at the layout's chunk length is timed as well
+and reported under "at_layout_chunk_len".
+
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload mamba2_130m_fp32]
 """
 from __future__ import annotations
@@ -25,12 +30,23 @@ PEAK_FP32_MFMA = 157.3e12   # FLOP/s, MI355X dense fp32 matrix
 PEAK_HBM = 8.0e12           # B/s
 
 
-def kernel_work(w, kernel: str):
-    """Algorithmic work of ONE launch of `kernel` for workload w: (amount, kind).
+def kernel_chunk_len(w, requested: int = 0) -> int:
+    """The chunk length the kernels run at (the library's rule for 0: min(l, 128))."""
+    return requested or min(w.chunk_len, 128)
+
+
+def _shape(w, k):
+    """(b, n, l, h, p, r) of workload w run at kernel chunk length k."""
+    return w.batch, w.seq // k, k, w.nheads, w.headdim, w.dstate
+
+
+def kernel_work(w, kernel: str, k: int):
+    """Algorithmic work of ONE launch of `kernel` for workload w run at kernel chunk
+    length k: (amount, kind).
 
     kind "flop": the products the kernel performs, causal triangle only
     (pairs s <= t of a chunk); kind "byte": the HBM bytes the kernel must move."""
-    b, n, l, h, p, r = w.batch, w.nchunks, w.chunk_len, w.nheads, w.headdim, w.dstate
+    b, n, l, h, p, r = _shape(w, k)
     ch = b * n * h                      # chunk-heads
     tok = ch * l                        # token-heads
     pairs = l * (l + 1) // 2            # (t, s) pairs with s <= t per chunk
@@ -53,9 +69,9 @@ def kernel_work(w, kernel: str):
     return None, None
 
 
-def moments_kernel_work(w, kernel: str):
+def moments_kernel_work(w, kernel: str, k: int):
     """Algorithmic flops of one launch of a moments kernel (pairs over the whole chunk)."""
-    b, n, l, h, p, r = w.batch, w.nchunks, w.chunk_len, w.nheads, w.headdim, w.dstate
+    b, n, l, h, p, r = _shape(w, k)
     ch = b * n * h
     if kernel == "km_fwd_rows":    # G tiles (l^2 p) + Z = Q B (l^2 r) + U = B^T Z (l r^2)
         return (2 * l * l * p + 2 * l * l * r + 2 * l * r * r) * ch
@@ -66,9 +82,10 @@ def moments_kernel_work(w, kernel: str):
     return None
 
 
-def method_flops(w):
-    """Algorithmic fwd + bwd flops of the method per step (causal triangle only)."""
-    b, n, l, h, p, r = w.batch, w.nchunks, w.chunk_len, w.nheads, w.headdim, w.dstate
+def method_flops(w, k):
+    """Algorithmic fwd + bwd flops of the method per step at chunk length k (causal
+    triangle only)."""
+    b, n, l, h, p, r = _shape(w, k)
     per_tok_fwd = (l + 1) * r + 4 * p * r + (l + 1) * p
     per_tok_bwd = 3 * (l + 1) * r + 12 * p * r + 2 * (l + 1) * p
     return (per_tok_fwd + per_tok_bwd) * b * n * l * h
@@ -134,7 +151,7 @@ def timed_regions(step, args, stream):
     return ms, ev0.elapsed_time(ev1) / args.steps, ssd.ssd_timing_collect()
 
 
-def bench_moments(args, inp_cache):
+def bench_moments(args):
     """ssd_state_moments (with y) + ssd_state_moments_bwd on the moments workload."""
     import torch
     from mamba_ssd_chunked_amd import inputs, ssd
@@ -143,6 +160,7 @@ def bench_moments(args, inp_cache):
     dev = torch.device("cuda", 0)
     d = {k: v.to(dev) for k, v in inp.items() if isinstance(v, torch.Tensor) and k != "valid_len"}
     valid = inp["valid_len"].clone()
+    k = kernel_chunk_len(w)
     dims = ssd.dims_of(d["x"], d["B"])
     m2 = torch.empty_like(d["d_m2"])
     m1 = torch.empty_like(d["d_m1"])
@@ -170,10 +188,10 @@ def bench_moments(args, inp_cache):
     for name, (tot, cnt) in kt.items():
         avg = tot / cnt
         ent = {"avg_ms": round(avg, 5), "launches_per_step": cnt / args.steps}
-        work = moments_kernel_work(w, name)
+        work = moments_kernel_work(w, name, k)
         if work is None and name in ("k_chunk_states", "k5_chunk_scan", "k1_cumsum", "k4_state_pass",
                                      "k4_state_pass_bwd"):
-            work, kind = kernel_work(w, name)
+            work, kind = kernel_work(w, name, k)
             if kind == "byte":
                 ent.update(gbps=round(work / (avg / 1e3) / 1e9, 1))
                 work = None
@@ -181,7 +199,7 @@ def bench_moments(args, inp_cache):
             rate = work / (avg / 1e3)
             ent.update(tflops=round(rate / 1e12, 2), mfma_frac=round(rate / PEAK_FP32_MFMA, 4))
         kernels[name] = ent
-    res = {"workload": w.describe(), "ms_per_step": round(ms, 4),
+    res = {"workload": {**w.describe(), "kernel_chunk_len": k}, "ms_per_step": round(ms, 4),
            "ms_per_step_with_kernel_events": round(ms_ev, 4),
            "value": round(w.batch * w.seq / (ms / 1e3), 1), "unit": "tokens/s",
            "step": "ssd_state_moments (with y) + ssd_state_moments_bwd", "kernels": kernels}
@@ -212,6 +230,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-moments", action="store_true",
                     help="skip the state-moments leg (moments_valid_len_fp32 workload)")
+    ap.add_argument("--kernel-chunk-len", type=int, default=0,
+                    help="chunk length the kernels run at (0: the library's automatic choice)")
+    ap.add_argument("--moments-only", action="store_true",
+                    help="run only the state-moments leg and print its JSON object")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (a plain copy "
                          "kernel of known size, to calibrate HBM byte counters)")
@@ -224,40 +246,49 @@ def main():
     import torch
     from mamba_ssd_chunked_amd import inputs, ssd
 
+    if args.moments_only:
+        torch.cuda.set_device(0)
+        print(json.dumps(bench_moments(args)), flush=True)
+        return
+
     w = inputs.WORKLOADS[args.workload]
     inp = inputs.make_inputs(w)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     d = {k: v.to(dev) for k, v in inp.items() if isinstance(v, torch.Tensor) and k != "valid_len"}
-    dims = ssd.dims_of(d["x"], d["B"])
     init = d["init"] if w.init_std > 0 else None
     y = torch.empty_like(d["x"])
     final = torch.empty_like(d["d_final"])
     gx, gB, gC = torch.empty_like(d["x"]), torch.empty_like(d["B"]), torch.empty_like(d["C"])
     gdt, gA, gD = torch.empty_like(d["dt"]), torch.empty_like(d["A"]), torch.empty_like(d["D"])
     ginit = torch.empty_like(d["d_final"])
-    ws_f = ssd.workspace(dims, ssd.SSD_OP_FWD, dev)
-    ws_b = ssd.workspace(dims, ssd.SSD_OP_BWD, dev)
     stream = torch.cuda.current_stream()
 
-    def step():
-        rc = ssd.ssd_fwd(dims, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], init, y, final,
-                         ws_f, stream)
-        if rc:
-            raise ssd.SsdError(rc, "ssd_fwd", ssd.ssd_last_error())
-        rc = ssd.ssd_bwd(dims, d["dy"], None, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
-                         init, gx, gdt, gA, gB, gC, gD, ginit, ws_b, stream)
-        if rc:
-            raise ssd.SsdError(rc, "ssd_bwd", ssd.ssd_last_error())
+    def make_step(kcl):
+        dims = ssd.dims_of(d["x"], d["B"], kcl)
+        ws_f = ssd.workspace(dims, ssd.SSD_OP_FWD, dev)
+        ws_b = ssd.workspace(dims, ssd.SSD_OP_BWD, dev)
 
-    ms, ms_ev, kt = timed_regions(step, args, stream)
+        def step():
+            rc = ssd.ssd_fwd(dims, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], init, y,
+                             final, ws_f, stream)
+            if rc:
+                raise ssd.SsdError(rc, "ssd_fwd", ssd.ssd_last_error())
+            rc = ssd.ssd_bwd(dims, d["dy"], None, d["x"], d["dt"], d["A"], d["B"], d["C"],
+                             d["D"], init, gx, gdt, gA, gB, gC, gD, ginit, ws_b, stream)
+            if rc:
+                raise ssd.SsdError(rc, "ssd_bwd", ssd.ssd_last_error())
+        return step
+
+    k = kernel_chunk_len(w, args.kernel_chunk_len)
+    ms, ms_ev, kt = timed_regions(make_step(args.kernel_chunk_len), args, stream)
     tokens = w.batch * w.seq
     value = tokens / (ms / 1e3)
 
     kernels = {}
     for name, (tot, cnt) in kt.items():
         avg = tot / cnt
-        work, kind = kernel_work(w, name)
+        work, kind = kernel_work(w, name, k)
         ent = {"avg_ms": round(avg, 5), "launches_per_step": cnt / args.steps}
         if name == "k_chunk_states":
             # launched once in ssd_fwd (1 job) and once in ssd_bwd (2 jobs): average work
@@ -269,8 +300,8 @@ def main():
             else:
                 ent.update(gbps=round(rate / 1e9, 1), hbm_frac=round(rate / PEAK_HBM, 4))
         kernels[name] = ent
-    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches_per_step"])
-    work, kind = kernel_work(w, dom)
+    dom = max(kernels, key=lambda n: kernels[n]["avg_ms"] * kernels[n]["launches_per_step"])
+    work, kind = kernel_work(w, dom, k)
     davg = kernels[dom]["avg_ms"]
     if kind == "flop":
         ach = work / (davg / 1e3) / 1e12
@@ -287,15 +318,20 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "io_dtype": w.io,
         "data": "synthetic (seeded draws of the workload recipe; no dataset)",
-        "config": w.describe(),
+        "config": {**w.describe(), "kernel_chunk_len": k},
         "roofline": roof,
-        "method_tflops": round(method_flops(w) / (ms / 1e3) / 1e12, 3),
+        "method_tflops": round(method_flops(w, k) / (ms / 1e3) / 1e12, 3),
         "kernels": kernels,
     }
+    if k != w.chunk_len:
+        # the same step with the kernels run at the layout's chunk length
+        ms_l, _, _ = timed_regions(make_step(w.chunk_len), args, stream)
+        out["at_layout_chunk_len"] = {"kernel_chunk_len": w.chunk_len, "ms_per_step": round(ms_l, 4),
+                                      "value": round(tokens / (ms_l / 1e3), 1)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp)
     if not args.no_moments:
-        out["moments"] = bench_moments(args, inp_cache={})
+        out["moments"] = bench_moments(args)
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, device=dev)

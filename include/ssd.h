@@ -42,7 +42,18 @@
  *    {16, 32, 64, 128}; batch >= 0, nchunks >= 0 (an empty sequence is valid:
  *    final = init, d_init = d_final, d_A = d_D = 0).  Tensor pointers must be
  *    16-byte aligned (8-byte for bf16 tensors).
- *  - Results are bitwise reproducible for equal inputs (no float atomics).
+ *  - kernel_chunk_len: the chunked algorithm is an exact re-association of the
+ *    recurrence above for every chunk length, so the kernels may run it at a
+ *    shorter chunk than the caller's layout: the [b, n, l, ...] buffers are the
+ *    same memory as [b, n * l / k, k, ...] for any k dividing l.  0 picks
+ *    min(chunk_len, 128) (on gfx950 the intra-chunk pair work per token grows
+ *    with k on the fp32 matrix cores and the inter-chunk state traffic per
+ *    token falls with 1/k; 128 balances them for the shapes measured).  Any
+ *    other value must be 64, 128 or 256 and divide chunk_len
+ *    (SSD_ERR_UNSUPPORTED otherwise).  Results for different kernel_chunk_len
+ *    agree up to floating-point rounding; ssd_workspace_size() depends on it.
+ *  - Results are bitwise reproducible for equal inputs and kernel_chunk_len
+ *    (no float atomics).
  *  - Every call validates all arguments before it enqueues anything.  Return 0
  *    on success or one of the ssd_status codes; ssd_last_error() then gives a
  *    message (thread-local, valid until the next call on the thread).
@@ -65,7 +76,7 @@ typedef struct ssd_dims {
     int64_t headdim;   /* p (per_head_dim) */
     int64_t dstate;    /* r (state_rank) */
     int32_t io_dtype;  /* SSD_F32 or SSD_BF16 */
-    int32_t reserved;  /* must be 0 */
+    int32_t kernel_chunk_len; /* chunk length the kernels run at; 0 = automatic (see below) */
 } ssd_dims;
 
 enum ssd_io_dtype { SSD_F32 = 0, SSD_BF16 = 1 };
@@ -75,7 +86,7 @@ enum ssd_status {
     SSD_ERR_NULL = 1,        /* a required pointer is NULL */
     SSD_ERR_SHAPE = 2,       /* a dimension is negative / zero where not allowed, or valid_len out of range */
     SSD_ERR_UNSUPPORTED = 3, /* shape or alignment outside the supported set above */
-    SSD_ERR_DTYPE = 4,       /* io_dtype not SSD_F32 / SSD_BF16, or reserved != 0 */
+    SSD_ERR_DTYPE = 4,       /* io_dtype not SSD_F32 / SSD_BF16 */
     SSD_ERR_WORKSPACE = 5,   /* ws_bytes smaller than ssd_workspace_size(), or ws NULL */
     SSD_ERR_HIP = 6          /* a HIP launch failed (message names the kernel) */
 };

@@ -41,9 +41,8 @@ bool pow2_in(int64_t v, int64_t lo, int64_t hi) {
 
 int validate_dims(const ssd_dims* d, ssd::Shape* s) {
     if (!d) return fail(SSD_ERR_NULL, "dims is NULL");
-    if ((d->io_dtype != SSD_F32 && d->io_dtype != SSD_BF16) || d->reserved != 0)
-        return fail(SSD_ERR_DTYPE, "io_dtype must be SSD_F32 (0) or SSD_BF16 (1) and reserved 0 (got %d, %d)",
-                    d->io_dtype, d->reserved);
+    if (d->io_dtype != SSD_F32 && d->io_dtype != SSD_BF16)
+        return fail(SSD_ERR_DTYPE, "io_dtype must be SSD_F32 (0) or SSD_BF16 (1) (got %d)", d->io_dtype);
     if (d->batch < 0 || d->nchunks < 0 || d->chunk_len <= 0 || d->nheads <= 0 || d->headdim <= 0 ||
         d->dstate <= 0)
         return fail(SSD_ERR_SHAPE,
@@ -63,9 +62,19 @@ int validate_dims(const ssd_dims* d, ssd::Shape* s) {
     if (ch_blocks > 2.0e9 || elems > 4.0e18 || d->nchunks > (1 << 30) || d->nheads > (1 << 30) ||
         d->batch > (1 << 30))
         return fail(SSD_ERR_UNSUPPORTED, "problem too large for one call (split the batch)");
+    // The kernels run the chunked algorithm at chunk length k (a divisor of chunk_len):
+    // the caller's [b, n, l, ...] buffers are the same memory as [b, n l / k, k, ...].
+    const int64_t k = d->kernel_chunk_len == 0 ? (d->chunk_len < 128 ? d->chunk_len : 128)
+                                               : d->kernel_chunk_len;
+    if (!pow2_in(k, 64, 256) || k > d->chunk_len || d->chunk_len % k != 0)
+        return fail(SSD_ERR_UNSUPPORTED,
+                    "kernel_chunk_len must be 0 or one of 64, 128, 256 dividing chunk_len "
+                    "(got %d for chunk_len %lld)", d->kernel_chunk_len, (long long)d->chunk_len);
+    if (d->nchunks * (d->chunk_len / k) > (1 << 30))
+        return fail(SSD_ERR_UNSUPPORTED, "problem too large for one call (split the batch)");
     s->B = (int)d->batch;
-    s->N = (int)d->nchunks;
-    s->L = (int)d->chunk_len;
+    s->N = (int)(d->nchunks * (d->chunk_len / k));
+    s->L = (int)k;
     s->H = (int)d->nheads;
     s->P = (int)d->headdim;
     s->R = (int)d->dstate;

@@ -35,12 +35,12 @@ class ssd_dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("nchunks", ctypes.c_int64),
                 ("chunk_len", ctypes.c_int64), ("nheads", ctypes.c_int64),
                 ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64),
-                ("io_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("io_dtype", ctypes.c_int32), ("kernel_chunk_len", ctypes.c_int32)]
 
     def __repr__(self):
-        return ("ssd_dims(b=%d, n=%d, l=%d, h=%d, p=%d, r=%d, io=%d)" %
+        return ("ssd_dims(b=%d, n=%d, l=%d, h=%d, p=%d, r=%d, io=%d, kernel_chunk_len=%d)" %
                 (self.batch, self.nchunks, self.chunk_len, self.nheads, self.headdim,
-                 self.dstate, self.io_dtype))
+                 self.dstate, self.io_dtype, self.kernel_chunk_len))
 
 
 class SsdError(RuntimeError):
@@ -84,16 +84,17 @@ def load_library(path: str = LIB_PATH):
 
 
 # ------------------------------------------------------------------ marshalling
-def make_dims(batch, nchunks, chunk_len, nheads, headdim, dstate, io_dtype=SSD_F32) -> ssd_dims:
+def make_dims(batch, nchunks, chunk_len, nheads, headdim, dstate, io_dtype=SSD_F32,
+              kernel_chunk_len=0) -> ssd_dims:
     return ssd_dims(int(batch), int(nchunks), int(chunk_len), int(nheads), int(headdim),
-                    int(dstate), int(io_dtype), 0)
+                    int(dstate), int(io_dtype), int(kernel_chunk_len))
 
 
-def dims_of(x: torch.Tensor, B: torch.Tensor) -> ssd_dims:
+def dims_of(x: torch.Tensor, B: torch.Tensor, kernel_chunk_len: int = 0) -> ssd_dims:
     """dims from x ``[b, n, l, h, p]`` and B ``[b, n, l, h, r]``."""
     b, n, l, h, p = x.shape
     io_dtype = SSD_BF16 if x.dtype == torch.bfloat16 else SSD_F32
-    return make_dims(b, n, l, h, p, B.shape[-1], io_dtype)
+    return make_dims(b, n, l, h, p, B.shape[-1], io_dtype, kernel_chunk_len)
 
 
 def _io_dtype(d: ssd_dims):
@@ -246,9 +247,10 @@ def workspace(dims: ssd_dims, op: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
-def forward(x, dt, A, B, C, D, init=None, want_final=True, ws=None, stream=None):
+def forward(x, dt, A, B, C, D, init=None, want_final=True, ws=None, stream=None,
+            kernel_chunk_len=0):
     """y, final_state = SSD(x, dt, A, B, C, D, init)."""
-    d = dims_of(x, B)
+    d = dims_of(x, B, kernel_chunk_len)
     y = torch.empty_like(x)
     final = torch.empty((d.batch, d.nheads, d.headdim, d.dstate), device=x.device,
                         dtype=torch.float32) if want_final else None
@@ -258,9 +260,9 @@ def forward(x, dt, A, B, C, D, init=None, want_final=True, ws=None, stream=None)
 
 
 def backward(dy, x, dt, A, B, C, D, init=None, d_final=None, want_d_init=True, ws=None,
-             stream=None):
+             stream=None, kernel_chunk_len=0):
     """Returns dict(d_x, d_dt, d_A, d_B, d_C, d_D, d_init)."""
-    d = dims_of(x, B)
+    d = dims_of(x, B, kernel_chunk_len)
     out = dict(d_x=torch.empty_like(x), d_dt=torch.empty_like(dt), d_A=torch.empty_like(A),
                d_B=torch.empty_like(B), d_C=torch.empty_like(C), d_D=torch.empty_like(D),
                d_init=torch.empty((d.batch, d.nheads, d.headdim, d.dstate), device=x.device,
@@ -272,9 +274,9 @@ def backward(dy, x, dt, A, B, C, D, init=None, d_final=None, want_d_init=True, w
 
 
 def state_moments(x, dt, A, B, init=None, valid_len=None, C=None, D=None, want_y=False,
-                  want_final=False, ws=None, stream=None):
+                  want_final=False, ws=None, stream=None, kernel_chunk_len=0):
     """Returns dict(m2, m1, count[, y][, final_state])."""
-    d = dims_of(x, B)
+    d = dims_of(x, B, kernel_chunk_len)
     dev = x.device
     out = dict(m2=torch.empty((d.batch, d.nheads, d.dstate, d.dstate), device=dev),
                m1=torch.empty((d.batch, d.nheads, d.dstate), device=dev),
@@ -294,9 +296,9 @@ def state_moments(x, dt, A, B, init=None, valid_len=None, C=None, D=None, want_y
 
 
 def state_moments_bwd(d_m2, x, dt, A, B, init=None, valid_len=None, d_m1=None, want_d_init=True,
-                      ws=None, stream=None):
+                      ws=None, stream=None, kernel_chunk_len=0):
     """Returns dict(d_x, d_dt, d_A, d_B, d_init)."""
-    d = dims_of(x, B)
+    d = dims_of(x, B, kernel_chunk_len)
     dev = x.device
     out = dict(d_x=torch.empty_like(x), d_dt=torch.empty_like(dt), d_A=torch.empty_like(A),
                d_B=torch.empty_like(B),

@@ -41,12 +41,14 @@ def to_dev(t: dict) -> dict:
     return out
 
 
-def gpu_fwd_bwd(inp: dict, use_init=True, use_d_final=True):
+def gpu_fwd_bwd(inp: dict, use_init=True, use_d_final=True, kernel_chunk_len=0):
     d = to_dev(inp)
     init = d["init"] if use_init else None
-    y, fin = ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], init)
+    y, fin = ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], init,
+                         kernel_chunk_len=kernel_chunk_len)
     g = ssd.backward(d["dy"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], init,
-                     d_final=d["d_final"] if use_d_final else None)
+                     d_final=d["d_final"] if use_d_final else None,
+                     kernel_chunk_len=kernel_chunk_len)
     torch.cuda.synchronize()
     out = dict(y=y.float().cpu().numpy(), final=fin.cpu().numpy())
     for k, v in g.items():

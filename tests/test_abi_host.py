@@ -50,15 +50,29 @@ def dims(b=2, n=3, l=64, h=2, p=16, r=32, io=0):
     return ssd.make_dims(b, n, l, h, p, r, io)
 
 
-def test_workspace_plan(lib):
+@pytest.mark.parametrize("kcl,k", [(256, 256), (128, 128), (64, 64), (0, 128)])
+def test_workspace_plan(lib, kcl, k):
+    """The plan at kernel chunk length k: the 8 x 256-token chunks become 8 * 256 / k."""
     d = dims(b=4, n=8, l=256, h=24, p=64, r=128)
+    d.kernel_chunk_len = kcl
     up = lambda v: (v + 255) // 256 * 256  # noqa: E731
-    tok, chunks = 4 * 24 * 8 * 256, 4 * 24 * 8
+    tok, chunks = 4 * 24 * 8 * 256, 4 * 24 * 8 * 256 // k
     states = chunks * 64 * 128
     assert ssd.ssd_workspace_size(d, ssd.SSD_OP_FWD) == up(8 * tok) + up(4 * states)
     bwd = up(8 * tok) + 2 * up(4 * states) + 3 * up(4 * tok) + up(4 * chunks) \
-        + 3 * up(8 * chunks * 4)
+        + 3 * up(8 * chunks * (k // 64))
     assert ssd.ssd_workspace_size(d, ssd.SSD_OP_BWD) == bwd
+
+
+@pytest.mark.parametrize("l,kcl", [(256, 96), (256, 512), (128, 256), (64, 128), (256, -64),
+                                   (128, 32)])
+def test_bad_kernel_chunk_len_is_rejected(lib, l, kcl):
+    d = dims(l=l)
+    d.kernel_chunk_len = kcl
+    out = ctypes.c_size_t(0)
+    assert lib.ssd_workspace_size(ctypes.byref(d), 0, ctypes.byref(out)) == 3
+    assert "kernel_chunk_len" in ssd.ssd_last_error()
+    assert lib.ssd_fwd(ctypes.byref(d), *([FAKE] * 10), 1 << 30, FAKE) == 3
 
 
 @pytest.mark.parametrize("bad,code", [

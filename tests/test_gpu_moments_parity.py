@@ -26,13 +26,15 @@ def _need_gpu():
     ssd.load_library()
 
 
-def gpu_moments(inp, valid, use_init=True, use_dm1=True):
+def gpu_moments(inp, valid, use_init=True, use_dm1=True, kernel_chunk_len=0):
     d = to_dev(inp)
     init = d["init"] if use_init else None
     mo = ssd.state_moments(d["x"], d["dt"], d["A"], d["B"], init, valid_len=valid, C=d["C"],
-                           D=d["D"], want_y=True, want_final=True)
+                           D=d["D"], want_y=True, want_final=True,
+                           kernel_chunk_len=kernel_chunk_len)
     g = ssd.state_moments_bwd(d["d_m2"], d["x"], d["dt"], d["A"], d["B"], init, valid_len=valid,
-                              d_m1=d["d_m1"] if use_dm1 else None)
+                              d_m1=d["d_m1"] if use_dm1 else None,
+                              kernel_chunk_len=kernel_chunk_len)
     torch.cuda.synchronize()
     out = {k: (v.float().cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in mo.items()}
     out.update({k: v.float().cpu().numpy() for k, v in g.items()})
@@ -94,6 +96,18 @@ def test_moments_shapes_full(shape):
     ref = oracle_moments(inp, list(valid))
     compare(gpu, ref, TOL[io], ("m2", "m1") + MGRADS, f"moments {shape}")
     assert list(gpu["count"]) == list(ref["count"])
+
+
+@pytest.mark.parametrize("kcl", [64, 128, 256])
+def test_moments_kernel_chunk_len(kcl):
+    """Moments at every kernel chunk length of 256-token chunks, valid_len mid-chunk."""
+    w = inputs.custom(batch=2, seq=768, nheads=2, headdim=64, dstate=64, chunk_len=256,
+                      init_std=0.3, valid_len=(768, 333), seed=800 + kcl)
+    say(f"case moments chunk_len 256 kernel_chunk_len {kcl}")
+    inp = inputs.make_inputs(w)
+    gpu = gpu_moments(inp, [768, 333], kernel_chunk_len=kcl)
+    ref = oracle_moments(inp, [768, 333])
+    compare(gpu, ref, TOL["f32"], ("m2", "m1") + MGRADS, f"moments k={kcl}")
 
 
 def test_moments_workload_sampled_heads():

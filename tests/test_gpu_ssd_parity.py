@@ -65,21 +65,40 @@ def test_shapes_full(shape):
     compare(gpu, ref, TOL[io], KEYS, str(shape))
 
 
-FULL = [("mamba2_130m_fp32", [0, 13]), ("mamba2_2p7b_bf16", [41]),
-        ("long_context_64k_fp32", [7]), ("moments_valid_len_fp32", [3])]
+# (workload, sampled heads, kernel_chunk_len): 0 is the automatic choice the benchmark
+# times; 256 runs the 256-token chunks of the workloads unsplit.
+FULL = [("mamba2_130m_fp32", [0, 13], 0), ("mamba2_130m_fp32", [5], 256),
+        ("mamba2_2p7b_bf16", [41], 0), ("long_context_64k_fp32", [7], 0),
+        ("long_context_64k_fp32", [30], 256), ("moments_valid_len_fp32", [3], 0)]
 
 
-@pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])
-def test_full_size_sampled_heads(name, heads):
+@pytest.mark.parametrize("name,heads,kcl", FULL, ids=[f"{f[0]}-k{f[2]}" for f in FULL])
+def test_full_size_sampled_heads(name, heads, kcl):
     w = inputs.WORKLOADS[name]
-    say(f"case {name} full size, heads {heads}")
+    say(f"case {name} full size, heads {heads}, kernel_chunk_len {kcl}")
     inp = inputs.make_inputs(w)
     use_init = w.init_std > 0
-    gpu = gpu_fwd_bwd(inp, use_init=use_init, use_d_final=False)
+    gpu = gpu_fwd_bwd(inp, use_init=use_init, use_d_final=False, kernel_chunk_len=kcl)
     ref = oracle_fwd_bwd(inp, heads=heads, use_init=use_init, use_d_final=False)
     compare(select_heads(gpu, heads), ref, TOL[w.io], KEYS, name)
     for k in KEYS:
         assert np.all(np.isfinite(gpu[k])), k
+
+
+KCL = [(256, 64, "f32"), (256, 128, "f32"), (256, 256, "f32"), (128, 64, "f32"),
+       (256, 64, "bf16"), (256, 256, "bf16")]
+
+
+@pytest.mark.parametrize("l,kcl,io", KCL, ids=[f"l{k[0]}_k{k[1]}_{k[2]}" for k in KCL])
+def test_kernel_chunk_len_matches_oracle(l, kcl, io):
+    """Every kernel chunk length gives the recurrence's outputs (to the same bar)."""
+    w = inputs.custom(batch=2, seq=768 if l == 256 else 384, nheads=3, headdim=64, dstate=128,
+                      chunk_len=l, io=io, init_std=0.3, seed=700 + kcl)
+    say(f"case chunk_len {l} kernel_chunk_len {kcl} {io}")
+    inp = inputs.make_inputs(w)
+    gpu = gpu_fwd_bwd(inp, kernel_chunk_len=kcl)
+    ref = oracle_fwd_bwd(inp)
+    compare(gpu, ref, TOL[io], KEYS, f"l={l} k={kcl} {io}")
 
 
 def test_bitwise_deterministic():
