@@ -30,6 +30,31 @@ PEAK_FP32_MFMA = 157.3e12   # FLOP/s, MI355X dense fp32 matrix
 PEAK_HBM = 8.0e12           # B/s
 
 
+# HBM bytes per launch (read, write) of a kernel from two rocprofv3 --pmc runs (FETCH_SIZE,
+# WRITE_SIZE; scaled x2.0 / x1.0 by the same counters on a 256 MiB device copy), keyed by
+# (kernel, workload, kernel chunk length), valid only while the hash of the kernel's sources is
+# the one they were taken on (profiles/ssd_kernels_mamba2_130m_fp32.md has the runs).
+TRAFFIC = {
+    ("k_bwd_source", "mamba2_130m_fp32", 128): (483_895_296, 153_614_336, "f6bec228a111e4c3"),
+}
+TRAFFIC_SOURCES = {"k_bwd_source": ("k_chunk_bwd.hip", "ssd_device.hpp", "ssd_launch.hpp"),
+                   "k_bwd_target": ("k_chunk_bwd.hip", "ssd_device.hpp", "ssd_launch.hpp")}
+
+
+def measured_traffic(kernel: str, w, k: int):
+    """HBM bytes per launch of `kernel` from the counter runs, or None when none were taken for
+    this workload or the kernel's sources changed since."""
+    import hashlib
+    ent = TRAFFIC.get((kernel, w.name, k))
+    if ent is None:
+        return None
+    m = hashlib.sha256()
+    for f in TRAFFIC_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "mamba_ssd_chunked_amd", "csrc", f), "rb") as fh:
+            m.update(fh.read())
+    return ent[0] + ent[1] if m.hexdigest()[:16] == ent[2] else None
+
+
 def kernel_chunk_len(w, requested: int = 0) -> int:
     """The chunk length the kernels run at (the library's rule for 0: min(l, 128))."""
     return requested or min(w.chunk_len, 128)
@@ -232,6 +257,8 @@ def main():
                     help="skip the state-moments leg (moments_valid_len_fp32 workload)")
     ap.add_argument("--kernel-chunk-len", type=int, default=0,
                     help="chunk length the kernels run at (0: the library's automatic choice)")
+    ap.add_argument("--no-layout-chunk", action="store_true",
+                    help="skip the second timing with the kernels at the layout's chunk length")
     ap.add_argument("--moments-only", action="store_true",
                     help="run only the state-moments leg and print its JSON object")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -306,11 +333,13 @@ def main():
     if kind == "flop":
         ach = work / (davg / 1e3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 3), "peak": 157.3,
-                "unit": "TFLOP/s", "frac": round(ach / 157.3, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / 157.3, 4),
+                "traffic": measured_traffic(dom, w, k)}
     else:
         ach = work / (davg / 1e3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": 8000.0,
-                "unit": "GB/s", "frac": round(ach / 8000.0, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(ach / 8000.0, 4),
+                "traffic": measured_traffic(dom, w, k)}
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -323,7 +352,7 @@ def main():
         "method_tflops": round(method_flops(w, k) / (ms / 1e3) / 1e12, 3),
         "kernels": kernels,
     }
-    if k != w.chunk_len:
+    if k != w.chunk_len and not args.no_layout_chunk:
         # the same step with the kernels run at the layout's chunk length
         ms_l, _, _ = timed_regions(make_step(w.chunk_len), args, stream)
         out["at_layout_chunk_len"] = {"kernel_chunk_len": w.chunk_len, "ms_per_step": round(ms_l, 4),

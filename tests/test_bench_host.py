@@ -1,0 +1,53 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU refusal, the algorithmic work
+model behind the roofline, and the source-hash gate on the measured HBM traffic."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from mamba_ssd_chunked_amd import inputs  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_kernel_chunk_len_rule():
+    w = inputs.WORKLOADS["mamba2_130m_fp32"]
+    assert bench.kernel_chunk_len(w) == 128
+    assert bench.kernel_chunk_len(w, 256) == 256
+    assert bench.kernel_chunk_len(inputs.WORKLOADS["tiny_fp32"]) == 64
+
+
+def test_work_model_counts_the_causal_products():
+    """k5 at k = 128 on c1: 1536 chunk-heads x (2 k p r + 2 pairs (r + p)), by hand."""
+    w = inputs.WORKLOADS["mamba2_130m_fp32"]
+    pairs = 128 * 129 // 2
+    ch = 4 * (2048 // 128) * 24
+    assert bench.kernel_work(w, "k5_chunk_scan", 128) == ((2 * 128 * 64 * 128 + 2 * pairs * 192) * ch,
+                                                          "flop")
+    # the same step at k = 256 has half the chunk-heads and (k + 1) / 2 pairs per token
+    f128 = bench.kernel_work(w, "k_bwd_source", 128)[0]
+    f256 = bench.kernel_work(w, "k_bwd_source", 256)[0]
+    assert f256 > f128
+    assert bench.kernel_work(w, "k4_state_pass", 128)[1] == "byte"
+    # the method total is per token-head, independent of how the kernels split it
+    assert bench.method_flops(w, 128) < bench.method_flops(w, 256)
+
+
+def test_traffic_is_reported_only_for_the_profiled_sources(monkeypatch):
+    w = inputs.WORKLOADS["mamba2_130m_fp32"]
+    key = ("k_bwd_source", w.name, 128)
+    rd, wr, h = bench.TRAFFIC[key]
+    monkeypatch.setitem(bench.TRAFFIC, key, (rd, wr, "0" * 16))
+    assert bench.measured_traffic("k_bwd_source", w, 128) is None
+    assert bench.measured_traffic("k_bwd_source", w, 256) is None  # never profiled at 256
+    assert bench.measured_traffic("k5_chunk_scan", w, 128) is None
