@@ -433,6 +433,8 @@ hipError_t launch_bwd_target(const Shape& s, const void* dy, const void* x, cons
                              const void* Bm, const void* Cm, const float* A, const double* cdt,
                              const float* S, const float* dS, void* dC, float* g1, float* d_end,
                              double* dA_T, hipStream_t st) {
+    if (wide_supported(s))
+        return launch_bwd_target_wide(s, dy, x, dt, Bm, Cm, A, cdt, S, dS, dC, g1, d_end, dA_T, st);
     return s.io == 1 ? target_io<BF16>(s, dy, x, dt, Bm, Cm, A, cdt, S, dS, dC, g1, d_end, dA_T, st)
                      : target_io<F32>(s, dy, x, dt, Bm, Cm, A, cdt, S, dS, dC, g1, d_end, dA_T, st);
 }

@@ -299,6 +299,7 @@ static hipError_t k5_io(const Shape& s, const void* x, const float* dt, const vo
 hipError_t launch_k5_scan(const Shape& s, const void* x, const float* dt, const void* Bm,
                           const void* Cm, const float* A, const float* D, const double* cdt,
                           const float* S, void* y, hipStream_t st) {
+    if (wide_supported(s)) return launch_k5_scan_wide(s, x, dt, Bm, Cm, A, D, cdt, S, y, st);
     return s.io == 1 ? k5_io<BF16>(s, x, dt, Bm, Cm, A, D, cdt, S, y, st)
                      : k5_io<F32>(s, x, dt, Bm, Cm, A, D, cdt, S, y, st);
 }

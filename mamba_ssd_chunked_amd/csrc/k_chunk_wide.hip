@@ -1,0 +1,456 @@
+// Whole-chunk variants of two ORANGE kernels (K5 forward output and the
+// backward's target rows) for 128-token chunks: one workgroup per chunk-head
+// instead of one per (chunk-head, 64-token block).
+//
+// Page: burn-mamba "mamba2/ssd/serial_recalculated/combined_backward.rs"; the
+// per-element formulas are those of k_chunk_fwd.hip (K5: BLUE + ORANGE + D x)
+// and of k_bwd_target in k_chunk_bwd.hip (BLUE, ORANGE and K2 backward, K4
+// backward's d_end, pair-form d_A).
+//
+// Why a second shape.  In a causal chunk, row tile k of 8 has k + 1 partner
+// tiles as a target and 8 - k as a source.  The block kernels give each wave one
+// row tile, so the waves of a workgroup carry 1..4 tiles on the diagonal block
+// and wait for each other at every block change; each workgroup also re-stages
+// the partner blocks it shares with the other blocks of its chunk.  Here wave w
+// owns the two row tiles w and 7 - w, which as targets pair with
+// (w + 1) + (8 - w) = 9 partner tiles for every wave.  The partner rows are
+// staged in two halves of 64 rows: the even 16-row tiles, then the odd ones.
+// With that split every wave has 5 pair tiles in the even half and 4 in the
+// odd one, so the barrier between the halves costs no waiting, and the LDS of
+// one half (about 52 KB at
+// (p, r) = (64, 128), shared with the chunk's p x r state of the prologue)
+// leaves room for two workgroups per CU.  The source-row side keeps its block
+// kernel: two row tiles of B and x operands plus the d_x and d_B accumulators
+// are 192 registers per lane at (64, 128), which does not leave room for the
+// rest within the 256 registers of two waves per SIMD.
+//
+// Layouts and the MFMA operand convention are those of ssd_device.hpp; every
+// 16x16 product tile is formed with its M index along the rows the next
+// product contracts over, so its registers are the next MFMA's operand.
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+namespace {
+
+constexpr int KC = 128;       // the chunk length these kernels take
+constexpr int NRT = KC / 16;  // row tiles per chunk
+
+// Shapes that take the whole-chunk kernels: two row tiles of operands and
+// accumulators per wave must fit the 256 registers of two waves per SIMD.
+template <int P, int R>
+constexpr bool wide_fits() {
+    return P * R <= 64 * 128;
+}
+
+// LDS floats of the main buffer: the [P, R] state, or one half of the partner rows.
+template <int P, int R>
+constexpr int wide_main() {
+    return P * (R + 4) > TB * (R + 4) + TB * (P + 4) ? P * (R + 4) : TB * (R + 4) + TB * (P + 4);
+}
+
+template <int N>
+struct Q {
+    static constexpr int value = N;
+};
+
+}  // namespace
+
+// ------------------------------------------------------------------------- K5
+// Wave w owns target tiles tt = {w, 7 - w}.  acc[q][pt][v] is y[t][p] with
+// t = 16 tt[q] + 4g + v, p = 16 pt + i (BLUE e_t C_t S_in, then ORANGE, then D x).
+template <class IO, int P, int R>
+__global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
+    const typename IO::T* __restrict__ x, const float* __restrict__ dt,
+    const typename IO::T* __restrict__ Bm, const typename IO::T* __restrict__ Cm,
+    const float* __restrict__ Av, const float* __restrict__ Dv, const double* __restrict__ cdt,
+    const float* __restrict__ S, typename IO::T* __restrict__ y, int N, int H) {
+    constexpr int RS = R + 4, PS = P + 4, L = KC;
+    __shared__ float sM[wide_main<P, R>()];  // S_in [P, R], then one half of B | x
+    float* sB = sM;
+    float* sX = sM + TB * RS;
+    __shared__ __align__(16) double sCdt[KC];
+    __shared__ __align__(16) float sDt[KC];
+    const ChunkHead c = decode_ch(blockIdx.x, N, H);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    const int64_t xrow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(P);
+    const int64_t xstride = static_cast<int64_t>(H) * P;
+    const int64_t brow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(R);
+    const int64_t bstride = static_cast<int64_t>(H) * R;
+    const double* cc = cdt + c.c_bhn * L;
+    const double la2 = static_cast<double>(Av[c.h]) * kLog2e;
+    const int tt[2] = {wave, NRT - 1 - wave};
+    const int tl[2] = {16 * tt[0] + i, 16 * tt[1] + i};
+
+    v4f creg[2][R / 16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int kk = 0; kk < R / 16; ++kk)
+            creg[q][kk] = io<IO>::ld4(Cm, brow0 + static_cast<int64_t>(tl[q]) * bstride + 16 * kk + 4 * g);
+    stage_mat<R, P>(sM, S + c.ch * (P * R));
+    if (tid < KC) {
+        sCdt[tid] = cc[tid];
+        sDt[tid] = dt[c.c_bhn * L + tid];
+    }
+    __syncthreads();
+
+    v4f acc[2][P / 16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt) acc[q][pt] = zero4();
+    // BLUE: A = C rows (k = r), B operand = S_in[p, r] read along r
+#pragma unroll
+    for (int kk = 0; kk < R / 16; ++kk) {
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt) {
+            const v4f bop = *reinterpret_cast<const v4f*>(sM + (pt * 16 + i) * RS + 16 * kk + 4 * g);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) acc[q][pt] = mfma16(creg[q][kk][v], bop[v], acc[q][pt]);
+        }
+    }
+    double ct[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        ct[q] = sCdt[tl[q]];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float e = exp2_of(la2 * sCdt[16 * tt[q] + 4 * g + v]);
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt) acc[q][pt][v] *= e;
+        }
+    }
+
+    // ORANGE over source tiles j <= tt[q]; tt[0] < tt[1], so tile j pairs with
+    // both own tiles while j <= tt[0] and with tt[1] alone after that.
+    auto tile = [&](int j, int u, auto qlo) {
+        constexpr int QLO = decltype(qlo)::value;
+        v4f cbt[2];
+#pragma unroll
+        for (int q = QLO; q < 2; ++q) cbt[q] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < R / 16; ++kk) {
+            const v4f aop = *reinterpret_cast<const v4f*>(sB + (16 * u + i) * RS + 16 * kk + 4 * g);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int q = QLO; q < 2; ++q) cbt[q] = mfma16(aop[v], creg[q][kk][v], cbt[q]);
+        }
+        const v2d cs01 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g);
+        const v2d cs23 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g + 2);
+        const v4f dts = *reinterpret_cast<const v4f*>(sDt + 16 * j + 4 * g);
+        const double csv[4] = {cs01.x, cs01.y, cs23.x, cs23.y};
+        float wv[2][4];
+#pragma unroll
+        for (int q = QLO; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const bool keep = (j < tt[q]) || (16 * j + 4 * g + v <= tl[q]);
+                const float e = exp2_of(la2 * (ct[q] - csv[v]));  // masked pairs discarded
+                wv[q][v] = keep ? cbt[q][v] * e * dts[v] : 0.0f;
+            }
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt) {
+                const float xs = sX[(16 * u + 4 * g + v) * PS + pt * 16 + i];
+#pragma unroll
+                for (int q = QLO; q < 2; ++q) acc[q][pt] = mfma16(wv[q][v], xs, acc[q][pt]);
+            }
+    };
+    const float Dh = Dv[c.h];
+    for (int half = 0; half < 2; ++half) {
+        v4f preB[RowTiles<R, TB>::IT], preX[RowTiles<P, TB>::IT];
+        load_half_rows<IO, R>(preB, Bm + brow0, bstride, half);
+        load_half_rows<IO, P>(preX, x + xrow0, xstride, half);
+        __syncthreads();  // the previous contents of sM are consumed
+        store_rows<R, TB>(sB, preB);
+        store_rows<P, TB>(sX, preX);
+        __syncthreads();
+        // SKIP: D x of this wave's target rows that sit in this half
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            if ((tt[q] & 1) == half)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+#pragma unroll
+                    for (int pt = 0; pt < P / 16; ++pt)
+                        acc[q][pt][v] += Dh * sX[(16 * (tt[q] >> 1) + 4 * g + v) * PS + pt * 16 + i];
+        for (int u = 0; u < 4; ++u) {
+            const int j = 2 * u + half;
+            if (j <= tt[0]) tile(j, u, Q<0>{});
+            else if (j <= tt[1]) tile(j, u, Q<1>{});
+        }
+    }
+
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t row = xrow0 + static_cast<int64_t>(16 * tt[q] + 4 * g + v) * xstride;
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt) io<IO>::st(y, row + pt * 16 + i, acc[q][pt][v]);
+        }
+}
+
+// ---------------------------------------------------------- backward, rows t
+// Wave w owns target tiles tt = {w, 7 - w}; acc[q][rt][v] is d_C[t][r] with
+// t = 16 tt[q] + i, r = 16 rt + 4g + v.
+template <class IO, int P, int R>
+__global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
+    const typename IO::T* __restrict__ dy, const typename IO::T* __restrict__ x,
+    const float* __restrict__ dt, const typename IO::T* __restrict__ Bm,
+    const typename IO::T* __restrict__ Cm, const float* __restrict__ Av,
+    const double* __restrict__ cdt, const float* __restrict__ S, const float* __restrict__ dS,
+    typename IO::T* __restrict__ dC, float* __restrict__ g1, float* __restrict__ d_end,
+    double* __restrict__ dA_T, int N, int H) {
+    constexpr int RS = R + 4, PS = P + 4, L = KC, NBLK = KC / TB;
+    __shared__ float sM[wide_main<P, R>()];  // S_in [P, R], then one half of B | x
+    float* sB = sM;
+    float* sX = sM + TB * RS;
+    __shared__ __align__(16) double sCdt[KC];
+    __shared__ __align__(16) float sDt[KC];
+    __shared__ double sRed[NT / 64];
+    const ChunkHead c = decode_ch(blockIdx.x, N, H);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    const int64_t xrow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(P);
+    const int64_t xstride = static_cast<int64_t>(H) * P;
+    const int64_t brow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(R);
+    const int64_t bstride = static_cast<int64_t>(H) * R;
+    const double* cc = cdt + c.c_bhn * L;
+    const double a = static_cast<double>(Av[c.h]);
+    const double la2 = a * kLog2e;
+    const int tt[2] = {wave, NRT - 1 - wave};
+    const int tl[2] = {16 * tt[0] + i, 16 * tt[1] + i};
+
+    v4f creg[2][R / 16], dyreg[2][P / 16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int kk = 0; kk < R / 16; ++kk)
+            creg[q][kk] = io<IO>::ld4(Cm, brow0 + static_cast<int64_t>(tl[q]) * bstride + 16 * kk + 4 * g);
+#pragma unroll
+        for (int kk = 0; kk < P / 16; ++kk)
+            dyreg[q][kk] = io<IO>::ld4(dy, xrow0 + static_cast<int64_t>(tl[q]) * xstride + 16 * kk + 4 * g);
+    }
+    stage_mat<R, P>(sM, S + c.ch * (P * R));
+    if (tid < KC) {
+        sCdt[tid] = cc[tid];
+        sDt[tid] = dt[c.c_bhn * L + tid];
+    }
+    __syncthreads();
+
+    double dA = 0.0;  // this thread's part of the chunk's d_A (pair form)
+    // K4 backward: d_end = exp(A cdt[L-1]) <d_intra, S_in>
+    {
+        const float* dsp = dS + c.ch * (P * R);
+        double part = 0.0;
+        for (int idx = tid; idx < P * (R / 4); idx += NT) {
+            const int row = idx / (R / 4), c4 = idx - (idx / (R / 4)) * (R / 4);
+            const v4f u = *reinterpret_cast<const v4f*>(dsp + row * R + c4 * 4);
+            const v4f w = *reinterpret_cast<const v4f*>(sM + row * RS + c4 * 4);
+            part += static_cast<double>(u[0] * w[0] + u[1] * w[1]) +
+                    static_cast<double>(u[2] * w[2] + u[3] * w[3]);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+        if (lane == 0) sRed[wave] = part;
+        __syncthreads();
+        if (tid == 0) {
+            const double end = sCdt[L - 1];
+            const double de = (sRed[0] + sRed[1] + sRed[2] + sRed[3]) * exp(a * end);
+            const float def = static_cast<float>(de);
+            d_end[c.c_bhn] = def;
+            dA += static_cast<double>(def) * end;
+        }
+    }
+
+    // BLUE: d_C^T[r, t] = e_t sum_p S_in[p, r] dy[t, p]
+    v4f acc[2][R / 16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt) acc[q][rt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < P / 16; ++kk)
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float sv = sM[(16 * kk + 4 * g + v) * RS + rt * 16 + i];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) acc[q][rt] = mfma16(sv, dyreg[q][kk][v], acc[q][rt]);
+            }
+    double ct[2];
+    float gsum[2];  // this lane's part of g1[t = tl[q]]
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        ct[q] = sCdt[tl[q]];
+        const float et = exp2_of(la2 * ct[q]);
+        gsum[q] = 0.0f;
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt) {
+            acc[q][rt] *= et;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) gsum[q] += creg[q][rt][v] * acc[q][rt][v];
+        }
+        dA += static_cast<double>(gsum[q]) * ct[q];
+    }
+
+    // ORANGE / K2 backward, one (partner tile j, own tile q) pair at a time: the two
+    // own tiles' operands and accumulators already fill most of the register budget
+    auto pair = [&](int j, int u, auto qc) {
+        constexpr int q = decltype(qc)::value;
+        v4f cbt = zero4(), dwt = zero4();
+#pragma unroll
+        for (int kk = 0; kk < R / 16; ++kk) {
+            const v4f w = *reinterpret_cast<const v4f*>(sB + (16 * u + i) * RS + 16 * kk + 4 * g);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) cbt = mfma16(w[v], creg[q][kk][v], cbt);
+        }
+#pragma unroll
+        for (int kk = 0; kk < P / 16; ++kk) {
+            const v4f w = *reinterpret_cast<const v4f*>(sX + (16 * u + i) * PS + 16 * kk + 4 * g);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) dwt = mfma16(w[v], dyreg[q][kk][v], dwt);
+        }
+        const v2d cs01 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g);
+        const v2d cs23 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g + 2);
+        const v4f dts = *reinterpret_cast<const v4f*>(sDt + 16 * j + 4 * g);
+        const double csv[4] = {cs01.x, cs01.y, cs23.x, cs23.y};
+        float dcb[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const bool keep = (j < tt[q]) || (16 * j + 4 * g + v <= tl[q]);
+            const double gap = ct[q] - csv[v];
+            const float e = exp2_of(la2 * gap);  // masked pairs: gap < 0, discarded
+            const float dec = keep ? e : 0.0f;
+            dcb[v] = dwt[v] * dts[v] * dec;
+            const float ddiff = dcb[v] * cbt[v];
+            gsum[q] += ddiff;
+            dA += static_cast<double>(ddiff) * gap;
+        }
+        // K2 backward: d_C^T[r, t] += sum_s B[s, r] d_CB[t, s]
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                acc[q][rt] = mfma16(sB[(16 * u + 4 * g + v) * RS + rt * 16 + i], dcb[v], acc[q][rt]);
+    };
+    for (int half = 0; half < 2; ++half) {
+        __syncthreads();  // the previous contents of sM are consumed
+        stage_half_rows<IO, R>(sB, Bm + brow0, bstride, half);
+        stage_half_rows<IO, P>(sX, x + xrow0, xstride, half);
+        __syncthreads();
+        for (int u = 0; u < 4; ++u) {
+            const int j = 2 * u + half;
+            if (j <= tt[0]) pair(j, u, Q<0>{});
+            if (j <= tt[1]) pair(j, u, Q<1>{});
+        }
+    }
+
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int64_t row = brow0 + static_cast<int64_t>(tl[q]) * bstride;
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt) io<IO>::st4(dC, row + rt * 16 + 4 * g, acc[q][rt]);
+        const float gs = sum_over_g(gsum[q]);
+        if (g == 0) g1[c.c_bhn * L + tl[q]] = gs;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dA += __shfl_xor(dA, off);
+    __syncthreads();
+    if (lane == 0) sRed[wave] = dA;
+    __syncthreads();
+    if (tid == 0) {
+        // one partial per 64-token block slot: the chunk's total in the first, zeros after
+        dA_T[c.ch * NBLK] = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+        for (int b = 1; b < NBLK; ++b) dA_T[c.ch * NBLK + b] = 0.0;
+    }
+}
+
+// ------------------------------------------------------------------ dispatch
+#define SSD_WIDE_PR(X) \
+    X(16, 16) X(16, 32) X(16, 64) X(16, 128) \
+    X(32, 16) X(32, 32) X(32, 64) X(32, 128) \
+    X(64, 16) X(64, 32) X(64, 64) X(64, 128) \
+    X(128, 16) X(128, 32) X(128, 64) X(128, 128)
+
+bool wide_supported(const Shape& s) {
+    if (s.L != KC) return false;
+#define X(PP, RR) \
+    if (s.P == PP && s.R == RR) return wide_fits<PP, RR>();
+    SSD_WIDE_PR(X)
+#undef X
+    return false;
+}
+
+template <class IO>
+static hipError_t k5_wide_io(const Shape& s, const void* x, const float* dt, const void* Bm,
+                             const void* Cm, const float* A, const float* D, const double* cdt,
+                             const float* S, void* y, hipStream_t st) {
+    using T = typename IO::T;
+    const int64_t CH = static_cast<int64_t>(s.B) * s.N * s.H;
+    if (CH == 0) return hipSuccess;
+#define X(PP, RR)                                                                                 \
+    if (s.P == PP && s.R == RR) {                                                                 \
+        if constexpr (wide_fits<PP, RR>()) {                                                      \
+            hipLaunchKernelGGL((k5_chunk_scan_w<IO, PP, RR>), dim3(static_cast<unsigned>(CH)),    \
+                               dim3(NT), 0, st, static_cast<const T*>(x), dt,                     \
+                               static_cast<const T*>(Bm), static_cast<const T*>(Cm), A, D, cdt, S, \
+                               static_cast<T*>(y), s.N, s.H);                                     \
+            return hipGetLastError();                                                             \
+        }                                                                                         \
+        return hipErrorInvalidValue;                                                              \
+    }
+    SSD_WIDE_PR(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_k5_scan_wide(const Shape& s, const void* x, const float* dt, const void* Bm,
+                               const void* Cm, const float* A, const float* D, const double* cdt,
+                               const float* S, void* y, hipStream_t st) {
+    return s.io == 1 ? k5_wide_io<BF16>(s, x, dt, Bm, Cm, A, D, cdt, S, y, st)
+                     : k5_wide_io<F32>(s, x, dt, Bm, Cm, A, D, cdt, S, y, st);
+}
+
+template <class IO>
+static hipError_t target_wide_io(const Shape& s, const void* dy, const void* x, const float* dt,
+                                 const void* Bm, const void* Cm, const float* A,
+                                 const double* cdt, const float* S, const float* dS, void* dC,
+                                 float* g1, float* d_end, double* dA_T, hipStream_t st) {
+    using T = typename IO::T;
+    const int64_t CH = static_cast<int64_t>(s.B) * s.N * s.H;
+    if (CH == 0) return hipSuccess;
+#define X(PP, RR)                                                                                  \
+    if (s.P == PP && s.R == RR) {                                                                  \
+        if constexpr (wide_fits<PP, RR>()) {                                                       \
+            hipLaunchKernelGGL((k_bwd_target_w<IO, PP, RR>), dim3(static_cast<unsigned>(CH)),      \
+                               dim3(NT), 0, st, static_cast<const T*>(dy),                         \
+                               static_cast<const T*>(x), dt, static_cast<const T*>(Bm),            \
+                               static_cast<const T*>(Cm), A, cdt, S, dS, static_cast<T*>(dC), g1,  \
+                               d_end, dA_T, s.N, s.H);                                             \
+            return hipGetLastError();                                                              \
+        }                                                                                          \
+        return hipErrorInvalidValue;                                                               \
+    }
+    SSD_WIDE_PR(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_target_wide(const Shape& s, const void* dy, const void* x, const float* dt,
+                                  const void* Bm, const void* Cm, const float* A,
+                                  const double* cdt, const float* S, const float* dS, void* dC,
+                                  float* g1, float* d_end, double* dA_T, hipStream_t st) {
+    return s.io == 1
+               ? target_wide_io<BF16>(s, dy, x, dt, Bm, Cm, A, cdt, S, dS, dC, g1, d_end, dA_T, st)
+               : target_wide_io<F32>(s, dy, x, dt, Bm, Cm, A, cdt, S, dS, dC, g1, d_end, dA_T, st);
+}
+
+}  // namespace ssd

@@ -171,6 +171,66 @@ __device__ __forceinline__ void stage_rows2(float* l1, const typename IO::T* g1,
     }
 }
 
+// Row staging split in two so the loads can be issued long before the LDS
+// writes: one float4 per (thread, step), element idx = tid + it * NT is row
+// idx / (W / 4), float4 column idx % (W / 4); store_rows writes ROWS rows to LDS
+// rows of stride W + 4.
+template <int W, int ROWS>
+struct RowTiles {
+    static constexpr int V = W / 4, TOTAL = ROWS * V, IT = (TOTAL + NT - 1) / NT;
+};
+// Load the 64 rows of one half of a 128-row chunk that holds its even (half 0)
+// or odd (half 1) 16-row tiles: LDS row 16u + e is chunk row 16 (2u + half) + e.
+template <class IO, int W>
+__device__ __forceinline__ void load_half_rows(v4f* r, const typename IO::T* g, int64_t gstride,
+                                               int half) {
+    using RT = RowTiles<W, 64>;
+#pragma unroll
+    for (int it = 0; it < RT::IT; ++it) {
+        const int idx = static_cast<int>(threadIdx.x) + it * NT;
+        const int lr = idx / RT::V;
+        const int crow = 16 * (2 * (lr >> 4) + half) + (lr & 15);
+        if (RT::TOTAL % NT == 0 || idx < RT::TOTAL)
+            r[it] = io<IO>::ld4(g, static_cast<int64_t>(crow) * gstride + (idx % RT::V) * 4);
+    }
+}
+// Load and store one half (as load_half_rows) in batches of at most 4 float4
+// per thread, for callers with few registers to spare.
+template <class IO, int W>
+__device__ __forceinline__ void stage_half_rows(float* lds, const typename IO::T* g, int64_t gstride,
+                                                int half) {
+    using RT = RowTiles<W, 64>;
+    constexpr int BATCH = RT::IT < 4 ? RT::IT : 4;
+#pragma unroll
+    for (int b0 = 0; b0 < RT::IT; b0 += BATCH) {
+        v4f tmp[BATCH];
+#pragma unroll
+        for (int it = 0; it < BATCH; ++it) {
+            const int idx = static_cast<int>(threadIdx.x) + (b0 + it) * NT;
+            const int lr = idx / RT::V;
+            const int crow = 16 * (2 * (lr >> 4) + half) + (lr & 15);
+            if (b0 + it < RT::IT && (RT::TOTAL % NT == 0 || idx < RT::TOTAL))
+                tmp[it] = io<IO>::ld4(g, static_cast<int64_t>(crow) * gstride + (idx % RT::V) * 4);
+        }
+#pragma unroll
+        for (int it = 0; it < BATCH; ++it) {
+            const int idx = static_cast<int>(threadIdx.x) + (b0 + it) * NT;
+            if (b0 + it < RT::IT && (RT::TOTAL % NT == 0 || idx < RT::TOTAL))
+                *reinterpret_cast<v4f*>(lds + (idx / RT::V) * (W + 4) + (idx % RT::V) * 4) = tmp[it];
+        }
+    }
+}
+template <int W, int ROWS>
+__device__ __forceinline__ void store_rows(float* lds, const v4f* r) {
+    using RT = RowTiles<W, ROWS>;
+#pragma unroll
+    for (int it = 0; it < RT::IT; ++it) {
+        const int idx = static_cast<int>(threadIdx.x) + it * NT;
+        if (RT::TOTAL % NT == 0 || idx < RT::TOTAL)
+            *reinterpret_cast<v4f*>(lds + (idx / RT::V) * (W + 4) + (idx % RT::V) * 4) = r[it];
+    }
+}
+
 // Stage a contiguous fp32 [ROWS, W] matrix into LDS rows of stride W + 4.
 template <int W, int ROWS>
 __device__ __forceinline__ void stage_mat(float* lds, const float* g) {

@@ -86,6 +86,19 @@ hipError_t launch_k5_scan(const Shape& s, const void* x, const float* dt, const 
                           const void* Cm, const float* A, const float* D, const double* cdt,
                           const float* S, void* y, hipStream_t st);
 
+// Whole-chunk variants (k_chunk_wide.hip) of K5 and the backward target-row
+// kernel for 128-token chunks: one workgroup per chunk-head.  wide_supported(s)
+// says whether s takes them (chunk length 128, p * r <= 8192); launch_k5_scan
+// and launch_bwd_target route to them then.
+bool wide_supported(const Shape& s);
+hipError_t launch_k5_scan_wide(const Shape& s, const void* x, const float* dt, const void* Bm,
+                               const void* Cm, const float* A, const float* D, const double* cdt,
+                               const float* S, void* y, hipStream_t st);
+hipError_t launch_bwd_target_wide(const Shape& s, const void* dy, const void* x, const float* dt,
+                                  const void* Bm, const void* Cm, const float* A,
+                                  const double* cdt, const float* S, const float* dS, void* dC,
+                                  float* g1, float* d_end, double* dA_T, hipStream_t st);
+
 // Backward, target side (rows t): d_C, g1 (BLUE + ORANGE-target gradient w.r.t. the
 // cumsum), d_end, and d_A partials dA_T [b,n,h,block].
 hipError_t launch_bwd_target(const Shape& s, const void* dy, const void* x, const float* dt,
