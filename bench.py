@@ -12,7 +12,7 @@ length (min(chunk_len, 128); the workload's chunk_len fixes the buffer layout);
 the same step with the kernels at the layout's chunk length is timed as well
 and reported under "at_layout_chunk_len".
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload mamba2_130m_fp32]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 30] [--workload mamba2_130m_fp32] [--graph]
 """
 from __future__ import annotations
 
@@ -150,9 +150,11 @@ def cpu_baseline(w, inp, budget_s: float = 12.0, cap_s: float = 40.0):
 
 
 def timed_regions(step, args, stream):
-    """W warm-up steps, then K steps timed with torch events on the launch stream
-    (bracketed by device synchronisations) -> ms per step; then K more steps with the
-    library's per-kernel HIP events enabled -> {kernel: (total ms, launches)}.  The
+    """W warm-up steps, then K steps timed with torch events on the launch stream,
+    bracketed by device synchronisations -> ms per step (with --graph: K replays of the
+    step captured once into a HIP graph; the library neither allocates nor
+    synchronises, so capture needs nothing else); then K steps with the library's
+    per-kernel HIP events -> (ms per step, {kernel: (total ms, launches)}).  The
     per-kernel events sit between launches, so they are kept out of the first region."""
     import torch
     from mamba_ssd_chunked_amd import ssd
@@ -160,20 +162,28 @@ def timed_regions(step, args, stream):
         step()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+
+    def region(run):
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            run()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / args.steps
+
+    run = step
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()  # one untimed replay
+        run = graph.replay
+    ms = region(run)
     ssd.ssd_timing_enable(True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    ms_ev = region(step)
     ssd.ssd_timing_enable(False)
-    return ms, ev0.elapsed_time(ev1) / args.steps, ssd.ssd_timing_collect()
+    return ms, ms_ev, ssd.ssd_timing_collect()
 
 
 def bench_moments(args):
@@ -199,12 +209,13 @@ def bench_moments(args):
     stream = torch.cuda.current_stream()
 
     def step():
+        st = torch.cuda.current_stream()
         rc = ssd.ssd_state_moments(dims, d["x"], d["dt"], d["A"], d["B"], None, valid, m2, m1, count,
-                                   y, d["C"], d["D"], None, ws_f, stream)
+                                   y, d["C"], d["D"], None, ws_f, st)
         if rc:
             raise ssd.SsdError(rc, "ssd_state_moments", ssd.ssd_last_error())
         rc = ssd.ssd_state_moments_bwd(dims, d["d_m2"], d["d_m1"], d["x"], d["dt"], d["A"], d["B"],
-                                       None, valid, gx, gdt, gA, gB, ginit, ws_b, stream)
+                                       None, valid, gx, gdt, gA, gB, ginit, ws_b, st)
         if rc:
             raise ssd.SsdError(rc, "ssd_state_moments_bwd", ssd.ssd_last_error())
 
@@ -250,7 +261,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed steps first (the clocks settle within about 20 ms)")
     ap.add_argument("--workload", default="mamba2_130m_fp32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-moments", action="store_true",
@@ -259,6 +271,9 @@ def main():
                     help="chunk length the kernels run at (0: the library's automatic choice)")
     ap.add_argument("--no-layout-chunk", action="store_true",
                     help="skip the second timing with the kernels at the layout's chunk length")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured into a HIP graph (on this ROCm about "
+                         "1 %% slower than eager launches)")
     ap.add_argument("--moments-only", action="store_true",
                     help="run only the state-moments leg and print its JSON object")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -297,12 +312,13 @@ def main():
         ws_b = ssd.workspace(dims, ssd.SSD_OP_BWD, dev)
 
         def step():
+            st = torch.cuda.current_stream()
             rc = ssd.ssd_fwd(dims, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], init, y,
-                             final, ws_f, stream)
+                             final, ws_f, st)
             if rc:
                 raise ssd.SsdError(rc, "ssd_fwd", ssd.ssd_last_error())
             rc = ssd.ssd_bwd(dims, d["dy"], None, d["x"], d["dt"], d["A"], d["B"], d["C"],
-                             d["D"], init, gx, gdt, gA, gB, gC, gD, ginit, ws_b, stream)
+                             d["D"], init, gx, gdt, gA, gB, gC, gD, ginit, ws_b, st)
             if rc:
                 raise ssd.SsdError(rc, "ssd_bwd", ssd.ssd_last_error())
         return step

@@ -137,3 +137,42 @@ def test_empty_sequence_and_batch():
     inp0 = inputs.make_inputs(w0)
     gpu0 = gpu_fwd_bwd(inp0)
     assert gpu0["y"].size == 0 and np.all(gpu0["d_A"] == 0) and np.all(gpu0["d_D"] == 0)
+
+
+def test_graph_replay_matches_eager():
+    """The library neither allocates nor synchronises, so a fwd + bwd step can be captured
+    into a HIP graph; every replay (with eager work of the program in between) must give
+    the eager outputs bit for bit."""
+    w = inputs.custom(batch=2, seq=512, nheads=3, headdim=64, dstate=128, chunk_len=256,
+                      init_std=0.3, seed=57)
+    inp = inputs.make_inputs(w)
+    say("case graph capture of ssd_fwd + ssd_bwd")
+    d = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor) and k != "valid_len"}
+    dims = ssd.dims_of(d["x"], d["B"])
+    y, fin = torch.empty_like(d["x"]), torch.empty_like(d["d_final"])
+    outs = [torch.empty_like(d[k]) for k in ("x", "dt", "A", "B", "C", "D", "d_final")]
+    wf, wb = ssd.workspace(dims, ssd.SSD_OP_FWD), ssd.workspace(dims, ssd.SSD_OP_BWD)
+
+    def step():
+        st = torch.cuda.current_stream()
+        assert ssd.ssd_fwd(dims, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init"], y,
+                           fin, wf, st) == 0
+        assert ssd.ssd_bwd(dims, d["dy"], d["d_final"], d["x"], d["dt"], d["A"], d["B"], d["C"],
+                           d["D"], d["init"], *outs, wb, st) == 0
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in [y, fin] + outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for it in range(3):
+        for t in [y, fin] + outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip([y, fin] + outs, ref):
+            assert torch.equal(a, b), f"replay {it}"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
