@@ -189,9 +189,9 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target(
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const bool keep = (sb < tb) || (16 * j + 4 * g + v <= tl);
-                const double gap = ct - csv[v];
-                const float e = exp2_of(la2 * gap);  // masked pairs: gap < 0, discarded below
-                const float dec = keep ? e : 0.0f;
+                // masked pairs (s > t) take gap 0 and weight 0: arithmetic, not a branch
+                const double gap = keep ? ct - csv[v] : 0.0;
+                const float dec = exp2_of(la2 * gap) * (keep ? 1.0f : 0.0f);
                 dcb[v] = dwt[v] * dts[v] * dec;
                 const float ddiff = dcb[v] * cbt[v];
                 gsum += ddiff;
@@ -343,8 +343,9 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const bool keep = (tb > sb) || (16 * j + 4 * g + v >= sl);
-                const float e = exp2_of(la2 * (ctv[v] - cs));  // masked pairs discarded below
-                const float dec = keep ? e : 0.0f;
+                // masked pairs (t < s) take gap 0 and weight 0: arithmetic, not a branch
+                const double gap = keep ? ctv[v] - cs : 0.0;
+                const float dec = exp2_of(la2 * gap) * (keep ? 1.0f : 0.0f);
                 const float cbd = cb[v] * dec;
                 wv[v] = cbd * dts;
                 dcb[v] = dw[v] * dts * dec;

@@ -210,8 +210,9 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan(
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const bool keep = (sb < tb) || (16 * j + 4 * g + v <= tl);
-                const float e = exp2_of(la2 * (ct - csv[v]));  // masked pairs discarded below
-                wv[v] = keep ? cbt[v] * e * dts[v] : 0.0f;
+                // masked pairs (s > t) take gap 0 and weight 0: arithmetic, not a branch
+                const double gap = keep ? ct - csv[v] : 0.0;
+                wv[v] = cbt[v] * exp2_of(la2 * gap) * dts[v] * (keep ? 1.0f : 0.0f);
             }
 #pragma unroll
             for (int pt = 0; pt < P / 16; ++pt) {

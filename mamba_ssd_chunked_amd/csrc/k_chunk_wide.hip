@@ -144,23 +144,28 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
         const v2d cs23 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g + 2);
         const v4f dts = *reinterpret_cast<const v4f*>(sDt + 16 * j + 4 * g);
         const double csv[4] = {cs01.x, cs01.y, cs23.x, cs23.y};
+        // the update's x operands, read before the decay math so their LDS latency overlaps it
+        float xs[4][P / 16];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt) xs[v][pt] = sX[(16 * u + 4 * g + v) * PS + pt * 16 + i];
         float wv[2][4];
 #pragma unroll
         for (int q = QLO; q < 2; ++q)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
+                // masked pairs (s > t) take gap 0 and weight 0: arithmetic, not a branch
                 const bool keep = (j < tt[q]) || (16 * j + 4 * g + v <= tl[q]);
-                const float e = exp2_of(la2 * (ct[q] - csv[v]));  // masked pairs discarded
-                wv[q][v] = keep ? cbt[q][v] * e * dts[v] : 0.0f;
+                const double gap = keep ? ct[q] - csv[v] : 0.0;
+                wv[q][v] = cbt[q][v] * exp2_of(la2 * gap) * dts[v] * (keep ? 1.0f : 0.0f);
             }
 #pragma unroll
         for (int v = 0; v < 4; ++v)
 #pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt) {
-                const float xs = sX[(16 * u + 4 * g + v) * PS + pt * 16 + i];
+            for (int pt = 0; pt < P / 16; ++pt)
 #pragma unroll
-                for (int q = QLO; q < 2; ++q) acc[q][pt] = mfma16(wv[q][v], xs, acc[q][pt]);
-            }
+                for (int q = QLO; q < 2; ++q) acc[q][pt] = mfma16(wv[q][v], xs[v][pt], acc[q][pt]);
     };
     const float Dh = Dv[c.h];
     for (int half = 0; half < 2; ++half) {
@@ -326,9 +331,9 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const bool keep = (j < tt[q]) || (16 * j + 4 * g + v <= tl[q]);
-            const double gap = ct[q] - csv[v];
-            const float e = exp2_of(la2 * gap);  // masked pairs: gap < 0, discarded
-            const float dec = keep ? e : 0.0f;
+            // masked pairs (s > t) take gap 0 and weight 0: arithmetic, not a branch
+            const double gap = keep ? ct[q] - csv[v] : 0.0;
+            const float dec = exp2_of(la2 * gap) * (keep ? 1.0f : 0.0f);
             dcb[v] = dwt[v] * dts[v] * dec;
             const float ddiff = dcb[v] * cbt[v];
             gsum[q] += ddiff;
