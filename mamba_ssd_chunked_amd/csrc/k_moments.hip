@@ -476,7 +476,7 @@ __global__ __launch_bounds__(NT) void km_symmetrise(float* __restrict__ m2, int 
 
 // ----------------------------------------------------------- backward rows
 template <class IO, int P, int R>
-__global__ __launch_bounds__(NT) void km_bwd_rows(
+__global__ __launch_bounds__(NT, (P * R <= 64 * 64 && P <= 64) ? 2 : 1) void km_bwd_rows(
     const typename IO::T* __restrict__ x, const typename IO::T* __restrict__ Bm,
     const float* __restrict__ dt, const float* __restrict__ Av, const double* __restrict__ cdt,
     const double* __restrict__ phi, const double* __restrict__ psi,
@@ -667,6 +667,7 @@ __global__ __launch_bounds__(NT) void km_bwd_rows(
             sDt[tid] = dtc[b2 * TB + tid];
         }
         __syncthreads();
+#pragma unroll 1
         for (int j = 0; j < 4; ++j) {
             v4f gt = zero4(), qt = zero4();
 #pragma unroll
