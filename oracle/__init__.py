@@ -7,7 +7,8 @@ and its HIP library) never imports, links or calls it, and the two share no code
 The computation lives in ``ssd_oracle.c`` (plain C, fp64, single-threaded): the
 token-by-token recurrence ``h_t = exp(dt_t A) h_{t-1} + dt_t x_t (outer) B_t``,
 ``y_t = C_t . h_t + D x_t`` and its reverse-mode recurrence, plus the pooled
-state moments of the burn-mamba ``state_moments.rs`` page and their gradient.
+state moments of the burn-mamba ``state_moments.rs`` page and their gradient, and
+that page's participation ratio of the moments with its gradient.
 This module only builds the shared library with gcc and marshals numpy arrays.
 
 Every function takes and returns float64 numpy arrays in the pages' layouts:
@@ -72,6 +73,9 @@ def _open(path):
     lib.oracle_ssd_bwd.argtypes = [ctypes.POINTER(_Dims)] + [P] * 16 + [ctypes.c_int64]
     lib.oracle_state_moments.argtypes = [ctypes.POINTER(_Dims)] + [P] * 9
     lib.oracle_state_moments_bwd.argtypes = [ctypes.POINTER(_Dims)] + [P] * 13 + [ctypes.c_int64]
+    I64 = ctypes.c_int64
+    lib.oracle_moments_pr.argtypes = [I64, I64, I64, P, P, P, ctypes.c_int, P, P]
+    lib.oracle_moments_pr_bwd.argtypes = [I64, I64, I64, P, P, P, P, ctypes.c_int, P, P]
     for f in (lib.oracle_ssd_fwd, lib.oracle_ssd_bwd, lib.oracle_state_moments,
               lib.oracle_state_moments_bwd):
         f.restype = ctypes.c_int
@@ -165,3 +169,32 @@ def state_moments_bwd(d_m2, d_m1, x, dt, A, B, init=None, valid_len=None, seg: i
                                           _ptr(out["d_init"]), int(seg))
     _check(rc, "state_moments_bwd")
     return out
+
+
+def moments_pr(m2, m1, count, center=False):
+    """Participation ratio of the pooled moments (StateMoments::pr) and the raw
+    trace (StateMoments::trace).  m2 ``[b, h, r, r]``, m1 ``[b, h, r]``, count ``[b]``.
+    Returns ``(pr, trace)``, each ``[b, h]``."""
+    m2, m1 = _f64(m2), _f64(m1)
+    b, h, r, _ = m2.shape
+    cnt = np.ascontiguousarray(np.asarray(count, dtype=np.int64).reshape(b))
+    pr = np.empty((b, h))
+    tr = np.empty((b, h))
+    rc = _load().oracle_moments_pr(b, h, r, _ptr(m2), _ptr(m1), _ptr(cnt), int(bool(center)),
+                                   _ptr(pr), _ptr(tr))
+    _check(rc, "moments_pr")
+    return pr, tr
+
+
+def moments_pr_bwd(d_pr, m2, m1, count, center=False):
+    """Gradient of ``<d_pr, PR>`` w.r.t. m2 and m1 with the trace normaliser held
+    fixed.  Returns ``(d_m2, d_m1)``."""
+    d_pr, m2, m1 = _f64(d_pr), _f64(m2), _f64(m1)
+    b, h, r, _ = m2.shape
+    cnt = np.ascontiguousarray(np.asarray(count, dtype=np.int64).reshape(b))
+    d_m2 = np.empty_like(m2)
+    d_m1 = np.empty((b, h, r))
+    rc = _load().oracle_moments_pr_bwd(b, h, r, _ptr(d_pr), _ptr(m2), _ptr(m1), _ptr(cnt),
+                                       int(bool(center)), _ptr(d_m2), _ptr(d_m1))
+    _check(rc, "moments_pr_bwd")
+    return d_m2, d_m1

@@ -14,6 +14,9 @@
  *             d_A and d_initial_state.
  *   moments   m2 = sum_t h_t^T h_t, m1 = sum_t sum_p h_t[p,:] over the valid
  *             tokens, and their reverse-mode gradient.
+ *   PR        the participation ratio (tr S)^2 / ||S||_F^2 of S = m2 / count
+ *             (optionally centred), the raw trace tr(m2) / count, and the PR's
+ *             gradient with respect to m2 and m1.
  *
  * The chunked SSD of the burn-mamba "combined_backward.rs" page (kernels K1-K5
  * and the recompute backward) is a re-association of exactly this recurrence:
@@ -345,6 +348,106 @@ int oracle_state_moments_bwd(const oracle_dims* d, const double* d_m2,
             int rc = reverse_sweep(d, b, h, &c, x, dt, A, B, init, NULL, d_x, d_dt, &d_A[h],
                                    d_B, NULL, &unused, d_init, seg);
             if (rc) { free(S); return rc; }
+        }
+    }
+    free(S);
+    return 0;
+}
+
+/* ------------------------------------------------------- participation ratio
+ * StateMoments::pr of the burn-mamba "state_moments.rs" page, per (batch, head):
+ *   Sigma     = m2 / count            (centred: minus mu mu^T, mu = m1 / count)
+ *   s         = max(tr Sigma, min_positive)          (held fixed for the gradient)
+ *   Sigma_hat = Sigma / s
+ *   PR        = tr(Sigma_hat)^2 / max(||Sigma_hat||_F^2, div_eps)
+ * and StateMoments::trace = tr(m2) / count.  The floors are the page's fp32 ones:
+ * min_positive = 2^-126 (fp32's smallest normal) and div_eps = 1e-12 (the value
+ * the page's trace() documentation gives for PR's denominator clamp).  count is
+ * per batch row here; every count must be positive (the page asserts samples). */
+#define PR_MIN_POSITIVE 1.1754943508222875e-38
+#define PR_DIV_EPS 1e-12
+
+static void pr_sigma(int64_t R, const double* M2, const double* M1, double n, int center,
+                     double* S, double* mu) {
+    for (int64_t i = 0; i < R; ++i) mu[i] = (center && M1) ? M1[i] / n : 0.0;
+    for (int64_t i = 0; i < R; ++i)
+        for (int64_t j = 0; j < R; ++j) S[i * R + j] = M2[i * R + j] / n - mu[i] * mu[j];
+}
+
+int oracle_moments_pr(int64_t batch, int64_t nheads, int64_t R, const double* m2,
+                      const double* m1, const int64_t* count, int center, double* pr,
+                      double* trace) {
+    if (batch < 0 || nheads <= 0 || R <= 0 || !m2 || !count || !pr || (center && !m1)) return -1;
+    double* S = (double*)malloc(sizeof(double) * (R * R + R));
+    if (!S) return -2;
+    double* mu = S + R * R;
+    for (int64_t b = 0; b < batch; ++b) {
+        if (count[b] <= 0) { free(S); return -1; }
+        const double n = (double)count[b];
+        for (int64_t h = 0; h < nheads; ++h) {
+            const int64_t o = b * nheads + h;
+            pr_sigma(R, m2 + o * R * R, m1 ? m1 + o * R : NULL, n, center, S, mu);
+            double tr = 0.0, trm2 = 0.0;
+            for (int64_t i = 0; i < R; ++i) {
+                tr += S[i * R + i];
+                trm2 += m2[o * R * R + i * R + i];
+            }
+            const double s = tr > PR_MIN_POSITIVE ? tr : PR_MIN_POSITIVE;
+            double tr1 = 0.0, tr2 = 0.0;
+            for (int64_t i = 0; i < R; ++i) tr1 += S[i * R + i] / s;
+            for (int64_t k = 0; k < R * R; ++k) tr2 += (S[k] / s) * (S[k] / s);
+            if (tr2 < PR_DIV_EPS) tr2 = PR_DIV_EPS;
+            pr[o] = tr1 * tr1 / tr2;
+            if (trace) trace[o] = trm2 / n;
+        }
+    }
+    free(S);
+    return 0;
+}
+
+/* Gradient of sum_{b,h} d_pr * PR with the normaliser s held fixed (the page
+ * detaches it): with G_hat = dPR/dSigma_hat = 2 tr1/tr2 I - 2 tr1^2/tr2^2 Sigma_hat
+ * (the second term only while ||Sigma_hat||^2 exceeds div_eps, where the clamp
+ * is inactive), dPR/dSigma = G_hat / s, d_m2 = dPR/dSigma / count and, centred,
+ * d_m1 = -(G + G^T) mu / count with G = dPR/dSigma; uncentred d_m1 = 0. */
+int oracle_moments_pr_bwd(int64_t batch, int64_t nheads, int64_t R, const double* d_pr,
+                          const double* m2, const double* m1, const int64_t* count, int center,
+                          double* d_m2, double* d_m1) {
+    if (batch < 0 || nheads <= 0 || R <= 0 || !d_pr || !m2 || !count || !d_m2 ||
+        (center && !m1))
+        return -1;
+    double* S = (double*)malloc(sizeof(double) * (2 * R * R + R));
+    if (!S) return -2;
+    double* G = S + R * R;
+    double* mu = G + R * R;
+    for (int64_t b = 0; b < batch; ++b) {
+        if (count[b] <= 0) { free(S); return -1; }
+        const double n = (double)count[b];
+        for (int64_t h = 0; h < nheads; ++h) {
+            const int64_t o = b * nheads + h;
+            pr_sigma(R, m2 + o * R * R, m1 ? m1 + o * R : NULL, n, center, S, mu);
+            double tr = 0.0;
+            for (int64_t i = 0; i < R; ++i) tr += S[i * R + i];
+            const double s = tr > PR_MIN_POSITIVE ? tr : PR_MIN_POSITIVE;
+            double tr1 = 0.0, tr2 = 0.0;
+            for (int64_t i = 0; i < R; ++i) tr1 += S[i * R + i] / s;
+            for (int64_t k = 0; k < R * R; ++k) tr2 += (S[k] / s) * (S[k] / s);
+            const int live = tr2 > PR_DIV_EPS;
+            if (!live) tr2 = PR_DIV_EPS;
+            for (int64_t i = 0; i < R; ++i)
+                for (int64_t j = 0; j < R; ++j) {
+                    double gh = (i == j) ? 2.0 * tr1 / tr2 : 0.0;
+                    if (live) gh -= 2.0 * tr1 * tr1 / (tr2 * tr2) * (S[i * R + j] / s);
+                    G[i * R + j] = d_pr[o] * gh / s;
+                }
+            for (int64_t k = 0; k < R * R; ++k) d_m2[o * R * R + k] = G[k] / n;
+            if (d_m1)
+                for (int64_t i = 0; i < R; ++i) {
+                    double acc = 0.0;
+                    if (center)
+                        for (int64_t j = 0; j < R; ++j) acc -= (G[i * R + j] + G[j * R + i]) * mu[j];
+                    d_m1[o * R + i] = acc / n;
+                }
         }
     }
     free(S);

@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 import test_oracle_moments as tm
+import test_oracle_pr as tp
 import test_oracle_ssd as ts
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")
@@ -34,6 +35,14 @@ MUTANTS = {
     "dx_transposed_contraction": ("for (int64_t r = 0; r < R; ++r) acc += G[p * R + r] * Bt[r];",
                                   "for (int64_t r = 0; r < R; ++r) acc += G[r * (P > R ? 0 : 1) + p * R] * Bt[r];"),
     "moments_count_without_headdim": ("count[b] = v * P;", "count[b] = v;"),
+    "pr_centre_sign": ("S[i * R + j] = M2[i * R + j] / n - mu[i] * mu[j];",
+                       "S[i * R + j] = M2[i * R + j] / n + mu[i] * mu[j];"),
+    "pr_trace_of_sigma": ("if (trace) trace[o] = trm2 / n;", "if (trace) trace[o] = tr;"),
+    "pr_grad_drops_numerator": ("double gh = (i == j) ? 2.0 * tr1 / tr2 : 0.0;",
+                                "double gh = 0.0;"),
+    "pr_dm1_not_transposed": ("acc -= (G[i * R + j] + G[j * R + i]) * mu[j];",
+                              "acc -= 2.0 * G[i * R + j] * mu[j];"),
+    "pr_dm2_missing_count": ("d_m2[o * R * R + k] = G[k] / n;", "d_m2[o * R * R + k] = G[k];"),
 }
 
 PINS = [
@@ -47,6 +56,10 @@ PINS = [
     tm.test_I7_closed_form_matches,
     tm.test_moments_finite_differences,
     tm.test_golden_hand_worked_moments,
+    lambda: tp.test_pr_equals_the_eigenvalue_form(True),
+    tp.test_trace_is_the_mean_squared_sample_norm,
+    lambda: tp.test_pr_gradient_matches_direct_formula(True),
+    tp.test_pr_gradient_has_no_radial_part,
 ]
 
 
