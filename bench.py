@@ -186,6 +186,51 @@ def timed_regions(step, args, stream):
     return ms, ms_ev, ssd.ssd_timing_collect()
 
 
+def pr_bytes(w, kernel: str):
+    """Algorithmic HBM bytes of one launch of a PR kernel over all (b, h) slices (centred):
+    fwd reads m2, m1 and writes pr, trace; bwd reads d_pr, m2, m1 and writes d_m2, d_m1."""
+    bh, r = w.batch * w.nheads, w.dstate
+    if kernel == "k_pr_fwd":
+        return bh * (4 * (r * r + r) + 8)
+    if kernel == "k_pr_bwd":
+        return bh * (8 * (r * r + r) + 4)
+    return None
+
+
+def bench_pr(args, w, dims, m2, m1, count, stream):
+    """ssd_moments_pr + ssd_moments_pr_bwd (centred) on the moments of the workload."""
+    import torch
+    from mamba_ssd_chunked_amd import ssd
+    dev = m2.device
+    bh = (w.batch, w.nheads, w.dstate)
+    pr = torch.empty(w.batch, w.nheads, device=dev)
+    tr = torch.empty_like(pr)
+    dpr = torch.ones_like(pr)
+    gm2, gm1 = torch.empty_like(m2), torch.empty_like(m1)
+
+    def step():
+        st = torch.cuda.current_stream()
+        rc = ssd.ssd_moments_pr(*bh, m2, m1, count, 1, pr, tr, st)
+        if rc:
+            raise ssd.SsdError(rc, "ssd_moments_pr", ssd.ssd_last_error())
+        rc = ssd.ssd_moments_pr_bwd(*bh, dpr, m2, m1, count, 1, gm2, gm1, st)
+        if rc:
+            raise ssd.SsdError(rc, "ssd_moments_pr_bwd", ssd.ssd_last_error())
+
+    ms, _, kt = timed_regions(step, args, stream)
+    kernels = {}
+    for name, (tot, cnt) in kt.items():
+        avg = tot / cnt
+        ent = {"avg_us": round(avg * 1e3, 2), "launches_per_step": cnt / args.steps}
+        nbytes = pr_bytes(w, name)
+        if nbytes is not None:
+            rate = nbytes / (avg / 1e3)
+            ent.update(bytes=nbytes, gbps=round(rate / 1e9, 1), hbm_frac=round(rate / PEAK_HBM, 4))
+        kernels[name] = ent
+    return {"step": "ssd_moments_pr + ssd_moments_pr_bwd, centred, on the workload's m2 / m1",
+            "us_per_step": round(ms * 1e3, 2), "kernels": kernels}
+
+
 def bench_moments(args):
     """ssd_state_moments (with y) + ssd_state_moments_bwd on the moments workload."""
     import torch
@@ -239,6 +284,32 @@ def bench_moments(args):
            "ms_per_step_with_kernel_events": round(ms_ev, 4),
            "value": round(w.batch * w.seq / (ms / 1e3), 1), "unit": "tokens/s",
            "step": "ssd_state_moments (with y) + ssd_state_moments_bwd", "kernels": kernels}
+    res["pr"] = bench_pr(args, w, dims, m2, m1, count, stream)
+
+    # The PR-penalty loop: moments (with y) -> PR -> dPR/d(m2, m1) -> moments backward.
+    prv = torch.empty(w.batch, w.nheads, device=dev)
+    dpr = torch.ones_like(prv)
+    gm2, gm1 = torch.empty_like(m2), torch.empty_like(m1)
+    bh = (w.batch, w.nheads, w.dstate)
+
+    def loop_step():
+        st = torch.cuda.current_stream()
+        for rc, what in (
+                (ssd.ssd_state_moments(dims, d["x"], d["dt"], d["A"], d["B"], None, valid, m2, m1,
+                                       count, y, d["C"], d["D"], None, ws_f, st), "ssd_state_moments"),
+                (ssd.ssd_moments_pr(*bh, m2, m1, count, 1, prv, None, st), "ssd_moments_pr"),
+                (ssd.ssd_moments_pr_bwd(*bh, dpr, m2, m1, count, 1, gm2, gm1, st), "ssd_moments_pr_bwd"),
+                (ssd.ssd_state_moments_bwd(dims, gm2, gm1, d["x"], d["dt"], d["A"], d["B"], None, valid,
+                                           gx, gdt, gA, gB, ginit, ws_b, st), "ssd_state_moments_bwd")):
+            if rc:
+                raise ssd.SsdError(rc, what, ssd.ssd_last_error())
+
+    ms_loop, _, _ = timed_regions(loop_step, args, stream)
+    res["pr_penalty_loop"] = {
+        "step": "ssd_state_moments (with y) + ssd_moments_pr + ssd_moments_pr_bwd (centred) + "
+                "ssd_state_moments_bwd fed the PR gradient",
+        "ms_per_step": round(ms_loop, 4), "value": round(w.batch * w.seq / (ms_loop / 1e3), 1),
+        "unit": "tokens/s"}
     if not args.no_cpu_baseline:
         import oracle
         hs = [0]

@@ -155,6 +155,48 @@ int ssd_state_moments_bwd(const ssd_dims* dims, const float* d_m2, const float* 
                           float* d_dt, float* d_A, void* d_B, float* d_init, void* ws,
                           size_t ws_bytes, void* stream);
 
+/*
+ * Participation ratio of the pooled moments (state_moments.rs page,
+ * StateMoments::pr and StateMoments::trace), per (b, h) slice with
+ * n = count[b], mu = m1 / n:
+ *   Sigma = m2 / n  (center != 0: Sigma = m2 / n - mu mu^T)
+ *   s     = max(tr Sigma, 2^-126)          (fp32's smallest normal)
+ *   pr    = tr(Sigma/s)^2 / max(||Sigma/s||_F^2, 1e-12)
+ *   trace = tr(m2) / n                     (raw, never centred)
+ * The floors only act on a vanishing state: s on Sigma == 0, the 1e-12
+ * denominator clamp once the state has collapsed (it then drags pr below 1).
+ *   batch >= 0, nheads > 0, dstate in {16, 32, 64, 128} (as for the moments)
+ *   m2     [b,h,r,r] in, fp32, 16-byte aligned
+ *   m1     [b,h,r]   in, fp32; required when center != 0, else ignored (may be NULL)
+ *   count  [b]       in, HOST int64, each > 0 (ssd_state_moments' count; the page
+ *                    has one count for all rows, here each row has its own)
+ *   pr     [b,h]     out, fp32
+ *   trace  [b,h]     out, fp32, nullable (not written when NULL)
+ * Sums and Sigma are formed in fp64; results are rounded to fp32 once.
+ * Errors: SSD_ERR_NULL, SSD_ERR_SHAPE (a dimension out of range, count <= 0),
+ * SSD_ERR_UNSUPPORTED (dstate, alignment), SSD_ERR_HIP.  No workspace.
+ */
+int ssd_moments_pr(int64_t batch, int64_t nheads, int64_t dstate, const float* m2,
+                   const float* m1, const int64_t* count, int center, float* pr, float* trace,
+                   void* stream);
+
+/*
+ * Gradient of sum_{b,h} d_pr[b,h] * pr[b,h] with respect to m2 and m1, with the
+ * normaliser s held fixed as on the page (it is detached there; the ratio does
+ * not change with the scale of Sigma, so this is also the exact gradient of
+ * (tr Sigma)^2 / ||Sigma||_F^2 wherever the 1e-12 clamp is inactive):
+ *   G     = d_pr (2 tr1/tr2 I - 2 tr1^2/tr2^2 Sigma/s) / s,  tr1 = tr(Sigma)/s,
+ *           tr2 = max(||Sigma/s||_F^2, 1e-12); the Sigma term is dropped while
+ *           the clamp is active
+ *   d_m2  = G / n                                   [b,h,r,r] out, fp32, 16-byte aligned
+ *   d_m1  = -(G + G^T) mu / n when center, else 0   [b,h,r] out, fp32, nullable
+ * d_pr [b,h] in, fp32; m2, m1, count, center as for ssd_moments_pr.  The result
+ * stays finite for every state magnitude down to the floors.
+ */
+int ssd_moments_pr_bwd(int64_t batch, int64_t nheads, int64_t dstate, const float* d_pr,
+                       const float* m2, const float* m1, const int64_t* count, int center,
+                       float* d_m2, float* d_m1, void* stream);
+
 /* Message for the last nonzero status returned on this thread ("" if none). */
 const char* ssd_last_error(void);
 

@@ -245,6 +245,30 @@ int check_io_ptrs(const ssd::Shape& s, std::initializer_list<std::pair<const voi
     return SSD_OK;
 }
 
+// Shared checks of the two PR entry points (sizes, counts, pointers, alignment).
+int validate_pr(const char* who, int64_t batch, int64_t nheads, int64_t dstate, const float* m2,
+                const float* m1, const int64_t* count, int center, const void* out,
+                const void* out16) {
+    if (batch < 0 || nheads <= 0 || batch > (1 << 30) || nheads > (1 << 30) ||
+        batch * nheads > (int64_t(1) << 31) - 1)
+        return fail(SSD_ERR_SHAPE, "%s: need 0 <= batch, 0 < nheads and batch * nheads < 2^31 "
+                    "(got %lld, %lld)", who, (long long)batch, (long long)nheads);
+    if (!pow2_in(dstate, 16, 128))
+        return fail(SSD_ERR_UNSUPPORTED, "%s: dstate must be 16, 32, 64 or 128 (got %lld)", who,
+                    (long long)dstate);
+    if (batch == 0) return SSD_OK;
+    if (!m2 || !count || !out || (center && !m1))
+        return fail(SSD_ERR_NULL, "%s: m2, count, the outputs%s are required", who,
+                    center ? " and m1 (center)" : "");
+    for (int64_t b = 0; b < batch; ++b)
+        if (count[b] <= 0)
+            return fail(SSD_ERR_SHAPE, "%s: count[%lld] = %lld holds no samples", who, (long long)b,
+                        (long long)count[b]);
+    if (int rc = check_align(m2, "m2", 16)) return rc;
+    if (int rc = check_align(out16, "d_m2", 16)) return rc;
+    return SSD_OK;
+}
+
 int check_valid_len(const ssd::Shape& s, const int64_t* valid_len) {
     if (!valid_len) return SSD_OK;
     const int64_t seq = static_cast<int64_t>(s.N) * s.L;
@@ -518,6 +542,35 @@ int ssd_state_moments_bwd(const ssd_dims* dims, const float* d_m2, const float* 
     SSD_HIP(ssd::launch_km_scan_bwd(s, cdt, dt, A, vd, ddtW, rho, eta, zeta, hsh, hdm, dend2, d_dt, st),
             "km_scan_bwd");
     SSD_HIP(ssd::launch_reduce_heads(s, dA, nullptr, nullptr, s.nblk(), d_A, nullptr, st), "reduce_heads");
+    return ok();
+}
+
+int ssd_moments_pr(int64_t batch, int64_t nheads, int64_t dstate, const float* m2,
+                   const float* m1, const int64_t* count, int center, float* pr, float* trace,
+                   void* stream) {
+    if (int rc = validate_pr("ssd_moments_pr", batch, nheads, dstate, m2, m1, count, center, pr,
+                             nullptr))
+        return rc;
+    if (batch == 0) return ok();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    SSD_HIP(ssd::launch_pr_fwd((int)batch, (int)nheads, (int)dstate, m2, center ? m1 : nullptr,
+                               count, center != 0, pr, trace, st),
+            "k_pr_fwd");
+    return ok();
+}
+
+int ssd_moments_pr_bwd(int64_t batch, int64_t nheads, int64_t dstate, const float* d_pr,
+                       const float* m2, const float* m1, const int64_t* count, int center,
+                       float* d_m2, float* d_m1, void* stream) {
+    if (int rc = validate_pr("ssd_moments_pr_bwd", batch, nheads, dstate, m2, m1, count, center,
+                             d_m2, d_m2))
+        return rc;
+    if (batch == 0) return ok();
+    if (!d_pr) return fail(SSD_ERR_NULL, "ssd_moments_pr_bwd: d_pr is required");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    SSD_HIP(ssd::launch_pr_bwd((int)batch, (int)nheads, (int)dstate, d_pr, m2,
+                               center ? m1 : nullptr, count, center != 0, d_m2, d_m1, st),
+            "k_pr_bwd");
     return ok();
 }
 

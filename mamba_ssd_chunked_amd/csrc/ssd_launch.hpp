@@ -130,4 +130,23 @@ hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStrea
 // dst[i] = (vals ? vals[i] : fill) for i < n; the values travel as kernel arguments.
 hipError_t launch_set_i64(int64_t* dst, const int64_t* vals, int64_t fill, int64_t n, hipStream_t st);
 
+// ------------------------------------------------------ participation ratio
+// 1 / count[b] for up to kMax batch rows, passed by value to the PR kernels.
+struct PrCounts {
+    static constexpr int kMax = 64;
+    double inv_n[kMax];
+};
+
+// Per (b, h) slice of m2 [B,H,R,R] (m1 [B,H,R], read only when center != 0):
+// pr[b,h] and, if trace != NULL, trace[b,h] = tr(m2) / count[b].  count is host.
+hipError_t launch_pr_fwd(int B, int H, int R, const float* m2, const float* m1,
+                         const int64_t* count, int center, float* pr, float* trace,
+                         hipStream_t st);
+
+// Gradient of sum d_pr * pr: d_m2 [B,H,R,R] and, if d_m1 != NULL, d_m1 [B,H,R]
+// (zero unless center != 0).
+hipError_t launch_pr_bwd(int B, int H, int R, const float* d_pr, const float* m2, const float* m1,
+                         const int64_t* count, int center, float* d_m2, float* d_m1,
+                         hipStream_t st);
+
 }  // namespace ssd

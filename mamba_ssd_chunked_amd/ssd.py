@@ -28,7 +28,8 @@ SSD_OP_FWD, SSD_OP_BWD, SSD_OP_MOMENTS, SSD_OP_MOMENTS_BWD = 0, 1, 2, 3
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
           4: "SSD_ERR_DTYPE", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_HIP"}
 EXPORTS = ("ssd_workspace_size", "ssd_fwd", "ssd_bwd", "ssd_state_moments",
-           "ssd_state_moments_bwd", "ssd_last_error", "ssd_timing_enable", "ssd_timing_collect")
+           "ssd_state_moments_bwd", "ssd_moments_pr", "ssd_moments_pr_bwd", "ssd_last_error",
+           "ssd_timing_enable", "ssd_timing_collect")
 
 
 class ssd_dims(ctypes.Structure):
@@ -68,8 +69,11 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_bwd.argtypes = [D] + [P] * 17 + [ctypes.c_size_t, P]
     lib.ssd_state_moments.argtypes = [D] + [P] * 14 + [ctypes.c_size_t, P]
     lib.ssd_state_moments_bwd.argtypes = [D] + [P] * 14 + [ctypes.c_size_t, P]
+    I64 = ctypes.c_int64
+    lib.ssd_moments_pr.argtypes = [I64, I64, I64, P, P, P, ctypes.c_int, P, P, P]
+    lib.ssd_moments_pr_bwd.argtypes = [I64, I64, I64, P, P, P, P, ctypes.c_int, P, P, P]
     for f in ("ssd_workspace_size", "ssd_fwd", "ssd_bwd", "ssd_state_moments",
-              "ssd_state_moments_bwd"):
+              "ssd_state_moments_bwd", "ssd_moments_pr", "ssd_moments_pr_bwd"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ssd_last_error.argtypes = []
     lib.ssd_last_error.restype = ctypes.c_char_p
@@ -236,6 +240,28 @@ def ssd_state_moments_bwd(dims, d_m2, d_m1, x, dt, A, B, init, valid_len, d_x, d
                                                 _stream(stream))
 
 
+def ssd_moments_pr(batch, nheads, dstate, m2, m1, count, center, pr, trace, stream=None) -> int:
+    f, bh = torch.float32, batch * nheads
+    args = [_ptr(m2, "m2", f, bh * dstate * dstate, True),
+            _ptr(m1, "m1", f, bh * dstate, bool(center)),
+            _ptr(count, "count", torch.int64, batch, True)]
+    outs = [_ptr(pr, "pr", f, bh, True), _ptr(trace, "trace", f, bh, False)]
+    return load_library().ssd_moments_pr(batch, nheads, dstate, *args, int(bool(center)), *outs,
+                                         _stream(stream))
+
+
+def ssd_moments_pr_bwd(batch, nheads, dstate, d_pr, m2, m1, count, center, d_m2, d_m1,
+                       stream=None) -> int:
+    f, bh = torch.float32, batch * nheads
+    args = [_ptr(d_pr, "d_pr", f, bh, True), _ptr(m2, "m2", f, bh * dstate * dstate, True),
+            _ptr(m1, "m1", f, bh * dstate, bool(center)),
+            _ptr(count, "count", torch.int64, batch, True)]
+    outs = [_ptr(d_m2, "d_m2", f, bh * dstate * dstate, True),
+            _ptr(d_m1, "d_m1", f, bh * dstate, False)]
+    return load_library().ssd_moments_pr_bwd(batch, nheads, dstate, *args, int(bool(center)),
+                                             *outs, _stream(stream))
+
+
 # ------------------------------------------------------------ allocating helpers
 def _check(rc: int, where: str):
     if rc != 0:
@@ -311,3 +337,34 @@ def state_moments_bwd(d_m2, x, dt, A, B, init=None, valid_len=None, d_m1=None, w
                                  out["d_dt"], out["d_A"], out["d_B"], out["d_init"], ws, stream),
            "ssd_state_moments_bwd")
     return out
+
+
+def _count_tensor(count, batch):
+    if not isinstance(count, torch.Tensor):
+        count = torch.tensor(list(count) if hasattr(count, "__len__") else [count] * batch,
+                             dtype=torch.int64)
+    return count.to(torch.int64).contiguous()
+
+
+def moments_pr(m2, m1, count, center=False, stream=None):
+    """Participation ratio and raw trace of pooled moments: returns ``(pr, trace)``,
+    each ``[b, h]`` fp32.  m2 ``[b, h, r, r]``, m1 ``[b, h, r]`` (device), count host
+    int64 ``[b]`` (or one int for every row)."""
+    b, h, r, _ = m2.shape
+    count = _count_tensor(count, b)
+    pr = torch.empty((b, h), device=m2.device)
+    trace = torch.empty((b, h), device=m2.device)
+    _check(ssd_moments_pr(b, h, r, m2, m1 if center else None, count, center, pr, trace, stream),
+           "ssd_moments_pr")
+    return pr, trace
+
+
+def moments_pr_bwd(d_pr, m2, m1, count, center=False, want_d_m1=True, stream=None):
+    """Gradient of ``<d_pr, PR>``: returns ``(d_m2, d_m1)`` (d_m1 None unless wanted)."""
+    b, h, r, _ = m2.shape
+    count = _count_tensor(count, b)
+    d_m2 = torch.empty_like(m2)
+    d_m1 = torch.empty((b, h, r), device=m2.device) if want_d_m1 else None
+    _check(ssd_moments_pr_bwd(b, h, r, d_pr, m2, m1 if center else None, count, center, d_m2,
+                              d_m1, stream), "ssd_moments_pr_bwd")
+    return d_m2, d_m1

@@ -147,3 +147,30 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(ssd, "_lib", None)
     with pytest.raises(ImportError, match="missing"):
         ssd.load_library("/nonexistent/libmamba_ssd_hip.so")
+
+
+def counts(*v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(b=-1), 2), (dict(h=0), 2), (dict(r=8), 3), (dict(r=48), 3), (dict(r=256), 3),
+    (dict(count=(4, 0)), 2), (dict(count=(-3, 4)), 2), (dict(m2=0), 1), (dict(out=0), 1),
+    (dict(center=1, m1=0), 1), (dict(m2=FAKE + 4), 3), (dict(out=FAKE + 8), 3),
+])
+def test_pr_entry_points_reject_bad_arguments(lib, case, code):
+    a = dict(b=2, h=3, r=32, m2=FAKE, m1=FAKE, count=(5, 7), center=0, out=FAKE)
+    a.update(case)
+    cnt = counts(*a["count"])
+    if "out" not in case or case["out"] == 0:  # pr itself needs no 16-byte alignment
+        rc = lib.ssd_moments_pr(a["b"], a["h"], a["r"], a["m2"], a["m1"], cnt, a["center"],
+                                a["out"], None, None)
+        assert rc == code, ssd.ssd_last_error()
+    rc = lib.ssd_moments_pr_bwd(a["b"], a["h"], a["r"], FAKE, a["m2"], a["m1"], cnt, a["center"],
+                                a["out"], None, None)
+    assert rc == code, ssd.ssd_last_error()
+
+
+def test_pr_of_an_empty_batch_is_a_no_op(lib):
+    assert lib.ssd_moments_pr(0, 3, 32, None, None, None, 1, None, None, None) == 0
+    assert lib.ssd_moments_pr_bwd(0, 3, 32, None, None, None, None, 1, None, None, None) == 0
