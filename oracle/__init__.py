@@ -8,7 +8,8 @@ The computation lives in ``ssd_oracle.c`` (plain C, fp64, single-threaded): the
 token-by-token recurrence ``h_t = exp(dt_t A) h_{t-1} + dt_t x_t (outer) B_t``,
 ``y_t = C_t . h_t + D x_t`` and its reverse-mode recurrence, plus the pooled
 state moments of the burn-mamba ``state_moments.rs`` page and their gradient, and
-that page's participation ratio of the moments with its gradient.
+that page's participation ratio of the moments with its gradient, and the
+gamma-weighted same-step correction ``y_diag`` of the Mamba-3 SSD with its gradient.
 This module only builds the shared library with gcc and marshals numpy arrays.
 
 Every function takes and returns float64 numpy arrays in the pages' layouts:
@@ -76,6 +77,8 @@ def _open(path):
     I64 = ctypes.c_int64
     lib.oracle_moments_pr.argtypes = [I64, I64, I64, P, P, P, ctypes.c_int, P, P]
     lib.oracle_moments_pr_bwd.argtypes = [I64, I64, I64, P, P, P, P, ctypes.c_int, P, P]
+    lib.oracle_diag_fwd.argtypes = [I64] * 5 + [P] * 5
+    lib.oracle_diag_bwd.argtypes = [I64] * 5 + [P] * 9
     for f in (lib.oracle_ssd_fwd, lib.oracle_ssd_bwd, lib.oracle_state_moments,
               lib.oracle_state_moments_bwd):
         f.restype = ctypes.c_int
@@ -198,3 +201,33 @@ def moments_pr_bwd(d_pr, m2, m1, count, center=False):
                                        int(bool(center)), _ptr(d_m2), _ptr(d_m1))
     _check(rc, "moments_pr_bwd")
     return d_m2, d_m1
+
+
+def _diag_dims(V, B):
+    """V ``[..., m, h, p]`` and B ``[..., m, h, r]``: the leading axes ([b, n, l]) are tokens."""
+    *lead, m, h, p = V.shape
+    r = B.shape[-1]
+    return int(np.prod(lead)) if lead else 1, m, h, p, r
+
+
+def diag_fwd(V, B, C, gamma):
+    """Same-step correction y_diag (mamba3 diag.rs page).  V ``[b, n, l, m, h, p]``,
+    B / C ``[b, n, l, m, h, r]``, gamma ``[b, n, l, h]``; returns y_diag like V."""
+    V, B, C, gamma = map(_f64, (V, B, C, gamma))
+    T, m, h, p, r = _diag_dims(V, B)
+    y = np.empty_like(V)
+    _check(_load().oracle_diag_fwd(T, m, h, p, r, _ptr(V), _ptr(B), _ptr(C), _ptr(gamma), _ptr(y)),
+           "diag_fwd")
+    return y
+
+
+def diag_bwd(dy, V, B, C, gamma):
+    """Gradients of ``<dy, y_diag>``: dict(d_v, d_b, d_c, d_gamma)."""
+    dy, V, B, C, gamma = map(_f64, (dy, V, B, C, gamma))
+    T, m, h, p, r = _diag_dims(V, B)
+    out = dict(d_v=np.empty_like(V), d_b=np.empty_like(B), d_c=np.empty_like(C),
+               d_gamma=np.empty_like(gamma))
+    _check(_load().oracle_diag_bwd(T, m, h, p, r, _ptr(dy), _ptr(V), _ptr(B), _ptr(C), _ptr(gamma),
+                                   _ptr(out["d_v"]), _ptr(out["d_b"]), _ptr(out["d_c"]),
+                                   _ptr(out["d_gamma"])), "diag_bwd")
+    return out

@@ -17,6 +17,9 @@
  *   PR        the participation ratio (tr S)^2 / ||S||_F^2 of S = m2 / count
  *             (optionally centred), the raw trace tr(m2) / count, and the PR's
  *             gradient with respect to m2 and m1.
+ *   y_diag    the gamma-weighted same-step correction of the Mamba-3 SSD
+ *             (per token and head: gamma * (C B^T) V over the mimo axis) and its
+ *             reverse-mode gradient.
  *
  * The chunked SSD of the burn-mamba "combined_backward.rs" page (kernels K1-K5
  * and the recompute backward) is a re-association of exactly this recurrence:
@@ -451,5 +454,103 @@ int oracle_moments_pr_bwd(int64_t batch, int64_t nheads, int64_t R, const double
         }
     }
     free(S);
+    return 0;
+}
+
+/* ------------------------------------------------------ same-step correction
+ * The gamma-weighted same-step term of the burn-mamba page
+ * "mamba3/single_ssd/ssd/serial_recalculated/diag.rs" (module doc and the
+ * general MIMO path), for every token t (the [b, n, l] axes flattened) and head h:
+ *   qk[mo][mi]   = sum_r C[t,mo,h,r] B[t,mi,h,r]
+ *   y[t,mo,h,p]  = gamma[t,h] sum_mi qk[mo][mi] V[t,mi,h,p]
+ * Layouts: V, y [T, M, H, P]; B, C [T, M, H, R]; gamma [T, H]. */
+static int64_t dg_off(int64_t t, int64_t m, int64_t h, int64_t M, int64_t H, int64_t W) {
+    return ((t * M + m) * H + h) * W;
+}
+
+int oracle_diag_fwd(int64_t T, int64_t M, int64_t H, int64_t P, int64_t R, const double* V,
+                    const double* B, const double* C, const double* gamma, double* y) {
+    if (T < 0 || M <= 0 || H <= 0 || P <= 0 || R <= 0) return -1;
+    if (T > 0 && (!V || !B || !C || !gamma || !y)) return -1;
+    double* qk = (double*)malloc(sizeof(double) * M * M);
+    if (!qk) return -2;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            for (int64_t mo = 0; mo < M; ++mo)
+                for (int64_t mi = 0; mi < M; ++mi) {
+                    double acc = 0.0;
+                    for (int64_t r = 0; r < R; ++r)
+                        acc += C[dg_off(t, mo, h, M, H, R) + r] * B[dg_off(t, mi, h, M, H, R) + r];
+                    qk[mo * M + mi] = acc;
+                }
+            const double g = gamma[t * H + h];
+            for (int64_t mo = 0; mo < M; ++mo)
+                for (int64_t p = 0; p < P; ++p) {
+                    double acc = 0.0;
+                    for (int64_t mi = 0; mi < M; ++mi) acc += qk[mo * M + mi] * V[dg_off(t, mi, h, M, H, P) + p];
+                    y[dg_off(t, mo, h, M, H, P) + p] = g * acc;
+                }
+        }
+    free(qk);
+    return 0;
+}
+
+/* Reverse mode of that definition, in the page's order (general MIMO backward):
+ *   yu = qk V (unweighted), d_gamma = sum dy o yu, dyu = gamma dy,
+ *   d_qk = dyu V^T, d_V = qk^T dyu, d_C = d_qk B, d_B = d_qk^T C. */
+int oracle_diag_bwd(int64_t T, int64_t M, int64_t H, int64_t P, int64_t R, const double* dy,
+                    const double* V, const double* B, const double* C, const double* gamma,
+                    double* d_v, double* d_b, double* d_c, double* d_gamma) {
+    if (T < 0 || M <= 0 || H <= 0 || P <= 0 || R <= 0) return -1;
+    if (T > 0 && (!dy || !V || !B || !C || !gamma || !d_v || !d_b || !d_c || !d_gamma)) return -1;
+    double* qk = (double*)malloc(sizeof(double) * 2 * M * M);
+    if (!qk) return -2;
+    double* dqk = qk + M * M;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            const double g = gamma[t * H + h];
+            for (int64_t mo = 0; mo < M; ++mo)
+                for (int64_t mi = 0; mi < M; ++mi) {
+                    double acc = 0.0;
+                    for (int64_t r = 0; r < R; ++r)
+                        acc += C[dg_off(t, mo, h, M, H, R) + r] * B[dg_off(t, mi, h, M, H, R) + r];
+                    qk[mo * M + mi] = acc;
+                }
+            double dg = 0.0;
+            for (int64_t mo = 0; mo < M; ++mo)
+                for (int64_t p = 0; p < P; ++p) {
+                    double yu = 0.0;
+                    for (int64_t mi = 0; mi < M; ++mi) yu += qk[mo * M + mi] * V[dg_off(t, mi, h, M, H, P) + p];
+                    dg += dy[dg_off(t, mo, h, M, H, P) + p] * yu;
+                }
+            d_gamma[t * H + h] = dg;
+            for (int64_t mo = 0; mo < M; ++mo)
+                for (int64_t mi = 0; mi < M; ++mi) {
+                    double acc = 0.0;
+                    for (int64_t p = 0; p < P; ++p)
+                        acc += g * dy[dg_off(t, mo, h, M, H, P) + p] * V[dg_off(t, mi, h, M, H, P) + p];
+                    dqk[mo * M + mi] = acc;
+                }
+            for (int64_t mi = 0; mi < M; ++mi)
+                for (int64_t p = 0; p < P; ++p) {
+                    double acc = 0.0;
+                    for (int64_t mo = 0; mo < M; ++mo)
+                        acc += qk[mo * M + mi] * g * dy[dg_off(t, mo, h, M, H, P) + p];
+                    d_v[dg_off(t, mi, h, M, H, P) + p] = acc;
+                }
+            for (int64_t mo = 0; mo < M; ++mo)
+                for (int64_t r = 0; r < R; ++r) {
+                    double acc = 0.0;
+                    for (int64_t mi = 0; mi < M; ++mi) acc += dqk[mo * M + mi] * B[dg_off(t, mi, h, M, H, R) + r];
+                    d_c[dg_off(t, mo, h, M, H, R) + r] = acc;
+                }
+            for (int64_t mi = 0; mi < M; ++mi)
+                for (int64_t r = 0; r < R; ++r) {
+                    double acc = 0.0;
+                    for (int64_t mo = 0; mo < M; ++mo) acc += dqk[mo * M + mi] * C[dg_off(t, mo, h, M, H, R) + r];
+                    d_b[dg_off(t, mi, h, M, H, R) + r] = acc;
+                }
+        }
+    free(qk);
     return 0;
 }

@@ -14,6 +14,7 @@ import pytest
 import oracle
 import test_oracle_moments as tm
 import test_oracle_pr as tp
+import test_oracle_diag as td
 import test_oracle_ssd as ts
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")
@@ -43,6 +44,12 @@ MUTANTS = {
     "pr_dm1_not_transposed": ("acc -= (G[i * R + j] + G[j * R + i]) * mu[j];",
                               "acc -= 2.0 * G[i * R + j] * mu[j];"),
     "pr_dm2_missing_count": ("d_m2[o * R * R + k] = G[k] / n;", "d_m2[o * R * R + k] = G[k];"),
+    "diag_fwd_transposed_qk": ("for (int64_t mi = 0; mi < M; ++mi) acc += qk[mo * M + mi] * V[",
+                               "for (int64_t mi = 0; mi < M; ++mi) acc += qk[mi * M + mo] * V["),
+    "diag_dgamma_drops_dy": ("dg += dy[dg_off(t, mo, h, M, H, P) + p] * yu;", "dg += yu;"),
+    "diag_db_not_transposed": ("acc += dqk[mo * M + mi] * C[dg_off(t, mo, h, M, H, R) + r];",
+                               "acc += dqk[mi * M + mo] * C[dg_off(t, mo, h, M, H, R) + r];"),
+    "diag_dv_missing_gamma": ("acc += qk[mo * M + mi] * g * dy[", "acc += qk[mo * M + mi] * dy["),
 }
 
 PINS = [
@@ -60,6 +67,10 @@ PINS = [
     tp.test_trace_is_the_mean_squared_sample_norm,
     lambda: tp.test_pr_gradient_matches_direct_formula(True),
     tp.test_pr_gradient_has_no_radial_part,
+    td.test_siso_path_equals_general_path,
+    td.test_memoryless_ssd_is_the_diagonal_term,
+    td.test_finite_differences_all_four_gradients,
+    lambda: td.test_linearity_in_each_input(2),
 ]
 
 
