@@ -231,6 +231,58 @@ def bench_pr(args, w, dims, m2, m1, count, stream):
             "us_per_step": round(ms * 1e3, 2), "kernels": kernels}
 
 
+def diag_bytes(w, kernel: str):
+    """Algorithmic HBM bytes of one launch of the same-step correction over all (token, head)
+    pairs: fwd reads v, B, C, gamma and writes y; bwd reads dy, v, B, C, gamma and writes
+    d_v, d_B, d_C, d_gamma."""
+    e = 2 if w.io == "bf16" else 4
+    m, p, r = w.mimo_rank, w.headdim, w.dstate
+    pairs = w.tokens * w.nheads
+    if kernel == "k_diag_fwd":
+        return pairs * (e * (2 * m * p + 2 * m * r) + 4)
+    if kernel == "k_diag_bwd":
+        return pairs * (e * (3 * m * p + 4 * m * r) + 8)
+    return None
+
+
+def bench_diag(args):
+    """ssd_y_diag + ssd_y_diag_bwd on each same-step-correction workload."""
+    import torch
+    from mamba_ssd_chunked_amd import inputs, ssd
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, w in inputs.DIAG_WORKLOADS.items():
+        d = {k: v.to(dev) for k, v in inputs.make_diag_inputs(w).items()}
+        y = torch.empty_like(d["v"])
+        g = dict(d_v=torch.empty_like(d["v"]), d_B=torch.empty_like(d["B"]),
+                 d_C=torch.empty_like(d["C"]), d_gamma=torch.empty_like(d["gamma"]))
+
+        def step():
+            st = torch.cuda.current_stream()
+            rc = ssd.ssd_y_diag(d["v"], d["B"], d["C"], d["gamma"], y, st)
+            if rc:
+                raise ssd.SsdError(rc, "ssd_y_diag", ssd.ssd_last_error())
+            rc = ssd.ssd_y_diag_bwd(d["dy"], d["v"], d["B"], d["C"], d["gamma"], g["d_v"], g["d_B"],
+                                    g["d_C"], g["d_gamma"], st)
+            if rc:
+                raise ssd.SsdError(rc, "ssd_y_diag_bwd", ssd.ssd_last_error())
+
+        ms, _, kt = timed_regions(step, args, stream)
+        kernels = {}
+        for kname, (tot, cnt) in kt.items():
+            avg = tot / cnt
+            nbytes = diag_bytes(w, kname)
+            rate = nbytes / (avg / 1e3)
+            kernels[kname] = {"avg_us": round(avg * 1e3, 2), "bytes": nbytes,
+                              "gbps": round(rate / 1e9, 1), "hbm_frac": round(rate / PEAK_HBM, 4)}
+        res[name] = {"workload": w.describe(), "ms_per_step": round(ms, 4),
+                     "value": round(w.tokens / (ms / 1e3), 1), "unit": "tokens/s",
+                     "step": "ssd_y_diag + ssd_y_diag_bwd", "kernels": kernels}
+        del d, y, g
+    return res
+
+
 def bench_moments(args):
     """ssd_state_moments (with y) + ssd_state_moments_bwd on the moments workload."""
     import torch
@@ -347,6 +399,10 @@ def main():
                          "1 %% slower than eager launches)")
     ap.add_argument("--moments-only", action="store_true",
                     help="run only the state-moments leg and print its JSON object")
+    ap.add_argument("--no-diag", action="store_true",
+                    help="skip the same-step-correction leg (Mamba-3 y_diag workloads)")
+    ap.add_argument("--diag-only", action="store_true",
+                    help="run only the same-step-correction leg and print its JSON object")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (a plain copy "
                          "kernel of known size, to calibrate HBM byte counters)")
@@ -362,6 +418,10 @@ def main():
     if args.moments_only:
         torch.cuda.set_device(0)
         print(json.dumps(bench_moments(args)), flush=True)
+        return
+    if args.diag_only:
+        torch.cuda.set_device(0)
+        print(json.dumps(bench_diag(args)), flush=True)
         return
 
     w = inputs.WORKLOADS[args.workload]
@@ -448,6 +508,8 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, inp)
     if not args.no_moments:
         out["moments"] = bench_moments(args)
+    if not args.no_diag:
+        out["y_diag"] = bench_diag(args)
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, device=dev)

@@ -197,6 +197,42 @@ int ssd_moments_pr_bwd(int64_t batch, int64_t nheads, int64_t dstate, const floa
                        const float* m2, const float* m1, const int64_t* count, int center,
                        float* d_m2, float* d_m1, void* stream);
 
+/*
+ * Gamma-weighted same-step correction of the Mamba-3 SSD (burn-mamba page
+ * "mamba3/single_ssd/ssd/serial_recalculated/diag.rs": module doc and the
+ * general MIMO path; at mimo_rank 1 its SISO path).  The term has no recurrence:
+ * per token t of the flattened [b, n, l] axes and head h,
+ *   qk[mo][mi]    = sum_r C[t,mo,h,r] B[t,mi,h,r]          (m x m, m = mimo_rank)
+ *   y_diag[t,mo,h,p] = gamma[t,h] sum_mi qk[mo][mi] v[t,mi,h,p]
+ * The Mamba-3 chunk scan adds it to its output; it is exposed here as its own
+ * term (overwritten, not added).
+ *   ntokens >= 0 (= b * n * l), mimo_rank in {1, 2, 4}, nheads > 0,
+ *   headdim and dstate in {16, 32, 64, 128}
+ *   v, y_diag   [T, m, h, p]  io dtype (the page's [b, n, l, m, h, p])
+ *   B, C        [T, m, h, r]  io dtype
+ *   gamma       [T, h]        fp32
+ * io tensors 16-byte aligned (8-byte for bf16).  fp32 accumulation; bf16
+ * outputs rounded to nearest even.  No workspace.  Errors: SSD_ERR_NULL,
+ * SSD_ERR_SHAPE, SSD_ERR_UNSUPPORTED, SSD_ERR_DTYPE, SSD_ERR_HIP.
+ */
+int ssd_y_diag(int64_t ntokens, int64_t mimo_rank, int64_t nheads, int64_t headdim,
+               int64_t dstate, int io_dtype, const void* v, const void* B, const void* C,
+               const float* gamma, void* y_diag, void* stream);
+
+/*
+ * Gradients of <dy, y_diag> (the page's analytic backward of the correction):
+ *   DV[mo][mi] = sum_p dy[mo,p] v[mi,p]
+ *   d_gamma    = sum_{mo,mi} qk[mo][mi] DV[mo][mi]                [T, h] fp32
+ *   d_v[mi,p]  = gamma sum_mo qk[mo][mi] dy[mo,p]                like v
+ *   d_C[mo,r]  = gamma sum_mi DV[mo][mi] B[mi,r]                 like C
+ *   d_B[mi,r]  = gamma sum_mo DV[mo][mi] C[mo,r]                 like B
+ * dy like y_diag; all outputs required and overwritten.
+ */
+int ssd_y_diag_bwd(int64_t ntokens, int64_t mimo_rank, int64_t nheads, int64_t headdim,
+                   int64_t dstate, int io_dtype, const void* dy, const void* v, const void* B,
+                   const void* C, const float* gamma, void* d_v, void* d_B, void* d_C,
+                   float* d_gamma, void* stream);
+
 /* Message for the last nonzero status returned on this thread ("" if none). */
 const char* ssd_last_error(void);
 

@@ -269,6 +269,43 @@ int validate_pr(const char* who, int64_t batch, int64_t nheads, int64_t dstate, 
     return SSD_OK;
 }
 
+// Shared checks of the two y_diag entry points; fills *d.
+int validate_diag(const char* who, int64_t ntokens, int64_t mimo_rank, int64_t nheads,
+                  int64_t headdim, int64_t dstate, int io_dtype, ssd::DiagShape* d) {
+    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16)
+        return fail(SSD_ERR_DTYPE, "%s: io_dtype must be SSD_F32 (0) or SSD_BF16 (1) (got %d)", who,
+                    io_dtype);
+    if (ntokens < 0 || mimo_rank <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0)
+        return fail(SSD_ERR_SHAPE,
+                    "%s: need ntokens >= 0 and mimo_rank, nheads, headdim, dstate > 0 "
+                    "(got %lld, %lld, %lld, %lld, %lld)", who, (long long)ntokens,
+                    (long long)mimo_rank, (long long)nheads, (long long)headdim, (long long)dstate);
+    if (mimo_rank != 1 && mimo_rank != 2 && mimo_rank != 4)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: mimo_rank must be 1, 2 or 4 (got %lld)", who,
+                    (long long)mimo_rank);
+    if (!pow2_in(headdim, 16, 128) || !pow2_in(dstate, 16, 128))
+        return fail(SSD_ERR_UNSUPPORTED, "%s: headdim and dstate must be 16, 32, 64 or 128 "
+                    "(got %lld, %lld)", who, (long long)headdim, (long long)dstate);
+    if (nheads > (1 << 30) || (double)ntokens * (double)nheads * 16.0 > 2.0e11 ||
+        (double)ntokens * mimo_rank * nheads * 128.0 > 4.0e18)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: problem too large for one call (split the tokens)", who);
+    d->T = ntokens;
+    d->M = (int)mimo_rank;
+    d->H = (int)nheads;
+    d->P = (int)headdim;
+    d->R = (int)dstate;
+    d->io = io_dtype;
+    return SSD_OK;
+}
+
+int check_diag_ptrs(const ssd::DiagShape& d,
+                    std::initializer_list<std::pair<const void*, const char*>> io) {
+    const size_t ia = d.io == SSD_BF16 ? 8 : 16;
+    for (auto& p : io)
+        if (int rc = check_align(p.first, p.second, ia)) return rc;
+    return SSD_OK;
+}
+
 int check_valid_len(const ssd::Shape& s, const int64_t* valid_len) {
     if (!valid_len) return SSD_OK;
     const int64_t seq = static_cast<int64_t>(s.N) * s.L;
@@ -571,6 +608,40 @@ int ssd_moments_pr_bwd(int64_t batch, int64_t nheads, int64_t dstate, const floa
     SSD_HIP(ssd::launch_pr_bwd((int)batch, (int)nheads, (int)dstate, d_pr, m2,
                                center ? m1 : nullptr, count, center != 0, d_m2, d_m1, st),
             "k_pr_bwd");
+    return ok();
+}
+
+int ssd_y_diag(int64_t ntokens, int64_t mimo_rank, int64_t nheads, int64_t headdim,
+               int64_t dstate, int io_dtype, const void* v, const void* B, const void* C,
+               const float* gamma, void* y_diag, void* stream) {
+    ssd::DiagShape d;
+    if (int rc = validate_diag("ssd_y_diag", ntokens, mimo_rank, nheads, headdim, dstate, io_dtype, &d))
+        return rc;
+    if (ntokens > 0 && (!v || !B || !C || !gamma || !y_diag))
+        return fail(SSD_ERR_NULL, "ssd_y_diag: v, B, C, gamma and y_diag are required");
+    if (int rc = check_diag_ptrs(d, {{v, "v"}, {B, "B"}, {C, "C"}, {y_diag, "y_diag"}})) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (ntokens > 0) SSD_HIP(ssd::launch_diag_fwd(d, v, B, C, gamma, y_diag, st), "k_diag_fwd");
+    return ok();
+}
+
+int ssd_y_diag_bwd(int64_t ntokens, int64_t mimo_rank, int64_t nheads, int64_t headdim,
+                   int64_t dstate, int io_dtype, const void* dy, const void* v, const void* B,
+                   const void* C, const float* gamma, void* d_v, void* d_B, void* d_C,
+                   float* d_gamma, void* stream) {
+    ssd::DiagShape d;
+    if (int rc = validate_diag("ssd_y_diag_bwd", ntokens, mimo_rank, nheads, headdim, dstate,
+                               io_dtype, &d))
+        return rc;
+    if (ntokens > 0 && (!dy || !v || !B || !C || !gamma || !d_v || !d_B || !d_C || !d_gamma))
+        return fail(SSD_ERR_NULL,
+                    "ssd_y_diag_bwd: dy, v, B, C, gamma, d_v, d_B, d_C and d_gamma are required");
+    if (int rc = check_diag_ptrs(d, {{dy, "dy"}, {v, "v"}, {B, "B"}, {C, "C"}, {d_v, "d_v"},
+                                     {d_B, "d_B"}, {d_C, "d_C"}}))
+        return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (ntokens > 0)
+        SSD_HIP(ssd::launch_diag_bwd(d, dy, v, B, C, gamma, d_v, d_B, d_C, d_gamma, st), "k_diag_bwd");
     return ok();
 }
 

@@ -149,4 +149,20 @@ hipError_t launch_pr_bwd(int B, int H, int R, const float* d_pr, const float* m2
                          const int64_t* count, int center, float* d_m2, float* d_m1,
                          hipStream_t st);
 
+// ------------------------------------------------- same-step correction y_diag
+struct DiagShape {
+    int64_t T;     // tokens (the [b, n, l] axes flattened)
+    int M, H, P, R;  // mimo rank, heads, headdim, dstate
+    int io;        // 0 = fp32, 1 = bf16
+};
+
+// y [T,M,H,P] = gamma [T,H] * (C B^T) V per (token, head); V [T,M,H,P], B/C [T,M,H,R].
+hipError_t launch_diag_fwd(const DiagShape& d, const void* V, const void* B, const void* C,
+                           const float* gamma, void* y, hipStream_t st);
+
+// Gradients of <dy, y>: d_v like V, d_b / d_c like B, d_gamma [T,H].
+hipError_t launch_diag_bwd(const DiagShape& d, const void* dy, const void* V, const void* B,
+                           const void* C, const float* gamma, void* d_v, void* d_b, void* d_c,
+                           float* d_gamma, hipStream_t st);
+
 }  // namespace ssd

@@ -18,6 +18,12 @@ tensor stays fp32.
 
 Layouts follow the pages' tensor naming: x/dy ``[b, n, l, h, p]``, B/C
 ``[b, n, l, h, r]``, dt ``[b, h, n, l]``, A/D ``[h]``, states ``[b, h, p, r]``.
+
+The Mamba-3 same-step correction (``DiagWorkload``) draws, in this order, v and
+dy ~ N(0, 1) ``[b, n, l, m, h, p]``, B and C ~ N(0, 1) / sqrt(dstate)
+``[b, n, l, m, h, r]`` and gamma = softplus(z - 2) ``[b, n, l, h]`` (a
+step-sized positive weight, like dt), after which bf16 workloads round v, B, C
+and dy to bfloat16.
 """
 from __future__ import annotations
 
@@ -109,3 +115,60 @@ def custom(name="custom", batch=1, seq=256, nheads=2, headdim=16, dstate=16, chu
     """A workload with the standard distributions and arbitrary shapes (for tests)."""
     return Workload(name, batch, seq, nheads, headdim, dstate, chunk_len, io=io,
                     dt_shift=dt_shift, init_std=init_std, valid_len=valid_len, seed=seed)
+
+
+@dataclasses.dataclass(frozen=True)
+class DiagWorkload:
+    """Shapes of the Mamba-3 same-step correction: tokens [b, n, l], mimo rank m."""
+    name: str
+    batch: int
+    seq: int
+    chunk_len: int
+    mimo_rank: int
+    nheads: int
+    headdim: int
+    dstate: int
+    io: str = "f32"
+    seed: int = 1005
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seq
+
+    def describe(self) -> dict:
+        return dict(workload=self.name, batch=self.batch, seq_len=self.seq, chunk_len=self.chunk_len,
+                    mimo_rank=self.mimo_rank, nheads=self.nheads, headdim=self.headdim,
+                    dstate=self.dstate, io_dtype=self.io)
+
+
+# The SSD benchmark's shapes (4 x 2048 tokens, 24 heads, p = 64, r = 128) at mimo rank 1
+# (the SISO path) and 4.
+DIAG_WORKLOADS = {
+    "mamba3_diag_siso_fp32": DiagWorkload("mamba3_diag_siso_fp32", 4, 2048, 256, 1, 24, 64, 128,
+                                          seed=1005),
+    "mamba3_diag_mimo4_fp32": DiagWorkload("mamba3_diag_mimo4_fp32", 4, 2048, 256, 4, 24, 64, 128,
+                                           seed=1006),
+}
+
+
+def make_diag_inputs(w: DiagWorkload) -> dict:
+    """Draw v, dy, B, C, gamma for the same-step correction (see module docstring)."""
+    g = torch.Generator().manual_seed(w.seed)
+    b, l, m, h, p, r = w.batch, w.chunk_len, w.mimo_rank, w.nheads, w.headdim, w.dstate
+    n = w.seq // l
+    if n * l != w.seq:
+        raise ValueError("seq must be a multiple of chunk_len")
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, dtype=torch.float32)
+
+    v = randn(b, n, l, m, h, p)
+    dy = randn(b, n, l, m, h, p)
+    B = randn(b, n, l, m, h, r) / math.sqrt(r)
+    C = randn(b, n, l, m, h, r) / math.sqrt(r)
+    gamma = torch.nn.functional.softplus(randn(b, n, l, h) - 2.0)
+    if w.io == "bf16":
+        v, dy, B, C = (t.to(torch.bfloat16) for t in (v, dy, B, C))
+    elif w.io != "f32":
+        raise ValueError(f"unknown io dtype {w.io!r}")
+    return dict(v=v, dy=dy, B=B, C=C, gamma=gamma)

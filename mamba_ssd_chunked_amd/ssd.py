@@ -15,6 +15,7 @@ raises immediately.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Optional
 
@@ -28,7 +29,8 @@ SSD_OP_FWD, SSD_OP_BWD, SSD_OP_MOMENTS, SSD_OP_MOMENTS_BWD = 0, 1, 2, 3
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
           4: "SSD_ERR_DTYPE", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_HIP"}
 EXPORTS = ("ssd_workspace_size", "ssd_fwd", "ssd_bwd", "ssd_state_moments",
-           "ssd_state_moments_bwd", "ssd_moments_pr", "ssd_moments_pr_bwd", "ssd_last_error",
+           "ssd_state_moments_bwd", "ssd_moments_pr", "ssd_moments_pr_bwd", "ssd_y_diag",
+           "ssd_y_diag_bwd", "ssd_last_error",
            "ssd_timing_enable", "ssd_timing_collect")
 
 
@@ -72,8 +74,11 @@ def load_library(path: str = LIB_PATH):
     I64 = ctypes.c_int64
     lib.ssd_moments_pr.argtypes = [I64, I64, I64, P, P, P, ctypes.c_int, P, P, P]
     lib.ssd_moments_pr_bwd.argtypes = [I64, I64, I64, P, P, P, P, ctypes.c_int, P, P, P]
+    lib.ssd_y_diag.argtypes = [I64] * 5 + [ctypes.c_int] + [P] * 6
+    lib.ssd_y_diag_bwd.argtypes = [I64] * 5 + [ctypes.c_int] + [P] * 10
     for f in ("ssd_workspace_size", "ssd_fwd", "ssd_bwd", "ssd_state_moments",
-              "ssd_state_moments_bwd", "ssd_moments_pr", "ssd_moments_pr_bwd"):
+              "ssd_state_moments_bwd", "ssd_moments_pr", "ssd_moments_pr_bwd", "ssd_y_diag",
+              "ssd_y_diag_bwd"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ssd_last_error.argtypes = []
     lib.ssd_last_error.restype = ctypes.c_char_p
@@ -262,6 +267,38 @@ def ssd_moments_pr_bwd(batch, nheads, dstate, d_pr, m2, m1, count, center, d_m2,
                                              *outs, _stream(stream))
 
 
+def _diag_sizes(v: torch.Tensor, B: torch.Tensor):
+    """(tokens, m, h, p, r, io dtype) of v [..., m, h, p] and B [..., m, h, r]."""
+    if v.dim() < 3 or B.dim() != v.dim() or B.shape[:-1] != v.shape[:-1]:
+        raise ValueError("v must be [..., m, h, p] and B [..., m, h, r] over the same leading axes")
+    m, h, p = v.shape[-3:]
+    T = math.prod(v.shape[:-3])
+    io = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}.get(v.dtype)
+    if io is None:
+        raise TypeError(f"v must be float32 or bfloat16 (got {v.dtype})")
+    return T, m, h, p, B.shape[-1], io
+
+
+def ssd_y_diag(v, B, C, gamma, y_diag, stream=None) -> int:
+    T, m, h, p, r, io = _diag_sizes(v, B)
+    dt = v.dtype
+    args = [_ptr(v, "v", dt, T * m * h * p, True), _ptr(B, "B", dt, T * m * h * r, True),
+            _ptr(C, "C", dt, T * m * h * r, True), _ptr(gamma, "gamma", torch.float32, T * h, True),
+            _ptr(y_diag, "y_diag", dt, T * m * h * p, True)]
+    return load_library().ssd_y_diag(T, m, h, p, r, io, *args, _stream(stream))
+
+
+def ssd_y_diag_bwd(dy, v, B, C, gamma, d_v, d_B, d_C, d_gamma, stream=None) -> int:
+    T, m, h, p, r, io = _diag_sizes(v, B)
+    dt, f = v.dtype, torch.float32
+    args = [_ptr(dy, "dy", dt, T * m * h * p, True), _ptr(v, "v", dt, T * m * h * p, True),
+            _ptr(B, "B", dt, T * m * h * r, True), _ptr(C, "C", dt, T * m * h * r, True),
+            _ptr(gamma, "gamma", f, T * h, True), _ptr(d_v, "d_v", dt, T * m * h * p, True),
+            _ptr(d_B, "d_B", dt, T * m * h * r, True), _ptr(d_C, "d_C", dt, T * m * h * r, True),
+            _ptr(d_gamma, "d_gamma", f, T * h, True)]
+    return load_library().ssd_y_diag_bwd(T, m, h, p, r, io, *args, _stream(stream))
+
+
 # ------------------------------------------------------------ allocating helpers
 def _check(rc: int, where: str):
     if rc != 0:
@@ -368,3 +405,19 @@ def moments_pr_bwd(d_pr, m2, m1, count, center=False, want_d_m1=True, stream=Non
     _check(ssd_moments_pr_bwd(b, h, r, d_pr, m2, m1 if center else None, count, center, d_m2,
                               d_m1, stream), "ssd_moments_pr_bwd")
     return d_m2, d_m1
+
+
+def y_diag(v, B, C, gamma, stream=None):
+    """Same-step correction gamma (C B^T) v per token and head (see ssd_y_diag)."""
+    y = torch.empty_like(v)
+    _check(ssd_y_diag(v, B, C, gamma, y, stream), "ssd_y_diag")
+    return y
+
+
+def y_diag_bwd(dy, v, B, C, gamma, stream=None):
+    """Returns dict(d_v, d_B, d_C, d_gamma)."""
+    out = dict(d_v=torch.empty_like(v), d_B=torch.empty_like(B), d_C=torch.empty_like(C),
+               d_gamma=torch.empty_like(gamma))
+    _check(ssd_y_diag_bwd(dy, v, B, C, gamma, out["d_v"], out["d_B"], out["d_C"], out["d_gamma"],
+                          stream), "ssd_y_diag_bwd")
+    return out

@@ -174,3 +174,24 @@ def test_pr_entry_points_reject_bad_arguments(lib, case, code):
 def test_pr_of_an_empty_batch_is_a_no_op(lib):
     assert lib.ssd_moments_pr(0, 3, 32, None, None, None, 1, None, None, None) == 0
     assert lib.ssd_moments_pr_bwd(0, 3, 32, None, None, None, None, 1, None, None, None) == 0
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(T=-1), 2), (dict(m=0), 2), (dict(h=0), 2), (dict(p=0), 2), (dict(m=3), 3), (dict(m=8), 3),
+    (dict(p=48), 3), (dict(r=256), 3), (dict(io=2), 4), (dict(v=0), 1), (dict(gamma=0), 1),
+    (dict(out=0), 1), (dict(v=FAKE + 4), 3), (dict(out=FAKE + 8), 3), (dict(io=1, v=FAKE + 4), 3),
+])
+def test_y_diag_entry_points_reject_bad_arguments(lib, case, code):
+    a = dict(T=10, m=2, h=3, p=32, r=64, io=0, v=FAKE, gamma=FAKE, out=FAKE)
+    a.update(case)
+    rc = lib.ssd_y_diag(a["T"], a["m"], a["h"], a["p"], a["r"], a["io"], a["v"], FAKE, FAKE,
+                        a["gamma"], a["out"], None)
+    assert rc == code, ssd.ssd_last_error()
+    rc = lib.ssd_y_diag_bwd(a["T"], a["m"], a["h"], a["p"], a["r"], a["io"], FAKE, a["v"], FAKE, FAKE,
+                            a["gamma"], a["out"], FAKE, FAKE, FAKE, None)
+    assert rc == code, ssd.ssd_last_error()
+
+
+def test_y_diag_of_no_tokens_is_a_no_op(lib):
+    assert lib.ssd_y_diag(0, 4, 3, 64, 128, 0, None, None, None, None, None, None) == 0
+    assert lib.ssd_y_diag_bwd(0, 4, 3, 64, 128, 0, *([None] * 10)) == 0

@@ -51,3 +51,12 @@ def test_traffic_is_reported_only_for_the_profiled_sources(monkeypatch):
     assert bench.measured_traffic("k_bwd_source", w, 128) is None
     assert bench.measured_traffic("k_bwd_source", w, 256) is None  # never profiled at 256
     assert bench.measured_traffic("k5_chunk_scan", w, 128) is None
+
+
+def test_diag_bytes_count_every_tensor_once():
+    w = inputs.DIAG_WORKLOADS["mamba3_diag_mimo4_fp32"]
+    pairs = 4 * 2048 * 24
+    # fwd: v, B, C, y (4 B each) + gamma; bwd: dy, v, B, C, d_v, d_B, d_C + gamma, d_gamma
+    assert bench.diag_bytes(w, "k_diag_fwd") == pairs * (4 * (4 * 64 + 2 * 4 * 128 + 4 * 64) + 4)
+    assert bench.diag_bytes(w, "k_diag_bwd") == pairs * (4 * (3 * 4 * 64 + 4 * 4 * 128) + 8)
+    assert bench.diag_bytes(w, "other") is None
