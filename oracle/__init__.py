@@ -9,7 +9,8 @@ token-by-token recurrence ``h_t = exp(dt_t A) h_{t-1} + dt_t x_t (outer) B_t``,
 ``y_t = C_t . h_t + D x_t`` and its reverse-mode recurrence, plus the pooled
 state moments of the burn-mamba ``state_moments.rs`` page and their gradient, and
 that page's participation ratio of the moments with its gradient, and the
-gamma-weighted same-step correction ``y_diag`` of the Mamba-3 SSD with its gradient.
+gamma-weighted same-step correction ``y_diag`` of the Mamba-3 SSD with its gradient,
+and the Mamba-3 quaternion cumulative-product scan with its gradient.
 This module only builds the shared library with gcc and marshals numpy arrays.
 
 Every function takes and returns float64 numpy arrays in the pages' layouts:
@@ -79,6 +80,8 @@ def _open(path):
     lib.oracle_moments_pr_bwd.argtypes = [I64, I64, I64, P, P, P, P, ctypes.c_int, P, P]
     lib.oracle_diag_fwd.argtypes = [I64] * 5 + [P] * 5
     lib.oracle_diag_bwd.argtypes = [I64] * 5 + [P] * 9
+    lib.oracle_quat_scan.argtypes = [I64] * 4 + [P] * 3
+    lib.oracle_quat_scan_bwd.argtypes = [I64] * 4 + [P] * 5
     for f in (lib.oracle_ssd_fwd, lib.oracle_ssd_bwd, lib.oracle_state_moments,
               lib.oracle_state_moments_bwd):
         f.restype = ctypes.c_int
@@ -231,3 +234,24 @@ def diag_bwd(dy, V, B, C, gamma):
                                    _ptr(out["d_v"]), _ptr(out["d_b"]), _ptr(out["d_c"]),
                                    _ptr(out["d_gamma"])), "diag_bwd")
     return out
+
+
+def quat_scan(q, init=None):
+    """Quaternion cumulative product cum[t] = q_t (x) cum[t-1] (mamba3 quat_scan page).
+    q ``[b, s, h, j, 4]`` (w, x, y, z), init ``[b, h, j, 4]`` or None (identity)."""
+    q, init = _f64(q), _f64(init)
+    b, s, h, j, _ = q.shape
+    cum = np.empty_like(q)
+    _check(_load().oracle_quat_scan(b, s, h, j, _ptr(q), _ptr(init), _ptr(cum)), "quat_scan")
+    return cum
+
+
+def quat_scan_bwd(q, init, d_cum):
+    """Exact reverse mode of quat_scan: returns ``(d_q, d_init)``."""
+    q, init, d_cum = _f64(q), _f64(init), _f64(d_cum)
+    b, s, h, j, _ = q.shape
+    d_q = np.empty_like(q)
+    d_init = np.empty((b, h, j, 4))
+    _check(_load().oracle_quat_scan_bwd(b, s, h, j, _ptr(q), _ptr(init), _ptr(d_cum), _ptr(d_q),
+                                        _ptr(d_init)), "quat_scan_bwd")
+    return d_q, d_init

@@ -20,6 +20,8 @@
  *   y_diag    the gamma-weighted same-step correction of the Mamba-3 SSD
  *             (per token and head: gamma * (C B^T) V over the mimo axis) and its
  *             reverse-mode gradient.
+ *   quat scan the quaternion cumulative product cum[t] = q_t (x) cum[t-1] of the
+ *             Mamba-3 rotation and its exact reverse-mode gradient.
  *
  * The chunked SSD of the burn-mamba "combined_backward.rs" page (kernels K1-K5
  * and the recompute backward) is a re-association of exactly this recurrence:
@@ -552,5 +554,92 @@ int oracle_diag_bwd(int64_t T, int64_t M, int64_t H, int64_t P, int64_t R, const
                 }
         }
     free(qk);
+    return 0;
+}
+
+/* --------------------------------------------- quaternion cumulative product
+ * The scan of the burn-mamba page "mamba3/quat_scan/backward.rs" (Gradient
+ * math): for every lane (b, h, j), cum[t] = q_t (x) cum[t-1], cum[-1] = init,
+ * with the Hamilton product of quaternions stored as (w, x, y, z).
+ * Layouts: q, cum, d_cum, d_q [B, S, H, J, 4]; init, d_init [B, H, J, 4]
+ * (init NULL = the identity quaternion). */
+static void qmul(const double* a, const double* b, double* o) {
+    const double w = a[0] * b[0] - a[1] * b[1] - a[2] * b[2] - a[3] * b[3];
+    const double x = a[0] * b[1] + a[1] * b[0] + a[2] * b[3] - a[3] * b[2];
+    const double y = a[0] * b[2] - a[1] * b[3] + a[2] * b[0] + a[3] * b[1];
+    const double z = a[0] * b[3] + a[1] * b[2] - a[2] * b[1] + a[3] * b[0];
+    o[0] = w;
+    o[1] = x;
+    o[2] = y;
+    o[3] = z;
+}
+
+static void qconj(const double* a, double* o) {
+    o[0] = a[0];
+    o[1] = -a[1];
+    o[2] = -a[2];
+    o[3] = -a[3];
+}
+
+int oracle_quat_scan(int64_t B, int64_t S, int64_t H, int64_t J, const double* q,
+                     const double* init, double* cum) {
+    if (B < 0 || S < 0 || H <= 0 || J <= 0) return -1;
+    if (B > 0 && S > 0 && (!q || !cum)) return -1;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t j = 0; j < J; ++j) {
+                double c[4] = {1.0, 0.0, 0.0, 0.0};
+                if (init)
+                    for (int e = 0; e < 4; ++e) c[e] = init[((b * H + h) * J + j) * 4 + e];
+                for (int64_t t = 0; t < S; ++t) {
+                    const int64_t o = (((b * S + t) * H + h) * J + j) * 4;
+                    double n[4];
+                    qmul(q + o, c, n);
+                    for (int e = 0; e < 4; ++e) cum[o + e] = c[e] = n[e];
+                }
+            }
+    return 0;
+}
+
+/* Reverse mode of that scan, exact for all quaternions: with o = a (x) b and a
+ * cotangent g of o, the real inner product gives grad_a = g (x) conj(b) and
+ * grad_b = conj(a) (x) g (the page's per-factor VJPs).  The total cotangent G_t
+ * of cum[t] is d_cum[t] plus what cum[t+1] hands back:
+ *   G_t = d_cum[t] + conj(q_{t+1}) (x) G_{t+1},  d_q[t] = G_t (x) conj(cum[t-1]),
+ *   d_init = conj(q_0) (x) G_0. */
+int oracle_quat_scan_bwd(int64_t B, int64_t S, int64_t H, int64_t J, const double* q,
+                         const double* init, const double* d_cum, double* d_q, double* d_init) {
+    if (B < 0 || S < 0 || H <= 0 || J <= 0) return -1;
+    if (B > 0 && S > 0 && (!q || !d_cum || !d_q)) return -1;
+    double* cum = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1) * 4);
+    if (!cum) return -2;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t j = 0; j < J; ++j) {
+                double c0[4] = {1.0, 0.0, 0.0, 0.0};
+                if (init)
+                    for (int e = 0; e < 4; ++e) c0[e] = init[((b * H + h) * J + j) * 4 + e];
+                double c[4] = {c0[0], c0[1], c0[2], c0[3]};
+                for (int64_t t = 0; t < S; ++t) {  /* forward again: cum[t] of this lane */
+                    double n[4];
+                    qmul(q + (((b * S + t) * H + h) * J + j) * 4, c, n);
+                    for (int e = 0; e < 4; ++e) cum[t * 4 + e] = c[e] = n[e];
+                }
+                double G[4] = {0.0, 0.0, 0.0, 0.0};
+                for (int64_t t = S - 1; t >= 0; --t) {
+                    const int64_t o = (((b * S + t) * H + h) * J + j) * 4;
+                    for (int e = 0; e < 4; ++e) G[e] += d_cum[o + e];
+                    const double* prev = t > 0 ? cum + (t - 1) * 4 : c0;
+                    double pc[4], qc[4], n[4];
+                    qconj(prev, pc);
+                    qmul(G, pc, d_q + o);
+                    qconj(q + o, qc);
+                    qmul(qc, G, n);
+                    for (int e = 0; e < 4; ++e) G[e] = n[e];
+                }
+                if (d_init)
+                    for (int e = 0; e < 4; ++e) d_init[((b * H + h) * J + j) * 4 + e] = G[e];
+            }
+    free(cum);
     return 0;
 }

@@ -15,6 +15,7 @@ import oracle
 import test_oracle_moments as tm
 import test_oracle_pr as tp
 import test_oracle_diag as td
+import test_oracle_quat as tq
 import test_oracle_ssd as ts
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")
@@ -50,6 +51,11 @@ MUTANTS = {
     "diag_db_not_transposed": ("acc += dqk[mo * M + mi] * C[dg_off(t, mo, h, M, H, R) + r];",
                                "acc += dqk[mi * M + mo] * C[dg_off(t, mo, h, M, H, R) + r];"),
     "diag_dv_missing_gamma": ("acc += qk[mo * M + mi] * g * dy[", "acc += qk[mo * M + mi] * dy["),
+    "quat_product_sign": ("const double y = a[0] * b[2] - a[1] * b[3] + a[2] * b[0] + a[3] * b[1];",
+                          "const double y = a[0] * b[2] + a[1] * b[3] + a[2] * b[0] + a[3] * b[1];"),
+    "quat_bwd_factor_order": ("qmul(qc, G, n);", "qmul(G, qc, n);"),
+    "quat_bwd_uses_current_state": ("const double* prev = t > 0 ? cum + (t - 1) * 4 : c0;",
+                                    "const double* prev = cum + t * 4;"),
 }
 
 PINS = [
@@ -71,6 +77,10 @@ PINS = [
     td.test_memoryless_ssd_is_the_diagonal_term,
     td.test_finite_differences_all_four_gradients,
     lambda: td.test_linearity_in_each_input(2),
+    tq.test_unit_table,
+    tq.test_matches_scipy_rotation_composition,
+    tq.test_finite_differences_general_quaternions,
+    tq.test_page_closed_form_for_unit_quaternions,
 ]
 
 
