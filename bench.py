@@ -37,8 +37,8 @@ PEAK_HBM = 8.0e12           # B/s
 TRAFFIC = {
     ("k_bwd_source", "mamba2_130m_fp32", 128): (484_145_997, 153_610_867, "e9a6bedb6c5ed229"),
 }
-TRAFFIC_SOURCES = {"k_bwd_source": ("k_chunk_bwd.hip", "ssd_device.hpp", "ssd_launch.hpp"),
-                   "k_bwd_target": ("k_chunk_bwd.hip", "ssd_device.hpp", "ssd_launch.hpp")}
+TRAFFIC_SOURCES = {"k_bwd_source": ("k_chunk_bwd.hip", "ssd_device.hpp"),
+                   "k_bwd_target": ("k_chunk_bwd.hip", "ssd_device.hpp")}
 
 
 def measured_traffic(kernel: str, w, k: int):
@@ -283,6 +283,67 @@ def bench_diag(args):
     return res
 
 
+def quat_bytes(w, kernel: str):
+    """HBM bytes one launch of a quaternion-scan kernel must move (16 B per quaternion):
+    fwd reads q and writes cum (plus init); the carry pass reads q; the reverse pass reads q
+    and d_cum and writes d_q (plus init, d_init).  The carry pass's read of q is a re-read of
+    the backward's input: the backward's algorithmic bytes are those of the reverse pass."""
+    n = w.batch * w.seq * w.nheads * w.nquat
+    lanes = w.batch * w.nheads * w.nquat
+    if kernel == "k_quat_fwd":
+        return 32 * n + 16 * lanes
+    if kernel == "k_quat_carry":
+        return 16 * n + 16 * lanes
+    if kernel == "k_quat_bwd":
+        return 48 * n + 32 * lanes
+    return None
+
+
+def bench_quat(args):
+    """ssd_quat_scan + ssd_quat_scan_bwd on the quaternion-scan workload."""
+    import torch
+    from mamba_ssd_chunked_amd import inputs, ssd
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, w in inputs.QUAT_WORKLOADS.items():
+        i = inputs.make_quat_inputs(w)
+        q, dc = i["q"].to(dev), i["d_cum"].to(dev)
+        init = i["init"].to(dev) if i["init"] is not None else None
+        cum, d_q = torch.empty_like(q), torch.empty_like(q)
+        d_init = torch.empty((w.batch, w.nheads, w.nquat, 4), device=dev)
+        ws_f, ws_b = ssd.quat_workspace(q, False), ssd.quat_workspace(q, True)
+
+        def step():
+            st = torch.cuda.current_stream()
+            rc = ssd.ssd_quat_scan(q, init, cum, ws_f, st)
+            if rc:
+                raise ssd.SsdError(rc, "ssd_quat_scan", ssd.ssd_last_error())
+            rc = ssd.ssd_quat_scan_bwd(q, init, dc, d_q, d_init, ws_b, st)
+            if rc:
+                raise ssd.SsdError(rc, "ssd_quat_scan_bwd", ssd.ssd_last_error())
+
+        ms, _, kt = timed_regions(step, args, stream)
+        kernels = {}
+        for kname, (tot, cnt) in kt.items():
+            avg = tot / cnt
+            ent = {"avg_us": round(avg * 1e3, 2), "launches_per_step": cnt / args.steps}
+            nbytes = quat_bytes(w, kname)
+            if nbytes is not None:
+                rate = nbytes / (avg / 1e3)
+                ent.update(bytes=nbytes, gbps=round(rate / 1e9, 1), hbm_frac=round(rate / PEAK_HBM, 4))
+            kernels[kname] = ent
+        algo = quat_bytes(w, "k_quat_fwd") + quat_bytes(w, "k_quat_bwd")
+        tokens = w.batch * w.seq
+        res[name] = {"workload": w.describe(), "ms_per_step": round(ms, 4),
+                     "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s",
+                     "step": "ssd_quat_scan + ssd_quat_scan_bwd",
+                     "step_algorithmic_gbps": round(algo / (ms / 1e3) / 1e9, 1),
+                     "kernels": kernels}
+        del q, dc, init, cum, d_q, d_init, ws_f, ws_b
+    return res
+
+
 def bench_moments(args):
     """ssd_state_moments (with y) + ssd_state_moments_bwd on the moments workload."""
     import torch
@@ -403,6 +464,10 @@ def main():
                     help="skip the same-step-correction leg (Mamba-3 y_diag workloads)")
     ap.add_argument("--diag-only", action="store_true",
                     help="run only the same-step-correction leg and print its JSON object")
+    ap.add_argument("--no-quat", action="store_true",
+                    help="skip the quaternion-scan leg (Mamba-3 rotation workload)")
+    ap.add_argument("--quat-only", action="store_true",
+                    help="run only the quaternion-scan leg and print its JSON object")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (a plain copy "
                          "kernel of known size, to calibrate HBM byte counters)")
@@ -422,6 +487,10 @@ def main():
     if args.diag_only:
         torch.cuda.set_device(0)
         print(json.dumps(bench_diag(args)), flush=True)
+        return
+    if args.quat_only:
+        torch.cuda.set_device(0)
+        print(json.dumps(bench_quat(args)), flush=True)
         return
 
     w = inputs.WORKLOADS[args.workload]
@@ -510,6 +579,8 @@ def main():
         out["moments"] = bench_moments(args)
     if not args.no_diag:
         out["y_diag"] = bench_diag(args)
+    if not args.no_quat:
+        out["quat_scan"] = bench_quat(args)
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, device=dev)

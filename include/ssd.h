@@ -53,7 +53,7 @@
  *    (SSD_ERR_UNSUPPORTED otherwise).  Results for different kernel_chunk_len
  *    agree up to floating-point rounding; ssd_workspace_size() depends on it.
  *  - Results are bitwise reproducible for equal inputs and kernel_chunk_len
- *    (no float atomics).
+ *    (no float atomics), except for the quaternion scan (see ssd_quat_scan).
  *  - Every call validates all arguments before it enqueues anything.  Return 0
  *    on success or one of the ssd_status codes; ssd_last_error() then gives a
  *    message (thread-local, valid until the next call on the thread).
@@ -232,6 +232,44 @@ int ssd_y_diag_bwd(int64_t ntokens, int64_t mimo_rank, int64_t nheads, int64_t h
                    int64_t dstate, int io_dtype, const void* dy, const void* v, const void* B,
                    const void* C, const float* gamma, void* d_v, void* d_B, void* d_C,
                    float* d_gamma, void* stream);
+
+/*
+ * Quaternion cumulative-product scan of the Mamba-3 rotation (burn-mamba page
+ * "mamba3/quat_scan/backward.rs", module doc and "Gradient math").  For every
+ * lane (b, h, j), with the Hamilton product (x) on components (w, x, y, z):
+ *   cum[b,t,h,j] = q[b,t,h,j] (x) cum[b,t-1,h,j],   cum[b,-1,h,j] = init[b,h,j]
+ *   q, cum   [b, s, h, j, 4]  fp32 (nquat = j quaternion blocks per head)
+ *   init     [b, h, j, 4]     fp32, nullable (NULL = the identity quaternion)
+ * batch >= 0, seq >= 0 (an empty sequence writes nothing), nheads, nquat > 0.
+ * Quaternions need not be unit.  Tensors 16-byte aligned; the workspace
+ * (ssd_quat_workspace_size, 256-byte aligned) is caller-owned and used by one
+ * call at a time.  Products and carries are fp64; cum is rounded to fp32 once.
+ * Unlike the SSD entry points, results are not bitwise reproducible: segments
+ * are chained by a look-back whose order of combination depends on timing, so
+ * two runs may round to neighbouring fp32 values: each output quaternion agrees
+ * to within two fp32 ulps of its norm.
+ * Errors: SSD_ERR_NULL, SSD_ERR_SHAPE, SSD_ERR_UNSUPPORTED (size, alignment),
+ * SSD_ERR_WORKSPACE, SSD_ERR_HIP.
+ */
+int ssd_quat_scan(int64_t batch, int64_t seq, int64_t nheads, int64_t nquat, const float* q,
+                  const float* init, float* cum, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Gradient of <d_cum, cum> (the page's recompute backward: only the leaves q and
+ * init are taken; the scan is recomputed).  Exact for every quaternion: with
+ * G_t = d_cum[t] + conj(q_{t+1}) (x) G_{t+1} (G past the end = 0),
+ *   d_q[t] = G_t (x) conj(cum[t-1])     [b, s, h, j, 4] out, fp32
+ *   d_init = conj(q_0) (x) G_0          [b, h, j, 4]    out, fp32, nullable
+ * (for unit quaternions this equals the page's closed form S[0]).  d_cum like q.
+ * An empty sequence sets d_init to 0.
+ */
+int ssd_quat_scan_bwd(int64_t batch, int64_t seq, int64_t nheads, int64_t nquat, const float* q,
+                      const float* init, const float* d_cum, float* d_q, float* d_init, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Workspace bytes of ssd_quat_scan (bwd == 0) or ssd_quat_scan_bwd (bwd != 0). */
+int ssd_quat_workspace_size(int64_t batch, int64_t seq, int64_t nheads, int64_t nquat, int bwd,
+                            size_t* bytes);
 
 /* Message for the last nonzero status returned on this thread ("" if none). */
 const char* ssd_last_error(void);

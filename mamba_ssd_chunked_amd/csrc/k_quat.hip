@@ -1,0 +1,529 @@
+// Quaternion cumulative-product scan of the Mamba-3 rotation, and its gradient.
+//
+// Page: burn-mamba "mamba3/quat_scan/backward.rs" (module doc, "Gradient math").
+// For every lane (b, h, j) of q [B, S, H, J, 4] (components w, x, y, z):
+//   cum[t] = q_t (x) cum[t-1],   cum[-1] = init   (Hamilton product)
+// and, for an upstream gradient d_cum, the exact reverse mode (valid for every
+// quaternion, not only unit ones): with the per-factor VJPs of o = a (x) b,
+// grad_a = g (x) conj(b) and grad_b = conj(a) (x) g, the cotangent G_t reaching
+// cum[t] obeys G_t = d_cum[t] + conj(q_{t+1}) (x) G_{t+1}, and
+//   d_q[t] = G_t (x) conj(cum[t-1]),    d_init = conj(q_0) (x) G_0.
+// The page's parallel closed form of that recurrence (prefix product, suffix
+// sum) assumes unit quaternions; the carries below need no such assumption.
+//
+// The scan moves 32 bytes per quaternion (q in, cum out) for about 28 flops, so
+// it is bound by HBM.  Both directions are first-order recurrences along t whose
+// step is associative, so the sequence is cut into segments of SEG = 4 * TS
+// steps handled by one workgroup each, and the segments are chained with a
+// single-pass decoupled look-back:
+//  * a workgroup covers 64 consecutive lanes (h, j) of one batch row -- one
+//    lane per thread of a wave, 16 contiguous bytes each, so a wave reads 1 KB
+//    of a row per step -- and its 4 waves take 4 consecutive sub-segments of TS
+//    steps, holding their q (and d_cum) in registers, so HBM is read once;
+//  * each wave reduces its sub-segment to one map (a product for the forward,
+//    an affine map M (x) H + v for the reverse), the workgroup combines the 4
+//    through LDS, publishes that aggregate, then wave 0 walks back over the
+//    preceding segments' records: an inclusive record ends the walk, an
+//    aggregate is folded in and the walk goes on.  One poll reads the status
+//    words of 64 neighbours (one per lane; a ballot finds the nearest inclusive
+//    record) and the records folded are loaded in batches, so the walk costs a
+//    few memory round trips, not one per neighbour;
+//  * a workgroup's chain (b, lane group) follows from its index; its segment is
+//    the ticket it draws from its chain's atomic counter when it starts, taken
+//    in dependency order (forward: from the first segment; reverse: from the
+//    last), so a workgroup only ever waits for workgroups of its chain that have
+//    already started, which never wait for it.  Every wait is bounded: past
+//    kMaxSpins polls the carry becomes NaN and is published, so the grid always
+//    drains (a wrong result, never a hang);
+//  * no memory fences: on gfx950 an agent-scope release writes back the whole
+//    L2 of the XCD, and one per workgroup serialised the scan (6x slower).
+//    Instead every record word is an fp64 value whose 16 lowest mantissa bits
+//    carry the call's tag, written and read with agent-scope relaxed 64-bit
+//    atomics (coherent across the XCDs' L2s without fences).  A reader accepts
+//    a record once all four of its words carry the current tag, and retries
+//    otherwise, so the order in which a record and its status word become
+//    visible does not matter.  The tag perturbs a record by at most 2^-36 of its
+//    value.  The status words and tickets are zeroed before every call.
+// Products and carries are fp64 (the fp32 inputs are exact in fp64), so the
+// result is within a few fp32 roundings of the exact scan at any length; cum
+// and d_q are rounded to fp32 once.  Which records a walk meets depends on
+// timing, so runs can differ in the last bit.
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kLanes = 64;     // lanes (quaternions of a row) per workgroup
+constexpr int kWaves = 4;      // sub-segments per workgroup
+constexpr int kThreads = kLanes * kWaves;
+constexpr uint32_t kAggregate = 1u, kInclusive = 2u;
+constexpr int kMaxSpins = 1 << 20;
+constexpr uint64_t kTagMask = 0xffffull;
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef double d4 __attribute__((ext_vector_type(4)));
+
+// Hamilton product a (x) b on (w, x, y, z).
+__device__ __forceinline__ d4 qmul(d4 a, d4 b) {
+    return d4{a[0] * b[0] - a[1] * b[1] - a[2] * b[2] - a[3] * b[3],
+              a[0] * b[1] + a[1] * b[0] + a[2] * b[3] - a[3] * b[2],
+              a[0] * b[2] - a[1] * b[3] + a[2] * b[0] + a[3] * b[1],
+              a[0] * b[3] + a[1] * b[2] - a[2] * b[1] + a[3] * b[0]};
+}
+
+__device__ __forceinline__ d4 qconj(d4 a) { return d4{a[0], -a[1], -a[2], -a[3]}; }
+__device__ __forceinline__ d4 to_d(f4 a) { return d4{a[0], a[1], a[2], a[3]}; }
+__device__ __forceinline__ f4 to_f(d4 a) {
+    return f4{static_cast<float>(a[0]), static_cast<float>(a[1]), static_cast<float>(a[2]),
+              static_cast<float>(a[3])};
+}
+__device__ __forceinline__ d4 qone() { return d4{1.0, 0.0, 0.0, 0.0}; }
+__device__ __forceinline__ d4 qzero() { return d4{0.0, 0.0, 0.0, 0.0}; }
+__device__ __forceinline__ d4 qnan() {
+    const double n = __builtin_nan("");
+    return d4{n, n, n, n};
+}
+
+// ------------------------------------------------------------ tagged records
+// Record r of lane `lane` in a pass's array: 4 words at ((r * 64 + lane) * 4).
+__device__ __forceinline__ void store_record(uint64_t* rec, int64_t r, int lane, d4 v,
+                                             uint32_t tag) {
+    uint64_t* p = rec + (r * kLanes + lane) * 4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint64_t w = (static_cast<uint64_t>(__double_as_longlong(v[c])) & ~kTagMask) | tag;
+        __hip_atomic_store(p + c, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Loads the record and reports whether every word carries `tag`.
+__device__ __forceinline__ bool load_record(const uint64_t* rec, int64_t r, int lane, uint32_t tag,
+                                            d4& v) {
+    uint64_t* p = const_cast<uint64_t*>(rec) + (r * kLanes + lane) * 4;
+    bool ok = true;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint64_t w = __hip_atomic_load(p + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = ok && (w & kTagMask) == tag;
+        v[c] = __longlong_as_double(static_cast<long long>(w));
+    }
+    return ok;
+}
+
+// Waits (bounded) until the record carries the tag; NaN if it never does.
+__device__ __forceinline__ d4 await_record(const uint64_t* rec, int64_t r, int lane, uint32_t tag) {
+    d4 v;
+    for (int i = 0; i < kMaxSpins; ++i) {
+        if (__all(load_record(rec, r, lane, tag, v))) return v;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return qnan();
+}
+
+__device__ __forceinline__ void set_status(uint32_t* status, uint32_t v, int lane) {
+    if (lane == 0) __hip_atomic_store(status, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One poll of the look-back window: lane i reads the status of the neighbour
+// j0 + dir * i (0 outside [0, nseg)).  Returns, in walk order, c = the first
+// neighbour holding an inclusive record and z = the first holding nothing yet
+// (64: none).
+__device__ __forceinline__ void poll_window(const uint32_t* status_row, int j0, int dir, int nseg,
+                                            int lane, int& c, int& z) {
+    const int j = j0 + dir * lane;
+    uint32_t s = 0;
+    if (j >= 0 && j < nseg)
+        s = __hip_atomic_load(const_cast<uint32_t*>(status_row + j), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t inc = __ballot(s == kInclusive);
+    const uint64_t none = __ballot(s == 0u);
+    c = inc ? __ffsll(static_cast<unsigned long long>(inc)) - 1 : 64;
+    z = none ? __ffsll(static_cast<unsigned long long>(none)) - 1 : 64;
+}
+
+// The walk shared by both directions: fold(j0, n) folds the aggregates of the n
+// neighbours j0, j0 + dir, ... in walk order, finish(j) ends with the inclusive
+// record of neighbour j; fold returns false when a record never arrives.
+// Returns false when kMaxSpins polls pass without progress or a record is lost.
+template <class Fold, class Finish>
+__device__ __forceinline__ bool look_back(const uint32_t* status_row, int j0, int dir, int nseg,
+                                          int lane, Fold fold, Finish finish) {
+    for (int spins = 0; spins < kMaxSpins;) {
+        int c, z;
+        poll_window(status_row, j0, dir, nseg, lane, c, z);
+        if (c < z) {  // every neighbour before the inclusive one holds an aggregate
+            if (!fold(j0, c)) return false;
+            finish(j0 + dir * c);
+            return true;
+        }
+        if (z > 0) {  // fold what is there and move the window on
+            if (!fold(j0, z)) return false;
+            j0 += dir * z;
+            spins = 0;
+            continue;
+        }
+        ++spins;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
+}
+
+// The chain (b, group) is the workgroup's blockIdx.x % BG; its position in the
+// chain is the ticket it draws from the chain's own counter (one 256-byte line
+// per chain, so chains do not queue on one address).
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* tickets, int bg, uint32_t* s_vid) {
+    if (threadIdx.x == 0) *s_vid = atomicAdd(tickets + 64 * bg, 1u);
+    __syncthreads();
+    return *s_vid;
+}
+
+}  // namespace
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        p[i] = v;
+}
+
+// Forward scan.  WRITE: store cum; otherwise only the segment records (the
+// backward's forward carries: inc[k] = cum at the end of segment k).
+template <int TS, bool WRITE>
+__global__ __launch_bounds__(kThreads) void k_quat_fwd(const float* __restrict__ q,
+                                                        const float* __restrict__ init,
+                                                        float* __restrict__ cum, QuatRecords rec,
+                                                        int nb, int64_t S, int W, int G, int nseg,
+                                                        uint32_t tag) {
+    constexpr int SEG = kWaves * TS;
+    __shared__ uint32_t s_vid;
+    __shared__ d4 s_part[kWaves][kLanes];
+    __shared__ d4 s_carry[kLanes];
+    const int wave = threadIdx.x / kLanes, lane = threadIdx.x % kLanes;
+    const int BG = nb * G;
+    const int bg = static_cast<int>(blockIdx.x % BG);
+    const int seg = static_cast<int>(take_ticket(rec.ticket, bg, &s_vid));
+    const int b = bg / G, g = bg % G;
+    const int col = g * kLanes + lane;
+    const bool act = col < W;
+    const int64_t t0 = static_cast<int64_t>(seg) * SEG + wave * TS;
+    const int64_t row = static_cast<int64_t>(W) * 4;
+    const float* qb = q + (static_cast<int64_t>(b) * S * W + col) * 4;
+
+    f4 x[TS];
+#pragma unroll
+    for (int i = 0; i < TS; ++i) {
+        const int64_t t = t0 + i;
+        x[i] = act && t < S ? *reinterpret_cast<const f4*>(qb + t * row) : f4{1.f, 0.f, 0.f, 0.f};
+    }
+    d4 P = to_d(x[0]);
+#pragma unroll
+    for (int i = 1; i < TS; ++i) P = qmul(to_d(x[i]), P);
+    s_part[wave][lane] = P;
+    __syncthreads();
+
+    if (wave == 0) {
+        const int64_t row0 = static_cast<int64_t>(bg) * nseg;
+        const int64_t k = row0 + seg;
+        d4 a = s_part[0][lane];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) a = qmul(s_part[w][lane], a);
+        d4 carry = qone();
+        if (seg == 0) {
+            if (init && act)
+                carry = to_d(*reinterpret_cast<const f4*>(init + (static_cast<int64_t>(b) * W + col) * 4));
+        } else {
+            store_record(rec.agg, k, lane, a, tag);
+            set_status(rec.status + k, kAggregate, lane);
+            d4 acc = qone();  // product of the aggregates walked over, latest first
+            auto fold = [&](int j0, int n) {
+                for (int base = 0; base < n; base += 8) {
+                    d4 r[8];
+                    bool ok = false;
+                    for (int spin = 0; spin < kMaxSpins && !ok; ++spin) {
+                        bool all = true;
+#pragma unroll
+                        for (int u = 0; u < 8; ++u)
+                            if (base + u < n)
+                                all = load_record(rec.agg, row0 + j0 - base - u, lane, tag, r[u]) && all;
+                        ok = __all(all);
+                        if (!ok) __builtin_amdgcn_s_sleep(1);
+                    }
+                    if (!ok) return false;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (base + u < n) acc = qmul(acc, r[u]);
+                }
+                return true;
+            };
+            auto finish = [&](int j) { carry = qmul(acc, await_record(rec.inc, row0 + j, lane, tag)); };
+            if (!look_back(rec.status + row0, seg - 1, -1, nseg, lane, fold, finish))
+                carry = qnan();  // timed out: publish NaN
+        }
+        store_record(rec.inc, k, lane, qmul(a, carry), tag);
+        set_status(rec.status + k, kInclusive, lane);
+        s_carry[lane] = carry;
+    }
+    if constexpr (WRITE) {
+        __syncthreads();
+        d4 c = s_carry[lane];
+#pragma unroll
+        for (int w = 0; w < kWaves - 1; ++w)
+            if (w < wave) c = qmul(s_part[w][lane], c);
+        float* cb = cum + (static_cast<int64_t>(b) * S * W + col) * 4;
+#pragma unroll
+        for (int i = 0; i < TS; ++i) {
+            const int64_t t = t0 + i;
+            c = qmul(to_d(x[i]), c);
+            if (act && t < S) __builtin_nontemporal_store(to_f(c), reinterpret_cast<f4*>(cb + t * row));
+        }
+    }
+}
+
+// Reverse pass of the backward.  With H_t = conj(q_t) (x) G_t (the cotangent that
+// cum[t] hands to cum[t-1]; H_S = 0), a sub-segment [t0, t0 + TS) maps the H
+// entering its end to the H leaving its start affinely: H_t0 = M (x) H_end + v.
+// fwd_inc: the forward-carry pass's inclusive records (cum at the end of each
+// segment; written by the previous kernel, so read as plain memory).
+template <int TS>
+__global__ __launch_bounds__(kThreads) void k_quat_bwd(const float* __restrict__ q,
+                                                        const float* __restrict__ init,
+                                                        const float* __restrict__ d_cum,
+                                                        float* __restrict__ d_q,
+                                                        float* __restrict__ d_init,
+                                                        const uint64_t* __restrict__ fwd_inc,
+                                                        QuatRecords rec, int nb, int64_t S, int W,
+                                                        int G, int nseg, uint32_t tag) {
+    constexpr int SEG = kWaves * TS;
+    __shared__ uint32_t s_vid;
+    __shared__ d4 s_P[kWaves][kLanes], s_M[kWaves][kLanes], s_V[kWaves][kLanes];
+    __shared__ d4 s_H[kLanes], s_C[kLanes];
+    const int wave = threadIdx.x / kLanes, lane = threadIdx.x % kLanes;
+    const int BG = nb * G;
+    const int bg = static_cast<int>(blockIdx.x % BG);
+    const int seg = nseg - 1 - static_cast<int>(take_ticket(rec.ticket, bg, &s_vid));
+    const int b = bg / G, g = bg % G;
+    const int col = g * kLanes + lane;
+    const bool act = col < W;
+    const int64_t t0 = static_cast<int64_t>(seg) * SEG + wave * TS;
+    const int64_t row = static_cast<int64_t>(W) * 4;
+    const int64_t base = (static_cast<int64_t>(b) * S * W + col) * 4;
+
+    f4 x[TS], dc[TS];
+#pragma unroll
+    for (int i = 0; i < TS; ++i) {
+        const int64_t t = t0 + i;
+        const bool in = act && t < S;
+        x[i] = in ? *reinterpret_cast<const f4*>(q + base + t * row) : f4{1.f, 0.f, 0.f, 0.f};
+        dc[i] = in ? *reinterpret_cast<const f4*>(d_cum + base + t * row) : f4{0.f, 0.f, 0.f, 0.f};
+    }
+    {
+        d4 P = to_d(x[0]);
+#pragma unroll
+        for (int i = 1; i < TS; ++i) P = qmul(to_d(x[i]), P);
+        d4 M = qone(), v = qzero();
+#pragma unroll
+        for (int i = TS - 1; i >= 0; --i) {
+            const d4 cq = qconj(to_d(x[i]));
+            v = qmul(cq, to_d(dc[i]) + v);
+            M = qmul(cq, M);
+        }
+        s_P[wave][lane] = P;
+        s_M[wave][lane] = M;
+        s_V[wave][lane] = v;
+    }
+    __syncthreads();
+
+    if (wave == 0) {
+        const int64_t row0 = static_cast<int64_t>(bg) * nseg;
+        const int64_t k = row0 + seg;
+        // the workgroup's map f_0 o f_1 o f_2 o f_3 (sub-segment 0 is the earliest)
+        d4 M = s_M[kWaves - 1][lane], v = s_V[kWaves - 1][lane];
+#pragma unroll
+        for (int w = kWaves - 2; w >= 0; --w) {
+            v = qmul(s_M[w][lane], v) + s_V[w][lane];
+            M = qmul(s_M[w][lane], M);
+        }
+        d4 carry = qzero();  // H entering the end of this segment
+        if (seg != nseg - 1) {
+            store_record(rec.agg, k, lane, M, tag);
+            store_record(rec.agg2, k, lane, v, tag);
+            set_status(rec.status + k, kAggregate, lane);
+            d4 aM = qone(), av = qzero();  // composition of the maps walked over
+            auto fold = [&](int j0, int n) {
+                for (int base4 = 0; base4 < n; base4 += 4) {
+                    d4 rm[4], rv[4];
+                    bool ok = false;
+                    for (int spin = 0; spin < kMaxSpins && !ok; ++spin) {
+                        bool all = true;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (base4 + u < n) {
+                                const int64_t r = row0 + j0 + base4 + u;
+                                all = load_record(rec.agg, r, lane, tag, rm[u]) && all;
+                                all = load_record(rec.agg2, r, lane, tag, rv[u]) && all;
+                            }
+                        ok = __all(all);
+                        if (!ok) __builtin_amdgcn_s_sleep(1);
+                    }
+                    if (!ok) return false;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (base4 + u < n) {
+                            av = qmul(aM, rv[u]) + av;
+                            aM = qmul(aM, rm[u]);
+                        }
+                }
+                return true;
+            };
+            auto finish = [&](int j) { carry = qmul(aM, await_record(rec.inc, row0 + j, lane, tag)) + av; };
+            if (!look_back(rec.status + row0, seg + 1, 1, nseg, lane, fold, finish))
+                carry = qnan();  // timed out: publish NaN
+        }
+        const d4 h_start = qmul(M, carry) + v;
+        store_record(rec.inc, k, lane, h_start, tag);
+        set_status(rec.status + k, kInclusive, lane);
+        if (seg == 0 && d_init && act)
+            *reinterpret_cast<f4*>(d_init + (static_cast<int64_t>(b) * W + col) * 4) = to_f(h_start);
+        s_H[lane] = carry;
+        d4 c0 = qone();
+        if (seg == 0) {
+            if (init && act)
+                c0 = to_d(*reinterpret_cast<const f4*>(init + (static_cast<int64_t>(b) * W + col) * 4));
+        } else {
+            const uint64_t* p = fwd_inc + ((k - 1) * kLanes + lane) * 4;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) c0[c] = __longlong_as_double(static_cast<long long>(p[c]));
+        }
+        s_C[lane] = c0;
+    }
+    __syncthreads();
+
+    d4 h = s_H[lane];  // H entering the end of this wave's sub-segment
+#pragma unroll
+    for (int w = kWaves - 1; w > 0; --w)
+        if (w > wave) h = qmul(s_M[w][lane], h) + s_V[w][lane];
+    d4 c = s_C[lane];  // cum[t0 - 1]
+#pragma unroll
+    for (int w = 0; w < kWaves - 1; ++w)
+        if (w < wave) c = qmul(s_P[w][lane], c);
+    f4 prev[TS];  // cum[t - 1] for the sub-segment's steps (rounded: it only scales d_q)
+#pragma unroll
+    for (int i = 0; i < TS; ++i) {
+        prev[i] = to_f(c);
+        c = qmul(to_d(x[i]), c);
+    }
+#pragma unroll
+    for (int i = TS - 1; i >= 0; --i) {
+        const d4 G = to_d(dc[i]) + h;
+        const int64_t t = t0 + i;
+        if (act && t < S)
+            __builtin_nontemporal_store(to_f(qmul(G, qconj(to_d(prev[i])))),
+                                        reinterpret_cast<f4*>(d_q + base + t * row));
+        h = qmul(qconj(to_d(x[i])), G);
+    }
+}
+
+// ------------------------------------------------------------------ host side
+QuatPlan quat_plan(const QuatShape& s, bool bwd) {
+    QuatPlan p;
+    if (s.B <= 0 || s.S <= 0) return p;
+    const int64_t blocks = static_cast<int64_t>(s.B) * s.G * s.nseg;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) & ~static_cast<size_t>(255);
+        return at;
+    };
+    // per pass: one ticket per chain (each in its own 256 bytes), then one status
+    // word per workgroup
+    const int64_t chains = static_cast<int64_t>(s.B) * s.G;
+    p.words_per_pass = 64 * chains + (blocks + 63) / 64 * 64;
+    p.flag_words = p.words_per_pass * (bwd ? 2 : 1);
+    p.flags = take(4 * static_cast<size_t>(p.flag_words));
+    const size_t rec = static_cast<size_t>(blocks) * kLanes * 4 * sizeof(uint64_t);
+    p.agg = take(rec);
+    p.inc = take(rec);
+    if (bwd) {
+        p.agg_b = take(rec);
+        p.agg2_b = take(rec);
+        p.inc_b = take(rec);
+    }
+    p.total = off;
+    return p;
+}
+
+QuatShape quat_shape(int64_t B, int64_t S, int64_t H, int64_t J) {
+    QuatShape s;
+    s.B = static_cast<int>(B);
+    s.S = S;
+    s.W = static_cast<int>(H * J);
+    s.G = static_cast<int>((s.W + kLanes - 1) / kLanes);
+    s.nseg = static_cast<int>((S + kQuatSeg - 1) / kQuatSeg);
+    return s;
+}
+
+namespace {
+
+QuatRecords records(const QuatShape& s, const QuatPlan& p, void* ws, int pass) {
+    char* w = static_cast<char*>(ws);
+    uint32_t* flags = reinterpret_cast<uint32_t*>(w + p.flags) + pass * p.words_per_pass;
+    QuatRecords r;
+    r.ticket = flags;
+    r.status = flags + 64 * static_cast<int64_t>(s.B) * s.G;
+    if (pass == 0) {
+        r.agg = reinterpret_cast<uint64_t*>(w + p.agg);
+        r.agg2 = nullptr;
+        r.inc = reinterpret_cast<uint64_t*>(w + p.inc);
+    } else {
+        r.agg = reinterpret_cast<uint64_t*>(w + p.agg_b);
+        r.agg2 = reinterpret_cast<uint64_t*>(w + p.agg2_b);
+        r.inc = reinterpret_cast<uint64_t*>(w + p.inc_b);
+    }
+    return r;
+}
+
+hipError_t fill_u32(uint32_t* p, int64_t n, hipStream_t st) {
+    const int64_t blocks = (n + 255) / 256;
+    const unsigned grid = static_cast<unsigned>(blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks));
+    k_fill_u32<<<dim3(grid), dim3(256), 0, st>>>(p, n, 0u);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quat_clear(const QuatShape& s, bool bwd, void* ws, hipStream_t st) {
+    const QuatPlan p = quat_plan(s, bwd);
+    return fill_u32(reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + p.flags), p.flag_words, st);
+}
+
+hipError_t launch_quat_fwd(const QuatShape& s, const float* q, const float* init, float* cum,
+                           void* ws, uint32_t epoch, hipStream_t st) {
+    const QuatPlan p = quat_plan(s, false);
+    const int64_t blocks = static_cast<int64_t>(s.B) * s.G * s.nseg;
+    k_quat_fwd<kQuatTS, true><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+        q, init, cum, records(s, p, ws, 0), s.B, s.S, s.W, s.G, s.nseg, epoch & 0xffffu);
+    return hipGetLastError();
+}
+
+hipError_t launch_quat_bwd(const QuatShape& s, const float* q, const float* init,
+                           const float* d_cum, float* d_q, float* d_init, void* ws,
+                           uint32_t epoch, hipStream_t st, int stage) {
+    const QuatPlan p = quat_plan(s, true);
+    const int64_t blocks = static_cast<int64_t>(s.B) * s.G * s.nseg;
+    const QuatRecords r0 = records(s, p, ws, 0);
+    if (stage == 0) {
+        k_quat_fwd<kQuatTS, false><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+            q, init, nullptr, r0, s.B, s.S, s.W, s.G, s.nseg, epoch & 0xffffu);
+    } else {
+        k_quat_bwd<kQuatTS><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+            q, init, d_cum, d_q, d_init, r0.inc, records(s, p, ws, 1), s.B, s.S, s.W, s.G, s.nseg,
+            epoch & 0xffffu);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quat_zero(float* p, int64_t n, hipStream_t st) {
+    return fill_u32(reinterpret_cast<uint32_t*>(p), n, st);
+}
+
+}  // namespace ssd

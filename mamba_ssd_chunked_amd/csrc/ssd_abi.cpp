@@ -6,6 +6,7 @@
 // synchronising.  The workspace is caller-owned; the library allocates nothing.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -303,6 +304,34 @@ int check_diag_ptrs(const ssd::DiagShape& d,
     const size_t ia = d.io == SSD_BF16 ? 8 : 16;
     for (auto& p : io)
         if (int rc = check_align(p.first, p.second, ia)) return rc;
+    return SSD_OK;
+}
+
+// Tag of one quaternion-scan call: its look-back records carry the low 16 bits,
+// which must differ from the previous call's on the same workspace and never be
+// 0 (the value of zeroed memory).
+uint32_t next_quat_tag() {
+    static std::atomic<uint32_t> counter{0};
+    for (;;) {
+        const uint32_t e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+        if ((e & 0xffffu) != 0) return e;
+    }
+}
+
+// Shared checks of the quaternion-scan entry points; fills *s.
+int validate_quat(const char* who, int64_t batch, int64_t seq, int64_t nheads, int64_t nquat,
+                  ssd::QuatShape* s) {
+    if (batch < 0 || seq < 0 || nheads <= 0 || nquat <= 0)
+        return fail(SSD_ERR_SHAPE,
+                    "%s: need batch >= 0, seq >= 0 and nheads, nquat > 0 (got %lld, %lld, %lld, %lld)",
+                    who, (long long)batch, (long long)seq, (long long)nheads, (long long)nquat);
+    const double lanes = (double)nheads * (double)nquat;
+    if (lanes > (double)(1 << 24) || batch > (1 << 30) || seq > (int64_t(1) << 40) ||
+        (double)batch * seq * lanes * 4.0 > 4.0e18)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: problem too large for one call", who);
+    *s = ssd::quat_shape(batch, seq, nheads, nquat);
+    if ((double)s->B * s->G * s->nseg > 2.0e9)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: problem too large for one call (split the batch)", who);
     return SSD_OK;
 }
 
@@ -642,6 +671,67 @@ int ssd_y_diag_bwd(int64_t ntokens, int64_t mimo_rank, int64_t nheads, int64_t h
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (ntokens > 0)
         SSD_HIP(ssd::launch_diag_bwd(d, dy, v, B, C, gamma, d_v, d_B, d_C, d_gamma, st), "k_diag_bwd");
+    return ok();
+}
+
+int ssd_quat_workspace_size(int64_t batch, int64_t seq, int64_t nheads, int64_t nquat, int bwd,
+                            size_t* bytes) {
+    ssd::QuatShape s;
+    if (int rc = validate_quat("ssd_quat_workspace_size", batch, seq, nheads, nquat, &s)) return rc;
+    if (!bytes) return fail(SSD_ERR_NULL, "ssd_quat_workspace_size: bytes is NULL");
+    *bytes = ssd::quat_plan(s, bwd != 0).total;
+    return ok();
+}
+
+int ssd_quat_scan(int64_t batch, int64_t seq, int64_t nheads, int64_t nquat, const float* q,
+                  const float* init, float* cum, void* ws, size_t ws_bytes, void* stream) {
+    ssd::QuatShape s;
+    if (int rc = validate_quat("ssd_quat_scan", batch, seq, nheads, nquat, &s)) return rc;
+    const bool work = batch > 0 && seq > 0;
+    if (work && (!q || !cum)) return fail(SSD_ERR_NULL, "ssd_quat_scan: q and cum are required");
+    for (auto p : {std::make_pair((const void*)q, "q"), std::make_pair((const void*)init, "init"),
+                   std::make_pair((const void*)cum, "cum")})
+        if (int rc = check_align(p.first, p.second, 16)) return rc;
+    const ssd::QuatPlan plan = ssd::quat_plan(s, false);
+    if (plan.total > 0 && (!ws || ws_bytes < plan.total))
+        return fail(SSD_ERR_WORKSPACE, "ssd_quat_scan: workspace needs %zu bytes (got %zu%s)",
+                    plan.total, ws_bytes, ws ? "" : ", NULL pointer");
+    if (int rc = check_align(ws, "workspace", 256)) return rc;
+    if (!work) return ok();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint32_t tag = next_quat_tag();
+    SSD_HIP(ssd::launch_quat_clear(s, false, ws, st), "k_fill_u32");
+    SSD_HIP(ssd::launch_quat_fwd(s, q, init, cum, ws, tag, st), "k_quat_fwd");
+    return ok();
+}
+
+int ssd_quat_scan_bwd(int64_t batch, int64_t seq, int64_t nheads, int64_t nquat, const float* q,
+                      const float* init, const float* d_cum, float* d_q, float* d_init, void* ws,
+                      size_t ws_bytes, void* stream) {
+    ssd::QuatShape s;
+    if (int rc = validate_quat("ssd_quat_scan_bwd", batch, seq, nheads, nquat, &s)) return rc;
+    const bool work = batch > 0 && seq > 0;
+    if (work && (!q || !d_cum || !d_q))
+        return fail(SSD_ERR_NULL, "ssd_quat_scan_bwd: q, d_cum and d_q are required");
+    for (auto p : {std::make_pair((const void*)q, "q"), std::make_pair((const void*)init, "init"),
+                   std::make_pair((const void*)d_cum, "d_cum"), std::make_pair((const void*)d_q, "d_q"),
+                   std::make_pair((const void*)d_init, "d_init")})
+        if (int rc = check_align(p.first, p.second, 16)) return rc;
+    const ssd::QuatPlan plan = ssd::quat_plan(s, true);
+    if (plan.total > 0 && (!ws || ws_bytes < plan.total))
+        return fail(SSD_ERR_WORKSPACE, "ssd_quat_scan_bwd: workspace needs %zu bytes (got %zu%s)",
+                    plan.total, ws_bytes, ws ? "" : ", NULL pointer");
+    if (int rc = check_align(ws, "workspace", 256)) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!work) {  // nothing flows back: d_init = 0
+        if (batch > 0 && d_init)
+            SSD_HIP(ssd::launch_quat_zero(d_init, batch * nheads * nquat * 4, st), "k_fill_u32");
+        return ok();
+    }
+    const uint32_t tag = next_quat_tag();
+    SSD_HIP(ssd::launch_quat_clear(s, true, ws, st), "k_fill_u32");
+    SSD_HIP(ssd::launch_quat_bwd(s, q, init, d_cum, d_q, d_init, ws, tag, st, 0), "k_quat_carry");
+    SSD_HIP(ssd::launch_quat_bwd(s, q, init, d_cum, d_q, d_init, ws, tag, st, 1), "k_quat_bwd");
     return ok();
 }
 

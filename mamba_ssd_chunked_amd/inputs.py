@@ -24,6 +24,13 @@ dy ~ N(0, 1) ``[b, n, l, m, h, p]``, B and C ~ N(0, 1) / sqrt(dstate)
 ``[b, n, l, m, h, r]`` and gamma = softplus(z - 2) ``[b, n, l, h]`` (a
 step-sized positive weight, like dt), after which bf16 workloads round v, B, C
 and dy to bfloat16.
+
+The Mamba-3 quaternion rotation scan (``QuatWorkload``) draws, in this order,
+g ~ N(0, 1) ``[b, s, h, j, 4]``, z ~ N(0, 1) ``[b, s, h, j]``, g0 ~ N(0, 1)
+``[b, h, j, 4]`` and d_cum ~ N(0, 1) ``[b, s, h, j, 4]``.  The step quaternions
+are q = g / |g| (uniform on the unit 3-sphere: Haar-random rotations, the
+largest per-step rotations a rotation can produce), times exp(norm_std * z)
+when norm_std > 0 (non-unit steps); init = g0 / |g0| or None (the identity).
 """
 from __future__ import annotations
 
@@ -172,3 +179,42 @@ def make_diag_inputs(w: DiagWorkload) -> dict:
     elif w.io != "f32":
         raise ValueError(f"unknown io dtype {w.io!r}")
     return dict(v=v, dy=dy, B=B, C=C, gamma=gamma)
+
+
+@dataclasses.dataclass(frozen=True)
+class QuatWorkload:
+    """Shapes of the quaternion cumulative-product scan: q [b, s, h, j, 4]."""
+    name: str
+    batch: int
+    seq: int
+    nheads: int
+    nquat: int                 # quaternion blocks per head (state_rank / 4 when fully rotated)
+    norm_std: float = 0.0      # 0: unit step quaternions
+    random_init: bool = True   # False: init = None (the identity)
+    seed: int = 1007
+
+    def describe(self) -> dict:
+        return dict(workload=self.name, batch=self.batch, seq_len=self.seq, nheads=self.nheads,
+                    nquat=self.nquat, unit=self.norm_std == 0.0,
+                    init="random unit" if self.random_init else "identity")
+
+
+# The SSD benchmark's shapes with its 128-wide state rotated as 32 quaternion blocks.
+QUAT_WORKLOADS = {
+    "mamba3_quat_scan_fp32": QuatWorkload("mamba3_quat_scan_fp32", 4, 2048, 24, 32, seed=1007),
+}
+
+
+def make_quat_inputs(w: QuatWorkload) -> dict:
+    """Draw q, init, d_cum for the quaternion scan (see module docstring)."""
+    g = torch.Generator().manual_seed(w.seed)
+    b, s, h, j = w.batch, w.seq, w.nheads, w.nquat
+    raw = torch.randn(b, s, h, j, 4, generator=g, dtype=torch.float32)
+    z = torch.randn(b, s, h, j, generator=g, dtype=torch.float32)
+    raw0 = torch.randn(b, h, j, 4, generator=g, dtype=torch.float32)
+    d_cum = torch.randn(b, s, h, j, 4, generator=g, dtype=torch.float32)
+    q = raw / raw.norm(dim=-1, keepdim=True)
+    if w.norm_std > 0:
+        q = q * torch.exp(w.norm_std * z)[..., None]
+    init = raw0 / raw0.norm(dim=-1, keepdim=True) if w.random_init else None
+    return dict(q=q.contiguous(), init=init, d_cum=d_cum)

@@ -30,8 +30,8 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPP
           4: "SSD_ERR_DTYPE", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_HIP"}
 EXPORTS = ("ssd_workspace_size", "ssd_fwd", "ssd_bwd", "ssd_state_moments",
            "ssd_state_moments_bwd", "ssd_moments_pr", "ssd_moments_pr_bwd", "ssd_y_diag",
-           "ssd_y_diag_bwd", "ssd_last_error",
-           "ssd_timing_enable", "ssd_timing_collect")
+           "ssd_y_diag_bwd", "ssd_quat_scan", "ssd_quat_scan_bwd", "ssd_quat_workspace_size",
+           "ssd_last_error", "ssd_timing_enable", "ssd_timing_collect")
 
 
 class ssd_dims(ctypes.Structure):
@@ -76,9 +76,12 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_moments_pr_bwd.argtypes = [I64, I64, I64, P, P, P, P, ctypes.c_int, P, P, P]
     lib.ssd_y_diag.argtypes = [I64] * 5 + [ctypes.c_int] + [P] * 6
     lib.ssd_y_diag_bwd.argtypes = [I64] * 5 + [ctypes.c_int] + [P] * 10
+    lib.ssd_quat_scan.argtypes = [I64] * 4 + [P] * 4 + [ctypes.c_size_t, P]
+    lib.ssd_quat_scan_bwd.argtypes = [I64] * 4 + [P] * 6 + [ctypes.c_size_t, P]
+    lib.ssd_quat_workspace_size.argtypes = [I64] * 4 + [ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
     for f in ("ssd_workspace_size", "ssd_fwd", "ssd_bwd", "ssd_state_moments",
               "ssd_state_moments_bwd", "ssd_moments_pr", "ssd_moments_pr_bwd", "ssd_y_diag",
-              "ssd_y_diag_bwd"):
+              "ssd_y_diag_bwd", "ssd_quat_scan", "ssd_quat_scan_bwd", "ssd_quat_workspace_size"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ssd_last_error.argtypes = []
     lib.ssd_last_error.restype = ctypes.c_char_p
@@ -299,6 +302,42 @@ def ssd_y_diag_bwd(dy, v, B, C, gamma, d_v, d_B, d_C, d_gamma, stream=None) -> i
     return load_library().ssd_y_diag_bwd(T, m, h, p, r, io, *args, _stream(stream))
 
 
+def _quat_sizes(q: torch.Tensor):
+    """(b, s, h, j) of q ``[b, s, h, j, 4]``."""
+    if q.dim() != 5 or q.shape[-1] != 4:
+        raise ValueError("q must be [b, s, h, j, 4]")
+    return tuple(int(v) for v in q.shape[:4])
+
+
+def ssd_quat_workspace_size(batch, seq, nheads, nquat, bwd) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load_library().ssd_quat_workspace_size(batch, seq, nheads, nquat, int(bool(bwd)),
+                                                ctypes.byref(n))
+    if rc != 0:
+        raise SsdError(rc, "ssd_quat_workspace_size", ssd_last_error())
+    return n.value
+
+
+def ssd_quat_scan(q, init, cum, ws, stream=None) -> int:
+    b, s, h, j = _quat_sizes(q)
+    f = torch.float32
+    w, nbytes = _ws(ws)
+    args = [_ptr(q, "q", f, b * s * h * j * 4, True), _ptr(init, "init", f, b * h * j * 4, False),
+            _ptr(cum, "cum", f, b * s * h * j * 4, True)]
+    return load_library().ssd_quat_scan(b, s, h, j, *args, w, nbytes, _stream(stream))
+
+
+def ssd_quat_scan_bwd(q, init, d_cum, d_q, d_init, ws, stream=None) -> int:
+    b, s, h, j = _quat_sizes(q)
+    f = torch.float32
+    w, nbytes = _ws(ws)
+    args = [_ptr(q, "q", f, b * s * h * j * 4, True), _ptr(init, "init", f, b * h * j * 4, False),
+            _ptr(d_cum, "d_cum", f, b * s * h * j * 4, True),
+            _ptr(d_q, "d_q", f, b * s * h * j * 4, True),
+            _ptr(d_init, "d_init", f, b * h * j * 4, False)]
+    return load_library().ssd_quat_scan_bwd(b, s, h, j, *args, w, nbytes, _stream(stream))
+
+
 # ------------------------------------------------------------ allocating helpers
 def _check(rc: int, where: str):
     if rc != 0:
@@ -421,3 +460,27 @@ def y_diag_bwd(dy, v, B, C, gamma, stream=None):
     _check(ssd_y_diag_bwd(dy, v, B, C, gamma, out["d_v"], out["d_B"], out["d_C"], out["d_gamma"],
                           stream), "ssd_y_diag_bwd")
     return out
+
+
+def quat_workspace(q: torch.Tensor, bwd: bool) -> torch.Tensor:
+    b, s, h, j = _quat_sizes(q)
+    n = ssd_quat_workspace_size(b, s, h, j, bwd)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def quat_scan(q, init=None, ws=None, stream=None):
+    """cum[t] = q_t (x) cum[t-1] over q ``[b, s, h, j, 4]`` (see ssd_quat_scan)."""
+    cum = torch.empty_like(q)
+    ws = quat_workspace(q, False) if ws is None else ws
+    _check(ssd_quat_scan(q, init, cum, ws, stream), "ssd_quat_scan")
+    return cum
+
+
+def quat_scan_bwd(q, init, d_cum, want_d_init=True, ws=None, stream=None):
+    """Returns ``(d_q, d_init)`` (d_init None unless wanted)."""
+    b, s, h, j = _quat_sizes(q)
+    d_q = torch.empty_like(q)
+    d_init = torch.empty((b, h, j, 4), device=q.device) if want_d_init else None
+    ws = quat_workspace(q, True) if ws is None else ws
+    _check(ssd_quat_scan_bwd(q, init, d_cum, d_q, d_init, ws, stream), "ssd_quat_scan_bwd")
+    return d_q, d_init

@@ -195,3 +195,46 @@ def test_y_diag_entry_points_reject_bad_arguments(lib, case, code):
 def test_y_diag_of_no_tokens_is_a_no_op(lib):
     assert lib.ssd_y_diag(0, 4, 3, 64, 128, 0, None, None, None, None, None, None) == 0
     assert lib.ssd_y_diag_bwd(0, 4, 3, 64, 128, 0, *([None] * 10)) == 0
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(b=-1), 2), (dict(s=-1), 2), (dict(h=0), 2), (dict(j=0), 2), (dict(h=1 << 13, j=1 << 12), 3),
+    (dict(q=0), 1), (dict(out=0), 1), (dict(q=FAKE + 4), 3), (dict(out=FAKE + 8), 3),
+    (dict(init=FAKE + 4), 3), (dict(ws=0), 5), (dict(ws_bytes=16), 5), (dict(ws=FAKE + 64), 3),
+])
+def test_quat_entry_points_reject_bad_arguments(lib, case, code):
+    a = dict(b=2, s=50, h=3, j=5, q=FAKE, init=None, out=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(case)
+    rc = lib.ssd_quat_scan(a["b"], a["s"], a["h"], a["j"], a["q"], a["init"], a["out"], a["ws"],
+                           a["ws_bytes"], None)
+    assert rc == code, ssd.ssd_last_error()
+    rc = lib.ssd_quat_scan_bwd(a["b"], a["s"], a["h"], a["j"], a["q"], a["init"], FAKE, a["out"],
+                               None, a["ws"], a["ws_bytes"], None)
+    assert rc == code, ssd.ssd_last_error()
+
+
+def test_quat_workspace_plan(lib):
+    # a ticket per (batch, 64-lane group) chain (64 words each), one status word per
+    # (chain, 64-step segment), and fp64 quaternion records per lane: 2 arrays
+    # forward, 5 backward
+    b, s, h, j = 4, 2048, 24, 32
+    chains = b * (h * j // 64)
+    blocks = chains * (s // 64)
+    words = 64 * chains + -(-blocks // 64) * 64
+    fwd = ssd.ssd_quat_workspace_size(b, s, h, j, False)
+    bwd = ssd.ssd_quat_workspace_size(b, s, h, j, True)
+    assert fwd == 4 * words + 2 * blocks * 64 * 32
+    assert bwd == 8 * words + 5 * blocks * 64 * 32
+    # ragged: 15 lanes still take a whole group, 97 steps two segments
+    assert ssd.ssd_quat_workspace_size(2, 97, 3, 5, False) == 4 * (2 * 64 + 64) + 2 * (2 * 2 * 64 * 32)
+    for args in ((0, 10, 2, 2), (3, 0, 2, 2)):
+        assert ssd.ssd_quat_workspace_size(*args, False) == 0
+        assert ssd.ssd_quat_workspace_size(*args, True) == 0
+
+
+def test_quat_of_nothing_is_a_no_op(lib):
+    assert lib.ssd_quat_scan(0, 10, 2, 2, None, None, None, None, 0, None) == 0
+    assert lib.ssd_quat_scan(3, 0, 2, 2, None, None, None, None, 0, None) == 0
+    assert lib.ssd_quat_scan_bwd(0, 10, 2, 2, None, None, None, None, None, None, 0, None) == 0
+    # an empty sequence with no d_init requested enqueues nothing
+    assert lib.ssd_quat_scan_bwd(3, 0, 2, 2, None, None, None, None, None, None, 0, None) == 0

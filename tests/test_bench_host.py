@@ -60,3 +60,13 @@ def test_diag_bytes_count_every_tensor_once():
     assert bench.diag_bytes(w, "k_diag_fwd") == pairs * (4 * (4 * 64 + 2 * 4 * 128 + 4 * 64) + 4)
     assert bench.diag_bytes(w, "k_diag_bwd") == pairs * (4 * (3 * 4 * 64 + 4 * 4 * 128) + 8)
     assert bench.diag_bytes(w, "other") is None
+
+
+def test_quat_bytes_count_every_tensor_once():
+    w = inputs.QUAT_WORKLOADS["mamba3_quat_scan_fp32"]
+    n, lanes = 4 * 2048 * 24 * 32, 4 * 24 * 32
+    # fwd: q in, cum out (16 B per quaternion each) + init; reverse pass: q, d_cum, d_q + init, d_init
+    assert bench.quat_bytes(w, "k_quat_fwd") == 32 * n + 16 * lanes
+    assert bench.quat_bytes(w, "k_quat_bwd") == 48 * n + 32 * lanes
+    assert bench.quat_bytes(w, "k_quat_carry") == 16 * n + 16 * lanes
+    assert bench.quat_bytes(w, "k_fill_u32") is None

@@ -1,0 +1,143 @@
+"""GPU parity of ssd_quat_scan / ssd_quat_scan_bwd against the CPU oracle.
+
+The Mamba-3 quaternion cumulative-product scan cum[t] = q_t (x) cum[t-1]
+(burn-mamba mamba3/quat_scan backward.rs page) and its exact reverse mode,
+through the C ABI, on seeded inputs: one step; partial 64-lane groups and
+ragged last segments; identity and random init; non-unit step quaternions;
+look-back chains of 32 to 2048 segments; the full-size workload on sampled
+heads (lanes are independent, so the oracle computes exactly those outputs)
+plus the unit-norm property on every output; workspace reuse across calls of
+different sizes; empty sequence and batch; run-to-run agreement.  Bar:
+per-tensor relative L2 <= 1e-5 (fp32 inputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import TOL, compare, say
+from mamba_ssd_chunked_amd import inputs, ssd
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("cum", "d_q", "d_init")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ssd.load_library()
+
+
+def gpu_quat(i, ws_fwd=None, ws_bwd=None):
+    q = i["q"].cuda()
+    init = i["init"].cuda() if i["init"] is not None else None
+    dc = i["d_cum"].cuda()
+    cum = ssd.quat_scan(q, init, ws=ws_fwd)
+    d_q, d_init = ssd.quat_scan_bwd(q, init, dc, ws=ws_bwd)
+    torch.cuda.synchronize()
+    return dict(cum=cum.cpu().numpy(), d_q=d_q.cpu().numpy(), d_init=d_init.cpu().numpy())
+
+
+def oracle_quat(i, heads=None):
+    def sel(t, axis):
+        if t is None:
+            return None
+        t = t.double().numpy()
+        return t if heads is None else np.take(t, heads, axis=axis)
+    q, init, dc = sel(i["q"], 2), sel(i["init"], 1), sel(i["d_cum"], 2)
+    cum = oracle.quat_scan(q, init)
+    d_q, d_init = oracle.quat_scan_bwd(q, init, dc)
+    return dict(cum=cum, d_q=d_q, d_init=d_init)
+
+
+SHAPES = [
+    # batch, seq, nheads, nquat, norm_std, random_init
+    (1, 1, 1, 1, 0.0, True),       # a single step
+    (2, 37, 3, 5, 0.0, True),      # 15 lanes (part of one 64-lane group), ragged last segment
+    (1, 32, 1, 64, 0.0, False),    # exactly one segment and one full group, identity init
+    (2, 300, 2, 40, 0.0, True),    # 80 lanes: a full and a partial group, 10 segments
+    (1, 1000, 4, 32, 0.0, True),   # 2 groups, 32 segments
+    (3, 129, 5, 3, 0.05, True),    # non-unit steps (norms exp(0.05 z)), ragged
+    (2, 64, 3, 7, 0.3, False),     # strongly non-unit steps, identity init
+    (1, 4096, 1, 16, 0.0, False),  # 128-segment chains
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"b{s[0]}_s{s[1]}_h{s[2]}_j{s[3]}_n{s[4]}" for s in SHAPES])
+def test_quat_small_shapes(shape):
+    b, s, h, j, nstd, rinit = shape
+    w = inputs.QuatWorkload("t", b, s, h, j, norm_std=nstd, random_init=rinit, seed=17 + s + j)
+    say(f"quat parity {shape}")
+    i = inputs.make_quat_inputs(w)
+    compare(gpu_quat(i), oracle_quat(i), TOL["f32"], KEYS, f"quat {shape}")
+
+
+def test_quat_full_workload_sampled_heads():
+    w = inputs.QUAT_WORKLOADS["mamba3_quat_scan_fp32"]
+    say(f"quat parity {w.describe()}")
+    i = inputs.make_quat_inputs(w)
+    g = gpu_quat(i)
+    heads = [0, 11, 23]
+    ref = oracle_quat(i, heads)
+    sub = dict(cum=g["cum"][:, :, heads], d_q=g["d_q"][:, :, heads], d_init=g["d_init"][:, heads])
+    compare(sub, ref, TOL["f32"], KEYS, "quat full workload, heads 0, 11, 23")
+    # every output: the norm is multiplicative, |cum[t]| = prod_{s<=t} |q_s| |init|
+    # (fp64 from the fp32 inputs, whose own norms are 1 only to fp32 rounding)
+    qn = np.linalg.norm(i["q"].double().numpy(), axis=-1)
+    expect = np.cumprod(qn, axis=1) * np.linalg.norm(i["init"].double().numpy(), axis=-1)[:, None]
+    norms = np.linalg.norm(g["cum"].astype(np.float64), axis=-1)
+    dev = np.abs(norms / expect - 1).max()
+    say(f"  max | |cum| / (prod |q| |init|) - 1 | = {dev:.2e}")
+    assert dev < 1e-6
+
+
+def test_quat_long_chains():
+    # one 64-lane group, 65536 steps: 2048 segments chained by the look-back
+    w = inputs.QuatWorkload("long", 1, 65536, 2, 32, seed=1009)
+    say("quat parity long chains (1, 65536, 2, 32)")
+    i = inputs.make_quat_inputs(w)
+    compare(gpu_quat(i), oracle_quat(i), TOL["f32"], KEYS, "quat 64k steps")
+
+
+def test_quat_workspace_reused_across_sizes():
+    big = inputs.make_quat_inputs(inputs.QuatWorkload("a", 2, 700, 3, 24, seed=31))
+    small = inputs.make_quat_inputs(inputs.QuatWorkload("b", 1, 200, 2, 40, seed=32))
+    qb = big["q"].cuda()
+    ws_f = ssd.quat_workspace(qb, False)
+    ws_b = ssd.quat_workspace(qb, True)
+    for name, i in (("big", big), ("small", small), ("big again", big)):
+        say(f"quat workspace reuse: {name}")
+        compare(gpu_quat(i, ws_f, ws_b), oracle_quat(i), TOL["f32"], KEYS, f"reuse {name}")
+
+
+def test_quat_empty_sequence_and_batch():
+    q = torch.zeros((2, 0, 3, 4, 4), device="cuda")
+    init = torch.randn((2, 3, 4, 4), device="cuda")
+    cum = ssd.quat_scan(q, init)
+    d_q, d_init = ssd.quat_scan_bwd(q, init, q)
+    torch.cuda.synchronize()
+    assert cum.numel() == 0 and d_q.numel() == 0
+    assert torch.all(d_init == 0)
+    q0 = torch.zeros((0, 5, 3, 4, 4), device="cuda")
+    assert ssd.quat_scan(q0).numel() == 0
+    d_q0, d_i0 = ssd.quat_scan_bwd(q0, None, q0)
+    assert d_q0.numel() == 0 and d_i0.numel() == 0
+
+
+def test_quat_runs_agree_to_fp32_rounding():
+    # the look-back meets a timing-dependent set of records (fp64, each perturbed by
+    # at most 2^-36 by the tag bits), so two runs may round to neighbouring fp32
+    # values -- in d_q also through cum[t-1], which the reverse pass rounds to fp32
+    # and which scales |G|: every quaternion agrees to two fp32 ulps of its norm
+    w = inputs.QUAT_WORKLOADS["mamba3_quat_scan_fp32"]
+    i = inputs.make_quat_inputs(w)
+    a, b = gpu_quat(i), gpu_quat(i)
+    for k in KEYS:
+        x, y = a[k].astype(np.float64), b[k].astype(np.float64)
+        diff = np.abs(x - y).max(axis=-1)
+        bound = 2 * np.spacing(np.linalg.norm(x, axis=-1).astype(np.float32)).astype(np.float64)
+        say(f"  {k}: {int(np.count_nonzero(a[k] != b[k]))} of {x.size} elements differ between "
+            f"runs, max diff / (2 ulp of the quaternion's norm) = {float((diff / bound).max()):.2f}")
+        assert np.all(diff <= bound)
