@@ -441,6 +441,19 @@ def bench_moments(args):
     return res
 
 
+def copy_probe(mib: int) -> int:
+    """Copy a device buffer of `mib` MiB three times (a plain copy kernel of known size, to
+    calibrate HBM byte counters); returns the bytes copied per launch."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return 4 * n
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -490,7 +503,10 @@ def main():
         return
     if args.quat_only:
         torch.cuda.set_device(0)
-        print(json.dumps(bench_quat(args)), flush=True)
+        res = bench_quat(args)
+        if args.copy_probe_mib > 0:
+            res["copy_probe_bytes"] = copy_probe(args.copy_probe_mib)
+        print(json.dumps(res), flush=True)
         return
 
     w = inputs.WORKLOADS[args.workload]
@@ -582,13 +598,7 @@ def main():
     if not args.no_quat:
         out["quat_scan"] = bench_quat(args)
     if args.copy_probe_mib > 0:
-        n = args.copy_probe_mib * (1 << 20) // 4
-        src = torch.ones(n, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        out["copy_probe_bytes"] = 4 * n
+        out["copy_probe_bytes"] = copy_probe(args.copy_probe_mib)
     print(json.dumps(out), flush=True)
 
 

@@ -26,7 +26,8 @@
 //    preceding segments' records: an inclusive record ends the walk, an
 //    aggregate is folded in and the walk goes on.  One poll reads the status
 //    words of 64 neighbours (one per lane; a ballot finds the nearest inclusive
-//    record) and the records folded are loaded in batches, so the walk costs a
+//    record) and the records folded are loaded in batches of 4 (8 records per
+//    batch held 64 more registers and halved the occupancy), so the walk costs a
 //    few memory round trips, not one per neighbour;
 //  * a workgroup's chain (b, lane group) follows from its index; its segment is
 //    the ticket it draws from its chain's atomic counter when it starts, taken
@@ -86,25 +87,32 @@ __device__ __forceinline__ d4 qnan() {
 }
 
 // ------------------------------------------------------------ tagged records
-// Record r of lane `lane` in a pass's array: 4 words at ((r * 64 + lane) * 4).
+// Component c of record r of lane `lane` in a pass's array sits at word
+// (r * 4 + c) * 64 + lane: one store or load instruction of a wave covers 512
+// contiguous bytes (lane-interleaved records made every 8-byte write-through
+// store a partial-line write: 4x the record bytes in HBM writes).
+__device__ __forceinline__ int64_t word_of(int64_t r, int c, int lane) {
+    return (r * 4 + c) * kLanes + lane;
+}
+
 __device__ __forceinline__ void store_record(uint64_t* rec, int64_t r, int lane, d4 v,
                                              uint32_t tag) {
-    uint64_t* p = rec + (r * kLanes + lane) * 4;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const uint64_t w = (static_cast<uint64_t>(__double_as_longlong(v[c])) & ~kTagMask) | tag;
-        __hip_atomic_store(p + c, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(rec + word_of(r, c, lane), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 // Loads the record and reports whether every word carries `tag`.
 __device__ __forceinline__ bool load_record(const uint64_t* rec, int64_t r, int lane, uint32_t tag,
                                             d4& v) {
-    uint64_t* p = const_cast<uint64_t*>(rec) + (r * kLanes + lane) * 4;
+    uint64_t* p = const_cast<uint64_t*>(rec);
     bool ok = true;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const uint64_t w = __hip_atomic_load(p + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t w = __hip_atomic_load(p + word_of(r, c, lane), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
         ok = ok && (w & kTagMask) == tag;
         v[c] = __longlong_as_double(static_cast<long long>(w));
     }
@@ -236,13 +244,13 @@ __global__ __launch_bounds__(kThreads) void k_quat_fwd(const float* __restrict__
             set_status(rec.status + k, kAggregate, lane);
             d4 acc = qone();  // product of the aggregates walked over, latest first
             auto fold = [&](int j0, int n) {
-                for (int base = 0; base < n; base += 8) {
-                    d4 r[8];
+                for (int base = 0; base < n; base += 4) {
+                    d4 r[4];
                     bool ok = false;
                     for (int spin = 0; spin < kMaxSpins && !ok; ++spin) {
                         bool all = true;
 #pragma unroll
-                        for (int u = 0; u < 8; ++u)
+                        for (int u = 0; u < 4; ++u)
                             if (base + u < n)
                                 all = load_record(rec.agg, row0 + j0 - base - u, lane, tag, r[u]) && all;
                         ok = __all(all);
@@ -250,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void k_quat_fwd(const float* __restrict__
                     }
                     if (!ok) return false;
 #pragma unroll
-                    for (int u = 0; u < 8; ++u)
+                    for (int u = 0; u < 4; ++u)
                         if (base + u < n) acc = qmul(acc, r[u]);
                 }
                 return true;
@@ -390,9 +398,9 @@ __global__ __launch_bounds__(kThreads) void k_quat_bwd(const float* __restrict__
             if (init && act)
                 c0 = to_d(*reinterpret_cast<const f4*>(init + (static_cast<int64_t>(b) * W + col) * 4));
         } else {
-            const uint64_t* p = fwd_inc + ((k - 1) * kLanes + lane) * 4;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) c0[c] = __longlong_as_double(static_cast<long long>(p[c]));
+            for (int c = 0; c < 4; ++c)
+                c0[c] = __longlong_as_double(static_cast<long long>(fwd_inc[word_of(k - 1, c, lane)]));
         }
         s_C[lane] = c0;
     }
