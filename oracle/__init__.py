@@ -10,7 +10,8 @@ token-by-token recurrence ``h_t = exp(dt_t A) h_{t-1} + dt_t x_t (outer) B_t``,
 state moments of the burn-mamba ``state_moments.rs`` page and their gradient, and
 that page's participation ratio of the moments with its gradient, and the
 gamma-weighted same-step correction ``y_diag`` of the Mamba-3 SSD with its gradient,
-and the Mamba-3 quaternion cumulative-product scan with its gradient.
+and the Mamba-3 quaternion cumulative-product scan with its gradient; the
+decode step is the forward over one token from a cached state.
 This module only builds the shared library with gcc and marshals numpy arrays.
 
 Every function takes and returns float64 numpy arrays in the pages' layouts:
@@ -121,6 +122,19 @@ def ssd_fwd(x, dt, A, B, C, D, init=None):
                                 _ptr(D), _ptr(init), _ptr(y), _ptr(final))
     _check(rc, "ssd_fwd")
     return y, final
+
+
+def ssd_step(x, dt, A, B, C, D, state):
+    """One decode step of the recurrence from the cached state (the token-by-token
+    ``step`` loop the state_moments.rs page refers to): the forward over a single
+    token with ``init = state``.  x ``[b, h, p]``, dt ``[b, h]``, B/C ``[b, h, r]``,
+    state ``[b, h, p, r]``.  Returns ``(y [b, h, p], new_state [b, h, p, r])``."""
+    x, dt, B, C, state = map(_f64, (x, dt, B, C, state))
+    b, h, p = x.shape
+    r = B.shape[-1]
+    y, new_state = ssd_fwd(x.reshape(b, 1, 1, h, p), dt.reshape(b, h, 1, 1), A,
+                           B.reshape(b, 1, 1, h, r), C.reshape(b, 1, 1, h, r), D, state)
+    return y.reshape(b, h, p), new_state
 
 
 def ssd_bwd(dy, d_final, x, dt, A, B, C, D, init=None, seg: int = 256):
