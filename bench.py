@@ -344,6 +344,47 @@ def bench_quat(args):
     return res
 
 
+def step_bytes(w):
+    """Algorithmic HBM bytes of one decode step over the batch: the state read and written
+    (4 B each per element), x, B, C read and y written (io dtype), dt read (fp32)."""
+    e = 2 if w.io == "bf16" else 4
+    bh = w.batch * w.nheads
+    return bh * (8 * w.headdim * w.dstate + e * (2 * w.headdim + 2 * w.dstate) + 4)
+
+
+def bench_step(args):
+    """ssd_step (in place) on each decode workload: tokens/s = sequences per step."""
+    import torch
+    from mamba_ssd_chunked_amd import inputs, ssd
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, w in inputs.STEP_WORKLOADS.items():
+        d = {k: v.to(dev) for k, v in inputs.make_step_inputs(w).items()}
+        y = torch.empty_like(d["x"])
+
+        def step():
+            st = torch.cuda.current_stream()
+            rc = ssd.ssd_step(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["state"],
+                              d["state"], y, st)
+            if rc:
+                raise ssd.SsdError(rc, "ssd_step", ssd.ssd_last_error())
+
+        ms, _, kt = timed_regions(step, args, stream)
+        kernels = {}
+        nbytes = step_bytes(w)
+        for kname, (tot, cnt) in kt.items():
+            avg = tot / cnt
+            rate = nbytes / (avg / 1e3)
+            kernels[kname] = {"avg_us": round(avg * 1e3, 2), "bytes": nbytes,
+                              "gbps": round(rate / 1e9, 1), "hbm_frac": round(rate / PEAK_HBM, 4)}
+        res[name] = {"workload": w.describe(), "us_per_step": round(ms * 1e3, 2),
+                     "value": round(w.batch / (ms / 1e3), 1), "unit": "tokens/s",
+                     "step": "ssd_step (in place)", "kernels": kernels}
+        del d, y
+    return res
+
+
 def bench_moments(args):
     """ssd_state_moments (with y) + ssd_state_moments_bwd on the moments workload."""
     import torch
@@ -481,6 +522,10 @@ def main():
                     help="skip the quaternion-scan leg (Mamba-3 rotation workload)")
     ap.add_argument("--quat-only", action="store_true",
                     help="run only the quaternion-scan leg and print its JSON object")
+    ap.add_argument("--no-step", action="store_true",
+                    help="skip the decode-step leg")
+    ap.add_argument("--step-only", action="store_true",
+                    help="run only the decode-step leg and print its JSON object")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (a plain copy "
                          "kernel of known size, to calibrate HBM byte counters)")
@@ -500,6 +545,13 @@ def main():
     if args.diag_only:
         torch.cuda.set_device(0)
         print(json.dumps(bench_diag(args)), flush=True)
+        return
+    if args.step_only:
+        torch.cuda.set_device(0)
+        res = bench_step(args)
+        if args.copy_probe_mib > 0:
+            res["copy_probe_bytes"] = copy_probe(args.copy_probe_mib)
+        print(json.dumps(res), flush=True)
         return
     if args.quat_only:
         torch.cuda.set_device(0)
@@ -597,6 +649,8 @@ def main():
         out["y_diag"] = bench_diag(args)
     if not args.no_quat:
         out["quat_scan"] = bench_quat(args)
+    if not args.no_step:
+        out["decode_step"] = bench_step(args)
     if args.copy_probe_mib > 0:
         out["copy_probe_bytes"] = copy_probe(args.copy_probe_mib)
     print(json.dumps(out), flush=True)

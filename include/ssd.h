@@ -271,6 +271,28 @@ int ssd_quat_scan_bwd(int64_t batch, int64_t seq, int64_t nheads, int64_t nquat,
 int ssd_quat_workspace_size(int64_t batch, int64_t seq, int64_t nheads, int64_t nquat, int bwd,
                             size_t* bytes);
 
+/*
+ * Decode step: one token of the recurrence from a cached state (the
+ * token-by-token `step` loop the burn-mamba "modules/state_moments.rs" page
+ * refers to; the recurrence is the one the combined_backward.rs page chunks).
+ * Per (b, h):
+ *   new_state = exp(dt A) state + dt x (outer) B       [p, r]
+ *   y         = new_state C + D x                       [p]
+ * which is ssd_fwd over a single token with init = state (final = new_state).
+ *   x, y      [b, h, p]     io dtype (the [b, n, l, h, p] layout at n = l = 1)
+ *   dt        [b, h]        fp32
+ *   A, D      [h]           fp32
+ *   B, C      [b, h, r]     io dtype
+ *   state, new_state [b, h, p, r]  fp32; new_state may equal state (updated in
+ *             place), otherwise the two must not overlap (SSD_ERR_UNSUPPORTED)
+ * batch >= 0; headdim and dstate in {16, 32, 64, 128}.  B, C, state, new_state
+ * 16-byte aligned (B, C 8-byte for bf16).  No workspace.  Bitwise reproducible.
+ * Errors: SSD_ERR_NULL, SSD_ERR_SHAPE, SSD_ERR_UNSUPPORTED, SSD_ERR_DTYPE, SSD_ERR_HIP.
+ */
+int ssd_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, int io_dtype,
+             const void* x, const float* dt, const float* A, const void* B, const void* C,
+             const float* D, const float* state, float* new_state, void* y, void* stream);
+
 /* Message for the last nonzero status returned on this thread ("" if none). */
 const char* ssd_last_error(void);
 

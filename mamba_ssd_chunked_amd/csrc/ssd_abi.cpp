@@ -735,4 +735,39 @@ int ssd_quat_scan_bwd(int64_t batch, int64_t seq, int64_t nheads, int64_t nquat,
     return ok();
 }
 
+int ssd_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, int io_dtype,
+             const void* x, const float* dt, const float* A, const void* B, const void* C,
+             const float* D, const float* state, float* new_state, void* y, void* stream) {
+    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16)
+        return fail(SSD_ERR_DTYPE, "ssd_step: io_dtype must be SSD_F32 (0) or SSD_BF16 (1) (got %d)",
+                    io_dtype);
+    if (batch < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0)
+        return fail(SSD_ERR_SHAPE, "ssd_step: need batch >= 0 and nheads, headdim, dstate > 0 "
+                    "(got %lld, %lld, %lld, %lld)", (long long)batch, (long long)nheads,
+                    (long long)headdim, (long long)dstate);
+    if (!pow2_in(headdim, 16, 128) || !pow2_in(dstate, 16, 128))
+        return fail(SSD_ERR_UNSUPPORTED, "ssd_step: headdim and dstate must be 16, 32, 64 or 128 "
+                    "(got %lld, %lld)", (long long)headdim, (long long)dstate);
+    if (batch > (1 << 30) || nheads > (1 << 30) ||
+        (double)batch * nheads * headdim * dstate / 4.0 / 256.0 > 2.0e9)
+        return fail(SSD_ERR_UNSUPPORTED, "ssd_step: problem too large for one call (split the batch)");
+    if (batch == 0) return ok();
+    if (!x || !dt || !A || !B || !C || !D || !state || !new_state || !y)
+        return fail(SSD_ERR_NULL, "ssd_step: every pointer is required");
+    const size_t ia = io_dtype == SSD_BF16 ? 8 : 16;
+    if (int rc = check_align(B, "B", ia)) return rc;
+    if (int rc = check_align(C, "C", ia)) return rc;
+    if (int rc = check_align(state, "state", 16)) return rc;
+    if (int rc = check_align(new_state, "new_state", 16)) return rc;
+    const size_t sbytes = (size_t)batch * nheads * headdim * dstate * sizeof(float);
+    const char* a = reinterpret_cast<const char*>(state);
+    const char* b = reinterpret_cast<const char*>(new_state);
+    if (a != b && a < b + sbytes && b < a + sbytes)
+        return fail(SSD_ERR_UNSUPPORTED, "ssd_step: state and new_state overlap without being equal");
+    ssd::StepShape s{(int)batch, (int)nheads, (int)headdim, (int)dstate, io_dtype};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    SSD_HIP(ssd::launch_step(s, x, dt, A, B, C, D, state, new_state, y, st), "k_step");
+    return ok();
+}
+
 }  // extern "C"

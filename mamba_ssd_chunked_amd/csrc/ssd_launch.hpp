@@ -211,4 +211,17 @@ hipError_t launch_quat_bwd(const QuatShape& s, const float* q, const float* init
 // n floats of p set to 0.
 hipError_t launch_quat_zero(float* p, int64_t n, hipStream_t st);
 
+// ------------------------------------------------- decode step
+struct StepShape {
+    int B, H, P, R;  // batch, heads, headdim, dstate (16..128)
+    int io;          // 0 = fp32, 1 = bf16
+};
+
+// One token from the cached state: new_state = exp(dt A) state + dt x (outer) B,
+// y = new_state C + D x.  x/y [B,H,P], dt [B,H], B/C [B,H,R], state [B,H,P,R]
+// (state may equal new_state).
+hipError_t launch_step(const StepShape& s, const void* x, const float* dt, const float* A,
+                       const void* B, const void* C, const float* D, const float* state,
+                       float* new_state, void* y, hipStream_t st);
+
 }  // namespace ssd

@@ -31,6 +31,12 @@ g ~ N(0, 1) ``[b, s, h, j, 4]``, z ~ N(0, 1) ``[b, s, h, j]``, g0 ~ N(0, 1)
 are q = g / |g| (uniform on the unit 3-sphere: Haar-random rotations, the
 largest per-step rotations a rotation can produce), times exp(norm_std * z)
 when norm_std > 0 (non-unit steps); init = g0 / |g0| or None (the identity).
+
+The decode step (``StepWorkload``) draws, in this order, x ~ N(0, 1) ``[b, h, p]``,
+B and C ~ N(0, 1) / sqrt(dstate) ``[b, h, r]``, z ~ N(0, 1) ``[b, h]`` (dt =
+softplus(z - 2)), u ~ U(0, 1) ``[h]`` (A = -exp(u ln 16)), D ~ N(0, 1) ``[h]`` and
+the cached state = state_std * N(0, 1) ``[b, h, p, r]``; bf16 workloads round x,
+B and C to bfloat16.
 """
 from __future__ import annotations
 
@@ -218,3 +224,52 @@ def make_quat_inputs(w: QuatWorkload) -> dict:
         q = q * torch.exp(w.norm_std * z)[..., None]
     init = raw0 / raw0.norm(dim=-1, keepdim=True) if w.random_init else None
     return dict(q=q.contiguous(), init=init, d_cum=d_cum)
+
+
+@dataclasses.dataclass(frozen=True)
+class StepWorkload:
+    """Shapes of the decode step: one token for each of `batch` sequences."""
+    name: str
+    batch: int
+    nheads: int
+    headdim: int
+    dstate: int
+    io: str = "f32"
+    state_std: float = 0.5
+    seed: int = 1010
+
+    def describe(self) -> dict:
+        return dict(workload=self.name, batch=self.batch, nheads=self.nheads, headdim=self.headdim,
+                    dstate=self.dstate, io_dtype=self.io)
+
+
+# Decode batches of 128 (130M shapes, fp32) and 64 (2.7B shapes, bf16 x/B/C/y) sequences.
+STEP_WORKLOADS = {
+    "mamba2_130m_decode_fp32": StepWorkload("mamba2_130m_decode_fp32", 128, 24, 64, 128, seed=1010),
+    "mamba2_2p7b_decode_bf16": StepWorkload("mamba2_2p7b_decode_bf16", 64, 80, 64, 128, io="bf16",
+                                            seed=1011),
+}
+
+
+def make_step_inputs(w: StepWorkload) -> dict:
+    """Draw x, B, C, dt, A, D and the cached state for one decode step (see module docstring)."""
+    g = torch.Generator().manual_seed(w.seed)
+    b, h, p, r = w.batch, w.nheads, w.headdim, w.dstate
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, dtype=torch.float32)
+
+    x = randn(b, h, p)
+    B = randn(b, h, r) / math.sqrt(r)
+    C = randn(b, h, r) / math.sqrt(r)
+    z = randn(b, h)
+    u = torch.rand(h, generator=g, dtype=torch.float32)
+    D = randn(h)
+    state = randn(b, h, p, r) * w.state_std
+    dt = torch.nn.functional.softplus(z - 2.0)
+    A = -torch.exp(u * math.log(16.0))
+    if w.io == "bf16":
+        x, B, C = (t.to(torch.bfloat16) for t in (x, B, C))
+    elif w.io != "f32":
+        raise ValueError(f"unknown io dtype {w.io!r}")
+    return dict(x=x, dt=dt, A=A, B=B, C=C, D=D, state=state)

@@ -31,7 +31,7 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPP
 EXPORTS = ("ssd_workspace_size", "ssd_fwd", "ssd_bwd", "ssd_state_moments",
            "ssd_state_moments_bwd", "ssd_moments_pr", "ssd_moments_pr_bwd", "ssd_y_diag",
            "ssd_y_diag_bwd", "ssd_quat_scan", "ssd_quat_scan_bwd", "ssd_quat_workspace_size",
-           "ssd_last_error", "ssd_timing_enable", "ssd_timing_collect")
+           "ssd_step", "ssd_last_error", "ssd_timing_enable", "ssd_timing_collect")
 
 
 class ssd_dims(ctypes.Structure):
@@ -79,9 +79,10 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_quat_scan.argtypes = [I64] * 4 + [P] * 4 + [ctypes.c_size_t, P]
     lib.ssd_quat_scan_bwd.argtypes = [I64] * 4 + [P] * 6 + [ctypes.c_size_t, P]
     lib.ssd_quat_workspace_size.argtypes = [I64] * 4 + [ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ssd_step.argtypes = [I64] * 4 + [ctypes.c_int] + [P] * 10
     for f in ("ssd_workspace_size", "ssd_fwd", "ssd_bwd", "ssd_state_moments",
               "ssd_state_moments_bwd", "ssd_moments_pr", "ssd_moments_pr_bwd", "ssd_y_diag",
-              "ssd_y_diag_bwd", "ssd_quat_scan", "ssd_quat_scan_bwd", "ssd_quat_workspace_size"):
+              "ssd_y_diag_bwd", "ssd_quat_scan", "ssd_quat_scan_bwd", "ssd_quat_workspace_size", "ssd_step"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ssd_last_error.argtypes = []
     lib.ssd_last_error.restype = ctypes.c_char_p
@@ -338,6 +339,25 @@ def ssd_quat_scan_bwd(q, init, d_cum, d_q, d_init, ws, stream=None) -> int:
     return load_library().ssd_quat_scan_bwd(b, s, h, j, *args, w, nbytes, _stream(stream))
 
 
+def ssd_step(x, dt, A, B, C, D, state, new_state, y, stream=None) -> int:
+    """x ``[b, h, p]``, dt ``[b, h]``, B/C ``[b, h, r]``, state/new_state ``[b, h, p, r]``
+    (new_state may be state itself), y like x."""
+    if x.dim() != 3 or B.dim() != 3 or B.shape[:2] != x.shape[:2]:
+        raise ValueError("x must be [b, h, p] and B [b, h, r]")
+    b, h, p = x.shape
+    r = B.shape[-1]
+    io = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}.get(x.dtype)
+    if io is None:
+        raise TypeError(f"x must be float32 or bfloat16 (got {x.dtype})")
+    dt_, f = x.dtype, torch.float32
+    args = [_ptr(x, "x", dt_, b * h * p, True), _ptr(dt, "dt", f, b * h, True),
+            _ptr(A, "A", f, h, True), _ptr(B, "B", dt_, b * h * r, True),
+            _ptr(C, "C", dt_, b * h * r, True), _ptr(D, "D", f, h, True),
+            _ptr(state, "state", f, b * h * p * r, True),
+            _ptr(new_state, "new_state", f, b * h * p * r, True), _ptr(y, "y", dt_, b * h * p, True)]
+    return load_library().ssd_step(b, h, p, r, io, *args, _stream(stream))
+
+
 # ------------------------------------------------------------ allocating helpers
 def _check(rc: int, where: str):
     if rc != 0:
@@ -484,3 +504,12 @@ def quat_scan_bwd(q, init, d_cum, want_d_init=True, ws=None, stream=None):
     ws = quat_workspace(q, True) if ws is None else ws
     _check(ssd_quat_scan_bwd(q, init, d_cum, d_q, d_init, ws, stream), "ssd_quat_scan_bwd")
     return d_q, d_init
+
+
+def step(x, dt, A, B, C, D, state, in_place=False, stream=None):
+    """One decode step: returns ``(y, new_state)``; with ``in_place`` the state tensor is
+    updated and returned as new_state."""
+    y = torch.empty_like(x)
+    new_state = state if in_place else torch.empty_like(state)
+    _check(ssd_step(x, dt, A, B, C, D, state, new_state, y, stream), "ssd_step")
+    return y, new_state

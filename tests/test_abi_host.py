@@ -238,3 +238,25 @@ def test_quat_of_nothing_is_a_no_op(lib):
     assert lib.ssd_quat_scan_bwd(0, 10, 2, 2, None, None, None, None, None, None, 0, None) == 0
     # an empty sequence with no d_init requested enqueues nothing
     assert lib.ssd_quat_scan_bwd(3, 0, 2, 2, None, None, None, None, None, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(b=-1), 2), (dict(h=0), 2), (dict(p=0), 2), (dict(p=48), 3), (dict(r=8), 3), (dict(r=256), 3),
+    (dict(io=2), 4), (dict(x=0), 1), (dict(state=0), 1), (dict(y=0), 1), (dict(B=FAKE + 4), 3),
+    (dict(state=FAKE + 8), 3), (dict(io=1, B=FAKE + 4), 3),
+    # new_state overlapping state without being it
+    (dict(new=FAKE + 4096), 3),
+])
+def test_step_rejects_bad_arguments(lib, case, code):
+    a = dict(b=2, h=3, p=32, r=64, io=0, x=FAKE, B=FAKE, state=FAKE + (1 << 24), new=None, y=FAKE)
+    a.update(case)
+    new = a["new"] if a["new"] is not None else a["state"]
+    if "new" in case:
+        a["state"] = FAKE
+    rc = lib.ssd_step(a["b"], a["h"], a["p"], a["r"], a["io"], a["x"], FAKE, FAKE, a["B"], FAKE,
+                      FAKE, a["state"], new, a["y"], None)
+    assert rc == code, ssd.ssd_last_error()
+
+
+def test_step_of_an_empty_batch_is_a_no_op(lib):
+    assert lib.ssd_step(0, 3, 64, 128, 0, *([None] * 10)) == 0

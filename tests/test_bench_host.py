@@ -70,3 +70,10 @@ def test_quat_bytes_count_every_tensor_once():
     assert bench.quat_bytes(w, "k_quat_bwd") == 48 * n + 32 * lanes
     assert bench.quat_bytes(w, "k_quat_carry") == 16 * n + 16 * lanes
     assert bench.quat_bytes(w, "k_fill_u32") is None
+
+
+def test_step_bytes_count_every_tensor_once():
+    w = inputs.STEP_WORKLOADS["mamba2_2p7b_decode_bf16"]
+    bh = 64 * 80
+    # state read + written in fp32; x, y (p each) and B, C (r each) in bf16; dt fp32
+    assert bench.step_bytes(w) == bh * (8 * 64 * 128 + 2 * (2 * 64 + 2 * 128) + 4)
