@@ -9,13 +9,16 @@
 //   S' = exp(dt A) S + dt x (outer) B,    y = S' C + D x.
 //
 // Two flops per state element against 8 bytes of state traffic (read + write):
-// bound by HBM, no matrix cores.  The state of every slice is one stream of
-// float4s; thread f takes float4 f, so a wave reads 1 KB of contiguous state,
-// and a state row (r / 4 float4s) is held by r / 4 consecutive lanes of one wave,
-// which reduce their partial dot products with C by butterflies; the row's first
-// lane writes y.  The decay exponent is formed in fp64 and raised once in fp32;
-// the state stays fp32, x, B, C, y are the io dtype.  The state may be updated in
-// place: each element is read and written by the same thread.
+// bound by HBM, no matrix cores.  One workgroup per (b, h) slice: thread t owns
+// column group c4 = t % (r / 4) of the rows t / (r / 4) + k * (256 / (r / 4)), so
+// a wave reads contiguous state, a state row (r / 4 float4s) is held by r / 4
+// consecutive lanes of one wave, which reduce their partial dot products with C
+// by butterflies (the row's first lane writes y), and each thread loads its
+// slices of B and C once (reloading them per row cost 1.23x the algorithmic
+// HBM reads).  All of a thread's state loads are issued before the first use.
+// The decay exponent is formed in fp64 and raised once in fp32; the state stays
+// fp32, x, B, C, y are the io dtype.  The state may be updated in place: each
+// element is read and written by the same thread.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -29,8 +32,8 @@ __device__ __forceinline__ float dot4(v4f a, v4f b) {
 
 }  // namespace
 
-// R4 = dstate / 4: lanes per state row.
-template <class IO, int R4>
+// R4 = dstate / 4: lanes per state row; P = headdim.
+template <class IO, int R4, int P>
 __global__ __launch_bounds__(NT) void k_step(const typename IO::T* __restrict__ x,
                                              const float* __restrict__ dt,
                                              const float* __restrict__ A,
@@ -38,49 +41,77 @@ __global__ __launch_bounds__(NT) void k_step(const typename IO::T* __restrict__ 
                                              const typename IO::T* __restrict__ Cm,
                                              const float* __restrict__ D, const float* state,
                                              float* new_state, typename IO::T* __restrict__ y,
-                                             int64_t total4, int H, int P) {
-    const int64_t f = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
-    if (f >= total4) return;  // whole rows leave together (total4 and NT are multiples of R4)
-    const int64_t row = f / R4;    // (b, h, p)
-    const int c4 = static_cast<int>(f % R4);
-    const int64_t slice = row / P;  // (b, h)
-    const int pp = static_cast<int>(row % P);
+                                             int H) {
+    constexpr int ROWS = NT / R4;                         // rows per pass of the workgroup
+    constexpr int K = P > ROWS ? P / ROWS : 1;            // passes
+    const int64_t slice = blockIdx.x;                     // (b, h)
+    const int c4 = threadIdx.x % R4;
+    const int r0 = threadIdx.x / R4;
     const int h = static_cast<int>(slice % H);
     const float dtv = dt[slice];
     const float a = exp2_of(static_cast<double>(dtv) * static_cast<double>(A[h]) * kLog2e);
-    const float xv = io<IO>::ld(x, slice * P + pp);
+    const float dh = D[h];
     const v4f bv = io<IO>::ld4(Bm, slice * (4 * R4) + 4 * c4);
     const v4f cv = io<IO>::ld4(Cm, slice * (4 * R4) + 4 * c4);
-    v4f s = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(state) + f);
-    s = a * s + (dtv * xv) * bv;
-    __builtin_nontemporal_store(s, reinterpret_cast<v4f*>(new_state) + f);
-    float part = dot4(cv, s);
+    const v4f* src = reinterpret_cast<const v4f*>(state) + slice * P * R4;
+    v4f* dst = reinterpret_cast<v4f*>(new_state) + slice * P * R4;
+    v4f s[K];
+    float xv[K];
 #pragma unroll
-    for (int o = R4 / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
-    if (c4 == 0) io<IO>::st(y, slice * P + pp, part + D[h] * xv);
+    for (int k = 0; k < K; ++k) {
+        const int pp = r0 + k * ROWS;
+        if (pp < P) {
+            s[k] = __builtin_nontemporal_load(src + pp * R4 + c4);
+            xv[k] = io<IO>::ld(x, slice * P + pp);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int pp = r0 + k * ROWS;
+        if (pp < P) {  // whole rows are in or out together
+            const v4f n = a * s[k] + (dtv * xv[k]) * bv;
+            __builtin_nontemporal_store(n, dst + pp * R4 + c4);
+            float part = dot4(cv, n);
+#pragma unroll
+            for (int o = R4 / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+            if (c4 == 0) io<IO>::st(y, slice * P + pp, part + dh * xv[k]);
+        }
+    }
 }
 
 namespace {
+
+template <class IO, int R4>
+hipError_t step_r(const StepShape& s, const void* x, const float* dt, const float* A, const void* B,
+                  const void* C, const float* D, const float* state, float* new_state, void* y,
+                  hipStream_t st) {
+    using T = typename IO::T;
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(s.B) * s.H)), block(NT);
+    const T* xx = static_cast<const T*>(x);
+    const T* bb = static_cast<const T*>(B);
+    const T* cc = static_cast<const T*>(C);
+    T* yy = static_cast<T*>(y);
+    switch (s.P) {
+        case 16: k_step<IO, R4, 16><<<grid, block, 0, st>>>(xx, dt, A, bb, cc, D, state, new_state, yy, s.H); break;
+        case 32: k_step<IO, R4, 32><<<grid, block, 0, st>>>(xx, dt, A, bb, cc, D, state, new_state, yy, s.H); break;
+        case 64: k_step<IO, R4, 64><<<grid, block, 0, st>>>(xx, dt, A, bb, cc, D, state, new_state, yy, s.H); break;
+        case 128: k_step<IO, R4, 128><<<grid, block, 0, st>>>(xx, dt, A, bb, cc, D, state, new_state, yy, s.H); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 template <class IO>
 hipError_t step_io(const StepShape& s, const void* x, const float* dt, const float* A,
                    const void* B, const void* C, const float* D, const float* state,
                    float* new_state, void* y, hipStream_t st) {
-    using T = typename IO::T;
-    const int64_t total4 = static_cast<int64_t>(s.B) * s.H * s.P * (s.R / 4);
-    const dim3 grid(static_cast<unsigned>((total4 + NT - 1) / NT)), block(NT);
-    const T* xx = static_cast<const T*>(x);
-    const T* bb = static_cast<const T*>(B);
-    const T* cc = static_cast<const T*>(C);
-    T* yy = static_cast<T*>(y);
     switch (s.R) {
-        case 16: k_step<IO, 4><<<grid, block, 0, st>>>(xx, dt, A, bb, cc, D, state, new_state, yy, total4, s.H, s.P); break;
-        case 32: k_step<IO, 8><<<grid, block, 0, st>>>(xx, dt, A, bb, cc, D, state, new_state, yy, total4, s.H, s.P); break;
-        case 64: k_step<IO, 16><<<grid, block, 0, st>>>(xx, dt, A, bb, cc, D, state, new_state, yy, total4, s.H, s.P); break;
-        case 128: k_step<IO, 32><<<grid, block, 0, st>>>(xx, dt, A, bb, cc, D, state, new_state, yy, total4, s.H, s.P); break;
+        case 16: return step_r<IO, 4>(s, x, dt, A, B, C, D, state, new_state, y, st);
+        case 32: return step_r<IO, 8>(s, x, dt, A, B, C, D, state, new_state, y, st);
+        case 64: return step_r<IO, 16>(s, x, dt, A, B, C, D, state, new_state, y, st);
+        case 128: return step_r<IO, 32>(s, x, dt, A, B, C, D, state, new_state, y, st);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace

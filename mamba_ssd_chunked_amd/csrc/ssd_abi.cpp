@@ -748,8 +748,7 @@ int ssd_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, int
     if (!pow2_in(headdim, 16, 128) || !pow2_in(dstate, 16, 128))
         return fail(SSD_ERR_UNSUPPORTED, "ssd_step: headdim and dstate must be 16, 32, 64 or 128 "
                     "(got %lld, %lld)", (long long)headdim, (long long)dstate);
-    if (batch > (1 << 30) || nheads > (1 << 30) ||
-        (double)batch * nheads * headdim * dstate / 4.0 / 256.0 > 2.0e9)
+    if (batch > (1 << 30) || nheads > (1 << 30) || (double)batch * nheads > 2.0e9)
         return fail(SSD_ERR_UNSUPPORTED, "ssd_step: problem too large for one call (split the batch)");
     if (batch == 0) return ok();
     if (!x || !dt || !A || !B || !C || !D || !state || !new_state || !y)
