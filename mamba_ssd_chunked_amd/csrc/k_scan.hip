@@ -62,12 +62,67 @@ hipError_t launch_k1_cumsum(const Shape& s, const float* dt, double* cdt, hipStr
 
 // ---------------------------------------------------------------------- K4
 // One thread per (b, h, 4 consecutive state elements); a serial loop over the
-// chunks.  The load of chunk i+1 is issued before the store of chunk i so the
-// memory pipe stays ahead of the FMA chain.
+// chunks.
 __device__ __forceinline__ float chunk_decay(const double* cdt_bh, double a, int i, int L) {
     return static_cast<float>(exp(a * cdt_bh[static_cast<int64_t>(i) * L + (L - 1)]));
 }
 
+// The serial carry s <- dec_i s + in_i over the chunks of one (b, h, 4 state
+// elements), visited forward (i = 0 .. N-1) or in reverse; each chunk's input
+// at p0 + i * stride is overwritten in place by the carry entering it.  KF
+// chunks (input and chunk-end cumsum) are loaded ahead of the FMA chain -- with
+// one chunk ahead the long-sequence passes (512 chunks, 65536 threads) waited a
+// memory latency per chunk (2.7 TB/s; 8 ahead: 6.3 TB/s).  Every chunk's input
+// is loaded before its slot is overwritten.
+template <int KF>
+__device__ __forceinline__ v4f carry_pass(float* p0, int64_t stride, int N, bool reverse,
+                                          const double* cdt_bh, double a, int L, v4f s) {
+    // visit order as a start and a signed step; the ring holds raw inputs (a decay
+    // computed at load time would wait for its load, and the in-order load counter
+    // would drain every load behind it), and the steady-state loop is straight-line
+    // code so that each use waits only for its own load
+    float* const q0 = reverse ? p0 + static_cast<int64_t>(N - 1) * stride : p0;
+    const int64_t qs = reverse ? -stride : stride;
+    const double* const c0 = cdt_bh + (reverse ? static_cast<int64_t>(N - 1) * L : 0) + (L - 1);
+    const int64_t cs = reverse ? -static_cast<int64_t>(L) : static_cast<int64_t>(L);
+    v4f buf[KF];
+    double cend[KF];
+#pragma unroll
+    for (int k = 0; k < KF; ++k)
+        if (k < N) {
+            buf[k] = *reinterpret_cast<const v4f*>(q0 + k * qs);
+            cend[k] = c0[k * cs];
+        }
+    int kk = 0;
+    for (; kk + 2 * KF <= N; kk += KF) {  // every step loads the chunk KF ahead
+#pragma unroll
+        for (int k = 0; k < KF; ++k) {
+            const v4f cur = buf[k];
+            const float d = static_cast<float>(exp(a * cend[k]));
+            buf[k] = *reinterpret_cast<const v4f*>(q0 + (kk + k + KF) * qs);
+            cend[k] = c0[(kk + k + KF) * cs];
+            *reinterpret_cast<v4f*>(q0 + (kk + k) * qs) = s;
+            s = d * s + cur;
+        }
+    }
+    for (; kk < N; kk += KF) {  // the last chunks
+#pragma unroll
+        for (int k = 0; k < KF; ++k)
+            if (kk + k < N) {
+                const v4f cur = buf[k];
+                const float d = static_cast<float>(exp(a * cend[k]));
+                if (kk + k + KF < N) {
+                    buf[k] = *reinterpret_cast<const v4f*>(q0 + (kk + k + KF) * qs);
+                    cend[k] = c0[(kk + k + KF) * cs];
+                }
+                *reinterpret_cast<v4f*>(q0 + (kk + k) * qs) = s;
+                s = d * s + cur;
+            }
+    }
+    return s;
+}
+
+template <int KF>
 __global__ __launch_bounds__(NT) void k4_state_pass(float* __restrict__ S,
                                                      const double* __restrict__ cdt,
                                                      const float* __restrict__ A,
@@ -85,19 +140,11 @@ __global__ __launch_bounds__(NT) void k4_state_pass(float* __restrict__ S,
     const double a = static_cast<double>(A[h]);
     const int64_t stride = static_cast<int64_t>(H) * PR;
     v4f s = init ? *reinterpret_cast<const v4f*>(init + bh * PR + e) : zero4();
-    float* p = S + (b * N * H + h) * PR + e;
-    v4f cur = N > 0 ? *reinterpret_cast<const v4f*>(p) : zero4();
-    for (int i = 0; i < N; ++i) {
-        const v4f nxt = (i + 1 < N) ? *reinterpret_cast<const v4f*>(p + stride) : zero4();
-        *reinterpret_cast<v4f*>(p) = s;
-        const float dec = chunk_decay(cdt_bh, a, i, L);
-        s = dec * s + cur;
-        cur = nxt;
-        p += stride;
-    }
+    s = carry_pass<KF>(S + (b * N * H + h) * PR + e, stride, N, false, cdt_bh, a, L, s);
     if (final_state) *reinterpret_cast<v4f*>(final_state + bh * PR + e) = s;
 }
 
+template <int KF>
 __global__ __launch_bounds__(NT) void k4_state_pass_bwd(
     float* __restrict__ S, float* __restrict__ dS, const double* __restrict__ cdt,
     const float* __restrict__ A, const float* __restrict__ init, const float* __restrict__ d_final,
@@ -114,32 +161,19 @@ __global__ __launch_bounds__(NT) void k4_state_pass_bwd(
     const int64_t stride = static_cast<int64_t>(H) * PR;
     // forward: chunk-entry states
     if (forward) {
-        v4f s = init ? *reinterpret_cast<const v4f*>(init + bh * PR + e) : zero4();
-        float* p = S + (b * N * H + h) * PR + e;
-        v4f cur = N > 0 ? *reinterpret_cast<const v4f*>(p) : zero4();
-        for (int i = 0; i < N; ++i) {
-            const v4f nxt = (i + 1 < N) ? *reinterpret_cast<const v4f*>(p + stride) : zero4();
-            *reinterpret_cast<v4f*>(p) = s;
-            s = chunk_decay(cdt_bh, a, i, L) * s + cur;
-            cur = nxt;
-            p += stride;
-        }
+        const v4f s0 = init ? *reinterpret_cast<const v4f*>(init + bh * PR + e) : zero4();
+        carry_pass<KF>(S + (b * N * H + h) * PR + e, stride, N, false, cdt_bh, a, L, s0);
     }
     // reverse: gradient of the state leaving each chunk
     v4f gacc = d_final ? *reinterpret_cast<const v4f*>(d_final + bh * PR + e) : zero4();
-    if (N > 0) {
-        float* p = dS + ((b * N + (N - 1)) * H + h) * PR + e;
-        v4f cur = *reinterpret_cast<const v4f*>(p);
-        for (int i = N - 1; i >= 0; --i) {
-            const v4f nxt = (i > 0) ? *reinterpret_cast<const v4f*>(p - stride) : zero4();
-            *reinterpret_cast<v4f*>(p) = gacc;
-            gacc = chunk_decay(cdt_bh, a, i, L) * gacc + cur;
-            cur = nxt;
-            p -= stride;
-        }
-    }
+    gacc = carry_pass<KF>(dS + (b * N * H + h) * PR + e, stride, N, true, cdt_bh, a, L, gacc);
     if (d_init) *reinterpret_cast<v4f*>(d_init + bh * PR + e) = gacc;
 }
+
+// Chunks loaded ahead by the carry passes: 8 for chains of 64 chunks or more
+// (the 64k-token workload: 512 serial steps, 65536 threads), else 4 (measured on
+// gfx950: as fast as 1 with 196608 threads, 1.4x faster with 49152).
+int k4_depth(const Shape& s) { return s.N >= 64 ? 8 : 4; }
 
 hipError_t launch_k4_pass(const Shape& s, float* S, const double* cdt, const float* A,
                           const float* init, float* final_state, hipStream_t st) {
@@ -147,8 +181,12 @@ hipError_t launch_k4_pass(const Shape& s, float* S, const double* cdt, const flo
     const int64_t total4 = static_cast<int64_t>(s.B) * s.H * (PR / 4);
     if (total4 == 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>((total4 + NT - 1) / NT));
-    hipLaunchKernelGGL(k4_state_pass, grid, dim3(NT), 0, st, S, cdt, A, init, final_state, s.N, s.H,
-                       s.L, PR, total4);
+    if (k4_depth(s) == 8)
+        hipLaunchKernelGGL(k4_state_pass<8>, grid, dim3(NT), 0, st, S, cdt, A, init, final_state,
+                           s.N, s.H, s.L, PR, total4);
+    else
+        hipLaunchKernelGGL(k4_state_pass<4>, grid, dim3(NT), 0, st, S, cdt, A, init,
+                           final_state, s.N, s.H, s.L, PR, total4);
     return hipGetLastError();
 }
 
@@ -159,8 +197,12 @@ hipError_t launch_k4_pass_bwd(const Shape& s, float* S, float* dS, const double*
     const int64_t total4 = static_cast<int64_t>(s.B) * s.H * (PR / 4);
     if (total4 == 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>((total4 + NT - 1) / NT));
-    hipLaunchKernelGGL(k4_state_pass_bwd, grid, dim3(NT), 0, st, S, dS, cdt, A, init, d_final,
-                       d_init, s.N, s.H, s.L, PR, total4, forward ? 1 : 0);
+    if (k4_depth(s) == 8)
+        hipLaunchKernelGGL(k4_state_pass_bwd<8>, grid, dim3(NT), 0, st, S, dS, cdt, A, init,
+                           d_final, d_init, s.N, s.H, s.L, PR, total4, forward ? 1 : 0);
+    else
+        hipLaunchKernelGGL(k4_state_pass_bwd<4>, grid, dim3(NT), 0, st, S, dS, cdt, A,
+                           init, d_final, d_init, s.N, s.H, s.L, PR, total4, forward ? 1 : 0);
     return hipGetLastError();
 }
 
