@@ -44,7 +44,10 @@
 //    a record once all four of its words carry the current tag, and retries
 //    otherwise, so the order in which a record and its status word become
 //    visible does not matter.  The tag perturbs a record by at most 2^-36 of its
-//    value.  The status words and tickets are zeroed before every call.
+//    value.  Before every call one small kernel zeroes the status words and
+//    tickets and advances the tag word kept in the workspace (never 0 in its low
+//    16 bits); the scan kernels read the tag from there, so a call replayed from
+//    a captured graph still gets a new tag.
 // Products and carries are fp64 (the fp32 inputs are exact in fp64), so the
 // result is within a few fp32 roundings of the exact scan at any length; cum
 // and d_q are rounded to fp32 once.  Which records a walk meets depends on
@@ -194,6 +197,18 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
         p[i] = v;
 }
 
+// Zero n status / ticket words and advance the call's tag (one thread).
+__global__ void k_quat_clear(uint32_t* __restrict__ p, int64_t n, uint32_t* __restrict__ tag) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        p[i] = 0u;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        uint32_t t = *tag + 1u;
+        if ((t & 0xffffu) == 0u) t += 1u;
+        *tag = t;
+    }
+}
+
 // Forward scan.  WRITE: store cum; otherwise only the segment records (the
 // backward's forward carries: inc[k] = cum at the end of segment k).
 template <int TS, bool WRITE>
@@ -201,8 +216,9 @@ __global__ __launch_bounds__(kThreads) void k_quat_fwd(const float* __restrict__
                                                         const float* __restrict__ init,
                                                         float* __restrict__ cum, QuatRecords rec,
                                                         int nb, int64_t S, int W, int G, int nseg,
-                                                        uint32_t tag) {
+                                                        const uint32_t* __restrict__ tag_word) {
     constexpr int SEG = kWaves * TS;
+    const uint32_t tag = *tag_word & 0xffffu;
     __shared__ uint32_t s_vid;
     __shared__ d4 s_part[kWaves][kLanes];
     __shared__ d4 s_carry[kLanes];
@@ -300,8 +316,10 @@ __global__ __launch_bounds__(kThreads) void k_quat_bwd(const float* __restrict__
                                                         float* __restrict__ d_init,
                                                         const uint64_t* __restrict__ fwd_inc,
                                                         QuatRecords rec, int nb, int64_t S, int W,
-                                                        int G, int nseg, uint32_t tag) {
+                                                        int G, int nseg,
+                                                        const uint32_t* __restrict__ tag_word) {
     constexpr int SEG = kWaves * TS;
+    const uint32_t tag = *tag_word & 0xffffu;
     __shared__ uint32_t s_vid;
     __shared__ d4 s_P[kWaves][kLanes], s_M[kWaves][kLanes], s_V[kWaves][kLanes];
     __shared__ d4 s_H[kLanes], s_C[kLanes];
@@ -442,6 +460,7 @@ QuatPlan quat_plan(const QuatShape& s, bool bwd) {
         off += (bytes + 255) & ~static_cast<size_t>(255);
         return at;
     };
+    p.tag = take(256);  // the call tag (kept across calls)
     // per pass: one ticket per chain (each in its own 256 bytes), then one status
     // word per workgroup
     const int64_t chains = static_cast<int64_t>(s.B) * s.G;
@@ -501,31 +520,38 @@ hipError_t fill_u32(uint32_t* p, int64_t n, hipStream_t st) {
 
 hipError_t launch_quat_clear(const QuatShape& s, bool bwd, void* ws, hipStream_t st) {
     const QuatPlan p = quat_plan(s, bwd);
-    return fill_u32(reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + p.flags), p.flag_words, st);
+    char* w = static_cast<char*>(ws);
+    const int64_t blocks = (p.flag_words + 255) / 256;
+    const unsigned grid = static_cast<unsigned>(blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks));
+    k_quat_clear<<<dim3(grid), dim3(256), 0, st>>>(reinterpret_cast<uint32_t*>(w + p.flags),
+                                                   p.flag_words, reinterpret_cast<uint32_t*>(w + p.tag));
+    return hipGetLastError();
 }
 
 hipError_t launch_quat_fwd(const QuatShape& s, const float* q, const float* init, float* cum,
-                           void* ws, uint32_t epoch, hipStream_t st) {
+                           void* ws, hipStream_t st) {
     const QuatPlan p = quat_plan(s, false);
     const int64_t blocks = static_cast<int64_t>(s.B) * s.G * s.nseg;
+    const uint32_t* tag = reinterpret_cast<const uint32_t*>(static_cast<char*>(ws) + p.tag);
     k_quat_fwd<kQuatTS, true><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
-        q, init, cum, records(s, p, ws, 0), s.B, s.S, s.W, s.G, s.nseg, epoch & 0xffffu);
+        q, init, cum, records(s, p, ws, 0), s.B, s.S, s.W, s.G, s.nseg, tag);
     return hipGetLastError();
 }
 
 hipError_t launch_quat_bwd(const QuatShape& s, const float* q, const float* init,
-                           const float* d_cum, float* d_q, float* d_init, void* ws,
-                           uint32_t epoch, hipStream_t st, int stage) {
+                           const float* d_cum, float* d_q, float* d_init, void* ws, hipStream_t st,
+                           int stage) {
     const QuatPlan p = quat_plan(s, true);
     const int64_t blocks = static_cast<int64_t>(s.B) * s.G * s.nseg;
     const QuatRecords r0 = records(s, p, ws, 0);
+    const uint32_t* tag = reinterpret_cast<const uint32_t*>(static_cast<char*>(ws) + p.tag);
     if (stage == 0) {
         k_quat_fwd<kQuatTS, false><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
-            q, init, nullptr, r0, s.B, s.S, s.W, s.G, s.nseg, epoch & 0xffffu);
+            q, init, nullptr, r0, s.B, s.S, s.W, s.G, s.nseg, tag);
     } else {
         k_quat_bwd<kQuatTS><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
             q, init, d_cum, d_q, d_init, r0.inc, records(s, p, ws, 1), s.B, s.S, s.W, s.G, s.nseg,
-            epoch & 0xffffu);
+            tag);
     }
     return hipGetLastError();
 }

@@ -6,7 +6,6 @@
 // synchronising.  The workspace is caller-owned; the library allocates nothing.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -305,17 +304,6 @@ int check_diag_ptrs(const ssd::DiagShape& d,
     for (auto& p : io)
         if (int rc = check_align(p.first, p.second, ia)) return rc;
     return SSD_OK;
-}
-
-// Tag of one quaternion-scan call: its look-back records carry the low 16 bits,
-// which must differ from the previous call's on the same workspace and never be
-// 0 (the value of zeroed memory).
-uint32_t next_quat_tag() {
-    static std::atomic<uint32_t> counter{0};
-    for (;;) {
-        const uint32_t e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
-        if ((e & 0xffffu) != 0) return e;
-    }
 }
 
 // Shared checks of the quaternion-scan entry points; fills *s.
@@ -699,9 +687,8 @@ int ssd_quat_scan(int64_t batch, int64_t seq, int64_t nheads, int64_t nquat, con
     if (int rc = check_align(ws, "workspace", 256)) return rc;
     if (!work) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const uint32_t tag = next_quat_tag();
-    SSD_HIP(ssd::launch_quat_clear(s, false, ws, st), "k_fill_u32");
-    SSD_HIP(ssd::launch_quat_fwd(s, q, init, cum, ws, tag, st), "k_quat_fwd");
+    SSD_HIP(ssd::launch_quat_clear(s, false, ws, st), "k_quat_clear");
+    SSD_HIP(ssd::launch_quat_fwd(s, q, init, cum, ws, st), "k_quat_fwd");
     return ok();
 }
 
@@ -728,10 +715,9 @@ int ssd_quat_scan_bwd(int64_t batch, int64_t seq, int64_t nheads, int64_t nquat,
             SSD_HIP(ssd::launch_quat_zero(d_init, batch * nheads * nquat * 4, st), "k_fill_u32");
         return ok();
     }
-    const uint32_t tag = next_quat_tag();
-    SSD_HIP(ssd::launch_quat_clear(s, true, ws, st), "k_fill_u32");
-    SSD_HIP(ssd::launch_quat_bwd(s, q, init, d_cum, d_q, d_init, ws, tag, st, 0), "k_quat_carry");
-    SSD_HIP(ssd::launch_quat_bwd(s, q, init, d_cum, d_q, d_init, ws, tag, st, 1), "k_quat_bwd");
+    SSD_HIP(ssd::launch_quat_clear(s, true, ws, st), "k_quat_clear");
+    SSD_HIP(ssd::launch_quat_bwd(s, q, init, d_cum, d_q, d_init, ws, st, 0), "k_quat_carry");
+    SSD_HIP(ssd::launch_quat_bwd(s, q, init, d_cum, d_q, d_init, ws, st, 1), "k_quat_bwd");
     return ok();
 }
 

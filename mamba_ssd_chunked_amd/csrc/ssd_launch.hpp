@@ -188,26 +188,27 @@ struct QuatRecords {
     uint64_t* inc;   // inclusive value (forward: cum at the segment end; reverse: H at its start)
 };
 
-// Workspace layout (byte offsets, 256-byte aligned).  The status words of all
-// passes sit together at `flags` (flag_words 32-bit words) so one fill clears them.
+// Workspace layout (byte offsets, 256-byte aligned): the call tag word at `tag`
+// (kept across calls), then the status words of all passes together at `flags`
+// (flag_words 32-bit words) so one kernel clears them.
 struct QuatPlan {
-    size_t flags = 0, agg = 0, inc = 0, agg_b = 0, agg2_b = 0, inc_b = 0, total = 0;
+    size_t tag = 0, flags = 0, agg = 0, inc = 0, agg_b = 0, agg2_b = 0, inc_b = 0, total = 0;
     int64_t flag_words = 0, words_per_pass = 0;
 };
 
 QuatShape quat_shape(int64_t B, int64_t S, int64_t H, int64_t J);
 QuatPlan quat_plan(const QuatShape& s, bool bwd);
 
-// Zero the ticket and status words (must precede every forward / backward).
+// Zero the ticket and status words and advance the call tag (must precede every
+// forward / backward: the scan kernels read the tag from the workspace).
 hipError_t launch_quat_clear(const QuatShape& s, bool bwd, void* ws, hipStream_t st);
 // cum [B,S,H,J,4] = scan of q (init [B,H,J,4], NULL = identity).
-// `epoch` tags the records of this call (nonzero low 16 bits; a new value per call).
 hipError_t launch_quat_fwd(const QuatShape& s, const float* q, const float* init, float* cum,
-                           void* ws, uint32_t epoch, hipStream_t st);
+                           void* ws, hipStream_t st);
 // stage 0: forward-carry records; stage 1: reverse pass writing d_q (and d_init).
 hipError_t launch_quat_bwd(const QuatShape& s, const float* q, const float* init,
-                           const float* d_cum, float* d_q, float* d_init, void* ws,
-                           uint32_t epoch, hipStream_t st, int stage);
+                           const float* d_cum, float* d_q, float* d_init, void* ws, hipStream_t st,
+                           int stage);
 // n floats of p set to 0.
 hipError_t launch_quat_zero(float* p, int64_t n, hipStream_t st);
 

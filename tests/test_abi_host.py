@@ -223,10 +223,11 @@ def test_quat_workspace_plan(lib):
     words = 64 * chains + -(-blocks // 64) * 64
     fwd = ssd.ssd_quat_workspace_size(b, s, h, j, False)
     bwd = ssd.ssd_quat_workspace_size(b, s, h, j, True)
-    assert fwd == 4 * words + 2 * blocks * 64 * 32
-    assert bwd == 8 * words + 5 * blocks * 64 * 32
+    # (plus 256 bytes for the call tag kept across calls)
+    assert fwd == 256 + 4 * words + 2 * blocks * 64 * 32
+    assert bwd == 256 + 8 * words + 5 * blocks * 64 * 32
     # ragged: 15 lanes still take a whole group, 97 steps two segments
-    assert ssd.ssd_quat_workspace_size(2, 97, 3, 5, False) == 4 * (2 * 64 + 64) + 2 * (2 * 2 * 64 * 32)
+    assert ssd.ssd_quat_workspace_size(2, 97, 3, 5, False) == 256 + 4 * (2 * 64 + 64) + 2 * (2 * 2 * 64 * 32)
     for args in ((0, 10, 2, 2), (3, 0, 2, 2)):
         assert ssd.ssd_quat_workspace_size(*args, False) == 0
         assert ssd.ssd_quat_workspace_size(*args, True) == 0

@@ -69,7 +69,7 @@ def test_quat_bytes_count_every_tensor_once():
     assert bench.quat_bytes(w, "k_quat_fwd") == 32 * n + 16 * lanes
     assert bench.quat_bytes(w, "k_quat_bwd") == 48 * n + 32 * lanes
     assert bench.quat_bytes(w, "k_quat_carry") == 16 * n + 16 * lanes
-    assert bench.quat_bytes(w, "k_fill_u32") is None
+    assert bench.quat_bytes(w, "k_quat_clear") is None
 
 
 def test_step_bytes_count_every_tensor_once():

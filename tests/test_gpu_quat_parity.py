@@ -141,3 +141,42 @@ def test_quat_runs_agree_to_fp32_rounding():
         say(f"  {k}: {int(np.count_nonzero(a[k] != b[k]))} of {x.size} elements differ between "
             f"runs, max diff / (2 ulp of the quaternion's norm) = {float((diff / bound).max()):.2f}")
         assert np.all(diff <= bound)
+
+
+def test_quat_graph_replay_matches_eager():
+    # every call advances the tag kept in the workspace from a kernel of its own, so
+    # a call replayed from a captured graph uses a fresh tag; each replay (with eager
+    # calls on the same workspaces in between) must match the eager result and the oracle
+    w = inputs.QuatWorkload("graph", 2, 1500, 3, 24, norm_std=0.05, seed=58)
+    i = inputs.make_quat_inputs(w)
+    say("case graph capture of ssd_quat_scan + ssd_quat_scan_bwd")
+    q, init, dc = i["q"].cuda(), i["init"].cuda(), i["d_cum"].cuda()
+    cum, d_q = torch.empty_like(q), torch.empty_like(q)
+    d_init = torch.empty_like(init)
+    ws_f, ws_b = ssd.quat_workspace(q, False), ssd.quat_workspace(q, True)
+
+    def step():
+        st = torch.cuda.current_stream()
+        assert ssd.ssd_quat_scan(q, init, cum, ws_f, st) == 0
+        assert ssd.ssd_quat_scan_bwd(q, init, dc, d_q, d_init, ws_b, st) == 0
+
+    step()
+    torch.cuda.synchronize()
+    ref = {k: t.clone().cpu().numpy() for k, t in dict(cum=cum, d_q=d_q, d_init=d_init).items()}
+    compare(ref, oracle_quat(i), TOL["f32"], KEYS, "eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for it in range(3):
+        for t in (cum, d_q, d_init):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = dict(cum=cum.cpu().numpy(), d_q=d_q.cpu().numpy(), d_init=d_init.cpu().numpy())
+        for k in KEYS:
+            diff = np.abs(got[k].astype(np.float64) - ref[k]).max(axis=-1)
+            bound = 2 * np.spacing(np.linalg.norm(ref[k], axis=-1).astype(np.float32)).astype(np.float64)
+            assert np.all(diff <= bound), f"replay {it}: {k}"
+        step()  # eager calls on the same workspaces between replays
+        torch.cuda.synchronize()
