@@ -171,14 +171,12 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target(
 #pragma unroll
             for (int kk = 0; kk < R / 16; ++kk) {
                 const v4f u = *reinterpret_cast<const v4f*>(sBS + (16 * j + i) * RS + 16 * kk + 4 * g);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) cbt = mfma16(u[v], creg[kk][v], cbt);
+                cbt = mfma_k16<IO>(u, creg[kk], cbt);
             }
 #pragma unroll
             for (int kk = 0; kk < P / 16; ++kk) {
                 const v4f u = *reinterpret_cast<const v4f*>(sX + (16 * j + i) * PS + 16 * kk + 4 * g);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) dwt = mfma16(u[v], dyreg[kk][v], dwt);
+                dwt = mfma_k16<IO>(u, dyreg[kk], dwt);
             }
             // this lane's four source rows: cumsums and dt as 16-byte LDS reads
             const v2d cs01 = *reinterpret_cast<const v2d*>(sCdtS + 16 * j + 4 * g);
@@ -326,14 +324,12 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
 #pragma unroll
             for (int kk = 0; kk < R / 16; ++kk) {
                 const v4f u = *reinterpret_cast<const v4f*>(sCT + (16 * j + i) * RS + 16 * kk + 4 * g);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) cb = mfma16(u[v], breg[kk][v], cb);
+                cb = mfma_k16<IO>(u, breg[kk], cb);
             }
 #pragma unroll
             for (int kk = 0; kk < P / 16; ++kk) {
                 const v4f u = *reinterpret_cast<const v4f*>(sDY + (16 * j + i) * PS + 16 * kk + 4 * g);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) dw = mfma16(u[v], xreg[kk][v], dw);
+                dw = mfma_k16<IO>(u, xreg[kk], dw);
             }
             // this lane's four target rows: cumsums as two 16-byte LDS reads
             const v2d ct01 = *reinterpret_cast<const v2d*>(sCdtT + 16 * j + 4 * g);

@@ -198,8 +198,7 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan(
 #pragma unroll
             for (int kk = 0; kk < R / 16; ++kk) {
                 const v4f aop = *reinterpret_cast<const v4f*>(sBS + (16 * j + i) * RS + 16 * kk + 4 * g);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) cbt = mfma16(aop[v], creg[kk][v], cbt);
+                cbt = mfma_k16<IO>(aop, creg[kk], cbt);
             }
             // this lane's four source rows: cumsums and dt as 16-byte LDS reads
             const v2d cs01 = *reinterpret_cast<const v2d*>(sCumS + 16 * j + 4 * g);

@@ -136,9 +136,7 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
         for (int kk = 0; kk < R / 16; ++kk) {
             const v4f aop = *reinterpret_cast<const v4f*>(sB + (16 * u + i) * RS + 16 * kk + 4 * g);
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-#pragma unroll
-                for (int q = QLO; q < 2; ++q) cbt[q] = mfma16(aop[v], creg[q][kk][v], cbt[q]);
+            for (int q = QLO; q < 2; ++q) cbt[q] = mfma_k16<IO>(aop, creg[q][kk], cbt[q]);
         }
         const v2d cs01 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g);
         const v2d cs23 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g + 2);
@@ -314,14 +312,12 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
 #pragma unroll
         for (int kk = 0; kk < R / 16; ++kk) {
             const v4f w = *reinterpret_cast<const v4f*>(sB + (16 * u + i) * RS + 16 * kk + 4 * g);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) cbt = mfma16(w[v], creg[q][kk][v], cbt);
+            cbt = mfma_k16<IO>(w, creg[q][kk], cbt);
         }
 #pragma unroll
         for (int kk = 0; kk < P / 16; ++kk) {
             const v4f w = *reinterpret_cast<const v4f*>(sX + (16 * u + i) * PS + 16 * kk + 4 * g);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) dwt = mfma16(w[v], dyreg[q][kk][v], dwt);
+            dwt = mfma_k16<IO>(w, dyreg[q][kk], dwt);
         }
         const v2d cs01 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g);
         const v2d cs23 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g + 2);

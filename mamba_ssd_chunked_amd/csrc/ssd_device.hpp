@@ -39,6 +39,35 @@ __device__ __forceinline__ float exp2_of(double e2) {
 }
 
 // ------------------------------------------------------------------ io types
+struct F32;
+struct BF16;
+typedef short s4 __attribute__((ext_vector_type(4)));
+
+// fp32 values exact in bf16 (widened bf16 inputs) -> four packed bf16 (exact).
+__device__ __forceinline__ s4 pack_bf16x4(v4f a) {
+    return s4{static_cast<short>(__float_as_uint(a[0]) >> 16),
+              static_cast<short>(__float_as_uint(a[1]) >> 16),
+              static_cast<short>(__float_as_uint(a[2]) >> 16),
+              static_cast<short>(__float_as_uint(a[3]) >> 16)};
+}
+
+// One 16-wide k slice of a 16x16 product whose two operands are float4s of this
+// lane (k = 4g + v, v = 0..3, on both sides): four fp32 16x16x4 MFMAs -- or, for
+// a bf16 workload when both operands are (widened) bf16 inputs, one bf16
+// 16x16x16 MFMA, whose lane holds exactly those four k values of each operand
+// and whose result layout is the same: exact products, fp32 accumulation, a
+// sixteenth of the fp32 matrix-core time on gfx950.
+template <class IO>
+__device__ __forceinline__ v4f mfma_k16(v4f a, v4f b, v4f c) {
+    if constexpr (__is_same(IO, BF16)) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pack_bf16x4(a), pack_bf16x4(b), c, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) c = mfma16(a[v], b[v], c);
+        return c;
+    }
+}
+
 struct F32 {
     using T = float;
 };
