@@ -442,24 +442,42 @@ __global__ __launch_bounds__(NT) void km_reduce_sum(const float* __restrict__ U,
     const int64_t b = bh / H, h = bh - (bh / H) * H;
     const int RR = R * R;
     const int idx = blockIdx.y * NT + threadIdx.x;
-    if (idx < RR) {
-        double acc = 0.0;
-        for (int n = 0; n < N; ++n) {
-            const int64_t ch = (b * N + n) * H + h;
-            for (int k = 0; k < nblk; ++k) acc += static_cast<double>(U[(ch * nblk + k) * RR + idx]);
-            acc += static_cast<double>(W[ch * RR + idx]);
-        }
-        m2[bh * RR + idx] = static_cast<float>(acc);
-    } else if (idx < RR + R) {
-        const int r = idx - RR;
-        double acc = 0.0;
-        for (int n = 0; n < N; ++n) {
-            const int64_t ch = (b * N + n) * H + h;
-            for (int k = 0; k < nblk; ++k) acc += static_cast<double>(m1b[(ch * nblk + k) * R + r]);
-            acc += static_cast<double>(m1c[ch * R + r]);
-        }
-        m1[bh * R + r] = static_cast<float>(acc);
+    // the partials of CU chunks are loaded before they are added (in the fixed order
+    // chunk by chunk, blocks then the chunk term): one load in flight per thread made
+    // the sum latency-bound (2.4 TB/s); nblk <= 4
+    constexpr int CU = 4;
+    const bool is_m2 = idx < RR;
+    if (idx >= RR + R) return;
+    const int r = idx - RR;
+    const float* part = is_m2 ? U : m1b;
+    const float* term = is_m2 ? W : m1c;
+    const int width = is_m2 ? RR : R;
+    const int col = is_m2 ? idx : r;
+    double acc = 0.0;
+    for (int n0 = 0; n0 < N; n0 += CU) {
+        float v[CU][5];
+#pragma unroll
+        for (int u = 0; u < CU; ++u)
+            if (n0 + u < N) {
+                const int64_t ch = (b * N + n0 + u) * H + h;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (k < nblk) v[u][k] = part[(ch * nblk + k) * width + col];
+                v[u][4] = term[ch * width + col];
+            }
+#pragma unroll
+        for (int u = 0; u < CU; ++u)
+            if (n0 + u < N) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (k < nblk) acc += static_cast<double>(v[u][k]);
+                acc += static_cast<double>(v[u][4]);
+            }
     }
+    if (is_m2)
+        m2[bh * RR + idx] = static_cast<float>(acc);
+    else
+        m1[bh * R + r] = static_cast<float>(acc);
 }
 
 __global__ __launch_bounds__(NT) void km_symmetrise(float* __restrict__ m2, int R) {
