@@ -385,6 +385,102 @@ def bench_step(args):
     return res
 
 
+def bench_ssd(w, inp, args, layout=True, steps=None, warmup=None):
+    """ssd_fwd + ssd_bwd on workload w (inputs already drawn): step time, per-kernel rates and the
+    roofline of the dominant kernel; with `layout`, also the step at the layout's chunk length."""
+    import argparse as _ap
+    import torch
+    from mamba_ssd_chunked_amd import ssd
+    dev = torch.device("cuda", 0)
+    targs = _ap.Namespace(steps=steps or args.steps, warmup=warmup or args.warmup, graph=args.graph)
+    d = {k: v.to(dev) for k, v in inp.items() if isinstance(v, torch.Tensor) and k != "valid_len"}
+    init = d["init"] if w.init_std > 0 else None
+    y = torch.empty_like(d["x"])
+    final = torch.empty_like(d["d_final"])
+    gx, gB, gC = torch.empty_like(d["x"]), torch.empty_like(d["B"]), torch.empty_like(d["C"])
+    gdt, gA, gD = torch.empty_like(d["dt"]), torch.empty_like(d["A"]), torch.empty_like(d["D"])
+    ginit = torch.empty_like(d["d_final"])
+    stream = torch.cuda.current_stream()
+
+    def make_step(kcl):
+        dims = ssd.dims_of(d["x"], d["B"], kcl)
+        ws_f = ssd.workspace(dims, ssd.SSD_OP_FWD, dev)
+        ws_b = ssd.workspace(dims, ssd.SSD_OP_BWD, dev)
+
+        def step():
+            st = torch.cuda.current_stream()
+            rc = ssd.ssd_fwd(dims, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], init, y,
+                             final, ws_f, st)
+            if rc:
+                raise ssd.SsdError(rc, "ssd_fwd", ssd.ssd_last_error())
+            rc = ssd.ssd_bwd(dims, d["dy"], None, d["x"], d["dt"], d["A"], d["B"], d["C"],
+                             d["D"], init, gx, gdt, gA, gB, gC, gD, ginit, ws_b, st)
+            if rc:
+                raise ssd.SsdError(rc, "ssd_bwd", ssd.ssd_last_error())
+        return step
+
+    k = kernel_chunk_len(w, args.kernel_chunk_len)
+    ms, ms_ev, kt = timed_regions(make_step(args.kernel_chunk_len), targs, stream)
+    tokens = w.batch * w.seq
+
+    kernels = {}
+    for name, (tot, cnt) in kt.items():
+        avg = tot / cnt
+        work, kind = kernel_work(w, name, k)
+        ent = {"avg_ms": round(avg, 5), "launches_per_step": cnt / targs.steps}
+        if name == "k_chunk_states":
+            # launched once in ssd_fwd (1 job) and once in ssd_bwd (2 jobs): average work
+            work = work * 1.5
+        if work is not None:
+            rate = work / (avg / 1e3)
+            if kind == "flop":
+                ent.update(tflops=round(rate / 1e12, 2), mfma_frac=round(rate / PEAK_FP32_MFMA, 4))
+            else:
+                ent.update(gbps=round(rate / 1e9, 1), hbm_frac=round(rate / PEAK_HBM, 4))
+        kernels[name] = ent
+    dom = max(kernels, key=lambda n: kernels[n]["avg_ms"] * kernels[n]["launches_per_step"])
+    work, kind = kernel_work(w, dom, k)
+    davg = kernels[dom]["avg_ms"]
+    if kind == "flop":
+        ach = work / (davg / 1e3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 3), "peak": 157.3,
+                "unit": "TFLOP/s", "frac": round(ach / 157.3, 4),
+                "traffic": measured_traffic(dom, w, k)}
+    else:
+        ach = work / (davg / 1e3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": 8000.0,
+                "unit": "GB/s", "frac": round(ach / 8000.0, 4),
+                "traffic": measured_traffic(dom, w, k)}
+    res = {"value": round(tokens / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+           "ms_per_step_with_kernel_events": round(ms_ev, 4), "kernel_chunk_len": k,
+           "roofline": roof, "method_tflops": round(method_flops(w, k) / (ms / 1e3) / 1e12, 3),
+           "kernels": kernels}
+    if layout and k != w.chunk_len:
+        # the same step with the kernels run at the layout's chunk length
+        ms_l, _, _ = timed_regions(make_step(w.chunk_len), targs, stream)
+        res["at_layout_chunk_len"] = {"kernel_chunk_len": w.chunk_len, "ms_per_step": round(ms_l, 4),
+                                      "value": round(tokens / (ms_l / 1e3), 1)}
+    del d, y, final, gx, gB, gC, gdt, gA, gD, ginit
+    return res
+
+
+def bench_other_workloads(args):
+    """The SSD step on the other full-size workloads (bf16 2.7B-shaped, 64k tokens), fewer steps."""
+    from mamba_ssd_chunked_amd import inputs
+    res = {}
+    for name in ("mamba2_2p7b_bf16", "long_context_64k_fp32"):
+        if name == args.workload:
+            continue
+        w = inputs.WORKLOADS[name]
+        r = bench_ssd(w, inputs.make_inputs(w), args, layout=False, steps=min(args.steps, 10),
+                      warmup=min(args.warmup, 5))
+        res[name] = {"workload": w.describe(), "kernel_chunk_len": r["kernel_chunk_len"],
+                     "ms_per_step": r["ms_per_step"], "value": r["value"], "unit": "tokens/s",
+                     "roofline": r["roofline"],
+                     "kernels": {k: v.get("mfma_frac", v.get("hbm_frac")) for k, v in r["kernels"].items()}}
+    return res
+
+
 def bench_moments(args):
     """ssd_state_moments (with y) + ssd_state_moments_bwd on the moments workload."""
     import torch
@@ -522,6 +618,8 @@ def main():
                     help="skip the quaternion-scan leg (Mamba-3 rotation workload)")
     ap.add_argument("--quat-only", action="store_true",
                     help="run only the quaternion-scan leg and print its JSON object")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the SSD step on the bf16 2.7B-shaped and 64k-token workloads")
     ap.add_argument("--no-step", action="store_true",
                     help="skip the decode-step leg")
     ap.add_argument("--step-only", action="store_true",
@@ -565,82 +663,21 @@ def main():
     inp = inputs.make_inputs(w)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    d = {k: v.to(dev) for k, v in inp.items() if isinstance(v, torch.Tensor) and k != "valid_len"}
-    init = d["init"] if w.init_std > 0 else None
-    y = torch.empty_like(d["x"])
-    final = torch.empty_like(d["d_final"])
-    gx, gB, gC = torch.empty_like(d["x"]), torch.empty_like(d["B"]), torch.empty_like(d["C"])
-    gdt, gA, gD = torch.empty_like(d["dt"]), torch.empty_like(d["A"]), torch.empty_like(d["D"])
-    ginit = torch.empty_like(d["d_final"])
-    stream = torch.cuda.current_stream()
-
-    def make_step(kcl):
-        dims = ssd.dims_of(d["x"], d["B"], kcl)
-        ws_f = ssd.workspace(dims, ssd.SSD_OP_FWD, dev)
-        ws_b = ssd.workspace(dims, ssd.SSD_OP_BWD, dev)
-
-        def step():
-            st = torch.cuda.current_stream()
-            rc = ssd.ssd_fwd(dims, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], init, y,
-                             final, ws_f, st)
-            if rc:
-                raise ssd.SsdError(rc, "ssd_fwd", ssd.ssd_last_error())
-            rc = ssd.ssd_bwd(dims, d["dy"], None, d["x"], d["dt"], d["A"], d["B"], d["C"],
-                             d["D"], init, gx, gdt, gA, gB, gC, gD, ginit, ws_b, st)
-            if rc:
-                raise ssd.SsdError(rc, "ssd_bwd", ssd.ssd_last_error())
-        return step
-
-    k = kernel_chunk_len(w, args.kernel_chunk_len)
-    ms, ms_ev, kt = timed_regions(make_step(args.kernel_chunk_len), args, stream)
-    tokens = w.batch * w.seq
-    value = tokens / (ms / 1e3)
-
-    kernels = {}
-    for name, (tot, cnt) in kt.items():
-        avg = tot / cnt
-        work, kind = kernel_work(w, name, k)
-        ent = {"avg_ms": round(avg, 5), "launches_per_step": cnt / args.steps}
-        if name == "k_chunk_states":
-            # launched once in ssd_fwd (1 job) and once in ssd_bwd (2 jobs): average work
-            work = work * 1.5
-        if work is not None:
-            rate = work / (avg / 1e3)
-            if kind == "flop":
-                ent.update(tflops=round(rate / 1e12, 2), mfma_frac=round(rate / PEAK_FP32_MFMA, 4))
-            else:
-                ent.update(gbps=round(rate / 1e9, 1), hbm_frac=round(rate / PEAK_HBM, 4))
-        kernels[name] = ent
-    dom = max(kernels, key=lambda n: kernels[n]["avg_ms"] * kernels[n]["launches_per_step"])
-    work, kind = kernel_work(w, dom, k)
-    davg = kernels[dom]["avg_ms"]
-    if kind == "flop":
-        ach = work / (davg / 1e3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 3), "peak": 157.3,
-                "unit": "TFLOP/s", "frac": round(ach / 157.3, 4),
-                "traffic": measured_traffic(dom, w, k)}
-    else:
-        ach = work / (davg / 1e3) / 1e9
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": 8000.0,
-                "unit": "GB/s", "frac": round(ach / 8000.0, 4),
-                "traffic": measured_traffic(dom, w, k)}
+    r = bench_ssd(w, inp, args, layout=not args.no_layout_chunk)
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "ms_per_step_with_kernel_events": round(ms_ev, 4),
+        "metric": METRIC, "value": r["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
+        "ms_per_step_with_kernel_events": r["ms_per_step_with_kernel_events"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "io_dtype": w.io,
         "data": "synthetic (seeded draws of the workload recipe; no dataset)",
-        "config": {**w.describe(), "kernel_chunk_len": k},
-        "roofline": roof,
-        "method_tflops": round(method_flops(w, k) / (ms / 1e3) / 1e12, 3),
-        "kernels": kernels,
+        "config": {**w.describe(), "kernel_chunk_len": r["kernel_chunk_len"]},
+        "roofline": r["roofline"],
+        "method_tflops": r["method_tflops"],
+        "kernels": r["kernels"],
     }
-    if k != w.chunk_len and not args.no_layout_chunk:
-        # the same step with the kernels run at the layout's chunk length
-        ms_l, _, _ = timed_regions(make_step(w.chunk_len), args, stream)
-        out["at_layout_chunk_len"] = {"kernel_chunk_len": w.chunk_len, "ms_per_step": round(ms_l, 4),
-                                      "value": round(tokens / (ms_l / 1e3), 1)}
+    if "at_layout_chunk_len" in r:
+        out["at_layout_chunk_len"] = r["at_layout_chunk_len"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp)
     if not args.no_moments:
@@ -651,6 +688,8 @@ def main():
         out["quat_scan"] = bench_quat(args)
     if not args.no_step:
         out["decode_step"] = bench_step(args)
+    if not args.no_other_workloads:
+        out["other_workloads"] = bench_other_workloads(args)
     if args.copy_probe_mib > 0:
         out["copy_probe_bytes"] = copy_probe(args.copy_probe_mib)
     print(json.dumps(out), flush=True)
