@@ -39,7 +39,7 @@ __global__ __launch_bounds__(NT) void k_chunk_states(
     constexpr int TS = TB + 4;  // token stride of the transposed tiles
     __shared__ float sU[P * TS];
     __shared__ float sV[R * TS];
-    __shared__ float sw[TB];
+    __shared__ float sw[256];  // token weights of the chunk (L <= 256)
     const int job = job0 + static_cast<int>(blockIdx.y);
     const ChunkHead c = decode_ch(blockIdx.x, N, H);
     const typename IO::T* U = job == 1 ? dy : x;
@@ -67,18 +67,25 @@ __global__ __launch_bounds__(NT) void k_chunk_states(
 #pragma unroll
         for (int k = 0; k < RPW; ++k) acc[q][k] = zero4();
 
+    // The chunk's token weights and block 0's rows first; then every block's
+    // matrix work runs while the next block's rows load into registers.
+    v4f tu[RowsT<IO, P>::IT], tv[RowsT<IO, R>::IT];
+    load_rows_t<IO, P>(tu, U + urow0, ustride);
+    load_rows_t<IO, R>(tv, V + vrow0, vstride);
+    for (int t = tid; t < L; t += NT)
+        sw[t] = job == 0   ? dtc[t] * expf(static_cast<float>(a * (end - cc[t])))
+                : job == 1 ? expf(static_cast<float>(a * cc[t]))
+                           : static_cast<float>(static_cast<double>(dtc[t]) * exp(a * cc[t]) *
+                                                phi[c.c_bhn * L + t]);
+    __syncthreads();
     for (int t0 = 0; t0 < L; t0 += TB) {
-        if (tid < TB) {
-            const int t = t0 + tid;
-            sw[tid] = job == 0   ? dtc[t] * expf(static_cast<float>(a * (end - cc[t])))
-                      : job == 1 ? expf(static_cast<float>(a * cc[t]))
-                                 : static_cast<float>(static_cast<double>(dtc[t]) * exp(a * cc[t]) *
-                                                      phi[c.c_bhn * L + t]);
+        store_rows_t<IO, P>(sU, tu, nullptr);
+        store_rows_t<IO, R>(sV, tv, sw + t0);
+        __syncthreads();
+        if (t0 + TB < L) {
+            load_rows_t<IO, P>(tu, U + urow0 + (t0 + TB) * ustride, ustride);
+            load_rows_t<IO, R>(tv, V + vrow0 + (t0 + TB) * vstride, vstride);
         }
-        __syncthreads();
-        stage_rows_t<IO, P>(sU, U + urow0 + t0 * ustride, ustride, nullptr);
-        stage_rows_t<IO, R>(sV, V + vrow0 + t0 * vstride, vstride, sw);
-        __syncthreads();
         if (active) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
@@ -96,6 +103,7 @@ __global__ __launch_bounds__(NT) void k_chunk_states(
                 }
             }
         }
+        __syncthreads();
     }
     if (active) {
 #pragma unroll

@@ -271,32 +271,51 @@ __device__ __forceinline__ void stage_mat(float* lds, const float* g) {
 // index idx with t % 16 = idx % 16, c4 % 4 = (idx / 16) % 4, t / 16 = (idx / 64) % 4,
 // c4 / 4 = idx / 256: one 64-lane store then covers 16 rows x 4 columns, i.e.
 // 64 distinct LDS banks (the token stride TB + 4 shifts each column by 4 banks),
-// and every row is still read as a 64-byte segment.
+// and every row is still read as a 64-byte segment.  The load half (into
+// registers) and the store half (into LDS) are separate so that a kernel can
+// issue the next block's loads before its matrix work on the current one.
 template <class IO, int W>
-__device__ __forceinline__ void stage_rows_t(float* lds, const typename IO::T* g, int64_t gstride,
-                                             const float* scale) {
-    constexpr int V = W / 4, TOTAL = TB * V, IT = (TOTAL + NT - 1) / NT;
-    constexpr int CL = V < 4 ? V : 4;  // float4 columns per 64-lane group
-    v4f tmp[IT];
+struct RowsT {
+    static constexpr int V = W / 4, TOTAL = TB * V, IT = (TOTAL + NT - 1) / NT;
+    static constexpr int CL = V < 4 ? V : 4;  // float4 columns per 64-lane group
+    __device__ static int row(int idx) { return (idx & 15) + 16 * ((idx / (16 * CL)) & 3); }
+    __device__ static int col4(int idx) { return (idx / 16) % CL + CL * (idx / (64 * CL)); }
+};
+
+template <class IO, int W, int IT>
+__device__ __forceinline__ void load_rows_t(v4f (&tmp)[IT], const typename IO::T* g, int64_t gstride) {
+    using RT = RowsT<IO, W>;
+    static_assert(IT == RT::IT, "register tile size");
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
+    for (int it = 0; it < RT::IT; ++it) {
         const int idx = static_cast<int>(threadIdx.x) + it * NT;
-        const int row = (idx & 15) + 16 * ((idx / (16 * CL)) & 3);
-        const int c4 = (idx / 16) % CL + CL * (idx / (64 * CL));
-        if (TOTAL % NT == 0 || idx < TOTAL)
-            tmp[it] = io<IO>::ld4(g, static_cast<int64_t>(row) * gstride + c4 * 4);
+        if (RT::TOTAL % NT == 0 || idx < RT::TOTAL)
+            tmp[it] = io<IO>::ld4(g, static_cast<int64_t>(RT::row(idx)) * gstride + RT::col4(idx) * 4);
     }
+}
+
+template <class IO, int W, int IT>
+__device__ __forceinline__ void store_rows_t(float* lds, const v4f (&tmp)[IT], const float* scale) {
+    using RT = RowsT<IO, W>;
+    static_assert(IT == RT::IT, "register tile size");
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
+    for (int it = 0; it < RT::IT; ++it) {
         const int idx = static_cast<int>(threadIdx.x) + it * NT;
-        const int row = (idx & 15) + 16 * ((idx / (16 * CL)) & 3);
-        const int c4 = (idx / 16) % CL + CL * (idx / (64 * CL));
-        if (TOTAL % NT == 0 || idx < TOTAL) {
+        if (RT::TOTAL % NT == 0 || idx < RT::TOTAL) {
+            const int row = RT::row(idx), c4 = RT::col4(idx);
             const v4f v = scale ? tmp[it] * scale[row] : tmp[it];
 #pragma unroll
             for (int e = 0; e < 4; ++e) lds[(c4 * 4 + e) * (TB + 4) + row] = v[e];
         }
     }
+}
+
+template <class IO, int W>
+__device__ __forceinline__ void stage_rows_t(float* lds, const typename IO::T* g, int64_t gstride,
+                                             const float* scale) {
+    v4f tmp[RowsT<IO, W>::IT];
+    load_rows_t<IO, W>(tmp, g, gstride);
+    store_rows_t<IO, W>(lds, tmp, scale);
 }
 
 // Sum over the four lane groups g = 0..3 that share i = lane % 16.

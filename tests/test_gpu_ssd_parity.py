@@ -101,6 +101,28 @@ def test_kernel_chunk_len_matches_oracle(l, kcl, io):
     compare(gpu, ref, TOL[io], KEYS, f"l={l} k={kcl} {io}")
 
 
+# Many short slices: 8192 and 16384 chunks (batch x heads x chunks) at each kernel
+# chunk length (the cumsum's lane widths 1, 2, 4), small headdim and dstate.
+# (batch, seq, nheads, chunk_len, kernel_chunk_len, heads compared or None for all);
+# headdim = dstate = 16.
+MANY = [(2, 4096, 64, 64, 64, None), (2, 4096, 128, 64, 64, None),
+        (2, 4096, 128, 128, 128, None), (2, 16384, 128, 256, 256, [0, 77, 127])]
+
+
+@pytest.mark.parametrize("b,seq,h,l,kcl,heads", MANY,
+                         ids=[f"b{m[0]}_s{m[1]}_h{m[2]}_k{m[4]}" for m in MANY])
+def test_many_chunks(b, seq, h, l, kcl, heads):
+    w = inputs.custom(batch=b, seq=seq, nheads=h, headdim=16, dstate=16, chunk_len=l, io="f32",
+                      init_std=0.3, seed=800 + h + kcl)
+    say(f"case many chunks b={b} seq={seq} h={h} kernel_chunk_len {kcl}")
+    inp = inputs.make_inputs(w)
+    gpu = gpu_fwd_bwd(inp, kernel_chunk_len=kcl)
+    ref = oracle_fwd_bwd(inp, heads=heads)
+    if heads is not None:
+        gpu = select_heads(gpu, heads)
+    compare(gpu, ref, TOL["f32"], KEYS, f"many chunks h={h} k={kcl}")
+
+
 def test_bitwise_deterministic():
     w = inputs.custom(batch=2, seq=1024, nheads=4, headdim=64, dstate=128, chunk_len=256,
                       init_std=0.2, seed=77)
