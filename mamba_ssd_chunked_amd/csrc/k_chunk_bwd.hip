@@ -264,6 +264,11 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     const float dec_end = expf(static_cast<float>(a * (end - cs)));
     const float bbar = dts * dec_end;
     __syncthreads();
+    // the first partner block (this block itself) loads into registers during K3
+    v4f preC[RowTiles<R, TB>::IT], preD[RowTiles<P, TB>::IT];
+    load_rows<IO, R, TB>(preC, Cm + brow0 + static_cast<int64_t>(sb * TB) * bstride, bstride);
+    load_rows<IO, P, TB>(preD, dy + xrow0 + static_cast<int64_t>(sb * TB) * xstride, xstride);
+    const double cpre = tid < TB ? cc[sb * TB + tid] : 0.0;
 
     // K3 backward.  d_b_scaled^T[r, s] = sum_p d_intra[p, r] x[s, p]
     v4f accB[R / 16];
@@ -310,13 +315,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     }
 
     float ddt_or = 0.0f, dsrc = 0.0f;
-    for (int tb = sb; tb < nblk; ++tb) {
-        __syncthreads();
-        const double cnext = tid < TB ? cc[tb * TB + tid] : 0.0;
-        stage_rows<IO, R>(sCT, Cm + brow0 + static_cast<int64_t>(tb * TB) * bstride, bstride);
-        stage_rows<IO, P>(sDY, dy + xrow0 + static_cast<int64_t>(tb * TB) * xstride, xstride);
-        if (tid < TB) sCdtT[tid] = cnext;
-        __syncthreads();
+    auto partner_block = [&](int tb) {
         const int jmin = (tb == sb) ? wave : 0;  // diagonal block: t-tiles from this wave's on
         for (int j = jmin; j < 4; ++j) {
             // tiles with M = t (16j + 4g + v), N = s (sl)
@@ -363,6 +362,21 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
                     accB[rt] = mfma16(sCT[(16 * j + 4 * g + v) * RS + rt * 16 + i], dcb[v], accB[rt]);
             }
         }
+    };
+    __syncthreads();  // K3 is done with d_intra
+    store_rows<R, TB>(sCT, preC);
+    store_rows<P, TB>(sDY, preD);
+    if (tid < TB) sCdtT[tid] = cpre;
+    __syncthreads();
+    partner_block(sb);
+    for (int tb = sb + 1; tb < nblk; ++tb) {
+        __syncthreads();
+        const double cnext = tid < TB ? cc[tb * TB + tid] : 0.0;
+        stage_rows<IO, R>(sCT, Cm + brow0 + static_cast<int64_t>(tb * TB) * bstride, bstride);
+        stage_rows<IO, P>(sDY, dy + xrow0 + static_cast<int64_t>(tb * TB) * xstride, xstride);
+        if (tid < TB) sCdtT[tid] = cnext;
+        __syncthreads();
+        partner_block(tb);
     }
 #pragma unroll
     for (int pt = 0; pt < P / 16; ++pt) io<IO>::st4(dx, xrow + pt * 16 + 4 * g, accX[pt]);

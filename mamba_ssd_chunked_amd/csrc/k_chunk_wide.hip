@@ -96,6 +96,10 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
     }
     __syncthreads();
 
+    // the even half of the source rows loads into registers during BLUE
+    v4f preB[RowTiles<R, TB>::IT], preX[RowTiles<P, TB>::IT];
+    load_half_rows<IO, R>(preB, Bm + brow0, bstride, 0);
+    load_half_rows<IO, P>(preX, x + xrow0, xstride, 0);
     v4f acc[2][P / 16];
 #pragma unroll
     for (int q = 0; q < 2; ++q)
@@ -167,13 +171,14 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
     };
     const float Dh = Dv[c.h];
     for (int half = 0; half < 2; ++half) {
-        v4f preB[RowTiles<R, TB>::IT], preX[RowTiles<P, TB>::IT];
-        load_half_rows<IO, R>(preB, Bm + brow0, bstride, half);
-        load_half_rows<IO, P>(preX, x + xrow0, xstride, half);
         __syncthreads();  // the previous contents of sM are consumed
         store_rows<R, TB>(sB, preB);
         store_rows<P, TB>(sX, preX);
         __syncthreads();
+        if (half == 0) {
+            load_half_rows<IO, R>(preB, Bm + brow0, bstride, 1);
+            load_half_rows<IO, P>(preX, x + xrow0, xstride, 1);
+        }
         // SKIP: D x of this wave's target rows that sit in this half
 #pragma unroll
         for (int q = 0; q < 2; ++q)
@@ -240,36 +245,47 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
         for (int kk = 0; kk < P / 16; ++kk)
             dyreg[q][kk] = io<IO>::ld4(dy, xrow0 + static_cast<int64_t>(tl[q]) * xstride + 16 * kk + 4 * g);
     }
-    stage_mat<R, P>(sM, S + c.ch * (P * R));
+    // S_in into LDS, and K4 backward's d_end = exp(A cdt[L-1]) <d_intra, S_in> from the
+    // same registers: both matrices' loads are in flight together with the operand rows'
+    double dA = 0.0;  // this thread's part of the chunk's d_A (pair form)
+    {
+        constexpr int V = R / 4, TOT = P * V, IT = (TOT + NT - 1) / NT;
+        const float* sp = S + c.ch * (P * R);
+        const float* dsp = dS + c.ch * (P * R);
+        v4f sv[IT], dv[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = tid + it * NT;
+            if (TOT % NT == 0 || idx < TOT) {
+                sv[it] = *reinterpret_cast<const v4f*>(sp + idx * 4);
+                dv[it] = *reinterpret_cast<const v4f*>(dsp + idx * 4);
+            }
+        }
+        double part = 0.0;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = tid + it * NT;
+            if (TOT % NT == 0 || idx < TOT) {
+                *reinterpret_cast<v4f*>(sM + (idx / V) * RS + (idx % V) * 4) = sv[it];
+                part += static_cast<double>(dv[it][0] * sv[it][0] + dv[it][1] * sv[it][1]) +
+                        static_cast<double>(dv[it][2] * sv[it][2] + dv[it][3] * sv[it][3]);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+        if (lane == 0) sRed[wave] = part;
+    }
     if (tid < KC) {
         sCdt[tid] = cc[tid];
         sDt[tid] = dt[c.c_bhn * L + tid];
     }
     __syncthreads();
-
-    double dA = 0.0;  // this thread's part of the chunk's d_A (pair form)
-    // K4 backward: d_end = exp(A cdt[L-1]) <d_intra, S_in>
-    {
-        const float* dsp = dS + c.ch * (P * R);
-        double part = 0.0;
-        for (int idx = tid; idx < P * (R / 4); idx += NT) {
-            const int row = idx / (R / 4), c4 = idx - (idx / (R / 4)) * (R / 4);
-            const v4f u = *reinterpret_cast<const v4f*>(dsp + row * R + c4 * 4);
-            const v4f w = *reinterpret_cast<const v4f*>(sM + row * RS + c4 * 4);
-            part += static_cast<double>(u[0] * w[0] + u[1] * w[1]) +
-                    static_cast<double>(u[2] * w[2] + u[3] * w[3]);
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-        if (lane == 0) sRed[wave] = part;
-        __syncthreads();
-        if (tid == 0) {
-            const double end = sCdt[L - 1];
-            const double de = (sRed[0] + sRed[1] + sRed[2] + sRed[3]) * exp(a * end);
-            const float def = static_cast<float>(de);
-            d_end[c.c_bhn] = def;
-            dA += static_cast<double>(def) * end;
-        }
+    if (tid == 0) {
+        const double end = sCdt[L - 1];
+        const double de = (sRed[0] + sRed[1] + sRed[2] + sRed[3]) * exp(a * end);
+        const float def = static_cast<float>(de);
+        d_end[c.c_bhn] = def;
+        dA += static_cast<double>(def) * end;
     }
 
     // BLUE: d_C^T[r, t] = e_t sum_p S_in[p, r] dy[t, p]

@@ -208,16 +208,35 @@ __global__ __launch_bounds__(NT, 2) void km_fwd_rows(
     v4f z[R / 16];
 #pragma unroll
     for (int rt = 0; rt < R / 16; ++rt) z[rt] = zero4();
-    for (int b2 = 0; b2 < nblk; ++b2) {
-        __syncthreads();
-        stage_rows<IO, P>(sX, x + xrow0 + static_cast<int64_t>(b2 * TB) * xstride, xstride);
-        stage_rows<IO, R>(sB, Bm + brow0 + static_cast<int64_t>(b2 * TB) * bstride, bstride);
+    // Partner blocks in the order sb + 1, ..., nblk - 1, 0, ..., sb: the last one
+    // staged is the own block, whose B rows the U product below reads from sB.
+    // Each block's rows load into registers while the previous block's tiles run.
+    v4f preX[RowTiles<P, TB>::IT], preB[RowTiles<R, TB>::IT];
+    double pc = 0.0, pp = 0.0;
+    float pd = 0.0f;
+    auto load_block = [&](int b2) {
+        load_rows<IO, P, TB>(preX, x + xrow0 + static_cast<int64_t>(b2 * TB) * xstride, xstride);
+        load_rows<IO, R, TB>(preB, Bm + brow0 + static_cast<int64_t>(b2 * TB) * bstride, bstride);
         if (tid < TB) {
-            sC[tid] = cc[b2 * TB + tid];
-            sPhi[tid] = ph[b2 * TB + tid];
-            sDt[tid] = dtc[b2 * TB + tid];
+            pc = cc[b2 * TB + tid];
+            pp = ph[b2 * TB + tid];
+            pd = dtc[b2 * TB + tid];
+        }
+    };
+    auto block_at = [&](int k) { return sb + 1 + k < nblk ? sb + 1 + k : sb + 1 + k - nblk; };
+    load_block(block_at(0));
+    for (int k = 0; k < nblk; ++k) {
+        const int b2 = block_at(k);
+        __syncthreads();
+        store_rows<P, TB>(sX, preX);
+        store_rows<R, TB>(sB, preB);
+        if (tid < TB) {
+            sC[tid] = pc;
+            sPhi[tid] = pp;
+            sDt[tid] = pd;
         }
         __syncthreads();
+        if (k + 1 < nblk) load_block(block_at(k + 1));
         for (int j = 0; j < 4; ++j) {
             // G^T tile: M = s' (16j + 4g + v), N = s
             v4f gt = zero4();
@@ -249,12 +268,11 @@ __global__ __launch_bounds__(NT, 2) void km_fwd_rows(
         }
     }
     __syncthreads();
-    // own block: B rows into sB, Z rows into sZ, u_s (1^T x_s) into sUx
+    // own block: its B rows are in sB already; Z rows into sZ, u_s (1^T x_s) into sUx
 #pragma unroll
     for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) sZ[(16 * wave + 4 * g + v) * RS + rt * 16 + i] = z[rt][v];
-    stage_rows<IO, R>(sB, Bm + brow0 + static_cast<int64_t>(sb * TB) * bstride, bstride);
     {
         float xs = 0.f;
 #pragma unroll

@@ -208,6 +208,17 @@ template <int W, int ROWS>
 struct RowTiles {
     static constexpr int V = W / 4, TOTAL = ROWS * V, IT = (TOTAL + NT - 1) / NT;
 };
+// Load ROWS consecutive rows (global row stride gstride) for store_rows.
+template <class IO, int W, int ROWS>
+__device__ __forceinline__ void load_rows(v4f* r, const typename IO::T* g, int64_t gstride) {
+    using RT = RowTiles<W, ROWS>;
+#pragma unroll
+    for (int it = 0; it < RT::IT; ++it) {
+        const int idx = static_cast<int>(threadIdx.x) + it * NT;
+        if (RT::TOTAL % NT == 0 || idx < RT::TOTAL)
+            r[it] = io<IO>::ld4(g, static_cast<int64_t>(idx / RT::V) * gstride + (idx % RT::V) * 4);
+    }
+}
 // Load the 64 rows of one half of a 128-row chunk that holds its even (half 0)
 // or odd (half 1) 16-row tiles: LDS row 16u + e is chunk row 16 (2u + half) + e.
 template <class IO, int W>
