@@ -235,6 +235,8 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     __shared__ float sDY[TB * PS];
     __shared__ __align__(16) double sCdtT[TB];
     __shared__ double sRed[2 * (NT / 64)];
+    constexpr int NEX = 4 * (P / 16 + R / 16) + 2;  // floats per lane handed from wave 3 to wave 0
+    __shared__ float sEx[NEX * 64];
     const int nblk = L / TB;
     const int sb = static_cast<int>(blockIdx.x / CH);  // block 0 has the most targets
     const ChunkHead c = decode_ch(blockIdx.x % CH, N, H);
@@ -264,11 +266,11 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     const float dec_end = expf(static_cast<float>(a * (end - cs)));
     const float bbar = dts * dec_end;
     __syncthreads();
-    // the first partner block (this block itself) loads into registers during K3
+    // the first partner block (the farthest, nblk - 1) loads into registers during K3
     v4f preC[RowTiles<R, TB>::IT], preD[RowTiles<P, TB>::IT];
-    load_rows<IO, R, TB>(preC, Cm + brow0 + static_cast<int64_t>(sb * TB) * bstride, bstride);
-    load_rows<IO, P, TB>(preD, dy + xrow0 + static_cast<int64_t>(sb * TB) * xstride, xstride);
-    const double cpre = tid < TB ? cc[sb * TB + tid] : 0.0;
+    load_rows<IO, R, TB>(preC, Cm + brow0 + static_cast<int64_t>((nblk - 1) * TB) * bstride, bstride);
+    load_rows<IO, P, TB>(preD, dy + xrow0 + static_cast<int64_t>((nblk - 1) * TB) * xstride, xstride);
+    const double cpre = tid < TB ? cc[(nblk - 1) * TB + tid] : 0.0;
 
     // K3 backward.  d_b_scaled^T[r, s] = sum_p d_intra[p, r] x[s, p]
     v4f accB[R / 16];
@@ -315,68 +317,142 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     }
 
     float ddt_or = 0.0f, dsrc = 0.0f;
-    auto partner_block = [&](int tb) {
-        const int jmin = (tb == sb) ? wave : 0;  // diagonal block: t-tiles from this wave's on
-        for (int j = jmin; j < 4; ++j) {
-            // tiles with M = t (16j + 4g + v), N = s (sl)
-            v4f cb = zero4(), dw = zero4();
+    // One (16-row target tile j of block tb, 16-row source tile) pair: the source tile's
+    // operands xr / br, cumsum csr, dt dtr and row srow inside the block, its accumulators.
+    auto tile = [&](int j, int tb, const v4f (&xr)[P / 16], const v4f (&br)[R / 16], double csr,
+                    float dtr, int srow, v4f (&aX)[P / 16], v4f (&aB)[R / 16], float& ddt,
+                    float& dsr) __attribute__((always_inline)) {
+        // tiles with M = t (16j + 4g + v), N = s
+        v4f cb = zero4(), dw = zero4();
 #pragma unroll
-            for (int kk = 0; kk < R / 16; ++kk) {
-                const v4f u = *reinterpret_cast<const v4f*>(sCT + (16 * j + i) * RS + 16 * kk + 4 * g);
-                cb = mfma_k16<IO>(u, breg[kk], cb);
-            }
+        for (int kk = 0; kk < R / 16; ++kk) {
+            const v4f u = *reinterpret_cast<const v4f*>(sCT + (16 * j + i) * RS + 16 * kk + 4 * g);
+            cb = mfma_k16<IO>(u, br[kk], cb);
+        }
 #pragma unroll
-            for (int kk = 0; kk < P / 16; ++kk) {
-                const v4f u = *reinterpret_cast<const v4f*>(sDY + (16 * j + i) * PS + 16 * kk + 4 * g);
-                dw = mfma_k16<IO>(u, xreg[kk], dw);
-            }
-            // this lane's four target rows: cumsums as two 16-byte LDS reads
-            const v2d ct01 = *reinterpret_cast<const v2d*>(sCdtT + 16 * j + 4 * g);
-            const v2d ct23 = *reinterpret_cast<const v2d*>(sCdtT + 16 * j + 4 * g + 2);
-            const double ctv[4] = {ct01.x, ct01.y, ct23.x, ct23.y};
-            float wv[4], dcb[4];
+        for (int kk = 0; kk < P / 16; ++kk) {
+            const v4f u = *reinterpret_cast<const v4f*>(sDY + (16 * j + i) * PS + 16 * kk + 4 * g);
+            dw = mfma_k16<IO>(u, xr[kk], dw);
+        }
+        // this lane's four target rows: cumsums as two 16-byte LDS reads
+        const v2d ct01 = *reinterpret_cast<const v2d*>(sCdtT + 16 * j + 4 * g);
+        const v2d ct23 = *reinterpret_cast<const v2d*>(sCdtT + 16 * j + 4 * g + 2);
+        const double ctv[4] = {ct01.x, ct01.y, ct23.x, ct23.y};
+        float wv[4], dcb[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const bool keep = (tb > sb) || (16 * j + 4 * g + v >= sl);
-                // masked pairs (t < s) take gap 0 and weight 0: arithmetic, not a branch
-                const double gap = keep ? ctv[v] - cs : 0.0;
-                const float dec = exp2_of(la2 * gap) * (keep ? 1.0f : 0.0f);
-                const float cbd = cb[v] * dec;
-                wv[v] = cbd * dts;
-                dcb[v] = dw[v] * dts * dec;
-                ddt_or += dw[v] * cbd;
-                dsrc += dcb[v] * cb[v];
-            }
-            // ORANGE: d_x^T[p, s] += sum_t dy[t, p] W[t, s]
+        for (int v = 0; v < 4; ++v) {
+            const bool keep = (tb > sb) || (16 * j + 4 * g + v >= srow);
+            // masked pairs (t < s) take gap 0 and weight 0: arithmetic, not a branch
+            const double gap = keep ? ctv[v] - csr : 0.0;
+            const float dec = exp2_of(la2 * gap) * (keep ? 1.0f : 0.0f);
+            const float cbd = cb[v] * dec;
+            wv[v] = cbd * dtr;
+            dcb[v] = dw[v] * dtr * dec;
+            ddt += dw[v] * cbd;
+            dsr += dcb[v] * cb[v];
+        }
+        // ORANGE: d_x^T[p, s] += sum_t dy[t, p] W[t, s]
 #pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt) {
+        for (int pt = 0; pt < P / 16; ++pt) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    accX[pt] = mfma16(sDY[(16 * j + 4 * g + v) * PS + pt * 16 + i], wv[v], accX[pt]);
-            }
-            // K2 backward: d_B^T[r, s] += sum_t C[t, r] d_CB[t, s]
+            for (int v = 0; v < 4; ++v)
+                aX[pt] = mfma16(sDY[(16 * j + 4 * g + v) * PS + pt * 16 + i], wv[v], aX[pt]);
+        }
+        // K2 backward: d_B^T[r, s] += sum_t C[t, r] d_CB[t, s]
 #pragma unroll
-            for (int rt = 0; rt < R / 16; ++rt) {
+        for (int rt = 0; rt < R / 16; ++rt) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    accB[rt] = mfma16(sCT[(16 * j + 4 * g + v) * RS + rt * 16 + i], dcb[v], accB[rt]);
-            }
+            for (int v = 0; v < 4; ++v)
+                aB[rt] = mfma16(sCT[(16 * j + 4 * g + v) * RS + rt * 16 + i], dcb[v], aB[rt]);
+        }
+    };
+    // Partner blocks from the farthest to the diagonal one.  On the diagonal block wave w
+    // owns the t-tiles j >= w (4, 3, 2, 1 tiles); with fp32 io wave 0's last one (j = 3)
+    // goes to wave 3, which is idle there otherwise, so no wave carries more than 3 and
+    // the block's barrier-to-end time drops by one tile.  (With bf16 io the hand-over's
+    // registers spill and the kernel is 5 % slower, so there wave 0 keeps all four.)
+    constexpr bool kSplit = sizeof(typename IO::T) == 4;
+    auto partner_block = [&](int tb) __attribute__((always_inline)) {
+        const bool diag = tb == sb;
+        const int jmin = diag ? wave : 0;
+        const int jmax = (kSplit && diag && wave == 0) ? 3 : 4;
+        for (int j = jmin; j < jmax; ++j) tile(j, tb, xreg, breg, cs, dts, sl, accX, accB, ddt_or, dsrc);
+    };
+    // wave 0 hands its source tile's operands (lane for lane) and dt to wave 3 through sEx
+    // before the barrier that opens the diagonal block
+    auto handoff = [&]() __attribute__((always_inline)) {
+        if (kSplit && wave == 0) {
+#pragma unroll
+            for (int kk = 0; kk < P / 16; ++kk)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) sEx[(4 * kk + v) * 64 + lane] = xreg[kk][v];
+#pragma unroll
+            for (int kk = 0; kk < R / 16; ++kk)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) sEx[(4 * (P / 16) + 4 * kk + v) * 64 + lane] = breg[kk][v];
+            sEx[(NEX - 2) * 64 + lane] = dts;
         }
     };
     __syncthreads();  // K3 is done with d_intra
     store_rows<R, TB>(sCT, preC);
     store_rows<P, TB>(sDY, preD);
     if (tid < TB) sCdtT[tid] = cpre;
+    if (nblk - 1 == sb) handoff();
     __syncthreads();
-    partner_block(sb);
-    for (int tb = sb + 1; tb < nblk; ++tb) {
+    partner_block(nblk - 1);
+    for (int tb = nblk - 2; tb >= sb; --tb) {
         __syncthreads();
         const double cnext = tid < TB ? cc[tb * TB + tid] : 0.0;
         stage_rows<IO, R>(sCT, Cm + brow0 + static_cast<int64_t>(tb * TB) * bstride, bstride);
         stage_rows<IO, P>(sDY, dy + xrow0 + static_cast<int64_t>(tb * TB) * xstride, xstride);
         if (tid < TB) sCdtT[tid] = cnext;
+        if (tb == sb) handoff();
         __syncthreads();
         partner_block(tb);
+    }
+    // wave 3: the pair (t-tile 3, source tile 0) of the diagonal block, still in LDS; the
+    // source tile's cumsums are the diagonal block's own (sCdtT).  Its partial sums go
+    // back to wave 0 through sEx, lane for lane
+    if (kSplit && wave == 3) {
+        v4f x0[P / 16], b0[R / 16], aX0[P / 16], aB0[R / 16];
+#pragma unroll
+        for (int kk = 0; kk < P / 16; ++kk) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) x0[kk][v] = sEx[(4 * kk + v) * 64 + lane];
+            aX0[kk] = zero4();
+        }
+#pragma unroll
+        for (int kk = 0; kk < R / 16; ++kk) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) b0[kk][v] = sEx[(4 * (P / 16) + 4 * kk + v) * 64 + lane];
+            aB0[kk] = zero4();
+        }
+        const float dts0 = sEx[(NEX - 2) * 64 + lane];
+        float ddt0 = 0.0f, dsr0 = 0.0f;
+        tile(3, sb, x0, b0, sCdtT[i], dts0, i, aX0, aB0, ddt0, dsr0);
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sEx[(4 * pt + v) * 64 + lane] = aX0[pt][v];
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sEx[(4 * (P / 16) + 4 * rt + v) * 64 + lane] = aB0[rt][v];
+        sEx[(NEX - 2) * 64 + lane] = ddt0;
+        sEx[(NEX - 1) * 64 + lane] = dsr0;
+    }
+    if (kSplit) __syncthreads();
+    if (kSplit && wave == 0) {
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) accX[pt][v] += sEx[(4 * pt + v) * 64 + lane];
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) accB[rt][v] += sEx[(4 * (P / 16) + 4 * rt + v) * 64 + lane];
+        ddt_or += sEx[(NEX - 2) * 64 + lane];
+        dsrc += sEx[(NEX - 1) * 64 + lane];
     }
 #pragma unroll
     for (int pt = 0; pt < P / 16; ++pt) io<IO>::st4(dx, xrow + pt * 16 + 4 * g, accX[pt]);
