@@ -373,23 +373,72 @@ __global__ __launch_bounds__(NT) void km_chunk(
         }
         return;
     }
-    // backward: S = dm2 + dm2^T into LDS
-    const float* d2 = dm2 + bh * (R * R);
-    for (int idx = tid; idx < R * R; idx += NT) {
-        const int r1 = idx / R, r2 = idx - (idx / R) * R;
-        sA[r1 * RS + r2] = d2[r1 * R + r2] + d2[r2 * R + r1];
-    }
-    __syncthreads();
+    // backward.  The first pass's H and T rows and the first B rows load into registers
+    // ahead of the S staging, so their latency overlaps it.
     const float* d1 = dm1 ? dm1 + bh * R : nullptr;
+    const int64_t brow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(R);
+    const int64_t bstride = static_cast<int64_t>(H) * R;
+    v4f ah[R / 16], at[R / 16], ab[R / 16];
+    {
+        const int row = 16 * wave + i;
+        if (row < P) {
+#pragma unroll
+            for (int kk = 0; kk < R / 16; ++kk) {
+                ah[kk] = *reinterpret_cast<const v4f*>(Hm + row * R + 16 * kk + 4 * g);
+                at[kk] = *reinterpret_cast<const v4f*>(Tc + row * R + 16 * kk + 4 * g);
+            }
+        }
+        if (row < L) {
+            const int64_t brow = brow0 + static_cast<int64_t>(row) * bstride;
+#pragma unroll
+            for (int kk = 0; kk < R / 16; ++kk) ab[kk] = io<IO>::ld4(Bm, brow + 16 * kk + 4 * g);
+        }
+    }
+    // S = dm2 + dm2^T into LDS: coalesced loads of dm2, then each unordered pair {r1, r2}
+    // is summed and written to both places by one thread (the sum is symmetric exactly)
+    {
+        const float* d2 = dm2 + bh * (R * R);
+        constexpr int V = R / 4, TOT = R * V, IT = (TOT + NT - 1) / NT;
+        v4f dv[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = tid + it * NT;
+            if (TOT % NT == 0 || idx < TOT) dv[it] = *reinterpret_cast<const v4f*>(d2 + idx * 4);
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = tid + it * NT;
+            if (TOT % NT == 0 || idx < TOT)
+                *reinterpret_cast<v4f*>(sA + (idx / V) * RS + (idx % V) * 4) = dv[it];
+        }
+        __syncthreads();
+        for (int idx = tid; idx < R * R; idx += NT) {
+            const int r1 = idx / R, r2 = idx - (idx / R) * R;
+            if (r1 < r2) {
+                const float v = sA[r1 * RS + r2] + sA[r2 * RS + r1];
+                sA[r1 * RS + r2] = v;
+                sA[r2 * RS + r1] = v;
+            } else if (r1 == r2) {
+                sA[r1 * RS + r1] = sA[r1 * RS + r1] + sA[r1 * RS + r1];
+            }
+        }
+        __syncthreads();
+    }
     double part_hsh = 0.0, part_hdm = 0.0;
     // HS = H S and dS_local = (c2 H + T) S + c1 1 dm1^T, 16 rows per wave per pass
     for (int r0 = 16 * wave; r0 < P; r0 += 64) {
-        v4f ah[R / 16], av[R / 16];
         const int row = r0 + i;
+        if (r0 != 16 * wave) {
+#pragma unroll
+            for (int kk = 0; kk < R / 16; ++kk) {
+                ah[kk] = *reinterpret_cast<const v4f*>(Hm + row * R + 16 * kk + 4 * g);
+                at[kk] = *reinterpret_cast<const v4f*>(Tc + row * R + 16 * kk + 4 * g);
+            }
+        }
+        v4f av[R / 16];
 #pragma unroll
         for (int kk = 0; kk < R / 16; ++kk) {
-            ah[kk] = *reinterpret_cast<const v4f*>(Hm + row * R + 16 * kk + 4 * g);
-            av[kk] = static_cast<float>(c2) * ah[kk] + *reinterpret_cast<const v4f*>(Tc + row * R + 16 * kk + 4 * g);
+            av[kk] = static_cast<float>(c2) * ah[kk] + at[kk];
             if (d1) {
                 const v4f dv = *reinterpret_cast<const v4f*>(d1 + 16 * kk + 4 * g);
                 part_hdm += static_cast<double>(ah[kk][0] * dv[0] + ah[kk][1] * dv[1]) +
@@ -412,13 +461,12 @@ __global__ __launch_bounds__(NT) void km_chunk(
             }
     }
     // BS = B S for the chunk's tokens
-    const int64_t brow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(R);
-    const int64_t bstride = static_cast<int64_t>(H) * R;
     for (int r0 = 16 * wave; r0 < L; r0 += 64) {
-        v4f ab[R / 16];
-        const int64_t row = brow0 + static_cast<int64_t>(r0 + i) * bstride;
+        if (r0 != 16 * wave) {
+            const int64_t brow = brow0 + static_cast<int64_t>(r0 + i) * bstride;
 #pragma unroll
-        for (int kk = 0; kk < R / 16; ++kk) ab[kk] = io<IO>::ld4(Bm, row + 16 * kk + 4 * g);
+            for (int kk = 0; kk < R / 16; ++kk) ab[kk] = io<IO>::ld4(Bm, brow + 16 * kk + 4 * g);
+        }
         v4f o[R / 16];
 #pragma unroll
         for (int nt = 0; nt < R / 16; ++nt) o[nt] = zero4();
