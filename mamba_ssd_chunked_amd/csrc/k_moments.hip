@@ -630,9 +630,19 @@ __global__ __launch_bounds__(NT, (P * R <= 64 * 64 && P <= 64) ? 2 : 1) void km_
 
     v4f accX[P / 16], accB[R / 16];
     float eta_s = 0.f, xdb = 0.f;
-    // phase 1a: HS terms
+    // phase 1a: HS terms; d_intra loads into registers meanwhile
     stage_mat<R, P>(sM, HS + c.ch * (P * R));
     __syncthreads();
+    constexpr int MV = R / 4, MTOT = P * MV, MIT = (MTOT + NT - 1) / NT;
+    v4f pre_dI[MIT];
+    {
+        const float* g = dI + c.ch * (P * R);
+#pragma unroll
+        for (int it = 0; it < MIT; ++it) {
+            const int idx = tid + it * NT;
+            if (MTOT % NT == 0 || idx < MTOT) pre_dI[it] = *reinterpret_cast<const v4f*>(g + idx * 4);
+        }
+    }
     {
         v4f t[P / 16];
 #pragma unroll
@@ -669,9 +679,26 @@ __global__ __launch_bounds__(NT, (P * R <= 64 * 64 && P <= 64) ? 2 : 1) void km_
         }
     }
     __syncthreads();
-    // phase 1b: d_intra (the carried gradient of the chunk's last state) terms
-    stage_mat<R, P>(sM, dI + c.ch * (P * R));
+    // phase 1b: d_intra (the carried gradient of the chunk's last state) terms; the first
+    // partner block's rows load into registers meanwhile
+#pragma unroll
+    for (int it = 0; it < MIT; ++it) {
+        const int idx = tid + it * NT;
+        if (MTOT % NT == 0 || idx < MTOT)
+            *reinterpret_cast<v4f*>(sM + (idx / MV) * RS + (idx % MV) * 4) = pre_dI[it];
+    }
     __syncthreads();
+    v4f preX[RowTiles<P, TB>::IT], preQ[RowTiles<R, TB>::IT];
+    load_rows<IO, P, TB>(preX, x + xrow0, xstride);
+    load_rows<F32, R, TB>(preQ, BS + c.ch * L * static_cast<int64_t>(R), R);
+    double pc = 0.0, pph = 0.0, ppt = 0.0;
+    float pdt = 0.0f;
+    if (tid < TB) {
+        pc = cc[tid];
+        pph = ph[tid];
+        ppt = phit[c.c_bhn * L + tid];
+        pdt = dtc[tid];
+    }
     {
         v4f t[P / 16];
 #pragma unroll
@@ -709,13 +736,16 @@ __global__ __launch_bounds__(NT, (P * R <= 64 * 64 && P <= 64) ? 2 : 1) void km_
         const float* he = (c.n + 1 < N) ? Sin + (c.ch + H) * (P * R) : final_state + bh * (P * R);
         const float* hm = Sin + c.ch * (P * R);
         double part = 0.0, part2 = 0.0;
-        for (int idx = tid; idx < P * (R / 4); idx += NT) {
-            const int row = idx / (R / 4), c4 = idx - (idx / (R / 4)) * (R / 4);
-            const v4f u = *reinterpret_cast<const v4f*>(he + row * R + c4 * 4);
-            const v4f u2 = *reinterpret_cast<const v4f*>(hm + row * R + c4 * 4);
-            const v4f w = *reinterpret_cast<const v4f*>(sM + row * RS + c4 * 4);
-            part += static_cast<double>(u[0] * w[0] + u[1] * w[1]) + static_cast<double>(u[2] * w[2] + u[3] * w[3]);
-            part2 += static_cast<double>(u2[0] * w[0] + u2[1] * w[1]) + static_cast<double>(u2[2] * w[2] + u2[3] * w[3]);
+#pragma unroll
+        for (int it = 0; it < MIT; ++it) {
+            const int idx = tid + it * NT;
+            if (MTOT % NT == 0 || idx < MTOT) {
+                const v4f u = *reinterpret_cast<const v4f*>(he + idx * 4);
+                const v4f u2 = *reinterpret_cast<const v4f*>(hm + idx * 4);
+                const v4f w = *reinterpret_cast<const v4f*>(sM + (idx / MV) * RS + (idx % MV) * 4);
+                part += static_cast<double>(u[0] * w[0] + u[1] * w[1]) + static_cast<double>(u[2] * w[2] + u[3] * w[3]);
+                part2 += static_cast<double>(u2[0] * w[0] + u2[1] * w[1]) + static_cast<double>(u2[2] * w[2] + u2[3] * w[3]);
+            }
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
@@ -742,13 +772,24 @@ __global__ __launch_bounds__(NT, (P * R <= 64 * 64 && P <= 64) ? 2 : 1) void km_
     float kpn = 0.f, rh = 0.f;
     for (int b2 = 0; b2 < nblk; ++b2) {
         __syncthreads();
-        stage_rows<IO, P>(sX, x + xrow0 + static_cast<int64_t>(b2 * TB) * xstride, xstride);
-        stage_mat<R, TB>(sQ, BS + (c.ch * L + b2 * TB) * static_cast<int64_t>(R));
-        if (tid < TB) {
-            sC[tid] = cc[b2 * TB + tid];
-            sPhi[tid] = ph[b2 * TB + tid];
-            sPhit[tid] = phit[c.c_bhn * L + b2 * TB + tid];
-            sDt[tid] = dtc[b2 * TB + tid];
+        if (b2 == 0) {
+            store_rows<P, TB>(sX, preX);
+            store_rows<R, TB>(sQ, preQ);
+            if (tid < TB) {
+                sC[tid] = pc;
+                sPhi[tid] = pph;
+                sPhit[tid] = ppt;
+                sDt[tid] = pdt;
+            }
+        } else {
+            stage_rows<IO, P>(sX, x + xrow0 + static_cast<int64_t>(b2 * TB) * xstride, xstride);
+            stage_mat<R, TB>(sQ, BS + (c.ch * L + b2 * TB) * static_cast<int64_t>(R));
+            if (tid < TB) {
+                sC[tid] = cc[b2 * TB + tid];
+                sPhi[tid] = ph[b2 * TB + tid];
+                sPhit[tid] = phit[c.c_bhn * L + b2 * TB + tid];
+                sDt[tid] = dtc[b2 * TB + tid];
+            }
         }
         __syncthreads();
 #pragma unroll 1
