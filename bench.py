@@ -89,8 +89,8 @@ def kernel_work(w, kernel: str, k: int):
         return 8 * p * r * ch + 8 * ch + 8 * b * h * p * r, "byte"
     if kernel == "k4_state_pass_bwd":
         return 16 * p * r * ch + 8 * ch + 8 * b * h * p * r, "byte"
-    if kernel == "k1t_revcumsum":
-        return 24 * tok + 8 * ch, "byte"
+    if kernel == "k1t_revcumsum":       # with the per-head d_A / d_D sums in the same launch
+        return 24 * tok + 8 * ch + 24 * ch * (l // 64) + 8 * h, "byte"
     return None, None
 
 

@@ -239,13 +239,13 @@ hipError_t launch_k4_pass_bwd(const Shape& s, float* S, float* dS, const double*
 // (end - cumsum[k] sums dA over positions k+1..L-1, so d_delta[k] reaches every
 // t > k), and d_dt[t] += A d_da[t].  (d_A is assembled from per-pair weights in
 // the chunk kernels instead of sum_t d_da[t] dt[t], which cancels badly.)
-__global__ __launch_bounds__(NT) void k1t_revcumsum(
-    const float* __restrict__ g1, const float* __restrict__ g2,
-    const float* __restrict__ d_delta, const float* __restrict__ d_end,
-    const float* __restrict__ A, float* __restrict__ d_dt, int64_t nchunks_total, int H, int N,
-    int L) {
+__device__ __forceinline__ void k1t_block(const float* __restrict__ g1, const float* __restrict__ g2,
+                                          const float* __restrict__ d_delta,
+                                          const float* __restrict__ d_end,
+                                          const float* __restrict__ A, float* __restrict__ d_dt,
+                                          int64_t nchunks_total, int H, int N, int L, int64_t blk) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t c = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    const int64_t c = blk * 4 + wave;
     if (c >= nchunks_total) return;
     const int h = static_cast<int>((c / N) % H);
     const double a = static_cast<double>(A[h]);
@@ -293,29 +293,19 @@ __global__ __launch_bounds__(NT) void k1t_revcumsum(
         }
 }
 
-hipError_t launch_k1t(const Shape& s, const float* g1, const float* g2, const float* d_delta,
-                      const float* d_end, const float* A, float* d_dt, hipStream_t st) {
-    const int64_t nc = s.chunks();
-    if (nc == 0) return hipSuccess;
-    const dim3 grid(static_cast<unsigned>((nc + 3) / 4));
-    hipLaunchKernelGGL(k1t_revcumsum, grid, dim3(NT), 0, st, g1, g2, d_delta, d_end, A, d_dt, nc,
-                       s.H, s.N, s.L);
-    return hipGetLastError();
-}
 
 // ------------------------------------------------------------- head reductions
 // One workgroup per head sums partials stored in [b, n, h, k] order (k < nk) in
 // a fixed order: thread j takes a fixed strided subset, then a fixed tree, so
 // the result does not depend on scheduling.  Up to two arrays are summed per
 // output (d_A gets the target- and source-side partials).
-__global__ __launch_bounds__(NT) void reduce_heads(const double* __restrict__ a0,
-                                                   const double* __restrict__ a1,
-                                                   const double* __restrict__ d0,
-                                                   float* __restrict__ d_A,
-                                                   float* __restrict__ d_D, int B, int H,
-                                                   int N, int nk) {
+__device__ __forceinline__ void reduce_head(const double* __restrict__ a0,
+                                            const double* __restrict__ a1,
+                                            const double* __restrict__ d0, float* __restrict__ d_A,
+                                            float* __restrict__ d_D, int B, int H, int N, int nk,
+                                            int h) {
     __shared__ double ra[NT], rd[NT];
-    const int h = blockIdx.x, tid = threadIdx.x;
+    const int tid = threadIdx.x;
     double a = 0.0, d = 0.0;
     const int64_t total = static_cast<int64_t>(B) * N * nk;
     for (int64_t j = tid; j < total; j += NT) {
@@ -339,6 +329,46 @@ __global__ __launch_bounds__(NT) void reduce_heads(const double* __restrict__ a0
         if (d_A) d_A[h] = static_cast<float>(ra[0]);
         if (d_D) d_D[h] = static_cast<float>(rd[0]);
     }
+}
+
+__global__ __launch_bounds__(NT) void reduce_heads(const double* __restrict__ a0,
+                                                   const double* __restrict__ a1,
+                                                   const double* __restrict__ d0,
+                                                   float* __restrict__ d_A,
+                                                   float* __restrict__ d_D, int B, int H, int N,
+                                                   int nk) {
+    reduce_head(a0, a1, d0, d_A, d_D, B, H, N, nk, blockIdx.x);
+}
+
+// K1^T and the per-head d_A / d_D sums of the SSD backward in one launch (both read
+// only what the chunk kernels wrote): blocks [0, nk1t) take four chunks each, block
+// nk1t + h sums head h.  One launch instead of two: the two small grids run side by side.
+__global__ __launch_bounds__(NT) void k1t_and_heads(
+    const float* __restrict__ g1, const float* __restrict__ g2,
+    const float* __restrict__ d_delta, const float* __restrict__ d_end,
+    const float* __restrict__ A, float* __restrict__ d_dt, int64_t nchunks_total, int H, int N,
+    int L, int64_t nk1t, const double* __restrict__ a0, const double* __restrict__ a1,
+    const double* __restrict__ d0, float* __restrict__ d_A, float* __restrict__ d_D, int B,
+    int nk) {
+    const int64_t blk = blockIdx.x;
+    if (blk < nk1t)
+        k1t_block(g1, g2, d_delta, d_end, A, d_dt, nchunks_total, H, N, L, blk);
+    else
+        reduce_head(a0, a1, d0, d_A, d_D, B, H, N, nk, static_cast<int>(blk - nk1t));
+}
+
+hipError_t launch_k1t_heads(const Shape& s, const float* g1, const float* g2, const float* d_delta,
+                            const float* d_end, const float* A, float* d_dt,
+                            const double* dA_part0, const double* dA_part1, const double* dD_part,
+                            int nk, float* d_A, float* d_D, hipStream_t st) {
+    const int64_t nc = s.chunks();
+    const int64_t nk1t = (nc + 3) / 4;
+    const int64_t blocks = nk1t + s.H;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(k1t_and_heads, dim3(static_cast<unsigned>(blocks)), dim3(NT), 0, st, g1, g2,
+                       d_delta, d_end, A, d_dt, nc, s.H, s.N, s.L, nk1t, dA_part0, dA_part1,
+                       dD_part, d_A, d_D, s.B, nk);
+    return hipGetLastError();
 }
 
 hipError_t launch_reduce_heads(const Shape& s, const double* dA_part0, const double* dA_part1,

@@ -469,8 +469,8 @@ int ssd_bwd(const ssd_dims* dims, const void* dy, const float* d_final, const vo
             "k_bwd_target");
     SSD_HIP(ssd::launch_bwd_source(s, dy, x, dt, B, C, A, D, cdt, dS, d_x, d_B, d_dt, g2, dlt, dAS, dDp, st),
             "k_bwd_source");
-    SSD_HIP(ssd::launch_k1t(s, g1, g2, dlt, dend, A, d_dt, st), "k1t_revcumsum");
-    SSD_HIP(ssd::launch_reduce_heads(s, dAT, dAS, dDp, s.nblk(), d_A, d_D, st), "reduce_heads");
+    SSD_HIP(ssd::launch_k1t_heads(s, g1, g2, dlt, dend, A, d_dt, dAT, dAS, dDp, s.nblk(), d_A, d_D, st),
+            "k1t_revcumsum");
     return ok();
 }
 

@@ -114,9 +114,12 @@ hipError_t launch_bwd_source(const Shape& s, const void* dy, const void* x, cons
                              float* g2, float* d_delta, double* dA_S, double* dD_part,
                              hipStream_t st);
 
-// K1 backward: suffix sums inside each chunk, d_dt += A d_da.
-hipError_t launch_k1t(const Shape& s, const float* g1, const float* g2, const float* d_delta,
-                      const float* d_end, const float* A, float* d_dt, hipStream_t st);
+// K1 backward (suffix sums inside each chunk, d_dt += A d_da) and, in the same launch,
+// the per-head sums of launch_reduce_heads below.
+hipError_t launch_k1t_heads(const Shape& s, const float* g1, const float* g2, const float* d_delta,
+                            const float* d_end, const float* A, float* d_dt,
+                            const double* dA_part0, const double* dA_part1, const double* dD_part,
+                            int nk, float* d_A, float* d_D, hipStream_t st);
 
 // Deterministic per-head sums of partials in [b, n, h, k] order (k < nk):
 // d_A[h] = sum of dA_part0 + dA_part1, d_D[h] = sum of dD_part.  NULL parts/outputs are skipped.
