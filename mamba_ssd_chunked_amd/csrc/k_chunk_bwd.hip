@@ -31,7 +31,7 @@
 //     g2[s]      = -sum_{t>=s} d_diff[t,s]                    (ORANGE d_da, source side)
 //     d_delta[s] = d_bbar[s] dt[s] exp(end - cum[s])          (K3: gradient of end - cum[s])
 //     dD_part    = sum dy x                                   (SKIP, d_D)
-// k1t_revcumsum then turns g1 + g2, d_delta and d_end into d_cum's suffix sum
+// k1t_and_heads (K1^T) then turns g1 + g2, d_delta and d_end into d_cum's suffix sum
 // (for d_dt).
 //
 // d_A is NOT formed as sum_t d_da[t] dt[t]: the suffix sums of rowsum - colsum
