@@ -455,9 +455,9 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
         dsrc += sEx[(NEX - 1) * 64 + lane];
     }
 #pragma unroll
-    for (int pt = 0; pt < P / 16; ++pt) io<IO>::st4(dx, xrow + pt * 16 + 4 * g, accX[pt]);
+    for (int pt = 0; pt < P / 16; ++pt) st4_nt<IO>(dx, xrow + pt * 16 + 4 * g, accX[pt]);
 #pragma unroll
-    for (int rt = 0; rt < R / 16; ++rt) io<IO>::st4(dB, brow + rt * 16 + 4 * g, accB[rt]);
+    for (int rt = 0; rt < R / 16; ++rt) st4_nt<IO>(dB, brow + rt * 16 + 4 * g, accB[rt]);
 
     dbb = sum_over_g(dbb);
     ddt_or = sum_over_g(ddt_or);

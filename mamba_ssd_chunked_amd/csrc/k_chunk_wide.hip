@@ -201,7 +201,7 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
         for (int v = 0; v < 4; ++v) {
             const int64_t row = xrow0 + static_cast<int64_t>(16 * tt[q] + 4 * g + v) * xstride;
 #pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt) io<IO>::st(y, row + pt * 16 + i, acc[q][pt][v]);
+            for (int pt = 0; pt < P / 16; ++pt) st_nt<IO>(y, row + pt * 16 + i, acc[q][pt][v]);
         }
 }
 
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
     for (int q = 0; q < 2; ++q) {
         const int64_t row = brow0 + static_cast<int64_t>(tl[q]) * bstride;
 #pragma unroll
-        for (int rt = 0; rt < R / 16; ++rt) io<IO>::st4(dC, row + rt * 16 + 4 * g, acc[q][rt]);
+        for (int rt = 0; rt < R / 16; ++rt) st4_nt<IO>(dC, row + rt * 16 + 4 * g, acc[q][rt]);
         const float gs = sum_over_g(gsum[q]);
         if (g == 0) g1[c.c_bhn * L + tl[q]] = gs;
     }

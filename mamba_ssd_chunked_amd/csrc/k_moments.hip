@@ -842,9 +842,9 @@ __global__ __launch_bounds__(NT, (P * R <= 64 * 64 && P <= 64) ? 2 : 1) void km_
         }
     }
 #pragma unroll
-    for (int pt = 0; pt < P / 16; ++pt) io<IO>::st4(dx, xrow + pt * 16 + 4 * g, accX[pt]);
+    for (int pt = 0; pt < P / 16; ++pt) st4_nt<IO>(dx, xrow + pt * 16 + 4 * g, accX[pt]);
 #pragma unroll
-    for (int rt = 0; rt < R / 16; ++rt) io<IO>::st4(dB, brow + rt * 16 + 4 * g, accB[rt]);
+    for (int rt = 0; rt < R / 16; ++rt) st4_nt<IO>(dB, brow + rt * 16 + 4 * g, accB[rt]);
     eta_s = sum_over_g(eta_s);
     xdb = sum_over_g(xdb);
     kpn = sum_over_g(kpn);
