@@ -454,10 +454,39 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
         ddt_or += sEx[(NEX - 2) * 64 + lane];
         dsrc += sEx[(NEX - 1) * 64 + lane];
     }
+    // fp32 io: d_x and d_B leave through LDS so that each non-temporal store instruction
+    // writes whole rows (16 B per lane scattered over 64-byte row pieces wrote 20 % more
+    // bytes than the outputs hold): wave w's 16 rows go to sDY / sCT, then back out
+    // row-major.  bf16 io stores straight from the accumulators (ordinary stores; the
+    // detour through LDS made that kernel 4 % slower).
+    if constexpr (sizeof(typename IO::T) != 4) {
 #pragma unroll
-    for (int pt = 0; pt < P / 16; ++pt) st4_nt<IO>(dx, xrow + pt * 16 + 4 * g, accX[pt]);
+        for (int pt = 0; pt < P / 16; ++pt) io<IO>::st4(dx, xrow + pt * 16 + 4 * g, accX[pt]);
 #pragma unroll
-    for (int rt = 0; rt < R / 16; ++rt) st4_nt<IO>(dB, brow + rt * 16 + 4 * g, accB[rt]);
+        for (int rt = 0; rt < R / 16; ++rt) io<IO>::st4(dB, brow + rt * 16 + 4 * g, accB[rt]);
+    } else {
+        __syncthreads();  // every wave is done with the partner rows
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt)
+            *reinterpret_cast<v4f*>(sDY + sl * PS + pt * 16 + 4 * g) = accX[pt];
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt)
+            *reinterpret_cast<v4f*>(sCT + sl * RS + rt * 16 + 4 * g) = accB[rt];
+        __syncthreads();
+        const int64_t row0 = static_cast<int64_t>(sb * TB + 16 * wave);
+#pragma unroll
+        for (int k = lane; k < 16 * (P / 4); k += 64) {
+            const int r_ = k / (P / 4), c4 = k % (P / 4);
+            st4_nt<IO>(dx, xrow0 + (row0 + r_) * xstride + c4 * 4,
+                       *reinterpret_cast<const v4f*>(sDY + (16 * wave + r_) * PS + c4 * 4));
+        }
+#pragma unroll
+        for (int k = lane; k < 16 * (R / 4); k += 64) {
+            const int r_ = k / (R / 4), c4 = k % (R / 4);
+            st4_nt<IO>(dB, brow0 + (row0 + r_) * bstride + c4 * 4,
+                       *reinterpret_cast<const v4f*>(sCT + (16 * wave + r_) * RS + c4 * 4));
+        }
+    }
 
     dbb = sum_over_g(dbb);
     ddt_or = sum_over_g(ddt_or);

@@ -372,9 +372,27 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
 
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        const int64_t row = brow0 + static_cast<int64_t>(tl[q]) * bstride;
+        if constexpr (sizeof(typename IO::T) != 4) {
+            const int64_t row = brow0 + static_cast<int64_t>(tl[q]) * bstride;
 #pragma unroll
-        for (int rt = 0; rt < R / 16; ++rt) st4_nt<IO>(dC, row + rt * 16 + 4 * g, acc[q][rt]);
+            for (int rt = 0; rt < R / 16; ++rt) io<IO>::st4(dC, row + rt * 16 + 4 * g, acc[q][rt]);
+        } else {
+            // fp32 io: the tile's d_C rows leave through LDS so that each non-temporal
+            // store instruction writes whole rows (scattered 64-byte row pieces wrote 20 %
+            // more bytes than the output holds)
+            __syncthreads();  // sM's previous contents are consumed
+#pragma unroll
+            for (int rt = 0; rt < R / 16; ++rt)
+                *reinterpret_cast<v4f*>(sM + (16 * wave + i) * RS + rt * 16 + 4 * g) = acc[q][rt];
+            __syncthreads();
+            const int64_t row0 = brow0 + static_cast<int64_t>(16 * tt[q]) * bstride;
+#pragma unroll
+            for (int k = lane; k < 16 * (R / 4); k += 64) {
+                const int r_ = k / (R / 4), c4 = k % (R / 4);
+                st4_nt<IO>(dC, row0 + r_ * bstride + c4 * 4,
+                           *reinterpret_cast<const v4f*>(sM + (16 * wave + r_) * RS + c4 * 4));
+            }
+        }
         const float gs = sum_over_g(gsum[q]);
         if (g == 0) g1[c.c_bhn * L + tl[q]] = gs;
     }

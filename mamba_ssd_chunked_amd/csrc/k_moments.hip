@@ -841,10 +841,36 @@ __global__ __launch_bounds__(NT, (P * R <= 64 * 64 && P <= 64) ? 2 : 1) void km_
                     accB[rt] = mfma16(sQ[(16 * j + 4 * g + v) * RS + rt * 16 + i], kg[v], accB[rt]);
         }
     }
+    if constexpr (sizeof(typename IO::T) != 4) {
 #pragma unroll
-    for (int pt = 0; pt < P / 16; ++pt) st4_nt<IO>(dx, xrow + pt * 16 + 4 * g, accX[pt]);
+        for (int pt = 0; pt < P / 16; ++pt) io<IO>::st4(dx, xrow + pt * 16 + 4 * g, accX[pt]);
 #pragma unroll
-    for (int rt = 0; rt < R / 16; ++rt) st4_nt<IO>(dB, brow + rt * 16 + 4 * g, accB[rt]);
+        for (int rt = 0; rt < R / 16; ++rt) io<IO>::st4(dB, brow + rt * 16 + 4 * g, accB[rt]);
+    } else {
+        // fp32 io: the rows leave through LDS so that each non-temporal store instruction
+        // writes whole rows (scattered 64-byte row pieces wrote 20 % more bytes)
+        __syncthreads();  // every wave is done with the partner rows
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt)
+            *reinterpret_cast<v4f*>(sX + sl * PS + pt * 16 + 4 * g) = accX[pt];
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt)
+            *reinterpret_cast<v4f*>(sQ + sl * RS + rt * 16 + 4 * g) = accB[rt];
+        __syncthreads();
+        const int64_t row0 = static_cast<int64_t>(sb * TB + 16 * wave);
+#pragma unroll
+        for (int k = lane; k < 16 * (P / 4); k += 64) {
+            const int r_ = k / (P / 4), c4 = k % (P / 4);
+            st4_nt<IO>(dx, xrow0 + (row0 + r_) * xstride + c4 * 4,
+                       *reinterpret_cast<const v4f*>(sX + (16 * wave + r_) * PS + c4 * 4));
+        }
+#pragma unroll
+        for (int k = lane; k < 16 * (R / 4); k += 64) {
+            const int r_ = k / (R / 4), c4 = k % (R / 4);
+            st4_nt<IO>(dB, brow0 + (row0 + r_) * bstride + c4 * 4,
+                       *reinterpret_cast<const v4f*>(sQ + (16 * wave + r_) * RS + c4 * 4));
+        }
+    }
     eta_s = sum_over_g(eta_s);
     xdb = sum_over_g(xdb);
     kpn = sum_over_g(kpn);
