@@ -281,21 +281,29 @@ __global__ __launch_bounds__(NT, 2) void km_fwd_rows(
         if (g == 0) sUx[sl] = static_cast<float>(static_cast<double>(dts) * psi[c.c_bhn * L + spos]) * xs;
     }
     __syncthreads();
-    // U[r1, r2] = sum_s B[s, r1] Z[s, r2]; 16x16 tiles dealt round-robin to the waves
-    constexpr int NTR = R / 16, NTILE = NTR * NTR;
+    // U[r1, r2] = sum_s B[s, r1] Z[s, r2]; wave w takes the 16-row strips r1t = w, w + 4, ...
+    // with all their column tiles at once (independent accumulator chains; one tile at a
+    // time made every MFMA wait for the one before it)
+    constexpr int NTR = R / 16;
     float* Uo = U + (c.ch * nblk + sb) * static_cast<int64_t>(R * R);
-    for (int tile = wave; tile < NTILE; tile += 4) {
-        const int r1t = tile / NTR, r2t = tile - (tile / NTR) * NTR;
-        v4f acc = zero4();
+    for (int r1t = wave; r1t < NTR; r1t += 4) {
+        v4f acc[NTR];
+#pragma unroll
+        for (int r2t = 0; r2t < NTR; ++r2t) acc[r2t] = zero4();
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int s_ = 16 * kk + 4 * g + v;
-                acc = mfma16(sB[s_ * RS + r1t * 16 + i], sZ[s_ * RS + r2t * 16 + i], acc);
+                const float av = sB[s_ * RS + r1t * 16 + i];
+#pragma unroll
+                for (int r2t = 0; r2t < NTR; ++r2t)
+                    acc[r2t] = mfma16(av, sZ[s_ * RS + r2t * 16 + i], acc[r2t]);
             }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) Uo[(r1t * 16 + 4 * g + v) * R + r2t * 16 + i] = acc[v];
+        for (int r2t = 0; r2t < NTR; ++r2t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) Uo[(r1t * 16 + 4 * g + v) * R + r2t * 16 + i] = acc[r2t][v];
     }
     float* mo = m1b + (c.ch * nblk + sb) * static_cast<int64_t>(R);
     for (int r = tid; r < R; r += NT) {
@@ -352,19 +360,27 @@ __global__ __launch_bounds__(NT) void km_chunk(
             *reinterpret_cast<v4f*>(sV + row * RS + c4 * 4) = 2.0f * tv + static_cast<float>(c2) * hv;
         }
         __syncthreads();
-        constexpr int NTR = R / 16, NTILE = NTR * NTR;
+        // wave w takes the 16-row strips r1t = w, w + 4, ... with all their column tiles at
+        // once (independent accumulator chains)
+        constexpr int NTR = R / 16;
         float* Wo = W + c.ch * static_cast<int64_t>(R * R);
-        for (int tile = wave; tile < NTILE; tile += 4) {
-            const int r1t = tile / NTR, r2t = tile - (tile / NTR) * NTR;
-            v4f acc = zero4();
+        for (int r1t = wave; r1t < NTR; r1t += 4) {
+            v4f acc[NTR];
+#pragma unroll
+            for (int r2t = 0; r2t < NTR; ++r2t) acc[r2t] = zero4();
             for (int kk = 0; kk < P / 16; ++kk)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int p_ = 16 * kk + 4 * g + v;
-                    acc = mfma16(sA[p_ * RS + r1t * 16 + i], sV[p_ * RS + r2t * 16 + i], acc);
+                    const float av = sA[p_ * RS + r1t * 16 + i];
+#pragma unroll
+                    for (int r2t = 0; r2t < NTR; ++r2t)
+                        acc[r2t] = mfma16(av, sV[p_ * RS + r2t * 16 + i], acc[r2t]);
                 }
 #pragma unroll
-            for (int v = 0; v < 4; ++v) Wo[(r1t * 16 + 4 * g + v) * R + r2t * 16 + i] = acc[v];
+            for (int r2t = 0; r2t < NTR; ++r2t)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) Wo[(r1t * 16 + 4 * g + v) * R + r2t * 16 + i] = acc[r2t][v];
         }
         for (int r = tid; r < R; r += NT) {
             float acc = 0.f;
