@@ -94,6 +94,31 @@ def kernel_work(w, kernel: str, k: int):
     return None, None
 
 
+RIDGE_FP32 = PEAK_FP32_MFMA / PEAK_HBM  # flop/B where the fp32 matrix and HBM roofs meet
+
+
+def chunk_kernel_bytes(w, kernel: str, k: int):
+    """Algorithmic HBM bytes of one launch of a chunk (matrix) kernel: every input it needs read
+    once and every output written once (io-dtype token rows, fp32 dt and chunk states, fp64
+    cumsums), for the roofline it is not bound by.  None for the other kernels."""
+    b, n, l, h, p, r = _shape(w, k)
+    ch = b * n * h
+    tok = ch * l
+    io = 2 if w.io == "bf16" else 4
+    st = 4 * p * r * ch                 # one fp32 [p, r] state per chunk-head
+    if kernel == "k_chunk_states":      # mean of the fwd launch (job 0) and the bwd one (jobs 0, 1)
+        job0 = tok * (io * (p + r) + 12) + st     # x, B, dt, cdt -> S
+        job1 = tok * (io * (p + r) + 8) + st      # dy, C, cdt -> dS
+        return (2 * job0 + job1) / 2
+    if kernel == "k5_chunk_scan":       # x, B, C, dt, cdt, S_in -> y
+        return tok * (io * (2 * p + 2 * r) + 12) + st
+    if kernel == "k_bwd_target":        # dy, x, B, C, dt, cdt, S_in, d_intra -> d_C, g1, d_end
+        return tok * (io * (2 * p + 3 * r) + 16) + 2 * st + 8 * ch
+    if kernel == "k_bwd_source":        # dy, x, B, C, dt, cdt, d_intra -> d_x, d_B, d_dt, g2, d_delta
+        return tok * (io * (3 * p + 3 * r) + 24) + st
+    return None
+
+
 def moments_kernel_work(w, kernel: str, k: int):
     """Algorithmic flops of one launch of a moments kernel (pairs over the whole chunk)."""
     b, n, l, h, p, r = _shape(w, k)
@@ -435,8 +460,14 @@ def bench_ssd(w, inp, args, layout=True, steps=None, warmup=None):
             rate = work / (avg / 1e3)
             if kind == "flop":
                 ent.update(tflops=round(rate / 1e12, 2), mfma_frac=round(rate / PEAK_FP32_MFMA, 4))
+                nbytes = chunk_kernel_bytes(w, name, k)
+                if nbytes:
+                    # both roofs, and the one that binds: arithmetic intensity against the fp32 ridge
+                    ent.update(gbps=round(nbytes / (avg / 1e3) / 1e9, 1),
+                               hbm_frac=round(nbytes / (avg / 1e3) / PEAK_HBM, 4),
+                               bound="mfma" if work / nbytes >= RIDGE_FP32 else "hbm")
             else:
-                ent.update(gbps=round(rate / 1e9, 1), hbm_frac=round(rate / PEAK_HBM, 4))
+                ent.update(gbps=round(rate / 1e9, 1), hbm_frac=round(rate / PEAK_HBM, 4), bound="hbm")
         kernels[name] = ent
     dom = max(kernels, key=lambda n: kernels[n]["avg_ms"] * kernels[n]["launches_per_step"])
     work, kind = kernel_work(w, dom, k)
@@ -477,7 +508,8 @@ def bench_other_workloads(args):
         res[name] = {"workload": w.describe(), "kernel_chunk_len": r["kernel_chunk_len"],
                      "ms_per_step": r["ms_per_step"], "value": r["value"], "unit": "tokens/s",
                      "roofline": r["roofline"],
-                     "kernels": {k: v.get("mfma_frac", v.get("hbm_frac")) for k, v in r["kernels"].items()}}
+                     "kernels": {k: {f: v[f] for f in ("mfma_frac", "hbm_frac", "bound") if f in v}
+                                 for k, v in r["kernels"].items()}}
     return res
 
 

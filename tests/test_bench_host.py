@@ -77,3 +77,20 @@ def test_step_bytes_count_every_tensor_once():
     bh = 64 * 80
     # state read + written in fp32; x, y (p each) and B, C (r each) in bf16; dt fp32
     assert bench.step_bytes(w) == bh * (8 * 64 * 128 + 2 * (2 * 64 + 2 * 128) + 4)
+
+
+def test_chunk_kernel_bytes_count_every_tensor_once():
+    """The matrix kernels' HBM bytes on the 130M-shaped workload at k = 128 (1536 chunk-heads,
+    196608 token-heads): each token row, dt, cumsum and chunk state once."""
+    w = inputs.WORKLOADS["mamba2_130m_fp32"]
+    tok, st = 196608, 4 * 64 * 128 * 1536
+    assert bench.chunk_kernel_bytes(w, "k5_chunk_scan", 128) == tok * (4 * (64 + 2 * 128) + 4 * 64 + 12) + st
+    assert bench.chunk_kernel_bytes(w, "k_bwd_source", 128) == tok * (4 * (2 * 64 + 2 * 128) + 4 * (64 + 128) + 24) + st
+    assert bench.chunk_kernel_bytes(w, "k_bwd_target", 128) == tok * (4 * (2 * 64 + 2 * 128) + 4 * 128 + 16) + 2 * st + 8 * 1536
+    job0 = tok * (4 * 192 + 12) + st
+    job1 = tok * (4 * 192 + 8) + st
+    assert bench.chunk_kernel_bytes(w, "k_chunk_states", 128) == (2 * job0 + job1) / 2
+    assert bench.chunk_kernel_bytes(w, "k4_state_pass", 128) is None
+    # bf16 io halves the token rows only
+    wb = inputs.Workload("b", 4, 2048, 24, 64, 128, 256, io="bf16")
+    assert bench.chunk_kernel_bytes(wb, "k5_chunk_scan", 128) == tok * (2 * (2 * 64 + 2 * 128) + 12) + st
