@@ -141,6 +141,24 @@ def method_flops(w, k):
     return (per_tok_fwd + per_tok_bwd) * b * n * l * h
 
 
+def host_cpu() -> dict:
+    """The host the oracle runs on: CPU model and the logical CPUs this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count()
+    return {"cpu_model": model, "logical_cpus": n}
+
+
 def cpu_baseline(w, inp, budget_s: float = 12.0, cap_s: float = 40.0):
     """Time the oracle (single-threaded fp64 C) on (batch, head) slices of the
     workload, in order, until about `budget_s` of CPU work; scale to full tokens/s."""
@@ -169,7 +187,7 @@ def cpu_baseline(w, inp, budget_s: float = 12.0, cap_s: float = 40.0):
     del torch
     token_heads_per_s = sl * seq / t_tot
     return {"value": token_heads_per_s / w.nheads, "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "host": host_cpu(),
             "sample": f"fwd+bwd of {sl} (batch, head) slice(s) x {seq} tokens of {w.name} "
                       f"in {t_tot:.1f} s; tokens/s = token-heads/s / {w.nheads} heads"}
 
@@ -565,6 +583,7 @@ def bench_moments(args):
     res = {"workload": {**w.describe(), "kernel_chunk_len": k}, "ms_per_step": round(ms, 4),
            "ms_per_step_with_kernel_events": round(ms_ev, 4),
            "value": round(w.batch * w.seq / (ms / 1e3), 1), "unit": "tokens/s",
+           "valid_tokens_per_s": round(sum(min(v, w.seq) for v in w.valid_len) / (ms / 1e3), 1),
            "step": "ssd_state_moments (with y) + ssd_state_moments_bwd", "kernels": kernels}
     res["pr"] = bench_pr(args, w, dims, m2, m1, count, stream)
 
@@ -604,7 +623,7 @@ def bench_moments(args):
                                  sl["x"], dt, A, sl["B"], None, list(w.valid_len))
         el = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": round(w.batch * w.seq / w.nheads / el, 2), "unit": "tokens/s",
-                               "cores": 1, "kind": "oracle",
+                               "cores": 1, "kind": "oracle", "host": host_cpu(),
                                "sample": f"moments fwd+bwd of head 0, all {w.batch} batches x {w.seq} "
                                          f"tokens in {el:.1f} s; tokens/s = token-heads/s / {w.nheads} heads"}
     return res
