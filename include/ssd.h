@@ -88,7 +88,8 @@ enum ssd_status {
     SSD_ERR_UNSUPPORTED = 3, /* shape or alignment outside the supported set above */
     SSD_ERR_DTYPE = 4,       /* io_dtype not SSD_F32 / SSD_BF16 */
     SSD_ERR_WORKSPACE = 5,   /* ws_bytes smaller than ssd_workspace_size(), or ws NULL */
-    SSD_ERR_HIP = 6          /* a HIP launch failed (message names the kernel) */
+    SSD_ERR_HIP = 6,         /* a HIP launch failed (message names the kernel) */
+    SSD_ERR_NONFINITE = 7    /* debug mode only: an output holds a NaN or an infinity */
 };
 
 enum ssd_op { SSD_OP_FWD = 0, SSD_OP_BWD = 1, SSD_OP_MOMENTS = 2, SSD_OP_MOMENTS_BWD = 3 };
@@ -295,6 +296,18 @@ int ssd_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, int
 
 /* Message for the last nonzero status returned on this thread ("" if none). */
 const char* ssd_last_error(void);
+
+/*
+ * Debug mode (off by default; a process-wide switch).  While it is on, ssd_fwd,
+ * ssd_bwd, ssd_state_moments and ssd_state_moments_bwd end by scanning every output
+ * they wrote for a NaN or an infinity, which synchronises `stream`, and return
+ * SSD_ERR_NONFINITE (ssd_last_error() names the first such output) instead of 0.
+ * The outputs are written as usual.  Not for code under HIP graph capture (the
+ * check synchronises); the scan keeps one flag word per output in a small static
+ * device array, so calls that overlap on one GPU in debug mode may report each
+ * other's outputs.  Returns 0.
+ */
+int ssd_debug_enable(int on);
 
 /*
  * Benchmark instrumentation (not part of the computation).  While enabled, every

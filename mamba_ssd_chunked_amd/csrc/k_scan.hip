@@ -424,4 +424,56 @@ hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStrea
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ debug checks
+// One flag word per checked tensor (a file-scope device array; each GPU has its own
+// copy, found with hipGetSymbolAddress).  The scan stores 1 into its word when it meets
+// a NaN or an infinity: plain stores of one value, so concurrent finds need no atomics.
+constexpr int kMaxChecked = 16;
+static __device__ int g_nonfinite[kMaxChecked];
+
+__global__ void k_clear_flags(int* __restrict__ f, int n) {
+    if (static_cast<int>(threadIdx.x) < n) f[threadIdx.x] = 0;
+}
+
+__global__ __launch_bounds__(NT) void k_nonfinite(const void* __restrict__ p, int64_t n, int bf16,
+                                                  int* __restrict__ flag) {
+    bool bad = false;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * NT) {
+        const uint32_t e = bf16 ? (static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16)
+                                : static_cast<const uint32_t*>(p)[i];
+        bad |= (e & 0x7f800000u) == 0x7f800000u;  // exponent all ones: infinity or NaN
+    }
+    if (bad) *flag = 1;
+}
+
+hipError_t nonfinite_flags(int** flags) {
+    static int* addr[64] = {nullptr};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!addr[dev]) {
+        void* a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(g_nonfinite));
+        if (e != hipSuccess) return e;
+        addr[dev] = static_cast<int*>(a);
+    }
+    *flags = addr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_clear_flags(int* flags, int n, hipStream_t st) {
+    hipLaunchKernelGGL(k_clear_flags, dim3(1), dim3(64), 0, st, flags, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_nonfinite(const void* p, int64_t n, bool bf16, int* flag, hipStream_t st) {
+    if (n <= 0 || !p) return hipSuccess;
+    const int64_t want = (n + NT - 1) / NT;
+    const unsigned grid = static_cast<unsigned>(want < 4096 ? want : 4096);
+    hipLaunchKernelGGL(k_nonfinite, dim3(grid), dim3(NT), 0, st, p, n, bf16 ? 1 : 0, flag);
+    return hipGetLastError();
+}
+
 }  // namespace ssd

@@ -6,6 +6,7 @@
 // synchronising.  The workspace is caller-owned; the library allocates nothing.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -225,6 +226,39 @@ hipError_t timed(const char* name, hipStream_t st, F&& launch) {
             return fail(SSD_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e_)); \
     } while (0)
 
+// Debug mode (ssd_debug_enable): after an entry point's work, scan its outputs for NaN or
+// infinity (a stream synchronisation).
+std::atomic<bool> g_debug{false};
+
+struct Checked {
+    const void* p;
+    int64_t n;
+    bool bf16;
+    const char* name;
+};
+
+int check_outputs(hipStream_t st, const char* where, std::initializer_list<Checked> outs) {
+    int* flags = nullptr;
+    hipError_t e = ssd::nonfinite_flags(&flags);
+    const char* names[16];
+    int n = 0;
+    if (e == hipSuccess) e = ssd::launch_clear_flags(flags, 16, st);
+    for (const Checked& o : outs) {
+        if (e != hipSuccess || n == 16) break;
+        if (!o.p || o.n <= 0) continue;
+        e = ssd::launch_nonfinite(o.p, o.n, o.bf16, flags + n, st);
+        names[n++] = o.name;
+    }
+    int host[16] = {0};
+    if (e == hipSuccess && n > 0) e = hipMemcpyAsync(host, flags, sizeof(int) * n, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess)
+        return fail(SSD_ERR_HIP, "%s: output check failed: %s", where, hipGetErrorString(e));
+    for (int k = 0; k < n; ++k)
+        if (host[k]) return fail(SSD_ERR_NONFINITE, "%s: %s holds a NaN or an infinity", where, names[k]);
+    return SSD_OK;
+}
+
 int check_ws(const ssd::Shape& s, int op, void* ws, size_t ws_bytes) {
     const size_t need = plan(s, op).total;
     if (need > 0 && (!ws || ws_bytes < need))
@@ -339,6 +373,11 @@ extern "C" {
 
 const char* ssd_last_error(void) { return g_err; }
 
+int ssd_debug_enable(int on) {
+    g_debug = on != 0;
+    return ok();
+}
+
 int ssd_timing_enable(int on) {
     std::lock_guard<std::mutex> lk(g_tm);
     g_timing = on != 0;
@@ -425,6 +464,12 @@ int ssd_fwd(const ssd_dims* dims, const void* x, const float* dt, const float* A
             "k_chunk_states");
     SSD_HIP(ssd::launch_k4_pass(s, S, cdt, A, init, final_state, st), "k4_state_pass");
     SSD_HIP(ssd::launch_k5_scan(s, x, dt, B, C, A, D, cdt, S, y, st), "k5_chunk_scan");
+    if (g_debug) {
+        const bool bf = s.io == SSD_BF16;
+        const int64_t tp = static_cast<int64_t>(s.B) * s.N * s.L * s.H * s.P;
+        if (int rc = check_outputs(st, "ssd_fwd", {{y, tp, bf, "y"}, {final_state, nstate, false, "final_state"}}))
+            return rc;
+    }
     return ok();
 }
 
@@ -471,6 +516,15 @@ int ssd_bwd(const ssd_dims* dims, const void* dy, const float* d_final, const vo
             "k_bwd_source");
     SSD_HIP(ssd::launch_k1t_heads(s, g1, g2, dlt, dend, A, d_dt, dAT, dAS, dDp, s.nblk(), d_A, d_D, st),
             "k1t_revcumsum");
+    if (g_debug) {
+        const bool bf = s.io == SSD_BF16;
+        const int64_t tk = static_cast<int64_t>(s.B) * s.N * s.L * s.H;
+        if (int rc = check_outputs(st, "ssd_bwd",
+                                   {{d_x, tk * s.P, bf, "d_x"}, {d_dt, tk, false, "d_dt"}, {d_A, s.H, false, "d_A"},
+                                    {d_B, tk * s.R, bf, "d_B"}, {d_C, tk * s.R, bf, "d_C"}, {d_D, s.H, false, "d_D"},
+                                    {d_init, nstate, false, "d_init"}}))
+            return rc;
+    }
     return ok();
 }
 
@@ -527,6 +581,14 @@ int ssd_state_moments(const ssd_dims* dims, const void* x, const float* dt, cons
                                   at<float>(ws, w.m1c), m2, m1, st),
             "km_reduce");
     if (y) SSD_HIP(ssd::launch_k5_scan(s, x, dt, B, C, A, D, cdt, S, y, st), "k5_chunk_scan");
+    if (g_debug) {
+        const int64_t bh = static_cast<int64_t>(s.B) * s.H;
+        const int64_t tp = static_cast<int64_t>(s.B) * s.N * s.L * s.H * s.P;
+        if (int rc = check_outputs(st, "ssd_state_moments",
+                                   {{m2, bh * s.R * s.R, false, "m2"}, {m1, bh * s.R, false, "m1"},
+                                    {y, tp, s.io == SSD_BF16, "y"}, {final_state, nstate, false, "final_state"}}))
+            return rc;
+    }
     return ok();
 }
 
@@ -596,6 +658,14 @@ int ssd_state_moments_bwd(const ssd_dims* dims, const float* d_m2, const float* 
     SSD_HIP(ssd::launch_km_scan_bwd(s, cdt, dt, A, vd, ddtW, rho, eta, zeta, hsh, hdm, dend2, d_dt, st),
             "km_scan_bwd");
     SSD_HIP(ssd::launch_reduce_heads(s, dA, nullptr, nullptr, s.nblk(), d_A, nullptr, st), "reduce_heads");
+    if (g_debug) {
+        const bool bf = s.io == SSD_BF16;
+        const int64_t tk = static_cast<int64_t>(s.B) * s.N * s.L * s.H;
+        if (int rc = check_outputs(st, "ssd_state_moments_bwd",
+                                   {{d_x, tk * s.P, bf, "d_x"}, {d_dt, tk, false, "d_dt"}, {d_A, s.H, false, "d_A"},
+                                    {d_B, tk * s.R, bf, "d_B"}, {d_init, nstate, false, "d_init"}}))
+            return rc;
+    }
     return ok();
 }
 

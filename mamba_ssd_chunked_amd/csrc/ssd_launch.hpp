@@ -131,6 +131,12 @@ hipError_t launch_reduce_heads(const Shape& s, const double* dA_part0, const dou
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t st);
 
 // dst[i] = (vals ? vals[i] : fill) for i < n; the values travel as kernel arguments.
+// Debug checks: the device's flag words (kMaxChecked of them), clearing them, and a
+// scan that sets *flag when n floats (or bf16 values) at p hold a NaN or an infinity.
+hipError_t nonfinite_flags(int** flags);
+hipError_t launch_clear_flags(int* flags, int n, hipStream_t st);
+hipError_t launch_nonfinite(const void* p, int64_t n, bool bf16, int* flag, hipStream_t st);
+
 hipError_t launch_set_i64(int64_t* dst, const int64_t* vals, int64_t fill, int64_t n, hipStream_t st);
 
 // ------------------------------------------------------ participation ratio

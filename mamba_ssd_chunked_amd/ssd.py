@@ -27,11 +27,12 @@ LIB_PATH = os.path.join(_PKG, "_build", "libmamba_ssd_hip.so")
 SSD_F32, SSD_BF16 = 0, 1
 SSD_OP_FWD, SSD_OP_BWD, SSD_OP_MOMENTS, SSD_OP_MOMENTS_BWD = 0, 1, 2, 3
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
-          4: "SSD_ERR_DTYPE", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_HIP"}
+          4: "SSD_ERR_DTYPE", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_HIP", 7: "SSD_ERR_NONFINITE"}
 EXPORTS = ("ssd_workspace_size", "ssd_fwd", "ssd_bwd", "ssd_state_moments",
            "ssd_state_moments_bwd", "ssd_moments_pr", "ssd_moments_pr_bwd", "ssd_y_diag",
            "ssd_y_diag_bwd", "ssd_quat_scan", "ssd_quat_scan_bwd", "ssd_quat_workspace_size",
-           "ssd_step", "ssd_last_error", "ssd_timing_enable", "ssd_timing_collect")
+           "ssd_step", "ssd_last_error", "ssd_debug_enable", "ssd_timing_enable",
+           "ssd_timing_collect")
 
 
 class ssd_dims(ctypes.Structure):
@@ -86,6 +87,8 @@ def load_library(path: str = LIB_PATH):
         getattr(lib, f).restype = ctypes.c_int
     lib.ssd_last_error.argtypes = []
     lib.ssd_last_error.restype = ctypes.c_char_p
+    lib.ssd_debug_enable.argtypes = [ctypes.c_int]
+    lib.ssd_debug_enable.restype = ctypes.c_int
     lib.ssd_timing_enable.argtypes = [ctypes.c_int]
     lib.ssd_timing_enable.restype = ctypes.c_int
     lib.ssd_timing_collect.argtypes = [ctypes.c_int, ctypes.c_char_p, ctypes.c_size_t,
@@ -160,6 +163,12 @@ def _stream(stream) -> ctypes.c_void_p:
 # ------------------------------------------------------------ C-named functions
 def ssd_last_error() -> str:
     return load_library().ssd_last_error().decode()
+
+
+def ssd_debug_enable(on: bool) -> int:
+    """Debug mode: the SSD and moments entry points check their outputs for NaN / inf
+    (synchronising) and return SSD_ERR_NONFINITE when they find one."""
+    return load_library().ssd_debug_enable(1 if on else 0)
 
 
 def ssd_timing_enable(on: bool) -> int:

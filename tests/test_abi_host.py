@@ -261,3 +261,10 @@ def test_step_rejects_bad_arguments(lib, case, code):
 
 def test_step_of_an_empty_batch_is_a_no_op(lib):
     assert lib.ssd_step(0, 3, 64, 128, 0, *([None] * 10)) == 0
+
+
+def test_debug_switch_is_host_only(lib):
+    """ssd_debug_enable only flips a host flag (no device call): it works without a GPU."""
+    assert lib.ssd_debug_enable(1) == 0
+    assert lib.ssd_debug_enable(0) == 0
+    assert ssd.STATUS[7] == "SSD_ERR_NONFINITE"
