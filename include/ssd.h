@@ -42,6 +42,14 @@
  *    {16, 32, 64, 128}; batch >= 0, nchunks >= 0 (an empty sequence is valid:
  *    final = init, d_init = d_final, d_A = d_D = 0).  Tensor pointers must be
  *    16-byte aligned (8-byte for bf16 tensors).
+ *  - Size limit: one launch holds at most 2^32 - 1 work-items along x (the
+ *    dispatch packet's grid size is 32 bits).  Every entry point rejects with
+ *    SSD_ERR_UNSUPPORTED a problem whose largest launch would exceed that: for
+ *    the chunked entry points batch * nheads * max(4 * nchunks * chunk_len,
+ *    headdim * dstate, dstate^2) < 2^32; for ssd_y_diag 16 * ntokens * nheads;
+ *    for ssd_step and ssd_moments_pr 256 * batch * nheads; for the quaternion
+ *    scan 256 per (batch, 64 quaternions of a row, 64 steps).  Larger problems
+ *    are split by the caller (over batch or heads, which are independent).
  *  - kernel_chunk_len: the chunked algorithm is an exact re-association of the
  *    recurrence above for every chunk length, so the kernels may run it at a
  *    shorter chunk than the caller's layout: the [b, n, l, ...] buffers are the
@@ -175,7 +183,7 @@ int ssd_state_moments_bwd(const ssd_dims* dims, const float* d_m2, const float* 
  *   trace  [b,h]     out, fp32, nullable (not written when NULL)
  * Sums and Sigma are formed in fp64; results are rounded to fp32 once.
  * Errors: SSD_ERR_NULL, SSD_ERR_SHAPE (a dimension out of range, count <= 0),
- * SSD_ERR_UNSUPPORTED (dstate, alignment), SSD_ERR_HIP.  No workspace.
+ * SSD_ERR_UNSUPPORTED (dstate, alignment, size limit), SSD_ERR_HIP.  No workspace.
  */
 int ssd_moments_pr(int64_t batch, int64_t nheads, int64_t dstate, const float* m2,
                    const float* m1, const int64_t* count, int center, float* pr, float* trace,

@@ -6,6 +6,7 @@
 // synchronising.  The workspace is caller-owned; the library allocates nothing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdint>
@@ -56,13 +57,18 @@ int validate_dims(const ssd_dims* d, ssd::Shape* s) {
     if (!pow2_in(d->headdim, 16, 128) || !pow2_in(d->dstate, 16, 128))
         return fail(SSD_ERR_UNSUPPORTED, "headdim and dstate must be 16, 32, 64 or 128 (got %lld, %lld)",
                     (long long)d->headdim, (long long)d->dstate);
-    // index arithmetic and grid limits
-    const double ch_blocks = (double)d->batch * (double)d->nchunks * (double)d->nheads *
-                             (double)(d->chunk_len / 64);
+    // index arithmetic and grid limits.  The largest grids: the per-64-token-block kernels
+    // (256 work-items per block, 4 per token-head), the state copies (one per state
+    // element, p r or r r per (b, h)) and the carry passes (a quarter or half of that).
+    const double bh = (double)d->batch * (double)d->nheads;
+    const double per_bh = std::max({4.0 * (double)d->nchunks * (double)d->chunk_len,
+                                    (double)d->headdim * d->dstate, (double)d->dstate * d->dstate});
     const double elems = (double)d->batch * d->nchunks * d->chunk_len * d->nheads * 128.0;
-    if (ch_blocks > 2.0e9 || elems > 4.0e18 || d->nchunks > (1 << 30) || d->nheads > (1 << 30) ||
-        d->batch > (1 << 30))
-        return fail(SSD_ERR_UNSUPPORTED, "problem too large for one call (split the batch)");
+    if (bh * per_bh > ssd::kMaxGridItems || elems > 4.0e18 || d->nchunks > (1 << 30) ||
+        d->nheads > (1 << 30) || d->batch > (1 << 30))
+        return fail(SSD_ERR_UNSUPPORTED,
+                    "problem too large for one call: a launch would exceed 2^32 work-items "
+                    "(split the batch or the heads)");
     // The kernels run the chunked algorithm at chunk length k (a divisor of chunk_len):
     // the caller's [b, n, l, ...] buffers are the same memory as [b, n l / k, k, ...].
     const int64_t k = d->kernel_chunk_len == 0 ? (d->chunk_len < 128 ? d->chunk_len : 128)
@@ -283,10 +289,14 @@ int check_io_ptrs(const ssd::Shape& s, std::initializer_list<std::pair<const voi
 int validate_pr(const char* who, int64_t batch, int64_t nheads, int64_t dstate, const float* m2,
                 const float* m1, const int64_t* count, int center, const void* out,
                 const void* out16) {
-    if (batch < 0 || nheads <= 0 || batch > (1 << 30) || nheads > (1 << 30) ||
-        batch * nheads > (int64_t(1) << 31) - 1)
-        return fail(SSD_ERR_SHAPE, "%s: need 0 <= batch, 0 < nheads and batch * nheads < 2^31 "
-                    "(got %lld, %lld)", who, (long long)batch, (long long)nheads);
+    if (batch < 0 || nheads <= 0)
+        return fail(SSD_ERR_SHAPE, "%s: need 0 <= batch and 0 < nheads (got %lld, %lld)", who,
+                    (long long)batch, (long long)nheads);
+    // one workgroup of at most 256 work-items per (b, h)
+    if (batch > (1 << 30) || nheads > (1 << 30) ||
+        (double)batch * nheads * 256.0 > ssd::kMaxGridItems)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: problem too large for one call: a launch would exceed "
+                    "2^32 work-items (split the batch)", who);
     if (!pow2_in(dstate, 16, 128))
         return fail(SSD_ERR_UNSUPPORTED, "%s: dstate must be 16, 32, 64 or 128 (got %lld)", who,
                     (long long)dstate);
@@ -320,9 +330,11 @@ int validate_diag(const char* who, int64_t ntokens, int64_t mimo_rank, int64_t n
     if (!pow2_in(headdim, 16, 128) || !pow2_in(dstate, 16, 128))
         return fail(SSD_ERR_UNSUPPORTED, "%s: headdim and dstate must be 16, 32, 64 or 128 "
                     "(got %lld, %lld)", who, (long long)headdim, (long long)dstate);
-    if (nheads > (1 << 30) || (double)ntokens * (double)nheads * 16.0 > 2.0e11 ||
+    // the backward launches 16 work-items per (token, head)
+    if (nheads > (1 << 30) || (double)ntokens * (double)nheads * 16.0 > ssd::kMaxGridItems ||
         (double)ntokens * mimo_rank * nheads * 128.0 > 4.0e18)
-        return fail(SSD_ERR_UNSUPPORTED, "%s: problem too large for one call (split the tokens)", who);
+        return fail(SSD_ERR_UNSUPPORTED, "%s: problem too large for one call: a launch would "
+                    "exceed 2^32 work-items (split the tokens)", who);
     d->T = ntokens;
     d->M = (int)mimo_rank;
     d->H = (int)nheads;
@@ -352,8 +364,10 @@ int validate_quat(const char* who, int64_t batch, int64_t seq, int64_t nheads, i
         (double)batch * seq * lanes * 4.0 > 4.0e18)
         return fail(SSD_ERR_UNSUPPORTED, "%s: problem too large for one call", who);
     *s = ssd::quat_shape(batch, seq, nheads, nquat);
-    if ((double)s->B * s->G * s->nseg > 2.0e9)
-        return fail(SSD_ERR_UNSUPPORTED, "%s: problem too large for one call (split the batch)", who);
+    // one workgroup of 256 work-items per (b, 64-lane group, segment)
+    if ((double)s->B * s->G * s->nseg * 256.0 > ssd::kMaxGridItems)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: problem too large for one call: a launch would "
+                    "exceed 2^32 work-items (split the batch)", who);
     return SSD_OK;
 }
 
@@ -804,8 +818,11 @@ int ssd_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, int
     if (!pow2_in(headdim, 16, 128) || !pow2_in(dstate, 16, 128))
         return fail(SSD_ERR_UNSUPPORTED, "ssd_step: headdim and dstate must be 16, 32, 64 or 128 "
                     "(got %lld, %lld)", (long long)headdim, (long long)dstate);
-    if (batch > (1 << 30) || nheads > (1 << 30) || (double)batch * nheads > 2.0e9)
-        return fail(SSD_ERR_UNSUPPORTED, "ssd_step: problem too large for one call (split the batch)");
+    // one workgroup of 256 work-items per (b, h)
+    if (batch > (1 << 30) || nheads > (1 << 30) ||
+        (double)batch * nheads * 256.0 > ssd::kMaxGridItems)
+        return fail(SSD_ERR_UNSUPPORTED, "ssd_step: problem too large for one call: a launch would "
+                    "exceed 2^32 work-items (split the batch)");
     if (batch == 0) return ok();
     if (!x || !dt || !A || !B || !C || !D || !state || !new_state || !y)
         return fail(SSD_ERR_NULL, "ssd_step: every pointer is required");

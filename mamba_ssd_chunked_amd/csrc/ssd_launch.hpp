@@ -6,6 +6,12 @@
 
 namespace ssd {
 
+// Work-items one launch may have along x: the AQL dispatch packet stores the grid
+// size in 32 bits.  No workgroup of the library has more than 256 work-items, so
+// an entry point that bounds its largest grid by this (less one workgroup for the
+// rounding up of block counts) never asks for a grid the packet cannot hold.
+constexpr double kMaxGridItems = 4294967295.0 - 256.0;
+
 struct Shape {
     int B, N, L, H, P, R;  // batch, nchunks, chunk_len, nheads, headdim, dstate
     int io;                // 0 = fp32, 1 = bf16

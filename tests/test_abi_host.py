@@ -268,3 +268,38 @@ def test_debug_switch_is_host_only(lib):
     assert lib.ssd_debug_enable(1) == 0
     assert lib.ssd_debug_enable(0) == 0
     assert ssd.STATUS[7] == "SSD_ERR_NONFINITE"
+
+
+# Every launch's grid must fit the 32-bit work-item count of a dispatch: each entry point
+# rejects, before any device call, a problem whose largest launch would not.
+@pytest.mark.parametrize("b,n,l,h,p,r,ok", [
+    (1, 1 << 12, 256, 1024, 16, 16, False),   # per-token-block kernels: 4 b h n l = 2^32
+    (1, 1 << 11, 256, 1024, 16, 16, True),    # 2^31
+    (1, 1, 64, 1 << 18, 128, 128, False),     # state copies: b h p r = 2^32
+    (1, 1, 64, 1 << 17, 128, 128, True),
+])
+def test_ssd_grid_size_limit(lib, b, n, l, h, p, r, ok):
+    d = dims(b=b, n=n, l=l, h=h, p=p, r=r)
+    out = ctypes.c_size_t(0)
+    for op in range(4):
+        rc = lib.ssd_workspace_size(ctypes.byref(d), op, ctypes.byref(out))
+        if ok:
+            assert rc == 0, ssd.ssd_last_error()
+        else:
+            assert rc == 3 and "2^32 work-items" in ssd.ssd_last_error()
+    if not ok:
+        assert lib.ssd_fwd(ctypes.byref(d), *([FAKE] * 10), 1 << 62, FAKE) == 3
+
+
+def test_other_entry_points_grid_size_limit(lib):
+    def rejected(rc):
+        return rc == 3 and "2^32 work-items" in ssd.ssd_last_error()
+    # y_diag: 16 work-items per (token, head)
+    assert rejected(lib.ssd_y_diag(1 << 28, 1, 1, 16, 16, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None))
+    assert rejected(lib.ssd_y_diag_bwd(1 << 28, 1, 1, 16, 16, 0, *([FAKE] * 9), None))
+    # quaternion scan: 256 per (batch, 64-lane group, 64-step segment)
+    assert rejected(lib.ssd_quat_scan(1, 1 << 20, 1 << 13, 8, FAKE, None, FAKE, FAKE, 1 << 62, None))
+    # decode step and participation ratio: 256 per (batch, head)
+    assert rejected(lib.ssd_step(1 << 12, 1 << 12, 16, 16, 0, *([FAKE] * 10)))
+    cnt = counts(1)
+    assert rejected(lib.ssd_moments_pr(1 << 12, 1 << 12, 16, FAKE, FAKE, cnt, 0, FAKE, None, None))
