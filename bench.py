@@ -2,17 +2,23 @@
 
 One step = ``ssd_fwd`` + ``ssd_bwd`` (K1-K5 forward, then the recompute
 backward) over one batch of the workload, inputs already resident in HBM.
-Prints ONE JSON line with tokens/s, the roofline of the dominant kernel
-(algorithmic work per launch / its mean duration, measured with HIP events on
-the launch stream during the timed region) and the CPU oracle timed on a
-bounded sample of the same workload.
+The headline workload is the largest one that fits one GPU: 65536 tokens x 32
+heads (p = 64, r = 128, fp32).  Prints ONE JSON line with tokens/s, the roofline
+of the dominant kernel (algorithmic work per launch / its mean duration,
+measured with HIP events on the launch stream during the timed region) and the
+CPU oracle timed on a bounded sample of the same workload, single-threaded and
+over all host cores.
 
-The kernels run the chunked algorithm at the library's automatic kernel chunk
-length (min(chunk_len, 128); the workload's chunk_len fixes the buffer layout);
-the same step with the kernels at the layout's chunk length is timed as well
-and reported under "at_layout_chunk_len".
+Warm-up: the --warmup steps, then more steps until at least --warmup-ms of GPU
+time has passed (the clocks take tens of milliseconds to settle); both counts
+are reported.  The kernels run the chunked algorithm at the library's automatic
+kernel chunk length (min(chunk_len, 128); the workload's chunk_len fixes the
+buffer layout); the same step with the kernels at the layout's chunk length is
+timed as well and reported under "at_layout_chunk_len".  The Mamba-2-130M- and
+2.7B-shaped workloads are timed the same way under "other_workloads".
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 30] [--workload mamba2_130m_fp32] [--graph]
+    python bench.py [--gpus 1] [--steps 30] [--warmup 10] [--warmup-ms 300]
+                    [--workload long_context_64k_fp32] [--graph]
 """
 from __future__ import annotations
 
@@ -27,7 +33,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SSD fwd+bwd tokens/s on 1 MI355X; % MFMA peak (GEMMs), % HBM BW (K1/K4)"
 PEAK_FP32_MFMA = 157.3e12   # FLOP/s, MI355X dense fp32 matrix
+PEAK_BF16_MFMA = 2.5e15     # FLOP/s, MI355X dense bf16 matrix
 PEAK_HBM = 8.0e12           # B/s
+HEADLINE = "long_context_64k_fp32"
 
 
 # HBM bytes per launch (read, write) of a kernel from two rocprofv3 --pmc runs (FETCH_SIZE,
@@ -65,6 +73,33 @@ def _shape(w, k):
     return w.batch, w.seq // k, k, w.nheads, w.headdim, w.dstate
 
 
+def matrix_flops(w, kernel: str, k: int):
+    """Algorithmic flops of ONE launch of a matrix kernel for workload w run at kernel chunk
+    length k, split by the matrix-core type that performs them: (fp32 flops, bf16 flops), or
+    None for a kernel without products.  Only the causal triangle counts (pairs s <= t of a
+    chunk).  With bf16 io the products whose two operands are both bf16 inputs -- C B^T and
+    dy x^T -- run on bf16 MFMAs; every product with an fp32 operand (states, decay-weighted
+    tiles, gradients) runs on fp32 ones."""
+    b, n, l, h, p, r = _shape(w, k)
+    ch = b * n * h                      # chunk-heads
+    pairs = l * (l + 1) // 2            # (t, s) pairs with s <= t per chunk
+    both_bf16 = w.io == "bf16"
+    cb, dw = 2 * pairs * r, 2 * pairs * p          # C B^T and dy x^T tiles
+    if kernel == "k_chunk_states":      # fwd: 1 job; bwd: 2 jobs (timed per launch: see jobs)
+        f32, bf = 2 * l * p * r, 0
+    elif kernel == "k5_chunk_scan":     # BLUE C S_in, C B^T, W x
+        f32, bf = 2 * l * p * r + 2 * pairs * p, cb
+    elif kernel == "k_bwd_target":      # BLUE dy S_in, C B^T, dy x^T, d_CB B
+        f32, bf = 2 * l * p * r + 2 * pairs * r, cb + dw
+    elif kernel == "k_bwd_source":      # K3 (two products), C B^T, dy x^T, W^T dy, d_CB^T C
+        f32, bf = 4 * l * p * r + 2 * pairs * p + 2 * pairs * r, cb + dw
+    else:
+        return None
+    if not both_bf16:
+        f32, bf = f32 + bf, 0
+    return f32 * ch, bf * ch
+
+
 def kernel_work(w, kernel: str, k: int):
     """Algorithmic work of ONE launch of `kernel` for workload w run at kernel chunk
     length k: (amount, kind).
@@ -74,15 +109,9 @@ def kernel_work(w, kernel: str, k: int):
     b, n, l, h, p, r = _shape(w, k)
     ch = b * n * h                      # chunk-heads
     tok = ch * l                        # token-heads
-    pairs = l * (l + 1) // 2            # (t, s) pairs with s <= t per chunk
-    if kernel == "k_chunk_states":      # fwd: 1 job; bwd: 2 jobs (timed per launch: see jobs)
-        return 2 * l * p * r * ch, "flop"
-    if kernel == "k5_chunk_scan":
-        return (2 * l * p * r + 2 * pairs * r + 2 * pairs * p) * ch, "flop"
-    if kernel == "k_bwd_target":
-        return (2 * l * p * r + 2 * pairs * r + 2 * pairs * p + 2 * pairs * r) * ch, "flop"
-    if kernel == "k_bwd_source":
-        return (4 * l * p * r + 2 * pairs * r + 2 * pairs * p + 2 * pairs * p + 2 * pairs * r) * ch, "flop"
+    mf = matrix_flops(w, kernel, k)
+    if mf is not None:
+        return mf[0] + mf[1], "flop"
     if kernel == "k1_cumsum":
         return 12 * tok + 4 * h, "byte"
     if kernel == "k4_state_pass":
@@ -92,6 +121,13 @@ def kernel_work(w, kernel: str, k: int):
     if kernel == "k1t_revcumsum":       # with the per-head d_A / d_D sums in the same launch
         return 24 * tok + 8 * ch + 24 * ch * (l // 64) + 8 * h, "byte"
     return None, None
+
+
+def mfma_roof_s(w, kernel: str, k: int, launches: float = 1.0):
+    """Seconds the matrix cores need at their dense peaks for `launches` launches of a
+    matrix kernel: fp32 flops at the fp32 peak plus bf16 flops at the bf16 peak."""
+    f32, bf = matrix_flops(w, kernel, k)
+    return launches * (f32 / PEAK_FP32_MFMA + bf / PEAK_BF16_MFMA)
 
 
 RIDGE_FP32 = PEAK_FP32_MFMA / PEAK_HBM  # flop/B where the fp32 matrix and HBM roofs meet
@@ -159,41 +195,66 @@ def host_cpu() -> dict:
     return {"cpu_model": model, "logical_cpus": n}
 
 
-def cpu_baseline(w, inp, budget_s: float = 12.0, cap_s: float = 40.0):
-    """Time the oracle (single-threaded fp64 C) on (batch, head) slices of the
-    workload, in order, until about `budget_s` of CPU work; scale to full tokens/s."""
+def _oracle_slice(inp, b: int, h: int):
+    """fp64 numpy arrays of the (batch b, head h) slice of the workload's inputs."""
+    sl = lambda k: inp[k][b:b + 1, :, :, h:h + 1].double().numpy()  # noqa: E731
+    return dict(x=sl("x"), dy=sl("dy"), B=sl("B"), C=sl("C"),
+                dt=inp["dt"][b:b + 1, h:h + 1].double().numpy(),
+                A=inp["A"][h:h + 1].double().numpy(), D=inp["D"][h:h + 1].double().numpy(),
+                init=inp["init"][b:b + 1, h:h + 1].double().numpy())
+
+
+def _oracle_fwd_bwd(a):
     import oracle
-    import torch
-    seq = w.seq
-    sl = 0
-    t_tot = 0.0
-    for k in range(w.batch * w.nheads):
-        bs, hs = [k // w.nheads], [k % w.nheads]
-        x = inp["x"][bs][:, :, :, hs].double().numpy()
-        dy = inp["dy"][bs][:, :, :, hs].double().numpy()
-        B = inp["B"][bs][:, :, :, hs].double().numpy()
-        C = inp["C"][bs][:, :, :, hs].double().numpy()
-        dt = inp["dt"][bs][:, hs].double().numpy()
-        A = inp["A"][hs].double().numpy()
-        D = inp["D"][hs].double().numpy()
-        init = inp["init"][bs][:, hs].double().numpy()
+    oracle.ssd_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["init"])
+    oracle.ssd_bwd(a["dy"], None, a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["init"])
+
+
+def cpu_baseline(w, inp, budget_s: float = 10.0):
+    """The oracle (plain fp64 C, one (batch, head) slice per call) on the workload's own
+    slices, scaled to whole-workload tokens/s (token-heads/s / heads):
+      * single-threaded: slices in order until about `budget_s` of CPU time (the baseline);
+      * all host cores: one thread per logical CPU (ctypes releases the GIL during the
+        oracle's C calls), two slices per thread, wall time of the whole pool."""
+    import concurrent.futures
+    host = host_cpu()
+    nslices = w.batch * w.nheads
+    order = [(k // w.nheads, k % w.nheads) for k in range(nslices)]
+    done, t_tot = 0, 0.0
+    for b, h in order:
+        a = _oracle_slice(inp, b, h)
         t0 = time.perf_counter()
-        oracle.ssd_fwd(x, dt, A, B, C, D, init)
-        oracle.ssd_bwd(dy, None, x, dt, A, B, C, D, init)
+        _oracle_fwd_bwd(a)
         t_tot += time.perf_counter() - t0
-        sl += 1
-        if t_tot >= budget_s or t_tot >= cap_s:
+        done += 1
+        if t_tot >= budget_s:
             break
-    del torch
-    token_heads_per_s = sl * seq / t_tot
-    return {"value": token_heads_per_s / w.nheads, "unit": "tokens/s", "cores": 1,
-            "kind": "oracle", "host": host_cpu(),
-            "sample": f"fwd+bwd of {sl} (batch, head) slice(s) x {seq} tokens of {w.name} "
-                      f"in {t_tot:.1f} s; tokens/s = token-heads/s / {w.nheads} heads"}
+    one = done * w.seq / t_tot / w.nheads
+    res = {"value": round(one, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle", "host": host,
+           "sample": f"fwd+bwd of {done} (batch, head) slice(s) x {w.seq} tokens of {w.name}, one "
+                     f"thread, in {t_tot:.1f} s; tokens/s = token-heads/s / {w.nheads} heads"}
+    threads = max(1, min(host["logical_cpus"] or 1, nslices))
+    m = min(nslices, 2 * threads)
+    sl = [_oracle_slice(inp, b, h) for b, h in order[:m]]
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(_oracle_fwd_bwd, sl))
+    el = time.perf_counter() - t0
+    del sl
+    res["all_cores"] = {
+        "value": round(m * w.seq / el / w.nheads, 2), "unit": "tokens/s", "cores": threads,
+        "kind": "oracle", "nproc": host["logical_cpus"],
+        "sample": f"fwd+bwd of {m} (batch, head) slices x {w.seq} tokens of {w.name} on "
+                  f"{threads} threads in {el:.1f} s wall; tokens/s = token-heads/s / {w.nheads} heads"}
+    return res
+
+
+WARMUP_DONE: dict = {}  # warm-up of the last timed_regions call: steps run, wall ms
 
 
 def timed_regions(step, args, stream):
-    """W warm-up steps, then K steps timed with torch events on the launch stream,
+    """W warm-up steps (then more until --warmup-ms of GPU time has passed), then K steps
+    timed with torch events on the launch stream,
     bracketed by device synchronisations -> ms per step (with --graph: K replays of the
     step captured once into a HIP graph; the library neither allocates nor
     synchronises, so capture needs nothing else); then K steps with the library's
@@ -201,9 +262,24 @@ def timed_regions(step, args, stream):
     per-kernel events sit between launches, so they are kept out of the first region."""
     import torch
     from mamba_ssd_chunked_amd import ssd
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    n_warm = args.warmup
+    # keep warming until the GPU has run at least --warmup-ms (whole batches of steps
+    # between synchronisations, sized from the rate so far)
+    min_ms = getattr(args, "warmup_ms", 0.0)
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        el = (time.perf_counter() - t0) * 1e3
+        per = el / max(n_warm, 1)
+        more = max(1, min(1000, int((min_ms - el) / max(per, 1e-3)) + 1))
+        for _ in range(more):
+            step()
+        torch.cuda.synchronize()
+        n_warm += more
+    WARMUP_DONE.update(steps=n_warm, ms=round((time.perf_counter() - t0) * 1e3, 1))
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def region(run):
@@ -435,7 +511,8 @@ def bench_ssd(w, inp, args, layout=True, steps=None, warmup=None):
     import torch
     from mamba_ssd_chunked_amd import ssd
     dev = torch.device("cuda", 0)
-    targs = _ap.Namespace(steps=steps or args.steps, warmup=warmup or args.warmup, graph=args.graph)
+    targs = _ap.Namespace(steps=steps or args.steps, warmup=warmup or args.warmup, graph=args.graph,
+                          warmup_ms=args.warmup_ms)
     d = {k: v.to(dev) for k, v in inp.items() if isinstance(v, torch.Tensor) and k != "valid_len"}
     init = d["init"] if w.init_std > 0 else None
     y = torch.empty_like(d["x"])
@@ -466,42 +543,56 @@ def bench_ssd(w, inp, args, layout=True, steps=None, warmup=None):
     ms, ms_ev, kt = timed_regions(make_step(args.kernel_chunk_len), targs, stream)
     tokens = w.batch * w.seq
 
+    warm = dict(WARMUP_DONE)
     kernels = {}
     for name, (tot, cnt) in kt.items():
         avg = tot / cnt
         work, kind = kernel_work(w, name, k)
         ent = {"avg_ms": round(avg, 5), "launches_per_step": cnt / targs.steps}
+        jobs = 1.5 if name == "k_chunk_states" else 1.0
         if name == "k_chunk_states":
             # launched once in ssd_fwd (1 job) and once in ssd_bwd (2 jobs): average work
-            work = work * 1.5
+            work = work * jobs
         if work is not None:
-            rate = work / (avg / 1e3)
             if kind == "flop":
-                ent.update(tflops=round(rate / 1e12, 2), mfma_frac=round(rate / PEAK_FP32_MFMA, 4))
+                # matrix roof: fp32 flops at the fp32 peak + bf16 flops at the bf16 peak;
+                # HBM roof: each input read once, each output written once
+                roof_s = mfma_roof_s(w, name, k, jobs)
                 nbytes = chunk_kernel_bytes(w, name, k)
+                ent.update(tflops=round(work / (avg / 1e3) / 1e12, 2),
+                           mfma_frac=round(roof_s / (avg / 1e3), 4))
                 if nbytes:
-                    # both roofs, and the one that binds: arithmetic intensity against the fp32 ridge
+                    hbm_s = nbytes / PEAK_HBM
                     ent.update(gbps=round(nbytes / (avg / 1e3) / 1e9, 1),
-                               hbm_frac=round(nbytes / (avg / 1e3) / PEAK_HBM, 4),
-                               bound="mfma" if work / nbytes >= RIDGE_FP32 else "hbm")
+                               hbm_frac=round(hbm_s / (avg / 1e3), 4),
+                               bound="mfma" if roof_s >= hbm_s else "hbm")
+                if w.io == "bf16":
+                    f32, bf = matrix_flops(w, name, k)
+                    ent.update(fp32_mfma_gflop=round(jobs * f32 / 1e9, 2),
+                               bf16_mfma_gflop=round(jobs * bf / 1e9, 2))
             else:
+                rate = work / (avg / 1e3)
                 ent.update(gbps=round(rate / 1e9, 1), hbm_frac=round(rate / PEAK_HBM, 4), bound="hbm")
         kernels[name] = ent
     dom = max(kernels, key=lambda n: kernels[n]["avg_ms"] * kernels[n]["launches_per_step"])
     work, kind = kernel_work(w, dom, k)
     davg = kernels[dom]["avg_ms"]
-    if kind == "flop":
+    if kind == "flop" and kernels[dom].get("bound", "mfma") == "mfma":
+        roof_s = mfma_roof_s(w, dom, k)
         ach = work / (davg / 1e3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 3), "peak": 157.3,
-                "unit": "TFLOP/s", "frac": round(ach / 157.3, 4),
+        peak = work / roof_s / 1e12   # the fp32 peak; with bf16 io the flop mix's peak
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 3), "peak": round(peak, 1),
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                 "traffic": measured_traffic(dom, w, k)}
     else:
-        ach = work / (davg / 1e3) / 1e9
+        nbytes = work if kind == "byte" else chunk_kernel_bytes(w, dom, k)
+        ach = nbytes / (davg / 1e3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": 8000.0,
                 "unit": "GB/s", "frac": round(ach / 8000.0, 4),
                 "traffic": measured_traffic(dom, w, k)}
     res = {"value": round(tokens / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
            "ms_per_step_with_kernel_events": round(ms_ev, 4), "kernel_chunk_len": k,
+           "warmup_steps_run": warm.get("steps"), "warmup_ms_run": warm.get("ms"),
            "roofline": roof, "method_tflops": round(method_flops(w, k) / (ms / 1e3) / 1e12, 3),
            "kernels": kernels}
     if layout and k != w.chunk_len:
@@ -514,20 +605,21 @@ def bench_ssd(w, inp, args, layout=True, steps=None, warmup=None):
 
 
 def bench_other_workloads(args):
-    """The SSD step on the other full-size workloads (bf16 2.7B-shaped, 64k tokens), fewer steps."""
+    """The SSD step on the other full-size SSD workloads (the Mamba-2-130M- and 2.7B-shaped
+    ones, or the 64k-token one when another workload is the headline), same step counts."""
     from mamba_ssd_chunked_amd import inputs
     res = {}
-    for name in ("mamba2_2p7b_bf16", "long_context_64k_fp32"):
+    for name in ("mamba2_130m_fp32", "mamba2_2p7b_bf16", "long_context_64k_fp32"):
         if name == args.workload:
             continue
         w = inputs.WORKLOADS[name]
-        r = bench_ssd(w, inputs.make_inputs(w), args, layout=False, steps=min(args.steps, 10),
-                      warmup=min(args.warmup, 5))
+        r = bench_ssd(w, inputs.make_inputs(w), args, layout=False)
         res[name] = {"workload": w.describe(), "kernel_chunk_len": r["kernel_chunk_len"],
+                     "steps": args.steps, "warmup_steps_run": r["warmup_steps_run"],
+                     "warmup_ms_run": r["warmup_ms_run"],
                      "ms_per_step": r["ms_per_step"], "value": r["value"], "unit": "tokens/s",
-                     "roofline": r["roofline"],
-                     "kernels": {k: {f: v[f] for f in ("mfma_frac", "hbm_frac", "bound") if f in v}
-                                 for k, v in r["kernels"].items()}}
+                     "roofline": r["roofline"], "method_tflops": r["method_tflops"],
+                     "kernels": r["kernels"]}
     return res
 
 
@@ -645,10 +737,12 @@ def copy_probe(mib: int) -> int:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=30,
-                    help="untimed steps first (the clocks settle within about 20 ms)")
-    ap.add_argument("--workload", default="mamba2_130m_fp32")
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10, help="untimed steps first")
+    ap.add_argument("--warmup-ms", type=float, default=300.0,
+                    help="after the --warmup steps, keep running untimed steps until this much "
+                         "GPU time has passed (the clocks take tens of ms to settle)")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-moments", action="store_true",
                     help="skip the state-moments leg (moments_valid_len_fp32 workload)")
@@ -670,7 +764,7 @@ def main():
     ap.add_argument("--quat-only", action="store_true",
                     help="run only the quaternion-scan leg and print its JSON object")
     ap.add_argument("--no-other-workloads", action="store_true",
-                    help="skip the SSD step on the bf16 2.7B-shaped and 64k-token workloads")
+                    help="skip the SSD step on the other full-size SSD workloads")
     ap.add_argument("--no-step", action="store_true",
                     help="skip the decode-step leg")
     ap.add_argument("--step-only", action="store_true",
@@ -717,10 +811,12 @@ def main():
     r = bench_ssd(w, inp, args, layout=not args.no_layout_chunk)
     out = {
         "metric": METRIC, "value": r["value"], "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
+        "steps": args.steps, "warmup": args.warmup, "warmup_min_ms": args.warmup_ms,
+        "warmup_steps_run": r["warmup_steps_run"], "warmup_ms_run": r["warmup_ms_run"],
+        "ms_per_step": r["ms_per_step"],
         "ms_per_step_with_kernel_events": r["ms_per_step_with_kernel_events"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "io_dtype": w.io,
+        "dtype": "f32" if w.io == "f32" else "f32+bf16", "io_dtype": w.io,
         "data": "synthetic (seeded draws of the workload recipe; no dataset)",
         "config": {**w.describe(), "kernel_chunk_len": r["kernel_chunk_len"]},
         "roofline": r["roofline"],

@@ -94,3 +94,37 @@ def test_chunk_kernel_bytes_count_every_tensor_once():
     # bf16 io halves the token rows only
     wb = inputs.Workload("b", 4, 2048, 24, 64, 128, 256, io="bf16")
     assert bench.chunk_kernel_bytes(wb, "k5_chunk_scan", 128) == tok * (2 * (2 * 64 + 2 * 128) + 12) + st
+
+
+def test_matrix_flops_split_by_matrix_core_type():
+    """bf16 io: C B^T and dy x^T run on bf16 MFMAs, products with an fp32 operand on fp32
+    ones; fp32 io: everything on fp32 ones.  The total is the same either way."""
+    pairs = 128 * 129 // 2
+    wb = inputs.WORKLOADS["mamba2_2p7b_bf16"]
+    ch = 2 * (4096 // 128) * 80
+    f32, bf = bench.matrix_flops(wb, "k_bwd_source", 128)
+    assert f32 == (4 * 128 * 64 * 128 + 2 * pairs * 64 + 2 * pairs * 128) * ch
+    assert bf == (2 * pairs * 128 + 2 * pairs * 64) * ch
+    assert f32 + bf == bench.kernel_work(wb, "k_bwd_source", 128)[0]
+    assert bench.matrix_flops(wb, "k_chunk_states", 128)[1] == 0
+    assert bench.mfma_roof_s(wb, "k_bwd_source", 128) == pytest.approx(f32 / 157.3e12 + bf / 2.5e15)
+    wf = inputs.WORKLOADS["long_context_64k_fp32"]
+    f32, bf = bench.matrix_flops(wf, "k_bwd_target", 128)
+    assert bf == 0 and f32 == bench.kernel_work(wf, "k_bwd_target", 128)[0]
+    assert bench.matrix_flops(wf, "k4_state_pass", 128) is None
+
+
+def test_cpu_baseline_has_a_single_thread_and_an_all_cores_leg():
+    w = inputs.WORKLOADS["tiny_fp32"]
+    res = bench.cpu_baseline(w, inputs.make_inputs(w), budget_s=0.01)
+    assert res["kind"] == "oracle" and res["cores"] == 1 and res["value"] > 0
+    allc = res["all_cores"]
+    assert allc["kind"] == "oracle" and allc["value"] > 0
+    assert 1 <= allc["cores"] <= w.batch * w.nheads
+    assert allc["nproc"] == bench.host_cpu()["logical_cpus"]
+
+
+def test_headline_is_the_largest_single_gpu_workload():
+    big = max(("mamba2_130m_fp32", "mamba2_2p7b_bf16", "long_context_64k_fp32"),
+              key=lambda n: bench.method_flops(inputs.WORKLOADS[n], 128))
+    assert bench.HEADLINE == big == "long_context_64k_fp32"
