@@ -7,13 +7,16 @@ and compares each output tensor with the fp64 oracle by relative L2 error:
 bf16-rounded values).  Small shapes are compared in full; the five named
 workloads run at full size in the benchmark's launch configuration and are
 compared on all batches of sampled heads (heads are independent, so the oracle
-computes exactly those outputs).
+computes exactly those outputs); on those, every head of the device's outputs is
+also held to the exact linearity identities of the scan.  Besides the per-tensor
+error, every (batch, head, chunk) block is held to its own bound (gpu_common).
 """
 import numpy as np
 import pytest
 import torch
 
-from gpu_common import (GRADS, TOL, compare, gpu_fwd_bwd, oracle_fwd_bwd, say, select_heads)
+from gpu_common import (GRADS, TOL, check_identities_all_heads, compare, gpu_fwd_bwd,
+                        oracle_fwd_bwd, say, select_heads)
 from mamba_ssd_chunked_amd import inputs, ssd
 
 pytestmark = pytest.mark.gpu
@@ -83,6 +86,8 @@ def test_full_size_sampled_heads(name, heads, kcl):
     compare(select_heads(gpu, heads), ref, TOL[w.io], KEYS, name)
     for k in KEYS:
         assert np.all(np.isfinite(gpu[k])), k
+    # every head of the device's outputs, through the exact linearity identities
+    check_identities_all_heads(inp, gpu, TOL[w.io], use_init, False, name)
 
 
 KCL = [(256, 64, "f32"), (256, 128, "f32"), (256, 256, "f32"), (128, 64, "f32"),

@@ -22,7 +22,7 @@ import numpy as np
 import pytest
 
 import oracle
-import pages_chunked
+import chunked_scan
 from mamba_ssd_chunked_amd import inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -81,9 +81,8 @@ def closed_form(i, valid):
       m1 += (sum M e) 1^T H + sum_s u_s (1^T x_s) B_s,  u = L^T M 1."""
     b, n, l, h, p = i["x"].shape
     r = i["B"].shape[-1]
-    cum, end = pages_chunked.k1_cumsum(i["dt"], i["A"])
-    intra, _, _, _ = pages_chunked.k3_states(i["x"], i["B"], cum, i["dt"])
-    s_in, _ = pages_chunked.k4_pass(intra, end, i["init"])
+    cum = chunked_scan.within_chunk_cumsum(i["dt"], i["A"])
+    s_in = chunked_scan.chunk_entry_states(i["x"], i["dt"], i["A"], i["B"], i["init"])
     m2 = np.zeros((b, h, r, r))
     m1 = np.zeros((b, h, r))
     tril = np.tril(np.ones((l, l)))

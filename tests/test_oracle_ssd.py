@@ -4,13 +4,16 @@ The oracle is the token-by-token recurrence and its reverse-mode recurrence.
 Nothing here retypes its loops: every check compares it with something else
 that fixes the answer --
 
-* the chunked algorithm of the burn-mamba combined_backward.rs page (K1-K5 and
-  its recompute backward), restated in numpy fp64 (``pages_chunked``), at several
-  chunk lengths (invariant I1);
+* a chunked evaluation of the scan (``chunked_scan``: per-chunk affine state maps
+  and causal kernel matrices, chunks combined by a prefix-doubling scan; plain
+  PyTorch fp64) at several chunk lengths (invariant I1), and its reverse-mode
+  automatic differentiation for the seven gradients;
 * chaining two calls through the final state (I1b);
 * ``scipy.signal.lfilter`` on the scalar special case (I2);
 * central finite differences of the forward for all seven gradients (I3);
-* the page's test-only local d_da identity "out_x . dout - ddt . dt" (I4);
+* the local d_da identity of the combined_backward.rs page's CombinedGrads docs
+  (gradient w.r.t. the within-chunk cumsum through the chunk's own terms equals
+  out_x . dout - ddt . dt), on the chunked evaluation, with out_x from the oracle (I4);
 * Euler / linearity identities that hold exactly for this scan (I5);
 * closed forms for dt = 0, for a memoryless decay and for an empty sequence;
 * a hand-worked three-token example (``golden/hand_worked_p1r1_seq3.json``).
@@ -25,7 +28,7 @@ import numpy as np
 import pytest
 
 import oracle
-import pages_chunked
+import chunked_scan
 from mamba_ssd_chunked_amd import inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -76,7 +79,7 @@ GRADS = ("d_x", "d_dt", "d_A", "d_B", "d_C", "d_D", "d_init")
 def test_I1_chunked_forward_matches_recurrence(l):
     i = rechunk(tiny(), l)
     y, fin = fwd(i)
-    y2, fin2 = pages_chunked.forward(i["x"], i["dt"], i["A"], i["B"], i["C"], i["D"], i["init"])
+    y2, fin2 = chunked_scan.forward(i["x"], i["dt"], i["A"], i["B"], i["C"], i["D"], i["init"])
     assert rel(y, y2) < 1e-12
     assert rel(fin, fin2) < 1e-12
 
@@ -184,10 +187,11 @@ def test_golden_hand_worked_example():
 # ---------------------------------------------------------------- backward pins
 @pytest.mark.parametrize("l", [1, 4, 16])
 def test_chunked_backward_matches_reverse_recurrence(l):
+    """The oracle's reverse recurrence == autodiff of the chunked evaluation."""
     i = rechunk(tiny(), l)
     g = bwd(i)
-    ref = pages_chunked.backward(i["dy"], i["d_final"], i["x"], i["dt"], i["A"], i["B"], i["C"],
-                                 i["D"], i["init"])
+    ref = chunked_scan.backward(i["dy"], i["d_final"], i["x"], i["dt"], i["A"], i["B"], i["C"],
+                                i["D"], i["init"])
     for k in GRADS:
         assert rel(g[k], ref[k]) < 1e-11, k
 
@@ -220,16 +224,18 @@ def test_I3_finite_differences_all_seven_gradients():
 
 
 def test_I4_local_dda_identity_of_the_page():
-    """d_da_local[t] = sum_p dy[t,p] out_x[t,p] - d_dt_orange[t] dt[t], out_x = y - D x."""
+    """d_da_local[t] = sum_p dy[t,p] out_x[t,p] - d_dt_orange[t] dt[t], out_x = y - D x:
+    the gradient w.r.t. the within-chunk cumsum through the chunk's own terms (entry-state
+    read-out and causal kernel) against the one w.r.t. dt through the kernel's source
+    weight, both by autodiff of the chunked evaluation; out_x from the oracle."""
     i = tiny(seq=32, chunk_len=8)
-    ref = pages_chunked.backward(i["dy"], i["d_final"], i["x"], i["dt"], i["A"], i["B"], i["C"],
-                                 i["D"], i["init"])
+    d_local, d_dt_kernel = chunked_scan.local_gradients(i["dy"], i["x"], i["dt"], i["A"], i["B"],
+                                                        i["C"], i["init"])
     y, _ = fwd(i)  # the oracle's y: ties the identity to the recurrence
     out_x = y - i["D"][None, None, None, :, None] * i["x"]
-    lhs = ref["d_da_local"]
     rhs = np.transpose(np.einsum("bnlhp,bnlhp->bnlh", i["dy"], out_x), (0, 3, 1, 2)) \
-        - ref["d_dt_orange"] * i["dt"]
-    assert np.max(np.abs(lhs - rhs)) < 1e-12 * max(1.0, np.max(np.abs(lhs)))
+        - d_dt_kernel * i["dt"]
+    assert np.max(np.abs(d_local - rhs)) < 1e-12 * max(1.0, np.max(np.abs(d_local)))
 
 
 def _dot(a, b):
