@@ -311,9 +311,10 @@ const char* ssd_last_error(void);
  * they wrote for a NaN or an infinity, which synchronises `stream`, and return
  * SSD_ERR_NONFINITE (ssd_last_error() names the first such output) instead of 0.
  * The outputs are written as usual.  Not for code under HIP graph capture (the
- * check synchronises); the scan keeps one flag word per output in a small static
- * device array, so calls that overlap on one GPU in debug mode may report each
- * other's outputs.  Returns 0.
+ * check synchronises).  The scan keeps one flag word per output in a small static
+ * device array; a host lock held from clearing those words until their values are
+ * back on the host makes checks of overlapping calls (other threads or streams)
+ * run one after another, so each call reports only its own outputs.  Returns 0.
  */
 int ssd_debug_enable(int on);
 

@@ -16,6 +16,8 @@
 // |cumsum| of several hundred an fp32 cumsum would put relative errors of
 // 1e-5..1e-4 on the decays; cdt also gives d_A its exact per-pair weights
 // (see k_chunk_bwd.hip).
+#include <mutex>
+
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -448,11 +450,13 @@ __global__ __launch_bounds__(NT) void k_nonfinite(const void* __restrict__ p, in
 }
 
 hipError_t nonfinite_flags(int** flags) {
+    static std::mutex mu;
     static int* addr[64] = {nullptr};
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
     if (!addr[dev]) {
         void* a = nullptr;
         e = hipGetSymbolAddress(&a, HIP_SYMBOL(g_nonfinite));

@@ -243,7 +243,13 @@ struct Checked {
     const char* name;
 };
 
+// The flag words are one device array per GPU shared by every caller, so a check holds
+// this lock from clearing them until its results are back on the host: overlapping
+// checks (other threads, other streams) wait instead of clearing each other's flags.
+std::mutex g_check_mu;
+
 int check_outputs(hipStream_t st, const char* where, std::initializer_list<Checked> outs) {
+    std::lock_guard<std::mutex> lk(g_check_mu);
     int* flags = nullptr;
     hipError_t e = ssd::nonfinite_flags(&flags);
     const char* names[16];
