@@ -120,6 +120,24 @@ int ssd_fwd(const ssd_dims* dims, const void* x, const float* dt, const float* A
             void* y, float* final_state, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The forward with no workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, outputs and kernels as ssd_fwd; the
+ * workspace ssd_fwd would take (ssd_workspace_size(dims, SSD_OP_FWD) bytes) is
+ * a fixed device array of SSD_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * GPU, held until the process ends.  Problems that need more return
+ * SSD_ERR_WORKSPACE (use ssd_fwd with a workspace of their own) before anything
+ * is enqueued.  The call allocates and frees nothing.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (different streams or
+ * threads) race and must be serialised by the caller.  Nothing in the array
+ * needs clearing between calls (the forward overwrites all of what it reads).
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int ssd_fwd_noalloc(const ssd_dims* dims, const void* x, const float* dt, const float* A,
+                    const void* B, const void* C, const float* D, const float* init,
+                    void* y, float* final_state, void* stream);
+
+/*
  * Recompute backward (combined_backward.rs page: recompute K1-K4, SKIP
  * backward, BLUE/ORANGE and K4 backward, K3/K2/K1 backward, combine).
  *   dy       [b,n,l,h,p] in, io dtype: gradient of y

@@ -387,6 +387,58 @@ int check_valid_len(const ssd::Shape& s, const int64_t* valid_len) {
     return SSD_OK;
 }
 
+// The forward of ssd_fwd and ssd_fwd_noalloc.  With `fixed_scratch` the workspace is
+// the library's fixed device array (ws / ws_bytes are ignored): problems that need
+// more are rejected before anything is enqueued, and nothing is allocated.
+int fwd_impl(const char* who, const ssd_dims* dims, const void* x, const float* dt, const float* A,
+             const void* B, const void* C, const float* D, const float* init, void* y,
+             float* final_state, void* ws, size_t ws_bytes, bool fixed_scratch, void* stream) {
+    ssd::Shape s;
+    if (int rc = validate_dims(dims, &s)) return rc;
+    const bool tok = s.B > 0 && s.N > 0;  // token tensors are non-empty
+    if (!A || !D || (tok && (!x || !dt || !B || !C || !y)))
+        return fail(SSD_ERR_NULL, "%s: x, dt, A, B, C, D and y are required", who);
+    if (int rc = check_io_ptrs(s, {{x, "x"}, {B, "B"}, {C, "C"}, {y, "y"}},
+                               {{dt, "dt"}, {init, "init"}, {final_state, "final_state"}}))
+        return rc;
+    if (fixed_scratch) {
+        const size_t need = plan(s, SSD_OP_FWD).total;
+        if (need > SSD_NOALLOC_SCRATCH_BYTES)
+            return fail(SSD_ERR_WORKSPACE,
+                        "%s: the problem needs %zu bytes of scratch, more than the %u bytes the "
+                        "library holds per GPU (call ssd_fwd with a workspace of %zu bytes)",
+                        who, need, SSD_NOALLOC_SCRATCH_BYTES, need);
+        if (need > 0) {
+            const hipError_t e = ssd::noalloc_scratch(&ws);
+            if (e != hipSuccess)
+                return fail(SSD_ERR_HIP, "%s: scratch lookup failed: %s", who, hipGetErrorString(e));
+            ws_bytes = SSD_NOALLOC_SCRATCH_BYTES;
+        }
+    }
+    if (int rc = check_ws(s, SSD_OP_FWD, ws, ws_bytes)) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t nstate = static_cast<int64_t>(s.B) * s.H * s.P * s.R;
+    if (s.B == 0 || s.N == 0) {
+        if (final_state) SSD_HIP(ssd::launch_copy_or_zero(final_state, init, nstate, st), "copy init");
+        return ok();
+    }
+    const Ws w = plan(s, SSD_OP_FWD);
+    double* cdt = at<double>(ws, w.cdt);
+    float* S = at<float>(ws, w.S);
+    SSD_HIP(ssd::launch_k1_cumsum(s, dt, cdt, st), "k1_cumsum");
+    SSD_HIP(ssd::launch_chunk_states(s, true, false, x, B, nullptr, nullptr, dt, A, cdt, S, nullptr, st),
+            "k_chunk_states");
+    SSD_HIP(ssd::launch_k4_pass(s, S, cdt, A, init, final_state, st), "k4_state_pass");
+    SSD_HIP(ssd::launch_k5_scan(s, x, dt, B, C, A, D, cdt, S, y, st), "k5_chunk_scan");
+    if (g_debug) {
+        const bool bf = s.io == SSD_BF16;
+        const int64_t tp = static_cast<int64_t>(s.B) * s.N * s.L * s.H * s.P;
+        if (int rc = check_outputs(st, who, {{y, tp, bf, "y"}, {final_state, nstate, false, "final_state"}}))
+            return rc;
+    }
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -461,36 +513,15 @@ int ssd_workspace_size(const ssd_dims* dims, int op, size_t* bytes) {
 int ssd_fwd(const ssd_dims* dims, const void* x, const float* dt, const float* A, const void* B,
             const void* C, const float* D, const float* init, void* y, float* final_state, void* ws,
             size_t ws_bytes, void* stream) {
-    ssd::Shape s;
-    if (int rc = validate_dims(dims, &s)) return rc;
-    const bool tok = s.B > 0 && s.N > 0;  // token tensors are non-empty
-    if (!A || !D || (tok && (!x || !dt || !B || !C || !y)))
-        return fail(SSD_ERR_NULL, "ssd_fwd: x, dt, A, B, C, D and y are required");
-    if (int rc = check_io_ptrs(s, {{x, "x"}, {B, "B"}, {C, "C"}, {y, "y"}},
-                               {{dt, "dt"}, {init, "init"}, {final_state, "final_state"}}))
-        return rc;
-    if (int rc = check_ws(s, SSD_OP_FWD, ws, ws_bytes)) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const int64_t nstate = static_cast<int64_t>(s.B) * s.H * s.P * s.R;
-    if (s.B == 0 || s.N == 0) {
-        if (final_state) SSD_HIP(ssd::launch_copy_or_zero(final_state, init, nstate, st), "copy init");
-        return ok();
-    }
-    const Ws w = plan(s, SSD_OP_FWD);
-    double* cdt = at<double>(ws, w.cdt);
-    float* S = at<float>(ws, w.S);
-    SSD_HIP(ssd::launch_k1_cumsum(s, dt, cdt, st), "k1_cumsum");
-    SSD_HIP(ssd::launch_chunk_states(s, true, false, x, B, nullptr, nullptr, dt, A, cdt, S, nullptr, st),
-            "k_chunk_states");
-    SSD_HIP(ssd::launch_k4_pass(s, S, cdt, A, init, final_state, st), "k4_state_pass");
-    SSD_HIP(ssd::launch_k5_scan(s, x, dt, B, C, A, D, cdt, S, y, st), "k5_chunk_scan");
-    if (g_debug) {
-        const bool bf = s.io == SSD_BF16;
-        const int64_t tp = static_cast<int64_t>(s.B) * s.N * s.L * s.H * s.P;
-        if (int rc = check_outputs(st, "ssd_fwd", {{y, tp, bf, "y"}, {final_state, nstate, false, "final_state"}}))
-            return rc;
-    }
-    return ok();
+    return fwd_impl("ssd_fwd", dims, x, dt, A, B, C, D, init, y, final_state, ws, ws_bytes, false,
+                    stream);
+}
+
+int ssd_fwd_noalloc(const ssd_dims* dims, const void* x, const float* dt, const float* A,
+                    const void* B, const void* C, const float* D, const float* init, void* y,
+                    float* final_state, void* stream) {
+    return fwd_impl("ssd_fwd_noalloc", dims, x, dt, A, B, C, D, init, y, final_state, nullptr, 0,
+                    true, stream);
 }
 
 int ssd_bwd(const ssd_dims* dims, const void* dy, const float* d_final, const void* x,

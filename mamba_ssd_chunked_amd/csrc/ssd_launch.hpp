@@ -143,6 +143,10 @@ hipError_t nonfinite_flags(int** flags);
 hipError_t launch_clear_flags(int* flags, int n, hipStream_t st);
 hipError_t launch_nonfinite(const void* p, int64_t n, bool bf16, int* flag, hipStream_t st);
 
+// Device address of the fixed scratch array of ssd_fwd_noalloc on the current
+// device (SSD_NOALLOC_SCRATCH_BYTES, 256-byte aligned), looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_set_i64(int64_t* dst, const int64_t* vals, int64_t fill, int64_t n, hipStream_t st);
 
 // ------------------------------------------------------ participation ratio

@@ -28,7 +28,7 @@ SSD_F32, SSD_BF16 = 0, 1
 SSD_OP_FWD, SSD_OP_BWD, SSD_OP_MOMENTS, SSD_OP_MOMENTS_BWD = 0, 1, 2, 3
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
           4: "SSD_ERR_DTYPE", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_HIP", 7: "SSD_ERR_NONFINITE"}
-EXPORTS = ("ssd_workspace_size", "ssd_fwd", "ssd_bwd", "ssd_state_moments",
+EXPORTS = ("ssd_workspace_size", "ssd_fwd", "ssd_fwd_noalloc", "ssd_bwd", "ssd_state_moments",
            "ssd_state_moments_bwd", "ssd_moments_pr", "ssd_moments_pr_bwd", "ssd_y_diag",
            "ssd_y_diag_bwd", "ssd_quat_scan", "ssd_quat_scan_bwd", "ssd_quat_workspace_size",
            "ssd_step", "ssd_last_error", "ssd_debug_enable", "ssd_timing_enable",
@@ -69,6 +69,7 @@ def load_library(path: str = LIB_PATH):
     D = ctypes.POINTER(ssd_dims)
     lib.ssd_workspace_size.argtypes = [D, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
     lib.ssd_fwd.argtypes = [D] + [P] * 10 + [ctypes.c_size_t, P]
+    lib.ssd_fwd_noalloc.argtypes = [D] + [P] * 10
     lib.ssd_bwd.argtypes = [D] + [P] * 17 + [ctypes.c_size_t, P]
     lib.ssd_state_moments.argtypes = [D] + [P] * 14 + [ctypes.c_size_t, P]
     lib.ssd_state_moments_bwd.argtypes = [D] + [P] * 14 + [ctypes.c_size_t, P]
@@ -81,7 +82,7 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_quat_scan_bwd.argtypes = [I64] * 4 + [P] * 6 + [ctypes.c_size_t, P]
     lib.ssd_quat_workspace_size.argtypes = [I64] * 4 + [ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
     lib.ssd_step.argtypes = [I64] * 4 + [ctypes.c_int] + [P] * 10
-    for f in ("ssd_workspace_size", "ssd_fwd", "ssd_bwd", "ssd_state_moments",
+    for f in ("ssd_workspace_size", "ssd_fwd", "ssd_fwd_noalloc", "ssd_bwd", "ssd_state_moments",
               "ssd_state_moments_bwd", "ssd_moments_pr", "ssd_moments_pr_bwd", "ssd_y_diag",
               "ssd_y_diag_bwd", "ssd_quat_scan", "ssd_quat_scan_bwd", "ssd_quat_workspace_size", "ssd_step"):
         getattr(lib, f).restype = ctypes.c_int
@@ -209,6 +210,22 @@ def ssd_fwd(dims, x, dt, A, B, C, D, init, y, final_state, ws, stream=None) -> i
             _ptr(final_state, "final_state", f, s["state"], False)]
     wp, wb = _ws(ws)
     return load_library().ssd_fwd(ctypes.byref(dims), *args, wp, wb, _stream(stream))
+
+
+# bytes of the library's fixed scratch array (SSD_NOALLOC_SCRATCH_BYTES in include/ssd.h)
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
+
+
+def ssd_fwd_noalloc(dims, x, dt, A, B, C, D, init, y, final_state, stream=None) -> int:
+    """ssd_fwd without a workspace: the library's fixed per-GPU scratch array stands in
+    for it (problems needing more than NOALLOC_SCRATCH_BYTES return SSD_ERR_WORKSPACE)."""
+    s, io, f = _sizes(dims), _io_dtype(dims), torch.float32
+    args = [_ptr(x, "x", io, s["tok_p"], True), _ptr(dt, "dt", f, s["dt"], True),
+            _ptr(A, "A", f, s["head"], True), _ptr(B, "B", io, s["tok_r"], True),
+            _ptr(C, "C", io, s["tok_r"], True), _ptr(D, "D", f, s["head"], True),
+            _ptr(init, "init", f, s["state"], False), _ptr(y, "y", io, s["tok_p"], True),
+            _ptr(final_state, "final_state", f, s["state"], False)]
+    return load_library().ssd_fwd_noalloc(ctypes.byref(dims), *args, _stream(stream))
 
 
 def ssd_bwd(dims, dy, d_final, x, dt, A, B, C, D, init, d_x, d_dt, d_A, d_B, d_C, d_D, d_init,

@@ -124,6 +124,30 @@ def test_workspace_too_small_and_misaligned(lib):
     assert lib.ssd_fwd(ctypes.byref(bf), *a[:9], FAKE + 4, need_bf, None) == 3  # ... not for ws
 
 
+def test_noalloc_forward_validation(lib):
+    """ssd_fwd_noalloc checks what ssd_fwd checks and rejects problems whose workspace
+    exceeds its fixed scratch with SSD_ERR_WORKSPACE, all before any HIP call."""
+    d = dims()
+    args = [FAKE] * 9
+    for i in (0, 1, 2, 3, 4, 5, 7):  # x, dt, A, B, C, D, y
+        a = list(args)
+        a[i] = None
+        assert lib.ssd_fwd_noalloc(ctypes.byref(d), *a, None) == 1, i
+    assert lib.ssd_fwd_noalloc(ctypes.byref(dims(l=96)), *args, None) == 3
+    a = list(args)
+    a[0] = FAKE + 4
+    assert lib.ssd_fwd_noalloc(ctypes.byref(d), *a, None) == 3
+    big = dims(b=1, n=256, l=256, h=32, p=64, r=128)  # the 64k-token workload: 0.55 GB
+    assert ssd.ssd_workspace_size(big, ssd.SSD_OP_FWD) > ssd.NOALLOC_SCRATCH_BYTES
+    assert lib.ssd_fwd_noalloc(ctypes.byref(big), *args, None) == 5
+    assert "scratch" in ssd.ssd_last_error()
+    fits = dims(b=4, n=8, l=256, h=24, p=64, r=128)  # the 130M-shaped workload: 51.9 MB
+    assert ssd.ssd_workspace_size(fits, ssd.SSD_OP_FWD) <= ssd.NOALLOC_SCRATCH_BYTES
+    header = open(HEADER).read()
+    assert "#define SSD_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)" in header
+    assert ssd.NOALLOC_SCRATCH_BYTES == 64 * 1024 * 1024
+
+
 def test_moments_validation(lib):
     d = dims()
     assert lib.ssd_state_moments(None, *([FAKE] * 14), 1 << 30, None) == 1
