@@ -41,9 +41,10 @@ HEADLINE = "long_context_64k_fp32"
 # HBM bytes per launch (read, write) of a kernel from two rocprofv3 --pmc runs (FETCH_SIZE,
 # WRITE_SIZE; scaled x2.0 / x1.0 by the same counters on a 256 MiB device copy), keyed by
 # (kernel, workload, kernel chunk length), valid only while the hash of the kernel's sources is
-# the one they were taken on (profiles/ssd_kernels_mamba2_130m_fp32.md has the runs).
+# the one they were taken on (profiles/ssd_kernels_*.md have the runs).
 TRAFFIC = {
     ("k_bwd_source", "mamba2_130m_fp32", 128): (499_015_680, 153_552_896, "e840692e9e07d1e5"),
+    ("k_bwd_source", "long_context_64k_fp32", 128): (5_365_651_456, 1_637_876_736, "e840692e9e07d1e5"),
 }
 TRAFFIC_SOURCES = {"k_bwd_source": ("k_chunk_bwd.hip", "ssd_device.hpp"),
                    "k_bwd_target": ("k_chunk_bwd.hip", "ssd_device.hpp")}
