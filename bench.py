@@ -90,8 +90,8 @@ def matrix_flops(w, kernel: str, k: int):
         f32, bf = 2 * l * p * r, 0
     elif kernel == "k5_chunk_scan":     # BLUE C S_in, C B^T, W x
         f32, bf = 2 * l * p * r + 2 * pairs * p, cb
-    elif kernel == "k_bwd_target":      # BLUE dy S_in, C B^T, dy x^T, d_CB B
-        f32, bf = 2 * l * p * r + 2 * pairs * r, cb + dw
+    elif kernel == "k_bwd_target":      # BLUE dy S_in, d_CB B (d_CB handed over by k_bwd_source)
+        f32, bf = 2 * l * p * r + 2 * pairs * r, 0
     elif kernel == "k_bwd_source":      # K3 (two products), C B^T, dy x^T, W^T dy, d_CB^T C
         f32, bf = 4 * l * p * r + 2 * pairs * p + 2 * pairs * r, cb + dw
     else:
@@ -149,10 +149,11 @@ def chunk_kernel_bytes(w, kernel: str, k: int):
         return (2 * job0 + job1) / 2
     if kernel == "k5_chunk_scan":       # x, B, C, dt, cdt, S_in -> y
         return tok * (io * (2 * p + 2 * r) + 12) + st
-    if kernel == "k_bwd_target":        # dy, x, B, C, dt, cdt, S_in, d_intra -> d_C, g1, d_end
-        return tok * (io * (2 * p + 3 * r) + 16) + 2 * st + 8 * ch
-    if kernel == "k_bwd_source":        # dy, x, B, C, dt, cdt, d_intra -> d_x, d_B, d_dt, g2, d_delta
-        return tok * (io * (3 * p + 3 * r) + 24) + st
+    tiles = 1024 * (l // 16) * (l // 16 + 1) // 2 * ch   # the causal d_CB pair tiles (fp32)
+    if kernel == "k_bwd_target":        # dy, C, B, cdt, S_in, d_intra, d_CB tiles, g2, d_delta,
+        return tok * (io * (p + 3 * r) + 24) + 2 * st + tiles   # d_dt -> d_C, d_dt
+    if kernel == "k_bwd_source":        # dy, x, B, C, dt, cdt, d_intra -> d_x, d_B, d_dt, g2,
+        return tok * (io * (3 * p + 3 * r) + 24) + st + tiles   # d_delta, d_CB tiles
     return None
 
 

@@ -14,13 +14,7 @@
 // d_CB = d_w * dt[s] * decay and d_diff = d_CB * CB (ORANGE backward), and
 // b_scaled = B * bbar with bbar = dt * exp(end - cum) (K3):
 //
-//   target side, rows t (bwd_target):
-//     d_C[t]     = e_t dy[t] S_in              (BLUE backward, d_C_blue)
-//                + sum_{s<=t} d_CB[t,s] B[s]    (K2 backward, d_c = d_cb B)
-//     g1[t]      = sum_r C[t,r] d_C_blue[t,r]   (BLUE d_da)
-//                + sum_{s<=t} d_diff[t,s]        (ORANGE d_da, target side)
-//     d_end      = exp(end) <d_intra, S_in>      (K4 backward, d_da_chunk_end)
-//   source side, rows s (bwd_source):
+//   source side, rows s (bwd_source, runs first):
 //     d_x[s]     = D dy[s]                                   (SKIP backward)
 //                + sum_{t>=s} W[t,s] dy[t]                    (ORANGE, d_x = w^T d_orange)
 //                + bbar[s] d_intra B[s]^T                     (K3, d_x = d_intra b_scaled^T)
@@ -31,8 +25,16 @@
 //     g2[s]      = -sum_{t>=s} d_diff[t,s]                    (ORANGE d_da, source side)
 //     d_delta[s] = d_bbar[s] dt[s] exp(end - cum[s])          (K3: gradient of end - cum[s])
 //     dD_part    = sum dy x                                   (SKIP, d_D)
-// k1t_and_heads (K1^T) then turns g1 + g2, d_delta and d_end into d_cum's suffix sum
-// (for d_dt).
+//   and it hands d_CB of every causal 16 x 16 pair tile to the target side, so C B^T and
+//   dy x^T are formed once per pair;
+//   target side, rows t (bwd_target, from those tiles):
+//     d_C[t]     = e_t dy[t] S_in              (BLUE backward, d_C_blue)
+//                + sum_{s<=t} d_CB[t,s] B[s]    (K2 backward, d_c = d_cb B)
+//     g1[t]      = sum_r C[t,r] d_C[t,r]        (BLUE d_da + ORANGE d_da, target side:
+//                  sum_{s<=t} d_diff[t,s] = sum_s d_CB[t,s] C_t . B_s = C_t . d_C_orange[t])
+//     d_end      = exp(end) <d_intra, S_in>      (K4 backward, d_da_chunk_end)
+// K1^T then turns g1 + g2, d_delta and d_end into d_cum's suffix sum (for d_dt):
+// k1t_and_heads, or the epilogue of the whole-chunk target kernel (k_chunk_wide.hip).
 //
 // d_A is NOT formed as sum_t d_da[t] dt[t]: the suffix sums of rowsum - colsum
 // cancel the large near-diagonal ORANGE terms, which costs d_A ~1e-5 relative
@@ -41,8 +43,8 @@
 //   d_A = sum_pairs d_diff[t,s] (cdt[t] - cdt[s]) + sum_t blue[t] cdt[t]
 //       + sum_s d_delta[s] (cdt[L-1] - cdt[s]) + d_end cdt[L-1]
 // per chunk, where near-diagonal pairs get small weights instead of cancelling.
-// The target side writes the first two sums (plus the d_end term), the source
-// side the third; reduce_heads adds them per head.
+// The source side writes the first and third sums, the target side the second
+// (plus the d_end term); reduce_heads adds them per head.
 //
 // Layout trick (no LDS transposes): every 16x16 product tile is computed with
 // its M index along the rows the NEXT product contracts over, so the four MFMA
@@ -57,19 +59,16 @@ namespace ssd {
 
 template <class IO, int P, int R>
 __global__ __launch_bounds__(NT, 2) void k_bwd_target(
-    const typename IO::T* __restrict__ dy, const typename IO::T* __restrict__ x,
-    const float* __restrict__ dt, const typename IO::T* __restrict__ Bm,
+    const typename IO::T* __restrict__ dy, const typename IO::T* __restrict__ Bm,
     const typename IO::T* __restrict__ Cm, const float* __restrict__ Av,
     const double* __restrict__ cdt, const float* __restrict__ S, const float* __restrict__ dS,
+    const float* __restrict__ dcbt,
     typename IO::T* __restrict__ dC, float* __restrict__ g1, float* __restrict__ d_end,
     double* __restrict__ dA_T, int N, int H, int L, int64_t CH) {
-    constexpr int RS = R + 4, PS = P + 4;
+    constexpr int RS = R + 4;
     constexpr int ROWS = P > TB ? P : TB;
     __shared__ float sBS[ROWS * RS];  // S_in [P, R], then B of the source block
-    __shared__ float sX[TB * PS];
     __shared__ __align__(16) double sCdtT[TB];
-    __shared__ __align__(16) double sCdtS[TB];
-    __shared__ __align__(16) float sDt[TB];
     __shared__ double sRed[NT / 64];
     const int nblk = L / TB;
     const int tb = nblk - 1 - static_cast<int>(blockIdx.x / CH);  // heaviest first
@@ -80,10 +79,10 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target(
     const int64_t brow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(R);
     const int64_t bstride = static_cast<int64_t>(H) * R;
     const double* cc = cdt + c.c_bhn * L;
-    const float* dtc = dt + c.c_bhn * L;
     const double a = static_cast<double>(Av[c.h]);
-    const double la2 = a * kLog2e;
     const int tl = 16 * wave + i;  // target row of this lane inside the block
+    const int it = 4 * tb + wave;  // this wave's target tile inside the chunk
+    const int64_t tiles0 = c.ch * pair_tiles_of(L);
 
     v4f creg[R / 16], dyreg[P / 16];
     {
@@ -138,69 +137,36 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target(
     }
     const double ct = sCdtT[tl];
     const float et = expf(static_cast<float>(a * ct));
-    float gsum = 0.0f;  // this lane's part of g1[t = tl]
+    float gblue = 0.0f;  // this lane's part of the BLUE gradient w.r.t. the cumsum at t = tl
 #pragma unroll
     for (int rt = 0; rt < R / 16; ++rt) {
         acc[rt] *= et;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) gsum += creg[rt][v] * acc[rt][v];
+        for (int v = 0; v < 4; ++v) gblue += creg[rt][v] * acc[rt][v];
     }
-    dA += static_cast<double>(gsum) * ct;
+    dA += static_cast<double>(gblue) * ct;
 
+    // K2 backward from the source-row kernel's d_CB tiles: d_C^T[r, t] += sum_s B[s, r] d_CB[t, s]
     for (int sb = 0; sb <= tb; ++sb) {
-        __syncthreads();
-        double cnext = 0.0;
-        float dnext = 0.0f;
-        if (tid < TB) {
-            cnext = cc[sb * TB + tid];
-            dnext = dtc[sb * TB + tid];
-        }
-        stage_rows2<IO, R, P>(sBS, Bm + brow0 + static_cast<int64_t>(sb * TB) * bstride, bstride,
-                              sX, x + xrow0 + static_cast<int64_t>(sb * TB) * xstride, xstride);
-        if (tid < TB) {
-            sCdtS[tid] = cnext;
-            sDt[tid] = dnext;
-        }
-        __syncthreads();
         const int jmax = (sb == tb) ? wave : 3;  // diagonal block: s-tiles up to this wave's
+        v4f dct[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (j > jmax) break;
-            // tiles with M = s (16j + 4g + v), N = t (tl)
-            v4f cbt = zero4(), dwt = zero4();
+            const int64_t tat = tiles0 + pair_index(it, 4 * sb + j);
+            dct[j] = *reinterpret_cast<const v4f*>(dcbt + tat * 256 + i * 16 + 4 * g);
+        }
+        __syncthreads();
+        stage_rows<IO, R>(sBS, Bm + brow0 + static_cast<int64_t>(sb * TB) * bstride, bstride);
+        __syncthreads();
 #pragma unroll
-            for (int kk = 0; kk < R / 16; ++kk) {
-                const v4f u = *reinterpret_cast<const v4f*>(sBS + (16 * j + i) * RS + 16 * kk + 4 * g);
-                cbt = mfma_k16<IO>(u, creg[kk], cbt);
-            }
-#pragma unroll
-            for (int kk = 0; kk < P / 16; ++kk) {
-                const v4f u = *reinterpret_cast<const v4f*>(sX + (16 * j + i) * PS + 16 * kk + 4 * g);
-                dwt = mfma_k16<IO>(u, dyreg[kk], dwt);
-            }
-            // this lane's four source rows: cumsums and dt as 16-byte LDS reads
-            const v2d cs01 = *reinterpret_cast<const v2d*>(sCdtS + 16 * j + 4 * g);
-            const v2d cs23 = *reinterpret_cast<const v2d*>(sCdtS + 16 * j + 4 * g + 2);
-            const v4f dts = *reinterpret_cast<const v4f*>(sDt + 16 * j + 4 * g);
-            const double csv[4] = {cs01.x, cs01.y, cs23.x, cs23.y};
-            float dcb[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const bool keep = (sb < tb) || (16 * j + 4 * g + v <= tl);
-                // masked pairs (s > t) take gap 0 and weight 0: arithmetic, not a branch
-                const double gap = keep ? ct - csv[v] : 0.0;
-                const float dec = exp2_of(la2 * gap) * (keep ? 1.0f : 0.0f);
-                dcb[v] = dwt[v] * dts[v] * dec;
-                const float ddiff = dcb[v] * cbt[v];
-                gsum += ddiff;
-                dA += static_cast<double>(ddiff) * gap;
-            }
-            // K2 backward: d_C^T[r, t] += sum_s B[s, r] d_CB[t, s]
+        for (int j = 0; j < 4; ++j) {
+            if (j > jmax) break;
 #pragma unroll
             for (int rt = 0; rt < R / 16; ++rt) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    acc[rt] = mfma16(sBS[(16 * j + 4 * g + v) * RS + rt * 16 + i], dcb[v], acc[rt]);
+                    acc[rt] = mfma16(sBS[(16 * j + 4 * g + v) * RS + rt * 16 + i], dct[j][v], acc[rt]);
             }
         }
     }
@@ -210,6 +176,13 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target(
 #pragma unroll
         for (int rt = 0; rt < R / 16; ++rt) io<IO>::st4(dC, row + rt * 16 + 4 * g, acc[rt]);
     }
+    // g1[t] = sum_r C[t, r] d_C[t, r]: the BLUE term plus ORANGE's target side, since
+    // sum_s d_diff[t, s] = sum_s d_CB[t, s] (C_t . B_s) = C_t . (sum_s d_CB[t, s] B_s)
+    float gsum = 0.0f;
+#pragma unroll
+    for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) gsum += creg[rt][v] * acc[rt][v];
     gsum = sum_over_g(gsum);
     if (g == 0) g1[c.c_bhn * L + tb * TB + tl] = gsum;
 #pragma unroll
@@ -228,7 +201,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     const float* __restrict__ Dv, const double* __restrict__ cdt, const float* __restrict__ dS,
     typename IO::T* __restrict__ dx, typename IO::T* __restrict__ dB, float* __restrict__ d_dt,
     float* __restrict__ g2, float* __restrict__ d_delta, double* __restrict__ dA_S,
-    double* __restrict__ dD_part, int N, int H, int L, int64_t CH) {
+    double* __restrict__ dD_part, float* __restrict__ dcbt, int N, int H, int L, int64_t CH) {
     constexpr int RS = R + 4, PS = P + 4;
     constexpr int ROWS = P > TB ? P : TB;
     __shared__ float sCT[ROWS * RS];  // d_intra [P, R], then C of the target block
@@ -317,8 +290,11 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     }
 
     float ddt_or = 0.0f, dsrc = 0.0f;
+    double dA = 0.0;  // this lane's part of the chunk's d_A (the pair terms and K3; file header)
+    const int64_t tiles0 = c.ch * pair_tiles_of(L);  // this chunk-head's first pair tile
     // One (16-row target tile j of block tb, 16-row source tile) pair: the source tile's
     // operands xr / br, cumsum csr, dt dtr and row srow inside the block, its accumulators.
+    // The pair's d_CB tile goes to the target-row kernel.
     auto tile = [&](int j, int tb, const v4f (&xr)[P / 16], const v4f (&br)[R / 16], double csr,
                     float dtr, int srow, v4f (&aX)[P / 16], v4f (&aB)[R / 16], float& ddt,
                     float& dsr) __attribute__((always_inline)) {
@@ -338,6 +314,10 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
         const v2d ct01 = *reinterpret_cast<const v2d*>(sCdtT + 16 * j + 4 * g);
         const v2d ct23 = *reinterpret_cast<const v2d*>(sCdtT + 16 * j + 4 * g + 2);
         const double ctv[4] = {ct01.x, ct01.y, ct23.x, ct23.y};
+        // hand-off: d_CB[t][s] of the pair tile, t-major, as the target-row kernel reads it
+        const int64_t tile_at =
+            tiles0 + pair_index(4 * tb + j, 4 * sb + __builtin_amdgcn_readfirstlane(srow >> 4));
+        float* const tdst = dcbt + tile_at * 256;
         float wv[4], dcb[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -349,7 +329,10 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
             wv[v] = cbd * dtr;
             dcb[v] = dw[v] * dtr * dec;
             ddt += dw[v] * cbd;
-            dsr += dcb[v] * cb[v];
+            const float dd = dcb[v] * cb[v];  // d_diff[t, s]
+            dsr += dd;
+            dA += static_cast<double>(dd) * gap;
+            tdst[(4 * g + v) * 16 + i] = dcb[v];
         }
         // ORANGE: d_x^T[p, s] += sum_t dy[t, p] W[t, s]
 #pragma unroll
@@ -491,14 +474,13 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     dbb = sum_over_g(dbb);
     ddt_or = sum_over_g(ddt_or);
     dsrc = sum_over_g(dsrc);
-    double dA = 0.0;
     if (g == 0) {
         const int64_t o = c.c_bhn * L + spos;
         const float dl = dbb * dts * dec_end;
         d_dt[o] = ddt_or + dbb * dec_end;
         g2[o] = -dsrc;
         d_delta[o] = dl;
-        dA = static_cast<double>(dl) * (end - cs);
+        dA += static_cast<double>(dl) * (end - cs);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -524,10 +506,10 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     X(128, 16) X(128, 32) X(128, 64) X(128, 128)
 
 template <class IO>
-static hipError_t target_io(const Shape& s, const void* dy, const void* x, const float* dt,
-                            const void* Bm, const void* Cm, const float* A, const double* cdt,
-                            const float* S, const float* dS, void* dC, float* g1, float* d_end,
-                            double* dA_T, hipStream_t st) {
+static hipError_t target_io(const Shape& s, const void* dy, const void* Bm, const void* Cm,
+                            const float* A, const double* cdt, const float* S, const float* dS,
+                            const float* dcbt, void* dC, float* g1, float* d_end, double* dA_T,
+                            hipStream_t st) {
     using T = typename IO::T;
     const int64_t CH = static_cast<int64_t>(s.B) * s.N * s.H;
     if (CH == 0) return hipSuccess;
@@ -535,8 +517,8 @@ static hipError_t target_io(const Shape& s, const void* dy, const void* x, const
 #define X(PP, RR)                                                                                \
     if (s.P == PP && s.R == RR) {                                                                \
         hipLaunchKernelGGL((k_bwd_target<IO, PP, RR>), grid, dim3(NT), 0, st,                   \
-                           static_cast<const T*>(dy), static_cast<const T*>(x), dt,              \
-                           static_cast<const T*>(Bm), static_cast<const T*>(Cm), A, cdt, S, dS,  \
+                           static_cast<const T*>(dy), static_cast<const T*>(Bm),                 \
+                           static_cast<const T*>(Cm), A, cdt, S, dS, dcbt,                       \
                            static_cast<T*>(dC), g1, d_end, dA_T, s.N, s.H, s.L, CH);             \
         return hipGetLastError();                                                                \
     }
@@ -545,14 +527,12 @@ static hipError_t target_io(const Shape& s, const void* dy, const void* x, const
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_target(const Shape& s, const void* dy, const void* x, const float* dt,
-                             const void* Bm, const void* Cm, const float* A, const double* cdt,
-                             const float* S, const float* dS, void* dC, float* g1, float* d_end,
-                             double* dA_T, hipStream_t st) {
-    if (wide_supported(s))
-        return launch_bwd_target_wide(s, dy, x, dt, Bm, Cm, A, cdt, S, dS, dC, g1, d_end, dA_T, st);
-    return s.io == 1 ? target_io<BF16>(s, dy, x, dt, Bm, Cm, A, cdt, S, dS, dC, g1, d_end, dA_T, st)
-                     : target_io<F32>(s, dy, x, dt, Bm, Cm, A, cdt, S, dS, dC, g1, d_end, dA_T, st);
+hipError_t launch_bwd_target(const Shape& s, const void* dy, const void* Bm, const void* Cm,
+                             const float* A, const double* cdt, const float* S, const float* dS,
+                             const float* dcbt, void* dC, float* g1, float* d_end, double* dA_T,
+                             hipStream_t st) {
+    return s.io == 1 ? target_io<BF16>(s, dy, Bm, Cm, A, cdt, S, dS, dcbt, dC, g1, d_end, dA_T, st)
+                     : target_io<F32>(s, dy, Bm, Cm, A, cdt, S, dS, dcbt, dC, g1, d_end, dA_T, st);
 }
 
 template <class IO>
@@ -560,7 +540,7 @@ static hipError_t source_io(const Shape& s, const void* dy, const void* x, const
                             const void* Bm, const void* Cm, const float* A, const float* D,
                             const double* cdt, const float* dS, void* dx, void* dB, float* d_dt,
                             float* g2, float* d_delta, double* dA_S, double* dD_part,
-                            hipStream_t st) {
+                            float* dcbt, hipStream_t st) {
     using T = typename IO::T;
     const int64_t CH = static_cast<int64_t>(s.B) * s.N * s.H;
     if (CH == 0) return hipSuccess;
@@ -571,7 +551,7 @@ static hipError_t source_io(const Shape& s, const void* dy, const void* x, const
                            static_cast<const T*>(dy), static_cast<const T*>(x), dt,               \
                            static_cast<const T*>(Bm), static_cast<const T*>(Cm), A, D, cdt, dS,   \
                            static_cast<T*>(dx), static_cast<T*>(dB), d_dt, g2, d_delta, dA_S,     \
-                           dD_part, s.N, s.H, s.L, CH);                                           \
+                           dD_part, dcbt, s.N, s.H, s.L, CH);                                     \
         return hipGetLastError();                                                                 \
     }
     SSD_FOR_EACH_PR(X)
@@ -583,11 +563,11 @@ hipError_t launch_bwd_source(const Shape& s, const void* dy, const void* x, cons
                              const void* Bm, const void* Cm, const float* A, const float* D,
                              const double* cdt, const float* dS, void* dx, void* dB, float* d_dt,
                              float* g2, float* d_delta, double* dA_S, double* dD_part,
-                             hipStream_t st) {
+                             float* dcbt, hipStream_t st) {
     return s.io == 1 ? source_io<BF16>(s, dy, x, dt, Bm, Cm, A, D, cdt, dS, dx, dB, d_dt, g2,
-                                       d_delta, dA_S, dD_part, st)
+                                       d_delta, dA_S, dD_part, dcbt, st)
                      : source_io<F32>(s, dy, x, dt, Bm, Cm, A, D, cdt, dS, dx, dB, d_dt, g2,
-                                      d_delta, dA_S, dD_part, st);
+                                      d_delta, dA_S, dD_part, dcbt, st);
 }
 
 }  // namespace ssd

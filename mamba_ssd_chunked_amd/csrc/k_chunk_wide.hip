@@ -206,23 +206,31 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
 }
 
 // ---------------------------------------------------------- backward, rows t
-// Wave w owns target tiles tt = {w, 7 - w}; acc[q][rt][v] is d_C[t][r] with
-// t = 16 tt[q] + i, r = 16 rt + 4g + v.
+// Runs after the source-row kernel, which leaves the d_CB tile of every causal pair tile
+// of the chunk (pair_index order).  Wave w owns
+// target tiles tt = {w, 7 - w} (9 pair tiles each); acc[q][rt][v] is d_C[t][r] with
+// t = 16 tt[q] + i, r = 16 rt + 4g + v.  The whole chunk is in this workgroup, so K1's
+// backward (the suffix sums of the gradient w.r.t. the within-chunk cumsum, and
+// d_dt += A d_da) runs in its epilogue, on the source-row kernel's g2, d_delta and d_dt.
+template <int P, int R>
+constexpr int wide_target_lds() {  // S_in [P, R], then the chunk's B rows [KC, R]
+    return (P > KC ? P : KC) * (R + 4);
+}
+
 template <class IO, int P, int R>
 __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
-    const typename IO::T* __restrict__ dy, const typename IO::T* __restrict__ x,
-    const float* __restrict__ dt, const typename IO::T* __restrict__ Bm,
+    const typename IO::T* __restrict__ dy, const typename IO::T* __restrict__ Bm,
     const typename IO::T* __restrict__ Cm, const float* __restrict__ Av,
     const double* __restrict__ cdt, const float* __restrict__ S, const float* __restrict__ dS,
-    typename IO::T* __restrict__ dC, float* __restrict__ g1, float* __restrict__ d_end,
+    const float* __restrict__ dcbt, const float* __restrict__ g2,
+    const float* __restrict__ d_delta, typename IO::T* __restrict__ dC, float* __restrict__ d_dt,
     double* __restrict__ dA_T, int N, int H) {
-    constexpr int RS = R + 4, PS = P + 4, L = KC, NBLK = KC / TB;
-    __shared__ float sM[wide_main<P, R>()];  // S_in [P, R], then one half of B | x
-    float* sB = sM;
-    float* sX = sM + TB * RS;
+    constexpr int RS = R + 4, L = KC, NBLK = KC / TB;
+    __shared__ float sM[wide_target_lds<P, R>()];
     __shared__ __align__(16) double sCdt[KC];
-    __shared__ __align__(16) float sDt[KC];
+    __shared__ double sG[KC];  // g1 per token: BLUE + ORANGE target side (gradient w.r.t. the cumsum)
     __shared__ double sRed[NT / 64];
+    __shared__ double sDend;
     const ChunkHead c = decode_ch(blockIdx.x, N, H);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
     const int64_t xrow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(P);
@@ -234,6 +242,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
     const double la2 = a * kLog2e;
     const int tt[2] = {wave, NRT - 1 - wave};
     const int tl[2] = {16 * tt[0] + i, 16 * tt[1] + i};
+    const int64_t tiles0 = c.ch * pair_tiles_of(L);
 
     v4f creg[2][R / 16], dyreg[2][P / 16];
 #pragma unroll
@@ -275,16 +284,13 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
         for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
         if (lane == 0) sRed[wave] = part;
     }
-    if (tid < KC) {
-        sCdt[tid] = cc[tid];
-        sDt[tid] = dt[c.c_bhn * L + tid];
-    }
+    if (tid < KC) sCdt[tid] = cc[tid];
     __syncthreads();
     if (tid == 0) {
         const double end = sCdt[L - 1];
         const double de = (sRed[0] + sRed[1] + sRed[2] + sRed[3]) * exp(a * end);
         const float def = static_cast<float>(de);
-        d_end[c.c_bhn] = def;
+        sDend = static_cast<double>(def);
         dA += static_cast<double>(def) * end;
     }
 
@@ -304,74 +310,64 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
 #pragma unroll
                 for (int q = 0; q < 2; ++q) acc[q][rt] = mfma16(sv, dyreg[q][kk][v], acc[q][rt]);
             }
-    double ct[2];
-    float gsum[2];  // this lane's part of g1[t = tl[q]]
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        ct[q] = sCdt[tl[q]];
-        const float et = exp2_of(la2 * ct[q]);
-        gsum[q] = 0.0f;
+        const double ct = sCdt[tl[q]];
+        const float et = exp2_of(la2 * ct);
+        float gblue = 0.0f;  // this lane's part of the BLUE gradient w.r.t. the cumsum at t
 #pragma unroll
         for (int rt = 0; rt < R / 16; ++rt) {
             acc[q][rt] *= et;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) gsum[q] += creg[q][rt][v] * acc[q][rt][v];
+            for (int v = 0; v < 4; ++v) gblue += creg[q][rt][v] * acc[q][rt][v];
         }
-        dA += static_cast<double>(gsum[q]) * ct[q];
+        dA += static_cast<double>(gblue) * ct;
     }
 
-    // ORANGE / K2 backward, one (partner tile j, own tile q) pair at a time: the two
-    // own tiles' operands and accumulators already fill most of the register budget
-    auto pair = [&](int j, int u, auto qc) {
+    // the wave's pair tiles in order k = 0 .. 8: (own tile tt[0], source tile k) for k <= w,
+    // then (tt[1], k - w - 1); each tile's d_CB (this lane's four s of row t = 16 tt + i)
+    // loads one tile ahead of its products
+    auto tile_at = [&](int k) -> int64_t {
+        return k <= wave ? tiles0 + pair_index(tt[0], k) : tiles0 + pair_index(tt[1], k - wave - 1);
+    };
+    v4f dnext = *reinterpret_cast<const v4f*>(dcbt + tile_at(0) * 256 + i * 16 + 4 * g);
+    // the chunk's B rows into LDS once S_in is consumed (4 rows' loads in flight per thread:
+    // the C rows of the own tiles stay in registers for g1)
+    __syncthreads();
+    stage_rows<IO, R, KC>(sM, Bm + brow0, bstride);
+    __syncthreads();
+    // K2 backward: d_C^T[r, t] += sum_s B[s, r] d_CB[t, s]
+    auto pair = [&](int j, v4f dcb, auto qc) __attribute__((always_inline)) {
         constexpr int q = decltype(qc)::value;
-        v4f cbt = zero4(), dwt = zero4();
-#pragma unroll
-        for (int kk = 0; kk < R / 16; ++kk) {
-            const v4f w = *reinterpret_cast<const v4f*>(sB + (16 * u + i) * RS + 16 * kk + 4 * g);
-            cbt = mfma_k16<IO>(w, creg[q][kk], cbt);
-        }
-#pragma unroll
-        for (int kk = 0; kk < P / 16; ++kk) {
-            const v4f w = *reinterpret_cast<const v4f*>(sX + (16 * u + i) * PS + 16 * kk + 4 * g);
-            dwt = mfma_k16<IO>(w, dyreg[q][kk], dwt);
-        }
-        const v2d cs01 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g);
-        const v2d cs23 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g + 2);
-        const v4f dts = *reinterpret_cast<const v4f*>(sDt + 16 * j + 4 * g);
-        const double csv[4] = {cs01.x, cs01.y, cs23.x, cs23.y};
-        float dcb[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const bool keep = (j < tt[q]) || (16 * j + 4 * g + v <= tl[q]);
-            // masked pairs (s > t) take gap 0 and weight 0: arithmetic, not a branch
-            const double gap = keep ? ct[q] - csv[v] : 0.0;
-            const float dec = exp2_of(la2 * gap) * (keep ? 1.0f : 0.0f);
-            dcb[v] = dwt[v] * dts[v] * dec;
-            const float ddiff = dcb[v] * cbt[v];
-            gsum[q] += ddiff;
-            dA += static_cast<double>(ddiff) * gap;
-        }
-        // K2 backward: d_C^T[r, t] += sum_s B[s, r] d_CB[t, s]
 #pragma unroll
         for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                acc[q][rt] = mfma16(sB[(16 * u + 4 * g + v) * RS + rt * 16 + i], dcb[v], acc[q][rt]);
+                acc[q][rt] = mfma16(sM[(16 * j + 4 * g + v) * RS + rt * 16 + i], dcb[v], acc[q][rt]);
     };
-    for (int half = 0; half < 2; ++half) {
-        __syncthreads();  // the previous contents of sM are consumed
-        stage_half_rows<IO, R>(sB, Bm + brow0, bstride, half);
-        stage_half_rows<IO, P>(sX, x + xrow0, xstride, half);
-        __syncthreads();
-        for (int u = 0; u < 4; ++u) {
-            const int j = 2 * u + half;
-            if (j <= tt[0]) pair(j, u, Q<0>{});
-            if (j <= tt[1]) pair(j, u, Q<1>{});
-        }
+    for (int k = 0; k < NRT + 1; ++k) {
+        const v4f dcur = dnext;
+        if (k + 1 < NRT + 1)
+            dnext = *reinterpret_cast<const v4f*>(dcbt + tile_at(k + 1) * 256 + i * 16 + 4 * g);
+        if (k <= wave)
+            pair(k, dcur, Q<0>{});
+        else
+            pair(k - wave - 1, dcur, Q<1>{});
     }
 
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
+        // g1[t] = sum_r C[t, r] d_C[t, r]: the BLUE term plus ORANGE's target side, since
+        // sum_s d_diff[t, s] = sum_s d_CB[t, s] (C_t . B_s) = C_t . (sum_s d_CB[t, s] B_s).
+        // The own C rows are read again here (from cache: this workgroup read them at its
+        // start) rather than held in registers through the pair products.
+        float gsum = 0.0f;
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt) {
+            const v4f cv = io<IO>::ld4(Cm, brow0 + static_cast<int64_t>(tl[q]) * bstride + 16 * rt + 4 * g);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) gsum += cv[v] * acc[q][rt][v];
+        }
         if constexpr (sizeof(typename IO::T) != 4) {
             const int64_t row = brow0 + static_cast<int64_t>(tl[q]) * bstride;
 #pragma unroll
@@ -393,13 +389,43 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
                            *reinterpret_cast<const v4f*>(sM + (16 * wave + r_) * RS + c4 * 4));
             }
         }
-        const float gs = sum_over_g(gsum[q]);
-        if (g == 0) g1[c.c_bhn * L + tl[q]] = gs;
+        const float gs = sum_over_g(gsum);
+        if (g == 0) sG[tl[q]] = static_cast<double>(gs);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) dA += __shfl_xor(dA, off);
-    __syncthreads();
+    __syncthreads();  // sG complete
     if (lane == 0) sRed[wave] = dA;
+    if (wave == 0) {
+        // K1 backward over the chunk (lane j owns tokens 2j, 2j + 1): with g = g1 + g2 the
+        // gradient w.r.t. the cumsum and d_delta that w.r.t. the decay exponents end - cumsum,
+        //   d_da[t] = sum_{k>=t} g[k] + sum_{k<t} d_delta[k] + d_end,   d_dt[t] += A d_da[t]
+        const int64_t base = c.c_bhn * L + 2 * lane;
+        const float2 g2v = *reinterpret_cast<const float2*>(g2 + base);
+        const float2 dlv = *reinterpret_cast<const float2*>(d_delta + base);
+        const float2 ddt = *reinterpret_cast<const float2*>(d_dt + base);
+        const double gv0 = sG[2 * lane] + static_cast<double>(g2v.x);
+        const double gv1 = sG[2 * lane + 1] + static_cast<double>(g2v.y);
+        const double dl0 = static_cast<double>(dlv.x), dl1 = static_cast<double>(dlv.y);
+        double suf = gv0 + gv1, pre = dl0 + dl1;  // this lane's totals, then scans over lanes
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const double o1 = __shfl_down(suf, off);
+            const double o2 = __shfl_up(pre, off);
+            if (lane + off < 64) suf += o1;
+            if (lane >= off) pre += o2;
+        }
+        double after = __shfl_down(suf, 1);  // sum of g over the later lanes
+        if (lane == 63) after = 0.0;
+        double before = __shfl_up(pre, 1);   // sum of d_delta over the earlier lanes
+        if (lane == 0) before = 0.0;
+        const double dend = sDend;
+        const double dda1 = after + gv1 + before + dl0 + dend;
+        const double dda0 = after + gv1 + gv0 + before + dend;
+        *reinterpret_cast<float2*>(d_dt + base) =
+            float2{static_cast<float>(static_cast<double>(ddt.x) + a * dda0),
+                   static_cast<float>(static_cast<double>(ddt.y) + a * dda1)};
+    }
     __syncthreads();
     if (tid == 0) {
         // one partial per 64-token block slot: the chunk's total in the first, zeros after
@@ -455,10 +481,11 @@ hipError_t launch_k5_scan_wide(const Shape& s, const void* x, const float* dt, c
 }
 
 template <class IO>
-static hipError_t target_wide_io(const Shape& s, const void* dy, const void* x, const float* dt,
-                                 const void* Bm, const void* Cm, const float* A,
-                                 const double* cdt, const float* S, const float* dS, void* dC,
-                                 float* g1, float* d_end, double* dA_T, hipStream_t st) {
+static hipError_t target_wide_io(const Shape& s, const void* dy, const void* Bm, const void* Cm,
+                                 const float* A, const double* cdt, const float* S, const float* dS,
+                                 const float* dcbt, const float* g2,
+                                 const float* d_delta, void* dC, float* d_dt, double* dA_T,
+                                 hipStream_t st) {
     using T = typename IO::T;
     const int64_t CH = static_cast<int64_t>(s.B) * s.N * s.H;
     if (CH == 0) return hipSuccess;
@@ -467,9 +494,9 @@ static hipError_t target_wide_io(const Shape& s, const void* dy, const void* x, 
         if constexpr (wide_fits<PP, RR>()) {                                                       \
             hipLaunchKernelGGL((k_bwd_target_w<IO, PP, RR>), dim3(static_cast<unsigned>(CH)),      \
                                dim3(NT), 0, st, static_cast<const T*>(dy),                         \
-                               static_cast<const T*>(x), dt, static_cast<const T*>(Bm),            \
-                               static_cast<const T*>(Cm), A, cdt, S, dS, static_cast<T*>(dC), g1,  \
-                               d_end, dA_T, s.N, s.H);                                             \
+                               static_cast<const T*>(Bm), static_cast<const T*>(Cm), A, cdt, S,    \
+                               dS, dcbt, g2, d_delta, static_cast<T*>(dC), d_dt, dA_T, s.N,        \
+                               s.H);                                                               \
             return hipGetLastError();                                                              \
         }                                                                                          \
         return hipErrorInvalidValue;                                                               \
@@ -479,13 +506,15 @@ static hipError_t target_wide_io(const Shape& s, const void* dy, const void* x, 
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_target_wide(const Shape& s, const void* dy, const void* x, const float* dt,
-                                  const void* Bm, const void* Cm, const float* A,
-                                  const double* cdt, const float* S, const float* dS, void* dC,
-                                  float* g1, float* d_end, double* dA_T, hipStream_t st) {
-    return s.io == 1
-               ? target_wide_io<BF16>(s, dy, x, dt, Bm, Cm, A, cdt, S, dS, dC, g1, d_end, dA_T, st)
-               : target_wide_io<F32>(s, dy, x, dt, Bm, Cm, A, cdt, S, dS, dC, g1, d_end, dA_T, st);
+hipError_t launch_bwd_target_wide(const Shape& s, const void* dy, const void* Bm, const void* Cm,
+                                  const float* A, const double* cdt, const float* S,
+                                  const float* dS, const float* dcbt, const float* g2,
+                                  const float* d_delta, void* dC, float* d_dt, double* dA_T,
+                                  hipStream_t st) {
+    return s.io == 1 ? target_wide_io<BF16>(s, dy, Bm, Cm, A, cdt, S, dS, dcbt, g2, d_delta, dC,
+                                            d_dt, dA_T, st)
+                     : target_wide_io<F32>(s, dy, Bm, Cm, A, cdt, S, dS, dcbt, g2, d_delta, dC,
+                                           d_dt, dA_T, st);
 }
 
 }  // namespace ssd

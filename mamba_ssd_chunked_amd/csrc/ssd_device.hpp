@@ -348,6 +348,11 @@ __device__ __forceinline__ void st_nt(typename IO::T* p, size_t i, float v) {
         io<IO>::st(p, i, v);
 }
 
+// The causal (target tile, source tile) pairs of a chunk in 16-row tiles, it >= jt,
+// numbered row by row (pair_tiles_of(L) of them): the backward's source-row kernel hands
+// each pair's d_CB tile (256 floats, t-major) to the target-row kernel in this order.
+__device__ __forceinline__ int pair_index(int it, int jt) { return it * (it + 1) / 2 + jt; }
+
 // Sum over the four lane groups g = 0..3 that share i = lane % 16.
 __device__ __forceinline__ float sum_over_g(float v) {
     v += __shfl_xor(v, 16);

@@ -20,6 +20,9 @@ struct Shape {
     int nblk() const { return L / 64; }
 };
 
+// Causal 16 x 16 (target tile, source tile) pairs of a chunk of L tokens.
+constexpr int pair_tiles_of(int L) { return (L / 16) * (L / 16 + 1) / 2; }
+
 // K1: cdt[b,h,n,t] = sum_{k<=t} dt[b,h,n,k]  (fp64; the cumsum of dt*A is A[h] * cdt)
 hipError_t launch_k1_cumsum(const Shape& s, const float* dt, double* cdt, hipStream_t st);
 
@@ -95,30 +98,37 @@ hipError_t launch_k5_scan(const Shape& s, const void* x, const float* dt, const 
 // Whole-chunk variants (k_chunk_wide.hip) of K5 and the backward target-row
 // kernel for 128-token chunks: one workgroup per chunk-head.  wide_supported(s)
 // says whether s takes them (chunk length 128, p * r <= 8192); launch_k5_scan
-// and launch_bwd_target route to them then.
+// routes to the K5 one then, and the backward calls launch_bwd_target_wide.
 bool wide_supported(const Shape& s);
 hipError_t launch_k5_scan_wide(const Shape& s, const void* x, const float* dt, const void* Bm,
                                const void* Cm, const float* A, const float* D, const double* cdt,
                                const float* S, void* y, hipStream_t st);
-hipError_t launch_bwd_target_wide(const Shape& s, const void* dy, const void* x, const float* dt,
-                                  const void* Bm, const void* Cm, const float* A,
-                                  const double* cdt, const float* S, const float* dS, void* dC,
-                                  float* g1, float* d_end, double* dA_T, hipStream_t st);
 
-// Backward, target side (rows t): d_C, g1 (BLUE + ORANGE-target gradient w.r.t. the
-// cumsum), d_end, and d_A partials dA_T [b,n,h,block].
-hipError_t launch_bwd_target(const Shape& s, const void* dy, const void* x, const float* dt,
-                             const void* Bm, const void* Cm, const float* A, const double* cdt,
-                             const float* S, const float* dS, void* dC, float* g1, float* d_end,
-                             double* dA_T, hipStream_t st);
-
-// Backward, source side (rows s): d_x, d_B, partial d_dt, g2 (-ORANGE-source), d_delta (K3),
-// d_A partials dA_S and d_D partials dD_part, both [b,n,h,block].
+// The backward's chunk kernels.  The source-row kernel runs first: rows s get d_x, d_B,
+// the ORANGE + K3 part of d_dt, g2 (-ORANGE d_da, source side), d_delta (K3) and the
+// d_A / d_D partials dA_S, dD_part [b,n,h,block] (with every pair's d_diff (cdt_t - cdt_s));
+// every causal pair tile of 16 x 16 (t, s) hands its d_CB tile to
+// dcbt [chunk-heads, pair_tiles_of(l), 256] (t-major).
 hipError_t launch_bwd_source(const Shape& s, const void* dy, const void* x, const float* dt,
                              const void* Bm, const void* Cm, const float* A, const float* D,
                              const double* cdt, const float* dS, void* dx, void* dB, float* d_dt,
                              float* g2, float* d_delta, double* dA_S, double* dD_part,
+                             float* dcbt, hipStream_t st);
+
+// Target side (rows t) from those tiles, per (chunk-head, 64-row block): d_C, g1 (BLUE +
+// ORANGE-target gradient w.r.t. the cumsum), d_end, and the d_A partials dA_T.
+hipError_t launch_bwd_target(const Shape& s, const void* dy, const void* Bm, const void* Cm,
+                             const float* A, const double* cdt, const float* S, const float* dS,
+                             const float* dcbt, void* dC, float* g1, float* d_end, double* dA_T,
                              hipStream_t st);
+
+// The same per whole 128-token chunk (wide_supported shapes), with K1's backward folded
+// in: d_C, d_dt (the source kernel's part plus A d_da, in place) and dA_T.
+hipError_t launch_bwd_target_wide(const Shape& s, const void* dy, const void* Bm, const void* Cm,
+                                  const float* A, const double* cdt, const float* S,
+                                  const float* dS, const float* dcbt, const float* g2,
+                                  const float* d_delta, void* dC, float* d_dt, double* dA_T,
+                                  hipStream_t st);
 
 // K1 backward (suffix sums inside each chunk, d_dt += A d_da) and, in the same launch,
 // the per-head sums of launch_reduce_heads below.

@@ -85,8 +85,9 @@ def test_chunk_kernel_bytes_count_every_tensor_once():
     w = inputs.WORKLOADS["mamba2_130m_fp32"]
     tok, st = 196608, 4 * 64 * 128 * 1536
     assert bench.chunk_kernel_bytes(w, "k5_chunk_scan", 128) == tok * (4 * (64 + 2 * 128) + 4 * 64 + 12) + st
-    assert bench.chunk_kernel_bytes(w, "k_bwd_source", 128) == tok * (4 * (2 * 64 + 2 * 128) + 4 * (64 + 128) + 24) + st
-    assert bench.chunk_kernel_bytes(w, "k_bwd_target", 128) == tok * (4 * (2 * 64 + 2 * 128) + 4 * 128 + 16) + 2 * st + 8 * 1536
+    tiles = 1024 * 36 * 1536  # 36 causal 16 x 16 d_CB tiles per 128-token chunk-head
+    assert bench.chunk_kernel_bytes(w, "k_bwd_source", 128) == tok * (4 * (2 * 64 + 2 * 128) + 4 * (64 + 128) + 24) + st + tiles
+    assert bench.chunk_kernel_bytes(w, "k_bwd_target", 128) == tok * (4 * (64 + 3 * 128) + 24) + 2 * st + tiles
     job0 = tok * (4 * 192 + 12) + st
     job1 = tok * (4 * 192 + 8) + st
     assert bench.chunk_kernel_bytes(w, "k_chunk_states", 128) == (2 * job0 + job1) / 2
@@ -111,6 +112,9 @@ def test_matrix_flops_split_by_matrix_core_type():
     wf = inputs.WORKLOADS["long_context_64k_fp32"]
     f32, bf = bench.matrix_flops(wf, "k_bwd_target", 128)
     assert bf == 0 and f32 == bench.kernel_work(wf, "k_bwd_target", 128)[0]
+    # the target-row kernel takes d_CB from the source-row kernel: BLUE and d_CB B only
+    assert f32 == (2 * 128 * 64 * 128 + 2 * pairs * 128) * (65536 // 128) * 32
+    assert bench.matrix_flops(wb, "k_bwd_target", 128)[1] == 0
     assert bench.matrix_flops(wf, "k4_state_pass", 128) is None
 
 
