@@ -358,16 +358,13 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         // g1[t] = sum_r C[t, r] d_C[t, r]: the BLUE term plus ORANGE's target side, since
-        // sum_s d_diff[t, s] = sum_s d_CB[t, s] (C_t . B_s) = C_t . (sum_s d_CB[t, s] B_s).
-        // The own C rows are read again here (from cache: this workgroup read them at its
-        // start) rather than held in registers through the pair products.
+        // sum_s d_diff[t, s] = sum_s d_CB[t, s] (C_t . B_s) = C_t . (sum_s d_CB[t, s] B_s)
+        // (the own C rows stay in registers: read again at this point they came from HBM)
         float gsum = 0.0f;
 #pragma unroll
-        for (int rt = 0; rt < R / 16; ++rt) {
-            const v4f cv = io<IO>::ld4(Cm, brow0 + static_cast<int64_t>(tl[q]) * bstride + 16 * rt + 4 * g);
+        for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) gsum += cv[v] * acc[q][rt][v];
-        }
+            for (int v = 0; v < 4; ++v) gsum += creg[q][rt][v] * acc[q][rt][v];
         if constexpr (sizeof(typename IO::T) != 4) {
             const int64_t row = brow0 + static_cast<int64_t>(tl[q]) * bstride;
 #pragma unroll
