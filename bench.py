@@ -74,31 +74,46 @@ def _shape(w, k):
     return w.batch, w.seq // k, k, w.nheads, w.headdim, w.dstate
 
 
+# Kernels whose products with one fp32 operand run, for the bf16 workloads, on the bf16 matrix
+# cores as three exact bf16 parts of that operand (each such product costs three bf16 products).
+SPLIT_BF16 = {"k_chunk_states"}
+
+
 def matrix_flops(w, kernel: str, k: int):
     """Algorithmic flops of ONE launch of a matrix kernel for workload w run at kernel chunk
-    length k, split by the matrix-core type that performs them: (fp32 flops, bf16 flops), or
-    None for a kernel without products.  Only the causal triangle counts (pairs s <= t of a
-    chunk).  With bf16 io the products whose two operands are both bf16 inputs -- C B^T and
-    dy x^T -- run on bf16 MFMAs; every product with an fp32 operand (states, decay-weighted
-    tiles, gradients) runs on fp32 ones."""
+    length k, by the matrix-core form that performs them: (fp32 MFMA, bf16 MFMA with two bf16
+    operands, bf16 MFMA on the three parts of an fp32 operand), or None for a kernel without
+    products.  Only the causal triangle counts (pairs s <= t of a chunk), each product once.
+    With bf16 io the products whose two operands are both bf16 inputs -- C B^T and dy x^T -- run
+    on bf16 MFMAs; a product with an fp32 operand (states, decay-weighted tiles, gradients) runs
+    on fp32 ones, or split in the kernels of SPLIT_BF16."""
     b, n, l, h, p, r = _shape(w, k)
     ch = b * n * h                      # chunk-heads
     pairs = l * (l + 1) // 2            # (t, s) pairs with s <= t per chunk
-    both_bf16 = w.io == "bf16"
     cb, dw = 2 * pairs * r, 2 * pairs * p          # C B^T and dy x^T tiles
     if kernel == "k_chunk_states":      # fwd: 1 job; bwd: 2 jobs (timed per launch: see jobs)
-        f32, bf = 2 * l * p * r, 0
+        f32, both = 2 * l * p * r, 0
     elif kernel == "k5_chunk_scan":     # BLUE C S_in, C B^T, W x
-        f32, bf = 2 * l * p * r + 2 * pairs * p, cb
+        f32, both = 2 * l * p * r + 2 * pairs * p, cb
     elif kernel == "k_bwd_target":      # BLUE dy S_in, d_CB B (d_CB handed over by k_bwd_source)
-        f32, bf = 2 * l * p * r + 2 * pairs * r, 0
+        f32, both = 2 * l * p * r + 2 * pairs * r, 0
     elif kernel == "k_bwd_source":      # K3 (two products), C B^T, dy x^T, W^T dy, d_CB^T C
-        f32, bf = 4 * l * p * r + 2 * pairs * p + 2 * pairs * r, cb + dw
+        f32, both = 4 * l * p * r + 2 * pairs * p + 2 * pairs * r, cb + dw
     else:
         return None
-    if not both_bf16:
-        f32, bf = f32 + bf, 0
-    return f32 * ch, bf * ch
+    if w.io != "bf16":
+        return (f32 + both) * ch, 0, 0
+    if kernel in SPLIT_BF16:
+        return 0, both * ch, f32 * ch
+    return f32 * ch, both * ch, 0
+
+
+def mfma_roof_s(w, kernel: str, k: int, launches: float = 1.0):
+    """Seconds the matrix cores need at their dense peaks for `launches` launches of a
+    matrix kernel: fp32 flops at the fp32 peak, bf16 flops at the bf16 peak, split products
+    three times at the bf16 peak."""
+    f32, both, split = matrix_flops(w, kernel, k)
+    return launches * (f32 / PEAK_FP32_MFMA + (both + 3 * split) / PEAK_BF16_MFMA)
 
 
 def kernel_work(w, kernel: str, k: int):
@@ -112,7 +127,7 @@ def kernel_work(w, kernel: str, k: int):
     tok = ch * l                        # token-heads
     mf = matrix_flops(w, kernel, k)
     if mf is not None:
-        return mf[0] + mf[1], "flop"
+        return sum(mf), "flop"
     if kernel == "k1_cumsum":
         return 12 * tok + 4 * h, "byte"
     if kernel == "k4_state_pass":
@@ -122,13 +137,6 @@ def kernel_work(w, kernel: str, k: int):
     if kernel == "k1t_revcumsum":       # with the per-head d_A / d_D sums in the same launch
         return 24 * tok + 8 * ch + 24 * ch * (l // 64) + 8 * h, "byte"
     return None, None
-
-
-def mfma_roof_s(w, kernel: str, k: int, launches: float = 1.0):
-    """Seconds the matrix cores need at their dense peaks for `launches` launches of a
-    matrix kernel: fp32 flops at the fp32 peak plus bf16 flops at the bf16 peak."""
-    f32, bf = matrix_flops(w, kernel, k)
-    return launches * (f32 / PEAK_FP32_MFMA + bf / PEAK_BF16_MFMA)
 
 
 RIDGE_FP32 = PEAK_FP32_MFMA / PEAK_HBM  # flop/B where the fp32 matrix and HBM roofs meet
@@ -569,9 +577,10 @@ def bench_ssd(w, inp, args, layout=True, steps=None, warmup=None):
                                hbm_frac=round(hbm_s / (avg / 1e3), 4),
                                bound="mfma" if roof_s >= hbm_s else "hbm")
                 if w.io == "bf16":
-                    f32, bf = matrix_flops(w, name, k)
+                    f32, both, split = matrix_flops(w, name, k)
                     ent.update(fp32_mfma_gflop=round(jobs * f32 / 1e9, 2),
-                               bf16_mfma_gflop=round(jobs * bf / 1e9, 2))
+                               bf16_mfma_gflop=round(jobs * both / 1e9, 2),
+                               split_bf16_mfma_gflop=round(jobs * split / 1e9, 2))
             else:
                 rate = work / (avg / 1e3)
                 ent.update(gbps=round(rate / 1e9, 1), hbm_frac=round(rate / PEAK_HBM, 4), bound="hbm")

@@ -116,6 +116,123 @@ __global__ __launch_bounds__(NT) void k_chunk_states(
     }
 }
 
+// The same contraction for bf16 io on the bf16 matrix cores.  U (x or dy) holds exact
+// bf16 values and is staged transposed as bf16; V (B or C) scaled by the token weight
+// is an fp32 operand, staged as its three exact bf16 parts (split3); each 32-token
+// slice is three 16x16x32 bf16 MFMAs per output tile instead of eight fp32 ones.  The
+// token stride of the bf16 tiles is 72 (144-byte rows: the 16-byte reads of 16
+// consecutive rows fall on distinct banks).
+template <int P, int R>
+__global__ __launch_bounds__(NT) void k_chunk_states_bf16(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
+    const uint16_t* __restrict__ dy, const uint16_t* __restrict__ Cm,
+    const float* __restrict__ dt, const float* __restrict__ Av, const double* __restrict__ cdt,
+    float* __restrict__ S, float* __restrict__ dS, const double* __restrict__ phi,
+    float* __restrict__ T, int N, int H, int L, int job0) {
+    constexpr int TS = TB + 8;
+    __shared__ __align__(16) uint16_t sU[P * TS];
+    __shared__ __align__(16) uint16_t sV[3][R * TS];
+    __shared__ float sw[256];  // token weights of the chunk (L <= 256)
+    const int job = job0 + static_cast<int>(blockIdx.y);
+    const ChunkHead c = decode_ch(blockIdx.x, N, H);
+    const uint16_t* U = job == 1 ? dy : x;
+    const uint16_t* V = job == 1 ? Cm : Bm;
+    float* out = (job == 0 ? S : job == 1 ? dS : T) + c.ch * (P * R);
+    const int64_t urow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(P);
+    const int64_t ustride = static_cast<int64_t>(H) * P;
+    const int64_t vrow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(R);
+    const int64_t vstride = static_cast<int64_t>(H) * R;
+    const double* cc = cdt + c.c_bhn * L;
+    const float* dtc = dt + c.c_bhn * L;
+    const double a = static_cast<double>(Av[c.h]);
+    const double end = cc[L - 1];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    constexpr int NPT = P / 16, NRT = R / 16;
+    constexpr int PPW = NPT >= 4 ? NPT / 4 : 1;
+    constexpr int WPS = NPT >= 4 ? 1 : 4 / NPT;
+    constexpr int RPW = NRT >= WPS ? NRT / WPS : 1;
+    const int pt0 = NPT >= 4 ? wave : wave / WPS;
+    const int rt0 = (NPT >= 4 ? 0 : wave % WPS) * RPW;
+    const bool active = rt0 < NRT;
+    v4f acc[PPW][RPW];
+#pragma unroll
+    for (int q = 0; q < PPW; ++q)
+#pragma unroll
+        for (int k = 0; k < RPW; ++k) acc[q][k] = zero4();
+
+    using RU = RowsT<BF16, P>;
+    using RV = RowsT<BF16, R>;
+    v4f tu[RU::IT], tv[RV::IT];
+    load_rows_t<BF16, P>(tu, U + urow0, ustride);
+    load_rows_t<BF16, R>(tv, V + vrow0, vstride);
+    for (int t = tid; t < L; t += NT)
+        sw[t] = job == 0   ? dtc[t] * expf(static_cast<float>(a * (end - cc[t])))
+                : job == 1 ? expf(static_cast<float>(a * cc[t]))
+                           : static_cast<float>(static_cast<double>(dtc[t]) * exp(a * cc[t]) *
+                                                phi[c.c_bhn * L + t]);
+    __syncthreads();
+    for (int t0 = 0; t0 < L; t0 += TB) {
+#pragma unroll
+        for (int it = 0; it < RU::IT; ++it) {
+            const int idx = tid + it * NT;
+            if (RU::TOTAL % NT == 0 || idx < RU::TOTAL) {
+                const int row = RU::row(idx), c4 = RU::col4(idx);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sU[(c4 * 4 + e) * TS + row] = static_cast<uint16_t>(__float_as_uint(tu[it][e]) >> 16);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < RV::IT; ++it) {
+            const int idx = tid + it * NT;
+            if (RV::TOTAL % NT == 0 || idx < RV::TOTAL) {
+                const int row = RV::row(idx), c4 = RV::col4(idx);
+                const float w = sw[t0 + row];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const Split3 sp = split3(tv[it][e] * w);
+                    sV[0][(c4 * 4 + e) * TS + row] = sp.hi;
+                    sV[1][(c4 * 4 + e) * TS + row] = sp.mid;
+                    sV[2][(c4 * 4 + e) * TS + row] = sp.lo;
+                }
+            }
+        }
+        __syncthreads();
+        if (t0 + TB < L) {
+            load_rows_t<BF16, P>(tu, U + urow0 + (t0 + TB) * ustride, ustride);
+            load_rows_t<BF16, R>(tv, V + vrow0 + (t0 + TB) * vstride, vstride);
+        }
+        if (active) {
+#pragma unroll
+            for (int kk = 0; kk < TB / 32; ++kk) {
+                b8v av[PPW];
+#pragma unroll
+                for (int q = 0; q < PPW; ++q)
+                    av[q] = *reinterpret_cast<const b8v*>(sU + ((pt0 + 4 * q) * 16 + i) * TS + 32 * kk + 8 * g);
+#pragma unroll
+                for (int k = 0; k < RPW; ++k) {
+                    const int o = ((rt0 + k) * 16 + i) * TS + 32 * kk + 8 * g;
+                    const b8v bh = *reinterpret_cast<const b8v*>(sV[0] + o);
+                    const b8v bm = *reinterpret_cast<const b8v*>(sV[1] + o);
+                    const b8v bl = *reinterpret_cast<const b8v*>(sV[2] + o);
+#pragma unroll
+                    for (int q = 0; q < PPW; ++q) acc[q][k] = mfma32_split(av[q], bh, bm, bl, acc[q][k]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (active) {
+#pragma unroll
+        for (int q = 0; q < PPW; ++q)
+#pragma unroll
+            for (int k = 0; k < RPW; ++k)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    out[((pt0 + 4 * q) * 16 + 4 * g + v) * R + (rt0 + k) * 16 + i] = acc[q][k][v];
+    }
+}
+
 // ------------------------------------------------------------------------- K5
 // One workgroup per (chunk-head, 64-token target block tb); wave w owns target
 // rows t = 16w .. 16w+15 of the block and keeps its C rows in registers.
@@ -263,10 +380,16 @@ static hipError_t states_io(const Shape& s, bool js, bool jd, const void* x, con
     const int job0 = jm ? 2 : js ? 0 : 1;
 #define X(PP, RR)                                                                                \
     if (s.P == PP && s.R == RR) {                                                                \
-        hipLaunchKernelGGL((k_chunk_states<IO, PP, RR>), grid, dim3(NT), 0, st,                 \
-                           static_cast<const T*>(x), static_cast<const T*>(Bm),                  \
-                           static_cast<const T*>(dy), static_cast<const T*>(Cm), dt, A, cdt, S, dS, \
-                           phi, Tm, s.N, s.H, s.L, job0);                                        \
+        if constexpr (sizeof(T) == 2)                                                            \
+            hipLaunchKernelGGL((k_chunk_states_bf16<PP, RR>), grid, dim3(NT), 0, st,             \
+                               static_cast<const T*>(x), static_cast<const T*>(Bm),              \
+                               static_cast<const T*>(dy), static_cast<const T*>(Cm), dt, A, cdt, \
+                               S, dS, phi, Tm, s.N, s.H, s.L, job0);                             \
+        else                                                                                     \
+            hipLaunchKernelGGL((k_chunk_states<IO, PP, RR>), grid, dim3(NT), 0, st,             \
+                               static_cast<const T*>(x), static_cast<const T*>(Bm),              \
+                               static_cast<const T*>(dy), static_cast<const T*>(Cm), dt, A, cdt, \
+                               S, dS, phi, Tm, s.N, s.H, s.L, job0);                             \
         return hipGetLastError();                                                                \
     }
     SSD_FOR_EACH_PR(X)

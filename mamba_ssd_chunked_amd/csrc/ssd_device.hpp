@@ -68,6 +68,40 @@ __device__ __forceinline__ v4f mfma_k16(v4f a, v4f b, v4f c) {
     }
 }
 
+// ------------------------------------------------- bf16 matrix cores, fp32 operands
+// A product with one operand of exact bf16 values (the bf16 workloads' x, B, C, dy)
+// and one fp32 operand (a state, a decay-weighted tile, a gradient) runs on the bf16
+// matrix cores without narrowing anything: the fp32 operand is split exactly into
+// three bf16 parts, x = hi + mid + lo, each bf16 x bf16 product is exact in fp32, and
+// the three products accumulate in fp32.  hi keeps the sign, the exponent and the top
+// 7 fraction bits (a truncation, so x - hi is exact in fp32 with at most 16
+// significant bits); the same step on that remainder leaves at most 8 significant
+// bits, which bf16 holds exactly.  Only parts below bf16's normal range (|x| < about
+// 2^-110) are lost.  On gfx950 a 16x16x32 bf16 MFMA issues in about the time of two
+// thirds of one fp32 16x16x4 MFMA's (measured 7.2 against 14 ns per SIMD), so a 32-wide
+// k slice takes three of them instead of eight fp32 ones.
+typedef __bf16 b8v __attribute__((ext_vector_type(8)));
+
+struct Split3 {
+    uint16_t hi, mid, lo;
+};
+__device__ __forceinline__ Split3 split3(float x) {
+    const uint32_t h = __float_as_uint(x) & 0xffff0000u;
+    const float r1 = x - __uint_as_float(h);
+    const uint32_t m = __float_as_uint(r1) & 0xffff0000u;
+    const float r2 = r1 - __uint_as_float(m);
+    return Split3{static_cast<uint16_t>(h >> 16), static_cast<uint16_t>(m >> 16),
+                  static_cast<uint16_t>(__float_as_uint(r2) >> 16)};
+}
+
+// One 32-wide k slice of a 16x16 product: a holds exact bf16 values, b an fp32 operand
+// given as its three parts (the smallest first into the fp32 accumulator).
+__device__ __forceinline__ v4f mfma32_split(b8v a, b8v bhi, b8v bmid, b8v blo, v4f c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, blo, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bmid, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bhi, c, 0, 0, 0);
+}
+
 struct F32 {
     using T = float;
 };

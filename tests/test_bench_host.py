@@ -103,18 +103,21 @@ def test_matrix_flops_split_by_matrix_core_type():
     pairs = 128 * 129 // 2
     wb = inputs.WORKLOADS["mamba2_2p7b_bf16"]
     ch = 2 * (4096 // 128) * 80
-    f32, bf = bench.matrix_flops(wb, "k_bwd_source", 128)
+    f32, both, split = bench.matrix_flops(wb, "k_bwd_source", 128)
     assert f32 == (4 * 128 * 64 * 128 + 2 * pairs * 64 + 2 * pairs * 128) * ch
-    assert bf == (2 * pairs * 128 + 2 * pairs * 64) * ch
-    assert f32 + bf == bench.kernel_work(wb, "k_bwd_source", 128)[0]
-    assert bench.matrix_flops(wb, "k_chunk_states", 128)[1] == 0
-    assert bench.mfma_roof_s(wb, "k_bwd_source", 128) == pytest.approx(f32 / 157.3e12 + bf / 2.5e15)
+    assert both == (2 * pairs * 128 + 2 * pairs * 64) * ch
+    assert f32 + both + split == bench.kernel_work(wb, "k_bwd_source", 128)[0]
+    assert bench.mfma_roof_s(wb, "k_bwd_source", 128) == pytest.approx(
+        f32 / 157.3e12 + (both + 3 * split) / 2.5e15)
+    # the state kernel's products run split on the bf16 cores: each costs three bf16 products
+    f32, both, split = bench.matrix_flops(wb, "k_chunk_states", 128)
+    assert f32 == 0 and both == 0 and split == 2 * 128 * 64 * 128 * ch
+    assert bench.mfma_roof_s(wb, "k_chunk_states", 128) == pytest.approx(3 * split / 2.5e15)
     wf = inputs.WORKLOADS["long_context_64k_fp32"]
-    f32, bf = bench.matrix_flops(wf, "k_bwd_target", 128)
-    assert bf == 0 and f32 == bench.kernel_work(wf, "k_bwd_target", 128)[0]
+    f32, both, split = bench.matrix_flops(wf, "k_bwd_target", 128)
+    assert both == 0 and split == 0 and f32 == bench.kernel_work(wf, "k_bwd_target", 128)[0]
     # the target-row kernel takes d_CB from the source-row kernel: BLUE and d_CB B only
     assert f32 == (2 * 128 * 64 * 128 + 2 * pairs * 128) * (65536 // 128) * 32
-    assert bench.matrix_flops(wb, "k_bwd_target", 128)[1] == 0
     assert bench.matrix_flops(wf, "k4_state_pass", 128) is None
 
 
