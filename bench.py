@@ -74,38 +74,33 @@ def _shape(w, k):
     return w.batch, w.seq // k, k, w.nheads, w.headdim, w.dstate
 
 
-# Kernels whose products with one fp32 operand run, for the bf16 workloads, on the bf16 matrix
-# cores as three exact bf16 parts of that operand (each such product costs three bf16 products).
-SPLIT_BF16 = {"k_chunk_states"}
-
-
 def matrix_flops(w, kernel: str, k: int):
     """Algorithmic flops of ONE launch of a matrix kernel for workload w run at kernel chunk
     length k, by the matrix-core form that performs them: (fp32 MFMA, bf16 MFMA with two bf16
-    operands, bf16 MFMA on the three parts of an fp32 operand), or None for a kernel without
-    products.  Only the causal triangle counts (pairs s <= t of a chunk), each product once.
-    With bf16 io the products whose two operands are both bf16 inputs -- C B^T and dy x^T -- run
-    on bf16 MFMAs; a product with an fp32 operand (states, decay-weighted tiles, gradients) runs
-    on fp32 ones, or split in the kernels of SPLIT_BF16."""
+    operands, bf16 MFMA on the three exact bf16 parts of an fp32 operand), or None for a kernel
+    without products.  Only the causal triangle counts (pairs s <= t of a chunk), each product
+    once.  With bf16 io the products whose two operands are both bf16 inputs -- C B^T and
+    dy x^T -- run on bf16 MFMAs; those with one exact-bf16 operand and an fp32 operand that
+    the kernel holds in registers -- the decay-weighted tile W, d_CB, and every product of
+    the state kernel, whose fp32 operand is staged split -- run split; the rest (the BLUE
+    and K3 products, whose fp32 operand streams from LDS) on fp32 MFMAs."""
     b, n, l, h, p, r = _shape(w, k)
     ch = b * n * h                      # chunk-heads
     pairs = l * (l + 1) // 2            # (t, s) pairs with s <= t per chunk
     cb, dw = 2 * pairs * r, 2 * pairs * p          # C B^T and dy x^T tiles
     if kernel == "k_chunk_states":      # fwd: 1 job; bwd: 2 jobs (timed per launch: see jobs)
-        f32, both = 2 * l * p * r, 0
+        f32, both, split = 0, 0, 2 * l * p * r
     elif kernel == "k5_chunk_scan":     # BLUE C S_in, C B^T, W x
-        f32, both = 2 * l * p * r + 2 * pairs * p, cb
+        f32, both, split = 2 * l * p * r, cb, 2 * pairs * p
     elif kernel == "k_bwd_target":      # BLUE dy S_in, d_CB B (d_CB handed over by k_bwd_source)
-        f32, both = 2 * l * p * r + 2 * pairs * r, 0
+        f32, both, split = 2 * l * p * r, 0, 2 * pairs * r
     elif kernel == "k_bwd_source":      # K3 (two products), C B^T, dy x^T, W^T dy, d_CB^T C
-        f32, both = 4 * l * p * r + 2 * pairs * p + 2 * pairs * r, cb + dw
+        f32, both, split = 4 * l * p * r, cb + dw, 2 * pairs * p + 2 * pairs * r
     else:
         return None
     if w.io != "bf16":
-        return (f32 + both) * ch, 0, 0
-    if kernel in SPLIT_BF16:
-        return 0, both * ch, f32 * ch
-    return f32 * ch, both * ch, 0
+        return (f32 + both + split) * ch, 0, 0
+    return f32 * ch, both * ch, split * ch
 
 
 def mfma_roof_s(w, kernel: str, k: int, launches: float = 1.0):

@@ -162,11 +162,22 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (j > jmax) break;
+            if constexpr (sizeof(typename IO::T) == 2) {
+                const S4x3 ds = split4(dct[j]);  // bf16 io: B exact, d_CB split (ssd_device.hpp)
 #pragma unroll
-            for (int rt = 0; rt < R / 16; ++rt) {
+                for (int rt = 0; rt < R / 16; ++rt) {
+                    v4f a;
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    acc[rt] = mfma16(sBS[(16 * j + 4 * g + v) * RS + rt * 16 + i], dct[j][v], acc[rt]);
+                    for (int v = 0; v < 4; ++v) a[v] = sBS[(16 * j + 4 * g + v) * RS + rt * 16 + i];
+                    acc[rt] = mfma16_split(pack_bf16x4(a), ds, acc[rt]);
+                }
+            } else {
+#pragma unroll
+                for (int rt = 0; rt < R / 16; ++rt) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc[rt] = mfma16(sBS[(16 * j + 4 * g + v) * RS + rt * 16 + i], dct[j][v], acc[rt]);
+                }
             }
         }
     }
@@ -334,19 +345,40 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
             dA += static_cast<double>(dd) * gap;
             tdst[(4 * g + v) * 16 + i] = dcb[v];
         }
-        // ORANGE: d_x^T[p, s] += sum_t dy[t, p] W[t, s]
+        if constexpr (sizeof(typename IO::T) == 2) {
+            // bf16 io: dy and C are exact bf16, W and d_CB fp32 tiles split once into
+            // three exact bf16 parts; one 16x16x16 bf16 MFMA per part (ssd_device.hpp)
+            const S4x3 ws = split4(v4f{wv[0], wv[1], wv[2], wv[3]});
+            const S4x3 ds = split4(v4f{dcb[0], dcb[1], dcb[2], dcb[3]});
 #pragma unroll
-        for (int pt = 0; pt < P / 16; ++pt) {
+            for (int pt = 0; pt < P / 16; ++pt) {
+                v4f a;
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                aX[pt] = mfma16(sDY[(16 * j + 4 * g + v) * PS + pt * 16 + i], wv[v], aX[pt]);
-        }
-        // K2 backward: d_B^T[r, s] += sum_t C[t, r] d_CB[t, s]
+                for (int v = 0; v < 4; ++v) a[v] = sDY[(16 * j + 4 * g + v) * PS + pt * 16 + i];
+                aX[pt] = mfma16_split(pack_bf16x4(a), ws, aX[pt]);
+            }
 #pragma unroll
-        for (int rt = 0; rt < R / 16; ++rt) {
+            for (int rt = 0; rt < R / 16; ++rt) {
+                v4f a;
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                aB[rt] = mfma16(sCT[(16 * j + 4 * g + v) * RS + rt * 16 + i], dcb[v], aB[rt]);
+                for (int v = 0; v < 4; ++v) a[v] = sCT[(16 * j + 4 * g + v) * RS + rt * 16 + i];
+                aB[rt] = mfma16_split(pack_bf16x4(a), ds, aB[rt]);
+            }
+        } else {
+            // ORANGE: d_x^T[p, s] += sum_t dy[t, p] W[t, s]
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    aX[pt] = mfma16(sDY[(16 * j + 4 * g + v) * PS + pt * 16 + i], wv[v], aX[pt]);
+            }
+            // K2 backward: d_B^T[r, s] += sum_t C[t, r] d_CB[t, s]
+#pragma unroll
+            for (int rt = 0; rt < R / 16; ++rt) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    aB[rt] = mfma16(sCT[(16 * j + 4 * g + v) * RS + rt * 16 + i], dcb[v], aB[rt]);
+            }
         }
     };
     // Partner blocks from the farthest to the diagonal one.  On the diagonal block wave w

@@ -162,12 +162,25 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
                 const double gap = keep ? ct[q] - csv[v] : 0.0;
                 wv[q][v] = cbt[q][v] * exp2_of(la2 * gap) * dts[v] * (keep ? 1.0f : 0.0f);
             }
+        if constexpr (sizeof(typename IO::T) == 2) {
+            // bf16 io: x exact, W split once per own tile (ssd_device.hpp)
+            S4x3 ws[2];
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+            for (int q = QLO; q < 2; ++q) ws[q] = split4(v4f{wv[q][0], wv[q][1], wv[q][2], wv[q][3]});
 #pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt)
+            for (int pt = 0; pt < P / 16; ++pt) {
+                const s4 b = pack_bf16x4(v4f{xs[0][pt], xs[1][pt], xs[2][pt], xs[3][pt]});
 #pragma unroll
-                for (int q = QLO; q < 2; ++q) acc[q][pt] = mfma16(wv[q][v], xs[v][pt], acc[q][pt]);
+                for (int q = QLO; q < 2; ++q) acc[q][pt] = mfma16_split(ws[q], b, acc[q][pt]);
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int pt = 0; pt < P / 16; ++pt)
+#pragma unroll
+                    for (int q = QLO; q < 2; ++q) acc[q][pt] = mfma16(wv[q][v], xs[v][pt], acc[q][pt]);
+        }
     };
     const float Dh = Dv[c.h];
     for (int half = 0; half < 2; ++half) {
@@ -339,11 +352,22 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
     // K2 backward: d_C^T[r, t] += sum_s B[s, r] d_CB[t, s]
     auto pair = [&](int j, v4f dcb, auto qc) __attribute__((always_inline)) {
         constexpr int q = decltype(qc)::value;
+        if constexpr (sizeof(typename IO::T) == 2) {
+            const S4x3 ds = split4(dcb);  // bf16 io: B exact, d_CB split (ssd_device.hpp)
 #pragma unroll
-        for (int rt = 0; rt < R / 16; ++rt)
+            for (int rt = 0; rt < R / 16; ++rt) {
+                v4f a;
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                acc[q][rt] = mfma16(sM[(16 * j + 4 * g + v) * RS + rt * 16 + i], dcb[v], acc[q][rt]);
+                for (int v = 0; v < 4; ++v) a[v] = sM[(16 * j + 4 * g + v) * RS + rt * 16 + i];
+                acc[q][rt] = mfma16_split(pack_bf16x4(a), ds, acc[q][rt]);
+            }
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[q][rt] = mfma16(sM[(16 * j + 4 * g + v) * RS + rt * 16 + i], dcb[v], acc[q][rt]);
+        }
     };
     for (int k = 0; k < NRT + 1; ++k) {
         const v4f dcur = dnext;

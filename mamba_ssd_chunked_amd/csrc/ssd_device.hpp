@@ -102,6 +102,35 @@ __device__ __forceinline__ v4f mfma32_split(b8v a, b8v bhi, b8v bmid, b8v blo, v
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bhi, c, 0, 0, 0);
 }
 
+// The same on the 16x16x16 bf16 MFMA (k slices of 16, four k values per lane, the layout
+// of four fp32 16x16x4 MFMAs): an fp32 operand tile split once into three packed parts,
+// reused against every exact-bf16 operand it meets.
+struct S4x3 {
+    s4 hi, mid, lo;
+};
+__device__ __forceinline__ S4x3 split4(v4f b) {
+    S4x3 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const Split3 sp = split3(b[e]);
+        o.hi[e] = static_cast<short>(sp.hi);
+        o.mid[e] = static_cast<short>(sp.mid);
+        o.lo[e] = static_cast<short>(sp.lo);
+    }
+    return o;
+}
+// a (exact bf16) x b (fp32, split) and a (fp32, split) x b (exact bf16)
+__device__ __forceinline__ v4f mfma16_split(s4 a, const S4x3& b, v4f c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b.lo, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b.mid, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b.hi, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma16_split(const S4x3& a, s4 b, v4f c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.mid, b, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b, c, 0, 0, 0);
+}
+
 struct F32 {
     using T = float;
 };
