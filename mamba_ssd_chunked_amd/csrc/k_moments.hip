@@ -351,13 +351,29 @@ __global__ __launch_bounds__(NT) void km_chunk(
     const float* Tc = Tm + c.ch * (P * R);
     const int64_t bh = static_cast<int64_t>(c.b) * H + c.h;
     if (!dm2) {
-        // forward: W = H^T (2T + c2 H), m1c = c1 colsum(H)
-        for (int idx = tid; idx < P * (R / 4); idx += NT) {
-            const int row = idx / (R / 4), c4 = idx - (idx / (R / 4)) * (R / 4);
-            const v4f hv = *reinterpret_cast<const v4f*>(Hm + row * R + c4 * 4);
-            const v4f tv = *reinterpret_cast<const v4f*>(Tc + row * R + c4 * 4);
-            *reinterpret_cast<v4f*>(sA + row * RS + c4 * 4) = hv;
-            *reinterpret_cast<v4f*>(sV + row * RS + c4 * 4) = 2.0f * tv + static_cast<float>(c2) * hv;
+        // forward: W = H^T (2T + c2 H), m1c = c1 colsum(H).  Every load of H and T is
+        // issued before the first LDS write (one memory latency, not one per row batch).
+        {
+            constexpr int V = R / 4, TOT = P * V, IT = (TOT + NT - 1) / NT;
+            v4f hv[IT], tv[IT];
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                const int idx = tid + it * NT;
+                if (TOT % NT == 0 || idx < TOT) {
+                    hv[it] = *reinterpret_cast<const v4f*>(Hm + idx * 4);
+                    tv[it] = *reinterpret_cast<const v4f*>(Tc + idx * 4);
+                }
+            }
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                const int idx = tid + it * NT;
+                if (TOT % NT == 0 || idx < TOT) {
+                    const int row = idx / V, c4 = idx % V;
+                    *reinterpret_cast<v4f*>(sA + row * RS + c4 * 4) = hv[it];
+                    *reinterpret_cast<v4f*>(sV + row * RS + c4 * 4) =
+                        2.0f * tv[it] + static_cast<float>(c2) * hv[it];
+                }
+            }
         }
         __syncthreads();
         // wave w takes the 16-row strips r1t = w, w + 4, ... with all their column tiles at
@@ -382,10 +398,23 @@ __global__ __launch_bounds__(NT) void km_chunk(
 #pragma unroll
                 for (int v = 0; v < 4; ++v) Wo[(r1t * 16 + 4 * g + v) * R + r2t * 16 + i] = acc[r2t][v];
         }
-        for (int r = tid; r < R; r += NT) {
+        // m1c: NT / R threads per column r, each summing a fixed slice of the P rows, then
+        // combined in a fixed order across lanes (the NT / R threads of r are R lanes apart)
+        {
+            constexpr int TPC = NT / R;  // threads per column (R <= 128 divides 256)
+            const int r = tid % R, part = tid / R;
             float acc = 0.f;
-            for (int p_ = 0; p_ < P; ++p_) acc += sA[p_ * RS + r];
-            m1c[c.ch * R + r] = static_cast<float>(c1) * acc;
+#pragma unroll 4
+            for (int p_ = part; p_ < P; p_ += TPC) acc += sA[p_ * RS + r];
+            __shared__ float sPart[NT];
+            sPart[tid] = acc;
+            __syncthreads();
+            if (part == 0) {
+                float tot = 0.f;
+#pragma unroll
+                for (int k = 0; k < TPC; ++k) tot += sPart[k * R + r];
+                m1c[c.ch * R + r] = static_cast<float>(c1) * tot;
+            }
         }
         return;
     }
@@ -461,6 +490,14 @@ __global__ __launch_bounds__(NT) void km_chunk(
                             static_cast<double>(ah[kk][2] * dv[2] + ah[kk][3] * dv[3]);
             }
         }
+        // H and dm1 in the result tiles' layout load during the products
+        float hq[R / 16][4], d1q[R / 16];
+#pragma unroll
+        for (int nt = 0; nt < R / 16; ++nt) {
+            d1q[nt] = d1 ? static_cast<float>(c1) * d1[nt * 16 + i] : 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) hq[nt][v] = Hm[(r0 + 4 * g + v) * R + nt * 16 + i];
+        }
         v4f o1[R / 16], o2[R / 16];
 #pragma unroll
         for (int nt = 0; nt < R / 16; ++nt) o1[nt] = o2[nt] = zero4();
@@ -472,8 +509,8 @@ __global__ __launch_bounds__(NT) void km_chunk(
             for (int v = 0; v < 4; ++v) {
                 const int p_ = r0 + 4 * g + v, r_ = nt * 16 + i;
                 HS[c.ch * (P * R) + p_ * R + r_] = o1[nt][v];
-                part_hsh += static_cast<double>(o1[nt][v]) * Hm[p_ * R + r_];
-                dSl[c.ch * (P * R) + p_ * R + r_] = o2[nt][v] + (d1 ? static_cast<float>(c1) * d1[r_] : 0.f);
+                part_hsh += static_cast<double>(o1[nt][v]) * hq[nt][v];
+                dSl[c.ch * (P * R) + p_ * R + r_] = o2[nt][v] + d1q[nt];
             }
     }
     // BS = B S for the chunk's tokens
