@@ -455,6 +455,323 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
     }
 }
 
+// ---------------------------------------------------------- backward, rows s
+// Whole-chunk source-row kernel: one 8-wave workgroup per chunk-head.  The chunk's
+// d_intra, then its C and dy rows, are staged into LDS once (the block kernel's second
+// 64-row block read d_intra and the partner rows again), and the pair tiles are spread
+// so that the two waves sharing a SIMD carry 9 tiles together.  Source tile s has
+// 8 - s target tiles.  Wave w < 4 owns source tile w and its first five target tiles;
+// wave w >= 4 owns source tile 11 - w (7, 6, 5, 4: w - 3 tiles) and, for w < 7, forms the
+// remaining targets of source tile w - 4 (tiles w + 1 .. 7) as a partial that it hands
+// to wave w - 4 through LDS.  Waves w and w + 4 (one SIMD, as the dispatcher places a
+// workgroup's waves round-robin) then carry 5 + 4 tiles.  Per-element formulas: those
+// of k_bwd_source (k_chunk_bwd.hip).
+//
+// bf16 io only.  The LDS of a whole chunk leaves one workgroup per CU, so nothing
+// overlaps its loads at the start of a chunk-head with matrix work.  With bf16 io the
+// block kernel is bound by its vector work (decays, splits, operand packing), which the
+// balance here cuts (2.7B-shaped workload: 589 -> 538 us); with fp32 io the block kernel's
+// two workgroups per CU overlap one another's loads, and this shape was slower there
+// (64k-token workload: 1.95 -> 2.26 ms).
+constexpr int NTS = 512;      // threads of the whole-chunk source kernel
+constexpr int NWS = NTS / 64; // its waves
+
+template <int P, int R>
+constexpr int wide_source_main() {  // the chunk's C rows | dy rows (d_intra first, in the C rows)
+    return KC * (R + 4) + KC * (P + 4);
+}
+
+template <int P, int R>
+__global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
+    const BF16::T* __restrict__ dy, const BF16::T* __restrict__ x,
+    const float* __restrict__ dt, const BF16::T* __restrict__ Bm,
+    const BF16::T* __restrict__ Cm, const float* __restrict__ Av,
+    const float* __restrict__ Dv, const double* __restrict__ cdt, const float* __restrict__ dS,
+    BF16::T* __restrict__ dx, BF16::T* __restrict__ dB, float* __restrict__ d_dt,
+    float* __restrict__ g2, float* __restrict__ d_delta, double* __restrict__ dA_S,
+    double* __restrict__ dD_part, float* __restrict__ dcbt, int N, int H) {
+    using IO = BF16;
+    constexpr int RS = R + 4, PS = P + 4, L = KC, NBLK = KC / TB;
+    static_assert(P <= KC, "d_intra shares the C rows' LDS");
+    constexpr int NEX = 4 * (P / 16 + R / 16) + 2;  // floats per lane of one handed-over partial
+    __shared__ float sM[wide_source_main<P, R>()];
+    float* const sC = sM;
+    float* const sDY = sM + KC * RS;
+    __shared__ float sPart[3 * NEX * 64];
+    __shared__ __align__(16) double sCdt[KC];
+    __shared__ double sRed[2 * NWS];
+    const ChunkHead c = decode_ch(blockIdx.x, N, H);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    const int64_t xrow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(P);
+    const int64_t xstride = static_cast<int64_t>(H) * P;
+    const int64_t brow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(R);
+    const int64_t bstride = static_cast<int64_t>(H) * R;
+    const double* cc = cdt + c.c_bhn * L;
+    const float* dtc = dt + c.c_bhn * L;
+    const double a = static_cast<double>(Av[c.h]);
+    const double la2 = a * kLog2e;
+    const int so = wave < 4 ? wave : 11 - wave;  // own source tile
+    const int spos = 16 * so + i;                // this lane's source row in the chunk
+    const int64_t tiles0 = c.ch * pair_tiles_of(L);
+
+    v4f xreg[P / 16], breg[R / 16];
+    const int64_t xrow = xrow0 + static_cast<int64_t>(spos) * xstride;
+    const int64_t brow = brow0 + static_cast<int64_t>(spos) * bstride;
+#pragma unroll
+    for (int kk = 0; kk < P / 16; ++kk) xreg[kk] = io<IO>::ld4(x, xrow + 16 * kk + 4 * g);
+#pragma unroll
+    for (int kk = 0; kk < R / 16; ++kk) breg[kk] = io<IO>::ld4(Bm, brow + 16 * kk + 4 * g);
+    {  // d_intra [P, R] into the C rows' LDS (row stride R + 4)
+        constexpr int V = R / 4, TOT = P * V, IT = (TOT + NTS - 1) / NTS;
+        const float* src = dS + c.ch * (P * R);
+        v4f tmp[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = tid + it * NTS;
+            if (TOT % NTS == 0 || idx < TOT) tmp[it] = *reinterpret_cast<const v4f*>(src + idx * 4);
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = tid + it * NTS;
+            if (TOT % NTS == 0 || idx < TOT)
+                *reinterpret_cast<v4f*>(sM + (idx / V) * RS + (idx % V) * 4) = tmp[it];
+        }
+    }
+    if (tid < KC) sCdt[tid] = cc[tid];
+    const double end = cc[L - 1];
+    const double cs = cc[spos];
+    const float dts = dtc[spos];
+    const float dec_end = expf(static_cast<float>(a * (end - cs)));
+    const float bbar = dts * dec_end;
+    __syncthreads();
+    // the chunk's C and dy rows load into registers during K3
+    constexpr int VC = R / 4, TC = KC * VC, ITC = (TC + NTS - 1) / NTS;
+    constexpr int VD = P / 4, TD = KC * VD, ITD = (TD + NTS - 1) / NTS;
+    v4f preC[ITC], preD[ITD];
+#pragma unroll
+    for (int it = 0; it < ITC; ++it) {
+        const int idx = tid + it * NTS;
+        if (TC % NTS == 0 || idx < TC)
+            preC[it] = io<IO>::ld4(Cm, brow0 + static_cast<int64_t>(idx / VC) * bstride + (idx % VC) * 4);
+    }
+#pragma unroll
+    for (int it = 0; it < ITD; ++it) {
+        const int idx = tid + it * NTS;
+        if (TD % NTS == 0 || idx < TD)
+            preD[it] = io<IO>::ld4(dy, xrow0 + static_cast<int64_t>(idx / VD) * xstride + (idx % VD) * 4);
+    }
+
+    // K3 backward.  d_b_scaled^T[r, s] = sum_p d_intra[p, r] x[s, p]
+    v4f accB[R / 16];
+#pragma unroll
+    for (int rt = 0; rt < R / 16; ++rt) accB[rt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < P / 16; ++kk)
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                accB[rt] = mfma16(sM[(16 * kk + 4 * g + v) * RS + rt * 16 + i], xreg[kk][v], accB[rt]);
+    float dbb = 0.0f;  // d_bbar[s] = sum_r d_b_scaled[s, r] B[s, r] (this lane's part)
+#pragma unroll
+    for (int rt = 0; rt < R / 16; ++rt) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dbb += accB[rt][v] * breg[rt][v];
+        accB[rt] *= bbar;
+    }
+    // d_x^T[p, s] = bbar[s] sum_r d_intra[p, r] B[s, r]
+    v4f accX[P / 16];
+#pragma unroll
+    for (int pt = 0; pt < P / 16; ++pt) accX[pt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < R / 16; ++kk)
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt) {
+            const v4f u = *reinterpret_cast<const v4f*>(sM + (pt * 16 + i) * RS + 16 * kk + 4 * g);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) accX[pt] = mfma16(u[v], breg[kk][v], accX[pt]);
+        }
+    // SKIP backward: d_x += D dy; d_D partial sum dy x
+    const float Dh = Dv[c.h];
+    double dD = 0.0;
+#pragma unroll
+    for (int pt = 0; pt < P / 16; ++pt) {
+        const v4f dyv = io<IO>::ld4(dy, xrow + pt * 16 + 4 * g);
+        accX[pt] = accX[pt] * bbar + Dh * dyv;
+        dD += static_cast<double>(dyv[0] * xreg[pt][0] + dyv[1] * xreg[pt][1]) +
+              static_cast<double>(dyv[2] * xreg[pt][2] + dyv[3] * xreg[pt][3]);
+    }
+    __syncthreads();  // K3 is done with d_intra
+#pragma unroll
+    for (int it = 0; it < ITC; ++it) {
+        const int idx = tid + it * NTS;
+        if (TC % NTS == 0 || idx < TC) *reinterpret_cast<v4f*>(sC + (idx / VC) * RS + (idx % VC) * 4) = preC[it];
+    }
+#pragma unroll
+    for (int it = 0; it < ITD; ++it) {
+        const int idx = tid + it * NTS;
+        if (TD % NTS == 0 || idx < TD) *reinterpret_cast<v4f*>(sDY + (idx / VD) * PS + (idx % VD) * 4) = preD[it];
+    }
+    __syncthreads();
+
+    double dA = 0.0;  // this lane's part of the chunk's d_A (the pair terms and K3)
+    // One (target tile j, source tile s) pair, j >= s: the source tile's operands xr / br,
+    // cumsum csr and dt dtr of this lane's source row 16 s + i, its accumulators.  The
+    // pair's d_CB tile goes to the target-row kernel.
+    auto tile = [&](int j, int s, const v4f (&xr)[P / 16], const v4f (&br)[R / 16], double csr,
+                    float dtr, v4f (&aX)[P / 16], v4f (&aB)[R / 16], float& ddt,
+                    float& dsr) __attribute__((always_inline)) {
+        // tiles with M = t (16j + 4g + v), N = s
+        v4f cb = zero4(), dw = zero4();
+#pragma unroll
+        for (int kk = 0; kk < R / 16; ++kk) {
+            const v4f u = *reinterpret_cast<const v4f*>(sC + (16 * j + i) * RS + 16 * kk + 4 * g);
+            cb = mfma_k16<IO>(u, br[kk], cb);
+        }
+#pragma unroll
+        for (int kk = 0; kk < P / 16; ++kk) {
+            const v4f u = *reinterpret_cast<const v4f*>(sDY + (16 * j + i) * PS + 16 * kk + 4 * g);
+            dw = mfma_k16<IO>(u, xr[kk], dw);
+        }
+        const v2d ct01 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g);
+        const v2d ct23 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g + 2);
+        const double ctv[4] = {ct01.x, ct01.y, ct23.x, ct23.y};
+        float* const tdst = dcbt + (tiles0 + pair_index(j, s)) * 256;
+        float wv[4], dcb[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const bool keep = 16 * j + 4 * g + v >= 16 * s + i;
+            // masked pairs (t < s) take gap 0 and weight 0: arithmetic, not a branch
+            const double gap = keep ? ctv[v] - csr : 0.0;
+            const float dec = exp2_of(la2 * gap) * (keep ? 1.0f : 0.0f);
+            const float cbd = cb[v] * dec;
+            wv[v] = cbd * dtr;
+            dcb[v] = dw[v] * dtr * dec;
+            ddt += dw[v] * cbd;
+            const float dd = dcb[v] * cb[v];  // d_diff[t, s]
+            dsr += dd;
+            dA += static_cast<double>(dd) * gap;
+            tdst[(4 * g + v) * 16 + i] = dcb[v];
+        }
+        // dy and C are exact bf16, W and d_CB are split once into three exact bf16 parts
+        {
+            const S4x3 ws = split4(v4f{wv[0], wv[1], wv[2], wv[3]});
+            const S4x3 ds = split4(v4f{dcb[0], dcb[1], dcb[2], dcb[3]});
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt) {
+                v4f av;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) av[v] = sDY[(16 * j + 4 * g + v) * PS + pt * 16 + i];
+                aX[pt] = mfma16_split(pack_bf16x4(av), ws, aX[pt]);
+            }
+#pragma unroll
+            for (int rt = 0; rt < R / 16; ++rt) {
+                v4f av;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) av[v] = sC[(16 * j + 4 * g + v) * RS + rt * 16 + i];
+                aB[rt] = mfma16_split(pack_bf16x4(av), ds, aB[rt]);
+            }
+        }
+    };
+    float ddt_or = 0.0f, dsrc = 0.0f;
+    const int jend = wave < 4 ? so + 4 : NRT - 1;
+    for (int j = so; j <= jend; ++j) tile(j, so, xreg, breg, cs, dts, accX, accB, ddt_or, dsrc);
+
+    // The own tile's outputs: d_x and d_B rows (stored from the accumulators: staging them
+    // through LDS for whole-row stores was 4 % slower), and per row d_dt (ORANGE + K3), g2,
+    // d_delta and the K3 term of d_A.
+    auto finalize = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt) io<IO>::st4(dx, xrow + pt * 16 + 4 * g, accX[pt]);
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt) io<IO>::st4(dB, brow + rt * 16 + 4 * g, accB[rt]);
+        const float db = sum_over_g(dbb);
+        const float dto = sum_over_g(ddt_or);
+        const float dsc = sum_over_g(dsrc);
+        if (g == 0) {
+            const int64_t o = c.c_bhn * L + spos;
+            const float dl = db * dts * dec_end;
+            d_dt[o] = dto + db * dec_end;
+            g2[o] = -dsc;
+            d_delta[o] = dl;
+            dA += static_cast<double>(dl) * (end - cs);
+        }
+    };
+    if (wave >= 4 && wave < 7) {
+        // source tiles 7, 6, 5 are complete: their outputs leave before this wave forms
+        // the partial of source tile s2 = w - 4 (its targets s2 + 5 .. 7) for wave s2
+        finalize();
+        const int s2 = wave - 4, sp2 = 16 * s2 + i;
+        v4f x2[P / 16], b2[R / 16], aX2[P / 16], aB2[R / 16];
+        const int64_t xr2 = xrow0 + static_cast<int64_t>(sp2) * xstride;
+        const int64_t br2 = brow0 + static_cast<int64_t>(sp2) * bstride;
+#pragma unroll
+        for (int kk = 0; kk < P / 16; ++kk) {
+            x2[kk] = io<IO>::ld4(x, xr2 + 16 * kk + 4 * g);
+            aX2[kk] = zero4();
+        }
+#pragma unroll
+        for (int kk = 0; kk < R / 16; ++kk) {
+            b2[kk] = io<IO>::ld4(Bm, br2 + 16 * kk + 4 * g);
+            aB2[kk] = zero4();
+        }
+        const double cs2 = sCdt[sp2];
+        const float dt2 = dtc[sp2];
+        float ddt2 = 0.0f, dsr2 = 0.0f;
+        for (int j = s2 + 5; j < NRT; ++j) tile(j, s2, x2, b2, cs2, dt2, aX2, aB2, ddt2, dsr2);
+        float* const pp = sPart + s2 * (NEX * 64);
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) pp[(4 * pt + v) * 64 + lane] = aX2[pt][v];
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) pp[(4 * (P / 16) + 4 * rt + v) * 64 + lane] = aB2[rt][v];
+        pp[(NEX - 2) * 64 + lane] = ddt2;
+        pp[(NEX - 1) * 64 + lane] = dsr2;
+    }
+    __syncthreads();  // every pair tile is done (the partner rows are free), partials are in
+    if (wave < 3) {
+        const float* pp = sPart + wave * (NEX * 64);
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) accX[pt][v] += pp[(4 * pt + v) * 64 + lane];
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) accB[rt][v] += pp[(4 * (P / 16) + 4 * rt + v) * 64 + lane];
+        ddt_or += pp[(NEX - 2) * 64 + lane];
+        dsrc += pp[(NEX - 1) * 64 + lane];
+    }
+    if (wave < 4 || wave == 7) finalize();
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        dD += __shfl_xor(dD, off);
+        dA += __shfl_xor(dA, off);
+    }
+    if (lane == 0) {
+        sRed[wave] = dD;
+        sRed[NWS + wave] = dA;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        // one partial per 64-token block slot: the chunk's total in the first, zeros after
+        double sd = 0.0, sa = 0.0;
+        for (int w = 0; w < NWS; ++w) {
+            sd += sRed[w];
+            sa += sRed[NWS + w];
+        }
+        dD_part[c.ch * NBLK] = sd;
+        dA_S[c.ch * NBLK] = sa;
+        for (int b = 1; b < NBLK; ++b) {
+            dD_part[c.ch * NBLK + b] = 0.0;
+            dA_S[c.ch * NBLK + b] = 0.0;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ dispatch
 #define SSD_WIDE_PR(X) \
     X(16, 16) X(16, 32) X(16, 64) X(16, 128) \
@@ -536,6 +853,43 @@ hipError_t launch_bwd_target_wide(const Shape& s, const void* dy, const void* Bm
                                             d_dt, dA_T, st)
                      : target_wide_io<F32>(s, dy, Bm, Cm, A, cdt, S, dS, dcbt, g2, d_delta, dC,
                                            d_dt, dA_T, st);
+}
+
+
+static hipError_t source_wide_bf16(const Shape& s, const void* dy, const void* x, const float* dt,
+                                 const void* Bm, const void* Cm, const float* A, const float* D,
+                                 const double* cdt, const float* dS, void* dx, void* dB,
+                                 float* d_dt, float* g2, float* d_delta, double* dA_S,
+                                 double* dD_part, float* dcbt, hipStream_t st) {
+    using T = BF16::T;
+    const int64_t CH = static_cast<int64_t>(s.B) * s.N * s.H;
+    if (CH == 0) return hipSuccess;
+#define X(PP, RR)                                                                                 \
+    if (s.P == PP && s.R == RR) {                                                                 \
+        if constexpr (wide_fits<PP, RR>()) {                                                      \
+            hipLaunchKernelGGL((k_bwd_source_w<PP, RR>), dim3(static_cast<unsigned>(CH)),     \
+                               dim3(NTS), 0, st, static_cast<const T*>(dy),                       \
+                               static_cast<const T*>(x), dt, static_cast<const T*>(Bm),           \
+                               static_cast<const T*>(Cm), A, D, cdt, dS, static_cast<T*>(dx),     \
+                               static_cast<T*>(dB), d_dt, g2, d_delta, dA_S, dD_part, dcbt, s.N,  \
+                               s.H);                                                              \
+            return hipGetLastError();                                                             \
+        }                                                                                         \
+        return hipErrorInvalidValue;                                                              \
+    }
+    SSD_WIDE_PR(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_source_wide(const Shape& s, const void* dy, const void* x, const float* dt,
+                                  const void* Bm, const void* Cm, const float* A, const float* D,
+                                  const double* cdt, const float* dS, void* dx, void* dB,
+                                  float* d_dt, float* g2, float* d_delta, double* dA_S,
+                                  double* dD_part, float* dcbt, hipStream_t st) {
+    if (s.io != 1) return hipErrorInvalidValue;  // bf16 io only (see the kernel)
+    return source_wide_bf16(s, dy, x, dt, Bm, Cm, A, D, cdt, dS, dx, dB, d_dt, g2, d_delta, dA_S,
+                            dD_part, dcbt, st);
 }
 
 }  // namespace ssd

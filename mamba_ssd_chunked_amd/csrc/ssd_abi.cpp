@@ -567,11 +567,20 @@ int ssd_bwd(const ssd_dims* dims, const void* dy, const float* d_final, const vo
     SSD_HIP(ssd::launch_chunk_states(s, true, true, x, B, dy, C, dt, A, cdt, S, dS, st), "k_chunk_states");
     SSD_HIP(ssd::launch_k4_pass_bwd(s, S, dS, cdt, A, init, d_final, d_init, st), "k4_state_pass_bwd");
     float* dcbt = at<float>(ws, w.dcbt);
-    // rows s first: they hand every causal pair tile's d_CB to rows t
-    SSD_HIP(ssd::launch_bwd_source(s, dy, x, dt, B, C, A, D, cdt, dS, d_x, d_B, d_dt, g2, dlt, dAS,
-                                   dDp, dcbt, st),
-            "k_bwd_source");
-    if (ssd::wide_supported(s)) {
+    // rows s first: they hand every causal pair tile's d_CB to rows t.  The whole-chunk
+    // source kernel (one workgroup per CU) pays off where the kernel is bound by its vector
+    // work (bf16 io); with fp32 io the two 64-row block workgroups per CU overlap one
+    // another's loads and are faster.
+    const bool wide = ssd::wide_supported(s);
+    if (wide && s.io == SSD_BF16)
+        SSD_HIP(ssd::launch_bwd_source_wide(s, dy, x, dt, B, C, A, D, cdt, dS, d_x, d_B, d_dt, g2,
+                                            dlt, dAS, dDp, dcbt, st),
+                "k_bwd_source");
+    else
+        SSD_HIP(ssd::launch_bwd_source(s, dy, x, dt, B, C, A, D, cdt, dS, d_x, d_B, d_dt, g2, dlt,
+                                       dAS, dDp, dcbt, st),
+                "k_bwd_source");
+    if (wide) {
         // whole chunks: K1's backward runs inside the target-row kernel
         SSD_HIP(ssd::launch_bwd_target_wide(s, dy, B, C, A, cdt, S, dS, dcbt, g2, dlt, d_C, d_dt,
                                             dAT, st),

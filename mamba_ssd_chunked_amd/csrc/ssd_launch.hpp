@@ -115,6 +115,15 @@ hipError_t launch_bwd_source(const Shape& s, const void* dy, const void* x, cons
                              float* g2, float* d_delta, double* dA_S, double* dD_part,
                              float* dcbt, hipStream_t st);
 
+// The same per whole 128-token chunk (wide_supported shapes, bf16 io only): one 8-wave
+// workgroup per chunk-head; the d_A / d_D partials go to the chunk-head's first block
+// slot, zeros after.
+hipError_t launch_bwd_source_wide(const Shape& s, const void* dy, const void* x, const float* dt,
+                                  const void* Bm, const void* Cm, const float* A, const float* D,
+                                  const double* cdt, const float* dS, void* dx, void* dB,
+                                  float* d_dt, float* g2, float* d_delta, double* dA_S,
+                                  double* dD_part, float* dcbt, hipStream_t st);
+
 // Target side (rows t) from those tiles, per (chunk-head, 64-row block): d_C, g1 (BLUE +
 // ORANGE-target gradient w.r.t. the cumsum), d_end, and the d_A partials dA_T.
 hipError_t launch_bwd_target(const Shape& s, const void* dy, const void* Bm, const void* Cm,

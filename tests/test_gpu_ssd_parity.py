@@ -53,6 +53,8 @@ SHAPES = [
     (1, 64, 1, 64, 64, 64, "f32"),
     (2, 512, 2, 64, 128, 256, "bf16"),
     (1, 384, 3, 32, 16, 128, "bf16"),
+    (1, 256, 2, 128, 64, 128, "bf16"),
+    (2, 384, 2, 16, 128, 128, "bf16"),
 ]
 
 
