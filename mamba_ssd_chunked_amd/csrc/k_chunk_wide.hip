@@ -60,8 +60,16 @@ struct Q {
 // ------------------------------------------------------------------------- K5
 // Wave w owns target tiles tt = {w, 7 - w}.  acc[q][pt][v] is y[t][p] with
 // t = 16 tt[q] + 4g + v, p = 16 pt + i (BLUE e_t C_t S_in, then ORANGE, then D x).
+// With bf16 io three workgroups per CU (168 registers; 221 -> 195 us on the 2.7B-shaped
+// workload) hide the loads of the halves that fp32 io hides with a register prefetch
+// (there the third workgroup's register limit spills: 0.93 -> 1.10 ms on 64k tokens).
+template <class IO>
+constexpr int k5w_groups() {
+    return sizeof(typename IO::T) == 2 ? 3 : 2;
+}
+
 template <class IO, int P, int R>
-__global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
+__global__ __launch_bounds__(NT, k5w_groups<IO>()) void k5_chunk_scan_w(
     const typename IO::T* __restrict__ x, const float* __restrict__ dt,
     const typename IO::T* __restrict__ Bm, const typename IO::T* __restrict__ Cm,
     const float* __restrict__ Av, const float* __restrict__ Dv, const double* __restrict__ cdt,
@@ -96,10 +104,13 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
     }
     __syncthreads();
 
-    // the even half of the source rows loads into registers during BLUE
-    v4f preB[RowTiles<R, TB>::IT], preX[RowTiles<P, TB>::IT];
-    load_half_rows<IO, R>(preB, Bm + brow0, bstride, 0);
-    load_half_rows<IO, P>(preX, x + xrow0, xstride, 0);
+    // fp32 io: the even half of the source rows loads into registers during BLUE
+    constexpr bool kPre = k5w_groups<IO>() == 2;
+    v4f preB[kPre ? RowTiles<R, TB>::IT : 1], preX[kPre ? RowTiles<P, TB>::IT : 1];
+    if constexpr (kPre) {
+        load_half_rows<IO, R>(preB, Bm + brow0, bstride, 0);
+        load_half_rows<IO, P>(preX, x + xrow0, xstride, 0);
+    }
     v4f acc[2][P / 16];
 #pragma unroll
     for (int q = 0; q < 2; ++q)
@@ -185,10 +196,15 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
     const float Dh = Dv[c.h];
     for (int half = 0; half < 2; ++half) {
         __syncthreads();  // the previous contents of sM are consumed
-        store_rows<R, TB>(sB, preB);
-        store_rows<P, TB>(sX, preX);
+        if constexpr (kPre) {
+            store_rows<R, TB>(sB, preB);
+            store_rows<P, TB>(sX, preX);
+        } else {
+            stage_half_rows<IO, R>(sB, Bm + brow0, bstride, half);
+            stage_half_rows<IO, P>(sX, x + xrow0, xstride, half);
+        }
         __syncthreads();
-        if (half == 0) {
+        if (kPre && half == 0) {
             load_half_rows<IO, R>(preB, Bm + brow0, bstride, 1);
             load_half_rows<IO, P>(preX, x + xrow0, xstride, 1);
         }
