@@ -206,12 +206,13 @@ __device__ __forceinline__ ChunkHead decode_ch(int64_t ch, int N, int H) {
 }
 
 // Stage ROWS rows of width W (io dtype in global, row stride gstride elements)
-// into LDS as fp32 rows of stride W + 4.  All global loads of a thread are
-// issued before its first LDS write, so the block waits for memory once.
-template <class IO, int W, int ROWS = TB>
+// into LDS as fp32 rows of stride W + 4, in batches of at most MAXB float4 loads
+// per thread, each batch's loads issued before its LDS writes (one memory latency
+// per batch; MAXB bounds the registers the staging takes).
+template <class IO, int W, int ROWS = TB, int MAXB = 4>
 __device__ __forceinline__ void stage_rows(float* lds, const typename IO::T* g, int64_t gstride) {
     constexpr int V = W / 4, TOTAL = ROWS * V, IT = (TOTAL + NT - 1) / NT;
-    constexpr int BATCH = IT < 4 ? IT : 4;  // at most 4 float4 in flight per thread
+    constexpr int BATCH = IT < MAXB ? IT : MAXB;  // at most MAXB float4 in flight per thread
 #pragma unroll
     for (int b0 = 0; b0 < IT; b0 += BATCH) {
         v4f tmp[BATCH];
