@@ -53,8 +53,7 @@ __device__ __forceinline__ void st4_out(typename IO::T* p, int64_t i, v4f v) {
         __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p + i));
     } else {
         typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-        const u2 w{static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16),
-                   static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16)};
+        const u2 w{f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3])};
         __builtin_nontemporal_store(w, reinterpret_cast<u2*>(p + i));
     }
 }

@@ -142,12 +142,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
     return __uint_as_float(static_cast<uint32_t>(u) << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN.
+// Two fp32 -> two bf16 packed in one word (a in the low half), round to nearest even,
+// NaN stays NaN: one v_cvt_pk_bf16_f32 on gfx950.  (Over every non-NaN fp32 bit pattern
+// it gives the same bits as the rounding written out -- add 0x7fff plus the kept lsb,
+// keep the high half -- which compiled to about 12 branchy instructions per value.)
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{a, b}, v2bf));
+}
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<uint16_t>((u >> 16) | 0x0040u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return static_cast<uint16_t>(f32x2_to_bf16x2(f, 0.0f) & 0xffffu);
 }
 
 template <class IO>
@@ -177,8 +182,8 @@ struct io<BF16> {
     }
     static __device__ __forceinline__ void st4(T* p, size_t i, v4f v) {
         uint2 w;
-        w.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-        w.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+        w.x = f32x2_to_bf16x2(v[0], v[1]);
+        w.y = f32x2_to_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2*>(p + i) = w;
     }
     static __device__ __forceinline__ void st(T* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
