@@ -493,10 +493,21 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
 constexpr int NTS = 512;      // threads of the whole-chunk source kernel
 constexpr int NWS = NTS / 64; // its waves
 
+// The chunk's C and dy rows are staged as bf16 twice: row-major (row stride w + 16) for
+// the C B^T and dy x^T tiles, whose A operand is four consecutive features of one row,
+// and in four-row groups ([t / 4][feature][t % 4], group stride w + 16) for the output
+// products, whose A operand is one feature of four consecutive rows: every MFMA operand
+// is then one 8-byte LDS read with no conversion (the fp32 staging read four scalars
+// and repacked them for every MFMA).  The paddings spread a wave's 8-byte reads over
+// the banks evenly.
 template <int P, int R>
-constexpr int wide_source_main() {  // the chunk's C rows | dy rows (d_intra first, in the C rows)
-    return KC * (R + 4) + KC * (P + 4);
-}
+struct SrcWLds {
+    static constexpr int RB = R + 16, PB = P + 16;                // bf16 row / group strides
+    static constexpr int CR = KC * RB, DR = KC * PB;              // row-major C, dy (uint16)
+    static constexpr int CQ = (KC / 4) * RB * 4, DQ = (KC / 4) * PB * 4;  // grouped C, dy
+    static constexpr int TOTAL = CR + DR + CQ + DQ;
+    static_assert(P * (R + 4) * 2 <= TOTAL, "d_intra (fp32) fits where the rows go");
+};
 
 template <int P, int R>
 __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
@@ -508,12 +519,15 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
     float* __restrict__ g2, float* __restrict__ d_delta, double* __restrict__ dA_S,
     double* __restrict__ dD_part, float* __restrict__ dcbt, int N, int H) {
     using IO = BF16;
-    constexpr int RS = R + 4, PS = P + 4, L = KC, NBLK = KC / TB;
-    static_assert(P <= KC, "d_intra shares the C rows' LDS");
+    using LY = SrcWLds<P, R>;
+    constexpr int RS = R + 4, RB = LY::RB, PB = LY::PB, L = KC, NBLK = KC / TB;
     constexpr int NEX = 4 * (P / 16 + R / 16) + 2;  // floats per lane of one handed-over partial
-    __shared__ float sM[wide_source_main<P, R>()];
-    float* const sC = sM;
-    float* const sDY = sM + KC * RS;
+    __shared__ __align__(16) uint16_t sMb[LY::TOTAL];
+    uint16_t* const sCr = sMb;
+    uint16_t* const sDr = sCr + LY::CR;
+    uint16_t* const sCq = sDr + LY::DR;
+    uint16_t* const sDq = sCq + LY::CQ;
+    float* const sDI = reinterpret_cast<float*>(sMb);  // d_intra [P, R] (stride R + 4) during K3
     __shared__ float sPart[3 * NEX * 64];
     __shared__ __align__(16) double sCdt[KC];
     __shared__ double sRed[2 * NWS];
@@ -530,6 +544,10 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
     const int so = wave < 4 ? wave : 11 - wave;  // own source tile
     const int spos = 16 * so + i;                // this lane's source row in the chunk
     const int64_t tiles0 = c.ch * pair_tiles_of(L);
+    // 8-byte LDS operand: four bf16
+    auto ld_s4 = [](const uint16_t* p) __attribute__((always_inline)) {
+        return *reinterpret_cast<const s4*>(p);
+    };
 
     v4f xreg[P / 16], breg[R / 16];
     const int64_t xrow = xrow0 + static_cast<int64_t>(spos) * xstride;
@@ -538,7 +556,7 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
     for (int kk = 0; kk < P / 16; ++kk) xreg[kk] = io<IO>::ld4(x, xrow + 16 * kk + 4 * g);
 #pragma unroll
     for (int kk = 0; kk < R / 16; ++kk) breg[kk] = io<IO>::ld4(Bm, brow + 16 * kk + 4 * g);
-    {  // d_intra [P, R] into the C rows' LDS (row stride R + 4)
+    {  // d_intra [P, R] (fp32) into LDS (row stride R + 4)
         constexpr int V = R / 4, TOT = P * V, IT = (TOT + NTS - 1) / NTS;
         const float* src = dS + c.ch * (P * R);
         v4f tmp[IT];
@@ -551,7 +569,7 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
         for (int it = 0; it < IT; ++it) {
             const int idx = tid + it * NTS;
             if (TOT % NTS == 0 || idx < TOT)
-                *reinterpret_cast<v4f*>(sM + (idx / V) * RS + (idx % V) * 4) = tmp[it];
+                *reinterpret_cast<v4f*>(sDI + (idx / V) * RS + (idx % V) * 4) = tmp[it];
         }
     }
     if (tid < KC) sCdt[tid] = cc[tid];
@@ -561,21 +579,30 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
     const float dec_end = expf(static_cast<float>(a * (end - cs)));
     const float bbar = dts * dec_end;
     __syncthreads();
-    // the chunk's C and dy rows load into registers during K3
-    constexpr int VC = R / 4, TC = KC * VC, ITC = (TC + NTS - 1) / NTS;
-    constexpr int VD = P / 4, TD = KC * VD, ITD = (TD + NTS - 1) / NTS;
-    v4f preC[ITC], preD[ITD];
+    // the chunk's C and dy rows load during K3, as raw bf16: item (row group q4, feature
+    // group f4) is rows 4 q4 .. 4 q4 + 3 at features 4 f4 .. 4 f4 + 3
+    constexpr int NIC = (KC / 4) * (R / 4), ITC = (NIC + NTS - 1) / NTS;
+    constexpr int NID = (KC / 4) * (P / 4), ITD = (NID + NTS - 1) / NTS;
+    uint2 pc[ITC][4], pd[ITD][4];
 #pragma unroll
     for (int it = 0; it < ITC; ++it) {
         const int idx = tid + it * NTS;
-        if (TC % NTS == 0 || idx < TC)
-            preC[it] = io<IO>::ld4(Cm, brow0 + static_cast<int64_t>(idx / VC) * bstride + (idx % VC) * 4);
+        if (NIC % NTS == 0 || idx < NIC) {
+            const int q4 = idx / (R / 4), f4 = idx % (R / 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                pc[it][e] = *reinterpret_cast<const uint2*>(Cm + brow0 + static_cast<int64_t>(4 * q4 + e) * bstride + 4 * f4);
+        }
     }
 #pragma unroll
     for (int it = 0; it < ITD; ++it) {
         const int idx = tid + it * NTS;
-        if (TD % NTS == 0 || idx < TD)
-            preD[it] = io<IO>::ld4(dy, xrow0 + static_cast<int64_t>(idx / VD) * xstride + (idx % VD) * 4);
+        if (NID % NTS == 0 || idx < NID) {
+            const int q4 = idx / (P / 4), f4 = idx % (P / 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                pd[it][e] = *reinterpret_cast<const uint2*>(dy + xrow0 + static_cast<int64_t>(4 * q4 + e) * xstride + 4 * f4);
+        }
     }
 
     // K3 backward.  d_b_scaled^T[r, s] = sum_p d_intra[p, r] x[s, p]
@@ -588,7 +615,7 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
         for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                accB[rt] = mfma16(sM[(16 * kk + 4 * g + v) * RS + rt * 16 + i], xreg[kk][v], accB[rt]);
+                accB[rt] = mfma16(sDI[(16 * kk + 4 * g + v) * RS + rt * 16 + i], xreg[kk][v], accB[rt]);
     float dbb = 0.0f;  // d_bbar[s] = sum_r d_b_scaled[s, r] B[s, r] (this lane's part)
 #pragma unroll
     for (int rt = 0; rt < R / 16; ++rt) {
@@ -604,7 +631,7 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
     for (int kk = 0; kk < R / 16; ++kk)
 #pragma unroll
         for (int pt = 0; pt < P / 16; ++pt) {
-            const v4f u = *reinterpret_cast<const v4f*>(sM + (pt * 16 + i) * RS + 16 * kk + 4 * g);
+            const v4f u = *reinterpret_cast<const v4f*>(sDI + (pt * 16 + i) * RS + 16 * kk + 4 * g);
 #pragma unroll
             for (int v = 0; v < 4; ++v) accX[pt] = mfma16(u[v], breg[kk][v], accX[pt]);
         }
@@ -618,38 +645,61 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
         dD += static_cast<double>(dyv[0] * xreg[pt][0] + dyv[1] * xreg[pt][1]) +
               static_cast<double>(dyv[2] * xreg[pt][2] + dyv[3] * xreg[pt][3]);
     }
+    // the own rows from here on only feed bf16 MFMAs: packed once
+    s4 xpk[P / 16], bpk[R / 16];
+#pragma unroll
+    for (int kk = 0; kk < P / 16; ++kk) xpk[kk] = pack_bf16x4(xreg[kk]);
+#pragma unroll
+    for (int kk = 0; kk < R / 16; ++kk) bpk[kk] = pack_bf16x4(breg[kk]);
     __syncthreads();  // K3 is done with d_intra
+    // the four rows of an item at one feature, as one 8-byte group entry
+    auto group4 = [](const uint2 (&r)[4], int f) __attribute__((always_inline)) {
+        const int sh = (f & 1) * 16;
+        const uint32_t w0 = (f < 2 ? r[0].x : r[0].y) >> sh, w1 = (f < 2 ? r[1].x : r[1].y) >> sh;
+        const uint32_t w2 = (f < 2 ? r[2].x : r[2].y) >> sh, w3 = (f < 2 ? r[3].x : r[3].y) >> sh;
+        return uint2{(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
+    };
 #pragma unroll
     for (int it = 0; it < ITC; ++it) {
         const int idx = tid + it * NTS;
-        if (TC % NTS == 0 || idx < TC) *reinterpret_cast<v4f*>(sC + (idx / VC) * RS + (idx % VC) * 4) = preC[it];
+        if (NIC % NTS == 0 || idx < NIC) {
+            const int q4 = idx / (R / 4), f4 = idx % (R / 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) *reinterpret_cast<uint2*>(sCr + (4 * q4 + e) * RB + 4 * f4) = pc[it][e];
+#pragma unroll
+            for (int f = 0; f < 4; ++f) *reinterpret_cast<uint2*>(sCq + (q4 * RB + 4 * f4 + f) * 4) = group4(pc[it], f);
+        }
     }
 #pragma unroll
     for (int it = 0; it < ITD; ++it) {
         const int idx = tid + it * NTS;
-        if (TD % NTS == 0 || idx < TD) *reinterpret_cast<v4f*>(sDY + (idx / VD) * PS + (idx % VD) * 4) = preD[it];
+        if (NID % NTS == 0 || idx < NID) {
+            const int q4 = idx / (P / 4), f4 = idx % (P / 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) *reinterpret_cast<uint2*>(sDr + (4 * q4 + e) * PB + 4 * f4) = pd[it][e];
+#pragma unroll
+            for (int f = 0; f < 4; ++f) *reinterpret_cast<uint2*>(sDq + (q4 * PB + 4 * f4 + f) * 4) = group4(pd[it], f);
+        }
     }
     __syncthreads();
 
     double dA = 0.0;  // this lane's part of the chunk's d_A (the pair terms and K3)
-    // One (target tile j, source tile s) pair, j >= s: the source tile's operands xr / br,
-    // cumsum csr and dt dtr of this lane's source row 16 s + i, its accumulators.  The
-    // pair's d_CB tile goes to the target-row kernel.
-    auto tile = [&](int j, int s, const v4f (&xr)[P / 16], const v4f (&br)[R / 16], double csr,
+    // One (target tile j, source tile s) pair, j >= s: the source tile's packed operands
+    // xr / br, cumsum csr and dt dtr of this lane's source row 16 s + i, its accumulators.
+    // The pair's d_CB tile goes to the target-row kernel.
+    auto tile = [&](int j, int s, const s4 (&xr)[P / 16], const s4 (&br)[R / 16], double csr,
                     float dtr, v4f (&aX)[P / 16], v4f (&aB)[R / 16], float& ddt,
                     float& dsr) __attribute__((always_inline)) {
-        // tiles with M = t (16j + 4g + v), N = s
+        // tiles with M = t (16j + 4g + v), N = s: exact bf16 products
         v4f cb = zero4(), dw = zero4();
 #pragma unroll
-        for (int kk = 0; kk < R / 16; ++kk) {
-            const v4f u = *reinterpret_cast<const v4f*>(sC + (16 * j + i) * RS + 16 * kk + 4 * g);
-            cb = mfma_k16<IO>(u, br[kk], cb);
-        }
+        for (int kk = 0; kk < R / 16; ++kk)
+            cb = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ld_s4(sCr + (16 * j + i) * RB + 16 * kk + 4 * g),
+                                                          br[kk], cb, 0, 0, 0);
 #pragma unroll
-        for (int kk = 0; kk < P / 16; ++kk) {
-            const v4f u = *reinterpret_cast<const v4f*>(sDY + (16 * j + i) * PS + 16 * kk + 4 * g);
-            dw = mfma_k16<IO>(u, xr[kk], dw);
-        }
+        for (int kk = 0; kk < P / 16; ++kk)
+            dw = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ld_s4(sDr + (16 * j + i) * PB + 16 * kk + 4 * g),
+                                                          xr[kk], dw, 0, 0, 0);
         const v2d ct01 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g);
         const v2d ct23 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g + 2);
         const double ctv[4] = {ct01.x, ct01.y, ct23.x, ct23.y};
@@ -670,29 +720,21 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
             dA += static_cast<double>(dd) * gap;
             tdst[(4 * g + v) * 16 + i] = dcb[v];
         }
-        // dy and C are exact bf16, W and d_CB are split once into three exact bf16 parts
-        {
-            const S4x3 ws = split4(v4f{wv[0], wv[1], wv[2], wv[3]});
-            const S4x3 ds = split4(v4f{dcb[0], dcb[1], dcb[2], dcb[3]});
+        // W and d_CB split once into three exact bf16 parts; dy and C exact
+        const S4x3 ws = split4(v4f{wv[0], wv[1], wv[2], wv[3]});
+        const S4x3 ds = split4(v4f{dcb[0], dcb[1], dcb[2], dcb[3]});
+        // ORANGE: d_x^T[p, s] += sum_t dy[t, p] W[t, s]
 #pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt) {
-                v4f av;
+        for (int pt = 0; pt < P / 16; ++pt)
+            aX[pt] = mfma16_split(ld_s4(sDq + ((4 * j + g) * PB + 16 * pt + i) * 4), ws, aX[pt]);
+        // K2 backward: d_B^T[r, s] += sum_t C[t, r] d_CB[t, s]
 #pragma unroll
-                for (int v = 0; v < 4; ++v) av[v] = sDY[(16 * j + 4 * g + v) * PS + pt * 16 + i];
-                aX[pt] = mfma16_split(pack_bf16x4(av), ws, aX[pt]);
-            }
-#pragma unroll
-            for (int rt = 0; rt < R / 16; ++rt) {
-                v4f av;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) av[v] = sC[(16 * j + 4 * g + v) * RS + rt * 16 + i];
-                aB[rt] = mfma16_split(pack_bf16x4(av), ds, aB[rt]);
-            }
-        }
+        for (int rt = 0; rt < R / 16; ++rt)
+            aB[rt] = mfma16_split(ld_s4(sCq + ((4 * j + g) * RB + 16 * rt + i) * 4), ds, aB[rt]);
     };
     float ddt_or = 0.0f, dsrc = 0.0f;
     const int jend = wave < 4 ? so + 4 : NRT - 1;
-    for (int j = so; j <= jend; ++j) tile(j, so, xreg, breg, cs, dts, accX, accB, ddt_or, dsrc);
+    for (int j = so; j <= jend; ++j) tile(j, so, xpk, bpk, cs, dts, accX, accB, ddt_or, dsrc);
 
     // The own tile's outputs: d_x and d_B rows (stored from the accumulators: staging them
     // through LDS for whole-row stores was 4 % slower), and per row d_dt (ORANGE + K3), g2,
@@ -719,17 +761,18 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
         // the partial of source tile s2 = w - 4 (its targets s2 + 5 .. 7) for wave s2
         finalize();
         const int s2 = wave - 4, sp2 = 16 * s2 + i;
-        v4f x2[P / 16], b2[R / 16], aX2[P / 16], aB2[R / 16];
+        s4 x2[P / 16], b2[R / 16];
+        v4f aX2[P / 16], aB2[R / 16];
         const int64_t xr2 = xrow0 + static_cast<int64_t>(sp2) * xstride;
         const int64_t br2 = brow0 + static_cast<int64_t>(sp2) * bstride;
 #pragma unroll
         for (int kk = 0; kk < P / 16; ++kk) {
-            x2[kk] = io<IO>::ld4(x, xr2 + 16 * kk + 4 * g);
+            x2[kk] = *reinterpret_cast<const s4*>(x + xr2 + 16 * kk + 4 * g);
             aX2[kk] = zero4();
         }
 #pragma unroll
         for (int kk = 0; kk < R / 16; ++kk) {
-            b2[kk] = io<IO>::ld4(Bm, br2 + 16 * kk + 4 * g);
+            b2[kk] = *reinterpret_cast<const s4*>(Bm + br2 + 16 * kk + 4 * g);
             aB2[kk] = zero4();
         }
         const double cs2 = sCdt[sp2];
@@ -748,7 +791,7 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
         pp[(NEX - 2) * 64 + lane] = ddt2;
         pp[(NEX - 1) * 64 + lane] = dsr2;
     }
-    __syncthreads();  // every pair tile is done (the partner rows are free), partials are in
+    __syncthreads();  // every pair tile is done, the partials are in
     if (wave < 3) {
         const float* pp = sPart + wave * (NEX * 64);
 #pragma unroll
