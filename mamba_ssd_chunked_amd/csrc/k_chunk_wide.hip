@@ -55,21 +55,24 @@ struct Q {
     static constexpr int value = N;
 };
 
+// bf16 rows staged in four-row groups ([t / 4][feature][t % 4]): r holds rows 4q .. 4q + 3
+// at features 4 f4 .. 4 f4 + 3 (raw bf16, two per word); the group entry of feature
+// 4 f4 + f is those four rows' values, one 8-byte LDS word.
+__device__ __forceinline__ uint2 group4(const uint2 (&r)[4], int f) {
+    const int sh = (f & 1) * 16;
+    const uint32_t w0 = (f < 2 ? r[0].x : r[0].y) >> sh, w1 = (f < 2 ? r[1].x : r[1].y) >> sh;
+    const uint32_t w2 = (f < 2 ? r[2].x : r[2].y) >> sh, w3 = (f < 2 ? r[3].x : r[3].y) >> sh;
+    return uint2{(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------- K5
 // Wave w owns target tiles tt = {w, 7 - w}.  acc[q][pt][v] is y[t][p] with
 // t = 16 tt[q] + 4g + v, p = 16 pt + i (BLUE e_t C_t S_in, then ORANGE, then D x).
-// With bf16 io three workgroups per CU (168 registers; 221 -> 195 us on the 2.7B-shaped
-// workload) hide the loads of the halves that fp32 io hides with a register prefetch
-// (there the third workgroup's register limit spills: 0.93 -> 1.10 ms on 64k tokens).
-template <class IO>
-constexpr int k5w_groups() {
-    return sizeof(typename IO::T) == 2 ? 3 : 2;
-}
-
+// fp32 io (bf16 io: k5_chunk_scan_wb below).
 template <class IO, int P, int R>
-__global__ __launch_bounds__(NT, k5w_groups<IO>()) void k5_chunk_scan_w(
+__global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
     const typename IO::T* __restrict__ x, const float* __restrict__ dt,
     const typename IO::T* __restrict__ Bm, const typename IO::T* __restrict__ Cm,
     const float* __restrict__ Av, const float* __restrict__ Dv, const double* __restrict__ cdt,
@@ -104,13 +107,10 @@ __global__ __launch_bounds__(NT, k5w_groups<IO>()) void k5_chunk_scan_w(
     }
     __syncthreads();
 
-    // fp32 io: the even half of the source rows loads into registers during BLUE
-    constexpr bool kPre = k5w_groups<IO>() == 2;
-    v4f preB[kPre ? RowTiles<R, TB>::IT : 1], preX[kPre ? RowTiles<P, TB>::IT : 1];
-    if constexpr (kPre) {
-        load_half_rows<IO, R>(preB, Bm + brow0, bstride, 0);
-        load_half_rows<IO, P>(preX, x + xrow0, xstride, 0);
-    }
+    // the even half of the source rows loads into registers during BLUE
+    v4f preB[RowTiles<R, TB>::IT], preX[RowTiles<P, TB>::IT];
+    load_half_rows<IO, R>(preB, Bm + brow0, bstride, 0);
+    load_half_rows<IO, P>(preX, x + xrow0, xstride, 0);
     v4f acc[2][P / 16];
 #pragma unroll
     for (int q = 0; q < 2; ++q)
@@ -173,38 +173,20 @@ __global__ __launch_bounds__(NT, k5w_groups<IO>()) void k5_chunk_scan_w(
                 const double gap = keep ? ct[q] - csv[v] : 0.0;
                 wv[q][v] = cbt[q][v] * exp2_of(la2 * gap) * dts[v] * (keep ? 1.0f : 0.0f);
             }
-        if constexpr (sizeof(typename IO::T) == 2) {
-            // bf16 io: x exact, W split once per own tile (ssd_device.hpp)
-            S4x3 ws[2];
 #pragma unroll
-            for (int q = QLO; q < 2; ++q) ws[q] = split4(v4f{wv[q][0], wv[q][1], wv[q][2], wv[q][3]});
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt) {
-                const s4 b = pack_bf16x4(v4f{xs[0][pt], xs[1][pt], xs[2][pt], xs[3][pt]});
+            for (int pt = 0; pt < P / 16; ++pt)
 #pragma unroll
-                for (int q = QLO; q < 2; ++q) acc[q][pt] = mfma16_split(ws[q], b, acc[q][pt]);
-            }
-        } else {
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-#pragma unroll
-                for (int pt = 0; pt < P / 16; ++pt)
-#pragma unroll
-                    for (int q = QLO; q < 2; ++q) acc[q][pt] = mfma16(wv[q][v], xs[v][pt], acc[q][pt]);
-        }
+                for (int q = QLO; q < 2; ++q) acc[q][pt] = mfma16(wv[q][v], xs[v][pt], acc[q][pt]);
     };
     const float Dh = Dv[c.h];
     for (int half = 0; half < 2; ++half) {
         __syncthreads();  // the previous contents of sM are consumed
-        if constexpr (kPre) {
-            store_rows<R, TB>(sB, preB);
-            store_rows<P, TB>(sX, preX);
-        } else {
-            stage_half_rows<IO, R>(sB, Bm + brow0, bstride, half);
-            stage_half_rows<IO, P>(sX, x + xrow0, xstride, half);
-        }
+        store_rows<R, TB>(sB, preB);
+        store_rows<P, TB>(sX, preX);
         __syncthreads();
-        if (kPre && half == 0) {
+        if (half == 0) {
             load_half_rows<IO, R>(preB, Bm + brow0, bstride, 1);
             load_half_rows<IO, P>(preX, x + xrow0, xstride, 1);
         }
@@ -234,6 +216,205 @@ __global__ __launch_bounds__(NT, k5w_groups<IO>()) void k5_chunk_scan_w(
         }
 }
 
+// K5 with bf16 io.  The halves' B rows are staged as bf16 row-major (stride R + 16): the
+// A operand of C B^T, four features of one row.  Their x rows go in four-row groups
+// (stride P + 16): the operand of W x, one feature of four rows.  The own C rows are
+// packed once after BLUE.  Every MFMA operand is one 8-byte read with no conversion
+// (the fp32 staging read scalars and repacked them for every MFMA), and the LDS of a half
+// fits within that of S_in.  Three workgroups per CU (at most 168 registers) hide the
+// loads of the halves, which fp32 io hides with a register prefetch.
+template <int P, int R>
+__global__ __launch_bounds__(NT, 3) void k5_chunk_scan_wb(
+    const BF16::T* __restrict__ x, const float* __restrict__ dt, const BF16::T* __restrict__ Bm,
+    const BF16::T* __restrict__ Cm, const float* __restrict__ Av, const float* __restrict__ Dv,
+    const double* __restrict__ cdt, const float* __restrict__ S, BF16::T* __restrict__ y, int N,
+    int H) {
+    using IO = BF16;
+    constexpr int RS = R + 4, L = KC, RB = R + 16, PB = P + 16;
+    constexpr int HB = TB * RB, HX = (TB / 4) * PB * 4;  // uint16 of a half: B rows, x groups
+    constexpr int MAINF = P * RS > (HB + HX) / 2 ? P * RS : (HB + HX) / 2;
+    __shared__ __align__(16) float sM[MAINF];  // S_in [P, R], then one half of B | x
+    uint16_t* const sBr = reinterpret_cast<uint16_t*>(sM);
+    uint16_t* const sXq = sBr + HB;
+    __shared__ __align__(16) double sCdt[KC];
+    __shared__ __align__(16) float sDt[KC];
+    const ChunkHead c = decode_ch(blockIdx.x, N, H);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    const int64_t xrow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(P);
+    const int64_t xstride = static_cast<int64_t>(H) * P;
+    const int64_t brow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(R);
+    const int64_t bstride = static_cast<int64_t>(H) * R;
+    const double* cc = cdt + c.c_bhn * L;
+    const double la2 = static_cast<double>(Av[c.h]) * kLog2e;
+    const int tt[2] = {wave, NRT - 1 - wave};
+    const int tl[2] = {16 * tt[0] + i, 16 * tt[1] + i};
+    auto ld_s4 = [](const uint16_t* p) __attribute__((always_inline)) {
+        return *reinterpret_cast<const s4*>(p);
+    };
+
+    v4f creg[2][R / 16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int kk = 0; kk < R / 16; ++kk)
+            creg[q][kk] = io<IO>::ld4(Cm, brow0 + static_cast<int64_t>(tl[q]) * bstride + 16 * kk + 4 * g);
+    stage_mat<R, P>(sM, S + c.ch * (P * R));
+    if (tid < KC) {
+        sCdt[tid] = cc[tid];
+        sDt[tid] = dt[c.c_bhn * L + tid];
+    }
+    __syncthreads();
+
+    v4f acc[2][P / 16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt) acc[q][pt] = zero4();
+    // BLUE: A = C rows (k = r), B operand = S_in[p, r] read along r (fp32 MFMAs: the fp32
+    // operand streams from LDS)
+#pragma unroll
+    for (int kk = 0; kk < R / 16; ++kk) {
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt) {
+            const v4f bop = *reinterpret_cast<const v4f*>(sM + (pt * 16 + i) * RS + 16 * kk + 4 * g);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) acc[q][pt] = mfma16(creg[q][kk][v], bop[v], acc[q][pt]);
+        }
+    }
+    double ct[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        ct[q] = sCdt[tl[q]];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float e = exp2_of(la2 * sCdt[16 * tt[q] + 4 * g + v]);
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt) acc[q][pt][v] *= e;
+        }
+    }
+    s4 cpk[2][R / 16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int kk = 0; kk < R / 16; ++kk) cpk[q][kk] = pack_bf16x4(creg[q][kk]);
+
+    // ORANGE over source tiles j <= tt[q] (u: the tile's place in its half)
+    auto tile = [&](int j, int u, auto qlo) {
+        constexpr int QLO = decltype(qlo)::value;
+        v4f cbt[2];
+#pragma unroll
+        for (int q = QLO; q < 2; ++q) cbt[q] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < R / 16; ++kk) {
+            const s4 aop = ld_s4(sBr + (16 * u + i) * RB + 16 * kk + 4 * g);
+#pragma unroll
+            for (int q = QLO; q < 2; ++q)
+                cbt[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, cpk[q][kk], cbt[q], 0, 0, 0);
+        }
+        const v2d cs01 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g);
+        const v2d cs23 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g + 2);
+        const v4f dts = *reinterpret_cast<const v4f*>(sDt + 16 * j + 4 * g);
+        const double csv[4] = {cs01.x, cs01.y, cs23.x, cs23.y};
+        // the update's x operands (rows 16 j + 4g .. + 3 at p = 16 pt + i), read before the
+        // decay math so their LDS latency overlaps it
+        s4 xb[P / 16];
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt) xb[pt] = ld_s4(sXq + ((4 * u + g) * PB + 16 * pt + i) * 4);
+        float wv[2][4];
+#pragma unroll
+        for (int q = QLO; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                // masked pairs (s > t) take gap 0 and weight 0: arithmetic, not a branch
+                const bool keep = (j < tt[q]) || (16 * j + 4 * g + v <= tl[q]);
+                const double gap = keep ? ct[q] - csv[v] : 0.0;
+                wv[q][v] = cbt[q][v] * exp2_of(la2 * gap) * dts[v] * (keep ? 1.0f : 0.0f);
+            }
+        // x exact, W split once per own tile (ssd_device.hpp)
+        S4x3 ws[2];
+#pragma unroll
+        for (int q = QLO; q < 2; ++q) ws[q] = split4(v4f{wv[q][0], wv[q][1], wv[q][2], wv[q][3]});
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt)
+#pragma unroll
+            for (int q = QLO; q < 2; ++q) acc[q][pt] = mfma16_split(ws[q], xb[pt], acc[q][pt]);
+    };
+    const float Dh = Dv[c.h];
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+        __syncthreads();  // the previous contents of sM are consumed
+        {
+            // LDS row 16 u + e of the half is chunk row 16 (2u + half) + e
+            auto crow = [&](int lr) { return 16 * (2 * (lr >> 4) + half) + (lr & 15); };
+            constexpr int NB = TB * (R / 4), ITB = (NB + NT - 1) / NT;
+            constexpr int NX = (TB / 4) * (P / 4), ITX = (NX + NT - 1) / NT;
+            uint2 rb[ITB], rx[ITX][4];
+#pragma unroll
+            for (int it = 0; it < ITB; ++it) {
+                const int idx = tid + it * NT;
+                if (NB % NT == 0 || idx < NB)
+                    rb[it] = *reinterpret_cast<const uint2*>(
+                        Bm + brow0 + static_cast<int64_t>(crow(idx / (R / 4))) * bstride + 4 * (idx % (R / 4)));
+            }
+#pragma unroll
+            for (int it = 0; it < ITX; ++it) {
+                const int idx = tid + it * NT;
+                if (NX % NT == 0 || idx < NX) {
+                    const int q4 = idx / (P / 4), f4 = idx % (P / 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        rx[it][e] = *reinterpret_cast<const uint2*>(
+                            x + xrow0 + static_cast<int64_t>(crow(4 * q4 + e)) * xstride + 4 * f4);
+                }
+            }
+#pragma unroll
+            for (int it = 0; it < ITB; ++it) {
+                const int idx = tid + it * NT;
+                if (NB % NT == 0 || idx < NB)
+                    *reinterpret_cast<uint2*>(sBr + (idx / (R / 4)) * RB + 4 * (idx % (R / 4))) = rb[it];
+            }
+#pragma unroll
+            for (int it = 0; it < ITX; ++it) {
+                const int idx = tid + it * NT;
+                if (NX % NT == 0 || idx < NX) {
+                    const int q4 = idx / (P / 4), f4 = idx % (P / 4);
+#pragma unroll
+                    for (int f = 0; f < 4; ++f)
+                        *reinterpret_cast<uint2*>(sXq + (q4 * PB + 4 * f4 + f) * 4) = group4(rx[it], f);
+                }
+            }
+        }
+        __syncthreads();
+        // SKIP: D x of this wave's target rows that sit in this half
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            if ((tt[q] & 1) == half)
+#pragma unroll
+                for (int pt = 0; pt < P / 16; ++pt) {
+                    const s4 xv = ld_s4(sXq + ((4 * (tt[q] >> 1) + g) * PB + 16 * pt + i) * 4);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc[q][pt][v] += Dh * bf16_to_f32(static_cast<uint16_t>(xv[v]));
+                }
+        for (int u = 0; u < 4; ++u) {
+            const int j = 2 * u + half;
+            if (j <= tt[0]) tile(j, u, Q<0>{});
+            else if (j <= tt[1]) tile(j, u, Q<1>{});
+        }
+    }
+
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t row = xrow0 + static_cast<int64_t>(16 * tt[q] + 4 * g + v) * xstride;
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt) st_nt<IO>(y, row + pt * 16 + i, acc[q][pt][v]);
+        }
+}
+
 // ---------------------------------------------------------- backward, rows t
 // Runs after the source-row kernel, which leaves the d_CB tile of every causal pair tile
 // of the chunk (pair_index order).  Wave w owns
@@ -241,9 +422,15 @@ __global__ __launch_bounds__(NT, k5w_groups<IO>()) void k5_chunk_scan_w(
 // t = 16 tt[q] + i, r = 16 rt + 4g + v.  The whole chunk is in this workgroup, so K1's
 // backward (the suffix sums of the gradient w.r.t. the within-chunk cumsum, and
 // d_dt += A d_da) runs in its epilogue, on the source-row kernel's g2, d_delta and d_dt.
-template <int P, int R>
-constexpr int wide_target_lds() {  // S_in [P, R], then the chunk's B rows [KC, R]
-    return (P > KC ? P : KC) * (R + 4);
+// LDS floats: S_in [P, R] (stride R + 4), then the chunk's B rows -- fp32 rows of stride
+// R + 4, or with bf16 io four-row groups of bf16 (group stride R + 16), the layout of
+// their one use, the A operand of d_C += d_CB B (one feature of four consecutive rows:
+// one 8-byte read, no conversion).
+template <class IO, int P, int R>
+constexpr int wide_target_lds() {
+    constexpr int sin = P * (R + 4);
+    constexpr int rows = sizeof(typename IO::T) == 2 ? (KC / 4) * (R + 16) * 2 : KC * (R + 4);
+    return sin > rows ? sin : rows;
 }
 
 template <class IO, int P, int R>
@@ -255,7 +442,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
     const float* __restrict__ d_delta, typename IO::T* __restrict__ dC, float* __restrict__ d_dt,
     double* __restrict__ dA_T, int N, int H) {
     constexpr int RS = R + 4, L = KC, NBLK = KC / TB;
-    __shared__ float sM[wide_target_lds<P, R>()];
+    __shared__ __align__(16) float sM[wide_target_lds<IO, P, R>()];
     __shared__ __align__(16) double sCdt[KC];
     __shared__ double sG[KC];  // g1 per token: BLUE + ORANGE target side (gradient w.r.t. the cumsum)
     __shared__ double sRed[NT / 64];
@@ -364,7 +551,34 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
     // before its first LDS write (one memory latency: 1105 -> 1067 us on the 64k-token
     // workload against four batches of four)
     __syncthreads();
-    stage_rows<IO, R, KC, 16>(sM, Bm + brow0, bstride);
+    constexpr bool kB16 = sizeof(typename IO::T) == 2;
+    constexpr int RB = R + 16;  // bf16 group stride
+    uint16_t* const sBq = reinterpret_cast<uint16_t*>(sM);
+    if constexpr (kB16) {
+        constexpr int NI = (KC / 4) * (R / 4), IT = (NI + NT - 1) / NT;
+        uint2 rq[IT][4];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = tid + it * NT;
+            if (NI % NT == 0 || idx < NI) {
+                const int q4 = idx / (R / 4), f4 = idx % (R / 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    rq[it][e] = *reinterpret_cast<const uint2*>(Bm + brow0 + static_cast<int64_t>(4 * q4 + e) * bstride + 4 * f4);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = tid + it * NT;
+            if (NI % NT == 0 || idx < NI) {
+                const int q4 = idx / (R / 4), f4 = idx % (R / 4);
+#pragma unroll
+                for (int f = 0; f < 4; ++f) *reinterpret_cast<uint2*>(sBq + (q4 * RB + 4 * f4 + f) * 4) = group4(rq[it], f);
+            }
+        }
+    } else {
+        stage_rows<IO, R, KC, 16>(sM, Bm + brow0, bstride);
+    }
     __syncthreads();
     // K2 backward: d_C^T[r, t] += sum_s B[s, r] d_CB[t, s]
     auto pair = [&](int j, v4f dcb, auto qc) __attribute__((always_inline)) {
@@ -372,12 +586,9 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
         if constexpr (sizeof(typename IO::T) == 2) {
             const S4x3 ds = split4(dcb);  // bf16 io: B exact, d_CB split (ssd_device.hpp)
 #pragma unroll
-            for (int rt = 0; rt < R / 16; ++rt) {
-                v4f a;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) a[v] = sM[(16 * j + 4 * g + v) * RS + rt * 16 + i];
-                acc[q][rt] = mfma16_split(pack_bf16x4(a), ds, acc[q][rt]);
-            }
+            for (int rt = 0; rt < R / 16; ++rt)
+                acc[q][rt] = mfma16_split(*reinterpret_cast<const s4*>(sBq + ((4 * j + g) * RB + 16 * rt + i) * 4),
+                                          ds, acc[q][rt]);
         } else {
 #pragma unroll
             for (int rt = 0; rt < R / 16; ++rt)
@@ -652,13 +863,6 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
 #pragma unroll
     for (int kk = 0; kk < R / 16; ++kk) bpk[kk] = pack_bf16x4(breg[kk]);
     __syncthreads();  // K3 is done with d_intra
-    // the four rows of an item at one feature, as one 8-byte group entry
-    auto group4 = [](const uint2 (&r)[4], int f) __attribute__((always_inline)) {
-        const int sh = (f & 1) * 16;
-        const uint32_t w0 = (f < 2 ? r[0].x : r[0].y) >> sh, w1 = (f < 2 ? r[1].x : r[1].y) >> sh;
-        const uint32_t w2 = (f < 2 ? r[2].x : r[2].y) >> sh, w3 = (f < 2 ? r[3].x : r[3].y) >> sh;
-        return uint2{(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
-    };
 #pragma unroll
     for (int it = 0; it < ITC; ++it) {
         const int idx = tid + it * NTS;
@@ -858,10 +1062,16 @@ static hipError_t k5_wide_io(const Shape& s, const void* x, const float* dt, con
 #define X(PP, RR)                                                                                 \
     if (s.P == PP && s.R == RR) {                                                                 \
         if constexpr (wide_fits<PP, RR>()) {                                                      \
-            hipLaunchKernelGGL((k5_chunk_scan_w<IO, PP, RR>), dim3(static_cast<unsigned>(CH)),    \
-                               dim3(NT), 0, st, static_cast<const T*>(x), dt,                     \
-                               static_cast<const T*>(Bm), static_cast<const T*>(Cm), A, D, cdt, S, \
-                               static_cast<T*>(y), s.N, s.H);                                     \
+            if constexpr (sizeof(T) == 2)                                                         \
+                hipLaunchKernelGGL((k5_chunk_scan_wb<PP, RR>), dim3(static_cast<unsigned>(CH)),   \
+                                   dim3(NT), 0, st, static_cast<const T*>(x), dt,                 \
+                                   static_cast<const T*>(Bm), static_cast<const T*>(Cm), A, D,    \
+                                   cdt, S, static_cast<T*>(y), s.N, s.H);                         \
+            else                                                                                  \
+                hipLaunchKernelGGL((k5_chunk_scan_w<IO, PP, RR>), dim3(static_cast<unsigned>(CH)), \
+                                   dim3(NT), 0, st, static_cast<const T*>(x), dt,                 \
+                                   static_cast<const T*>(Bm), static_cast<const T*>(Cm), A, D,    \
+                                   cdt, S, static_cast<T*>(y), s.N, s.H);                         \
             return hipGetLastError();                                                             \
         }                                                                                         \
         return hipErrorInvalidValue;                                                              \
