@@ -116,12 +116,13 @@ __global__ __launch_bounds__(NT) void k_chunk_states(
     }
 }
 
-// The same contraction for bf16 io on the bf16 matrix cores.  U (x or dy) holds exact
-// bf16 values and is staged transposed as bf16; V (B or C) scaled by the token weight
-// is an fp32 operand, staged as its three exact bf16 parts (split3); each 32-token
-// slice is three 16x16x32 bf16 MFMAs per output tile instead of eight fp32 ones.  The
-// token stride of the bf16 tiles is 72 (144-byte rows: the 16-byte reads of 16
-// consecutive rows fall on distinct banks).
+// The same contraction for bf16 io on the bf16 matrix cores.  The token weight goes on
+// the U side, S = sum_t (w_t U_t)^T V_t: V (B or C) holds exact bf16 values and is staged
+// transposed as bf16; w U (U = x or dy, the narrower operand) is an fp32 operand, staged
+// as its three exact bf16 parts (split3).  Each 32-token slice is three 16x16x32 bf16
+// MFMAs per output tile instead of eight fp32 ones; a wave reads its U parts once per
+// slice and reuses them over its r tiles.  The token stride of the bf16 tiles is 72
+// (144-byte rows: the 16-byte reads of 16 consecutive rows fall on distinct banks).
 template <int P, int R>
 __global__ __launch_bounds__(NT) void k_chunk_states_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
@@ -130,8 +131,8 @@ __global__ __launch_bounds__(NT) void k_chunk_states_bf16(
     float* __restrict__ S, float* __restrict__ dS, const double* __restrict__ phi,
     float* __restrict__ T, int N, int H, int L, int job0) {
     constexpr int TS = TB + 8;
-    __shared__ __align__(16) uint16_t sU[P * TS];
-    __shared__ __align__(16) uint16_t sV[3][R * TS];
+    __shared__ __align__(16) uint16_t sU[3][P * TS];
+    __shared__ __align__(16) uint16_t sV[R * TS];
     __shared__ float sw[256];  // token weights of the chunk (L <= 256)
     const int job = job0 + static_cast<int>(blockIdx.y);
     const ChunkHead c = decode_ch(blockIdx.x, N, H);
@@ -177,9 +178,14 @@ __global__ __launch_bounds__(NT) void k_chunk_states_bf16(
             const int idx = tid + it * NT;
             if (RU::TOTAL % NT == 0 || idx < RU::TOTAL) {
                 const int row = RU::row(idx), c4 = RU::col4(idx);
+                const float w = sw[t0 + row];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sU[(c4 * 4 + e) * TS + row] = static_cast<uint16_t>(__float_as_uint(tu[it][e]) >> 16);
+                for (int e = 0; e < 4; ++e) {
+                    const Split3 sp = split3(tu[it][e] * w);
+                    sU[0][(c4 * 4 + e) * TS + row] = sp.hi;
+                    sU[1][(c4 * 4 + e) * TS + row] = sp.mid;
+                    sU[2][(c4 * 4 + e) * TS + row] = sp.lo;
+                }
             }
         }
 #pragma unroll
@@ -187,14 +193,9 @@ __global__ __launch_bounds__(NT) void k_chunk_states_bf16(
             const int idx = tid + it * NT;
             if (RV::TOTAL % NT == 0 || idx < RV::TOTAL) {
                 const int row = RV::row(idx), c4 = RV::col4(idx);
-                const float w = sw[t0 + row];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const Split3 sp = split3(tv[it][e] * w);
-                    sV[0][(c4 * 4 + e) * TS + row] = sp.hi;
-                    sV[1][(c4 * 4 + e) * TS + row] = sp.mid;
-                    sV[2][(c4 * 4 + e) * TS + row] = sp.lo;
-                }
+                for (int e = 0; e < 4; ++e)
+                    sV[(c4 * 4 + e) * TS + row] = static_cast<uint16_t>(__float_as_uint(tv[it][e]) >> 16);
             }
         }
         __syncthreads();
@@ -205,18 +206,24 @@ __global__ __launch_bounds__(NT) void k_chunk_states_bf16(
         if (active) {
 #pragma unroll
             for (int kk = 0; kk < TB / 32; ++kk) {
-                b8v av[PPW];
+                b8v ah[PPW], am[PPW], al[PPW];
 #pragma unroll
-                for (int q = 0; q < PPW; ++q)
-                    av[q] = *reinterpret_cast<const b8v*>(sU + ((pt0 + 4 * q) * 16 + i) * TS + 32 * kk + 8 * g);
+                for (int q = 0; q < PPW; ++q) {
+                    const int o = ((pt0 + 4 * q) * 16 + i) * TS + 32 * kk + 8 * g;
+                    ah[q] = *reinterpret_cast<const b8v*>(sU[0] + o);
+                    am[q] = *reinterpret_cast<const b8v*>(sU[1] + o);
+                    al[q] = *reinterpret_cast<const b8v*>(sU[2] + o);
+                }
 #pragma unroll
                 for (int k = 0; k < RPW; ++k) {
-                    const int o = ((rt0 + k) * 16 + i) * TS + 32 * kk + 8 * g;
-                    const b8v bh = *reinterpret_cast<const b8v*>(sV[0] + o);
-                    const b8v bm = *reinterpret_cast<const b8v*>(sV[1] + o);
-                    const b8v bl = *reinterpret_cast<const b8v*>(sV[2] + o);
+                    const b8v bv = *reinterpret_cast<const b8v*>(sV + ((rt0 + k) * 16 + i) * TS + 32 * kk + 8 * g);
 #pragma unroll
-                    for (int q = 0; q < PPW; ++q) acc[q][k] = mfma32_split(av[q], bh, bm, bl, acc[q][k]);
+                    for (int q = 0; q < PPW; ++q) {
+                        // the smallest part first into the fp32 accumulator
+                        acc[q][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[q], bv, acc[q][k], 0, 0, 0);
+                        acc[q][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[q], bv, acc[q][k], 0, 0, 0);
+                        acc[q][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[q], bv, acc[q][k], 0, 0, 0);
+                    }
                 }
             }
         }

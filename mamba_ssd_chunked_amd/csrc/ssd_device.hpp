@@ -94,14 +94,6 @@ __device__ __forceinline__ Split3 split3(float x) {
                   static_cast<uint16_t>(__float_as_uint(r2) >> 16)};
 }
 
-// One 32-wide k slice of a 16x16 product: a holds exact bf16 values, b an fp32 operand
-// given as its three parts (the smallest first into the fp32 accumulator).
-__device__ __forceinline__ v4f mfma32_split(b8v a, b8v bhi, b8v bmid, b8v blo, v4f c) {
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, blo, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bmid, c, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bhi, c, 0, 0, 0);
-}
-
 // The same on the 16x16x16 bf16 MFMA (k slices of 16, four k values per lane, the layout
 // of four fp32 16x16x4 MFMAs): an fp32 operand tile split once into three packed parts,
 // reused against every exact-bf16 operand it meets.
