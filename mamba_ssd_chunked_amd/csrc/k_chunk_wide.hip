@@ -220,9 +220,12 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
 // A operand of C B^T, four features of one row.  Their x rows go in four-row groups
 // (stride P + 16): the operand of W x, one feature of four rows.  The own C rows are
 // packed once after BLUE.  Every MFMA operand is one 8-byte read with no conversion
-// (the fp32 staging read scalars and repacked them for every MFMA), and the LDS of a half
-// fits within that of S_in.  Three workgroups per CU (at most 168 registers) hide the
-// loads of the halves, which fp32 io hides with a register prefetch.
+// (the fp32 staging read scalars and repacked them for every MFMA).  S_in, the fp32
+// operand of BLUE, is split once into its three exact bf16 parts as it is staged, so
+// BLUE runs on the bf16 matrix cores too (three 16x16x16 MFMAs per 16-wide k slice
+// instead of four fp32 ones at twice their time); the LDS of a half fits within that of
+// the parts.  Three workgroups per CU (at most 168 registers) hide the loads of the
+// halves, which fp32 io hides with a register prefetch.
 template <int P, int R>
 __global__ __launch_bounds__(NT, 3) void k5_chunk_scan_wb(
     const BF16::T* __restrict__ x, const float* __restrict__ dt, const BF16::T* __restrict__ Bm,
@@ -230,11 +233,13 @@ __global__ __launch_bounds__(NT, 3) void k5_chunk_scan_wb(
     const double* __restrict__ cdt, const float* __restrict__ S, BF16::T* __restrict__ y, int N,
     int H) {
     using IO = BF16;
-    constexpr int RS = R + 4, L = KC, RB = R + 16, PB = P + 16;
+    constexpr int L = KC, RB = R + 16, PB = P + 16, SB = R + 8;
     constexpr int HB = TB * RB, HX = (TB / 4) * PB * 4;  // uint16 of a half: B rows, x groups
-    constexpr int MAINF = P * RS > (HB + HX) / 2 ? P * RS : (HB + HX) / 2;
-    __shared__ __align__(16) float sM[MAINF];  // S_in [P, R], then one half of B | x
-    uint16_t* const sBr = reinterpret_cast<uint16_t*>(sM);
+    constexpr int SP = P * SB;                           // uint16 of one S_in part
+    constexpr int MAINH = 3 * SP > HB + HX ? 3 * SP : HB + HX;
+    // S_in [P, R] as its three exact bf16 parts (row stride R + 8), then one half of B | x
+    __shared__ __align__(16) uint16_t sMh[MAINH];
+    uint16_t* const sBr = sMh;
     uint16_t* const sXq = sBr + HB;
     __shared__ __align__(16) double sCdt[KC];
     __shared__ __align__(16) float sDt[KC];
@@ -258,7 +263,28 @@ __global__ __launch_bounds__(NT, 3) void k5_chunk_scan_wb(
 #pragma unroll
         for (int kk = 0; kk < R / 16; ++kk)
             creg[q][kk] = io<IO>::ld4(Cm, brow0 + static_cast<int64_t>(tl[q]) * bstride + 16 * kk + 4 * g);
-    stage_mat<R, P>(sM, S + c.ch * (P * R));
+    {
+        // S_in split once: each part as four-feature words, one 8-byte write per part
+        constexpr int V = R / 4, TOT = P * V, IT = (TOT + NT - 1) / NT;
+        const float* src = S + c.ch * (P * R);
+        v4f tmp[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = tid + it * NT;
+            if (TOT % NT == 0 || idx < TOT) tmp[it] = *reinterpret_cast<const v4f*>(src + idx * 4);
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = tid + it * NT;
+            if (TOT % NT == 0 || idx < TOT) {
+                const S4x3 sp = split4(tmp[it]);
+                const int o = (idx / V) * SB + (idx % V) * 4;
+                *reinterpret_cast<s4*>(sMh + o) = sp.hi;
+                *reinterpret_cast<s4*>(sMh + SP + o) = sp.mid;
+                *reinterpret_cast<s4*>(sMh + 2 * SP + o) = sp.lo;
+            }
+        }
+    }
     if (tid < KC) {
         sCdt[tid] = cc[tid];
         sDt[tid] = dt[c.c_bhn * L + tid];
@@ -270,17 +296,20 @@ __global__ __launch_bounds__(NT, 3) void k5_chunk_scan_wb(
     for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int pt = 0; pt < P / 16; ++pt) acc[q][pt] = zero4();
-    // BLUE: A = C rows (k = r), B operand = S_in[p, r] read along r (fp32 MFMAs: the fp32
-    // operand streams from LDS)
+    s4 cpk[2][R / 16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int kk = 0; kk < R / 16; ++kk) cpk[q][kk] = pack_bf16x4(creg[q][kk]);
+    // BLUE: A = C rows (k = r, exact), B operand = S_in[p, r] read along r (its parts)
 #pragma unroll
     for (int kk = 0; kk < R / 16; ++kk) {
 #pragma unroll
         for (int pt = 0; pt < P / 16; ++pt) {
-            const v4f bop = *reinterpret_cast<const v4f*>(sM + (pt * 16 + i) * RS + 16 * kk + 4 * g);
+            const int o = (pt * 16 + i) * SB + 16 * kk + 4 * g;
+            const S4x3 bop{ld_s4(sMh + o), ld_s4(sMh + SP + o), ld_s4(sMh + 2 * SP + o)};
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-#pragma unroll
-                for (int q = 0; q < 2; ++q) acc[q][pt] = mfma16(creg[q][kk][v], bop[v], acc[q][pt]);
+            for (int q = 0; q < 2; ++q) acc[q][pt] = mfma16_split(cpk[q][kk], bop, acc[q][pt]);
         }
     }
     double ct[2];
@@ -294,12 +323,6 @@ __global__ __launch_bounds__(NT, 3) void k5_chunk_scan_wb(
             for (int pt = 0; pt < P / 16; ++pt) acc[q][pt][v] *= e;
         }
     }
-    s4 cpk[2][R / 16];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int kk = 0; kk < R / 16; ++kk) cpk[q][kk] = pack_bf16x4(creg[q][kk]);
-
     // ORANGE over source tiles j <= tt[q] (u: the tile's place in its half)
     auto tile = [&](int j, int u, auto qlo) {
         constexpr int QLO = decltype(qlo)::value;
