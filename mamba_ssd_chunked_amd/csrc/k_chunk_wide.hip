@@ -449,10 +449,14 @@ __global__ __launch_bounds__(NT, 3) void k5_chunk_scan_wb(
 // R + 4, or with bf16 io four-row groups of bf16 (group stride R + 16), the layout of
 // their one use, the A operand of d_C += d_CB B (one feature of four consecutive rows:
 // one 8-byte read, no conversion).
+// With bf16 io S_in is staged as its three exact bf16 parts in four-row groups (group
+// stride R + 16), the layout of BLUE's A operand (S_in^T: one r, four consecutive p), so
+// BLUE runs on the bf16 matrix cores.
 template <class IO, int P, int R>
 constexpr int wide_target_lds() {
-    constexpr int sin = P * (R + 4);
-    constexpr int rows = sizeof(typename IO::T) == 2 ? (KC / 4) * (R + 16) * 2 : KC * (R + 4);
+    constexpr bool b16 = sizeof(typename IO::T) == 2;
+    constexpr int sin = b16 ? 3 * (P / 4) * (R + 16) * 2 : P * (R + 4);
+    constexpr int rows = b16 ? (KC / 4) * (R + 16) * 2 : KC * (R + 4);
     return sin > rows ? sin : rows;
 }
 
@@ -496,7 +500,53 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
     // S_in into LDS, and K4 backward's d_end = exp(A cdt[L-1]) <d_intra, S_in> from the
     // same registers: both matrices' loads are in flight together with the operand rows'
     double dA = 0.0;  // this thread's part of the chunk's d_A (pair form)
-    {
+    constexpr bool kB16 = sizeof(typename IO::T) == 2;
+    constexpr int RB = R + 16;                // bf16 group stride
+    constexpr int SPG = (P / 4) * RB * 4;     // uint16 of one S_in part (bf16 io)
+    uint16_t* const sMh = reinterpret_cast<uint16_t*>(sM);
+    if constexpr (kB16) {
+        // item (p4, r4): rows 4 p4 .. + 3 at r = 4 r4 .. + 3; each r's four p values split
+        // into three parts, one 8-byte group entry per part
+        constexpr int NI = (P / 4) * (R / 4), IT = (NI + NT - 1) / NT;
+        const float* sp = S + c.ch * (P * R);
+        const float* dsp = dS + c.ch * (P * R);
+        v4f sv[IT][4], dv[IT][4];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = tid + it * NT;
+            if (NI % NT == 0 || idx < NI) {
+                const int p4 = idx / (R / 4), r4 = idx % (R / 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sv[it][e] = *reinterpret_cast<const v4f*>(sp + (4 * p4 + e) * R + 4 * r4);
+                    dv[it][e] = *reinterpret_cast<const v4f*>(dsp + (4 * p4 + e) * R + 4 * r4);
+                }
+            }
+        }
+        double part = 0.0;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = tid + it * NT;
+            if (NI % NT == 0 || idx < NI) {
+                const int p4 = idx / (R / 4), r4 = idx % (R / 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    part += static_cast<double>(dv[it][e][0] * sv[it][e][0] + dv[it][e][1] * sv[it][e][1]) +
+                            static_cast<double>(dv[it][e][2] * sv[it][e][2] + dv[it][e][3] * sv[it][e][3]);
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    const S4x3 pz = split4(v4f{sv[it][0][f], sv[it][1][f], sv[it][2][f], sv[it][3][f]});
+                    const int o = (p4 * RB + 4 * r4 + f) * 4;
+                    *reinterpret_cast<s4*>(sMh + o) = pz.hi;
+                    *reinterpret_cast<s4*>(sMh + SPG + o) = pz.mid;
+                    *reinterpret_cast<s4*>(sMh + 2 * SPG + o) = pz.lo;
+                }
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+        if (lane == 0) sRed[wave] = part;
+    } else {
         constexpr int V = R / 4, TOT = P * V, IT = (TOT + NT - 1) / NT;
         const float* sp = S + c.ch * (P * R);
         const float* dsp = dS + c.ch * (P * R);
@@ -539,16 +589,34 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
     for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int rt = 0; rt < R / 16; ++rt) acc[q][rt] = zero4();
+    if constexpr (kB16) {
+        // dy exact, S_in as its parts: one group entry (p = 16 kk + 4g .. + 3 at r) per part
 #pragma unroll
-    for (int kk = 0; kk < P / 16; ++kk)
+        for (int kk = 0; kk < P / 16; ++kk) {
+            s4 dyp[2];
 #pragma unroll
-        for (int rt = 0; rt < R / 16; ++rt)
+            for (int q = 0; q < 2; ++q) dyp[q] = pack_bf16x4(dyreg[q][kk]);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float sv = sM[(16 * kk + 4 * g + v) * RS + rt * 16 + i];
+            for (int rt = 0; rt < R / 16; ++rt) {
+                const int o = ((4 * kk + g) * RB + 16 * rt + i) * 4;
+                const S4x3 sa{*reinterpret_cast<const s4*>(sMh + o), *reinterpret_cast<const s4*>(sMh + SPG + o),
+                              *reinterpret_cast<const s4*>(sMh + 2 * SPG + o)};
 #pragma unroll
-                for (int q = 0; q < 2; ++q) acc[q][rt] = mfma16(sv, dyreg[q][kk][v], acc[q][rt]);
+                for (int q = 0; q < 2; ++q) acc[q][rt] = mfma16_split(sa, dyp[q], acc[q][rt]);
             }
+        }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < P / 16; ++kk)
+#pragma unroll
+            for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float sv = sM[(16 * kk + 4 * g + v) * RS + rt * 16 + i];
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) acc[q][rt] = mfma16(sv, dyreg[q][kk][v], acc[q][rt]);
+                }
+    }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const double ct = sCdt[tl[q]];
@@ -574,9 +642,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
     // before its first LDS write (one memory latency: 1105 -> 1067 us on the 64k-token
     // workload against four batches of four)
     __syncthreads();
-    constexpr bool kB16 = sizeof(typename IO::T) == 2;
-    constexpr int RB = R + 16;  // bf16 group stride
-    uint16_t* const sBq = reinterpret_cast<uint16_t*>(sM);
+    uint16_t* const sBq = sMh;
     if constexpr (kB16) {
         constexpr int NI = (KC / 4) * (R / 4), IT = (NI + NT - 1) / NT;
         uint2 rq[IT][4];
@@ -739,8 +805,11 @@ struct SrcWLds {
     static constexpr int RB = R + 16, PB = P + 16;                // bf16 row / group strides
     static constexpr int CR = KC * RB, DR = KC * PB;              // row-major C, dy (uint16)
     static constexpr int CQ = (KC / 4) * RB * 4, DQ = (KC / 4) * PB * 4;  // grouped C, dy
-    static constexpr int TOTAL = CR + DR + CQ + DQ;
-    static_assert(P * (R + 4) * 2 <= TOTAL, "d_intra (fp32) fits where the rows go");
+    // K3's d_intra [P, R] as its three exact bf16 parts, row-major (row stride R + 8) and in
+    // four-row groups (group stride R + 16), where the rows go later
+    static constexpr int IR = P * (R + 8), IQ = (P / 4) * RB * 4;
+    static constexpr int ROWS = CR + DR + CQ + DQ, PARTS = 3 * (IR + IQ);
+    static constexpr int TOTAL = ROWS > PARTS ? ROWS : PARTS;
 };
 
 template <int P, int R>
@@ -754,14 +823,15 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
     double* __restrict__ dD_part, float* __restrict__ dcbt, int N, int H) {
     using IO = BF16;
     using LY = SrcWLds<P, R>;
-    constexpr int RS = R + 4, RB = LY::RB, PB = LY::PB, L = KC, NBLK = KC / TB;
+    constexpr int RB = LY::RB, PB = LY::PB, IRS = R + 8, L = KC, NBLK = KC / TB;
     constexpr int NEX = 4 * (P / 16 + R / 16) + 2;  // floats per lane of one handed-over partial
     __shared__ __align__(16) uint16_t sMb[LY::TOTAL];
     uint16_t* const sCr = sMb;
     uint16_t* const sDr = sCr + LY::CR;
     uint16_t* const sCq = sDr + LY::DR;
     uint16_t* const sDq = sCq + LY::CQ;
-    float* const sDI = reinterpret_cast<float*>(sMb);  // d_intra [P, R] (stride R + 4) during K3
+    uint16_t* const sIr = sMb;                // d_intra's parts during K3: row-major ...
+    uint16_t* const sIq = sMb + 3 * LY::IR;   // ... and in four-row groups
     __shared__ float sPart[3 * NEX * 64];
     __shared__ __align__(16) double sCdt[KC];
     __shared__ double sRed[2 * NWS];
@@ -790,20 +860,47 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
     for (int kk = 0; kk < P / 16; ++kk) xreg[kk] = io<IO>::ld4(x, xrow + 16 * kk + 4 * g);
 #pragma unroll
     for (int kk = 0; kk < R / 16; ++kk) breg[kk] = io<IO>::ld4(Bm, brow + 16 * kk + 4 * g);
-    {  // d_intra [P, R] (fp32) into LDS (row stride R + 4)
-        constexpr int V = R / 4, TOT = P * V, IT = (TOT + NTS - 1) / NTS;
+    {
+        // d_intra split once into its three exact bf16 parts: item (p4, r4) is rows
+        // 4 p4 .. + 3 at r = 4 r4 .. + 3; its rows go to the row-major parts, its columns
+        // to the grouped ones
+        constexpr int NI = (P / 4) * (R / 4), IT = (NI + NTS - 1) / NTS;
         const float* src = dS + c.ch * (P * R);
-        v4f tmp[IT];
+        v4f tmp[IT][4];
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             const int idx = tid + it * NTS;
-            if (TOT % NTS == 0 || idx < TOT) tmp[it] = *reinterpret_cast<const v4f*>(src + idx * 4);
+            if (NI % NTS == 0 || idx < NI) {
+                const int p4 = idx / (R / 4), r4 = idx % (R / 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tmp[it][e] = *reinterpret_cast<const v4f*>(src + (4 * p4 + e) * R + 4 * r4);
+            }
         }
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             const int idx = tid + it * NTS;
-            if (TOT % NTS == 0 || idx < TOT)
-                *reinterpret_cast<v4f*>(sDI + (idx / V) * RS + (idx % V) * 4) = tmp[it];
+            if (NI % NTS == 0 || idx < NI) {
+                const int p4 = idx / (R / 4), r4 = idx % (R / 4);
+                Split3 sp[4][4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) sp[e][f] = split3(tmp[it][e][f]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int o = (4 * p4 + e) * IRS + 4 * r4;
+                    *reinterpret_cast<s4*>(sIr + o) = s4{short(sp[e][0].hi), short(sp[e][1].hi), short(sp[e][2].hi), short(sp[e][3].hi)};
+                    *reinterpret_cast<s4*>(sIr + LY::IR + o) = s4{short(sp[e][0].mid), short(sp[e][1].mid), short(sp[e][2].mid), short(sp[e][3].mid)};
+                    *reinterpret_cast<s4*>(sIr + 2 * LY::IR + o) = s4{short(sp[e][0].lo), short(sp[e][1].lo), short(sp[e][2].lo), short(sp[e][3].lo)};
+                }
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    const int o = (p4 * RB + 4 * r4 + f) * 4;
+                    *reinterpret_cast<s4*>(sIq + o) = s4{short(sp[0][f].hi), short(sp[1][f].hi), short(sp[2][f].hi), short(sp[3][f].hi)};
+                    *reinterpret_cast<s4*>(sIq + LY::IQ + o) = s4{short(sp[0][f].mid), short(sp[1][f].mid), short(sp[2][f].mid), short(sp[3][f].mid)};
+                    *reinterpret_cast<s4*>(sIq + 2 * LY::IQ + o) = s4{short(sp[0][f].lo), short(sp[1][f].lo), short(sp[2][f].lo), short(sp[3][f].lo)};
+                }
+            }
         }
     }
     if (tid < KC) sCdt[tid] = cc[tid];
@@ -839,7 +936,17 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
         }
     }
 
-    // K3 backward.  d_b_scaled^T[r, s] = sum_p d_intra[p, r] x[s, p]
+    // the own rows feed only bf16 MFMAs: packed once
+    s4 xpk[P / 16], bpk[R / 16];
+#pragma unroll
+    for (int kk = 0; kk < P / 16; ++kk) xpk[kk] = pack_bf16x4(xreg[kk]);
+#pragma unroll
+    for (int kk = 0; kk < R / 16; ++kk) bpk[kk] = pack_bf16x4(breg[kk]);
+    auto parts = [&](const uint16_t* p0, int stride_parts, int o) __attribute__((always_inline)) {
+        return S4x3{ld_s4(p0 + o), ld_s4(p0 + stride_parts + o), ld_s4(p0 + 2 * stride_parts + o)};
+    };
+    // K3 backward.  d_b_scaled^T[r, s] = sum_p d_intra[p, r] x[s, p]: A = d_intra^T (one r,
+    // four consecutive p: a group entry), x exact
     v4f accB[R / 16];
 #pragma unroll
     for (int rt = 0; rt < R / 16; ++rt) accB[rt] = zero4();
@@ -847,9 +954,7 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
     for (int kk = 0; kk < P / 16; ++kk)
 #pragma unroll
         for (int rt = 0; rt < R / 16; ++rt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                accB[rt] = mfma16(sDI[(16 * kk + 4 * g + v) * RS + rt * 16 + i], xreg[kk][v], accB[rt]);
+            accB[rt] = mfma16_split(parts(sIq, LY::IQ, ((4 * kk + g) * RB + 16 * rt + i) * 4), xpk[kk], accB[rt]);
     float dbb = 0.0f;  // d_bbar[s] = sum_r d_b_scaled[s, r] B[s, r] (this lane's part)
 #pragma unroll
     for (int rt = 0; rt < R / 16; ++rt) {
@@ -857,18 +962,16 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
         for (int v = 0; v < 4; ++v) dbb += accB[rt][v] * breg[rt][v];
         accB[rt] *= bbar;
     }
-    // d_x^T[p, s] = bbar[s] sum_r d_intra[p, r] B[s, r]
+    // d_x^T[p, s] = bbar[s] sum_r d_intra[p, r] B[s, r]: A = d_intra (one p, four
+    // consecutive r: a row-major word), B exact
     v4f accX[P / 16];
 #pragma unroll
     for (int pt = 0; pt < P / 16; ++pt) accX[pt] = zero4();
 #pragma unroll
     for (int kk = 0; kk < R / 16; ++kk)
 #pragma unroll
-        for (int pt = 0; pt < P / 16; ++pt) {
-            const v4f u = *reinterpret_cast<const v4f*>(sDI + (pt * 16 + i) * RS + 16 * kk + 4 * g);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) accX[pt] = mfma16(u[v], breg[kk][v], accX[pt]);
-        }
+        for (int pt = 0; pt < P / 16; ++pt)
+            accX[pt] = mfma16_split(parts(sIr, LY::IR, (pt * 16 + i) * IRS + 16 * kk + 4 * g), bpk[kk], accX[pt]);
     // SKIP backward: d_x += D dy; d_D partial sum dy x
     const float Dh = Dv[c.h];
     double dD = 0.0;
@@ -879,12 +982,6 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
         dD += static_cast<double>(dyv[0] * xreg[pt][0] + dyv[1] * xreg[pt][1]) +
               static_cast<double>(dyv[2] * xreg[pt][2] + dyv[3] * xreg[pt][3]);
     }
-    // the own rows from here on only feed bf16 MFMAs: packed once
-    s4 xpk[P / 16], bpk[R / 16];
-#pragma unroll
-    for (int kk = 0; kk < P / 16; ++kk) xpk[kk] = pack_bf16x4(xreg[kk]);
-#pragma unroll
-    for (int kk = 0; kk < R / 16; ++kk) bpk[kk] = pack_bf16x4(breg[kk]);
     __syncthreads();  // K3 is done with d_intra
 #pragma unroll
     for (int it = 0; it < ITC; ++it) {
