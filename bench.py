@@ -80,27 +80,27 @@ def matrix_flops(w, kernel: str, k: int):
     operands, bf16 MFMA on the three exact bf16 parts of an fp32 operand), or None for a kernel
     without products.  Only the causal triangle counts (pairs s <= t of a chunk), each product
     once.  With bf16 io the products whose two operands are both bf16 inputs -- C B^T and
-    dy x^T -- run on bf16 MFMAs; those with one exact-bf16 operand and an fp32 operand that
-    the kernel holds in registers -- the decay-weighted tile W, d_CB, and every product of
-    the state kernel, whose fp32 operand is staged split -- run split; the rest (the BLUE
-    and K3 products, whose fp32 operand streams from LDS) on fp32 MFMAs."""
+    dy x^T -- run on bf16 MFMAs; every other product has one exact-bf16 operand and one
+    fp32 operand (the decay-weighted tile W, d_CB, S_in in BLUE, d_intra in K3, the
+    token-weighted rows of the state kernel) and runs split: three bf16 MFMAs on the fp32
+    operand's exact bf16 parts.  None runs on fp32 MFMAs."""
     b, n, l, h, p, r = _shape(w, k)
     ch = b * n * h                      # chunk-heads
     pairs = l * (l + 1) // 2            # (t, s) pairs with s <= t per chunk
     cb, dw = 2 * pairs * r, 2 * pairs * p          # C B^T and dy x^T tiles
     if kernel == "k_chunk_states":      # fwd: 1 job; bwd: 2 jobs (timed per launch: see jobs)
-        f32, both, split = 0, 0, 2 * l * p * r
+        both, split = 0, 2 * l * p * r
     elif kernel == "k5_chunk_scan":     # BLUE C S_in, C B^T, W x
-        f32, both, split = 2 * l * p * r, cb, 2 * pairs * p
+        both, split = cb, 2 * l * p * r + 2 * pairs * p
     elif kernel == "k_bwd_target":      # BLUE dy S_in, d_CB B (d_CB handed over by k_bwd_source)
-        f32, both, split = 2 * l * p * r, 0, 2 * pairs * r
+        both, split = 0, 2 * l * p * r + 2 * pairs * r
     elif kernel == "k_bwd_source":      # K3 (two products), C B^T, dy x^T, W^T dy, d_CB^T C
-        f32, both, split = 4 * l * p * r, cb + dw, 2 * pairs * p + 2 * pairs * r
+        both, split = cb + dw, 4 * l * p * r + 2 * pairs * p + 2 * pairs * r
     else:
         return None
     if w.io != "bf16":
-        return (f32 + both + split) * ch, 0, 0
-    return f32 * ch, both * ch, split * ch
+        return (both + split) * ch, 0, 0
+    return 0, both * ch, split * ch
 
 
 def mfma_roof_s(w, kernel: str, k: int, launches: float = 1.0):

@@ -98,17 +98,21 @@ def test_chunk_kernel_bytes_count_every_tensor_once():
 
 
 def test_matrix_flops_split_by_matrix_core_type():
-    """bf16 io: C B^T and dy x^T run on bf16 MFMAs, products with a register-held fp32
-    operand on the bf16 ones split in three, the LDS-streamed fp32 operands' on fp32 ones;
-    fp32 io: everything on fp32 ones.  The total is the same either way."""
+    """bf16 io: C B^T and dy x^T run on bf16 MFMAs, every product with an fp32 operand on
+    the bf16 ones split in three (nothing on fp32 ones); fp32 io: everything on fp32 ones.
+    The total is the same either way."""
     pairs = 128 * 129 // 2
     wb = inputs.WORKLOADS["mamba2_2p7b_bf16"]
     ch = 2 * (4096 // 128) * 80
     f32, both, split = bench.matrix_flops(wb, "k_bwd_source", 128)
-    assert f32 == 4 * 128 * 64 * 128 * ch                      # K3: fp32 operand from LDS
+    assert f32 == 0
     assert both == (2 * pairs * 128 + 2 * pairs * 64) * ch      # C B^T, dy x^T
-    assert split == (2 * pairs * 64 + 2 * pairs * 128) * ch     # W^T dy, d_CB^T C
+    # K3 (d_intra's parts), W^T dy, d_CB^T C
+    assert split == (4 * 128 * 64 * 128 + 2 * pairs * 64 + 2 * pairs * 128) * ch
     assert f32 + both + split == bench.kernel_work(wb, "k_bwd_source", 128)[0]
+    k5 = bench.matrix_flops(wb, "k5_chunk_scan", 128)
+    assert k5[0] == 0 and k5[1] == 2 * pairs * 128 * ch            # C B^T
+    assert k5[2] == (2 * 128 * 64 * 128 + 2 * pairs * 64) * ch     # BLUE (S_in's parts), W x
     assert bench.mfma_roof_s(wb, "k_bwd_source", 128) == pytest.approx(
         f32 / 157.3e12 + (both + 3 * split) / 2.5e15)
     # the state kernel's products run split on the bf16 cores: each costs three bf16 products
