@@ -45,23 +45,33 @@ HEADLINE = "long_context_64k_fp32"
 TRAFFIC = {
     ("k_bwd_source", "long_context_64k_fp32", 128): (5_406_783_488, 2_241_860_608, "88ee39c330ba78de"),
     ("k_bwd_source", "mamba2_130m_fp32", 128): (503_322_624, 210_186_240, "88ee39c330ba78de"),
+    ("k_bwd_source", "mamba2_2p7b_bf16", 128): (743_546_880, 448_644_096, "d0fd949bba144132"),
 }
-TRAFFIC_SOURCES = {"k_bwd_source": ("k_chunk_bwd.hip", "ssd_device.hpp"),
-                   "k_bwd_target": ("k_chunk_bwd.hip", "ssd_device.hpp")}
+# the files a kernel's code comes from, by io type: with bf16 io the source-row kernel at
+# 128-token chunks is the whole-chunk one
+TRAFFIC_SOURCES = {("k_bwd_source", "f32"): ("k_chunk_bwd.hip", "ssd_device.hpp"),
+                   ("k_bwd_source", "bf16"): ("k_chunk_wide.hip", "ssd_device.hpp"),
+                   ("k_bwd_target", "f32"): ("k_chunk_wide.hip", "ssd_device.hpp"),
+                   ("k_bwd_target", "bf16"): ("k_chunk_wide.hip", "ssd_device.hpp")}
+
+
+def traffic_hash(kernel: str, io: str) -> str:
+    """First 16 hex digits of the sha256 of the kernel's source files (TRAFFIC_SOURCES)."""
+    import hashlib
+    m = hashlib.sha256()
+    for f in TRAFFIC_SOURCES[(kernel, io)]:
+        with open(os.path.join(ROOT, "mamba_ssd_chunked_amd", "csrc", f), "rb") as fh:
+            m.update(fh.read())
+    return m.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, w, k: int):
     """HBM bytes per launch of `kernel` from the counter runs, or None when none were taken for
     this workload or the kernel's sources changed since."""
-    import hashlib
     ent = TRAFFIC.get((kernel, w.name, k))
     if ent is None:
         return None
-    m = hashlib.sha256()
-    for f in TRAFFIC_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "mamba_ssd_chunked_amd", "csrc", f), "rb") as fh:
-            m.update(fh.read())
-    return ent[0] + ent[1] if m.hexdigest()[:16] == ent[2] else None
+    return ent[0] + ent[1] if traffic_hash(kernel, w.io) == ent[2] else None
 
 
 def kernel_chunk_len(w, requested: int = 0) -> int:
