@@ -633,11 +633,16 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
 
     // the wave's pair tiles in order k = 0 .. 8: (own tile tt[0], source tile k) for k <= w,
     // then (tt[1], k - w - 1); each tile's d_CB (this lane's four s of row t = 16 tt + i)
-    // loads one tile ahead of its products
+    // loads DQ tiles ahead of its products: two with bf16 io (256 -> 242 us on the
+    // 2.7B-shaped workload), one with fp32 io (two spill registers there: 1074 -> 1091 us
+    // on the 64k-token workload)
     auto tile_at = [&](int k) -> int64_t {
         return k <= wave ? tiles0 + pair_index(tt[0], k) : tiles0 + pair_index(tt[1], k - wave - 1);
     };
-    v4f dnext = *reinterpret_cast<const v4f*>(dcbt + tile_at(0) * 256 + i * 16 + 4 * g);
+    constexpr int DQ = sizeof(typename IO::T) == 2 ? 2 : 1;
+    v4f dq[DQ];
+#pragma unroll
+    for (int d = 0; d < DQ; ++d) dq[d] = *reinterpret_cast<const v4f*>(dcbt + tile_at(d) * 256 + i * 16 + 4 * g);
     // the chunk's B rows into LDS once S_in is consumed, every load of a thread in flight
     // before its first LDS write (one memory latency: 1105 -> 1067 us on the 64k-token
     // workload against four batches of four)
@@ -686,14 +691,19 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
                     acc[q][rt] = mfma16(sM[(16 * j + 4 * g + v) * RS + rt * 16 + i], dcb[v], acc[q][rt]);
         }
     };
-    for (int k = 0; k < NRT + 1; ++k) {
-        const v4f dcur = dnext;
-        if (k + 1 < NRT + 1)
-            dnext = *reinterpret_cast<const v4f*>(dcbt + tile_at(k + 1) * 256 + i * 16 + 4 * g);
+    auto step = [&](int k, v4f& slot) __attribute__((always_inline)) {
+        const v4f dcur = slot;
+        if (k + DQ < NRT + 1) slot = *reinterpret_cast<const v4f*>(dcbt + tile_at(k + DQ) * 256 + i * 16 + 4 * g);
         if (k <= wave)
             pair(k, dcur, Q<0>{});
         else
             pair(k - wave - 1, dcur, Q<1>{});
+    };
+    if constexpr (DQ == 1) {
+        for (int k = 0; k < NRT + 1; ++k) step(k, dq[0]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < NRT + 1; ++k) step(k, dq[k % DQ]);
     }
 
 #pragma unroll
