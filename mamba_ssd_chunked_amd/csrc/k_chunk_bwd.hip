@@ -62,7 +62,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target(
     const typename IO::T* __restrict__ dy, const typename IO::T* __restrict__ Bm,
     const typename IO::T* __restrict__ Cm, const float* __restrict__ Av,
     const double* __restrict__ cdt, const float* __restrict__ S, const float* __restrict__ dS,
-    const float* __restrict__ dcbt,
+    const float* __restrict__ dcbt, const float* __restrict__ ddg,
     typename IO::T* __restrict__ dC, float* __restrict__ g1, float* __restrict__ d_end,
     double* __restrict__ dA_T, int N, int H, int L, int64_t CH) {
     constexpr int RS = R + 4;
@@ -146,7 +146,11 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target(
     }
     dA += static_cast<double>(gblue) * ct;
 
-    // K2 backward from the source-row kernel's d_CB tiles: d_C^T[r, t] += sum_s B[s, r] d_CB[t, s]
+    // K2 backward from the source-row kernel's d_CB tiles: d_C^T[r, t] += sum_s B[s, r] d_CB[t, s].
+    // The tiles hold the diagonal elements d_CB[t, t] as zeros (they come in ddg), so g1
+    // below leaves out the diagonal pair's d_diff, as g2 does in the source-row kernel: in
+    // exact arithmetic the two cancel, in fp32 each side rounds its own way and
+    // d_dt = ... + A d_da would carry |A| times the difference.  They join d_C after g1.
     for (int sb = 0; sb <= tb; ++sb) {
         const int jmax = (sb == tb) ? wave : 3;  // diagonal block: s-tiles up to this wave's
         v4f dct[4];
@@ -181,14 +185,9 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target(
             }
         }
     }
-    // store d_C[t = tl][r = 16 rt + 4g .. +3]
-    {
-        const int64_t row = brow0 + static_cast<int64_t>(tb * TB + tl) * bstride;
-#pragma unroll
-        for (int rt = 0; rt < R / 16; ++rt) io<IO>::st4(dC, row + rt * 16 + 4 * g, acc[rt]);
-    }
     // g1[t] = sum_r C[t, r] d_C[t, r]: the BLUE term plus ORANGE's target side, since
     // sum_s d_diff[t, s] = sum_s d_CB[t, s] (C_t . B_s) = C_t . (sum_s d_CB[t, s] B_s)
+    // (s = t held out, above)
     float gsum = 0.0f;
 #pragma unroll
     for (int rt = 0; rt < R / 16; ++rt)
@@ -196,6 +195,17 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target(
         for (int v = 0; v < 4; ++v) gsum += creg[rt][v] * acc[rt][v];
     gsum = sum_over_g(gsum);
     if (g == 0) g1[c.c_bhn * L + tb * TB + tl] = gsum;
+    // the diagonal element: d_C[t] += d_CB[t, t] B_t (B of this block is still in LDS); store
+    // d_C[t = tl][r = 16 rt + 4g .. +3]
+    const float dgd = ddg[c.c_bhn * L + tb * TB + tl];
+    {
+        const int64_t row = brow0 + static_cast<int64_t>(tb * TB + tl) * bstride;
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt) {
+            acc[rt] += dgd * *reinterpret_cast<const v4f*>(sBS + tl * RS + rt * 16 + 4 * g);
+            io<IO>::st4(dC, row + rt * 16 + 4 * g, acc[rt]);
+        }
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) dA += __shfl_xor(dA, off);
     __syncthreads();
@@ -212,7 +222,8 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     const float* __restrict__ Dv, const double* __restrict__ cdt, const float* __restrict__ dS,
     typename IO::T* __restrict__ dx, typename IO::T* __restrict__ dB, float* __restrict__ d_dt,
     float* __restrict__ g2, float* __restrict__ d_delta, double* __restrict__ dA_S,
-    double* __restrict__ dD_part, float* __restrict__ dcbt, int N, int H, int L, int64_t CH) {
+    double* __restrict__ dD_part, float* __restrict__ dcbt, float* __restrict__ ddg, int N, int H,
+    int L, int64_t CH) {
     constexpr int RS = R + 4, PS = P + 4;
     constexpr int ROWS = P > TB ? P : TB;
     __shared__ float sCT[ROWS * RS];  // d_intra [P, R], then C of the target block
@@ -301,6 +312,10 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     }
 
     float ddt_or = 0.0f, dsrc = 0.0f;
+    // d_CB[s, s] of this lane's source row, on the lane of the diagonal tile that holds it:
+    // the one whose element v = i - 4 g lies in 0..3
+    float dgk = 0.0f;
+    const int dvl = i - 4 * g;
     double dA = 0.0;  // this lane's part of the chunk's d_A (the pair terms and K3; file header)
     const int64_t tiles0 = c.ch * pair_tiles_of(L);  // this chunk-head's first pair tile
     // One (16-row target tile j of block tb, 16-row source tile) pair: the source tile's
@@ -330,6 +345,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
             tiles0 + pair_index(4 * tb + j, 4 * sb + __builtin_amdgcn_readfirstlane(srow >> 4));
         float* const tdst = dcbt + tile_at * 256;
         float wv[4], dcb[4];
+        const bool dtile = tb == sb && 16 * j == (srow & ~15);  // the diagonal pair tile
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const bool keep = (tb > sb) || (16 * j + 4 * g + v >= srow);
@@ -341,9 +357,13 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
             dcb[v] = dw[v] * dtr * dec;
             ddt += dw[v] * cbd;
             const float dd = dcb[v] * cb[v];  // d_diff[t, s]
-            dsr += dd;
+            // the diagonal pair t = s: left out of g2 (the target side leaves it out of g1),
+            // its d_CB handed over in ddg, not in the tile
+            const bool diag = dtile && dvl == v;
+            dsr += diag ? 0.0f : dd;
             dA += static_cast<double>(dd) * gap;
-            tdst[(4 * g + v) * 16 + i] = dcb[v];
+            tdst[(4 * g + v) * 16 + i] = diag ? 0.0f : dcb[v];
+            dgk = diag ? dcb[v] : dgk;
         }
         if constexpr (sizeof(typename IO::T) == 2) {
             // bf16 io: dy and C are exact bf16, W and d_CB fp32 tiles split once into
@@ -506,8 +526,10 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     dbb = sum_over_g(dbb);
     ddt_or = sum_over_g(ddt_or);
     dsrc = sum_over_g(dsrc);
+    dgk = sum_over_g(dgk);  // one lane of the four holds it, the others 0
     if (g == 0) {
         const int64_t o = c.c_bhn * L + spos;
+        ddg[o] = dgk;
         const float dl = dbb * dts * dec_end;
         d_dt[o] = ddt_or + dbb * dec_end;
         g2[o] = -dsrc;
@@ -540,8 +562,8 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
 template <class IO>
 static hipError_t target_io(const Shape& s, const void* dy, const void* Bm, const void* Cm,
                             const float* A, const double* cdt, const float* S, const float* dS,
-                            const float* dcbt, void* dC, float* g1, float* d_end, double* dA_T,
-                            hipStream_t st) {
+                            const float* dcbt, const float* ddg, void* dC, float* g1,
+                            float* d_end, double* dA_T, hipStream_t st) {
     using T = typename IO::T;
     const int64_t CH = static_cast<int64_t>(s.B) * s.N * s.H;
     if (CH == 0) return hipSuccess;
@@ -550,7 +572,7 @@ static hipError_t target_io(const Shape& s, const void* dy, const void* Bm, cons
     if (s.P == PP && s.R == RR) {                                                                \
         hipLaunchKernelGGL((k_bwd_target<IO, PP, RR>), grid, dim3(NT), 0, st,                   \
                            static_cast<const T*>(dy), static_cast<const T*>(Bm),                 \
-                           static_cast<const T*>(Cm), A, cdt, S, dS, dcbt,                       \
+                           static_cast<const T*>(Cm), A, cdt, S, dS, dcbt, ddg,                  \
                            static_cast<T*>(dC), g1, d_end, dA_T, s.N, s.H, s.L, CH);             \
         return hipGetLastError();                                                                \
     }
@@ -561,10 +583,10 @@ static hipError_t target_io(const Shape& s, const void* dy, const void* Bm, cons
 
 hipError_t launch_bwd_target(const Shape& s, const void* dy, const void* Bm, const void* Cm,
                              const float* A, const double* cdt, const float* S, const float* dS,
-                             const float* dcbt, void* dC, float* g1, float* d_end, double* dA_T,
-                             hipStream_t st) {
-    return s.io == 1 ? target_io<BF16>(s, dy, Bm, Cm, A, cdt, S, dS, dcbt, dC, g1, d_end, dA_T, st)
-                     : target_io<F32>(s, dy, Bm, Cm, A, cdt, S, dS, dcbt, dC, g1, d_end, dA_T, st);
+                             const float* dcbt, const float* ddg, void* dC, float* g1,
+                             float* d_end, double* dA_T, hipStream_t st) {
+    return s.io == 1 ? target_io<BF16>(s, dy, Bm, Cm, A, cdt, S, dS, dcbt, ddg, dC, g1, d_end, dA_T, st)
+                     : target_io<F32>(s, dy, Bm, Cm, A, cdt, S, dS, dcbt, ddg, dC, g1, d_end, dA_T, st);
 }
 
 template <class IO>
@@ -572,7 +594,7 @@ static hipError_t source_io(const Shape& s, const void* dy, const void* x, const
                             const void* Bm, const void* Cm, const float* A, const float* D,
                             const double* cdt, const float* dS, void* dx, void* dB, float* d_dt,
                             float* g2, float* d_delta, double* dA_S, double* dD_part,
-                            float* dcbt, hipStream_t st) {
+                            float* dcbt, float* ddg, hipStream_t st) {
     using T = typename IO::T;
     const int64_t CH = static_cast<int64_t>(s.B) * s.N * s.H;
     if (CH == 0) return hipSuccess;
@@ -583,7 +605,7 @@ static hipError_t source_io(const Shape& s, const void* dy, const void* x, const
                            static_cast<const T*>(dy), static_cast<const T*>(x), dt,               \
                            static_cast<const T*>(Bm), static_cast<const T*>(Cm), A, D, cdt, dS,   \
                            static_cast<T*>(dx), static_cast<T*>(dB), d_dt, g2, d_delta, dA_S,     \
-                           dD_part, dcbt, s.N, s.H, s.L, CH);                                     \
+                           dD_part, dcbt, ddg, s.N, s.H, s.L, CH);                                \
         return hipGetLastError();                                                                 \
     }
     SSD_FOR_EACH_PR(X)
@@ -595,11 +617,11 @@ hipError_t launch_bwd_source(const Shape& s, const void* dy, const void* x, cons
                              const void* Bm, const void* Cm, const float* A, const float* D,
                              const double* cdt, const float* dS, void* dx, void* dB, float* d_dt,
                              float* g2, float* d_delta, double* dA_S, double* dD_part,
-                             float* dcbt, hipStream_t st) {
+                             float* dcbt, float* ddg, hipStream_t st) {
     return s.io == 1 ? source_io<BF16>(s, dy, x, dt, Bm, Cm, A, D, cdt, dS, dx, dB, d_dt, g2,
-                                       d_delta, dA_S, dD_part, dcbt, st)
+                                       d_delta, dA_S, dD_part, dcbt, ddg, st)
                      : source_io<F32>(s, dy, x, dt, Bm, Cm, A, D, cdt, dS, dx, dB, d_dt, g2,
-                                      d_delta, dA_S, dD_part, dcbt, st);
+                                      d_delta, dA_S, dD_part, dcbt, ddg, st);
 }
 
 }  // namespace ssd

@@ -465,7 +465,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
     const typename IO::T* __restrict__ dy, const typename IO::T* __restrict__ Bm,
     const typename IO::T* __restrict__ Cm, const float* __restrict__ Av,
     const double* __restrict__ cdt, const float* __restrict__ S, const float* __restrict__ dS,
-    const float* __restrict__ dcbt, const float* __restrict__ g2,
+    const float* __restrict__ dcbt, const float* __restrict__ ddg, const float* __restrict__ g2,
     const float* __restrict__ d_delta, typename IO::T* __restrict__ dC, float* __restrict__ d_dt,
     double* __restrict__ dA_T, int N, int H) {
     constexpr int RS = R + 4, L = KC, NBLK = KC / TB;
@@ -674,7 +674,11 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
         stage_rows<IO, R, KC, 16>(sM, Bm + brow0, bstride);
     }
     __syncthreads();
-    // K2 backward: d_C^T[r, t] += sum_s B[s, r] d_CB[t, s]
+    // K2 backward: d_C^T[r, t] += sum_s B[s, r] d_CB[t, s].  The tiles hold the diagonal
+    // elements d_CB[t, t] as zeros (they come in ddg), so g1 below leaves out the diagonal
+    // pair's d_diff, as g2 does in the source-row kernel: in exact arithmetic the two
+    // cancel, in fp32 each side rounds its own way and d_dt = ... + A d_da would carry |A|
+    // times the difference.  They join d_C after g1 is taken.
     auto pair = [&](int j, v4f dcb, auto qc) __attribute__((always_inline)) {
         constexpr int q = decltype(qc)::value;
         if constexpr (sizeof(typename IO::T) == 2) {
@@ -710,12 +714,29 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_target_w(
     for (int q = 0; q < 2; ++q) {
         // g1[t] = sum_r C[t, r] d_C[t, r]: the BLUE term plus ORANGE's target side, since
         // sum_s d_diff[t, s] = sum_s d_CB[t, s] (C_t . B_s) = C_t . (sum_s d_CB[t, s] B_s)
-        // (the own C rows stay in registers: read again at this point they came from HBM)
+        // (s = t held out, above; the own C rows stay in registers: read again at this
+        // point they came from HBM)
         float gsum = 0.0f;
 #pragma unroll
         for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) gsum += creg[q][rt][v] * acc[q][rt][v];
+        // then the diagonal element joins d_C: d_C[t] += d_CB[t, t] B_t, B_t from LDS (row t
+        // of the chunk's B rows; with fp32 io the d_C staging below overwrites rows 0 .. 63
+        // only, after tile tt[0] (< 4) has read its row, so tile tt[1]'s row is intact)
+        const float dg = ddg[c.c_bhn * L + tl[q]];
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt) {
+            if constexpr (sizeof(typename IO::T) != 4) {
+                v4f bt;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    bt[v] = bf16_to_f32(sBq[((tl[q] >> 2) * RB + 16 * rt + 4 * g + v) * 4 + (tl[q] & 3)]);
+                acc[q][rt] += dg * bt;
+            } else {
+                acc[q][rt] += dg * *reinterpret_cast<const v4f*>(sM + tl[q] * RS + rt * 16 + 4 * g);
+            }
+        }
         if constexpr (sizeof(typename IO::T) != 4) {
             const int64_t row = brow0 + static_cast<int64_t>(tl[q]) * bstride;
 #pragma unroll
@@ -830,7 +851,7 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
     const float* __restrict__ Dv, const double* __restrict__ cdt, const float* __restrict__ dS,
     BF16::T* __restrict__ dx, BF16::T* __restrict__ dB, float* __restrict__ d_dt,
     float* __restrict__ g2, float* __restrict__ d_delta, double* __restrict__ dA_S,
-    double* __restrict__ dD_part, float* __restrict__ dcbt, int N, int H) {
+    double* __restrict__ dD_part, float* __restrict__ dcbt, float* __restrict__ ddg, int N, int H) {
     using IO = BF16;
     using LY = SrcWLds<P, R>;
     constexpr int RB = LY::RB, PB = LY::PB, IRS = R + 8, L = KC, NBLK = KC / TB;
@@ -1018,6 +1039,7 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
     __syncthreads();
 
     double dA = 0.0;  // this lane's part of the chunk's d_A (the pair terms and K3)
+    float dgk = 0.0f;  // d_CB[s, s] of this lane's source row, on the lane whose tile holds it
     // One (target tile j, source tile s) pair, j >= s: the source tile's packed operands
     // xr / br, cumsum csr and dt dtr of this lane's source row 16 s + i, its accumulators.
     // The pair's d_CB tile goes to the target-row kernel.
@@ -1050,9 +1072,13 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
             dcb[v] = dw[v] * dtr * dec;
             ddt += dw[v] * cbd;
             const float dd = dcb[v] * cb[v];  // d_diff[t, s]
-            dsr += dd;
+            // the diagonal pair t = s: left out of g2 (the target side leaves it out of g1),
+            // its d_CB handed over in ddg, not in the tile
+            const bool diag = 16 * j + 4 * g + v == 16 * s + i;
+            dsr += diag ? 0.0f : dd;
             dA += static_cast<double>(dd) * gap;
-            tdst[(4 * g + v) * 16 + i] = dcb[v];
+            tdst[(4 * g + v) * 16 + i] = diag ? 0.0f : dcb[v];
+            dgk = diag ? dcb[v] : dgk;
         }
         // W and d_CB split once into three exact bf16 parts; dy and C exact
         const S4x3 ws = split4(v4f{wv[0], wv[1], wv[2], wv[3]});
@@ -1081,11 +1107,13 @@ __global__ __launch_bounds__(NTS, 1) void k_bwd_source_w(
         const float db = sum_over_g(dbb);
         const float dto = sum_over_g(ddt_or);
         const float dsc = sum_over_g(dsrc);
+        const float dgs = sum_over_g(dgk);  // one lane of the four holds it, the others 0
         if (g == 0) {
             const int64_t o = c.c_bhn * L + spos;
             const float dl = db * dts * dec_end;
             d_dt[o] = dto + db * dec_end;
             g2[o] = -dsc;
+            ddg[o] = dgs;
             d_delta[o] = dl;
             dA += static_cast<double>(dl) * (end - cs);
         }
@@ -1221,7 +1249,7 @@ hipError_t launch_k5_scan_wide(const Shape& s, const void* x, const float* dt, c
 template <class IO>
 static hipError_t target_wide_io(const Shape& s, const void* dy, const void* Bm, const void* Cm,
                                  const float* A, const double* cdt, const float* S, const float* dS,
-                                 const float* dcbt, const float* g2,
+                                 const float* dcbt, const float* ddg, const float* g2,
                                  const float* d_delta, void* dC, float* d_dt, double* dA_T,
                                  hipStream_t st) {
     using T = typename IO::T;
@@ -1233,7 +1261,7 @@ static hipError_t target_wide_io(const Shape& s, const void* dy, const void* Bm,
             hipLaunchKernelGGL((k_bwd_target_w<IO, PP, RR>), dim3(static_cast<unsigned>(CH)),      \
                                dim3(NT), 0, st, static_cast<const T*>(dy),                         \
                                static_cast<const T*>(Bm), static_cast<const T*>(Cm), A, cdt, S,    \
-                               dS, dcbt, g2, d_delta, static_cast<T*>(dC), d_dt, dA_T, s.N,        \
+                               dS, dcbt, ddg, g2, d_delta, static_cast<T*>(dC), d_dt, dA_T, s.N,   \
                                s.H);                                                               \
             return hipGetLastError();                                                              \
         }                                                                                          \
@@ -1246,13 +1274,13 @@ static hipError_t target_wide_io(const Shape& s, const void* dy, const void* Bm,
 
 hipError_t launch_bwd_target_wide(const Shape& s, const void* dy, const void* Bm, const void* Cm,
                                   const float* A, const double* cdt, const float* S,
-                                  const float* dS, const float* dcbt, const float* g2,
-                                  const float* d_delta, void* dC, float* d_dt, double* dA_T,
-                                  hipStream_t st) {
-    return s.io == 1 ? target_wide_io<BF16>(s, dy, Bm, Cm, A, cdt, S, dS, dcbt, g2, d_delta, dC,
-                                            d_dt, dA_T, st)
-                     : target_wide_io<F32>(s, dy, Bm, Cm, A, cdt, S, dS, dcbt, g2, d_delta, dC,
-                                           d_dt, dA_T, st);
+                                  const float* dS, const float* dcbt, const float* ddg,
+                                  const float* g2, const float* d_delta, void* dC, float* d_dt,
+                                  double* dA_T, hipStream_t st) {
+    return s.io == 1 ? target_wide_io<BF16>(s, dy, Bm, Cm, A, cdt, S, dS, dcbt, ddg, g2, d_delta,
+                                            dC, d_dt, dA_T, st)
+                     : target_wide_io<F32>(s, dy, Bm, Cm, A, cdt, S, dS, dcbt, ddg, g2, d_delta,
+                                           dC, d_dt, dA_T, st);
 }
 
 
@@ -1260,7 +1288,7 @@ static hipError_t source_wide_bf16(const Shape& s, const void* dy, const void* x
                                  const void* Bm, const void* Cm, const float* A, const float* D,
                                  const double* cdt, const float* dS, void* dx, void* dB,
                                  float* d_dt, float* g2, float* d_delta, double* dA_S,
-                                 double* dD_part, float* dcbt, hipStream_t st) {
+                                 double* dD_part, float* dcbt, float* ddg, hipStream_t st) {
     using T = BF16::T;
     const int64_t CH = static_cast<int64_t>(s.B) * s.N * s.H;
     if (CH == 0) return hipSuccess;
@@ -1271,8 +1299,8 @@ static hipError_t source_wide_bf16(const Shape& s, const void* dy, const void* x
                                dim3(NTS), 0, st, static_cast<const T*>(dy),                       \
                                static_cast<const T*>(x), dt, static_cast<const T*>(Bm),           \
                                static_cast<const T*>(Cm), A, D, cdt, dS, static_cast<T*>(dx),     \
-                               static_cast<T*>(dB), d_dt, g2, d_delta, dA_S, dD_part, dcbt, s.N,  \
-                               s.H);                                                              \
+                               static_cast<T*>(dB), d_dt, g2, d_delta, dA_S, dD_part, dcbt, ddg,  \
+                               s.N, s.H);                                                         \
             return hipGetLastError();                                                             \
         }                                                                                         \
         return hipErrorInvalidValue;                                                              \
@@ -1286,10 +1314,10 @@ hipError_t launch_bwd_source_wide(const Shape& s, const void* dy, const void* x,
                                   const void* Bm, const void* Cm, const float* A, const float* D,
                                   const double* cdt, const float* dS, void* dx, void* dB,
                                   float* d_dt, float* g2, float* d_delta, double* dA_S,
-                                  double* dD_part, float* dcbt, hipStream_t st) {
+                                  double* dD_part, float* dcbt, float* ddg, hipStream_t st) {
     if (s.io != 1) return hipErrorInvalidValue;  // bf16 io only (see the kernel)
     return source_wide_bf16(s, dy, x, dt, Bm, Cm, A, D, cdt, dS, dx, dB, d_dt, g2, d_delta, dA_S,
-                            dD_part, dcbt, st);
+                            dD_part, dcbt, ddg, st);
 }
 
 }  // namespace ssd

@@ -104,7 +104,8 @@ size_t round_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 //          g1, g2, dlt fp32 [b,h,n,l], dend fp32 [b,h,n],
 //          dAT, dAS, dD fp64 [b,n,h,l/64] (per-block d_A / d_D partials),
 //          dcbt fp32 [b,n,h,pairs,256]: the d_CB tiles of the causal 16 x 16 pair tiles
-//          (pairs = pair_tiles_of(l))
+//          (pairs = pair_tiles_of(l); the diagonal elements t = s held out as zeros),
+//          ddg fp32 [b,h,n,l]: those diagonal elements d_CB[t, t]
 //   moments: valid int64 [b]; phi, psi, phit, psit fp64 [b,h,n,l]; T fp32 [b,n,h,p,r];
 //          fwd: U [b,n,h,l/64,r,r], W [b,n,h,r,r], m1b [b,n,h,l/64,r], m1c [b,n,h,r] fp32
 //          bwd: HS, dS fp32 [b,n,h,p,r]; BS fp32 [b,n,h,l,r]; fin fp32 [b,h,p,r];
@@ -112,7 +113,7 @@ size_t round_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 //               [b,h,n,l]; dA fp64 [b,n,h,l/64]
 struct Ws {
     size_t cdt = 0, S = 0, dS = 0, g1 = 0, g2 = 0, dlt = 0, dend = 0, dAT = 0, dAS = 0, dD = 0,
-           dcbt = 0;
+           dcbt = 0, ddg = 0;
     size_t valid = 0, phi = 0, psi = 0, phit = 0, psit = 0, T = 0, U = 0, W = 0, m1b = 0, m1c = 0, HS = 0, BS = 0,
            fin = 0, hsh = 0, hdm = 0, dend2 = 0, ddtW = 0, rho = 0, eta = 0, zeta = 0, dA = 0;
     size_t total = 0;
@@ -143,6 +144,7 @@ Ws plan(const ssd::Shape& s, int op) {
         w.dD = take(8 * chunks * nb);
         const size_t tiles = chunks * static_cast<size_t>(ssd::pair_tiles_of(s.L));
         w.dcbt = take(4 * 256 * tiles);
+        w.ddg = take(4 * tok);
     }
     if (op == SSD_OP_MOMENTS || op == SSD_OP_MOMENTS_BWD) {
         w.valid = take(8 * static_cast<size_t>(s.B));
@@ -567,6 +569,7 @@ int ssd_bwd(const ssd_dims* dims, const void* dy, const float* d_final, const vo
     SSD_HIP(ssd::launch_chunk_states(s, true, true, x, B, dy, C, dt, A, cdt, S, dS, st), "k_chunk_states");
     SSD_HIP(ssd::launch_k4_pass_bwd(s, S, dS, cdt, A, init, d_final, d_init, st), "k4_state_pass_bwd");
     float* dcbt = at<float>(ws, w.dcbt);
+    float* ddg = at<float>(ws, w.ddg);
     // rows s first: they hand every causal pair tile's d_CB to rows t.  The whole-chunk
     // source kernel (one workgroup per CU) pays off where the kernel is bound by its vector
     // work (bf16 io); with fp32 io the two 64-row block workgroups per CU overlap one
@@ -574,20 +577,20 @@ int ssd_bwd(const ssd_dims* dims, const void* dy, const float* d_final, const vo
     const bool wide = ssd::wide_supported(s);
     if (wide && s.io == SSD_BF16)
         SSD_HIP(ssd::launch_bwd_source_wide(s, dy, x, dt, B, C, A, D, cdt, dS, d_x, d_B, d_dt, g2,
-                                            dlt, dAS, dDp, dcbt, st),
+                                            dlt, dAS, dDp, dcbt, ddg, st),
                 "k_bwd_source");
     else
         SSD_HIP(ssd::launch_bwd_source(s, dy, x, dt, B, C, A, D, cdt, dS, d_x, d_B, d_dt, g2, dlt,
-                                       dAS, dDp, dcbt, st),
+                                       dAS, dDp, dcbt, ddg, st),
                 "k_bwd_source");
     if (wide) {
         // whole chunks: K1's backward runs inside the target-row kernel
-        SSD_HIP(ssd::launch_bwd_target_wide(s, dy, B, C, A, cdt, S, dS, dcbt, g2, dlt, d_C, d_dt,
-                                            dAT, st),
+        SSD_HIP(ssd::launch_bwd_target_wide(s, dy, B, C, A, cdt, S, dS, dcbt, ddg, g2, dlt, d_C,
+                                            d_dt, dAT, st),
                 "k_bwd_target");
         SSD_HIP(ssd::launch_reduce_heads(s, dAT, dAS, dDp, s.nblk(), d_A, d_D, st), "reduce_heads");
     } else {
-        SSD_HIP(ssd::launch_bwd_target(s, dy, B, C, A, cdt, S, dS, dcbt, d_C, g1, dend, dAT, st),
+        SSD_HIP(ssd::launch_bwd_target(s, dy, B, C, A, cdt, S, dS, dcbt, ddg, d_C, g1, dend, dAT, st),
                 "k_bwd_target");
         SSD_HIP(ssd::launch_k1t_heads(s, g1, g2, dlt, dend, A, d_dt, dAT, dAS, dDp, s.nblk(), d_A,
                                       d_D, st),

@@ -108,12 +108,14 @@ hipError_t launch_k5_scan_wide(const Shape& s, const void* x, const float* dt, c
 // the ORANGE + K3 part of d_dt, g2 (-ORANGE d_da, source side), d_delta (K3) and the
 // d_A / d_D partials dA_S, dD_part [b,n,h,block] (with every pair's d_diff (cdt_t - cdt_s));
 // every causal pair tile of 16 x 16 (t, s) hands its d_CB tile to
-// dcbt [chunk-heads, pair_tiles_of(l), 256] (t-major).
+// dcbt [chunk-heads, pair_tiles_of(l), 256] (t-major), the diagonal elements t = s as zeros:
+// those go to ddg [b,h,n,l] (d_CB[t, t]), so that the target side can take g1 without
+// them (g2 leaves them out too) and add them to d_C afterwards.
 hipError_t launch_bwd_source(const Shape& s, const void* dy, const void* x, const float* dt,
                              const void* Bm, const void* Cm, const float* A, const float* D,
                              const double* cdt, const float* dS, void* dx, void* dB, float* d_dt,
                              float* g2, float* d_delta, double* dA_S, double* dD_part,
-                             float* dcbt, hipStream_t st);
+                             float* dcbt, float* ddg, hipStream_t st);
 
 // The same per whole 128-token chunk (wide_supported shapes, bf16 io only): one 8-wave
 // workgroup per chunk-head; the d_A / d_D partials go to the chunk-head's first block
@@ -122,22 +124,22 @@ hipError_t launch_bwd_source_wide(const Shape& s, const void* dy, const void* x,
                                   const void* Bm, const void* Cm, const float* A, const float* D,
                                   const double* cdt, const float* dS, void* dx, void* dB,
                                   float* d_dt, float* g2, float* d_delta, double* dA_S,
-                                  double* dD_part, float* dcbt, hipStream_t st);
+                                  double* dD_part, float* dcbt, float* ddg, hipStream_t st);
 
 // Target side (rows t) from those tiles, per (chunk-head, 64-row block): d_C, g1 (BLUE +
 // ORANGE-target gradient w.r.t. the cumsum), d_end, and the d_A partials dA_T.
 hipError_t launch_bwd_target(const Shape& s, const void* dy, const void* Bm, const void* Cm,
                              const float* A, const double* cdt, const float* S, const float* dS,
-                             const float* dcbt, void* dC, float* g1, float* d_end, double* dA_T,
-                             hipStream_t st);
+                             const float* dcbt, const float* ddg, void* dC, float* g1,
+                             float* d_end, double* dA_T, hipStream_t st);
 
 // The same per whole 128-token chunk (wide_supported shapes), with K1's backward folded
 // in: d_C, d_dt (the source kernel's part plus A d_da, in place) and dA_T.
 hipError_t launch_bwd_target_wide(const Shape& s, const void* dy, const void* Bm, const void* Cm,
                                   const float* A, const double* cdt, const float* S,
-                                  const float* dS, const float* dcbt, const float* g2,
-                                  const float* d_delta, void* dC, float* d_dt, double* dA_T,
-                                  hipStream_t st);
+                                  const float* dS, const float* dcbt, const float* ddg,
+                                  const float* g2, const float* d_delta, void* dC, float* d_dt,
+                                  double* dA_T, hipStream_t st);
 
 // K1 backward (suffix sums inside each chunk, d_dt += A d_da) and, in the same launch,
 // the per-head sums of launch_reduce_heads below.

@@ -61,7 +61,8 @@ def test_workspace_plan(lib, kcl, k):
     assert ssd.ssd_workspace_size(d, ssd.SSD_OP_FWD) == up(8 * tok) + up(4 * states)
     pair_tiles = (k // 16) * (k // 16 + 1) // 2  # causal 16 x 16 tiles per chunk (d_CB hand-off)
     bwd = up(8 * tok) + 2 * up(4 * states) + 3 * up(4 * tok) + up(4 * chunks) \
-        + 3 * up(8 * chunks * (k // 64)) + up(4 * 256 * chunks * pair_tiles)
+        + 3 * up(8 * chunks * (k // 64)) + up(4 * 256 * chunks * pair_tiles) \
+        + up(4 * tok)  # the diagonal d_CB[t, t], handed over beside the pair tiles
     assert ssd.ssd_workspace_size(d, ssd.SSD_OP_BWD) == bwd
 
 

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 from gpu_common import (GRADS, TOL, check_identities_all_heads, compare, gpu_fwd_bwd,
-                        oracle_fwd_bwd, say, select_heads)
+                        oracle_fwd_bwd, rel_l2, say, select_heads)
 from mamba_ssd_chunked_amd import inputs, ssd
 
 pytestmark = pytest.mark.gpu
@@ -106,6 +106,42 @@ def test_kernel_chunk_len_matches_oracle(l, kcl, io):
     gpu = gpu_fwd_bwd(inp, kernel_chunk_len=kcl)
     ref = oracle_fwd_bwd(inp)
     compare(gpu, ref, TOL[io], KEYS, f"l={l} k={kcl} {io}")
+
+
+# The limits of the decay, head by head: memoryless (A dt about -5e3: every decay between
+# distinct tokens underflows to exactly 0 in fp32 and fp64 alike), no step (dt = 0: a = 1
+# and nothing enters the state, d_A = 0), tiny steps, and an ordinary head; at the
+# whole-chunk (128) and block (64) kernel chunk lengths, fp32 and bf16 inputs.  d_dt gets
+# A d_da, and d_da's pair terms are a difference of the target- and source-side sums of
+# d_diff; the diagonal pair t = s, whose terms cancel exactly and dominate a memoryless
+# head, is held out of both sums, so A d_da carries no |A|-scaled rounding and every head,
+# A = -1e4 included, is held to the plain tolerance.
+EXTREME = [("f32", 128), ("f32", 64), ("bf16", 128), ("bf16", 64)]
+
+
+@pytest.mark.parametrize("io,kcl", EXTREME, ids=[f"{e[0]}_k{e[1]}" for e in EXTREME])
+def test_extreme_decay_regimes(io, kcl):
+    w = inputs.custom(batch=2, seq=256, nheads=4, headdim=32, dstate=32, chunk_len=128, io=io,
+                      init_std=0.3, seed=901)
+    inp = inputs.make_inputs(w)
+    A, dt = inp["A"].clone(), inp["dt"].clone()
+    A[0] = -1.0e4
+    dt[:, 0] = 0.5 + 0.5 * dt[:, 0].abs()
+    dt[:, 1] = 0.0
+    dt[:, 2] = dt[:, 2] * 1e-6
+    inp["A"], inp["dt"] = A, dt
+    say(f"case extreme decay {io} kernel_chunk_len {kcl}")
+    gpu = gpu_fwd_bwd(inp, kernel_chunk_len=kcl)
+    ref = oracle_fwd_bwd(inp)
+    for k in KEYS:
+        assert np.all(np.isfinite(gpu[k])), k
+    # the memoryless and no-step heads have no gradient w.r.t. A at all
+    assert np.all(gpu["d_A"][:2] == 0.0) and np.all(ref["d_A"][:2] == 0.0)
+    compare(gpu, ref, TOL[io], [k for k in KEYS if k != "d_dt"], f"extreme decay {io} k={kcl}")
+    for h in range(w.nheads):
+        e = rel_l2(gpu["d_dt"][:, h], ref["d_dt"][:, h])
+        say(f"  head {h} (A = {float(A[h]):.3g}) d_dt rel-L2 {e:.2e} (bound {TOL[io]:.1e})")
+        assert e <= TOL[io], (h, e)
 
 
 # Many short slices: 8192 and 16384 chunks (batch x heads x chunks) at each kernel
