@@ -43,9 +43,9 @@ HEADLINE = "long_context_64k_fp32"
 # (kernel, workload, kernel chunk length), valid only while the hash of the kernel's sources is
 # the one they were taken on (profiles/ssd_kernels_*.md have the runs).
 TRAFFIC = {
-    ("k_bwd_source", "long_context_64k_fp32", 128): (5_406_314_496, 2_241_860_608, "250f358f042c8ca1"),
-    ("k_bwd_source", "mamba2_130m_fp32", 128): (503_373_824, 210_184_192, "250f358f042c8ca1"),
-    ("k_bwd_source", "mamba2_2p7b_bf16", 128): (743_546_880, 448_644_096, "d0fd949bba144132"),
+    ("k_bwd_source", "long_context_64k_fp32", 128): (5_387_913_216, 2_250_261_504, "b101e8033bf86f7a"),
+    ("k_bwd_source", "mamba2_130m_fp32", 128): (501_182_464, 210_980_864, "b101e8033bf86f7a"),
+    ("k_bwd_source", "mamba2_2p7b_bf16", 128): (743_428_096, 451_325_952, "de9b5242e4bedd81"),
 }
 # the files a kernel's code comes from, by io type: with bf16 io the source-row kernel at
 # 128-token chunks is the whole-chunk one
@@ -163,10 +163,10 @@ def chunk_kernel_bytes(w, kernel: str, k: int):
     if kernel == "k5_chunk_scan":       # x, B, C, dt, cdt, S_in -> y
         return tok * (io * (2 * p + 2 * r) + 12) + st
     tiles = 1024 * (l // 16) * (l // 16 + 1) // 2 * ch   # the causal d_CB pair tiles (fp32)
-    if kernel == "k_bwd_target":        # dy, C, B, cdt, S_in, d_intra, d_CB tiles, g2, d_delta,
-        return tok * (io * (p + 3 * r) + 24) + 2 * st + tiles   # d_dt -> d_C, d_dt
+    if kernel == "k_bwd_target":        # dy, C, B, cdt, S_in, d_intra, d_CB tiles and diagonal,
+        return tok * (io * (p + 3 * r) + 28) + 2 * st + tiles   # g2, d_delta, d_dt -> d_C, d_dt
     if kernel == "k_bwd_source":        # dy, x, B, C, dt, cdt, d_intra -> d_x, d_B, d_dt, g2,
-        return tok * (io * (3 * p + 3 * r) + 24) + st + tiles   # d_delta, d_CB tiles
+        return tok * (io * (3 * p + 3 * r) + 28) + st + tiles   # d_delta, d_CB tiles and diagonal
     return None
 
 

@@ -86,8 +86,10 @@ def test_chunk_kernel_bytes_count_every_tensor_once():
     tok, st = 196608, 4 * 64 * 128 * 1536
     assert bench.chunk_kernel_bytes(w, "k5_chunk_scan", 128) == tok * (4 * (64 + 2 * 128) + 4 * 64 + 12) + st
     tiles = 1024 * 36 * 1536  # 36 causal 16 x 16 d_CB tiles per 128-token chunk-head
-    assert bench.chunk_kernel_bytes(w, "k_bwd_source", 128) == tok * (4 * (2 * 64 + 2 * 128) + 4 * (64 + 128) + 24) + st + tiles
-    assert bench.chunk_kernel_bytes(w, "k_bwd_target", 128) == tok * (4 * (64 + 3 * 128) + 24) + 2 * st + tiles
+    # per token-head besides the rows: source dt, cdt (fp64) in; d_dt, g2, d_delta, diagonal
+    # d_CB out; target cdt, g2, d_delta, diagonal d_CB in, d_dt in and out
+    assert bench.chunk_kernel_bytes(w, "k_bwd_source", 128) == tok * (4 * (2 * 64 + 2 * 128) + 4 * (64 + 128) + 12 + 16) + st + tiles
+    assert bench.chunk_kernel_bytes(w, "k_bwd_target", 128) == tok * (4 * (64 + 3 * 128) + 8 + 12 + 8) + 2 * st + tiles
     job0 = tok * (4 * 192 + 12) + st
     job1 = tok * (4 * 192 + 8) + st
     assert bench.chunk_kernel_bytes(w, "k_chunk_states", 128) == (2 * job0 + job1) / 2
