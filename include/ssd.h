@@ -350,6 +350,29 @@ int ssd_timing_enable(int on);
 int ssd_timing_collect(int max_kernels, char* names, size_t name_stride, double* total_ms,
                        int64_t* launches, int* n_kernels);
 
+/*
+ * Debug aid (not part of the computation): where ssd_bwd leaves its per-token
+ * partials of the gradient w.r.t. the within-chunk cumsum of dt*A in the
+ * workspace, so that a test can read them after the call.  They are the
+ * pieces the combined_backward.rs page's CombinedGrads exposes for its test
+ * of the local d_da: the BLUE + ORANGE gradient w.r.t. the cumsum through the
+ * chunk's own terms (entry-state read-out and causal kernel, the entry states
+ * held fixed), at the kernel chunk length, equals g1[t] + g2[t] with
+ *   "g1"       fp32 [b, h, n*l]: the target-row side, C_t . d_C[t] (BLUE plus
+ *              the ORANGE pairs (t, s < t));
+ *   "g2"       fp32 [b, h, n*l]: the source-row side, minus the ORANGE pairs
+ *              (t > s, s); the diagonal pair, which cancels, is in neither;
+ *   "d_delta"  fp32 [b, h, n*l]: the chunk-end state term of the same
+ *              gradient (not part of the local d_da).
+ * Writes the region's byte offset into a workspace of ssd_workspace_size(dims,
+ * SSD_OP_BWD) bytes and its size.  *bytes is 0 where ssd_bwd does not write the
+ * region for these dims: g1 when the whole-chunk kernels run (kernel chunk
+ * length 128 with headdim * dstate <= 8192), whose target-row kernel suffix-sums
+ * g1 in registers, and every region of an empty problem.  Returns
+ * SSD_ERR_SHAPE for an unknown name, SSD_ERR_NULL for a NULL argument.
+ */
+int ssd_bwd_partial_region(const ssd_dims* dims, const char* name, size_t* offset, size_t* bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -517,6 +517,29 @@ int ssd_workspace_size(const ssd_dims* dims, int op, size_t* bytes) {
     return ok();
 }
 
+int ssd_bwd_partial_region(const ssd_dims* dims, const char* name, size_t* offset, size_t* bytes) {
+    ssd::Shape s;
+    if (int rc = validate_dims(dims, &s)) return rc;
+    if (!name || !offset || !bytes)
+        return fail(SSD_ERR_NULL, "ssd_bwd_partial_region: name, offset and bytes are required");
+    const Ws w = plan(s, SSD_OP_BWD);
+    const size_t tok = static_cast<size_t>(s.B) * s.H * s.N * s.L;
+    if (std::strcmp(name, "g1") == 0) {
+        *offset = w.g1;
+        *bytes = ssd::wide_supported(s) ? 0 : 4 * tok;  // the whole-chunk kernel keeps it in registers
+    } else if (std::strcmp(name, "g2") == 0) {
+        *offset = w.g2;
+        *bytes = 4 * tok;
+    } else if (std::strcmp(name, "d_delta") == 0) {
+        *offset = w.dlt;
+        *bytes = 4 * tok;
+    } else {
+        return fail(SSD_ERR_SHAPE, "ssd_bwd_partial_region: unknown region '%s' (g1, g2, d_delta)",
+                    name);
+    }
+    return ok();
+}
+
 int ssd_fwd(const ssd_dims* dims, const void* x, const float* dt, const float* A, const void* B,
             const void* C, const float* D, const float* init, void* y, float* final_state, void* ws,
             size_t ws_bytes, void* stream) {

@@ -32,7 +32,7 @@ EXPORTS = ("ssd_workspace_size", "ssd_fwd", "ssd_fwd_noalloc", "ssd_bwd", "ssd_s
            "ssd_state_moments_bwd", "ssd_moments_pr", "ssd_moments_pr_bwd", "ssd_y_diag",
            "ssd_y_diag_bwd", "ssd_quat_scan", "ssd_quat_scan_bwd", "ssd_quat_workspace_size",
            "ssd_step", "ssd_last_error", "ssd_debug_enable", "ssd_timing_enable",
-           "ssd_timing_collect")
+           "ssd_timing_collect", "ssd_bwd_partial_region")
 
 
 class ssd_dims(ctypes.Structure):
@@ -96,6 +96,9 @@ def load_library(path: str = LIB_PATH):
                                        ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int)]
     lib.ssd_timing_collect.restype = ctypes.c_int
+    lib.ssd_bwd_partial_region.argtypes = [D, ctypes.c_char_p, ctypes.POINTER(ctypes.c_size_t),
+                                           ctypes.POINTER(ctypes.c_size_t)]
+    lib.ssd_bwd_partial_region.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -199,6 +202,17 @@ def ssd_workspace_size(dims: ssd_dims, op: int) -> int:
     if rc:
         raise SsdError(rc, "ssd_workspace_size", ssd_last_error())
     return int(out.value)
+
+
+def ssd_bwd_partial_region(dims: ssd_dims, name: str):
+    """(byte offset, bytes) of one of ssd_bwd's per-token partials ("g1", "g2", "d_delta")
+    in its workspace; bytes 0 where the backward does not write it for these dims."""
+    off, n = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    rc = load_library().ssd_bwd_partial_region(ctypes.byref(dims), name.encode(), ctypes.byref(off),
+                                               ctypes.byref(n))
+    if rc:
+        raise SsdError(rc, "ssd_bwd_partial_region", ssd_last_error())
+    return int(off.value), int(n.value)
 
 
 def ssd_fwd(dims, x, dt, A, B, C, D, init, y, final_state, ws, stream=None) -> int:

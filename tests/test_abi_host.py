@@ -66,6 +66,39 @@ def test_workspace_plan(lib, kcl, k):
     assert ssd.ssd_workspace_size(d, ssd.SSD_OP_BWD) == bwd
 
 
+@pytest.mark.parametrize("kcl,p,r,g1_written", [(64, 64, 128, True), (256, 64, 128, True),
+                                                 (128, 64, 128, False), (128, 128, 128, True)])
+def test_bwd_partial_regions(lib, kcl, p, r, g1_written):
+    """g1, g2, d_delta sit where the backward's plan puts them (after the cumsums and the
+    two state buffers, one fp32 per token-head each); g1 is reported unwritten where the
+    whole-chunk kernels run (kernel chunk 128, p * r <= 8192)."""
+    d = dims(b=2, n=4, l=256, h=3, p=p, r=r)
+    d.kernel_chunk_len = kcl
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    k = kcl
+    tok, chunks = 2 * 3 * 4 * 256, 2 * 3 * 4 * 256 // k
+    states = chunks * p * r
+    base = up(8 * tok) + 2 * up(4 * states)
+    assert ssd.ssd_bwd_partial_region(d, "g1") == (base, 4 * tok if g1_written else 0)
+    assert ssd.ssd_bwd_partial_region(d, "g2") == (base + up(4 * tok), 4 * tok)
+    assert ssd.ssd_bwd_partial_region(d, "d_delta") == (base + 2 * up(4 * tok), 4 * tok)
+    total = ssd.ssd_workspace_size(d, ssd.SSD_OP_BWD)
+    for name in ("g1", "g2", "d_delta"):
+        off, n = ssd.ssd_bwd_partial_region(d, name)
+        assert off + n <= total and off % 256 == 0
+
+
+def test_bwd_partial_region_rejects_bad_arguments(lib):
+    d = dims()
+    with pytest.raises(ssd.SsdError, match="unknown region"):
+        ssd.ssd_bwd_partial_region(d, "g3")
+    off = ctypes.c_size_t(0)
+    assert lib.ssd_bwd_partial_region(ctypes.byref(d), b"g1", ctypes.byref(off), None) == 1
+    assert lib.ssd_bwd_partial_region(ctypes.byref(d), None, ctypes.byref(off), ctypes.byref(off)) == 1
+    for name in ("g1", "g2", "d_delta"):  # an empty sequence writes none of them
+        assert ssd.ssd_bwd_partial_region(dims(n=0), name)[1] == 0
+
+
 @pytest.mark.parametrize("l,kcl", [(256, 96), (256, 512), (128, 256), (64, 128), (256, -64),
                                    (128, 32)])
 def test_bad_kernel_chunk_len_is_rejected(lib, l, kcl):

@@ -144,6 +144,44 @@ def test_extreme_decay_regimes(io, kcl):
         assert e <= TOL[io], (h, e)
 
 
+# The backward's local gradient w.r.t. the within-chunk cumsum before its suffix sums
+# (combined_backward.rs page, CombinedGrads: the local d_da of BLUE and ORANGE): g1 + g2,
+# read from the workspace after ssd_bwd, against autodiff of the chunked evaluation through
+# the chunk's own terms with the entry states held fixed (chunked_scan.local_gradients,
+# which the page's identity d_da_local = dy . out_x - d_dt_orange dt ties to the oracle on
+# the CPU).  At the layout's own chunk length, where the kernels' chunks are the layout's;
+# the block kernels at 64 and 256, and at 128 with p * r above the whole-chunk kernels'.
+LOCAL = [(64, 32, 64, "f32"), (256, 64, 128, "f32"), (128, 128, 128, "f32"), (64, 64, 32, "bf16")]
+
+
+@pytest.mark.parametrize("l,p,r,io", LOCAL, ids=[f"l{c[0]}_p{c[1]}_r{c[2]}_{c[3]}" for c in LOCAL])
+def test_local_dda_before_the_suffix_sums(l, p, r, io):
+    import chunked_scan
+    w = inputs.custom(batch=2, seq=3 * l, nheads=3, headdim=p, dstate=r, chunk_len=l, io=io,
+                      init_std=0.3, seed=1300 + l + p)
+    inp = inputs.make_inputs(w)
+    say(f"case local d_da l={l} p={p} r={r} {io}")
+    d = {k: v.cuda().contiguous() for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    dims = ssd.dims_of(d["x"], d["B"], l)
+    ws = ssd.workspace(dims, ssd.SSD_OP_BWD, d["x"].device)
+    ssd.backward(d["dy"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init"],
+                 d_final=d["d_final"], ws=ws, kernel_chunk_len=l)
+    torch.cuda.synchronize()
+
+    def region(name):
+        off, n = ssd.ssd_bwd_partial_region(dims, name)
+        assert n > 0, name
+        return ws[off:off + n].view(torch.float32).cpu().numpy().astype(np.float64)
+
+    local_dev = region("g1") + region("g2")
+    h = {k: inp[k].double().numpy() for k in ("dy", "x", "dt", "A", "B", "C", "init")}
+    ref, _ = chunked_scan.local_gradients(h["dy"], h["x"], h["dt"], h["A"], h["B"], h["C"],
+                                          h["init"])
+    e = rel_l2(local_dev, ref.reshape(-1))
+    say(f"  local d_da rel-L2 {e:.2e}")
+    assert e <= TOL[io], e
+
+
 # Many short slices: 8192 and 16384 chunks (batch x heads x chunks) at each kernel
 # chunk length (the cumsum's lane widths 1, 2, 4), small headdim and dstate.
 # (batch, seq, nheads, chunk_len, kernel_chunk_len, heads compared or None for all);
