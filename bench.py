@@ -40,12 +40,13 @@ HEADLINE = "long_context_64k_fp32"
 
 # HBM bytes per launch (read, write) of a kernel from two rocprofv3 --pmc runs (FETCH_SIZE,
 # WRITE_SIZE; scaled x2.0 / x1.0 by the same counters on a 256 MiB device copy), keyed by
-# (kernel, workload, kernel chunk length), valid only while the hash of the kernel's sources is
-# the one they were taken on (profiles/ssd_kernels_*.md have the runs).
+# (kernel, workload, kernel chunk length), valid only while the hash of the kernel's code (its
+# source files without comments) is the one they were taken on (profiles/ssd_kernels_*.md
+# have the runs).
 TRAFFIC = {
-    ("k_bwd_source", "long_context_64k_fp32", 128): (5_387_913_216, 2_250_261_504, "b101e8033bf86f7a"),
-    ("k_bwd_source", "mamba2_130m_fp32", 128): (501_182_464, 210_980_864, "b101e8033bf86f7a"),
-    ("k_bwd_source", "mamba2_2p7b_bf16", 128): (743_428_096, 451_325_952, "de9b5242e4bedd81"),
+    ("k_bwd_source", "long_context_64k_fp32", 128): (5_387_913_216, 2_250_261_504, "d812f1d2e08c1f78"),
+    ("k_bwd_source", "mamba2_130m_fp32", 128): (501_182_464, 210_980_864, "d812f1d2e08c1f78"),
+    ("k_bwd_source", "mamba2_2p7b_bf16", 128): (743_428_096, 451_325_952, "c331d4ce5e442097"),
 }
 # the files a kernel's code comes from, by io type: with bf16 io the source-row kernel at
 # 128-token chunks is the whole-chunk one
@@ -55,13 +56,39 @@ TRAFFIC_SOURCES = {("k_bwd_source", "f32"): ("k_chunk_bwd.hip", "ssd_device.hpp"
                    ("k_bwd_target", "bf16"): ("k_chunk_wide.hip", "ssd_device.hpp")}
 
 
+def code_of(src: str) -> str:
+    """C++ source without its comments and with runs of white space made one space: what the
+    compiler sees, so that an edited comment does not count as a changed kernel."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c == '"' or c == "'":  # a string or character literal, escapes included
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def traffic_hash(kernel: str, io: str) -> str:
-    """First 16 hex digits of the sha256 of the kernel's source files (TRAFFIC_SOURCES)."""
+    """First 16 hex digits of the sha256 of the code (comments dropped) of the kernel's source
+    files (TRAFFIC_SOURCES)."""
     import hashlib
     m = hashlib.sha256()
     for f in TRAFFIC_SOURCES[(kernel, io)]:
-        with open(os.path.join(ROOT, "mamba_ssd_chunked_amd", "csrc", f), "rb") as fh:
-            m.update(fh.read())
+        with open(os.path.join(ROOT, "mamba_ssd_chunked_amd", "csrc", f), encoding="utf-8") as fh:
+            m.update(code_of(fh.read()).encode())
     return m.hexdigest()[:16]
 
 

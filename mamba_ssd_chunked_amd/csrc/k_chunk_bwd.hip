@@ -22,17 +22,23 @@
 //                + bbar[s] x[s] d_intra                       (K3, d_b = d_b_scaled bbar)
 //     d_dt[s]    = sum_{t>=s} d_w CB decay                    (ORANGE d_dt)
 //                + d_bbar[s] exp(end - cum[s])                (K3 d_dt), d_bbar = <x[s] d_intra, B[s]>
-//     g2[s]      = -sum_{t>=s} d_diff[t,s]                    (ORANGE d_da, source side)
+//     g2[s]      = -sum_{t>s} d_diff[t,s]                     (ORANGE d_da, source side)
 //     d_delta[s] = d_bbar[s] dt[s] exp(end - cum[s])          (K3: gradient of end - cum[s])
 //     dD_part    = sum dy x                                   (SKIP, d_D)
 //   and it hands d_CB of every causal 16 x 16 pair tile to the target side, so C B^T and
-//   dy x^T are formed once per pair;
+//   dy x^T are formed once per pair: the tiles hold the diagonal elements d_CB[t,t] as 0
+//   and ddg[t] holds them;
 //   target side, rows t (bwd_target, from those tiles):
 //     d_C[t]     = e_t dy[t] S_in              (BLUE backward, d_C_blue)
-//                + sum_{s<=t} d_CB[t,s] B[s]    (K2 backward, d_c = d_cb B)
-//     g1[t]      = sum_r C[t,r] d_C[t,r]        (BLUE d_da + ORANGE d_da, target side:
-//                  sum_{s<=t} d_diff[t,s] = sum_s d_CB[t,s] C_t . B_s = C_t . d_C_orange[t])
+//                + sum_{s<t} d_CB[t,s] B[s]     (K2 backward, d_c = d_cb B)
+//                + ddg[t] B[t]                  (its s = t term, added after g1 is taken)
+//     g1[t]      = sum_r C[t,r] (d_C[t,r] - ddg[t] B[t,r])   (BLUE d_da + ORANGE d_da, target
+//                  side: sum_{s<t} d_diff[t,s] = C_t . sum_{s<t} d_CB[t,s] B_s)
 //     d_end      = exp(end) <d_intra, S_in>      (K4 backward, d_da_chunk_end)
+//   The diagonal pair's d_diff[t,t] is in neither g1 nor g2: in exact arithmetic it
+//   cancels between them, in fp32 each side would round it its own way, and d_dt gets
+//   A (g1 + g2 + ...), which would carry |A| times that difference (a memoryless head,
+//   A dt ~ -1e4, is nothing but diagonal pairs).
 // K1^T then turns g1 + g2, d_delta and d_end into d_cum's suffix sum (for d_dt):
 // k1t_and_heads, or the epilogue of the whole-chunk target kernel (k_chunk_wide.hip).
 //

@@ -143,3 +143,15 @@ def test_headline_is_the_largest_single_gpu_workload():
     big = max(("mamba2_130m_fp32", "mamba2_2p7b_bf16", "long_context_64k_fp32"),
               key=lambda n: bench.method_flops(inputs.WORKLOADS[n], 128))
     assert bench.HEADLINE == big == "long_context_64k_fp32"
+
+
+def test_traffic_hash_ignores_comments_not_code():
+    """The counters stay valid across comment edits and lapse on any change of code."""
+    a = 'int f(int x) { return x + 1; }  // one\n/* two */ const char* s = "// kept";\n'
+    b = '/* other */ int f(int x)\n{ return x + 1; }\nconst char* s = "// kept";  // three\n'
+    assert bench.code_of(a) == bench.code_of(b)
+    assert bench.code_of(a) != bench.code_of(a.replace("x + 1", "x + 2"))
+    assert bench.code_of(a) != bench.code_of(a.replace('"// kept"', '"// gone"'))
+    assert bench.code_of("char c = '\\'';  // q\nint y;") == "char c = '\\''; int y;"
+    for key in bench.TRAFFIC_SOURCES:
+        assert len(bench.traffic_hash(*key)) == 16
