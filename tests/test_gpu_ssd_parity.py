@@ -55,6 +55,7 @@ SHAPES = [
     (1, 384, 3, 32, 16, 128, "bf16"),
     (1, 256, 2, 128, 64, 128, "bf16"),
     (2, 384, 2, 16, 128, 128, "bf16"),
+    (1, 256, 2, 128, 128, 128, "bf16"),  # p * r above the whole-chunk kernels': block kernels
 ]
 
 
