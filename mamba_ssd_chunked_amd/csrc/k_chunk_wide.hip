@@ -13,7 +13,8 @@
 // and wait for each other at every block change; each workgroup also re-stages
 // the partner blocks it shares with the other blocks of its chunk.  Here wave w
 // owns the two row tiles w and 7 - w, which as targets pair with
-// (w + 1) + (8 - w) = 9 partner tiles for every wave.  The partner rows are
+// (w + 1) + (8 - w) = 9 partner tiles for every wave (the fp32 K5 gives the two tiles
+// to the two waves of one SIMD instead, below).  The partner rows are
 // staged in two halves of 64 rows: the even 16-row tiles, then the odd ones.
 // With that split every wave has 5 pair tiles in the even half and 4 in the
 // odd one, so the barrier between the halves costs no waiting, and the LDS of
@@ -68,17 +69,23 @@ __device__ __forceinline__ uint2 group4(const uint2 (&r)[4], int f) {
 }  // namespace
 
 // ------------------------------------------------------------------------- K5
-// Wave w owns target tiles tt = {w, 7 - w}.  acc[q][pt][v] is y[t][p] with
-// t = 16 tt[q] + 4g + v, p = 16 pt + i (BLUE e_t C_t S_in, then ORANGE, then D x).
-// fp32 io (bf16 io: k5_chunk_scan_wb below).
-template <class IO, int P, int R>
-__global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
-    const typename IO::T* __restrict__ x, const float* __restrict__ dt,
-    const typename IO::T* __restrict__ Bm, const typename IO::T* __restrict__ Cm,
-    const float* __restrict__ Av, const float* __restrict__ Dv, const double* __restrict__ cdt,
-    const float* __restrict__ S, typename IO::T* __restrict__ y, int N, int H) {
+// fp32 io (bf16 io: k5_chunk_scan_wb below).  Eight waves, one target row tile each:
+// wave w < 4 owns tile w, wave w >= 4 tile 11 - w, so the two waves that share a SIMD
+// (w and w + 4) own tiles w and 7 - w, (w + 1) + (8 - w) = 9 pair tiles per SIMD.  One
+// row tile's operands and accumulators fit 128 registers at (p, r) = (64, 128), so the two
+// workgroups of a CU are four waves per SIMD, which hide more of each other's vector,
+// LDS and barrier phases than two waves holding two tiles each (929 -> 894 us on the
+// 64k-token workload, 96.9 -> 91.3 us on the 130M-shaped one).  acc[pt][v] is y[t][p]
+// with t = 16 tt + 4g + v, p = 16 pt + i (BLUE e_t C_t S_in, then ORANGE, then D x).
+constexpr int NT8 = 2 * NT;  // threads of the fp32 K5 workgroup
+template <int P, int R>
+__global__ __launch_bounds__(NT8, 2) void k5_chunk_scan_w(
+    const float* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ Bm,
+    const float* __restrict__ Cm, const float* __restrict__ Av, const float* __restrict__ Dv,
+    const double* __restrict__ cdt, const float* __restrict__ S, float* __restrict__ y, int N,
+    int H) {
     constexpr int RS = R + 4, PS = P + 4, L = KC;
-    __shared__ float sM[wide_main<P, R>()];  // S_in [P, R], then one half of B | x
+    __shared__ __align__(16) float sM[wide_main<P, R>()];  // S_in [P, R], then one half of B | x
     float* sB = sM;
     float* sX = sM + TB * RS;
     __shared__ __align__(16) double sCdt[KC];
@@ -91,31 +98,76 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
     const int64_t bstride = static_cast<int64_t>(H) * R;
     const double* cc = cdt + c.c_bhn * L;
     const double la2 = static_cast<double>(Av[c.h]) * kLog2e;
-    const int tt[2] = {wave, NRT - 1 - wave};
-    const int tl[2] = {16 * tt[0] + i, 16 * tt[1] + i};
+    const int tt = wave < 4 ? wave : 11 - wave;
+    const int tl = 16 * tt + i;
 
-    v4f creg[2][R / 16];
+    v4f creg[R / 16];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int kk = 0; kk < R / 16; ++kk)
+        creg[kk] = *reinterpret_cast<const v4f*>(Cm + brow0 + static_cast<int64_t>(tl) * bstride + 16 * kk + 4 * g);
+    {
+        // S_in [P, R] into LDS, every load issued before the first store
+        constexpr int V = R / 4, TOT = P * V, IT = (TOT + NT8 - 1) / NT8;
+        const float* sp = S + c.ch * (P * R);
+        v4f sv[IT];
 #pragma unroll
-        for (int kk = 0; kk < R / 16; ++kk)
-            creg[q][kk] = io<IO>::ld4(Cm, brow0 + static_cast<int64_t>(tl[q]) * bstride + 16 * kk + 4 * g);
-    stage_mat<R, P>(sM, S + c.ch * (P * R));
+        for (int it = 0; it < IT; ++it) {
+            const int idx = tid + it * NT8;
+            if (TOT % NT8 == 0 || idx < TOT) sv[it] = *reinterpret_cast<const v4f*>(sp + idx * 4);
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = tid + it * NT8;
+            if (TOT % NT8 == 0 || idx < TOT)
+                *reinterpret_cast<v4f*>(sM + (idx / V) * RS + (idx % V) * 4) = sv[it];
+        }
+    }
     if (tid < KC) {
         sCdt[tid] = cc[tid];
         sDt[tid] = dt[c.c_bhn * L + tid];
     }
     __syncthreads();
 
+    // One half of the source rows (LDS row 16u + e is chunk row 16 (2u + half) + e) in
+    // registers, loaded while the matrix cores work, then stored after a barrier.
+    constexpr int VB = R / 4, TOTB = TB * VB, ITB = (TOTB + NT8 - 1) / NT8;
+    constexpr int VX = P / 4, TOTX = TB * VX, ITX = (TOTX + NT8 - 1) / NT8;
+    v4f preB[ITB], preX[ITX];
+    auto load_half = [&](int half) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < ITB; ++it) {
+            const int idx = tid + it * NT8, lr = idx / VB;
+            const int crow = 16 * (2 * (lr >> 4) + half) + (lr & 15);
+            if (TOTB % NT8 == 0 || idx < TOTB)
+                preB[it] = *reinterpret_cast<const v4f*>(Bm + brow0 + static_cast<int64_t>(crow) * bstride + (idx % VB) * 4);
+        }
+#pragma unroll
+        for (int it = 0; it < ITX; ++it) {
+            const int idx = tid + it * NT8, lr = idx / VX;
+            const int crow = 16 * (2 * (lr >> 4) + half) + (lr & 15);
+            if (TOTX % NT8 == 0 || idx < TOTX)
+                preX[it] = *reinterpret_cast<const v4f*>(x + xrow0 + static_cast<int64_t>(crow) * xstride + (idx % VX) * 4);
+        }
+    };
+    auto store_half = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < ITB; ++it) {
+            const int idx = tid + it * NT8;
+            if (TOTB % NT8 == 0 || idx < TOTB)
+                *reinterpret_cast<v4f*>(sB + (idx / VB) * RS + (idx % VB) * 4) = preB[it];
+        }
+#pragma unroll
+        for (int it = 0; it < ITX; ++it) {
+            const int idx = tid + it * NT8;
+            if (TOTX % NT8 == 0 || idx < TOTX)
+                *reinterpret_cast<v4f*>(sX + (idx / VX) * PS + (idx % VX) * 4) = preX[it];
+        }
+    };
     // the even half of the source rows loads into registers during BLUE
-    v4f preB[RowTiles<R, TB>::IT], preX[RowTiles<P, TB>::IT];
-    load_half_rows<IO, R>(preB, Bm + brow0, bstride, 0);
-    load_half_rows<IO, P>(preX, x + xrow0, xstride, 0);
-    v4f acc[2][P / 16];
+    load_half(0);
+    v4f acc[P / 16];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int pt = 0; pt < P / 16; ++pt) acc[q][pt] = zero4();
+    for (int pt = 0; pt < P / 16; ++pt) acc[pt] = zero4();
     // BLUE: A = C rows (k = r), B operand = S_in[p, r] read along r
 #pragma unroll
     for (int kk = 0; kk < R / 16; ++kk) {
@@ -123,35 +175,25 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
         for (int pt = 0; pt < P / 16; ++pt) {
             const v4f bop = *reinterpret_cast<const v4f*>(sM + (pt * 16 + i) * RS + 16 * kk + 4 * g);
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-#pragma unroll
-                for (int q = 0; q < 2; ++q) acc[q][pt] = mfma16(creg[q][kk][v], bop[v], acc[q][pt]);
+            for (int v = 0; v < 4; ++v) acc[pt] = mfma16(creg[kk][v], bop[v], acc[pt]);
         }
     }
-    double ct[2];
+    const double ct = sCdt[tl];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        ct[q] = sCdt[tl[q]];
+    for (int v = 0; v < 4; ++v) {
+        const float e = exp2_of(la2 * sCdt[16 * tt + 4 * g + v]);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const float e = exp2_of(la2 * sCdt[16 * tt[q] + 4 * g + v]);
-#pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt) acc[q][pt][v] *= e;
-        }
+        for (int pt = 0; pt < P / 16; ++pt) acc[pt][v] *= e;
     }
 
-    // ORANGE over source tiles j <= tt[q]; tt[0] < tt[1], so tile j pairs with
-    // both own tiles while j <= tt[0] and with tt[1] alone after that.
-    auto tile = [&](int j, int u, auto qlo) {
-        constexpr int QLO = decltype(qlo)::value;
-        v4f cbt[2];
-#pragma unroll
-        for (int q = QLO; q < 2; ++q) cbt[q] = zero4();
+    // ORANGE over source tiles j <= tt: CB^T[s, t] (lane: t = tl, s = 16j + 4g + v), its
+    // decay-weighted W, then y += W x.
+    auto tile = [&](int j, int u) __attribute__((always_inline)) {
+        v4f cbt = zero4();
 #pragma unroll
         for (int kk = 0; kk < R / 16; ++kk) {
             const v4f aop = *reinterpret_cast<const v4f*>(sB + (16 * u + i) * RS + 16 * kk + 4 * g);
-#pragma unroll
-            for (int q = QLO; q < 2; ++q) cbt[q] = mfma_k16<IO>(aop, creg[q][kk], cbt[q]);
+            cbt = mfma_k16<F32>(aop, creg[kk], cbt);
         }
         const v2d cs01 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g);
         const v2d cs23 = *reinterpret_cast<const v2d*>(sCdt + 16 * j + 4 * g + 2);
@@ -163,57 +205,44 @@ __global__ __launch_bounds__(NT, 2) void k5_chunk_scan_w(
         for (int v = 0; v < 4; ++v)
 #pragma unroll
             for (int pt = 0; pt < P / 16; ++pt) xs[v][pt] = sX[(16 * u + 4 * g + v) * PS + pt * 16 + i];
-        float wv[2][4];
+        float wv[4];
 #pragma unroll
-        for (int q = QLO; q < 2; ++q)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                // masked pairs (s > t) take gap 0 and weight 0: arithmetic, not a branch
-                const bool keep = (j < tt[q]) || (16 * j + 4 * g + v <= tl[q]);
-                const double gap = keep ? ct[q] - csv[v] : 0.0;
-                wv[q][v] = cbt[q][v] * exp2_of(la2 * gap) * dts[v] * (keep ? 1.0f : 0.0f);
-            }
+        for (int v = 0; v < 4; ++v) {
+            // masked pairs (s > t) take gap 0 and weight 0: arithmetic, not a branch
+            const bool keep = (j < tt) || (16 * j + 4 * g + v <= tl);
+            const double gap = keep ? ct - csv[v] : 0.0;
+            wv[v] = cbt[v] * exp2_of(la2 * gap) * dts[v] * (keep ? 1.0f : 0.0f);
+        }
 #pragma unroll
         for (int v = 0; v < 4; ++v)
 #pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt)
-#pragma unroll
-                for (int q = QLO; q < 2; ++q) acc[q][pt] = mfma16(wv[q][v], xs[v][pt], acc[q][pt]);
+            for (int pt = 0; pt < P / 16; ++pt) acc[pt] = mfma16(wv[v], xs[v][pt], acc[pt]);
     };
     const float Dh = Dv[c.h];
     for (int half = 0; half < 2; ++half) {
         __syncthreads();  // the previous contents of sM are consumed
-        store_rows<R, TB>(sB, preB);
-        store_rows<P, TB>(sX, preX);
+        store_half();
         __syncthreads();
-        if (half == 0) {
-            load_half_rows<IO, R>(preB, Bm + brow0, bstride, 1);
-            load_half_rows<IO, P>(preX, x + xrow0, xstride, 1);
-        }
-        // SKIP: D x of this wave's target rows that sit in this half
+        if (half == 0) load_half(1);
+        // SKIP: D x of this wave's target rows if they sit in this half
+        if ((tt & 1) == half)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-            if ((tt[q] & 1) == half)
+            for (int v = 0; v < 4; ++v)
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-#pragma unroll
-                    for (int pt = 0; pt < P / 16; ++pt)
-                        acc[q][pt][v] += Dh * sX[(16 * (tt[q] >> 1) + 4 * g + v) * PS + pt * 16 + i];
+                for (int pt = 0; pt < P / 16; ++pt)
+                    acc[pt][v] += Dh * sX[(16 * (tt >> 1) + 4 * g + v) * PS + pt * 16 + i];
         for (int u = 0; u < 4; ++u) {
             const int j = 2 * u + half;
-            if (j <= tt[0]) tile(j, u, Q<0>{});
-            else if (j <= tt[1]) tile(j, u, Q<1>{});
+            if (j <= tt) tile(j, u);
         }
     }
 
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int v = 0; v < 4; ++v) {
+        const int64_t row = xrow0 + static_cast<int64_t>(16 * tt + 4 * g + v) * xstride;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t row = xrow0 + static_cast<int64_t>(16 * tt[q] + 4 * g + v) * xstride;
-#pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt) st_nt<IO>(y, row + pt * 16 + i, acc[q][pt][v]);
-        }
+        for (int pt = 0; pt < P / 16; ++pt) st_nt<F32>(y, row + pt * 16 + i, acc[pt][v]);
+    }
 }
 
 // K5 with bf16 io.  The halves' B rows are staged as bf16 row-major (stride R + 16): the
@@ -1226,10 +1255,10 @@ static hipError_t k5_wide_io(const Shape& s, const void* x, const float* dt, con
                                    static_cast<const T*>(Bm), static_cast<const T*>(Cm), A, D,    \
                                    cdt, S, static_cast<T*>(y), s.N, s.H);                         \
             else                                                                                  \
-                hipLaunchKernelGGL((k5_chunk_scan_w<IO, PP, RR>), dim3(static_cast<unsigned>(CH)), \
-                                   dim3(NT), 0, st, static_cast<const T*>(x), dt,                 \
-                                   static_cast<const T*>(Bm), static_cast<const T*>(Cm), A, D,    \
-                                   cdt, S, static_cast<T*>(y), s.N, s.H);                         \
+                hipLaunchKernelGGL((k5_chunk_scan_w<PP, RR>), dim3(static_cast<unsigned>(CH)),     \
+                                   dim3(NT8), 0, st, static_cast<const float*>(x), dt,            \
+                                   static_cast<const float*>(Bm), static_cast<const float*>(Cm),  \
+                                   A, D, cdt, S, static_cast<float*>(y), s.N, s.H);               \
             return hipGetLastError();                                                             \
         }                                                                                         \
         return hipErrorInvalidValue;                                                              \
