@@ -197,6 +197,86 @@ def chunk_kernel_bytes(w, kernel: str, k: int):
     return None
 
 
+def kernel_rw(w, kernel: str, k: int):
+    """(read, write) split of the algorithmic HBM bytes of one launch (the totals of kernel_work
+    and chunk_kernel_bytes), for the comparison with the streaming rate of the same mix; None for
+    kernels without a byte count."""
+    b, n, l, h, p, r = _shape(w, k)
+    ch = b * n * h
+    tok = ch * l
+    io = 2 if w.io == "bf16" else 4
+    st = 4 * p * r * ch
+    tiles = 1024 * (l // 16) * (l // 16 + 1) // 2 * ch
+    if kernel == "k1_cumsum":
+        return 4 * tok + 4 * h, 8 * tok
+    if kernel == "k4_state_pass":
+        return 4 * p * r * ch + 8 * ch + 4 * b * h * p * r, 4 * p * r * ch + 4 * b * h * p * r
+    if kernel == "k4_state_pass_bwd":
+        return 8 * p * r * ch + 8 * ch + 4 * b * h * p * r, 8 * p * r * ch + 4 * b * h * p * r
+    if kernel == "k_chunk_states":      # mean of the fwd launch (job 0) and the bwd one (jobs 0, 1)
+        r0, r1 = tok * (io * (p + r) + 12), tok * (io * (p + r) + 8)
+        return (2 * r0 + r1) / 2, 1.5 * st
+    if kernel == "k5_chunk_scan":
+        return tok * (io * (p + 2 * r) + 12) + st, tok * io * p
+    if kernel == "k_bwd_target":
+        return tok * (io * (p + 2 * r) + 24) + 2 * st + tiles, tok * (io * r + 4)
+    if kernel == "k_bwd_source":
+        return tok * (io * (2 * p + 2 * r) + 12) + st, tok * (io * (p + r) + 16) + tiles
+    return None
+
+
+STREAM_MIXES = [(1, 0), (6, 1), (4, 1), (3, 1), (2, 1), (1, 1), (0, 1)]
+
+
+def stream_roofs(mib: int = 256, reps: int = 10) -> dict:
+    """HBM rate (bytes/s) of the library's streaming probe (ssd_stream_probe) for each
+    read:write mix, the better of cached and non-temporal accesses, over arrays of `mib` MiB:
+    what a kernel that only moves bytes in that mix reaches on this GPU."""
+    import torch
+    from mamba_ssd_chunked_amd import ssd
+    n16 = mib * (1 << 20) // 16
+    src = torch.zeros(6 * 4 * n16, device="cuda")
+    dst = torch.zeros(4 * n16, device="cuda")
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for nr, nw in STREAM_MIXES:
+        best = 0.0
+        for nt in (False, True):
+            sv = src[:4 * nr * n16] if nr else None
+            dv = dst[:4 * max(nw, 1) * n16]
+            for it in range(3 + reps):
+                if it == 3:
+                    e0.record(st)
+                rc = ssd.ssd_stream_probe(nr, nw, nt, sv, dv, n16, st)
+                if rc:
+                    raise ssd.SsdError(rc, "ssd_stream_probe", ssd.ssd_last_error())
+            e1.record(st)
+            e1.synchronize()
+            sec = e0.elapsed_time(e1) / 1e3 / reps
+            best = max(best, (nr + nw) * 16 * n16 / sec)
+        out[f"{nr}:{nw}"] = best
+    del src, dst
+    return out
+
+
+def annotate_stream(kernels: dict, w, k: int, roofs: dict):
+    """Each kernel with a byte rate gets its read:write split and the streaming rate of the
+    nearest mix (by read share): stream_roof_gbps, and stream_frac = its algorithmic bytes per
+    second over that rate."""
+    for name, ent in kernels.items():
+        rw = kernel_rw(w, name, k)
+        if rw is None or "gbps" not in ent:
+            continue
+        rd, wr = rw
+        share = rd / (rd + wr)
+        mix = min(STREAM_MIXES, key=lambda m: abs(m[0] / (m[0] + m[1]) - share))
+        roof = roofs[f"{mix[0]}:{mix[1]}"]
+        ent.update(read_share=round(share, 3), stream_mix=f"{mix[0]}:{mix[1]}",
+                   stream_roof_gbps=round(roof / 1e9, 1),
+                   stream_frac=round(ent["gbps"] * 1e9 / roof, 4))
+
+
 def moments_kernel_work(w, kernel: str, k: int):
     """Algorithmic flops of one launch of a moments kernel (pairs over the whole chunk)."""
     b, n, l, h, p, r = _shape(w, k)
@@ -812,6 +892,9 @@ def main():
                     help="skip the decode-step leg")
     ap.add_argument("--step-only", action="store_true",
                     help="run only the decode-step leg and print its JSON object")
+    ap.add_argument("--no-stream-probe", action="store_true",
+                    help="skip the streaming probe (the HBM rate of a plain kernel per read:write "
+                         "mix, against which each kernel's byte rate is also reported)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (a plain copy "
                          "kernel of known size, to calibrate HBM byte counters)")
@@ -868,6 +951,12 @@ def main():
     }
     if "at_layout_chunk_len" in r:
         out["at_layout_chunk_len"] = r["at_layout_chunk_len"]
+    roofs = None
+    if not args.no_stream_probe:
+        roofs = stream_roofs()
+        out["hbm_stream_roofs"] = {"unit": "GB/s", "probe": "ssd_stream_probe, 256 MiB arrays, best "
+                                   "of cached and non-temporal", **{m: round(v / 1e9, 1) for m, v in roofs.items()}}
+        annotate_stream(out["kernels"], w, r["kernel_chunk_len"], roofs)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp)
     if not args.no_moments:
@@ -880,6 +969,9 @@ def main():
         out["decode_step"] = bench_step(args)
     if not args.no_other_workloads:
         out["other_workloads"] = bench_other_workloads(args)
+        if roofs:
+            for name, res in out["other_workloads"].items():
+                annotate_stream(res["kernels"], inputs.WORKLOADS[name], res["kernel_chunk_len"], roofs)
     if args.copy_probe_mib > 0:
         out["copy_probe_bytes"] = copy_probe(args.copy_probe_mib)
     print(json.dumps(out), flush=True)

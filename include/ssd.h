@@ -351,6 +351,25 @@ int ssd_timing_collect(int max_kernels, char* names, size_t name_stride, double*
                        int64_t* launches, int* n_kernels);
 
 /*
+ * Benchmark instrumentation (not part of the computation): the HBM rate a plain
+ * streaming kernel reaches for a mix of reads and writes, the ceiling that the
+ * chunk kernels' byte rates are compared with (the nominal 8 TB/s is not reached
+ * by mixes with writes).  Enqueues on `stream` one launch that reads `reads`
+ * arrays of n16 16-byte elements from the device buffer src (array a at byte
+ * offset 16 * n16 * a) and writes their elementwise float sum to `writes` arrays
+ * in the device buffer dst (same layout); with writes = 0 nothing is written.
+ * nontemporal != 0 makes every load and store non-temporal.  (reads, writes) is
+ * one of (1,0), (6,1), (4,1), (3,1), (2,1), (1,1), (0,1); src must hold at least
+ * reads * n16 and dst writes * n16 elements (dst at least n16 with writes = 0),
+ * both 16-byte aligned; the caller owns them.  Returns 0, SSD_ERR_UNSUPPORTED for
+ * another mix, SSD_ERR_NULL for a missing buffer, SSD_ERR_SHAPE for n16 < 0,
+ * SSD_ERR_HIP if the launch fails.  (A grid-stride loop over at most 4096
+ * workgroups covers any n16.)
+ */
+int ssd_stream_probe(int reads, int writes, int nontemporal, const void* src, void* dst,
+                     int64_t n16, void* stream);
+
+/*
  * Debug aid (not part of the computation): where ssd_bwd leaves its per-token
  * partials of the gradient w.r.t. the within-chunk cumsum of dt*A in the
  * workspace, so that a test can read them after the call.  They are the

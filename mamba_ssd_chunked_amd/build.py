@@ -19,7 +19,7 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(OUT_DIR, "libmamba_ssd_hip.so")
 SOURCES = ["ssd_abi.cpp", "k_scan.hip", "k_chunk_fwd.hip", "k_chunk_bwd.hip", "k_chunk_wide.hip",
            "k_moments.hip", "k_pr.hip", "k_diag.hip", "k_quat.hip", "k_step.hip",
-           "noalloc_scratch.hip"]
+           "noalloc_scratch.hip", "k_stream.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are switched off for all device code.

@@ -507,6 +507,20 @@ int ssd_timing_collect(int max_kernels, char* names, size_t name_stride, double*
     return rc == SSD_OK ? ok() : rc;
 }
 
+int ssd_stream_probe(int reads, int writes, int nontemporal, const void* src, void* dst,
+                     int64_t n16, void* stream) {
+    static const int kMixes[][2] = {{1, 0}, {6, 1}, {4, 1}, {3, 1}, {2, 1}, {1, 1}, {0, 1}};
+    bool known = false;
+    for (const auto& m : kMixes) known = known || (m[0] == reads && m[1] == writes);
+    if (!known) return fail(SSD_ERR_UNSUPPORTED, "ssd_stream_probe: no (%d reads, %d writes) mix", reads, writes);
+    if (n16 < 0) return fail(SSD_ERR_SHAPE, "ssd_stream_probe: n16 = %lld", static_cast<long long>(n16));
+    if ((reads > 0 && !src) || !dst) return fail(SSD_ERR_NULL, "ssd_stream_probe: a buffer is NULL");
+    if (hipError_t e = ssd::launch_stream_probe(reads, writes, nontemporal != 0, src, dst, n16,
+                                                static_cast<hipStream_t>(stream)))
+        return fail(SSD_ERR_HIP, "ssd_stream_probe: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int ssd_workspace_size(const ssd_dims* dims, int op, size_t* bytes) {
     ssd::Shape s;
     if (int rc = validate_dims(dims, &s)) return rc;

@@ -35,6 +35,11 @@ hipError_t launch_chunk_states(const Shape& s, bool job_state, bool job_dstate, 
                                const float* A, const double* cdt, float* S, float* dS,
                                hipStream_t st, const double* phi = nullptr, float* T = nullptr);
 
+// Benchmark instrumentation (k_stream.hip): one streaming launch that reads `reads` and
+// writes `writes` arrays of n float4 (src / dst, array a at offset a * n).
+hipError_t launch_stream_probe(int reads, int writes, bool nontemporal, const void* src, void* dst,
+                               int64_t n, hipStream_t st);
+
 // ---------------------------------------------------------------- moments
 // Per chunk (one wave each): phi[t] = sum_{u>=t} mask_u exp(2A(cdt_u - cdt_t)),
 // psi[t] = sum_{u>=t} mask_u exp(A(cdt_u - cdt_t)), mask_u = (chunk start + u < valid[b]).

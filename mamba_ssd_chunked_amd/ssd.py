@@ -32,7 +32,7 @@ EXPORTS = ("ssd_workspace_size", "ssd_fwd", "ssd_fwd_noalloc", "ssd_bwd", "ssd_s
            "ssd_state_moments_bwd", "ssd_moments_pr", "ssd_moments_pr_bwd", "ssd_y_diag",
            "ssd_y_diag_bwd", "ssd_quat_scan", "ssd_quat_scan_bwd", "ssd_quat_workspace_size",
            "ssd_step", "ssd_last_error", "ssd_debug_enable", "ssd_timing_enable",
-           "ssd_timing_collect", "ssd_bwd_partial_region")
+           "ssd_timing_collect", "ssd_bwd_partial_region", "ssd_stream_probe")
 
 
 class ssd_dims(ctypes.Structure):
@@ -99,6 +99,8 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_bwd_partial_region.argtypes = [D, ctypes.c_char_p, ctypes.POINTER(ctypes.c_size_t),
                                            ctypes.POINTER(ctypes.c_size_t)]
     lib.ssd_bwd_partial_region.restype = ctypes.c_int
+    lib.ssd_stream_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int64, P]
+    lib.ssd_stream_probe.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -194,6 +196,18 @@ def ssd_timing_collect(max_kernels: int = 32) -> dict:
         nm = names.raw[k * stride:(k + 1) * stride].split(b"\0", 1)[0].decode()
         out[nm] = (float(ms[k]), int(cnt[k]))
     return out
+
+
+def ssd_stream_probe(reads: int, writes: int, nontemporal: bool, src: torch.Tensor,
+                     dst: torch.Tensor, n16: int, stream=None) -> int:
+    """Benchmark instrumentation: one streaming launch over `reads` source and `writes`
+    destination arrays of n16 16-byte elements (src / dst: contiguous fp32 device tensors of
+    exactly 4 * reads * n16 and 4 * max(writes, 1) * n16 elements; src may be None when
+    reads = 0)."""
+    ps = _ptr(src, "src", torch.float32, 4 * reads * n16, reads > 0)
+    pd = _ptr(dst, "dst", torch.float32, 4 * max(writes, 1) * n16, True)
+    return load_library().ssd_stream_probe(int(reads), int(writes), 1 if nontemporal else 0, ps, pd,
+                                           int(n16), _stream(stream))
 
 
 def ssd_workspace_size(dims: ssd_dims, op: int) -> int:

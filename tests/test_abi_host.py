@@ -362,3 +362,15 @@ def test_other_entry_points_grid_size_limit(lib):
     assert rejected(lib.ssd_step(1 << 12, 1 << 12, 16, 16, 0, *([FAKE] * 10)))
     cnt = counts(1)
     assert rejected(lib.ssd_moments_pr(1 << 12, 1 << 12, 16, FAKE, FAKE, cnt, 0, FAKE, None, None))
+
+
+def test_stream_probe_validates_before_any_launch(lib):
+    """The benchmark's streaming probe refuses an unknown mix, a missing buffer and a negative
+    size on the host."""
+    buf = ctypes.c_void_p(0x1000)
+    assert lib.ssd_stream_probe(5, 1, 0, buf, buf, 16, None) == 3      # SSD_ERR_UNSUPPORTED
+    assert lib.ssd_stream_probe(2, 2, 0, buf, buf, 16, None) == 3
+    assert lib.ssd_stream_probe(3, 1, 0, None, buf, 16, None) == 1     # SSD_ERR_NULL
+    assert lib.ssd_stream_probe(0, 1, 0, None, None, 16, None) == 1
+    assert lib.ssd_stream_probe(1, 1, 1, buf, buf, -1, None) == 2      # SSD_ERR_SHAPE
+    assert lib.ssd_stream_probe(1, 0, 0, buf, buf, 0, None) == 0       # nothing to move: no launch

@@ -155,3 +155,34 @@ def test_traffic_hash_ignores_comments_not_code():
     assert bench.code_of("char c = '\\'';  // q\nint y;") == "char c = '\\''; int y;"
     for key in bench.TRAFFIC_SOURCES:
         assert len(bench.traffic_hash(*key)) == 16
+
+
+@pytest.mark.parametrize("name", ["mamba2_130m_fp32", "mamba2_2p7b_bf16", "long_context_64k_fp32"])
+def test_read_write_split_adds_up_to_the_byte_counts(name):
+    """kernel_rw splits each kernel's algorithmic bytes into reads and writes without changing
+    the total that the byte rates use."""
+    w = inputs.WORKLOADS[name]
+    for k in (64, 128, 256):
+        for kern in ("k_chunk_states", "k5_chunk_scan", "k_bwd_target", "k_bwd_source"):
+            rd, wr = bench.kernel_rw(w, kern, k)
+            assert rd > 0 and wr > 0
+            assert rd + wr == pytest.approx(bench.chunk_kernel_bytes(w, kern, k), rel=1e-12), (kern, k)
+        for kern in ("k1_cumsum", "k4_state_pass", "k4_state_pass_bwd"):
+            rd, wr = bench.kernel_rw(w, kern, k)
+            total, kind = bench.kernel_work(w, kern, k)
+            assert kind == "byte" and rd + wr == total, (kern, k)
+    assert bench.kernel_rw(w, "reduce_heads", 128) is None
+
+
+def test_stream_annotation_takes_the_nearest_mix():
+    """A kernel's byte rate is set against the probe's rate for the mix nearest its read share."""
+    w = inputs.WORKLOADS["long_context_64k_fp32"]
+    roofs = {f"{r}:{wr}": 5e12 + 1e11 * i for i, (r, wr) in enumerate(bench.STREAM_MIXES)}
+    kernels = {"k4_state_pass": {"gbps": 6000.0}, "k_chunk_states": {"gbps": 5600.0},
+               "reduce_heads": {"avg_ms": 0.01}}
+    bench.annotate_stream(kernels, w, 128, roofs)
+    assert kernels["k4_state_pass"]["stream_mix"] == "1:1"
+    assert kernels["k4_state_pass"]["stream_frac"] == pytest.approx(6e12 / roofs["1:1"], rel=1e-3)
+    rd, wr = bench.kernel_rw(w, "k_chunk_states", 128)
+    assert 0.7 < rd / (rd + wr) < 0.8 and kernels["k_chunk_states"]["stream_mix"] == "3:1"
+    assert "stream_frac" not in kernels["reduce_heads"]
