@@ -328,7 +328,10 @@ __device__ __forceinline__ void rows_x_lds(const v4f* areg, const float* lds, in
                 acc[nt] = mfma16(areg[kk][v], lds[(16 * kk + 4 * g + v) * lds_ld + nt * 16 + i], acc[nt]);
 }
 
-template <class IO, int P, int R>
+// FWD selects the forward (dm2 == nullptr) or the backward instance: separate kernels, so that
+// each allocates only its own LDS (the backward's 17 KB at r = 64 instead of the forward's 35 KB
+// lets every chunk-head of the moments workload run in one round of the machine).
+template <class IO, int P, int R, bool FWD>
 __global__ __launch_bounds__(NT) void km_chunk(
     const float* __restrict__ Sin, const float* __restrict__ Tm, const double* __restrict__ cdt,
     const float* __restrict__ Av, const double* __restrict__ phi, const double* __restrict__ psi,
@@ -337,9 +340,7 @@ __global__ __launch_bounds__(NT) void km_chunk(
     float* __restrict__ dSl, float* __restrict__ BS, double* __restrict__ hsh,
     double* __restrict__ hdm, int N, int H, int L) {
     constexpr int RS = R + 4;
-    constexpr int MROWS = P > R ? P : R;
-    __shared__ float sA[MROWS * RS];  // fwd: H ; bwd: S = dm2 + dm2^T
-    __shared__ float sV[P * RS];      // fwd: 2T + c2 H
+    __shared__ float sA[(FWD ? P : R) * RS];  // fwd: H ; bwd: S = dm2 + dm2^T
     __shared__ double sRed[2 * (NT / 64)];
     const ChunkHead c = decode_ch(blockIdx.x, N, H);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
@@ -350,9 +351,10 @@ __global__ __launch_bounds__(NT) void km_chunk(
     const float* Hm = Sin + c.ch * (P * R);
     const float* Tc = Tm + c.ch * (P * R);
     const int64_t bh = static_cast<int64_t>(c.b) * H + c.h;
-    if (!dm2) {
+    if constexpr (FWD) {
         // forward: W = H^T (2T + c2 H), m1c = c1 colsum(H).  Every load of H and T is
         // issued before the first LDS write (one memory latency, not one per row batch).
+        __shared__ float sV[P * RS];  // 2T + c2 H
         {
             constexpr int V = R / 4, TOT = P * V, IT = (TOT + NT - 1) / NT;
             v4f hv[IT], tv[IT];
@@ -416,8 +418,7 @@ __global__ __launch_bounds__(NT) void km_chunk(
                 m1c[c.ch * R + r] = static_cast<float>(c1) * tot;
             }
         }
-        return;
-    }
+    } else {
     // backward.  The first pass's H and T rows and the first B rows load into registers
     // ahead of the S staging, so their latency overlaps it.
     const float* d1 = dm1 ? dm1 + bh * R : nullptr;
@@ -543,6 +544,7 @@ __global__ __launch_bounds__(NT) void km_chunk(
     if (tid == 0) {
         hsh[c.ch] = sRed[0] + sRed[1] + sRed[2] + sRed[3];
         hdm[c.ch] = sRed[4] + sRed[5] + sRed[6] + sRed[7];
+    }
     }
 }
 
@@ -1062,9 +1064,14 @@ static hipError_t chunk_io(const Shape& s, const float* Sin, const float* T, con
     const dim3 grid(static_cast<unsigned>(CH));
 #define X(PP, RR)                                                                                  \
     if (s.P == PP && s.R == RR) {                                                                  \
-        hipLaunchKernelGGL((km_chunk<IO, PP, RR>), grid, dim3(NT), 0, st, Sin, T, cdt, A, phi, psi, \
-                           W, m1c, dm2, dm1, static_cast<const TT*>(Bm), HS, dSl, BS, hsh, hdm,    \
-                           s.N, s.H, s.L);                                                         \
+        if (dm2)                                                                                   \
+            hipLaunchKernelGGL((km_chunk<IO, PP, RR, false>), grid, dim3(NT), 0, st, Sin, T, cdt, A, \
+                               phi, psi, W, m1c, dm2, dm1, static_cast<const TT*>(Bm), HS, dSl, BS, \
+                               hsh, hdm, s.N, s.H, s.L);                                           \
+        else                                                                                       \
+            hipLaunchKernelGGL((km_chunk<IO, PP, RR, true>), grid, dim3(NT), 0, st, Sin, T, cdt, A,  \
+                               phi, psi, W, m1c, dm2, dm1, static_cast<const TT*>(Bm), HS, dSl, BS, \
+                               hsh, hdm, s.N, s.H, s.L);                                           \
         return hipGetLastError();                                                                  \
     }
     SSD_FOR_EACH_PR(X)
