@@ -61,7 +61,7 @@
  *    (SSD_ERR_UNSUPPORTED otherwise).  Results for different kernel_chunk_len
  *    agree up to floating-point rounding; ssd_workspace_size() depends on it.
  *  - Results are bitwise reproducible for equal inputs and kernel_chunk_len
- *    (no float atomics), except for the quaternion scan (see ssd_quat_scan).
+ *    (no float atomics).
  *  - Every call validates all arguments before it enqueues anything.  Return 0
  *    on success or one of the ssd_status codes; ssd_last_error() then gives a
  *    message (thread-local, valid until the next call on the thread).
@@ -271,10 +271,8 @@ int ssd_y_diag_bwd(int64_t ntokens, int64_t mimo_rank, int64_t nheads, int64_t h
  * Quaternions need not be unit.  Tensors 16-byte aligned; the workspace
  * (ssd_quat_workspace_size, 256-byte aligned) is caller-owned and used by one
  * call at a time.  Products and carries are fp64; cum is rounded to fp32 once.
- * Unlike the SSD entry points, results are not bitwise reproducible: segments
- * are chained by a look-back whose order of combination depends on timing, so
- * two runs may round to neighbouring fp32 values: each output quaternion agrees
- * to within two fp32 ulps of its norm.
+ * Results are bitwise reproducible: every segment's carry combines the same
+ * records in the same order whatever the timing.
  * Errors: SSD_ERR_NULL, SSD_ERR_SHAPE, SSD_ERR_UNSUPPORTED (size, alignment),
  * SSD_ERR_WORKSPACE, SSD_ERR_HIP.
  */

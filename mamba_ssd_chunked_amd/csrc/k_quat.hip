@@ -14,44 +14,45 @@
 // The scan moves 32 bytes per quaternion (q in, cum out) for about 28 flops, so
 // it is bound by HBM.  Both directions are first-order recurrences along t whose
 // step is associative, so the sequence is cut into segments of SEG = 4 * TS
-// steps handled by one workgroup each, and the segments are chained with a
-// single-pass decoupled look-back:
+// steps handled by one workgroup each, and the segments are chained in one pass:
 //  * a workgroup covers 64 consecutive lanes (h, j) of one batch row -- one
 //    lane per thread of a wave, 16 contiguous bytes each, so a wave reads 1 KB
 //    of a row per step -- and its 4 waves take 4 consecutive sub-segments of TS
 //    steps, holding their q (and d_cum) in registers, so HBM is read once;
 //  * each wave reduces its sub-segment to one map (a product for the forward,
 //    an affine map M (x) H + v for the reverse), the workgroup combines the 4
-//    through LDS, publishes that aggregate, then wave 0 walks back over the
-//    preceding segments' records: an inclusive record ends the walk, an
-//    aggregate is folded in and the walk goes on.  One poll reads the status
-//    words of 64 neighbours (one per lane; a ballot finds the nearest inclusive
-//    record) and the records folded are loaded in batches of 4 (8 records per
-//    batch held 64 more registers and halved the occupancy), so the walk costs a
-//    few memory round trips, not one per neighbour;
+//    through LDS and publishes that aggregate;
+//  * the segments of a chain are grouped in blocks of kQuatBlock; a segment's
+//    carry is its block's earlier aggregates folded in order, then the earlier
+//    blocks' aggregates in order, applied to the chain's start value; the last
+//    segment of a block publishes the block's aggregate (its own aggregate
+//    combined with the fold it takes for its carry).  The order of every fold
+//    is fixed, so results are bitwise reproducible, and a segment waits only
+//    for aggregates, which are published before any wait: no serial chain
+//    through the segments.  A segment folds fewer than kQuatBlock + nseg /
+//    kQuatBlock records, loaded 4 at a time;
 //  * a workgroup's chain (b, lane group) follows from its index; its segment is
 //    the ticket it draws from its chain's atomic counter when it starts, taken
 //    in dependency order (forward: from the first segment; reverse: from the
 //    last), so a workgroup only ever waits for workgroups of its chain that have
-//    already started, which never wait for it.  Every wait is bounded: past
-//    kMaxSpins polls the carry becomes NaN and is published, so the grid always
-//    drains (a wrong result, never a hang);
+//    already started and publish their aggregates without waiting.  Every wait
+//    is bounded: past kMaxSpins polls the carry becomes NaN and is published,
+//    so the grid always drains (a wrong result, never a hang);
 //  * no memory fences: on gfx950 an agent-scope release writes back the whole
 //    L2 of the XCD, and one per workgroup serialised the scan (6x slower).
 //    Instead every record word is an fp64 value whose 16 lowest mantissa bits
 //    carry the call's tag, written and read with agent-scope relaxed 64-bit
 //    atomics (coherent across the XCDs' L2s without fences).  A reader accepts
 //    a record once all four of its words carry the current tag, and retries
-//    otherwise, so the order in which a record and its status word become
-//    visible does not matter.  The tag perturbs a record by at most 2^-36 of its
-//    value.  Before every call one small kernel zeroes the status words and
-//    tickets and advances the tag word kept in the workspace (never 0 in its low
-//    16 bits); the scan kernels read the tag from there, so a call replayed from
-//    a captured graph still gets a new tag.
+//    otherwise; it uses the value with the tag bits cleared, so a record
+//    carries its value truncated to 36 significant bits (2^-36 relative), the
+//    same in every call.  Before every call one small kernel zeroes the tickets
+//    and advances the tag word kept in the workspace (never 0 in its low 16
+//    bits); the scan kernels read the tag from there, so a call replayed from a
+//    captured graph still gets a new tag.
 // Products and carries are fp64 (the fp32 inputs are exact in fp64), so the
 // result is within a few fp32 roundings of the exact scan at any length; cum
-// and d_q are rounded to fp32 once.  Which records a walk meets depends on
-// timing, so runs can differ in the last bit.
+// and d_q are rounded to fp32 once.
 #include "ssd_launch.hpp"
 
 namespace ssd {
@@ -61,7 +62,6 @@ namespace {
 constexpr int kLanes = 64;     // lanes (quaternions of a row) per workgroup
 constexpr int kWaves = 4;      // sub-segments per workgroup
 constexpr int kThreads = kLanes * kWaves;
-constexpr uint32_t kAggregate = 1u, kInclusive = 2u;
 constexpr int kMaxSpins = 1 << 20;
 constexpr uint64_t kTagMask = 0xffffull;
 
@@ -117,67 +117,61 @@ __device__ __forceinline__ bool load_record(const uint64_t* rec, int64_t r, int 
         const uint64_t w = __hip_atomic_load(p + word_of(r, c, lane), __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
         ok = ok && (w & kTagMask) == tag;
-        v[c] = __longlong_as_double(static_cast<long long>(w));
+        v[c] = __longlong_as_double(static_cast<long long>(w & ~kTagMask));
     }
     return ok;
 }
 
-// Waits (bounded) until the record carries the tag; NaN if it never does.
-__device__ __forceinline__ d4 await_record(const uint64_t* rec, int64_t r, int lane, uint32_t tag) {
-    d4 v;
-    for (int i = 0; i < kMaxSpins; ++i) {
-        if (__all(load_record(rec, r, lane, tag, v))) return v;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    return qnan();
-}
-
-__device__ __forceinline__ void set_status(uint32_t* status, uint32_t v, int lane) {
-    if (lane == 0) __hip_atomic_store(status, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// One poll of the look-back window: lane i reads the status of the neighbour
-// j0 + dir * i (0 outside [0, nseg)).  Returns, in walk order, c = the first
-// neighbour holding an inclusive record and z = the first holding nothing yet
-// (64: none).
-__device__ __forceinline__ void poll_window(const uint32_t* status_row, int j0, int dir, int nseg,
-                                            int lane, int& c, int& z) {
-    const int j = j0 + dir * lane;
-    uint32_t s = 0;
-    if (j >= 0 && j < nseg)
-        s = __hip_atomic_load(const_cast<uint32_t*>(status_row + j), __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t inc = __ballot(s == kInclusive);
-    const uint64_t none = __ballot(s == 0u);
-    c = inc ? __ffsll(static_cast<unsigned long long>(inc)) - 1 : 64;
-    z = none ? __ffsll(static_cast<unsigned long long>(none)) - 1 : 64;
-}
-
-// The walk shared by both directions: fold(j0, n) folds the aggregates of the n
-// neighbours j0, j0 + dir, ... in walk order, finish(j) ends with the inclusive
-// record of neighbour j; fold returns false when a record never arrives.
-// Returns false when kMaxSpins polls pass without progress or a record is lost.
-template <class Fold, class Finish>
-__device__ __forceinline__ bool look_back(const uint32_t* status_row, int j0, int dir, int nseg,
-                                          int lane, Fold fold, Finish finish) {
-    for (int spins = 0; spins < kMaxSpins;) {
-        int c, z;
-        poll_window(status_row, j0, dir, nseg, lane, c, z);
-        if (c < z) {  // every neighbour before the inclusive one holds an aggregate
-            if (!fold(j0, c)) return false;
-            finish(j0 + dir * c);
-            return true;
+// acc <- acc (x) rec[r0] (x) rec[r0 - 1] (x) ... over n records (latest first), loaded 4
+// at a time, each waited for (bounded); false when a record never arrives.
+__device__ __forceinline__ bool fold_prod(const uint64_t* rec, int64_t r0, int n, int lane,
+                                          uint32_t tag, d4& acc) {
+    for (int base = 0; base < n; base += 4) {
+        d4 r[4];
+        bool ok = false;
+        for (int spin = 0; spin < kMaxSpins && !ok; ++spin) {
+            bool all = true;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (base + u < n) all = load_record(rec, r0 - base - u, lane, tag, r[u]) && all;
+            ok = __all(all);
+            if (!ok) __builtin_amdgcn_s_sleep(1);
         }
-        if (z > 0) {  // fold what is there and move the window on
-            if (!fold(j0, z)) return false;
-            j0 += dir * z;
-            spins = 0;
-            continue;
-        }
-        ++spins;
-        __builtin_amdgcn_s_sleep(1);
+        if (!ok) return false;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (base + u < n) acc = qmul(acc, r[u]);
     }
-    return false;
+    return true;
+}
+
+// (aM, av) <- (aM, av) o map[r0] o map[r0 + dir] o ... over n affine maps H -> M (x) H + v
+// (records recm / recv), loaded 4 at a time, each waited for (bounded).
+__device__ __forceinline__ bool fold_affine(const uint64_t* recm, const uint64_t* recv, int64_t r0,
+                                            int dir, int n, int lane, uint32_t tag, d4& aM, d4& av) {
+    for (int base = 0; base < n; base += 4) {
+        d4 rm[4], rv[4];
+        bool ok = false;
+        for (int spin = 0; spin < kMaxSpins && !ok; ++spin) {
+            bool all = true;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (base + u < n) {
+                    all = load_record(recm, r0 + dir * (base + u), lane, tag, rm[u]) && all;
+                    all = load_record(recv, r0 + dir * (base + u), lane, tag, rv[u]) && all;
+                }
+            ok = __all(all);
+            if (!ok) __builtin_amdgcn_s_sleep(1);
+        }
+        if (!ok) return false;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (base + u < n) {
+                av = qmul(aM, rv[u]) + av;
+                aM = qmul(aM, rm[u]);
+            }
+    }
+    return true;
 }
 
 // The chain (b, group) is the workgroup's blockIdx.x % BG; its position in the
@@ -197,7 +191,7 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
         p[i] = v;
 }
 
-// Zero n status / ticket words and advance the call's tag (one thread).
+// Zero n ticket words and advance the call's tag (one thread).
 __global__ void k_quat_clear(uint32_t* __restrict__ p, int64_t n, uint32_t* __restrict__ tag) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * blockDim.x)
@@ -247,44 +241,25 @@ __global__ __launch_bounds__(kThreads) void k_quat_fwd(const float* __restrict__
 
     if (wave == 0) {
         const int64_t row0 = static_cast<int64_t>(bg) * nseg;
+        const int nblk = (nseg + kQuatBlock - 1) / kQuatBlock;
+        const int64_t brow0 = static_cast<int64_t>(bg) * nblk;
         const int64_t k = row0 + seg;
         d4 a = s_part[0][lane];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) a = qmul(s_part[w][lane], a);
-        d4 carry = qone();
-        if (seg == 0) {
-            if (init && act)
-                carry = to_d(*reinterpret_cast<const f4*>(init + (static_cast<int64_t>(b) * W + col) * 4));
-        } else {
-            store_record(rec.agg, k, lane, a, tag);
-            set_status(rec.status + k, kAggregate, lane);
-            d4 acc = qone();  // product of the aggregates walked over, latest first
-            auto fold = [&](int j0, int n) {
-                for (int base = 0; base < n; base += 4) {
-                    d4 r[4];
-                    bool ok = false;
-                    for (int spin = 0; spin < kMaxSpins && !ok; ++spin) {
-                        bool all = true;
-#pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            if (base + u < n)
-                                all = load_record(rec.agg, row0 + j0 - base - u, lane, tag, r[u]) && all;
-                        ok = __all(all);
-                        if (!ok) __builtin_amdgcn_s_sleep(1);
-                    }
-                    if (!ok) return false;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (base + u < n) acc = qmul(acc, r[u]);
-                }
-                return true;
-            };
-            auto finish = [&](int j) { carry = qmul(acc, await_record(rec.inc, row0 + j, lane, tag)); };
-            if (!look_back(rec.status + row0, seg - 1, -1, nseg, lane, fold, finish))
-                carry = qnan();  // timed out: publish NaN
-        }
-        store_record(rec.inc, k, lane, qmul(a, carry), tag);
-        set_status(rec.status + k, kInclusive, lane);
+        const int m = seg / kQuatBlock, first = m * kQuatBlock;
+        store_record(rec.agg, k, lane, a, tag);  // for the block's later segments
+        d4 carry = qone();  // the chain's start value
+        if (init && act)
+            carry = to_d(*reinterpret_cast<const f4*>(init + (static_cast<int64_t>(b) * W + col) * 4));
+        // the product of every earlier segment, latest first: this block's, then earlier blocks'
+        d4 acc = qone();
+        bool ok = fold_prod(rec.agg, k - 1, seg - first, lane, tag, acc);
+        if (seg - first == kQuatBlock - 1)  // the block's last segment publishes its aggregate
+            store_record(rec.bagg, brow0 + m, lane, ok ? qmul(a, acc) : qnan(), tag);
+        ok = fold_prod(rec.bagg, brow0 + m - 1, m, lane, tag, acc) && ok;
+        carry = ok ? qmul(acc, carry) : qnan();  // NaN: a record never arrived
+        if constexpr (!WRITE) store_record(rec.inc, k, lane, qmul(a, carry), tag);
         s_carry[lane] = carry;
     }
     if constexpr (WRITE) {
@@ -369,45 +344,23 @@ __global__ __launch_bounds__(kThreads) void k_quat_bwd(const float* __restrict__
             v = qmul(s_M[w][lane], v) + s_V[w][lane];
             M = qmul(s_M[w][lane], M);
         }
-        d4 carry = qzero();  // H entering the end of this segment
-        if (seg != nseg - 1) {
-            store_record(rec.agg, k, lane, M, tag);
-            store_record(rec.agg2, k, lane, v, tag);
-            set_status(rec.status + k, kAggregate, lane);
-            d4 aM = qone(), av = qzero();  // composition of the maps walked over
-            auto fold = [&](int j0, int n) {
-                for (int base4 = 0; base4 < n; base4 += 4) {
-                    d4 rm[4], rv[4];
-                    bool ok = false;
-                    for (int spin = 0; spin < kMaxSpins && !ok; ++spin) {
-                        bool all = true;
-#pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            if (base4 + u < n) {
-                                const int64_t r = row0 + j0 + base4 + u;
-                                all = load_record(rec.agg, r, lane, tag, rm[u]) && all;
-                                all = load_record(rec.agg2, r, lane, tag, rv[u]) && all;
-                            }
-                        ok = __all(all);
-                        if (!ok) __builtin_amdgcn_s_sleep(1);
-                    }
-                    if (!ok) return false;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (base4 + u < n) {
-                            av = qmul(aM, rv[u]) + av;
-                            aM = qmul(aM, rm[u]);
-                        }
-                }
-                return true;
-            };
-            auto finish = [&](int j) { carry = qmul(aM, await_record(rec.inc, row0 + j, lane, tag)) + av; };
-            if (!look_back(rec.status + row0, seg + 1, 1, nseg, lane, fold, finish))
-                carry = qnan();  // timed out: publish NaN
+        // H entering the end of this segment: the maps of every later segment composed in
+        // order (this block's, then later blocks') applied to H past the end, 0
+        const int nblk = (nseg + kQuatBlock - 1) / kQuatBlock;
+        const int64_t brow0 = static_cast<int64_t>(bg) * nblk;
+        const int pos = nseg - 1 - seg;  // place in the reverse order
+        const int m = pos / kQuatBlock, last = nseg - 1 - m * kQuatBlock;  // block, its highest segment
+        store_record(rec.agg, k, lane, M, tag);  // for the block's earlier segments
+        store_record(rec.agg2, k, lane, v, tag);
+        d4 aM = qone(), av = qzero();
+        bool ok = fold_affine(rec.agg, rec.agg2, k + 1, 1, last - seg, lane, tag, aM, av);
+        if (pos - m * kQuatBlock == kQuatBlock - 1) {  // the block's last segment: its map
+            store_record(rec.bagg, brow0 + m, lane, ok ? qmul(M, aM) : qnan(), tag);
+            store_record(rec.bagg2, brow0 + m, lane, ok ? qmul(M, av) + v : qnan(), tag);
         }
+        ok = fold_affine(rec.bagg, rec.bagg2, brow0 + m - 1, -1, m, lane, tag, aM, av) && ok;
+        const d4 carry = ok ? av : qnan();  // NaN: a record never arrived
         const d4 h_start = qmul(M, carry) + v;
-        store_record(rec.inc, k, lane, h_start, tag);
-        set_status(rec.status + k, kInclusive, lane);
         if (seg == 0 && d_init && act)
             *reinterpret_cast<f4*>(d_init + (static_cast<int64_t>(b) * W + col) * 4) = to_f(h_start);
         s_H[lane] = carry;
@@ -418,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void k_quat_bwd(const float* __restrict__
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                c0[c] = __longlong_as_double(static_cast<long long>(fwd_inc[word_of(k - 1, c, lane)]));
+                c0[c] = __longlong_as_double(static_cast<long long>(fwd_inc[word_of(k - 1, c, lane)] & ~kTagMask));
         }
         s_C[lane] = c0;
     }
@@ -461,19 +414,22 @@ QuatPlan quat_plan(const QuatShape& s, bool bwd) {
         return at;
     };
     p.tag = take(256);  // the call tag (kept across calls)
-    // per pass: one ticket per chain (each in its own 256 bytes), then one status
-    // word per workgroup
+    // per pass one ticket per chain, each in its own 256 bytes
     const int64_t chains = static_cast<int64_t>(s.B) * s.G;
-    p.words_per_pass = 64 * chains + (blocks + 63) / 64 * 64;
+    p.words_per_pass = 64 * chains;
     p.flag_words = p.words_per_pass * (bwd ? 2 : 1);
     p.flags = take(4 * static_cast<size_t>(p.flag_words));
     const size_t rec = static_cast<size_t>(blocks) * kLanes * 4 * sizeof(uint64_t);
+    const size_t brec = static_cast<size_t>(chains) * ((s.nseg + kQuatBlock - 1) / kQuatBlock) *
+                        kLanes * 4 * sizeof(uint64_t);
     p.agg = take(rec);
-    p.inc = take(rec);
+    p.bagg = take(brec);
     if (bwd) {
+        p.inc = take(rec);
         p.agg_b = take(rec);
         p.agg2_b = take(rec);
-        p.inc_b = take(rec);
+        p.bagg_b = take(brec);
+        p.bagg2_b = take(brec);
     }
     p.total = off;
     return p;
@@ -496,15 +452,18 @@ QuatRecords records(const QuatShape& s, const QuatPlan& p, void* ws, int pass) {
     uint32_t* flags = reinterpret_cast<uint32_t*>(w + p.flags) + pass * p.words_per_pass;
     QuatRecords r;
     r.ticket = flags;
-    r.status = flags + 64 * static_cast<int64_t>(s.B) * s.G;
     if (pass == 0) {
         r.agg = reinterpret_cast<uint64_t*>(w + p.agg);
         r.agg2 = nullptr;
-        r.inc = reinterpret_cast<uint64_t*>(w + p.inc);
+        r.bagg = reinterpret_cast<uint64_t*>(w + p.bagg);
+        r.bagg2 = nullptr;
+        r.inc = p.inc ? reinterpret_cast<uint64_t*>(w + p.inc) : nullptr;
     } else {
         r.agg = reinterpret_cast<uint64_t*>(w + p.agg_b);
         r.agg2 = reinterpret_cast<uint64_t*>(w + p.agg2_b);
-        r.inc = reinterpret_cast<uint64_t*>(w + p.inc_b);
+        r.bagg = reinterpret_cast<uint64_t*>(w + p.bagg_b);
+        r.bagg2 = reinterpret_cast<uint64_t*>(w + p.bagg2_b);
+        r.inc = nullptr;
     }
     return r;
 }

@@ -222,29 +222,36 @@ struct QuatShape {
     int nseg;    // segments of kQuatSeg steps
 };
 
-// Look-back records of one pass: a ticket counter per (b, group) chain (64
-// words apart), one status word per (b, group, segment) workgroup, and per lane
-// of each workgroup one quaternion record of 4 tagged fp64 words (see k_quat.hip).
+// Segments per block of a chain: a segment's carry folds the aggregates of its block's
+// earlier segments and then the aggregates of the earlier blocks (k_quat.hip).
+constexpr int kQuatBlock = 8;
+
+// Records of one pass: a ticket counter per (b, group) chain (64 words apart), and per lane
+// one quaternion record of 4 tagged fp64 words per workgroup (its aggregate; the forward
+// carry pass also its inclusive value) and per block of kQuatBlock segments (the block's
+// aggregate), see k_quat.hip.
 struct QuatRecords {
     uint32_t* ticket;
-    uint32_t* status;
-    uint64_t* agg;   // aggregate (forward: product; reverse: M of the affine map)
-    uint64_t* agg2;  // reverse only: v of the affine map
-    uint64_t* inc;   // inclusive value (forward: cum at the segment end; reverse: H at its start)
+    uint64_t* agg;    // aggregate (forward: product; reverse: M of the affine map)
+    uint64_t* agg2;   // reverse only: v of the affine map
+    uint64_t* bagg;   // block aggregates, same meaning
+    uint64_t* bagg2;  // reverse only
+    uint64_t* inc;    // forward: cum at the segment end (read by the reverse pass)
 };
 
 // Workspace layout (byte offsets, 256-byte aligned): the call tag word at `tag`
-// (kept across calls), then the status words of all passes together at `flags`
-// (flag_words 32-bit words) so one kernel clears them.
+// (kept across calls), then the ticket words of all passes together at `flags`
+// (flag_words 32-bit words) so one kernel clears them, then the records.
 struct QuatPlan {
-    size_t tag = 0, flags = 0, agg = 0, inc = 0, agg_b = 0, agg2_b = 0, inc_b = 0, total = 0;
+    size_t tag = 0, flags = 0, agg = 0, bagg = 0, inc = 0, agg_b = 0, agg2_b = 0, bagg_b = 0,
+           bagg2_b = 0, total = 0;
     int64_t flag_words = 0, words_per_pass = 0;
 };
 
 QuatShape quat_shape(int64_t B, int64_t S, int64_t H, int64_t J);
 QuatPlan quat_plan(const QuatShape& s, bool bwd);
 
-// Zero the ticket and status words and advance the call tag (must precede every
+// Zero the ticket words and advance the call tag (must precede every
 // forward / backward: the scan kernels read the tag from the workspace).
 hipError_t launch_quat_clear(const QuatShape& s, bool bwd, void* ws, hipStream_t st);
 // cum [B,S,H,J,4] = scan of q (init [B,H,J,4], NULL = identity).

@@ -273,20 +273,23 @@ def test_quat_entry_points_reject_bad_arguments(lib, case, code):
 
 
 def test_quat_workspace_plan(lib):
-    # a ticket per (batch, 64-lane group) chain (64 words each), one status word per
-    # (chain, 64-step segment), and fp64 quaternion records per lane: 2 arrays
-    # forward, 5 backward
+    # a ticket per (batch, 64-lane group) chain (64 words each) and pass, and fp64
+    # quaternion records of 64 lanes x 4 words per segment (2 KiB each): forward the
+    # aggregates; backward also the forward-carry pass's inclusive values and the reverse
+    # pass's two aggregate arrays (M and v); plus per block of 8 segments the block
+    # aggregates (1 array forward, 3 backward)
     b, s, h, j = 4, 2048, 24, 32
     chains = b * (h * j // 64)
-    blocks = chains * (s // 64)
-    words = 64 * chains + -(-blocks // 64) * 64
+    segs = chains * (s // 64)
+    blocks = chains * -(-(s // 64) // 8)
+    rec = 64 * 32
     fwd = ssd.ssd_quat_workspace_size(b, s, h, j, False)
     bwd = ssd.ssd_quat_workspace_size(b, s, h, j, True)
     # (plus 256 bytes for the call tag kept across calls)
-    assert fwd == 256 + 4 * words + 2 * blocks * 64 * 32
-    assert bwd == 256 + 8 * words + 5 * blocks * 64 * 32
-    # ragged: 15 lanes still take a whole group, 97 steps two segments
-    assert ssd.ssd_quat_workspace_size(2, 97, 3, 5, False) == 256 + 4 * (2 * 64 + 64) + 2 * (2 * 2 * 64 * 32)
+    assert fwd == 256 + 4 * 64 * chains + rec * (segs + blocks)
+    assert bwd == 256 + 8 * 64 * chains + rec * (4 * segs + 3 * blocks)
+    # ragged: 15 lanes still take a whole group, 97 steps two segments (one block)
+    assert ssd.ssd_quat_workspace_size(2, 97, 3, 5, False) == 256 + 4 * 64 * 2 + rec * (2 * 2 + 2)
     for args in ((0, 10, 2, 2), (3, 0, 2, 2)):
         assert ssd.ssd_quat_workspace_size(*args, False) == 0
         assert ssd.ssd_quat_workspace_size(*args, True) == 0
