@@ -909,7 +909,10 @@ def main():
 
     if args.moments_only:
         torch.cuda.set_device(0)
-        print(json.dumps(bench_moments(args)), flush=True)
+        res = bench_moments(args)
+        if args.copy_probe_mib > 0:
+            res["copy_probe_bytes"] = copy_probe(args.copy_probe_mib)
+        print(json.dumps(res), flush=True)
         return
     if args.diag_only:
         torch.cuda.set_device(0)
