@@ -117,12 +117,15 @@ def test_kernel_chunk_len_matches_oracle(l, kcl, io):
 # d_diff; the diagonal pair t = s, whose terms cancel exactly and dominate a memoryless
 # head, is held out of both sums, so A d_da carries no |A|-scaled rounding and every head,
 # A = -1e4 included, is held to the plain tolerance.
-EXTREME = [("f32", 128), ("f32", 64), ("bf16", 128), ("bf16", 64)]
+# Also at the benchmarks' (headdim, dstate) = (64, 128), where the fp32 source-row kernel
+# hands a tile over between waves on the diagonal block and bf16 runs the whole-chunk kernels.
+EXTREME = [("f32", 128, 32, 32), ("f32", 64, 32, 32), ("bf16", 128, 32, 32), ("bf16", 64, 32, 32),
+           ("f32", 128, 64, 128), ("f32", 64, 64, 128), ("bf16", 128, 64, 128)]
 
 
-@pytest.mark.parametrize("io,kcl", EXTREME, ids=[f"{e[0]}_k{e[1]}" for e in EXTREME])
-def test_extreme_decay_regimes(io, kcl):
-    w = inputs.custom(batch=2, seq=256, nheads=4, headdim=32, dstate=32, chunk_len=128, io=io,
+@pytest.mark.parametrize("io,kcl,p,r", EXTREME, ids=[f"{e[0]}_k{e[1]}_p{e[2]}_r{e[3]}" for e in EXTREME])
+def test_extreme_decay_regimes(io, kcl, p, r):
+    w = inputs.custom(batch=2, seq=256, nheads=4, headdim=p, dstate=r, chunk_len=128, io=io,
                       init_std=0.3, seed=901)
     inp = inputs.make_inputs(w)
     A, dt = inp["A"].clone(), inp["dt"].clone()
@@ -131,7 +134,7 @@ def test_extreme_decay_regimes(io, kcl):
     dt[:, 1] = 0.0
     dt[:, 2] = dt[:, 2] * 1e-6
     inp["A"], inp["dt"] = A, dt
-    say(f"case extreme decay {io} kernel_chunk_len {kcl}")
+    say(f"case extreme decay {io} kernel_chunk_len {kcl} p {p} r {r}")
     gpu = gpu_fwd_bwd(inp, kernel_chunk_len=kcl)
     ref = oracle_fwd_bwd(inp)
     for k in KEYS:
