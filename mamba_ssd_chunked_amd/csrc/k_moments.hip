@@ -314,25 +314,27 @@ __global__ __launch_bounds__(NT, 2) void km_fwd_rows(
 }
 
 // ---------------------------------------------------------------- per chunk
-// Rows of a [rows, K] fp32 matrix (16 per wave, row stride ldg) times an LDS
-// matrix [K, NC] (stride lds_ld): out tiles in the MFMA result layout.
+// Rows of a [rows, K] fp32 matrix (16 per wave) times a SYMMETRIC LDS matrix [K, NC] (stride
+// lds_ld): out tiles in the MFMA result layout.  The B operand S[k][col] for k = 16 kk + 4 g + v
+// is read as S[col][16 kk + 4 g .. + 3], one float4 per k group instead of four scalars.
 template <int K, int NC>
-__device__ __forceinline__ void rows_x_lds(const v4f* areg, const float* lds, int lds_ld, v4f* acc,
-                                           int i, int g) {
+__device__ __forceinline__ void rows_x_sym_lds(const v4f* areg, const float* lds, int lds_ld, v4f* acc,
+                                               int i, int g) {
 #pragma unroll
     for (int kk = 0; kk < K / 16; ++kk)
 #pragma unroll
-        for (int nt = 0; nt < NC / 16; ++nt)
+        for (int nt = 0; nt < NC / 16; ++nt) {
+            const v4f b = *reinterpret_cast<const v4f*>(lds + (nt * 16 + i) * lds_ld + 16 * kk + 4 * g);
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                acc[nt] = mfma16(areg[kk][v], lds[(16 * kk + 4 * g + v) * lds_ld + nt * 16 + i], acc[nt]);
+            for (int v = 0; v < 4; ++v) acc[nt] = mfma16(areg[kk][v], b[v], acc[nt]);
+        }
 }
 
 // FWD selects the forward (dm2 == nullptr) or the backward instance: separate kernels, so that
 // each allocates only its own LDS (the backward's 17 KB at r = 64 instead of the forward's 35 KB
 // lets every chunk-head of the moments workload run in one round of the machine).
 template <class IO, int P, int R, bool FWD>
-__global__ __launch_bounds__(NT) void km_chunk(
+__global__ __launch_bounds__(NT, (FWD || R > 64) ? 1 : 3) void km_chunk(
     const float* __restrict__ Sin, const float* __restrict__ Tm, const double* __restrict__ cdt,
     const float* __restrict__ Av, const double* __restrict__ phi, const double* __restrict__ psi,
     float* __restrict__ W, float* __restrict__ m1c, const float* __restrict__ dm2,
@@ -340,7 +342,7 @@ __global__ __launch_bounds__(NT) void km_chunk(
     float* __restrict__ dSl, float* __restrict__ BS, double* __restrict__ hsh,
     double* __restrict__ hdm, int N, int H, int L) {
     constexpr int RS = R + 4;
-    __shared__ float sA[(FWD ? P : R) * RS];  // fwd: H ; bwd: S = dm2 + dm2^T
+    __shared__ __align__(16) float sA[(FWD ? P : R) * RS];  // fwd: H ; bwd: S = dm2 + dm2^T
     __shared__ double sRed[2 * (NT / 64)];
     const ChunkHead c = decode_ch(blockIdx.x, N, H);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
@@ -502,8 +504,8 @@ __global__ __launch_bounds__(NT) void km_chunk(
         v4f o1[R / 16], o2[R / 16];
 #pragma unroll
         for (int nt = 0; nt < R / 16; ++nt) o1[nt] = o2[nt] = zero4();
-        rows_x_lds<R, R>(ah, sA, RS, o1, i, g);
-        rows_x_lds<R, R>(av, sA, RS, o2, i, g);
+        rows_x_sym_lds<R, R>(ah, sA, RS, o1, i, g);
+        rows_x_sym_lds<R, R>(av, sA, RS, o2, i, g);
 #pragma unroll
         for (int nt = 0; nt < R / 16; ++nt)
 #pragma unroll
@@ -524,7 +526,7 @@ __global__ __launch_bounds__(NT) void km_chunk(
         v4f o[R / 16];
 #pragma unroll
         for (int nt = 0; nt < R / 16; ++nt) o[nt] = zero4();
-        rows_x_lds<R, R>(ab, sA, RS, o, i, g);
+        rows_x_sym_lds<R, R>(ab, sA, RS, o, i, g);
 #pragma unroll
         for (int nt = 0; nt < R / 16; ++nt)
 #pragma unroll
