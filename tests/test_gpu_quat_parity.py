@@ -4,10 +4,10 @@ The Mamba-3 quaternion cumulative-product scan cum[t] = q_t (x) cum[t-1]
 (burn-mamba mamba3/quat_scan backward.rs page) and its exact reverse mode,
 through the C ABI, on seeded inputs: one step; partial 64-lane groups and
 ragged last segments; identity and random init; non-unit step quaternions;
-look-back chains of 32 to 2048 segments; the full-size workload on sampled
-heads (lanes are independent, so the oracle computes exactly those outputs)
-plus the unit-norm property on every output; workspace reuse across calls of
-different sizes; empty sequence and batch; run-to-run agreement.  Bar:
+chains of 32 to 1024 segments; the full-size workload on sampled heads
+(lanes are independent, so the oracle computes exactly those outputs) plus the
+unit-norm property on every output; workspace reuse across calls of different
+sizes; empty sequence and batch; bitwise equality of repeated calls.  Bar:
 per-tensor relative L2 <= 1e-5 (fp32 inputs).
 """
 import numpy as np
