@@ -72,10 +72,12 @@ def test_shapes_full(shape):
 
 
 # (workload, sampled heads, kernel_chunk_len): 0 is the automatic choice the benchmark
-# times; 256 runs the 256-token chunks of the workloads unsplit.
+# times (128); 64 and 256 run the other kernel chunk lengths (256: the workloads' chunks unsplit).
 FULL = [("mamba2_130m_fp32", [0, 13], 0), ("mamba2_130m_fp32", [5], 256),
-        ("mamba2_2p7b_bf16", [41], 0), ("long_context_64k_fp32", [7], 0),
-        ("long_context_64k_fp32", [30], 256), ("moments_valid_len_fp32", [3], 0)]
+        ("mamba2_130m_fp32", [22], 64),
+        ("mamba2_2p7b_bf16", [41], 0), ("mamba2_2p7b_bf16", [12], 64), ("mamba2_2p7b_bf16", [63], 256),
+        ("long_context_64k_fp32", [7], 0), ("long_context_64k_fp32", [30], 256),
+        ("long_context_64k_fp32", [19], 64), ("moments_valid_len_fp32", [3], 0)]
 
 
 @pytest.mark.parametrize("name,heads,kcl", FULL, ids=[f"{f[0]}-k{f[2]}" for f in FULL])
