@@ -48,7 +48,8 @@
  *    the chunked entry points batch * nheads * max(4 * nchunks * chunk_len,
  *    headdim * dstate, dstate^2) < 2^32; for ssd_y_diag 16 * ntokens * nheads;
  *    for ssd_step and ssd_moments_pr 256 * batch * nheads; for the quaternion
- *    scan 256 per (batch, 64 quaternions of a row, 64 steps).  Larger problems
+ *    scan 256 per (batch, 64 quaternions of a row, 64 steps of ssd_quat_scan or
+ *    32 steps of ssd_quat_scan_bwd).  Larger problems
  *    are split by the caller (over batch or heads, which are independent).
  *  - kernel_chunk_len: the chunked algorithm is an exact re-association of the
  *    recurrence above for every chunk length, so the kernels may run it at a

@@ -82,6 +82,10 @@ __device__ __forceinline__ f4 to_f(d4 a) {
     return f4{static_cast<float>(a[0]), static_cast<float>(a[1]), static_cast<float>(a[2]),
               static_cast<float>(a[3])};
 }
+// The fp32 values pass through an empty asm statement, so the compiler cannot keep their fp64
+// conversions from an earlier phase alive across the barriers (8 registers per quaternion
+// instead of 4) and converts them again where they are used.
+__device__ __forceinline__ void reconvert(f4& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ d4 qone() { return d4{1.0, 0.0, 0.0, 0.0}; }
 __device__ __forceinline__ d4 qzero() { return d4{0.0, 0.0, 0.0, 0.0}; }
 __device__ __forceinline__ d4 qnan() {
@@ -216,10 +220,15 @@ __global__ __launch_bounds__(kThreads) void k_quat_fwd(const float* __restrict__
     __shared__ uint32_t s_vid;
     __shared__ d4 s_part[kWaves][kLanes];
     __shared__ d4 s_carry[kLanes];
-    const int wave = threadIdx.x / kLanes, lane = threadIdx.x % kLanes;
+    // the wave index and the workgroup's segment are the same in every lane of a wave: taken
+    // as scalars, the per-step row offsets below are scalar too (no 64-bit address per step
+    // held in vector registers)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    const int lane = threadIdx.x % kLanes;
     const int BG = nb * G;
     const int bg = static_cast<int>(blockIdx.x % BG);
-    const int seg = static_cast<int>(take_ticket(rec.ticket, bg, &s_vid));
+    const int seg =
+        __builtin_amdgcn_readfirstlane(static_cast<int>(take_ticket(rec.ticket, bg, &s_vid)));
     const int b = bg / G, g = bg % G;
     const int col = g * kLanes + lane;
     const bool act = col < W;
@@ -264,6 +273,8 @@ __global__ __launch_bounds__(kThreads) void k_quat_fwd(const float* __restrict__
     }
     if constexpr (WRITE) {
         __syncthreads();
+#pragma unroll
+        for (int i = 0; i < TS; ++i) reconvert(x[i]);
         d4 c = s_carry[lane];
 #pragma unroll
         for (int w = 0; w < kWaves - 1; ++w)
@@ -298,10 +309,15 @@ __global__ __launch_bounds__(kThreads) void k_quat_bwd(const float* __restrict__
     __shared__ uint32_t s_vid;
     __shared__ d4 s_P[kWaves][kLanes], s_M[kWaves][kLanes], s_V[kWaves][kLanes];
     __shared__ d4 s_H[kLanes], s_C[kLanes];
-    const int wave = threadIdx.x / kLanes, lane = threadIdx.x % kLanes;
+    // the wave index and the workgroup's segment are the same in every lane of a wave: taken
+    // as scalars, the per-step row offsets below are scalar too (no 64-bit address per step
+    // held in vector registers)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    const int lane = threadIdx.x % kLanes;
     const int BG = nb * G;
     const int bg = static_cast<int>(blockIdx.x % BG);
-    const int seg = nseg - 1 - static_cast<int>(take_ticket(rec.ticket, bg, &s_vid));
+    const int seg =
+        __builtin_amdgcn_readfirstlane(nseg - 1 - static_cast<int>(take_ticket(rec.ticket, bg, &s_vid)));
     const int b = bg / G, g = bg % G;
     const int col = g * kLanes + lane;
     const bool act = col < W;
@@ -377,6 +393,11 @@ __global__ __launch_bounds__(kThreads) void k_quat_bwd(const float* __restrict__
     }
     __syncthreads();
 
+#pragma unroll
+    for (int i = 0; i < TS; ++i) {
+        reconvert(x[i]);
+        reconvert(dc[i]);
+    }
     d4 h = s_H[lane];  // H entering the end of this wave's sub-segment
 #pragma unroll
     for (int w = kWaves - 1; w > 0; --w)
@@ -435,13 +456,13 @@ QuatPlan quat_plan(const QuatShape& s, bool bwd) {
     return p;
 }
 
-QuatShape quat_shape(int64_t B, int64_t S, int64_t H, int64_t J) {
+QuatShape quat_shape(int64_t B, int64_t S, int64_t H, int64_t J, bool bwd) {
     QuatShape s;
     s.B = static_cast<int>(B);
     s.S = S;
     s.W = static_cast<int>(H * J);
     s.G = static_cast<int>((s.W + kLanes - 1) / kLanes);
-    s.nseg = static_cast<int>((S + kQuatSeg - 1) / kQuatSeg);
+    s.nseg = static_cast<int>((S + quat_seg(bwd) - 1) / quat_seg(bwd));
     return s;
 }
 
@@ -492,7 +513,7 @@ hipError_t launch_quat_fwd(const QuatShape& s, const float* q, const float* init
     const QuatPlan p = quat_plan(s, false);
     const int64_t blocks = static_cast<int64_t>(s.B) * s.G * s.nseg;
     const uint32_t* tag = reinterpret_cast<const uint32_t*>(static_cast<char*>(ws) + p.tag);
-    k_quat_fwd<kQuatTS, true><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+    k_quat_fwd<kQuatTSFwd, true><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
         q, init, cum, records(s, p, ws, 0), s.B, s.S, s.W, s.G, s.nseg, tag);
     return hipGetLastError();
 }
@@ -505,10 +526,10 @@ hipError_t launch_quat_bwd(const QuatShape& s, const float* q, const float* init
     const QuatRecords r0 = records(s, p, ws, 0);
     const uint32_t* tag = reinterpret_cast<const uint32_t*>(static_cast<char*>(ws) + p.tag);
     if (stage == 0) {
-        k_quat_fwd<kQuatTS, false><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+        k_quat_fwd<kQuatTSBwd, false><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
             q, init, nullptr, r0, s.B, s.S, s.W, s.G, s.nseg, tag);
     } else {
-        k_quat_bwd<kQuatTS><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+        k_quat_bwd<kQuatTSBwd><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
             q, init, d_cum, d_q, d_init, r0.inc, records(s, p, ws, 1), s.B, s.S, s.W, s.G, s.nseg,
             tag);
     }

@@ -367,7 +367,7 @@ int check_diag_ptrs(const ssd::DiagShape& d,
 
 // Shared checks of the quaternion-scan entry points; fills *s.
 int validate_quat(const char* who, int64_t batch, int64_t seq, int64_t nheads, int64_t nquat,
-                  ssd::QuatShape* s) {
+                  bool bwd, ssd::QuatShape* s) {
     if (batch < 0 || seq < 0 || nheads <= 0 || nquat <= 0)
         return fail(SSD_ERR_SHAPE,
                     "%s: need batch >= 0, seq >= 0 and nheads, nquat > 0 (got %lld, %lld, %lld, %lld)",
@@ -376,7 +376,7 @@ int validate_quat(const char* who, int64_t batch, int64_t seq, int64_t nheads, i
     if (lanes > (double)(1 << 24) || batch > (1 << 30) || seq > (int64_t(1) << 40) ||
         (double)batch * seq * lanes * 4.0 > 4.0e18)
         return fail(SSD_ERR_UNSUPPORTED, "%s: problem too large for one call", who);
-    *s = ssd::quat_shape(batch, seq, nheads, nquat);
+    *s = ssd::quat_shape(batch, seq, nheads, nquat, bwd);
     // one workgroup of 256 work-items per (b, 64-lane group, segment)
     if ((double)s->B * s->G * s->nseg * 256.0 > ssd::kMaxGridItems)
         return fail(SSD_ERR_UNSUPPORTED, "%s: problem too large for one call: a launch would "
@@ -852,7 +852,7 @@ int ssd_y_diag_bwd(int64_t ntokens, int64_t mimo_rank, int64_t nheads, int64_t h
 int ssd_quat_workspace_size(int64_t batch, int64_t seq, int64_t nheads, int64_t nquat, int bwd,
                             size_t* bytes) {
     ssd::QuatShape s;
-    if (int rc = validate_quat("ssd_quat_workspace_size", batch, seq, nheads, nquat, &s)) return rc;
+    if (int rc = validate_quat("ssd_quat_workspace_size", batch, seq, nheads, nquat, bwd != 0, &s)) return rc;
     if (!bytes) return fail(SSD_ERR_NULL, "ssd_quat_workspace_size: bytes is NULL");
     *bytes = ssd::quat_plan(s, bwd != 0).total;
     return ok();
@@ -861,7 +861,7 @@ int ssd_quat_workspace_size(int64_t batch, int64_t seq, int64_t nheads, int64_t 
 int ssd_quat_scan(int64_t batch, int64_t seq, int64_t nheads, int64_t nquat, const float* q,
                   const float* init, float* cum, void* ws, size_t ws_bytes, void* stream) {
     ssd::QuatShape s;
-    if (int rc = validate_quat("ssd_quat_scan", batch, seq, nheads, nquat, &s)) return rc;
+    if (int rc = validate_quat("ssd_quat_scan", batch, seq, nheads, nquat, false, &s)) return rc;
     const bool work = batch > 0 && seq > 0;
     if (work && (!q || !cum)) return fail(SSD_ERR_NULL, "ssd_quat_scan: q and cum are required");
     for (auto p : {std::make_pair((const void*)q, "q"), std::make_pair((const void*)init, "init"),
@@ -883,7 +883,7 @@ int ssd_quat_scan_bwd(int64_t batch, int64_t seq, int64_t nheads, int64_t nquat,
                       const float* init, const float* d_cum, float* d_q, float* d_init, void* ws,
                       size_t ws_bytes, void* stream) {
     ssd::QuatShape s;
-    if (int rc = validate_quat("ssd_quat_scan_bwd", batch, seq, nheads, nquat, &s)) return rc;
+    if (int rc = validate_quat("ssd_quat_scan_bwd", batch, seq, nheads, nquat, true, &s)) return rc;
     const bool work = batch > 0 && seq > 0;
     if (work && (!q || !d_cum || !d_q))
         return fail(SSD_ERR_NULL, "ssd_quat_scan_bwd: q, d_cum and d_q are required");

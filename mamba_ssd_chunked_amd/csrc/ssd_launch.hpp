@@ -211,15 +211,20 @@ hipError_t launch_diag_bwd(const DiagShape& d, const void* dy, const void* V, co
                            float* d_gamma, hipStream_t st);
 
 // ------------------------------------------------- quaternion cumulative-product scan
-constexpr int kQuatTS = 16;            // steps per wave (sub-segment)
-constexpr int kQuatSeg = 4 * kQuatTS;  // steps per workgroup (segment)
+// Steps per wave (sub-segment); a workgroup's 4 waves take a segment of 4x as many.  The
+// forward holds 16 steps per lane (three waves per SIMD); the backward's passes (the carry
+// pass and the reverse pass, which share one segmentation) hold 8, since the reverse pass
+// keeps q and the upstream gradient and fits two waves per SIMD only at that length.
+constexpr int kQuatTSFwd = 16;
+constexpr int kQuatTSBwd = 8;
+constexpr int quat_seg(bool bwd) { return 4 * (bwd ? kQuatTSBwd : kQuatTSFwd); }
 
 struct QuatShape {
     int B;       // batch
     int64_t S;   // sequence length
     int W;       // quaternions per (b, t) row: nheads * nquat
     int G;       // 64-lane groups per row
-    int nseg;    // segments of kQuatSeg steps
+    int nseg;    // segments of quat_seg(bwd) steps
 };
 
 // Segments per block of a chain: a segment's carry folds the aggregates of its block's
@@ -248,7 +253,7 @@ struct QuatPlan {
     int64_t flag_words = 0, words_per_pass = 0;
 };
 
-QuatShape quat_shape(int64_t B, int64_t S, int64_t H, int64_t J);
+QuatShape quat_shape(int64_t B, int64_t S, int64_t H, int64_t J, bool bwd);
 QuatPlan quat_plan(const QuatShape& s, bool bwd);
 
 // Zero the ticket words and advance the call tag (must precede every

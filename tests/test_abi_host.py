@@ -277,19 +277,22 @@ def test_quat_workspace_plan(lib):
     # quaternion records of 64 lanes x 4 words per segment (2 KiB each): forward the
     # aggregates; backward also the forward-carry pass's inclusive values and the reverse
     # pass's two aggregate arrays (M and v); plus per block of 8 segments the block
-    # aggregates (1 array forward, 3 backward)
+    # aggregates (1 array forward, 3 backward).  Segments are 64 steps in the forward and
+    # 32 steps in the backward's two passes.
     b, s, h, j = 4, 2048, 24, 32
     chains = b * (h * j // 64)
-    segs = chains * (s // 64)
-    blocks = chains * -(-(s // 64) // 8)
+    segs_f, segs_b = chains * (s // 64), chains * (s // 32)
+    blocks_f, blocks_b = chains * -(-(s // 64) // 8), chains * -(-(s // 32) // 8)
     rec = 64 * 32
     fwd = ssd.ssd_quat_workspace_size(b, s, h, j, False)
     bwd = ssd.ssd_quat_workspace_size(b, s, h, j, True)
     # (plus 256 bytes for the call tag kept across calls)
-    assert fwd == 256 + 4 * 64 * chains + rec * (segs + blocks)
-    assert bwd == 256 + 8 * 64 * chains + rec * (4 * segs + 3 * blocks)
-    # ragged: 15 lanes still take a whole group, 97 steps two segments (one block)
+    assert fwd == 256 + 4 * 64 * chains + rec * (segs_f + blocks_f)
+    assert bwd == 256 + 8 * 64 * chains + rec * (4 * segs_b + 3 * blocks_b)
+    # ragged: 15 lanes still take a whole group; 97 steps are two forward segments and four
+    # backward ones (one block each)
     assert ssd.ssd_quat_workspace_size(2, 97, 3, 5, False) == 256 + 4 * 64 * 2 + rec * (2 * 2 + 2)
+    assert ssd.ssd_quat_workspace_size(2, 97, 3, 5, True) == 256 + 8 * 64 * 2 + rec * (4 * 2 * 4 + 3 * 2)
     for args in ((0, 10, 2, 2), (3, 0, 2, 2)):
         assert ssd.ssd_quat_workspace_size(*args, False) == 0
         assert ssd.ssd_quat_workspace_size(*args, True) == 0
@@ -359,8 +362,15 @@ def test_other_entry_points_grid_size_limit(lib):
     # y_diag: 16 work-items per (token, head)
     assert rejected(lib.ssd_y_diag(1 << 28, 1, 1, 16, 16, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None))
     assert rejected(lib.ssd_y_diag_bwd(1 << 28, 1, 1, 16, 16, 0, *([FAKE] * 9), None))
-    # quaternion scan: 256 per (batch, 64-lane group, 64-step segment)
+    # quaternion scan: 256 per (batch, 64-lane group, segment), segments of 64 steps in the
+    # forward and 32 in the backward, so 2^9 groups of 2^20 steps fit the forward (2^31
+    # work-items) but not the backward (2^32)
     assert rejected(lib.ssd_quat_scan(1, 1 << 20, 1 << 13, 8, FAKE, None, FAKE, FAKE, 1 << 62, None))
+    size = ctypes.c_size_t(0)
+    assert lib.ssd_quat_workspace_size(1, 1 << 20, 1 << 12, 8, 0, ctypes.byref(size)) == 0
+    assert rejected(lib.ssd_quat_workspace_size(1, 1 << 20, 1 << 12, 8, 1, ctypes.byref(size)))
+    assert rejected(lib.ssd_quat_scan_bwd(1, 1 << 20, 1 << 12, 8, FAKE, None, FAKE, FAKE, None,
+                                          FAKE, 1 << 62, None))
     # decode step and participation ratio: 256 per (batch, head)
     assert rejected(lib.ssd_step(1 << 12, 1 << 12, 16, 16, 0, *([FAKE] * 10)))
     cnt = counts(1)
