@@ -44,9 +44,9 @@ HEADLINE = "long_context_64k_fp32"
 # source files without comments) is the one they were taken on (profiles/ssd_kernels_*.md
 # have the runs).
 TRAFFIC = {
-    ("k_bwd_source", "long_context_64k_fp32", 128): (5_387_913_216, 2_250_261_504, "d812f1d2e08c1f78"),
-    ("k_bwd_source", "mamba2_130m_fp32", 128): (501_182_464, 210_980_864, "d812f1d2e08c1f78"),
-    ("k_bwd_source", "mamba2_2p7b_bf16", 128): (743_428_096, 451_325_952, "c331d4ce5e442097"),
+    ("k_bwd_source", "long_context_64k_fp32", 128): (5_383_494_528, 2_250_249_587, "73e7055f476ac366"),
+    ("k_bwd_source", "mamba2_130m_fp32", 128): (501_964_390, 210_973_709, "73e7055f476ac366"),
+    ("k_bwd_source", "mamba2_2p7b_bf16", 128): (743_907_430, 451_310_598, "b3ec7abfbf19eec6"),
 }
 # the files a kernel's code comes from, by io type: with bf16 io the source-row kernel at
 # 128-token chunks is the whole-chunk one
