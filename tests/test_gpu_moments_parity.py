@@ -190,3 +190,57 @@ def test_moments_null_d_m1_and_determinism():
     for k in MGRADS:
         assert np.array_equal(b[k], c[k]), k
         assert rel_l2(a[k], b[k]) < 1e-6, k
+
+
+def draw_moment_cases(seed=20261203, n=24):
+    """Random moments problems from one fixed seed: every headdim / dstate / chunk_len and
+    a kernel chunk length dividing it, valid lengths per batch row anywhere in [0, seq]
+    (0, the whole sequence, chunk boundaries and mid-chunk), with or without an initial
+    state and d_m1; sizes capped for the oracle."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        io = ["f32", "bf16"][rng.integers(2)]
+        p, r = (int(v) for v in rng.choice([16, 32, 64, 128], 2))
+        l = int(rng.choice([64, 128, 256]))
+        kcl = int(rng.choice([0] + [k for k in (64, 128, 256) if k <= l and l % k == 0]))
+        b, h, nch = int(rng.integers(1, 4)), int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        seq = nch * l
+        if b * seq * h * p * r > (1 << 24):
+            continue
+        # 0: no valid token, 1: all, 2: a chunk boundary, 3: anywhere
+        kinds = rng.choice(4, size=b, p=[0.1, 0.25, 0.25, 0.4])
+        valid = tuple(int(v) for v in np.where(
+            kinds == 0, 0, np.where(kinds == 1, seq, np.where(
+                kinds == 2, rng.integers(0, nch + 1, size=b) * l, rng.integers(1, seq, size=b)))))
+        cases.append((io, b, seq, h, p, r, l, kcl, valid, bool(rng.integers(2)),
+                      bool(rng.integers(2)), int(rng.integers(1 << 30))))
+    return cases
+
+
+MOMENT_CASES = draw_moment_cases()
+
+
+def moment_case_id(c):
+    io, b, seq, h, p, r, l, kcl, valid, ui, ud, _ = c
+    return (f"{io}_b{b}_s{seq}_h{h}_p{p}_r{r}_l{l}_k{kcl}_v{'-'.join(map(str, valid))}"
+            f"_i{int(ui)}_m{int(ud)}")
+
+
+@pytest.mark.parametrize("case", MOMENT_CASES, ids=[moment_case_id(c) for c in MOMENT_CASES])
+def test_moments_random_case(case):
+    io, b, seq, h, p, r, l, kcl, valid, use_init, use_dm1, seed = case
+    say(f"moments sweep case {moment_case_id(case)} seed {seed}")
+    w = inputs.custom(batch=b, seq=seq, nheads=h, headdim=p, dstate=r, chunk_len=l, io=io,
+                      init_std=0.3 if use_init else 0.0, valid_len=valid, seed=seed)
+    inp = inputs.make_inputs(w)
+    gpu = gpu_moments(inp, valid, use_init=use_init, use_dm1=use_dm1, kernel_chunk_len=kcl)
+    ref = oracle_moments(inp, list(valid), use_init=use_init, use_dm1=use_dm1)
+    compare(gpu, ref, TOL[io], ("m2", "m1") + MGRADS, moment_case_id(case))
+    assert list(gpu["count"]) == list(ref["count"])
+    # nothing flows back from tokens past a row's valid length
+    for bi, v in enumerate(valid):
+        tail_x = gpu["d_x"].reshape(b, seq, h, p)[bi, v:]
+        tail_dt = gpu["d_dt"].reshape(b, h, seq)[bi, :, v:]
+        tail_B = gpu["d_B"].reshape(b, seq, h, r)[bi, v:]
+        assert not tail_x.any() and not tail_dt.any() and not tail_B.any(), (bi, v)
