@@ -98,3 +98,29 @@ def test_y_diag_determinism_and_empty():
     e = {k: v[:, :0].contiguous() for k, v in i.items()}
     out = gpu_diag(e)
     assert all(v.size == 0 for v in out.values())
+
+
+def draw_diag_cases(seed=20261204, n=16):
+    """Random same-step-correction problems from one fixed seed: mimo rank 1, 2 or 4, every
+    headdim / dstate, io type, one or two chunks of 64 or 128 tokens, batch and head counts."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        l = int(rng.choice([64, 128]))
+        p, r = (int(v) for v in rng.choice([16, 32, 64, 128], 2))
+        cases.append((int(rng.integers(1, 4)), l * int(rng.integers(1, 3)), l,
+                      int(rng.choice([1, 2, 4])), int(rng.integers(1, 7)), p, r,
+                      ["f32", "bf16"][rng.integers(2)], int(rng.integers(1 << 30))))
+    return cases
+
+
+DIAG_CASES = draw_diag_cases()
+
+
+@pytest.mark.parametrize("case", DIAG_CASES, ids=lambda c: "b%d_s%d_l%d_m%d_h%d_p%d_r%d_%s" % c[:8])
+def test_y_diag_random_case(case):
+    b, seq, l, m, h, p, r, io, seed = case
+    w = inputs.DiagWorkload("sweep", b, seq, l, m, h, p, r, io=io, seed=seed)
+    say(f"y_diag sweep case {case}")
+    i = inputs.make_diag_inputs(w)
+    compare(gpu_diag(i), oracle_diag(i), TOL[io], KEYS, f"y_diag sweep {case}")

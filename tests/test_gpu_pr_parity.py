@@ -205,3 +205,36 @@ def test_pr_penalty_loop_on_the_moments_workload(center):
     og = oracle.state_moments_bwd(od_m2, od_m1, x, dt, A, B, None, valid)
     ref = dict(pr=opr, d_m2=od_m2, d_m1=od_m1, **{k: og[k] for k in ("d_x", "d_B", "d_dt", "d_A")})
     compare(gpu, ref, TOL["f32"], tuple(gpu), f"pr loop center={center}")
+
+
+def draw_pr_cases(seed=20261206, n=16):
+    """Random participation-ratio problems from one fixed seed: batch and head counts, every
+    dstate, counts from 1 to 2^18 per row (so the sample can be rank-deficient), mean offset
+    and magnitude, raw or centred."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        b = int(rng.integers(1, 6))
+        counts = tuple(int(c) for c in np.exp(rng.uniform(0, np.log(1 << 18), size=b)).astype(int) + 1)
+        cases.append((b, int(rng.integers(1, 9)), int(rng.choice([16, 32, 64, 128])), counts,
+                      float(rng.choice([0.0, 0.5, 3.0])), float(10.0 ** rng.uniform(-3, 3)),
+                      bool(rng.integers(2)), int(rng.integers(1 << 30))))
+    return cases
+
+
+PR_CASES = draw_pr_cases()
+
+
+@pytest.mark.parametrize("case", PR_CASES, ids=lambda c: "b%d_h%d_r%d_mean%g_%s" % (
+    c[0], c[1], c[2], c[4], "centred" if c[6] else "raw"))
+def test_pr_random_case(case):
+    b, h, r, counts, mean, scale, center, seed = case
+    say(f"pr sweep case {case}")
+    m2, m1, count = sample_moments(b, h, r, counts, seed=seed, mean=mean, scale=scale)
+    d_pr = torch.randn(b, h, generator=torch.Generator().manual_seed(seed + 1))
+    gpu = gpu_pr(m2, m1, count, center, d_pr)
+    ref = oracle_pr(m2, m1, count, center, d_pr)
+    keys = ("pr", "trace", "d_m2") + (("d_m1",) if center else ())
+    compare(gpu, ref, TOL["f32"], keys, f"pr sweep {case[:3]}")
+    if not center:
+        assert np.all(gpu["d_m1"] == 0)

@@ -181,3 +181,26 @@ def test_quat_graph_replay_matches_eager():
             assert np.all(diff <= bound), f"replay {it}: {k}"
         step()  # eager calls on the same workspaces between replays
         torch.cuda.synchronize()
+
+
+def draw_quat_cases(seed=20261207, n=12):
+    """Random quaternion-scan problems from one fixed seed: batch, lengths from 1 to 3000
+    steps (ragged last segments in both directions' segmentations), 1 to 200 lanes per row
+    (partial 64-lane groups), unit or non-unit steps, random or identity init."""
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 4)), int(rng.integers(1, 3001)), int(rng.integers(1, 5)),
+             int(rng.integers(1, 51)), float(rng.choice([0.0, 0.05, 0.2])), bool(rng.integers(2)),
+             int(rng.integers(1 << 30))) for _ in range(n)]
+
+
+QUAT_CASES = draw_quat_cases()
+
+
+@pytest.mark.parametrize("case", QUAT_CASES, ids=[f"b{c[0]}_s{c[1]}_h{c[2]}_j{c[3]}_n{c[4]}_i{int(c[5])}"
+                                                  for c in QUAT_CASES])
+def test_quat_random_case(case):
+    b, s, h, j, nstd, rinit, seed = case
+    w = inputs.QuatWorkload("sweep", b, s, h, j, norm_std=nstd, random_init=rinit, seed=seed)
+    say(f"quat sweep case {case}")
+    i = inputs.make_quat_inputs(w)
+    compare(gpu_quat(i), oracle_quat(i), TOL["f32"], KEYS, f"quat sweep {case}")

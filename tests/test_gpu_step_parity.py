@@ -111,3 +111,33 @@ def test_step_empty_batch():
     y, ns = ssd.step(x, torch.zeros((0, 3), device="cuda"), torch.zeros(3, device="cuda"), B, B,
                      torch.zeros(3, device="cuda"), st)
     assert y.numel() == 0 and ns.numel() == 0
+
+
+def draw_step_cases(seed=20261205, n=16):
+    """Random decode steps from one fixed seed: batch and head counts, every headdim /
+    dstate, io type, and a cached state of scale 0, 0.5 or 2."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        p, r = (int(v) for v in rng.choice([16, 32, 64, 128], 2))
+        cases.append((int(rng.integers(1, 7)), int(rng.integers(1, 9)), p, r,
+                      ["f32", "bf16"][rng.integers(2)], float(rng.choice([0.0, 0.5, 2.0])),
+                      int(rng.integers(1 << 30))))
+    return cases
+
+
+STEP_CASES = draw_step_cases()
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=[f"b{c[0]}_h{c[1]}_p{c[2]}_r{c[3]}_{c[4]}_s{c[5]:g}"
+                                                  for c in STEP_CASES])
+def test_step_random_case(case):
+    b, h, p, r, io, state_std, seed = case
+    w = inputs.StepWorkload("sweep", b, h, p, r, io=io, state_std=state_std, seed=seed)
+    say(f"step sweep case {case}")
+    i = inputs.make_step_inputs(w)
+    out = gpu_step(i)
+    compare(out, oracle_step(i), TOL[io], KEYS, f"step sweep {case}")
+    inp = gpu_step(i, in_place=True)
+    for k in KEYS:
+        assert np.array_equal(out[k], inp[k]), f"in-place {k} differs from out-of-place"
