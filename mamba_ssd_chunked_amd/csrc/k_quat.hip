@@ -30,7 +30,7 @@
 //    is fixed, so results are bitwise reproducible, and a segment waits only
 //    for aggregates, which are published before any wait: no serial chain
 //    through the segments.  A segment folds fewer than kQuatBlock + nseg /
-//    kQuatBlock records, loaded 4 at a time;
+//    kQuatBlock records, loaded 4 (forward) or 2 (reverse) at a time;
 //  * a workgroup's chain (b, lane group) follows from its index; its segment is
 //    the ticket it draws from its chain's atomic counter when it starts, taken
 //    in dependency order (forward: from the first segment; reverse: from the
@@ -150,16 +150,18 @@ __device__ __forceinline__ bool fold_prod(const uint64_t* rec, int64_t r0, int n
 }
 
 // (aM, av) <- (aM, av) o map[r0] o map[r0 + dir] o ... over n affine maps H -> M (x) H + v
-// (records recm / recv), loaded 4 at a time, each waited for (bounded).
+// (records recm / recv), loaded 2 at a time, each waited for (bounded): two maps in flight
+// are 32 registers per lane, which keeps the reverse pass at three waves per SIMD (four in
+// flight took it to 189 VGPRs and two waves: 73 against 66 us on the quaternion workload).
 __device__ __forceinline__ bool fold_affine(const uint64_t* recm, const uint64_t* recv, int64_t r0,
                                             int dir, int n, int lane, uint32_t tag, d4& aM, d4& av) {
-    for (int base = 0; base < n; base += 4) {
-        d4 rm[4], rv[4];
+    for (int base = 0; base < n; base += 2) {
+        d4 rm[2], rv[2];
         bool ok = false;
         for (int spin = 0; spin < kMaxSpins && !ok; ++spin) {
             bool all = true;
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 2; ++u)
                 if (base + u < n) {
                     all = load_record(recm, r0 + dir * (base + u), lane, tag, rm[u]) && all;
                     all = load_record(recv, r0 + dir * (base + u), lane, tag, rv[u]) && all;
@@ -169,7 +171,7 @@ __device__ __forceinline__ bool fold_affine(const uint64_t* recm, const uint64_t
         }
         if (!ok) return false;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 2; ++u)
             if (base + u < n) {
                 av = qmul(aM, rv[u]) + av;
                 aM = qmul(aM, rm[u]);
