@@ -209,13 +209,15 @@ __global__ void k_quat_clear(uint32_t* __restrict__ p, int64_t n, uint32_t* __re
     }
 }
 
-// Forward scan.  WRITE: store cum; otherwise only the segment records (the
-// backward's forward carries: inc[k] = cum at the end of segment k).
+// Forward scan.  WRITE: store cum; otherwise only the segment records (the backward's
+// forward carries: inc[j] = cum at the end of the j-th half of a segment, one per segment
+// of the reverse pass, nseg_inc of them per chain).
 template <int TS, bool WRITE>
 __global__ __launch_bounds__(kThreads) void k_quat_fwd(const float* __restrict__ q,
                                                         const float* __restrict__ init,
                                                         float* __restrict__ cum, QuatRecords rec,
                                                         int nb, int64_t S, int W, int G, int nseg,
+                                                        int nseg_inc,
                                                         const uint32_t* __restrict__ tag_word) {
     constexpr int SEG = kWaves * TS;
     const uint32_t tag = *tag_word & 0xffffu;
@@ -255,9 +257,12 @@ __global__ __launch_bounds__(kThreads) void k_quat_fwd(const float* __restrict__
         const int nblk = (nseg + kQuatBlock - 1) / kQuatBlock;
         const int64_t brow0 = static_cast<int64_t>(bg) * nblk;
         const int64_t k = row0 + seg;
-        d4 a = s_part[0][lane];
+        d4 a = s_part[0][lane], half = a;
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) a = qmul(s_part[w][lane], a);
+        for (int w = 1; w < kWaves; ++w) {
+            a = qmul(s_part[w][lane], a);
+            if (w == kWaves / 2 - 1) half = a;  // the first half's product
+        }
         const int m = seg / kQuatBlock, first = m * kQuatBlock;
         store_record(rec.agg, k, lane, a, tag);  // for the block's later segments
         d4 carry = qone();  // the chain's start value
@@ -270,7 +275,11 @@ __global__ __launch_bounds__(kThreads) void k_quat_fwd(const float* __restrict__
             store_record(rec.bagg, brow0 + m, lane, ok ? qmul(a, acc) : qnan(), tag);
         ok = fold_prod(rec.bagg, brow0 + m - 1, m, lane, tag, acc) && ok;
         carry = ok ? qmul(acc, carry) : qnan();  // NaN: a record never arrived
-        if constexpr (!WRITE) store_record(rec.inc, k, lane, qmul(a, carry), tag);
+        if constexpr (!WRITE) {  // cum at the end of each half of the segment
+            const int64_t j = static_cast<int64_t>(bg) * nseg_inc + 2 * seg;
+            store_record(rec.inc, j, lane, qmul(half, carry), tag);
+            if (2 * seg + 1 < nseg_inc) store_record(rec.inc, j + 1, lane, qmul(a, carry), tag);
+        }
         s_carry[lane] = carry;
     }
     if constexpr (WRITE) {
@@ -429,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void k_quat_bwd(const float* __restrict__
 QuatPlan quat_plan(const QuatShape& s, bool bwd) {
     QuatPlan p;
     if (s.B <= 0 || s.S <= 0) return p;
-    const int64_t blocks = static_cast<int64_t>(s.B) * s.G * s.nseg;
+    const int64_t chains = static_cast<int64_t>(s.B) * s.G;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -438,21 +447,23 @@ QuatPlan quat_plan(const QuatShape& s, bool bwd) {
     };
     p.tag = take(256);  // the call tag (kept across calls)
     // per pass one ticket per chain, each in its own 256 bytes
-    const int64_t chains = static_cast<int64_t>(s.B) * s.G;
     p.words_per_pass = 64 * chains;
     p.flag_words = p.words_per_pass * (bwd ? 2 : 1);
     p.flags = take(4 * static_cast<size_t>(p.flag_words));
-    const size_t rec = static_cast<size_t>(blocks) * kLanes * 4 * sizeof(uint64_t);
-    const size_t brec = static_cast<size_t>(chains) * ((s.nseg + kQuatBlock - 1) / kQuatBlock) *
-                        kLanes * 4 * sizeof(uint64_t);
-    p.agg = take(rec);
-    p.bagg = take(brec);
+    // one record per lane and segment (rec) or block of segments (brec) of a chain
+    constexpr size_t kRec = static_cast<size_t>(kLanes) * 4 * sizeof(uint64_t);
+    auto rec = [&](int nseg) { return static_cast<size_t>(chains) * nseg * kRec; };
+    auto brec = [&](int nseg) {
+        return static_cast<size_t>(chains) * ((nseg + kQuatBlock - 1) / kQuatBlock) * kRec;
+    };
+    p.agg = take(rec(s.nseg_c));  // the forward's, or the carry pass's
+    p.bagg = take(brec(s.nseg_c));
     if (bwd) {
-        p.inc = take(rec);
-        p.agg_b = take(rec);
-        p.agg2_b = take(rec);
-        p.bagg_b = take(brec);
-        p.bagg2_b = take(brec);
+        p.inc = take(rec(s.nseg));  // one per reverse-pass segment
+        p.agg_b = take(rec(s.nseg));
+        p.agg2_b = take(rec(s.nseg));
+        p.bagg_b = take(brec(s.nseg));
+        p.bagg2_b = take(brec(s.nseg));
     }
     p.total = off;
     return p;
@@ -464,7 +475,8 @@ QuatShape quat_shape(int64_t B, int64_t S, int64_t H, int64_t J, bool bwd) {
     s.S = S;
     s.W = static_cast<int>(H * J);
     s.G = static_cast<int>((s.W + kLanes - 1) / kLanes);
-    s.nseg = static_cast<int>((S + quat_seg(bwd) - 1) / quat_seg(bwd));
+    s.nseg_c = static_cast<int>((S + quat_seg(false) - 1) / quat_seg(false));
+    s.nseg = bwd ? static_cast<int>((S + quat_seg(true) - 1) / quat_seg(true)) : s.nseg_c;
     return s;
 }
 
@@ -516,7 +528,7 @@ hipError_t launch_quat_fwd(const QuatShape& s, const float* q, const float* init
     const int64_t blocks = static_cast<int64_t>(s.B) * s.G * s.nseg;
     const uint32_t* tag = reinterpret_cast<const uint32_t*>(static_cast<char*>(ws) + p.tag);
     k_quat_fwd<kQuatTSFwd, true><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
-        q, init, cum, records(s, p, ws, 0), s.B, s.S, s.W, s.G, s.nseg, tag);
+        q, init, cum, records(s, p, ws, 0), s.B, s.S, s.W, s.G, s.nseg, 0, tag);
     return hipGetLastError();
 }
 
@@ -528,8 +540,9 @@ hipError_t launch_quat_bwd(const QuatShape& s, const float* q, const float* init
     const QuatRecords r0 = records(s, p, ws, 0);
     const uint32_t* tag = reinterpret_cast<const uint32_t*>(static_cast<char*>(ws) + p.tag);
     if (stage == 0) {
-        k_quat_fwd<kQuatTSBwd, false><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
-            q, init, nullptr, r0, s.B, s.S, s.W, s.G, s.nseg, tag);
+        const int64_t cblocks = static_cast<int64_t>(s.B) * s.G * s.nseg_c;
+        k_quat_fwd<kQuatTSFwd, false><<<dim3(static_cast<unsigned>(cblocks)), dim3(kThreads), 0, st>>>(
+            q, init, nullptr, r0, s.B, s.S, s.W, s.G, s.nseg_c, s.nseg, tag);
     } else {
         k_quat_bwd<kQuatTSBwd><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
             q, init, d_cum, d_q, d_init, r0.inc, records(s, p, ws, 1), s.B, s.S, s.W, s.G, s.nseg,

@@ -212,19 +212,23 @@ hipError_t launch_diag_bwd(const DiagShape& d, const void* dy, const void* V, co
 
 // ------------------------------------------------- quaternion cumulative-product scan
 // Steps per wave (sub-segment); a workgroup's 4 waves take a segment of 4x as many.  The
-// forward holds 16 steps per lane (three waves per SIMD); the backward's passes (the carry
-// pass and the reverse pass, which share one segmentation) hold 8, since the reverse pass
-// keeps q and the upstream gradient and fits two waves per SIMD only at that length.
+// forward and the backward's forward-carry pass hold 16 steps per lane (64-step segments);
+// the reverse pass holds 8 (32-step segments), since it keeps q and the upstream gradient
+// and fits three waves per SIMD only at that length.  The carry pass publishes cum at the
+// end of each half of its segments: one record per reverse-pass segment.
 constexpr int kQuatTSFwd = 16;
 constexpr int kQuatTSBwd = 8;
-constexpr int quat_seg(bool bwd) { return 4 * (bwd ? kQuatTSBwd : kQuatTSFwd); }
+constexpr int quat_seg(bool reverse) { return 4 * (reverse ? kQuatTSBwd : kQuatTSFwd); }
+static_assert(2 * quat_seg(true) == quat_seg(false), "a carry segment is two reverse segments");
 
 struct QuatShape {
     int B;       // batch
     int64_t S;   // sequence length
     int W;       // quaternions per (b, t) row: nheads * nquat
     int G;       // 64-lane groups per row
-    int nseg;    // segments of quat_seg(bwd) steps
+    int nseg;    // segments: of quat_seg(false) steps for the forward, quat_seg(true) for the
+                 // backward's reverse pass
+    int nseg_c;  // segments of quat_seg(false) steps (the forward and the carry pass)
 };
 
 // Segments per block of a chain: a segment's carry folds the aggregates of its block's

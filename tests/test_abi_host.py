@@ -277,8 +277,9 @@ def test_quat_workspace_plan(lib):
     # quaternion records of 64 lanes x 4 words per segment (2 KiB each): forward the
     # aggregates; backward also the forward-carry pass's inclusive values and the reverse
     # pass's two aggregate arrays (M and v); plus per block of 8 segments the block
-    # aggregates (1 array forward, 3 backward).  Segments are 64 steps in the forward and
-    # 32 steps in the backward's two passes.
+    # aggregates (1 array forward, 3 backward).  Segments are 64 steps in the forward and the
+    # backward's carry pass (its aggregates and block aggregates) and 32 steps in the reverse
+    # pass (the inclusive values, one per reverse segment, and the reverse pass's arrays).
     b, s, h, j = 4, 2048, 24, 32
     chains = b * (h * j // 64)
     segs_f, segs_b = chains * (s // 64), chains * (s // 32)
@@ -288,11 +289,12 @@ def test_quat_workspace_plan(lib):
     bwd = ssd.ssd_quat_workspace_size(b, s, h, j, True)
     # (plus 256 bytes for the call tag kept across calls)
     assert fwd == 256 + 4 * 64 * chains + rec * (segs_f + blocks_f)
-    assert bwd == 256 + 8 * 64 * chains + rec * (4 * segs_b + 3 * blocks_b)
-    # ragged: 15 lanes still take a whole group; 97 steps are two forward segments and four
-    # backward ones (one block each)
+    assert bwd == 256 + 8 * 64 * chains + rec * (segs_f + blocks_f + 3 * segs_b + 2 * blocks_b)
+    # ragged: 15 lanes still take a whole group; 97 steps are two 64-step segments and four
+    # 32-step ones (one block each)
     assert ssd.ssd_quat_workspace_size(2, 97, 3, 5, False) == 256 + 4 * 64 * 2 + rec * (2 * 2 + 2)
-    assert ssd.ssd_quat_workspace_size(2, 97, 3, 5, True) == 256 + 8 * 64 * 2 + rec * (4 * 2 * 4 + 3 * 2)
+    assert ssd.ssd_quat_workspace_size(2, 97, 3, 5, True) == (
+        256 + 8 * 64 * 2 + rec * (2 * 2 + 2 + 3 * 2 * 4 + 2 * 2))
     for args in ((0, 10, 2, 2), (3, 0, 2, 2)):
         assert ssd.ssd_quat_workspace_size(*args, False) == 0
         assert ssd.ssd_quat_workspace_size(*args, True) == 0
